@@ -1,0 +1,294 @@
+"""Pins of the fp64 oracle to things other than itself (CPU only).
+
+Each test checks the oracle against a fact the method or the mathematics fixes: a special case that reduces
+to a library routine (dense softmax attention, elu), a closed form, an invariance, brute force on tiny inputs,
+IEEE fp32 arithmetic done by numpy, or a hand-worked fixture under tests/golden/.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import sagesla as orc
+from conftest import to_np
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def head(wl, seed=0, b=0, h=0):
+    q, k, v, w = synth.make(wl, seed)
+    return to_np(q[b, h]), to_np(k[b, h]), to_np(v[b, h]), to_np(w)
+
+
+def sdpa64(Q, K, V, scale):
+    """Library dense attention (torch, fp64, CPU)."""
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float64))[None, None]
+    return torch.nn.functional.scaled_dot_product_attention(t(Q), t(K), t(V), scale=scale)[0, 0].numpy()
+
+
+SMALL = [
+    synth.custom(1, 1, 512, blk_q=128, blk_k=64),
+    synth.custom(1, 1, 1000, blk_q=128, blk_k=64),  # ragged: q tail 104, k tail 40
+    synth.custom(1, 1, 330, blk_q=64, blk_k=64),  # ragged: tails 10
+    synth.custom(1, 1, 6 * 7 * 8, grid=(6, 7, 8), structured=True, blk_q=64, blk_k=64),
+]
+
+
+# ---------------------------------------------------------------------------------------------------------
+# dense equivalence: top-k 100 %, quantization off -> textbook softmax attention
+# ---------------------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("wl", SMALL, ids=lambda w: f"N{w.N}-bq{w.blk_q}")
+def test_dense_equivalence_unsmoothed(wl):
+    Q, K, V, W = head(wl)
+    r = orc.forward_head(Q, K, V, W, wl.blk_q, wl.blk_k, wl.n_kb, linear=False, smooth_k=False, quant=False)
+    ref = sdpa64(Q, K, V, 1 / math.sqrt(wl.D))
+    np.testing.assert_allclose(r["out"], ref, atol=1e-12, rtol=0)
+
+
+@pytest.mark.parametrize("wl", SMALL, ids=lambda w: f"N{w.N}-bq{w.blk_q}")
+def test_dense_equivalence_smoothed(wl):
+    # smoothing only adds the fp32 rounding of k' = K - mu (relative 2^-24), nothing else
+    Q, K, V, W = head(wl)
+    r = orc.forward_head(Q, K, V, W, wl.blk_q, wl.blk_k, wl.n_kb, linear=False, smooth_k=True, quant=False)
+    ref = sdpa64(Q, K, V, 1 / math.sqrt(wl.D))
+    np.testing.assert_allclose(r["out"], ref, atol=2e-5, rtol=0)
+
+
+def test_dense_equivalence_quantized():
+    # top-k 100 % with quantization on == dense attention on the dequantized Q and smoothed K
+    wl = SMALL[1]
+    Q, K, V, W = head(wl)
+    r = orc.forward_head(Q, K, V, W, wl.blk_q, wl.blk_k, wl.n_kb, linear=False)
+    Qd = r["q_codes"].astype(np.float64) * np.repeat(r["q_scales"], wl.blk_q)[: wl.N, None]
+    Kd = r["k_codes"].astype(np.float64) * np.repeat(r["k_scales"], wl.blk_k)[: wl.N, None]
+    ref = sdpa64(Qd, Kd, V, 1 / math.sqrt(wl.D))
+    np.testing.assert_allclose(r["out"], ref, atol=1e-12, rtol=0)
+
+
+# ---------------------------------------------------------------------------------------------------------
+# K-mean smoothing
+# ---------------------------------------------------------------------------------------------------------
+def test_smoothing_invariance():
+    # subtracting one vector from every key leaves each softmax row unchanged; here only the fp32 rounding of
+    # k' differs, so the outputs agree to that rounding, and far below what a wrong mean would give
+    wl = SMALL[1]
+    Q, K, V, W = head(wl)
+    a = orc.forward_head(Q, K, V, W, wl.blk_q, wl.blk_k, 3, linear=False, smooth_k=True, quant=False)
+    b = orc.forward_head(Q, K, V, W, wl.blk_q, wl.blk_k, 3, linear=False, smooth_k=False, quant=False,
+                         mask=a["idx"])
+    np.testing.assert_allclose(a["out"], b["out"], atol=2e-5, rtol=0)
+    # the selection is invariant too: logits of a row shift by qbar_I . mu / sqrt(D)
+    assert np.array_equal(a["idx"], b["idx"])
+    # and the smoothing matters for the quantization: the bias dominates raw K's absmax
+    assert np.mean(np.abs(a["mu"])) > 0.5
+
+
+def test_kmean_exact_sum():
+    Q, K, V, W = head(SMALL[1])
+    assert orc.exact_sum_ok(K)
+    mu = orc.k_mean(K)
+    for c in range(K.shape[1]):
+        ref = float(np.float32(math.fsum(K[:, c]) / K.shape[0]))
+        assert mu[c] == ref
+
+
+def test_exact_sum_precondition_detects_failure():
+    x = np.array([[2.0 ** 60], [2.0 ** -10]])
+    assert not orc.exact_sum_ok(x)
+    assert orc.exact_sum_ok(np.array([[1.0], [2.0 ** -10]]))
+
+
+# ---------------------------------------------------------------------------------------------------------
+# quantization
+# ---------------------------------------------------------------------------------------------------------
+def test_quant_roundtrip_and_ieee_fp32(rng):
+    X = rng.standard_normal((300, 128)).astype(np.float32).astype(np.float64) * 3.0
+    X[130:140] *= 50.0  # an outlier band inside block 1
+    codes, scales = orc.quantize(X, 64)
+    for i in range(orc.n_blocks(300, 64)):
+        rows = orc.block_rows(300, 64, i)
+        xb, cb, s = X[rows], codes[rows], scales[i]
+        a = np.max(np.abs(xb))
+        # scale is the fp32 quotient absmax/127 computed in IEEE fp32 by numpy
+        assert s == float(np.float32(a) / np.float32(127.0))
+        # codes == round-half-even of numpy's IEEE fp32 quotient, clamped
+        ref = np.clip(np.rint(xb.astype(np.float32) / np.float32(s)), -127, 127)
+        assert np.array_equal(cb.astype(np.float64), ref.astype(np.float64))
+        # round trip within half a step (the fp32 quotient adds at most 127 * 2^-24 of a step)
+        err = np.abs(xb - cb * s)
+        assert np.all(err <= s / 2 * (1 + 2.0 ** -16))
+        assert np.count_nonzero(err > s / 2) <= 2
+        # the absmax element maps to +-127
+        j = np.unravel_index(np.argmax(np.abs(xb)), xb.shape)
+        assert abs(int(cb[j])) == 127
+
+
+def test_quant_zero_block_and_half_even():
+    X = np.zeros((128, 4))
+    X[64:, 0] = 127.0  # block 1: absmax 127 -> scale exactly 1
+    X[64, 1:4] = [0.5, 1.5, -2.5]  # exact halves round to even
+    codes, scales = orc.quantize(X, 64)
+    assert scales[0] == 0.0 and not codes[:64].any()
+    assert scales[1] == 1.0
+    assert list(codes[64, :4]) == [127, 0, 2, -2]
+
+
+def test_golden_quant_fixture():
+    with open(os.path.join(GOLDEN, "quant_block.json")) as f:
+        g = json.load(f)
+    X = np.array(g["x"], dtype=np.float64)[:, None]
+    codes, scales = orc.quantize(X, len(g["x"]))
+    assert float(scales[0]) == float(np.float32(g["scale_fp32"]))
+    assert [int(c) for c in codes[:, 0]] == g["codes"]
+
+
+# ---------------------------------------------------------------------------------------------------------
+# selection
+# ---------------------------------------------------------------------------------------------------------
+def test_select_bruteforce(rng):
+    for trial in range(20):
+        nq, nk = rng.integers(1, 9), rng.integers(1, 25)
+        s = np.round(rng.standard_normal((nq, nk)), 1)  # coarse values: many exact ties
+        k = int(rng.integers(0, nk + 1))
+        idx, gap = orc.select_topk(s, k)
+        for I in range(nq):
+            order = sorted(range(nk), key=lambda J: (-s[I, J], J))
+            assert list(idx[I]) == sorted(order[:k])
+            if 0 < k < nk:
+                assert gap[I] == s[I, order[k - 1]] - s[I, order[k]]
+
+
+def test_select_constant_keys_and_full():
+    wl = SMALL[0]
+    Q, K, V, W = head(wl)
+    Kc = np.ones_like(K) * 0.75  # every smoothed key is 0 -> all scores 0 -> ties -> lowest indices
+    r = orc.forward_head(Q, Kc, V, W, wl.blk_q, wl.blk_k, 3)
+    assert np.array_equal(r["idx"], np.tile(np.arange(3), (wl.n_qb, 1)))
+    assert not r["k_codes"].any() and not r["k_scales"].any()
+    r = orc.forward_head(Q, K, V, W, wl.blk_q, wl.blk_k, wl.n_kb)
+    assert np.array_equal(r["idx"], np.tile(np.arange(wl.n_kb), (wl.n_qb, 1)))
+
+
+def test_topk_count():
+    assert [orc.topk_count(w.topk_frac, w.n_kb) for w in synth.WORKLOADS.values()] == [4, 512, 51, 118, 210]
+    assert orc.topk_count(0.001, 10) == 1
+
+
+def test_selection_prefers_local_blocks_on_structured_input():
+    # a shared smooth field makes neighbouring blocks the most similar: the diagonal block is kept
+    wl = synth.custom(1, 1, 8 * 16 * 16, grid=(8, 16, 16), structured=True, blk_q=64, blk_k=64)
+    Q, K, V, W = head(wl)
+    r = orc.forward_head(Q, K, V, W, 64, 64, 4, linear=False)
+    assert np.mean([I in r["idx"][I] for I in range(wl.n_qb)]) > 0.9
+
+
+# ---------------------------------------------------------------------------------------------------------
+# sparse attention
+# ---------------------------------------------------------------------------------------------------------
+def test_sparse_bruteforce(rng):
+    N, D, bq, bk = 150, 16, 32, 16
+    Q = rng.standard_normal((N, D))
+    K = rng.standard_normal((N, D)) + 1.0
+    V = rng.standard_normal((N, D))
+    qc, qs = orc.quantize(Q, bq)
+    kc, ks = orc.quantize(K, bk)
+    nqb, nkb = orc.n_blocks(N, bq), orc.n_blocks(N, bk)
+    idx = np.stack([np.sort(rng.choice(nkb, 3, replace=False)) for _ in range(nqb)])
+    out = orc.sparse_attention(qc, qs, kc, ks, V, idx, bq, bk, 0.3)
+    for i in range(N):
+        I = i // bq
+        zs, vs = [], []
+        for J in idx[I]:
+            for j in range(J * bk, min(N, (J + 1) * bk)):
+                dot = sum(int(qc[i, c]) * int(kc[j, c]) for c in range(D))
+                zs.append(dot * qs[I] * ks[J] * 0.3)
+                vs.append(V[j])
+        m = max(zs)
+        w = [math.exp(z - m) for z in zs]
+        ref = sum(wi * vi for wi, vi in zip(w, vs)) / sum(w)
+        np.testing.assert_allclose(out[i], ref, atol=1e-12, rtol=0)
+
+
+def test_sparse_block_order_invariance(rng):
+    wl = SMALL[1]
+    Q, K, V, W = head(wl)
+    r = orc.forward_head(Q, K, V, W, wl.blk_q, wl.blk_k, 5, linear=False)
+    perm = np.stack([rng.permutation(row) for row in r["idx"]])
+    o2 = orc.sparse_attention(r["q_codes"], r["q_scales"], r["k_codes"], r["k_scales"], V, perm,
+                              wl.blk_q, wl.blk_k, 1 / math.sqrt(wl.D))
+    np.testing.assert_allclose(o2, r["o_s"], atol=1e-12, rtol=0)
+
+
+# ---------------------------------------------------------------------------------------------------------
+# linear branch
+# ---------------------------------------------------------------------------------------------------------
+def _phi_lib(x):
+    return torch.nn.functional.elu(torch.from_numpy(np.asarray(x, np.float64))).numpy() + 1.0
+
+
+@pytest.mark.parametrize("wl", SMALL[:3], ids=lambda w: f"N{w.N}-bq{w.blk_q}")
+def test_linear_closed_form_all_marginal(wl):
+    # no critical block: O_l = phi(Q)(phi(K)^T V) / phi(Q).sum(phi(K)), the plain linear-attention closed form
+    Q, K, V, W = head(wl)
+    r = orc.forward_head(Q, K, V, W, wl.blk_q, wl.blk_k, 0)
+    PQ, PK = _phi_lib(Q), _phi_lib(K)
+    ref = (PQ @ (PK.T @ V)) / (PQ @ PK.sum(axis=0))[:, None]
+    np.testing.assert_allclose(r["o_l"], ref, rtol=1e-11, atol=1e-13)
+    assert not r["o_s"].any()
+    np.testing.assert_allclose(r["out"], ref @ W, rtol=1e-10, atol=1e-12)
+
+
+def test_linear_bruteforce_marginal_keys(rng):
+    N, D, bq, bk = 100, 8, 16, 8
+    Q = rng.standard_normal((N, D))
+    K = rng.standard_normal((N, D)) * 2
+    V = rng.standard_normal((N, D))
+    nqb, nkb = orc.n_blocks(N, bq), orc.n_blocks(N, bk)
+    idx = np.stack([np.sort(rng.choice(nkb, 4, replace=False)) for _ in range(nqb)])
+    H, Z = orc.linear_states(K, V, bk)
+    out = orc.linear_branch(Q, H, Z, idx, bq)
+    f = lambda x: x + 1 if x > 0 else math.exp(x)
+    for i in range(N):
+        crit = set(int(J) for J in idx[i // bq])
+        num = np.zeros(D)
+        den = 0.0
+        for j in range(N):
+            if j // bk in crit:
+                continue
+            w = sum(f(Q[i, c]) * f(K[j, c]) for c in range(D))
+            num += w * V[j]
+            den += w
+        np.testing.assert_allclose(out[i], num / den, rtol=1e-10, atol=1e-12)
+        # convex combination of the remaining value rows
+        marg = [j for j in range(N) if j // bk not in crit]
+        assert np.all(out[i] <= V[marg].max(axis=0) + 1e-12) and np.all(out[i] >= V[marg].min(axis=0) - 1e-12)
+
+
+def test_linear_zero_when_all_critical():
+    wl = SMALL[2]
+    Q, K, V, W = head(wl)
+    r = orc.forward_head(Q, K, V, W, wl.blk_q, wl.blk_k, wl.n_kb)
+    assert not r["o_l"].any()
+
+
+def test_phi_matches_library(rng):
+    x = rng.standard_normal(1000) * 4
+    np.testing.assert_allclose(orc.phi(x), _phi_lib(x), rtol=1e-11, atol=0)  # torch uses expm1(x)+1
+
+
+# ---------------------------------------------------------------------------------------------------------
+# combine
+# ---------------------------------------------------------------------------------------------------------
+def test_combine_special_cases():
+    wl = SMALL[1]
+    Q, K, V, W = head(wl)
+    r = orc.forward_head(Q, K, V, np.zeros_like(W), wl.blk_q, wl.blk_k, 4)
+    assert np.array_equal(r["out"], r["o_s"])
+    r = orc.forward_head(Q, K, np.zeros_like(V), W, wl.blk_q, wl.blk_k, 4)
+    assert not r["out"].any()
+    r = orc.forward_head(Q, K, V, np.eye(wl.D), wl.blk_q, wl.blk_k, 4)
+    np.testing.assert_allclose(r["out"], r["o_s"] + r["o_l"], atol=1e-15, rtol=0)

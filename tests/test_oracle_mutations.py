@@ -91,6 +91,7 @@ MUTATIONS = {
     "sparse_no_scale": ("sparse_attention", _sparse_no_scale),
     "sparse_drop_ragged_tail": ("sparse_attention", _sparse_drop_ragged_tail),
     "project_transposed": ("project", _project_transposed),
+    "pool_sum": ("pool", _pool_sum),
 }
 
 
@@ -105,6 +106,7 @@ def _run_pins():
         lambda: pins.test_golden_quant_fixture(),
         lambda: pins.test_select_bruteforce(rng()),
         lambda: pins.test_select_constant_keys_and_full(),
+        lambda: pins.test_block_score_is_mean_token_score(),
         lambda: pins.test_sparse_bruteforce(rng()),
         lambda: pins.test_linear_closed_form_all_marginal(pins.SMALL[0]),
         lambda: pins.test_linear_bruteforce_marginal_keys(rng()),

@@ -173,6 +173,20 @@ def test_select_constant_keys_and_full():
     assert np.array_equal(r["idx"], np.tile(np.arange(wl.n_kb), (wl.n_qb, 1)))
 
 
+def test_block_score_is_mean_token_score():
+    # by linearity, qbar_I . kbar_J equals the average over the valid keys j of block J (and the valid queries
+    # i of block I) of q_i . k'_j -- including the ragged last blocks
+    wl = SMALL[1]
+    Q, K, V, W = head(wl)
+    r = orc.forward_head(Q, K, V, W, wl.blk_q, wl.blk_k, 2, linear=False)
+    Kp = K - r["mu"][None, :]
+    tok = Q @ Kp.T / math.sqrt(wl.D)
+    for I in (0, wl.n_qb - 1):
+        for J in (0, 3, wl.n_kb - 1):
+            ref = tok[I * wl.blk_q:(I + 1) * wl.blk_q, J * wl.blk_k:(J + 1) * wl.blk_k].mean()
+            assert abs(r["scores"][I, J] - ref) < 1e-5
+
+
 def test_topk_count():
     assert [orc.topk_count(w.topk_frac, w.n_kb) for w in synth.WORKLOADS.values()] == [4, 512, 51, 118, 210]
     assert orc.topk_count(0.001, 10) == 1

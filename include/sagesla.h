@@ -1,0 +1,118 @@
+/*
+ * sagesla.h — C ABI of the SageSLA attention forward for AMD Instinct MI355X (gfx950).
+ *
+ * SageSLA is the attention of TurboDiffusion's video DiT layers: per query block, the top-k most important
+ * key blocks are attended with INT8-quantized scores (SageAttention), and the remaining key blocks go to an
+ * elu+1 linear-attention branch whose output passes through a D×D projection (SLA).
+ * Sources:
+ *   [TD-news]  "Turbo Diffusion：秒级生成与高清保真的视频扩散技术突破" (lanhy.cn): §三(一) SageAttention2++ items 1–3
+ *              (smoothing, per-block quantization, low-bit attention) and §三(二) SLA items 1–3 (top-k selection,
+ *              linear branch with projection, select-then-INT8 hybrid);
+ *   [TD-guide] "TurboDiffusion技术指南：突破视频生成效率瓶颈的实践方案" (blog.gitcode.com): inference flags
+ *              --attention_type sagesla and --sla_topk (fraction of blocks kept).
+ *
+ * Conventions shared by every entry point
+ *  - Tensors are row-major [B][H][N][D] with D contiguous; q, k, v and out are bf16 (raw 16-bit patterns).
+ *  - Every data pointer is a device pointer owned by the caller. The library never allocates, frees or
+ *    synchronizes device memory; all scratch lives in the caller's workspace.
+ *  - Calls are asynchronous on `stream` (a hipStream_t passed as void*; NULL is the null stream). Outputs are
+ *    ready when the stream reaches that point.
+ *  - Parameters are validated on the host before any launch; on an error nothing is launched and the status
+ *    says why. Exceptions never cross the ABI.
+ *  - Two calls that share a workspace or output buffers must not run concurrently.
+ *  - Results are deterministic: no floating-point atomics; every reduction has a fixed order.
+ *  - Inputs must be finite.
+ */
+#ifndef SAGESLA_H
+#define SAGESLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SAGESLA_OK = 0,
+  SAGESLA_E_NULL = 1,        /* a required pointer is NULL                                              */
+  SAGESLA_E_SHAPE = 2,       /* B, H or N < 1, B*H > 65535, topk outside [0, n_kb], sm_scale < 0 or NaN   */
+  SAGESLA_E_UNSUPPORTED = 3, /* D != 128, blk_k != 64, blk_q not in {64, 128}, unknown flag bits,
+                                N > 2^24, n_kb > 20480, or (linear branch) n_kb > 10174                   */
+  SAGESLA_E_WORKSPACE = 4,   /* workspace smaller than sagesla_workspace_bytes()                         */
+  SAGESLA_E_ALIGN = 5,       /* a pointer is not 16-byte aligned (workspace: 256-byte aligned)           */
+  SAGESLA_E_HIP = 6          /* a HIP call or launch failed; sagesla_last_hip_error() holds its code     */
+} sagesla_status;
+
+/* flags */
+#define SAGESLA_LINEAR 0x1u         /* run the linear branch on the non-selected blocks (needs w_proj)      */
+#define SAGESLA_SMOOTH_K 0x2u       /* subtract the per-channel mean of K over all N tokens before quantizing */
+#define SAGESLA_USE_GIVEN_MASK 0x4u /* sagesla_forward reads block_idx instead of selecting (block_idx required) */
+
+typedef struct sagesla_params {
+  int32_t B, H, N, D;   /* batch, heads, tokens, head dim (D == 128)                                       */
+  int32_t blk_q, blk_k; /* query block 64 or 128; key block 64                                             */
+  int32_t topk;         /* key blocks kept per query block, 0..n_kb (n_kb = ceil(N / blk_k))               */
+  uint32_t flags;       /* SAGESLA_* bits                                                                  */
+  float sm_scale;       /* softmax scale on the dequantized scores; 0 means 1/sqrt(D)                      */
+  const void* w_proj;   /* bf16 [D][D] row-major projection of the linear branch: out_row += o_l_row · W_p  */
+  void* workspace;      /* device scratch of workspace_bytes bytes, 256-byte aligned                        */
+  size_t workspace_bytes;
+  /* Optional intermediates (device, caller-owned). NULL keeps an intermediate inside the workspace; a
+     non-NULL pointer makes the library write it there (and read it back from there in later stages).     */
+  int8_t* q_i8;       /* [B][H][N][D]      INT8 codes of Q                                                */
+  float* q_scale;     /* [B][H][n_qb]      per query block: fp32(absmax/127), 0 for an all-zero block      */
+  int8_t* k_i8;       /* [B][H][N][D]      INT8 codes of the smoothed K                                   */
+  float* k_scale;     /* [B][H][n_kb]                                                                      */
+  float* k_mean;      /* [B][H][D]         fp32(sum_t K[t][c] / N), zeros without SAGESLA_SMOOTH_K         */
+  double* q_pool;     /* [B][H][n_qb][D]   mean of the raw Q rows of each query block                     */
+  double* k_pool;     /* [B][H][n_kb][D]   mean of the smoothed K rows of each key block                  */
+  int32_t* block_idx; /* [B][H][n_qb][topk] selected key blocks, ascending (input with USE_GIVEN_MASK)     */
+  float* o_lin;       /* [B][H][N][D]      linear-branch output after the projection (fp32)               */
+} sagesla_params;
+
+/* Bytes of workspace the three entry points need for these parameters (all intermediates kept inside).
+   Only sizes, block shapes and flags are read (pointers may be NULL). Returns 0 when those are invalid.
+   Host only; no device access. */
+size_t sagesla_workspace_bytes(const sagesla_params* p);
+
+/* Host-side validation of a parameter block (sizes, flags, w_proj presence and the alignment of every pointer
+   it carries; not the tensors passed separately): SAGESLA_OK or the first error found. */
+sagesla_status sagesla_validate(const sagesla_params* p);
+
+/* Quantize stage ([TD-news] §三(一) items 1–2).
+   Reads q, k (bf16 [B][H][N][D]). With SAGESLA_SMOOTH_K, k_mean = fp32(exact column sum / N) per (b, h) and
+   K is smoothed to k' = fp32(K - k_mean); otherwise k' = K. Per block of blk_q query rows (blk_k key rows) × D
+   channels, the last block holding only the remaining rows: scale = fp32(absmax/127) and
+   code = clamp(round-half-even(fp32(x / scale)), -127, 127) for Q and for k'. Also writes q_pool/k_pool, the
+   block means of raw Q and of k' (fp64). Codes, scales and k_mean are bit-exact functions of the inputs. */
+sagesla_status sagesla_quantize(const void* q, const void* k, const sagesla_params* p, void* stream);
+
+/* Select stage ([TD-news] §三(二) item 1; [TD-guide] --sla_topk).
+   Needs the pooled means written by sagesla_quantize with the same params and workspace. For every query
+   block I, ranks key blocks J by the fp64 score q_pool[I] · k_pool[J] (the /sqrt(D) does not change the
+   order), keeps the topk best with exact ties going to the lower J, and writes them ascending to block_idx. */
+sagesla_status sagesla_select(const sagesla_params* p, void* stream);
+
+/* Whole forward ([TD-news] §三(二) item 3: select first, then INT8 attention on the selected blocks, linear
+   attention on the rest). Runs quantize, select (or reads block_idx with SAGESLA_USE_GIVEN_MASK; indices are
+   clamped to [0, n_kb)), the linear branch (SAGESLA_LINEAR) and the sparse attention, and writes
+   out = bf16_rne(O_s + O_lin):
+     O_s[i]  = softmax over the selected keys j of z_ij = (codeQ_i · codeK_j) · scale_q(I) · scale_k(J) · sm_scale,
+               applied to the bf16 value rows (0 when topk == 0);
+     O_lin   = O_l · W_p, O_l[i] = phi(q_i) H_m / (phi(q_i) · Z_m), phi = elu + 1 on the raw bf16 q and k,
+               H_m / Z_m = the sum over all key blocks of phi(K_J)^T V_J / sum phi(K_J) minus the same sums over
+               the selected blocks (0 when every key block is selected). */
+sagesla_status sagesla_forward(const void* q, const void* k, const void* v, void* out, const sagesla_params* p,
+                               void* stream);
+
+/* Text of a status code (static storage). */
+const char* sagesla_status_str(sagesla_status s);
+
+/* hipError_t of the most recent SAGESLA_E_HIP in the calling thread (0 if none). */
+int sagesla_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SAGESLA_H */

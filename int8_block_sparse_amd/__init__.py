@@ -1,0 +1,250 @@
+"""SageSLA attention forward for AMD Instinct MI355X (gfx950): thin Python binding of libsagesla.so.
+
+Every step of the forward runs in the library's HIP kernels; this module only marshals arguments through the
+C ABI declared in include/sagesla.h. PyTorch provides device memory and the current stream. There is no CPU
+fallback: calls fail loudly if the library is missing or no GPU is present.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+__all__ = [
+    "LIB_PATH", "load", "Params", "SageSLAError", "topk_blocks", "n_blocks", "workspace_bytes", "validate",
+    "quantize", "select", "forward", "LINEAR", "SMOOTH_K", "USE_GIVEN_MASK", "STATUS",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsagesla.so")
+
+LINEAR = 0x1
+SMOOTH_K = 0x2
+USE_GIVEN_MASK = 0x4
+
+STATUS = {0: "OK", 1: "E_NULL", 2: "E_SHAPE", 3: "E_UNSUPPORTED", 4: "E_WORKSPACE", 5: "E_ALIGN", 6: "E_HIP"}
+
+
+class SageSLAError(RuntimeError):
+    def __init__(self, status: int, where: str, hip_error: int = 0):
+        self.status = status
+        msg = f"{where}: {STATUS.get(status, status)} ({_lib_status_str(status)})"
+        if status == 6:
+            msg += f", hipError {hip_error}"
+        super().__init__(msg)
+
+
+class Params(ctypes.Structure):
+    """Mirror of struct sagesla_params."""
+    _fields_ = [
+        ("B", ctypes.c_int32), ("H", ctypes.c_int32), ("N", ctypes.c_int32), ("D", ctypes.c_int32),
+        ("blk_q", ctypes.c_int32), ("blk_k", ctypes.c_int32), ("topk", ctypes.c_int32),
+        ("flags", ctypes.c_uint32), ("sm_scale", ctypes.c_float),
+        ("w_proj", ctypes.c_void_p), ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+        ("q_i8", ctypes.c_void_p), ("q_scale", ctypes.c_void_p), ("k_i8", ctypes.c_void_p),
+        ("k_scale", ctypes.c_void_p), ("k_mean", ctypes.c_void_p), ("q_pool", ctypes.c_void_p),
+        ("k_pool", ctypes.c_void_p), ("block_idx", ctypes.c_void_p), ("o_lin", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def load():
+    """Load libsagesla.so (built by __graft_entry__.build() / python -m int8_block_sparse_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m int8_block_sparse_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER(Params)
+    vp = ctypes.c_void_p
+    lib.sagesla_workspace_bytes.argtypes = [P]
+    lib.sagesla_workspace_bytes.restype = ctypes.c_size_t
+    lib.sagesla_validate.argtypes = [P]
+    lib.sagesla_validate.restype = ctypes.c_int
+    lib.sagesla_quantize.argtypes = [vp, vp, P, vp]
+    lib.sagesla_quantize.restype = ctypes.c_int
+    lib.sagesla_select.argtypes = [P, vp]
+    lib.sagesla_select.restype = ctypes.c_int
+    lib.sagesla_forward.argtypes = [vp, vp, vp, vp, P, vp]
+    lib.sagesla_forward.restype = ctypes.c_int
+    lib.sagesla_status_str.argtypes = [ctypes.c_int]
+    lib.sagesla_status_str.restype = ctypes.c_char_p
+    lib.sagesla_last_hip_error.argtypes = []
+    lib.sagesla_last_hip_error.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _lib_status_str(status: int) -> str:
+    try:
+        return load().sagesla_status_str(status).decode()
+    except Exception:  # noqa: BLE001 - message helper only
+        return "?"
+
+
+def n_blocks(n: int, blk: int) -> int:
+    return -(-n // blk)
+
+
+def topk_blocks(frac: float, n_kb: int) -> int:
+    """Key blocks kept per query block for the --sla_topk fraction: round half up, at least 1, all for frac >= 1."""
+    if frac >= 1.0:
+        return n_kb
+    return max(1, int(math.floor(frac * n_kb + 0.5)))
+
+
+@dataclass
+class Config:
+    B: int
+    H: int
+    N: int
+    D: int = 128
+    blk_q: int = 128
+    blk_k: int = 64
+    topk: int = 0
+    linear: bool = True
+    smooth_k: bool = True
+    sm_scale: float = 0.0
+
+    @property
+    def n_qb(self) -> int:
+        return n_blocks(self.N, self.blk_q)
+
+    @property
+    def n_kb(self) -> int:
+        return n_blocks(self.N, self.blk_k)
+
+    def params(self, **ptrs) -> Params:
+        flags = (LINEAR if self.linear else 0) | (SMOOTH_K if self.smooth_k else 0)
+        if ptrs.pop("given_mask", False):
+            flags |= USE_GIVEN_MASK
+        p = Params(B=self.B, H=self.H, N=self.N, D=self.D, blk_q=self.blk_q, blk_k=self.blk_k, topk=self.topk,
+                   flags=flags, sm_scale=self.sm_scale)
+        for k, v in ptrs.items():
+            setattr(p, k, v)
+        return p
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device):
+    import torch
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise SageSLAError(status, where, load().sagesla_last_hip_error())
+
+
+def validate(cfg: Config) -> int:
+    return load().sagesla_validate(ctypes.byref(cfg.params()))
+
+
+def workspace_bytes(cfg: Config) -> int:
+    n = load().sagesla_workspace_bytes(ctypes.byref(cfg.params()))
+    if n == 0:
+        _check(validate(cfg) or 2, "sagesla_workspace_bytes")
+    return n
+
+
+def _workspace(cfg: Config, device, workspace):
+    import torch
+    need = workspace_bytes(cfg)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+    return workspace
+
+
+def _shape_check(q, k, v, out, cfg: Config):
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        if t is None:
+            continue
+        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous bf16 CUDA tensor")
+        if tuple(t.shape) != (cfg.B, cfg.H, cfg.N, cfg.D):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {(cfg.B, cfg.H, cfg.N, cfg.D)}")
+
+
+def _exports(cfg: Config, device):
+    import torch
+    BH, N, D = cfg.B * cfg.H, cfg.N, cfg.D
+    f = dict(device=device)
+    ex = {
+        "q_i8": torch.empty(cfg.B, cfg.H, N, D, dtype=torch.int8, **f),
+        "q_scale": torch.empty(cfg.B, cfg.H, cfg.n_qb, dtype=torch.float32, **f),
+        "k_i8": torch.empty(cfg.B, cfg.H, N, D, dtype=torch.int8, **f),
+        "k_scale": torch.empty(cfg.B, cfg.H, cfg.n_kb, dtype=torch.float32, **f),
+        "k_mean": torch.empty(cfg.B, cfg.H, D, dtype=torch.float32, **f),
+        "q_pool": torch.empty(cfg.B, cfg.H, cfg.n_qb, D, dtype=torch.float64, **f),
+        "k_pool": torch.empty(cfg.B, cfg.H, cfg.n_kb, D, dtype=torch.float64, **f),
+        "block_idx": torch.empty(cfg.B, cfg.H, cfg.n_qb, max(cfg.topk, 1), dtype=torch.int32, **f),
+    }
+    if cfg.linear:
+        ex["o_lin"] = torch.empty(cfg.B, cfg.H, N, D, dtype=torch.float32, **f)
+    del BH
+    return ex
+
+
+def forward(q, k, v, w_proj=None, *, topk: int, blk_q: int = 128, blk_k: int = 64, linear: bool = True,
+            smooth_k: bool = True, sm_scale: float = 0.0, mask=None, out=None, workspace=None,
+            export: bool = False):
+    """SageSLA forward. q, k, v: bf16 [B, H, N, 128] CUDA tensors; w_proj: bf16 [128, 128] (needed with linear).
+
+    mask: optional int32 [B, H, n_qb, topk] ascending block lists used instead of the selection.
+    export=True also returns a dict of every intermediate (codes, scales, K mean, pooled means, block lists,
+    and the linear-branch output). Runs asynchronously on the current stream."""
+    B, H, N, D = q.shape
+    cfg = Config(B, H, N, D, blk_q, blk_k, topk, linear, smooth_k, sm_scale)
+    if out is None:
+        import torch
+        out = torch.empty_like(q)
+    _shape_check(q, k, v, out, cfg)
+    ws = _workspace(cfg, q.device, workspace)
+    ex = _exports(cfg, q.device) if export else {}
+    if mask is not None:
+        if not export:
+            ex = {}
+        ex["block_idx"] = mask
+    ptrs = {name: _ptr(t) for name, t in ex.items()}
+    p = cfg.params(w_proj=_ptr(w_proj), workspace=ws.data_ptr(), workspace_bytes=ws.numel(),
+                   given_mask=mask is not None, **ptrs)
+    _check(load().sagesla_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), ctypes.byref(p),
+                                  _stream(q.device)), "sagesla_forward")
+    return (out, ex) if export else out
+
+
+def quantize(q, k, *, blk_q: int = 128, blk_k: int = 64, smooth_k: bool = True, workspace=None):
+    """Quantize stage alone: returns dict(q_i8, q_scale, k_i8, k_scale, k_mean, q_pool, k_pool) and the workspace
+    (pass it to select())."""
+    B, H, N, D = q.shape
+    cfg = Config(B, H, N, D, blk_q, blk_k, 0, False, smooth_k)
+    _shape_check(q, k, None, None, cfg)
+    ws = _workspace(cfg, q.device, workspace)
+    ex = _exports(cfg, q.device)
+    ex.pop("block_idx")
+    p = cfg.params(workspace=ws.data_ptr(), workspace_bytes=ws.numel(), **{n: _ptr(t) for n, t in ex.items()})
+    _check(load().sagesla_quantize(q.data_ptr(), k.data_ptr(), ctypes.byref(p), _stream(q.device)),
+           "sagesla_quantize")
+    return ex, ws
+
+
+def select(q_pool, k_pool, *, N: int, topk: int, blk_q: int = 128, blk_k: int = 64, workspace=None):
+    """Select stage alone from pooled means (fp64 [B, H, n_blocks, 128]); returns int32 [B, H, n_qb, topk]."""
+    import torch
+    B, H = q_pool.shape[:2]
+    cfg = Config(B, H, N, q_pool.shape[-1], blk_q, blk_k, topk, False, True)
+    ws = _workspace(cfg, q_pool.device, workspace)
+    idx = torch.empty(B, H, cfg.n_qb, max(topk, 1), dtype=torch.int32, device=q_pool.device)
+    qp, kp = q_pool.contiguous(), k_pool.contiguous()
+    p = cfg.params(workspace=ws.data_ptr(), workspace_bytes=ws.numel(), q_pool=qp.data_ptr(),
+                   k_pool=kp.data_ptr(), block_idx=idx.data_ptr())
+    _check(load().sagesla_select(ctypes.byref(p), _stream(q_pool.device)), "sagesla_select")
+    return idx[..., :topk]

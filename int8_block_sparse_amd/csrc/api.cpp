@@ -1,0 +1,225 @@
+// C ABI of the SageSLA forward: host-side validation, workspace plan and launch order.
+// The entry points and their contracts are declared in include/sagesla.h.
+#include <math.h>
+#include <string.h>
+
+#include "internal.h"
+#include "sagesla.h"
+
+using namespace sagesla;
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr size_t kAlign = 256;
+constexpr int kColsumChunk = 512;
+constexpr int kMaxKeyBlocks = 20480;
+constexpr int kMaxN = 1 << 24;
+constexpr size_t kMaxLds = 160 * 1024;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int state_tile_width(int n_kb) {
+  for (int xw = 64; xw >= 4; xw >>= 1)
+    if (gather_lds_bytes(n_kb, xw) <= kMaxLds) return xw;
+  return 0;
+}
+
+bool misaligned(const void* ptr, size_t a) { return ptr && ((uintptr_t)ptr % a) != 0; }
+
+// sizes, block shapes and flags only
+sagesla_status check_shape(const sagesla_params* p) {
+  if (!p) return SAGESLA_E_NULL;
+  if (p->D != kD || p->blk_k != kBlkK || (p->blk_q != 64 && p->blk_q != 128)) return SAGESLA_E_UNSUPPORTED;
+  if (p->flags & ~(uint32_t)(SAGESLA_LINEAR | SAGESLA_SMOOTH_K | SAGESLA_USE_GIVEN_MASK)) return SAGESLA_E_UNSUPPORTED;
+  if (p->B < 1 || p->H < 1 || p->N < 1) return SAGESLA_E_SHAPE;
+  if ((int64_t)p->B * p->H > 65535) return SAGESLA_E_SHAPE;
+  if (p->N > kMaxN) return SAGESLA_E_UNSUPPORTED;
+  const int n_kb = (p->N + kBlkK - 1) / kBlkK;
+  if (n_kb > kMaxKeyBlocks) return SAGESLA_E_UNSUPPORTED;
+  if (p->topk < 0 || p->topk > n_kb) return SAGESLA_E_SHAPE;
+  if (!(isfinite(p->sm_scale) && p->sm_scale >= 0.f)) return SAGESLA_E_SHAPE;
+  const bool linear = (p->flags & SAGESLA_LINEAR) && p->topk < n_kb;
+  if (linear && state_tile_width(n_kb) == 0) return SAGESLA_E_UNSUPPORTED;
+  return SAGESLA_OK;
+}
+
+// the whole parameter block: shape plus the pointers it carries
+sagesla_status check_params(const sagesla_params* p) {
+  const sagesla_status st = check_shape(p);
+  if (st != SAGESLA_OK) return st;
+  if ((p->flags & SAGESLA_LINEAR) && !p->w_proj) return SAGESLA_E_NULL;
+  if (misaligned(p->w_proj, 16) || misaligned(p->q_i8, 16) || misaligned(p->k_i8, 16) ||
+      misaligned(p->q_scale, 16) || misaligned(p->k_scale, 16) || misaligned(p->k_mean, 16) ||
+      misaligned(p->q_pool, 16) || misaligned(p->k_pool, 16) || misaligned(p->block_idx, 16) ||
+      misaligned(p->o_lin, 16))
+    return SAGESLA_E_ALIGN;
+  return SAGESLA_OK;
+}
+
+// Sizes and placement of every intermediate. With ws == nullptr only the sizes are computed.
+void make_plan(const sagesla_params* p, unsigned char* ws, Plan* pl) {
+  memset(pl, 0, sizeof(*pl));
+  pl->B = p->B;
+  pl->H = p->H;
+  pl->BH = p->B * p->H;
+  pl->N = p->N;
+  pl->blk_q = p->blk_q;
+  pl->n_qb = (p->N + p->blk_q - 1) / p->blk_q;
+  pl->n_kb = (p->N + kBlkK - 1) / kBlkK;
+  pl->topk = p->topk;
+  pl->smooth = (p->flags & SAGESLA_SMOOTH_K) != 0;
+  pl->linear = (p->flags & SAGESLA_LINEAR) != 0;
+  pl->given_mask = (p->flags & SAGESLA_USE_GIVEN_MASK) != 0;
+  pl->sm_scale = p->sm_scale > 0.f ? p->sm_scale : 1.f / sqrtf((float)p->D);
+  pl->colsum_chunk = kColsumChunk;
+  pl->n_colsum_chunks = (p->N + kColsumChunk - 1) / kColsumChunk;
+  pl->w_proj = p->w_proj;
+  const bool lin_active = pl->linear && pl->topk < pl->n_kb;
+  if (lin_active) {
+    pl->state_xw = state_tile_width(pl->n_kb);
+    pl->n_state_xt = (kStateX + pl->state_xw - 1) / pl->state_xw;
+  }
+  const size_t BH = pl->BH, N = pl->N, D = kD, nqb = pl->n_qb, nkb = pl->n_kb;
+  size_t off = 0;
+  auto take = [&](size_t bytes) -> unsigned char* {
+    unsigned char* r = ws ? ws + off : nullptr;
+    off += align_up(bytes);
+    return r;
+  };
+  pl->colsum_part = (double*)take(BH * pl->n_colsum_chunks * D * sizeof(double));
+  pl->k_mean = (float*)take(BH * D * sizeof(float));
+  pl->q_i8 = (int8_t*)take(BH * N * D);
+  pl->k_i8 = (int8_t*)take(BH * N * D);
+  pl->q_scale = (float*)take(BH * nqb * sizeof(float));
+  pl->k_scale = (float*)take(BH * nkb * sizeof(float));
+  pl->q_pool = (double*)take(BH * nqb * D * sizeof(double));
+  pl->k_pool = (double*)take(BH * nkb * D * sizeof(double));
+  pl->scores = (double*)take(BH * nqb * nkb * sizeof(double));
+  pl->block_idx = (int32_t*)take(BH * nqb * (size_t)pl->topk * sizeof(int32_t));
+  if (lin_active) {
+    pl->wpt = (uint16_t*)take(D * D * sizeof(uint16_t));
+    pl->state = (float*)take(BH * pl->n_state_xt * nkb * pl->state_xw * sizeof(float));
+    pl->state_m = (float*)take(BH * nqb * kStateX * sizeof(float));
+    pl->o_lin = (float*)take(BH * N * D * sizeof(float));
+  }
+  pl->ws_bytes = off;
+  // caller-owned exports replace their workspace slice
+  if (p->k_mean) pl->k_mean = p->k_mean;
+  if (p->q_i8) pl->q_i8 = p->q_i8;
+  if (p->k_i8) pl->k_i8 = p->k_i8;
+  if (p->q_scale) pl->q_scale = p->q_scale;
+  if (p->k_scale) pl->k_scale = p->k_scale;
+  if (p->q_pool) pl->q_pool = p->q_pool;
+  if (p->k_pool) pl->k_pool = p->k_pool;
+  if (p->block_idx) pl->block_idx = p->block_idx;
+  if (p->o_lin && lin_active) pl->o_lin = p->o_lin;
+}
+
+sagesla_status check_workspace(const sagesla_params* p, const Plan& pl) {
+  if (p->workspace_bytes < pl.ws_bytes) return SAGESLA_E_WORKSPACE;
+  if (!p->workspace) return SAGESLA_E_WORKSPACE;
+  if (misaligned(p->workspace, kAlign)) return SAGESLA_E_ALIGN;
+  return SAGESLA_OK;
+}
+
+sagesla_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return SAGESLA_OK;
+  g_last_hip_error = (int)e;
+  return SAGESLA_E_HIP;
+}
+
+#define SAGESLA_TRY(expr)                         \
+  do {                                            \
+    sagesla_status st_ = hip_status(expr);        \
+    if (st_ != SAGESLA_OK) return st_;            \
+  } while (0)
+
+sagesla_status run_quantize(const Plan& pl, const void* q, const void* k, hipStream_t s) {
+  SAGESLA_TRY(launch_kmean(pl, (const uint16_t*)k, s));
+  SAGESLA_TRY(launch_quant(pl, (const uint16_t*)q, (const uint16_t*)k, s));
+  return SAGESLA_OK;
+}
+
+sagesla_status run_select(const Plan& pl, hipStream_t s) {
+  if (pl.topk > 0 && pl.topk < pl.n_kb) SAGESLA_TRY(launch_scores(pl, s));
+  if (pl.topk > 0) SAGESLA_TRY(launch_topk(pl, s));
+  return SAGESLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+sagesla_status sagesla_validate(const sagesla_params* p) { return check_params(p); }
+
+size_t sagesla_workspace_bytes(const sagesla_params* p) {
+  if (check_shape(p) != SAGESLA_OK) return 0;
+  Plan pl;
+  make_plan(p, nullptr, &pl);
+  return pl.ws_bytes;
+}
+
+sagesla_status sagesla_quantize(const void* q, const void* k, const sagesla_params* p, void* stream) {
+  sagesla_status st = check_params(p);
+  if (st != SAGESLA_OK) return st;
+  if (!q || !k) return SAGESLA_E_NULL;
+  if (misaligned(q, 16) || misaligned(k, 16)) return SAGESLA_E_ALIGN;
+  Plan pl;
+  make_plan(p, nullptr, &pl);
+  if ((st = check_workspace(p, pl)) != SAGESLA_OK) return st;
+  make_plan(p, (unsigned char*)p->workspace, &pl);
+  return run_quantize(pl, q, k, (hipStream_t)stream);
+}
+
+sagesla_status sagesla_select(const sagesla_params* p, void* stream) {
+  sagesla_status st = check_params(p);
+  if (st != SAGESLA_OK) return st;
+  Plan pl;
+  make_plan(p, nullptr, &pl);
+  if ((st = check_workspace(p, pl)) != SAGESLA_OK) return st;
+  make_plan(p, (unsigned char*)p->workspace, &pl);
+  return run_select(pl, (hipStream_t)stream);
+}
+
+sagesla_status sagesla_forward(const void* q, const void* k, const void* v, void* out, const sagesla_params* p,
+                               void* stream) {
+  sagesla_status st = check_params(p);
+  if (st != SAGESLA_OK) return st;
+  if (!q || !k || !v || !out) return SAGESLA_E_NULL;
+  if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(out, 16)) return SAGESLA_E_ALIGN;
+  if ((p->flags & SAGESLA_USE_GIVEN_MASK) && p->topk > 0 && !p->block_idx) return SAGESLA_E_NULL;
+  Plan pl;
+  make_plan(p, nullptr, &pl);
+  if ((st = check_workspace(p, pl)) != SAGESLA_OK) return st;
+  make_plan(p, (unsigned char*)p->workspace, &pl);
+  const hipStream_t s = (hipStream_t)stream;
+  if ((st = run_quantize(pl, q, k, s)) != SAGESLA_OK) return st;
+  if (!pl.given_mask && (st = run_select(pl, s)) != SAGESLA_OK) return st;
+  const bool lin_active = pl.linear && pl.topk < pl.n_kb;
+  if (lin_active) {
+    SAGESLA_TRY(launch_linear(pl, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, s));
+  } else if (p->o_lin) {
+    SAGESLA_TRY(launch_fill_f32(p->o_lin, (size_t)pl.BH * pl.N * kD, 0.f, s));
+  }
+  SAGESLA_TRY(launch_attn(pl, (const uint16_t*)v, (uint16_t*)out, s));
+  return SAGESLA_OK;
+}
+
+const char* sagesla_status_str(sagesla_status s) {
+  switch (s) {
+    case SAGESLA_OK: return "ok";
+    case SAGESLA_E_NULL: return "a required pointer is NULL";
+    case SAGESLA_E_SHAPE: return "invalid shape or parameter value";
+    case SAGESLA_E_UNSUPPORTED: return "unsupported configuration";
+    case SAGESLA_E_WORKSPACE: return "workspace missing or too small";
+    case SAGESLA_E_ALIGN: return "misaligned pointer";
+    case SAGESLA_E_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+int sagesla_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

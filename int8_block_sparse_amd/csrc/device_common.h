@@ -1,0 +1,62 @@
+// Small device helpers for the gfx950 kernels (wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sagesla {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+// bf16 bit pattern -> fp32 (exact)
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  v2f x = {a, b};
+  v2bf y = __builtin_convertvector(x, v2bf);
+  return __builtin_bit_cast(uint32_t, y);
+}
+
+// fp32 -> (hi, lo) bf16 split: hi = bf16(x), lo = bf16(x - hi); hi + lo carries ~16 significant bits
+__device__ __forceinline__ void split_bf16(float x, float& hi, float& lo) {
+  uint32_t h = pack_bf16x2(x, 0.f) & 0xffffu;
+  hi = __uint_as_float(h << 16);
+  lo = x - hi;
+}
+
+__device__ __forceinline__ float wave_max_f32(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+// value of lane (l ^ 32): swap the two 32-lane halves of the wave
+__device__ __forceinline__ int swap_halves_i32(int v) {
+  auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return r[0];
+}
+__device__ __forceinline__ float swap_halves_f32(float v) {
+  return __int_as_float(swap_halves_i32(__float_as_int(v)));
+}
+
+// XOR swizzle of the 16-byte chunk index inside a 128-byte LDS row, so that both 8 consecutive rows read at
+// one chunk and rows 8 apart written at one chunk land in different banks.
+__device__ __forceinline__ int swz8(int row) { return (row ^ (row >> 3)) & 7; }
+
+// Map a flat workgroup id to a work item so that each XCD (ids are dealt round-robin over 8 XCDs) gets one
+// contiguous range of work items: neighbouring query blocks of a head then share that XCD's L2.
+__device__ __forceinline__ int xcd_remap(int id, int total) {
+  const int q = total >> 3, r = total & 7;
+  const int x = id & 7, local = id >> 3;
+  return x * q + (x < r ? x : r) + local;
+}
+
+}  // namespace sagesla

@@ -1,0 +1,57 @@
+// Internal declarations shared by the SageSLA host orchestration and its gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sagesla {
+
+constexpr int kD = 128;       // head dim (the only one supported)
+constexpr int kBlkK = 64;     // key block
+constexpr int kStateX = kD * kD + kD;  // floats per linear-branch state: H^T W_p (D×D, e-major) then Z (D)
+
+// Everything a launch needs, resolved from the parameter block: sizes and where each intermediate lives
+// (a caller's export buffer or a slice of the workspace).
+struct Plan {
+  int B, H, BH, N, blk_q, n_qb, n_kb, topk;
+  bool smooth, linear, given_mask;
+  float sm_scale;
+  int colsum_chunk, n_colsum_chunks;
+  int state_xw, n_state_xt;     // linear-branch state gather: columns per tile, number of tiles
+  const void* w_proj;
+  // intermediates
+  double* colsum_part;  // [BH][n_colsum_chunks][D]
+  float* k_mean;        // [BH][D]
+  int8_t* q_i8;         // [BH][N][D]
+  int8_t* k_i8;
+  float* q_scale;       // [BH][n_qb]
+  float* k_scale;       // [BH][n_kb]
+  double* q_pool;       // [BH][n_qb][D]
+  double* k_pool;       // [BH][n_kb][D]
+  double* scores;       // [BH][n_qb][n_kb]
+  int32_t* block_idx;   // [BH][n_qb][topk]
+  uint16_t* wpt;        // [D][D] bf16: W_p^T in MFMA slot order
+  float* state;         // [BH][n_state_xt][n_kb][state_xw]
+  float* state_m;       // [BH][n_qb][kStateX]   remaining (non-selected) state per query block
+  float* o_lin;         // [BH][N][D]
+  size_t ws_bytes;
+};
+
+// K1: K-mean smoothing, per-block INT8 quantization and block mean pooling
+hipError_t launch_kmean(const Plan& p, const uint16_t* k, hipStream_t s);
+hipError_t launch_quant(const Plan& p, const uint16_t* q, const uint16_t* k, hipStream_t s);
+// K2: pooled block scores and top-k selection
+hipError_t launch_scores(const Plan& p, hipStream_t s);
+hipError_t launch_topk(const Plan& p, hipStream_t s);
+// K4: linear branch (block states, total-minus-selected gather, contraction with phi(Q))
+hipError_t launch_linear(const Plan& p, const uint16_t* q, const uint16_t* k, const uint16_t* v, hipStream_t s);
+// K3: block-sparse INT8 attention, epilogue adds the linear branch and writes bf16
+hipError_t launch_attn(const Plan& p, const uint16_t* v, uint16_t* out, hipStream_t s);
+// fills (graph-capture friendly replacements for memset)
+hipError_t launch_fill_f32(float* dst, size_t n, float val, hipStream_t s);
+// dynamic LDS of the kernels that size it at run time
+size_t topk_lds_bytes(int n_kb);
+size_t gather_lds_bytes(int n_kb, int xw);
+
+}  // namespace sagesla

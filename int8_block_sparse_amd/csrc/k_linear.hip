@@ -1,0 +1,324 @@
+// K4: the linear branch of SLA over the non-selected key blocks (gfx950).
+//
+// "Turbo Diffusion：秒级生成与高清保真的视频扩散技术突破" (lanhy.cn), §三(二) SLA item 2: the blocks that are not
+// selected are modelled with linear-complexity attention followed by a linear projection. With phi = elu + 1
+// on the raw bf16 q and k, per key block J the state is H_J = phi(K_J)^T V_J (D×D) and Z_J = sum phi(K_J) (D);
+// the totals over all blocks are formed once and each query block subtracts its selected blocks' states:
+//   O_l[i] = phi(q_i) H_m / (phi(q_i) . Z_m),  H_m = sum_J H_J - sum_{J selected} H_J,  out += O_l W_p.
+// Because the projection is linear and the denominator is a scalar per row, O_l W_p = phi(q_i) (H_m W_p) / den,
+// so the projection is applied to each block state once (k4_states) instead of to each output row.
+//
+// Kernels:
+//   k4_prep_wp   W_p^T with the MFMA key-slot order, bf16 (32 KB, once per call)
+//   k4_states    per key block: (H_J W_p)^T and Z_J into a column-tiled table (MFMA, HBM-bound)
+//   k4_gather    per (b,h) and column tile: the tile of all blocks' states sits in LDS; totals once, then for
+//                every query block H_m = total - sum over its selected blocks (LDS-bound)
+//   k4_out       per query block: O_lin = phi(Q) H_m / (phi(Q) . Z_m) (MFMA)
+// fp32 values enter the bf16 MFMAs as hi + lo bf16 pairs, so every product keeps ~16 significant bits.
+#include "device_common.h"
+#include "internal.h"
+
+namespace sagesla {
+
+// position of key/channel slot inside a 16-group such that the MFMA 32x32x16 lane (half g, slot i) reads
+// 8 consecutive positions: slot (g, i) <-> index 8*(i/4) + 4*g + (i%4); position 8*g + 4*(i/4) + (i%4).
+__device__ __forceinline__ int slot_pos16(int off) {  // off = index within the 16-group
+  return (off & 3) | ((off & 4) << 1) | ((off & 8) >> 1);
+}
+
+// W_p^T, positions permuted as above: wpt[f][p], p = slot_pos16 applied within each 16 of e.
+__global__ __launch_bounds__(256) void k4_prep_wp(const uint16_t* __restrict__ wp, uint16_t* __restrict__ wpt) {
+  const int i = blockIdx.x * 256 + threadIdx.x;  // 16384 elements
+  const int e = i >> 7, f = i & 127;             // wp[e][f]
+  const int p = (e & ~15) | slot_pos16(e & 15);
+  wpt[f * kD + p] = wp[i];
+}
+
+__device__ __forceinline__ float phi_f(float x) { return x > 0.f ? x + 1.f : expf(x); }
+
+// ---------------------------------------------------------------------------------------------------------
+// k4_states: grid (n_kb, BH), 256 threads (4 waves).
+// LDS holds phi(K)^T (hi, lo) and V^T as [channel][key] bf16 rows of 128 B, 16-byte chunks XOR-swizzled.
+// Wave w computes H^T[e][c] for all e and c in [32w, 32w+32) (A = V^T, B = phi(K)), then
+// (H W_p)^T[f][c] = sum_e W_p^T[f][e] H^T[e][c] with H^T taken straight from its accumulator registers.
+// ---------------------------------------------------------------------------------------------------------
+__device__ __forceinline__ int lds_off(int row, int key) {  // byte offset of (row, key) in a [128][64] bf16 tile
+  return row * 128 + (((key >> 3) ^ swz8(row)) << 4) + ((key & 7) << 1);
+}
+
+__global__ __launch_bounds__(256) void k4_states(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+                                                const uint16_t* __restrict__ wpt, float* __restrict__ table,
+                                                int N, int n_kb, int xw, int n_xt) {
+  __shared__ __attribute__((aligned(16))) unsigned char s_pkh[kD * 128];
+  __shared__ __attribute__((aligned(16))) unsigned char s_pkl[kD * 128];
+  __shared__ __attribute__((aligned(16))) unsigned char s_vt[kD * 128];
+  __shared__ float s_z[16][kD + 1];
+  const int J = blockIdx.x, bh = blockIdx.y;
+  const int t = threadIdx.x, w = t >> 6, l = t & 63, g = l >> 5, lr = l & 31;
+  const int cg = t & 15, kg = t >> 4;  // loader: channels 8cg..+7, keys 4kg..+3
+  const size_t base = ((size_t)bh * N + (size_t)J * kBlkK) * kD;
+  const int nv = min(kBlkK, N - J * kBlkK);
+
+  // ---- load, phi, split, transpose into LDS
+  float pk[4][8], vv[4][8];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const int r = 4 * kg + b;
+    uint4 a = make_uint4(0, 0, 0, 0), c = make_uint4(0, 0, 0, 0);
+    if (r < nv) {
+      a = *(const uint4*)(k + base + (size_t)r * kD + cg * 8);
+      c = *(const uint4*)(v + base + (size_t)r * kD + cg * 8);
+    }
+    const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, cw[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      pk[b][2 * u] = bf16_lo(aw[u]);
+      pk[b][2 * u + 1] = bf16_hi(aw[u]);
+      vv[b][2 * u] = bf16_lo(cw[u]);
+      vv[b][2 * u + 1] = bf16_hi(cw[u]);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pk[b][e] = (r < nv) ? phi_f(pk[b][e]) : 0.f;
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int row = cg * 8 + e;
+    float h[4], lo[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) split_bf16(pk[b][e], h[b], lo[b]);
+    const int off = lds_off(row, 4 * kg);
+    *(uint2*)(s_pkh + off) = make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
+    *(uint2*)(s_pkl + off) = make_uint2(pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]));
+    *(uint2*)(s_vt + off) = make_uint2(pack_bf16x2(vv[0][e], vv[1][e]), pack_bf16x2(vv[2][e], vv[3][e]));
+    s_z[kg][row] = (pk[0][e] + pk[1][e]) + (pk[2][e] + pk[3][e]);
+  }
+  __syncthreads();
+
+  // ---- H^T = V^T phi(K): m = e (4 tiles), n = c (tile w), k = key (4 steps of 16)
+  v16f acc[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) acc[mt] = (v16f){};
+  const int crow = 32 * w + lr;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int key = 16 * s + 8 * g;
+    const v8bf bh_ = *(const v8bf*)(s_pkh + lds_off(crow, key));
+    const v8bf bl_ = *(const v8bf*)(s_pkl + lds_off(crow, key));
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const v8bf a = *(const v8bf*)(s_vt + lds_off(32 * mt + lr, key));
+      acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bh_, acc[mt], 0, 0, 0);
+      acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bl_, acc[mt], 0, 0, 0);
+    }
+  }
+
+  // ---- (H W_p)^T = W_p^T H^T: m = f (4 tiles), n = c (tile w), k = e (8 steps of 16)
+  // B operand slot (g, i) of step s2 is e = 16 s2 + 8(i/4) + 4g + i%4 = accumulator register 8(s2%2)+i of
+  // tile s2/2 in this lane; the A operand reads W_p^T rows in the matching permuted order.
+  v16f acc2[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) acc2[mt] = (v16f){};
+#pragma unroll
+  for (int s2 = 0; s2 < 8; ++s2) {
+    const int src = s2 >> 1, r0 = 8 * (s2 & 1);
+    uint32_t hw[4], lw[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      float h0, l0, h1, l1;
+      split_bf16(acc[src][r0 + 2 * u], h0, l0);
+      split_bf16(acc[src][r0 + 2 * u + 1], h1, l1);
+      hw[u] = pack_bf16x2(h0, h1);
+      lw[u] = pack_bf16x2(l0, l1);
+    }
+    const v8bf bhi = __builtin_bit_cast(v8bf, make_uint4(hw[0], hw[1], hw[2], hw[3]));
+    const v8bf blo = __builtin_bit_cast(v8bf, make_uint4(lw[0], lw[1], lw[2], lw[3]));
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const int f = 32 * mt + lr;
+      const v8bf a = *(const v8bf*)(wpt + f * kD + 16 * s2 + 8 * g);
+      acc2[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bhi, acc2[mt], 0, 0, 0);
+      acc2[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, blo, acc2[mt], 0, 0, 0);
+    }
+  }
+
+  // ---- store: x = f*128 + c for (H W_p)^T[f][c]; x = 16384 + c for Z[c]
+  float* tb = table + (size_t)bh * n_xt * n_kb * xw;
+  const int c = 32 * w + lr;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int f = 32 * mt + 8 * (r >> 2) + 4 * g + (r & 3);
+      const int x = f * kD + c;
+      tb[((size_t)(x / xw) * n_kb + J) * xw + (x % xw)] = acc2[mt][r];
+    }
+  }
+  if (t < kD) {
+    float z = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) z += s_z[j][t];
+    const int x = kD * kD + t;
+    tb[((size_t)(x / xw) * n_kb + J) * xw + (x % xw)] = z;
+  }
+}
+
+// ---------------------------------------------------------------------------------------------------------
+// k4_gather: grid (n_xt, BH), 256 threads; dynamic LDS = n_kb * xw floats (+ partial sums).
+// Threads form 256/xw groups of xw columns. Totals: group g adds a fixed contiguous range of blocks, the
+// groups' partials are then added in group order. Gather: group g handles query blocks g, g + G, ...
+// ---------------------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k4_gather(const float* __restrict__ table, const int32_t* __restrict__ idx,
+                                                float* __restrict__ state_m, int n_qb, int n_kb, int topk, int xw,
+                                                int n_xt) {
+  extern __shared__ __attribute__((aligned(16))) float tile[];  // [n_kb][xw], then [G][xw] partials, [xw] totals
+  const int xt = blockIdx.x, bh = blockIdx.y;
+  const int t = threadIdx.x;
+  const int G = 256 / xw, grp = t / xw, xi = t % xw;
+  const float* src = table + ((size_t)bh * n_xt + xt) * n_kb * xw;
+  const int nflt = n_kb * xw;
+  for (int i = 4 * t; i < nflt; i += 4 * 256) *(float4*)(tile + i) = *(const float4*)(src + i);
+  float* part = tile + nflt;
+  float* tot = part + G * xw;
+  __syncthreads();
+  {
+    const int per = (n_kb + G - 1) / G;
+    const int j0 = grp * per, j1 = min(n_kb, j0 + per);
+    float s = 0.f;
+    for (int j = j0; j < j1; ++j) s += tile[j * xw + xi];
+    part[grp * xw + xi] = s;
+  }
+  __syncthreads();
+  if (t < xw) {
+    float s = 0.f;
+    for (int gg = 0; gg < G; ++gg) s += part[gg * xw + t];
+    tot[t] = s;
+  }
+  __syncthreads();
+  const float total = tot[xi];
+  const int x = xt * xw + xi;
+  const bool xok = x < kStateX;
+  for (int I = grp; I < n_qb; I += G) {
+    const int32_t* row = idx + ((size_t)bh * n_qb + I) * topk;
+    float s0 = 0.f, s1 = 0.f;
+    int j = 0;
+    for (; j + 1 < topk; j += 2) {
+      const int J0 = min(max(row[j], 0), n_kb - 1);
+      const int J1 = min(max(row[j + 1], 0), n_kb - 1);
+      s0 += tile[J0 * xw + xi];
+      s1 += tile[J1 * xw + xi];
+    }
+    if (j < topk) s0 += tile[min(max(row[j], 0), n_kb - 1) * xw + xi];
+    if (xok) state_m[((size_t)bh * n_qb + I) * kStateX + x] = total - (s0 + s1);
+  }
+}
+
+// ---------------------------------------------------------------------------------------------------------
+// k4_out: one workgroup per (bh, I) query block, BLKQ/32 waves; lane (i = l%32, half g) of wave w owns row
+// I*BLKQ + 32w + i. O^T[e][i] = sum_c Hm'^T[e][c] phi(Q)^T[c][i]: A = state rows (fp32 -> hi/lo), B = phi(q)
+// (fp32 -> hi/lo); hi*hi + hi*lo + lo*hi. den[i] = phi(q_i) . Z_m.
+// ---------------------------------------------------------------------------------------------------------
+template <int BLKQ>
+__global__ __launch_bounds__(BLKQ * 2) void k4_out(const uint16_t* __restrict__ q, const float* __restrict__ state_m,
+                                                  float* __restrict__ o_lin, int N, int n_qb, int total) {
+  const int item = xcd_remap(blockIdx.x, total);
+  const int bh = item / n_qb, I = item % n_qb;
+  const int t = threadIdx.x, w = t >> 6, l = t & 63, g = l >> 5, lr = l & 31;
+  const int row = I * BLKQ + 32 * w + lr;
+  const bool rok = row < N;
+  const float* sm = state_m + ((size_t)bh * n_qb + I) * kStateX;
+  const uint16_t* qrow = q + ((size_t)bh * N + (rok ? row : 0)) * kD;
+
+  // phi(q) of this lane's channels 16s + 8g + 0..7, split, and the partial denominator
+  v8bf bqh[8], bql[8];
+  float den = 0.f;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const int c0 = 16 * s + 8 * g;
+    uint4 wq = make_uint4(0, 0, 0, 0);
+    if (rok) wq = *(const uint4*)(qrow + c0);
+    const uint32_t ww[4] = {wq.x, wq.y, wq.z, wq.w};
+    const float4 z0 = *(const float4*)(sm + kD * kD + c0);
+    const float4 z1 = *(const float4*)(sm + kD * kD + c0 + 4);
+    const float zz[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
+    uint32_t hw[4], lw[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float p0 = phi_f(bf16_lo(ww[u])), p1 = phi_f(bf16_hi(ww[u]));
+      den = fmaf(p0, zz[2 * u], den);
+      den = fmaf(p1, zz[2 * u + 1], den);
+      float h0, l0, h1, l1;
+      split_bf16(p0, h0, l0);
+      split_bf16(p1, h1, l1);
+      hw[u] = pack_bf16x2(h0, h1);
+      lw[u] = pack_bf16x2(l0, l1);
+    }
+    bqh[s] = __builtin_bit_cast(v8bf, make_uint4(hw[0], hw[1], hw[2], hw[3]));
+    bql[s] = __builtin_bit_cast(v8bf, make_uint4(lw[0], lw[1], lw[2], lw[3]));
+  }
+  den += swap_halves_f32(den);
+  const float inv = 1.f / den;
+
+#pragma unroll
+  for (int et = 0; et < 4; ++et) {
+    v16f acc = {};
+    const int e = 32 * et + lr;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const float4 a0 = *(const float4*)(sm + e * kD + 16 * s + 8 * g);
+      const float4 a1 = *(const float4*)(sm + e * kD + 16 * s + 8 * g + 4);
+      const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+      uint32_t hw[4], lw[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        float h0, l0, h1, l1;
+        split_bf16(av[2 * u], h0, l0);
+        split_bf16(av[2 * u + 1], h1, l1);
+        hw[u] = pack_bf16x2(h0, h1);
+        lw[u] = pack_bf16x2(l0, l1);
+      }
+      const v8bf ah = __builtin_bit_cast(v8bf, make_uint4(hw[0], hw[1], hw[2], hw[3]));
+      const v8bf al = __builtin_bit_cast(v8bf, make_uint4(lw[0], lw[1], lw[2], lw[3]));
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bqh[s], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bql[s], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bqh[s], acc, 0, 0, 0);
+    }
+    if (rok) {
+      float* orow = o_lin + ((size_t)bh * N + row) * kD;
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int e0 = 32 * et + 8 * r4 + 4 * g;
+        *(float4*)(orow + e0) = make_float4(acc[4 * r4] * inv, acc[4 * r4 + 1] * inv, acc[4 * r4 + 2] * inv,
+                                            acc[4 * r4 + 3] * inv);
+      }
+    }
+  }
+}
+
+size_t gather_lds_bytes(int n_kb, int xw) { return ((size_t)n_kb * xw + 256 + xw) * sizeof(float); }
+
+hipError_t launch_linear(const Plan& p, const uint16_t* q, const uint16_t* k, const uint16_t* v, hipStream_t s) {
+  hipLaunchKernelGGL(k4_prep_wp, dim3(kD * kD / 256), dim3(256), 0, s, (const uint16_t*)p.w_proj, p.wpt);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k4_states, dim3(p.n_kb, p.BH), dim3(256), 0, s, k, v, p.wpt, p.state, p.N, p.n_kb, p.state_xw,
+                     p.n_state_xt);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const size_t lds = gather_lds_bytes(p.n_kb, p.state_xw);
+  static bool attr_set = false;  // raising the dynamic-LDS cap is idempotent; racing first calls are harmless
+  if (!attr_set) {
+    e = hipFuncSetAttribute((const void*)k4_gather, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(k4_gather, dim3(p.n_state_xt, p.BH), dim3(256), lds, s, p.state, p.block_idx, p.state_m,
+                     p.n_qb, p.n_kb, p.topk, p.state_xw, p.n_state_xt);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int total = p.BH * p.n_qb;
+  if (p.blk_q == 128)
+    hipLaunchKernelGGL(k4_out<128>, dim3(total), dim3(256), 0, s, q, p.state_m, p.o_lin, p.N, p.n_qb, total);
+  else
+    hipLaunchKernelGGL(k4_out<64>, dim3(total), dim3(128), 0, s, q, p.state_m, p.o_lin, p.N, p.n_qb, total);
+  return hipGetLastError();
+}
+
+}  // namespace sagesla

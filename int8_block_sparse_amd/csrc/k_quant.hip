@@ -1,0 +1,214 @@
+// K1: K-mean smoothing, per-block INT8 quantization and block mean pooling (gfx950).
+//
+// "Turbo Diffusion：秒级生成与高清保真的视频扩散技术突破" (lanhy.cn), §三(一) SageAttention2++: item 1 smooths
+// outliers before quantizing, item 2 gives every sub-block its own quantization parameters. Here:
+//   mu[c]   = fp32(exact sum over all N tokens of K[t][c] / N)     (per (b, h) channel mean of K)
+//   k'      = fp32(K - mu)                                          (Q and V are not smoothed)
+//   scale   = fp32(absmax / 127) per block of rows × all D channels (0 for an all-zero block)
+//   code    = clamp(round-half-even(fp32(x / scale)), -127, 127)
+//   pool    = fp64 mean of the block's rows (raw Q; smoothed K)
+// The fp64 column sums are exact when every partial sum is representable, which holds for bf16 inputs whose
+// sum of magnitudes stays below 2^53 units of the smallest ulp; the result is then independent of order.
+// HBM bound: K is read twice (sum, then quantize), Q once; int8 codes are written once.
+#include "device_common.h"
+#include "internal.h"
+
+namespace sagesla {
+
+// Partial column sums of K over row chunks, fp64. grid (n_chunks, BH), 256 threads:
+// thread t reads channels 8*(t%16)..+7 of rows t/16, t/16+16, ... (a wave reads 4 whole rows per load).
+__global__ __launch_bounds__(256) void k1_colsum_partial(const uint16_t* __restrict__ k, double* __restrict__ part,
+                                                        int N, int chunk_rows, int n_chunks) {
+  const int bh = blockIdx.y, ch = blockIdx.x;
+  const int t = threadIdx.x, cg = t & 15, rl = t >> 4;
+  const uint16_t* base = k + (size_t)bh * N * kD + cg * 8;
+  const int r0 = ch * chunk_rows, r1 = min(N, r0 + chunk_rows);
+  double acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.0;
+  int r = r0 + rl;
+  for (; r + 48 < r1; r += 64) {
+    uint4 w[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) w[u] = *(const uint4*)(base + (size_t)(r + 16 * u) * kD);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      acc[0] += bf16_lo(w[u].x); acc[1] += bf16_hi(w[u].x);
+      acc[2] += bf16_lo(w[u].y); acc[3] += bf16_hi(w[u].y);
+      acc[4] += bf16_lo(w[u].z); acc[5] += bf16_hi(w[u].z);
+      acc[6] += bf16_lo(w[u].w); acc[7] += bf16_hi(w[u].w);
+    }
+  }
+  for (; r < r1; r += 16) {
+    uint4 w = *(const uint4*)(base + (size_t)r * kD);
+    acc[0] += bf16_lo(w.x); acc[1] += bf16_hi(w.x);
+    acc[2] += bf16_lo(w.y); acc[3] += bf16_hi(w.y);
+    acc[4] += bf16_lo(w.z); acc[5] += bf16_hi(w.z);
+    acc[6] += bf16_lo(w.w); acc[7] += bf16_hi(w.w);
+  }
+  __shared__ double red[16][kD + 1];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) red[rl][cg * 8 + i] = acc[i];
+  __syncthreads();
+  if (t < kD) {
+    double s = 0.0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) s += red[j][t];
+    part[((size_t)bh * n_chunks + ch) * kD + t] = s;
+  }
+}
+
+// mu = fp32(S / N), S = the partial sums added in chunk order. grid BH, 128 threads.
+__global__ __launch_bounds__(128) void k1_colsum_final(const double* __restrict__ part, float* __restrict__ mu,
+                                                      int n_chunks, int N) {
+  const int bh = blockIdx.x, c = threadIdx.x;
+  const double* p = part + (size_t)bh * n_chunks * kD + c;
+  double s = 0.0;
+  for (int i = 0; i < n_chunks; ++i) s += p[(size_t)i * kD];
+  mu[bh * kD + c] = (float)(s / (double)N);
+}
+
+// The INT8 code of x for a block with scale s > 0 and r = fp32(1/s):
+// q = fp32(x * r) differs from the correctly rounded quotient f = fp32(x / s) by at most 1.9e-5 when |x/s| <= 127
+// (two roundings of relative 2^-24 each on a value below 127.00001, plus f's own half ulp 2^-18). round(q)
+// can differ from round(f) only if a half-integer lies within that distance of q, so such rare elements (and
+// non-finite q) are recomputed with the IEEE division.
+__device__ __forceinline__ int quant_code(float x, float s, float r) {
+#pragma clang fp contract(off)
+  const float qv = x * r;
+  float c = rintf(qv);
+  if (!(fabsf(qv - c) < 0.5f - 0x1p-15f)) c = rintf(x / s);
+  c = fminf(fmaxf(c, -127.f), 127.f);
+  return (int)c;
+}
+
+__device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {
+  return (uint32_t)(a & 0xff) | ((uint32_t)(b & 0xff) << 8) | ((uint32_t)(c & 0xff) << 16) | ((uint32_t)d << 24);
+}
+
+// One block of up to MAXROWS rows (valid: `rows`) × 128 channels, 256 threads. Thread t owns channels
+// 8*(t%16)..+7 of rows t/16 + 16*i.
+template <int MAXROWS>
+__device__ __forceinline__ void quant_block(const uint16_t* __restrict__ src, int rows, const float* __restrict__ mu,
+                                            int8_t* __restrict__ dst, float* __restrict__ scale_out,
+                                            double* __restrict__ pool_out, float* s_amax,
+                                            double (*s_red)[kD + 1]) {
+  constexpr int IT = MAXROWS / 16;
+  const int t = threadIdx.x, cg = t & 15, rl = t >> 4;
+  float m8[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) m8[e] = mu ? mu[cg * 8 + e] : 0.f;
+  float x[IT][8];
+  float amax = 0.f;
+  double psum[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) psum[e] = 0.0;
+#pragma unroll
+  for (int i = 0; i < IT; ++i) {
+    const int r = rl + 16 * i;
+    uint4 w = make_uint4(0, 0, 0, 0);
+    if (r < rows) w = *(const uint4*)(src + (size_t)r * kD + cg * 8);
+    x[i][0] = bf16_lo(w.x); x[i][1] = bf16_hi(w.x);
+    x[i][2] = bf16_lo(w.y); x[i][3] = bf16_hi(w.y);
+    x[i][4] = bf16_lo(w.z); x[i][5] = bf16_hi(w.z);
+    x[i][6] = bf16_lo(w.w); x[i][7] = bf16_hi(w.w);
+    if (mu && r < rows) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[i][e] = x[i][e] - m8[e];  // one IEEE fp32 subtraction
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      amax = fmaxf(amax, fabsf(x[i][e]));
+      psum[e] += (double)x[i][e];
+    }
+  }
+  amax = wave_max_f32(amax);
+  if ((t & 63) == 0) s_amax[t >> 6] = amax;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) s_red[rl][cg * 8 + e] = psum[e];
+  __syncthreads();
+  amax = fmaxf(fmaxf(s_amax[0], s_amax[1]), fmaxf(s_amax[2], s_amax[3]));
+  const float s = amax / 127.f;  // IEEE fp32 division (correctly rounded)
+  const float rcp = 1.f / s;
+#pragma unroll
+  for (int i = 0; i < IT; ++i) {
+    const int r = rl + 16 * i;
+    if (r < rows) {
+      int c[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) c[e] = (amax > 0.f) ? quant_code(x[i][e], s, rcp) : 0;
+      uint2 o;
+      o.x = pack4_i8(c[0], c[1], c[2], c[3]);
+      o.y = pack4_i8(c[4], c[5], c[6], c[7]);
+      *(uint2*)(dst + (size_t)r * kD + cg * 8) = o;
+    }
+  }
+  if (t < kD) {
+    double sum = 0.0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) sum += s_red[j][t];
+    pool_out[t] = sum / (double)rows;
+  }
+  if (t == 0) *scale_out = (amax > 0.f) ? s : 0.f;
+}
+
+// grid (n_qb + n_kb, BH): x < n_qb quantizes query block x, otherwise key block x - n_qb.
+template <int BLKQ>
+__global__ __launch_bounds__(256) void k1_quant(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                                               const float* __restrict__ mu, int8_t* __restrict__ q8,
+                                               int8_t* __restrict__ k8, float* __restrict__ qs,
+                                               float* __restrict__ ks, double* __restrict__ qp,
+                                               double* __restrict__ kp, int N, int n_qb, int n_kb) {
+  __shared__ float s_amax[4];
+  __shared__ double s_red[16][kD + 1];
+  const int bh = blockIdx.y;
+  const int x = blockIdx.x;
+  const size_t base = (size_t)bh * N * kD;
+  if (x < n_qb) {
+    const int r0 = x * BLKQ;
+    quant_block<BLKQ>(q + base + (size_t)r0 * kD, min(BLKQ, N - r0), nullptr, q8 + base + (size_t)r0 * kD,
+                      qs + (size_t)bh * n_qb + x, qp + ((size_t)bh * n_qb + x) * kD, s_amax, s_red);
+  } else {
+    const int j = x - n_qb;
+    const int r0 = j * kBlkK;
+    quant_block<kBlkK>(k + base + (size_t)r0 * kD, min(kBlkK, N - r0), mu ? mu + bh * kD : nullptr,
+                       k8 + base + (size_t)r0 * kD, ks + (size_t)bh * n_kb + j, kp + ((size_t)bh * n_kb + j) * kD,
+                       s_amax, s_red);
+  }
+}
+
+__global__ void k_fill_f32(float* __restrict__ d, size_t n, float v) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) d[i] = v;
+}
+
+hipError_t launch_fill_f32(float* dst, size_t n, float val, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  size_t blocks = (n + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(k_fill_f32, dim3((unsigned)blocks), dim3(256), 0, s, dst, n, val);
+  return hipGetLastError();
+}
+
+hipError_t launch_kmean(const Plan& p, const uint16_t* k, hipStream_t s) {
+  if (!p.smooth) return launch_fill_f32(p.k_mean, (size_t)p.BH * kD, 0.f, s);
+  hipLaunchKernelGGL(k1_colsum_partial, dim3(p.n_colsum_chunks, p.BH), dim3(256), 0, s, k, p.colsum_part, p.N,
+                     p.colsum_chunk, p.n_colsum_chunks);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k1_colsum_final, dim3(p.BH), dim3(kD), 0, s, p.colsum_part, p.k_mean, p.n_colsum_chunks, p.N);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant(const Plan& p, const uint16_t* q, const uint16_t* k, hipStream_t s) {
+  const dim3 grid(p.n_qb + p.n_kb, p.BH);
+  const float* mu = p.smooth ? p.k_mean : nullptr;
+  if (p.blk_q == 128)
+    hipLaunchKernelGGL(k1_quant<128>, grid, dim3(256), 0, s, q, k, mu, p.q_i8, p.k_i8, p.q_scale, p.k_scale,
+                       p.q_pool, p.k_pool, p.N, p.n_qb, p.n_kb);
+  else
+    hipLaunchKernelGGL(k1_quant<64>, grid, dim3(256), 0, s, q, k, mu, p.q_i8, p.k_i8, p.q_scale, p.k_scale,
+                       p.q_pool, p.k_pool, p.N, p.n_qb, p.n_kb);
+  return hipGetLastError();
+}
+
+}  // namespace sagesla

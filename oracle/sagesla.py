@@ -183,23 +183,24 @@ def select_topk(scores: np.ndarray, k: int):
 # --------------------------------------------------------------------------------------------------------
 # 6. INT8 block-sparse attention over the selected blocks  ([TD-news] §三(一) item 3, §三(二) item 3)
 # --------------------------------------------------------------------------------------------------------
-def sparse_attention(q_codes, q_scales, k_codes, k_scales, V, idx, blk_q, blk_k, sm_scale):
+def sparse_attention(q_codes, q_scales, k_codes, k_scales, V, idx, blk_q, blk_k, sm_scale, blocks=None):
     """O_s[i] = sum_j softmax_j(z_ij) v_j over the keys j of the selected blocks of i's query block.
 
     z_ij = (codeQ_i . codeK_j) * s_q(I) * s_k(J) * sm_scale; the integer dot product is exact in fp64.
-    The softmax is normalised over the selected keys only. A query block with no selected block gets 0."""
+    The softmax is normalised over the selected keys only. A query block with no selected block gets 0.
+    blocks: optional list of query blocks to compute (the rows of the others are left 0)."""
     N, D = V.shape
     V = np.asarray(V, np.float64)
     out = np.zeros((N, D), dtype=np.float64)
     qc = q_codes.astype(np.float64)
     kc = k_codes.astype(np.float64)
-    for I in range(n_blocks(N, blk_q)):
+    for I in (range(n_blocks(N, blk_q)) if blocks is None else blocks):
         rows = block_rows(N, blk_q, I)
-        blocks = list(idx[I])
-        if not blocks:
+        sel = list(idx[I])
+        if not sel:
             continue
-        key_rows = np.concatenate([np.arange(N)[block_rows(N, blk_k, J)] for J in blocks])
-        kscale = np.concatenate([np.full(block_rows(N, blk_k, J).stop - J * blk_k, k_scales[J]) for J in blocks])
+        key_rows = np.concatenate([np.arange(N)[block_rows(N, blk_k, J)] for J in sel])
+        kscale = np.concatenate([np.full(block_rows(N, blk_k, J).stop - J * blk_k, k_scales[J]) for J in sel])
         z = (qc[rows] @ kc[key_rows].T) * q_scales[I] * kscale[None, :] * sm_scale
         z = z - z.max(axis=1, keepdims=True)
         p = np.exp(z)
@@ -240,30 +241,31 @@ def linear_states(K, V, blk_k):
     return H, Z
 
 
-def linear_branch(Q, H, Z, idx, blk_q):
+def linear_branch(Q, H, Z, idx, blk_q, blocks=None):
     """O_l[i] = phi(q_i) H_m / (phi(q_i) . Z_m) with H_m = sum_J H_J - sum_{J in crit(I)} H_J and Z_m alike.
 
     The total over all blocks is formed once; each query block subtracts its selected blocks' states. The
     subtraction is written as one product of the 0/1 selection matrix with the stacked states. A query block
-    whose selection covers every key block has no remaining keys and gets O_l = 0."""
+    whose selection covers every key block has no remaining keys and gets O_l = 0.
+    blocks: optional list of query blocks to compute (the rows of the others are left 0)."""
     N, D = Q.shape
     nkb = H.shape[0]
-    nqb = n_blocks(N, blk_q)
+    todo = list(range(n_blocks(N, blk_q)) if blocks is None else blocks)
     PQ = phi(Q)
     Htot = H.sum(axis=0)
     Ztot = Z.sum(axis=0)
-    M = np.zeros((nqb, nkb))
-    for I in range(nqb):
-        M[I, idx[I]] = 1.0
-    Hcrit = (M @ H.reshape(nkb, D * D)).reshape(nqb, D, D)
+    M = np.zeros((len(todo), nkb))
+    for r, I in enumerate(todo):
+        M[r, idx[I]] = 1.0
+    Hcrit = (M @ H.reshape(nkb, D * D)).reshape(len(todo), D, D)
     Zcrit = M @ Z
     out = np.zeros((N, D))
-    for I in range(nqb):
+    for r, I in enumerate(todo):
         if len(set(int(j) for j in idx[I])) == nkb:
             continue
         rows = block_rows(N, blk_q, I)
-        Hm = Htot - Hcrit[I]
-        Zm = Ztot - Zcrit[I]
+        Hm = Htot - Hcrit[r]
+        Zm = Ztot - Zcrit[r]
         out[rows] = (PQ[rows] @ Hm) / (PQ[rows] @ Zm)[:, None]
     return out
 
@@ -277,12 +279,13 @@ def project(O_l, W_p):
 # 8. the whole forward
 # --------------------------------------------------------------------------------------------------------
 def forward_head(Q, K, V, W_p, blk_q, blk_k, topk, *, linear=True, smooth_k=True, quant=True,
-                 sm_scale=None, mask=None):
+                 sm_scale=None, mask=None, blocks=None):
     """SageSLA forward for one (b, h) slice. Q, K, V: [N, D] arrays of exact bf16 values; W_p: [D, D].
 
     Switches for the tests: smooth_k=False skips K-mean smoothing, quant=False attends with the unquantized
     fp32 values, mask (int [n_qb, k] ascending) replaces the selection (used to compare with a GPU's own
-    selection). Returns a dict with every intermediate and 'out' (fp64)."""
+    selection), blocks (list of query blocks) limits the attention outputs to those blocks. Returns a dict with
+    every intermediate and 'out' (fp64)."""
     Q = np.asarray(Q, np.float64)
     K = np.asarray(K, np.float64)
     V = np.asarray(V, np.float64)
@@ -306,7 +309,7 @@ def forward_head(Q, K, V, W_p, blk_q, blk_k, topk, *, linear=True, smooth_k=True
     idx = r["idx"] if mask is None else np.asarray(mask)
     if quant:
         r["o_s"] = sparse_attention(r["q_codes"], r["q_scales"], r["k_codes"], r["k_scales"], V, idx,
-                                    blk_q, blk_k, sm_scale)
+                                    blk_q, blk_k, sm_scale, blocks=blocks)
     else:
         ones_q = np.ones(n_blocks(N, blk_q))
         ones_k = np.ones(n_blocks(N, blk_k))
@@ -314,7 +317,7 @@ def forward_head(Q, K, V, W_p, blk_q, blk_k, topk, *, linear=True, smooth_k=True
         r["o_s"] = _sparse_float(Q, kp, V, idx, blk_q, blk_k, sm_scale, ones_q, ones_k)
     if linear:
         H, Z = linear_states(K, V, blk_k)
-        r["o_l"] = linear_branch(Q, H, Z, idx, blk_q)
+        r["o_l"] = linear_branch(Q, H, Z, idx, blk_q, blocks=blocks)
         r["o_lin"] = project(r["o_l"], W_p)
     else:
         r["o_l"] = np.zeros((N, D))

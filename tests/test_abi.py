@@ -1,0 +1,132 @@
+"""The C-ABI library: it loads, exports every entry point its header declares, its parameter block has the
+layout a C compiler gives it, and host-side validation returns the documented status codes without launching
+anything. CPU only (no kernel is called)."""
+import ctypes
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+import int8_block_sparse_amd as sg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sagesla.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(sg.LIB_PATH):
+        pytest.fail("libsagesla.so is not built (run __graft_entry__.build())")
+    return sg.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sagesla_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert {"sagesla_quantize", "sagesla_select", "sagesla_forward", "sagesla_workspace_bytes"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in sagesla.h but not exported"
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="needs gcc")
+def test_param_block_layout_matches_c(tmp_path):
+    fields = [f for f, _ in sg.Params._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text(
+        '#include <stdio.h>\n#include <stddef.h>\n#include "sagesla.h"\nint main(void){\n'
+        '  printf("%zu", sizeof(sagesla_params));\n'
+        + "".join(f'  printf(" %zu", offsetof(sagesla_params, {f}));\n' for f in fields)
+        + "  return 0;\n}\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
+    want = [ctypes.sizeof(sg.Params)] + [getattr(sg.Params, f).offset for f in fields]
+    assert got == want
+
+
+def test_status_strings(lib):
+    for code in range(7):
+        assert lib.sagesla_status_str(code)
+    assert lib.sagesla_last_hip_error() == 0
+
+
+# Validation must reject these before touching the device. The fake pointers below are never dereferenced on
+# the host; the tests are skipped where a GPU is visible so a validation bug can never launch with them.
+try:
+    import torch
+    _gpu = torch.cuda.is_available()
+except Exception:  # noqa: BLE001
+    _gpu = False
+cpu_only = pytest.mark.skipif(_gpu, reason="host-validation tests use fake device pointers; CPU only")
+
+FAKE = 1 << 40  # 256-byte aligned, never dereferenced
+
+
+def good(**kw):
+    cfg = sg.Config(B=1, H=2, N=1000, blk_q=128, blk_k=64, topk=2, linear=True)
+    p = cfg.params(w_proj=FAKE, workspace=FAKE, workspace_bytes=1 << 40)
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return p
+
+
+def fwd(lib, p, q=FAKE, k=FAKE, v=FAKE, out=FAKE):
+    return lib.sagesla_forward(q, k, v, out, ctypes.byref(p), None)
+
+
+@cpu_only
+@pytest.mark.parametrize("field,value,status", [
+    ("D", 64, 3), ("blk_k", 128, 3), ("blk_q", 32, 3), ("flags", 0x10, 3), ("N", (1 << 24) + 1, 3),
+    ("B", 0, 2), ("H", 0, 2), ("N", 0, 2), ("topk", -1, 2), ("topk", 17, 2), ("B", 300, 2),
+    ("sm_scale", float("nan"), 2), ("sm_scale", -1.0, 2),
+    ("w_proj", None, 1), ("workspace", None, 4), ("workspace_bytes", 100, 4),
+    ("workspace", FAKE + 16, 5), ("q_i8", FAKE + 8, 5), ("o_lin", FAKE + 4, 5), ("w_proj", FAKE + 2, 5),
+])
+def test_forward_validation(lib, field, value, status):
+    p = good(**{field: value})
+    if field == "B":
+        p.H = 300 if value == 300 else p.H
+    assert fwd(lib, p) == status
+
+
+@cpu_only
+def test_tensor_pointer_validation(lib):
+    assert fwd(lib, good(), q=None) == 1
+    assert fwd(lib, good(), out=None) == 1
+    assert fwd(lib, good(), v=FAKE + 2) == 5
+    p = good(flags=sg.LINEAR | sg.USE_GIVEN_MASK)
+    assert fwd(lib, p) == 1  # given mask without block_idx
+    p = good()
+    assert lib.sagesla_quantize(None, FAKE, ctypes.byref(p), None) == 1
+    p = good(D=96)
+    assert lib.sagesla_select(ctypes.byref(p), None) == 3
+    assert lib.sagesla_last_hip_error() == 0
+
+
+def test_workspace_bytes(lib):
+    cfg = sg.Config(B=2, H=40, N=75600, blk_q=128, blk_k=64, topk=118, linear=True)
+    n = lib.sagesla_workspace_bytes(ctypes.byref(cfg.params()))
+    # int8 codes of Q and K alone are 2*B*H*N*D bytes; the linear branch adds states, remainders and O_lin
+    assert n > 2 * 2 * 40 * 75600 * 128
+    assert n < 32 << 30
+    cfg_dense = sg.Config(B=1, H=12, N=32760, blk_q=128, blk_k=64, topk=512, linear=False)
+    assert 0 < lib.sagesla_workspace_bytes(ctypes.byref(cfg_dense.params())) < n
+    bad = sg.Config(B=1, H=1, N=100, D=64)
+    assert lib.sagesla_workspace_bytes(ctypes.byref(bad.params())) == 0
+    # the linear branch's LDS-resident state tile limits the key-block count
+    big = sg.Config(B=1, H=1, N=64 * 12000, topk=10, linear=True)
+    assert lib.sagesla_validate(ctypes.byref(big.params(w_proj=FAKE))) == 3
+    big.linear = False
+    assert lib.sagesla_validate(ctypes.byref(big.params())) == 0
+
+
+def test_topk_blocks_matches_flag_reading():
+    assert [sg.topk_blocks(f, n) for f, n in [(0.25, 16), (1.0, 512), (0.1, 512), (0.1, 1182), (0.05, 4208)]] == \
+        [4, 512, 51, 118, 210]

@@ -45,9 +45,9 @@ def _select_ties_high(scores, k):
     return np.sort(n - 1 - idx, axis=1), gap
 
 
-def _linear_no_subtraction(Q, H, Z, idx, blk_q):
+def _linear_no_subtraction(Q, H, Z, idx, blk_q, **kw):
     empty = np.zeros((idx.shape[0], 0), dtype=np.int32)
-    return _orig["linear_branch"](Q, H, Z, empty, blk_q)
+    return _orig["linear_branch"](Q, H, Z, empty, blk_q, **kw)
 
 
 def _linear_states_transposed(K, V, blk_k):
@@ -59,16 +59,16 @@ def _kmean_first_block(K):
     return _orig["k_mean"](np.asarray(K)[:64])
 
 
-def _sparse_no_scale(q_codes, q_scales, k_codes, k_scales, V, idx, blk_q, blk_k, sm_scale):
-    return _orig["sparse_attention"](q_codes, q_scales, k_codes, k_scales, V, idx, blk_q, blk_k, 1.0)
+def _sparse_no_scale(q_codes, q_scales, k_codes, k_scales, V, idx, blk_q, blk_k, sm_scale, **kw):
+    return _orig["sparse_attention"](q_codes, q_scales, k_codes, k_scales, V, idx, blk_q, blk_k, 1.0, **kw)
 
 
-def _sparse_drop_ragged_tail(q_codes, q_scales, k_codes, k_scales, V, idx, blk_q, blk_k, sm_scale):
+def _sparse_drop_ragged_tail(q_codes, q_scales, k_codes, k_scales, V, idx, blk_q, blk_k, sm_scale, **kw):
     # forgets the last (ragged) key block's rows
     N = V.shape[0]
     nkb = orc.n_blocks(N, blk_k)
     idx2 = [np.array([J for J in row if J != nkb - 1] or [0]) for row in idx]
-    return _orig["sparse_attention"](q_codes, q_scales, k_codes, k_scales, V, idx2, blk_q, blk_k, sm_scale)
+    return _orig["sparse_attention"](q_codes, q_scales, k_codes, k_scales, V, idx2, blk_q, blk_k, sm_scale, **kw)
 
 
 def _pool_sum(X, blk):

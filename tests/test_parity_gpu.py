@@ -1,0 +1,249 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle, element by element, on seeded inputs.
+
+Bars: INT8 codes, scales and the K mean bit-exact; the block mask bit-exact except in near-tie rows (oracle
+gap between the k-th and (k+1)-th score below 1e-6, flagged not failed); outputs, computed by the oracle
+with the GPU's own mask, within max-abs 2e-2 and cosine >= 0.999; the linear branch gated separately
+(cosine >= 0.999, relative L2 <= 1e-3) because its contribution is small next to the output tolerance.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import int8_block_sparse_amd as sg
+import synth
+from oracle import sagesla as orc
+from conftest import to_np
+
+pytestmark = pytest.mark.gpu
+
+OUT_ATOL = 2e-2
+OUT_COS = 0.999
+LIN_COS = 0.999
+LIN_REL = 1e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    sg.load()
+    return torch.device("cuda:0")
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def cos(a, b):
+    a, b = a.ravel(), b.ravel()
+    return float(a @ b / (np.linalg.norm(a) * np.linalg.norm(b) + 1e-300))
+
+
+def run_gpu(q, k, v, w, wl, topk, **kw):
+    torch.cuda.synchronize()
+    out, ex = sg.forward(q, k, v, w, topk=topk, blk_q=wl.blk_q, blk_k=wl.blk_k, export=True, **kw)
+    torch.cuda.synchronize()
+    return out, ex
+
+
+def check_quant(ex, r, b, h):
+    assert np.array_equal(ex["q_i8"][b, h].cpu().numpy(), r["q_codes"]), "Q codes differ"
+    assert np.array_equal(ex["k_i8"][b, h].cpu().numpy(), r["k_codes"]), "K codes differ"
+    assert np.array_equal(ex["q_scale"][b, h].cpu().numpy(), r["q_scales"].astype(np.float32)), "Q scales differ"
+    assert np.array_equal(ex["k_scale"][b, h].cpu().numpy(), r["k_scales"].astype(np.float32)), "K scales differ"
+    assert np.array_equal(ex["k_mean"][b, h].cpu().numpy(), r["mu"].astype(np.float32)), "K mean differs"
+    np.testing.assert_allclose(ex["q_pool"][b, h].cpu().numpy(), r["q_pool"], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(ex["k_pool"][b, h].cpu().numpy(), r["k_pool"], rtol=1e-10, atol=1e-13)
+
+
+def check_mask(gidx, r, topk):
+    """Bit-exact mask except near-tie rows; returns the number of flagged rows."""
+    want = r["idx"]
+    got = gidx[:, :topk] if topk else np.zeros((want.shape[0], 0), np.int32)
+    flagged = 0
+    for I in range(want.shape[0]):
+        if np.array_equal(got[I], want[I]):
+            continue
+        assert r["gap"][I] < orc.NEAR_TIE, f"mask row {I} differs with gap {r['gap'][I]:.3e}"
+        flagged += 1
+        assert np.all(np.diff(got[I]) > 0), "GPU row not ascending/unique"
+    return flagged
+
+
+def check_out(out, r, rows=None, lin=None):
+    o = out if rows is None else out[rows]
+    want = r["out"] if rows is None else r["out"][rows]
+    err = np.abs(o - want).max()
+    c = cos(o, want)
+    assert err <= OUT_ATOL and c >= OUT_COS, f"out max-abs {err:.3e} cos {c:.6f}"
+    if lin is not None:
+        lw = r["o_lin"] if rows is None else r["o_lin"][rows]
+        lg = lin if rows is None else lin[rows]
+        if np.abs(lw).max() == 0:
+            assert np.abs(lg).max() == 0
+        else:
+            rel = np.linalg.norm(lg - lw) / np.linalg.norm(lw)
+            assert cos(lg, lw) >= LIN_COS and rel <= LIN_REL, f"o_lin cos {cos(lg, lw):.6f} rel {rel:.3e}"
+    return err, c
+
+
+def full_case(wl, seed=0, topk=None, linear=None, smooth_k=True, scale_v=None, w_mul=1.0, prep=None):
+    topk = wl.topk if topk is None else topk
+    linear = wl.linear if linear is None else linear
+    q, k, v, w = synth.make(wl, seed)
+    if prep is not None:
+        q, k, v = prep(q, k, v)
+    w = (w.float() * w_mul).to(torch.bfloat16)
+    dq, dk, dv, dw = (t.cuda() for t in (q, k, v, w))
+    say(f"case {wl.name} B{wl.B} H{wl.H} N{wl.N} bq{wl.blk_q} topk{topk} linear{linear} smooth{smooth_k}")
+    out, ex = run_gpu(dq, dk, dv, dw, wl, topk, linear=linear, smooth_k=smooth_k)
+    outn = to_np(out)
+    W = to_np(w)
+    flagged = 0
+    for b in range(wl.B):
+        for h in range(wl.H):
+            Q, K, V = to_np(q[b, h]), to_np(k[b, h]), to_np(v[b, h])
+            gidx = ex["block_idx"][b, h].cpu().numpy()
+            r = orc.forward_head(Q, K, V, W, wl.blk_q, wl.blk_k, topk, linear=linear, smooth_k=smooth_k)
+            assert r["exact_sum_ok"]
+            check_quant(ex, r, b, h)
+            flagged += check_mask(gidx, r, topk)
+            rg = orc.forward_head(Q, K, V, W, wl.blk_q, wl.blk_k, topk, linear=linear, smooth_k=smooth_k,
+                                  mask=gidx[:, :topk] if topk else np.zeros((wl.n_qb, 0), np.int32))
+            lin = to_np(ex["o_lin"][b, h]) if linear else None
+            err, c = check_out(outn[b, h], rg, lin=lin)
+            say(f"  b{b} h{h}: out max-abs {err:.2e} cos {c:.6f}")
+    return flagged
+
+
+SMALL = {
+    "tiny": synth.workload(0),
+    "ragged128": synth.custom(1, 2, 1000, blk_q=128, topk_frac=0.2),
+    "ragged64": synth.custom(2, 1, 330, blk_q=64, topk_frac=0.34),
+    "grid": synth.custom(1, 1, 6 * 20 * 24, grid=(6, 20, 24), structured=True, blk_q=128, topk_frac=0.1),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_forward_small(name):
+    assert full_case(SMALL[name]) == 0
+
+
+def test_topk_zero_linear_only():
+    full_case(SMALL["ragged128"], topk=0)
+
+
+def test_topk_all_with_linear_is_dense():
+    wl = SMALL["ragged128"]
+    full_case(wl, topk=wl.n_kb, linear=True)
+
+
+def test_dense_no_linear():
+    wl = synth.custom(1, 2, 777, blk_q=128, topk_frac=1.0, linear=False)
+    full_case(wl)
+
+
+def test_no_smoothing():
+    full_case(SMALL["ragged64"], smooth_k=False)
+
+
+def test_linear_projection_x100():
+    # makes the linear branch visible in the output tolerance
+    full_case(SMALL["ragged128"], w_mul=100.0)
+
+
+def test_zero_and_constant_blocks():
+    def prep(q, k, v):
+        q = q.clone()
+        k = k.clone()
+        q[:, :, 128:256] = 0  # an all-zero query block: scale 0, codes 0
+        k[:, :, 64:128] = k[:, :, 64:65]  # a key block of identical rows
+        k[:, :, :, 5] = 0.75  # a constant channel: smoothed to exactly 0
+        return q, k, v
+    full_case(SMALL["ragged128"], prep=prep)
+
+
+def test_given_mask_matches_oracle_with_same_mask():
+    wl = SMALL["ragged128"]
+    q, k, v, w = synth.make(wl, 3)
+    rng = np.random.default_rng(5)
+    topk = 4
+    mask = np.stack([np.sort(rng.choice(wl.n_kb, topk, replace=False)) for _ in range(wl.B * wl.H * wl.n_qb)])
+    mask = mask.reshape(wl.B, wl.H, wl.n_qb, topk).astype(np.int32)
+    dmask = torch.from_numpy(mask).cuda()
+    out, ex = run_gpu(q.cuda(), k.cuda(), v.cuda(), w.cuda(), wl, topk, mask=dmask)
+    for h in range(wl.H):
+        r = orc.forward_head(to_np(q[0, h]), to_np(k[0, h]), to_np(v[0, h]), to_np(w), wl.blk_q, wl.blk_k, topk,
+                             mask=mask[0, h])
+        check_out(to_np(out[0, h]), r, lin=to_np(ex["o_lin"][0, h]))
+
+
+def test_deterministic():
+    wl = SMALL["grid"]
+    q, k, v, w = (t.cuda() for t in synth.make(wl, 1))
+    o1, e1 = run_gpu(q, k, v, w, wl, wl.topk)
+    o2, e2 = run_gpu(q, k, v, w, wl, wl.topk)
+    assert torch.equal(o1, o2)
+    for name in e1:
+        assert torch.equal(e1[name], e2[name]), name
+
+
+def test_stage_entry_points_agree_with_forward():
+    wl = SMALL["ragged128"]
+    q, k, v, w = (t.cuda() for t in synth.make(wl, 2))
+    out, ex = run_gpu(q, k, v, w, wl, 3)
+    qx, ws = sg.quantize(q, k, blk_q=wl.blk_q)
+    idx = sg.select(qx["q_pool"], qx["k_pool"], N=wl.N, topk=3, blk_q=wl.blk_q, workspace=ws)
+    torch.cuda.synchronize()
+    for name in ("q_i8", "k_i8", "q_scale", "k_scale", "k_mean", "q_pool", "k_pool"):
+        assert torch.equal(qx[name], ex[name]), name
+    assert torch.equal(idx, ex["block_idx"][..., :3])
+
+
+# ---------------------------------------------------------------------------------------------------------
+# the real layer shapes, in the launch configuration the benchmark times, checked on sampled (b, h) heads
+# and sampled query blocks (quantization and selection of a sampled head are checked in full)
+# ---------------------------------------------------------------------------------------------------------
+def sampled_case(cfg_id, heads, n_blocks_sample=6, seed=0):
+    wl = synth.workload(cfg_id)
+    say(f"full-size {wl.name}: generating")
+    q, k, v, w = synth.make(wl, seed, device="cuda")
+    torch.cuda.synchronize()
+    say(f"full-size {wl.name}: forward")
+    out, ex = run_gpu(q, k, v, w, wl, wl.topk, linear=wl.linear)
+    W = to_np(w)
+    rng = np.random.default_rng(cfg_id)
+    flagged = 0
+    for (b, h) in heads:
+        Q, K, V = to_np(q[b, h]), to_np(k[b, h]), to_np(v[b, h])
+        gidx = ex["block_idx"][b, h].cpu().numpy()[:, :wl.topk]
+        blocks = sorted(set([0, wl.n_qb - 1] + list(rng.choice(wl.n_qb, n_blocks_sample, replace=False))))
+        r = orc.forward_head(Q, K, V, W, wl.blk_q, wl.blk_k, wl.topk, linear=wl.linear, mask=gidx, blocks=blocks)
+        assert r["exact_sum_ok"]
+        check_quant(ex, r, b, h)
+        flagged_h = check_mask(gidx, r, wl.topk)
+        flagged += flagged_h
+        rows = np.concatenate([np.arange(wl.N)[orc.block_rows(wl.N, wl.blk_q, I)] for I in blocks])
+        lin = to_np(ex["o_lin"][b, h]) if wl.linear else None
+        err, c = check_out(to_np(out[b, h]), r, rows=rows, lin=lin)
+        say(f"  b{b} h{h}: {len(blocks)} query blocks, out max-abs {err:.2e} cos {c:.6f}, near-tie rows {flagged_h}"
+            f", min gap {np.min(r['gap']):.2e}")
+    del q, k, v, out, ex
+    torch.cuda.empty_cache()
+    return flagged
+
+
+def test_full_size_dense_480p():
+    sampled_case(1, [(0, 0), (0, 11)])
+
+
+def test_full_size_sla_480p():
+    sampled_case(2, [(0, 0), (0, 7)])
+
+
+def test_full_size_sla_720p_pair():
+    sampled_case(3, [(0, 0), (1, 39)])

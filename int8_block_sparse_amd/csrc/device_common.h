@@ -38,10 +38,12 @@ __device__ __forceinline__ float wave_max_f32(float v) {
   return v;
 }
 
-// value of lane (l ^ 32): swap the two 32-lane halves of the wave
+// value of lane (l ^ 32). v_permlane32_swap exchanges lanes 32..63 of its first operand with lanes 0..31 of
+// its second: with both operands = v, the first result holds the other half's value in lanes 32..63 and the
+// second result holds it in lanes 0..31.
 __device__ __forceinline__ int swap_halves_i32(int v) {
   auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
-  return r[0];
+  return (threadIdx.x & 32) ? r[0] : r[1];
 }
 __device__ __forceinline__ float swap_halves_f32(float v) {
   return __int_as_float(swap_halves_i32(__float_as_int(v)));

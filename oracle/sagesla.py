@@ -77,16 +77,20 @@ def topk_count(frac: float, n_kb: int) -> int:
 def exact_sum_ok(x: np.ndarray) -> bool:
     """True when every partial sum of each column of x (finite binary floats) is exact in fp64.
 
-    All values of a column are integer multiples of the smallest ulp u among them, so every partial sum is
-    an integer multiple of u bounded by sum|x|; it is exact when sum|x| / u < 2**53."""
+    Every value is an integer multiple of its granularity (the largest power of two dividing it), hence of the
+    smallest granularity u in the column; every partial sum is then an integer multiple of u bounded by sum|x|,
+    which fp64 holds exactly when sum|x| / u < 2**53."""
     x = np.asarray(x, dtype=np.float64)
     for c in range(x.shape[1]):
         col = x[:, c]
         nz = col[col != 0]
         if nz.size == 0:
             continue
-        # ulp of a binary float with p=24 significant bits covers bf16 (p=8) and fp32 values alike
-        u = float(np.min(np.ldexp(1.0, np.frexp(nz)[1] - 24)))
+        # granularity of each value: the largest power of two dividing it (x = m * 2^(e-53), m an integer)
+        m, e = np.frexp(nz)
+        mi = np.abs(m * 2.0 ** 53).astype(np.int64)
+        low = (mi & -mi).astype(np.float64)
+        u = float(np.min(np.ldexp(low, e - 53)))
         if float(np.sum(np.abs(nz))) / u >= 2.0 ** 53:
             return False
     return True

@@ -100,6 +100,16 @@ def test_exact_sum_precondition_detects_failure():
     x = np.array([[2.0 ** 60], [2.0 ** -10]])
     assert not orc.exact_sum_ok(x)
     assert orc.exact_sum_ok(np.array([[1.0], [2.0 ** -10]]))
+    # granularity is the value's lowest set bit, not its precision: 3 * 2^-40 needs 2^-40, 1.5 needs 2^-1
+    assert not orc.exact_sum_ok(np.array([[2.0 ** 13], [3 * 2.0 ** -40]]))
+    assert orc.exact_sum_ok(np.array([[2.0 ** 13], [3 * 2.0 ** -38]]))
+    # when the precondition holds the fp64 sum equals math.fsum in any order
+    rng = np.random.default_rng(0)
+    col = (rng.standard_normal(20000) * 2 + 1).astype(np.float32).astype(np.float64)
+    import torch
+    col = torch.from_numpy(col).to(torch.bfloat16).double().numpy()
+    assert orc.exact_sum_ok(col[:, None])
+    assert float(np.sum(col)) == math.fsum(col) == float(np.sum(col[::-1])) == float(np.sum(np.sort(col)))
 
 
 # ---------------------------------------------------------------------------------------------------------

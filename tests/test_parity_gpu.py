@@ -74,11 +74,29 @@ def check_mask(gidx, r, topk):
     return flagged
 
 
-def check_out(out, r, rows=None, lin=None):
+def bf16_half_ulp(x):
+    """Half the bf16 spacing at |x| (8 significant bits)."""
+    e = np.frexp(np.maximum(np.abs(x), 2.0 ** -126))[1]
+    return np.ldexp(1.0, e - 9)
+
+
+def check_out(out, r, rows=None, lin=None, bf16_bound=False):
+    """max-abs <= 2e-2 and cosine >= 0.999; with bf16_bound the allowance grows by the bf16 half-ulp of the
+    expected value (outputs beyond |8| cannot be stored in bf16 closer than 2e-2)."""
     o = out if rows is None else out[rows]
     want = r["out"] if rows is None else r["out"][rows]
-    err = np.abs(o - want).max()
+    excess = np.abs(o - want) - (bf16_half_ulp(want) if bf16_bound else 0.0)
+    err = excess.max()
     c = cos(o, want)
+    if not (err <= OUT_ATOL and c >= OUT_COS):
+        if lin is not None:
+            lg = lin if rows is None else lin[rows]
+            lw = r["o_lin"] if rows is None else r["o_lin"][rows]
+            ws = r["o_s"] if rows is None else r["o_s"][rows]
+            say(f"    diag: sparse part max-abs {np.abs(o - lg - ws).max():.3e} cos {cos(o - lg, ws):.6f}; "
+                f"linear part max-abs {np.abs(lg - lw).max():.3e} cos {cos(lg, lw):.6f}")
+        bad = np.argwhere(np.abs(o - want) > OUT_ATOL)
+        say(f"    diag: {len(bad)} elements over tolerance, first rows {np.unique(bad[:, 0])[:16]}")
     assert err <= OUT_ATOL and c >= OUT_COS, f"out max-abs {err:.3e} cos {c:.6f}"
     if lin is not None:
         lw = r["o_lin"] if rows is None else r["o_lin"][rows]
@@ -91,7 +109,7 @@ def check_out(out, r, rows=None, lin=None):
     return err, c
 
 
-def full_case(wl, seed=0, topk=None, linear=None, smooth_k=True, scale_v=None, w_mul=1.0, prep=None):
+def full_case(wl, seed=0, topk=None, linear=None, smooth_k=True, w_mul=1.0, prep=None):
     topk = wl.topk if topk is None else topk
     linear = wl.linear if linear is None else linear
     q, k, v, w = synth.make(wl, seed)
@@ -115,7 +133,7 @@ def full_case(wl, seed=0, topk=None, linear=None, smooth_k=True, scale_v=None, w
             rg = orc.forward_head(Q, K, V, W, wl.blk_q, wl.blk_k, topk, linear=linear, smooth_k=smooth_k,
                                   mask=gidx[:, :topk] if topk else np.zeros((wl.n_qb, 0), np.int32))
             lin = to_np(ex["o_lin"][b, h]) if linear else None
-            err, c = check_out(outn[b, h], rg, lin=lin)
+            err, c = check_out(outn[b, h], rg, lin=lin, bf16_bound=w_mul != 1.0)
             say(f"  b{b} h{h}: out max-abs {err:.2e} cos {c:.6f}")
     return flagged
 
@@ -152,7 +170,7 @@ def test_no_smoothing():
 
 
 def test_linear_projection_x100():
-    # makes the linear branch visible in the output tolerance
+    # makes the linear branch dominate the output; outputs reach |8|+, so the bf16 storage bound applies
     full_case(SMALL["ragged128"], w_mul=100.0)
 
 

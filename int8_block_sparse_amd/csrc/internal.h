@@ -33,6 +33,8 @@ struct Plan {
   int32_t* block_idx;   // [BH][n_qb][topk]
   uint16_t* wpt;        // [D][D] bf16: W_p^T in MFMA slot order
   float* state;         // [BH][n_state_xt][n_kb][state_xw]
+  int2* runs;           // [BH][n_qb][topk]      selection as runs [a, b) of consecutive key blocks
+  int32_t* run_cnt;     // [BH][n_qb]
   float* state_m;       // [BH][n_qb][kStateX]   remaining (non-selected) state per query block
   float* o_lin;         // [BH][N][D]
   size_t ws_bytes;

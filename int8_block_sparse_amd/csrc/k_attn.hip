@@ -102,7 +102,7 @@ __device__ __forceinline__ float attn_softmax_tile(const v16i& s, float c, float
 }
 
 template <int NW>
-__global__ __launch_bounds__(NW * 64) void k3_attn(const int8_t* __restrict__ q8, const int8_t* __restrict__ k8,
+__global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k3_attn(const int8_t* __restrict__ q8, const int8_t* __restrict__ k8,
                                                   const uint16_t* __restrict__ v, const float* __restrict__ qs,
                                                   const float* __restrict__ ks, const int32_t* __restrict__ idx,
                                                   const float* __restrict__ o_lin, uint16_t* __restrict__ out,

@@ -36,6 +36,11 @@ __global__ __launch_bounds__(256) void k4_prep_wp(const uint16_t* __restrict__ w
 
 __device__ __forceinline__ float phi_f(float x) { return x > 0.f ? x + 1.f : expf(x); }
 
+__global__ void k_fill_i32(int32_t* __restrict__ d, int n, int v) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) d[i] = v;
+}
+
 // ---------------------------------------------------------------------------------------------------------
 // k4_states: grid (n_kb, BH), 256 threads (4 waves).
 // LDS holds phi(K)^T (hi, lo) and V^T as [channel][key] bf16 rows of 128 B, 16-byte chunks XOR-swizzled.
@@ -163,52 +168,98 @@ __global__ __launch_bounds__(256) void k4_states(const uint16_t* __restrict__ k,
 }
 
 // ---------------------------------------------------------------------------------------------------------
-// k4_gather: grid (n_xt, BH), 256 threads; dynamic LDS = n_kb * xw floats (+ partial sums).
-// Threads form 256/xw groups of xw columns. Totals: group g adds a fixed contiguous range of blocks, the
-// groups' partials are then added in group order. Gather: group g handles query blocks g, g + G, ...
+// k4_runs: the selected blocks of each query block as runs of consecutive indices [a, b). One wave per
+// (bh, I) row. For any list (sorted or not) the sum over its elements equals the sum over these runs of
+// P[b] - P[a] with P the exclusive prefix sum over blocks; for the ascending selections there are only a
+// third as many runs as blocks on structured video inputs.
 // ---------------------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k4_gather(const float* __restrict__ table, const int32_t* __restrict__ idx,
-                                                float* __restrict__ state_m, int n_qb, int n_kb, int topk, int xw,
-                                                int n_xt) {
-  extern __shared__ __attribute__((aligned(16))) float tile[];  // [n_kb][xw], then [G][xw] partials, [xw] totals
+__global__ __launch_bounds__(64) void k4_runs(const int32_t* __restrict__ idx, int2* __restrict__ runs,
+                                             int32_t* __restrict__ run_cnt, int n_kb, int topk, int rows) {
+  const int row = blockIdx.x;
+  if (row >= rows) return;
+  const int l = threadIdx.x;
+  const int32_t* in = idx + (size_t)row * topk;
+  int2* out = runs + (size_t)row * topk;
+  int ns = 0, ne = 0;
+  for (int j0 = 0; j0 < topk; j0 += 64) {
+    const int j = j0 + l;
+    const bool ok = j < topk;
+    const int cur = ok ? min(max(in[j], 0), n_kb - 1) : 0;
+    const int prev = (ok && j > 0) ? min(max(in[j - 1], 0), n_kb - 1) : -2;
+    const int next = (ok && j + 1 < topk) ? min(max(in[j + 1], 0), n_kb - 1) : -2;
+    const bool st = ok && cur != prev + 1;
+    const bool en = ok && next != cur + 1;
+    const unsigned long long ms = __ballot(st), me = __ballot(en);
+    const unsigned long long lt = l ? (~0ull >> (64 - l)) : 0ull;
+    if (st) out[ns + __popcll(ms & lt)].x = cur;
+    if (en) out[ne + __popcll(me & lt)].y = cur + 1;
+    ns += __popcll(ms);
+    ne += __popcll(me);
+  }
+  if (l == 0) run_cnt[row] = ns;
+}
+
+// ---------------------------------------------------------------------------------------------------------
+// k4_gather: grid (n_xt, BH), 1024 threads (16 waves); LDS = (n_kb + 1) * xw floats + 1024 partials.
+// The state tile of all key blocks (xw columns) is loaded into LDS and turned in place into its exclusive
+// prefix sum over blocks, P[0..n_kb] (P[n_kb] = the total over all blocks). Segments of the scan and their
+// combination have a fixed order, so the result is deterministic.
+// Each wave then serves 64/xw query blocks at once (lane = (query block sub, column xi)):
+//   H_m[x] = P[n_kb][x] - sum over the runs [a, b) of the query block's selection of (P[b][x] - P[a][x]).
+// ---------------------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void k4_gather(const float* __restrict__ table, const int2* __restrict__ runs,
+                                                 const int32_t* __restrict__ run_cnt, float* __restrict__ state_m,
+                                                 int n_qb, int n_kb, int topk, int xw, int n_xt) {
+  extern __shared__ __attribute__((aligned(16))) float lds[];
+  float* P = lds;                          // [(n_kb + 1) * xw]
+  float* seg = lds + (size_t)(n_kb + 1) * xw;  // [1024]
   const int xt = blockIdx.x, bh = blockIdx.y;
   const int t = threadIdx.x;
-  const int G = 256 / xw, grp = t / xw, xi = t % xw;
   const float* src = table + ((size_t)bh * n_xt + xt) * n_kb * xw;
   const int nflt = n_kb * xw;
-  for (int i = 4 * t; i < nflt; i += 4 * 256) *(float4*)(tile + i) = *(const float4*)(src + i);
-  float* part = tile + nflt;
-  float* tot = part + G * xw;
+  for (int i = 4 * t; i < nflt; i += 4 * 1024) *(float4*)(P + i) = *(const float4*)(src + i);
   __syncthreads();
-  {
-    const int per = (n_kb + G - 1) / G;
-    const int j0 = grp * per, j1 = min(n_kb, j0 + per);
-    float s = 0.f;
-    for (int j = j0; j < j1; ++j) s += tile[j * xw + xi];
-    part[grp * xw + xi] = s;
+  // exclusive prefix over blocks: thread (sg, xi) scans rows [j0, j1) of column xi
+  const int nseg = 1024 / xw, sg = t / xw, xi = t % xw;
+  const int per = (n_kb + nseg - 1) / nseg;
+  const int j0 = min(n_kb, sg * per), j1 = min(n_kb, j0 + per);
+  float run = 0.f;
+  for (int j = j0; j < j1; ++j) run += P[j * xw + xi];
+  seg[t] = run;
+  __syncthreads();
+  float off = 0.f;
+  for (int s2 = 0; s2 < sg; ++s2) off += seg[s2 * xw + xi];
+  for (int j = j0; j < j1; ++j) {
+    const float v = P[j * xw + xi];
+    P[j * xw + xi] = off;
+    off += v;
   }
+  if (sg == nseg - 1) P[n_kb * xw + xi] = off;  // last segment ends at n_kb (empty segments pass their offset on)
   __syncthreads();
-  if (t < xw) {
-    float s = 0.f;
-    for (int gg = 0; gg < G; ++gg) s += part[gg * xw + t];
-    tot[t] = s;
-  }
-  __syncthreads();
-  const float total = tot[xi];
-  const int x = xt * xw + xi;
+
+  const int w = t >> 6, l = t & 63;
+  const int ipw = 64 / xw, sub = l / xw, col = l % xw;
+  const float total = P[n_kb * xw + col];
+  const int x = xt * xw + col;
   const bool xok = x < kStateX;
-  for (int I = grp; I < n_qb; I += G) {
-    const int32_t* row = idx + ((size_t)bh * n_qb + I) * topk;
-    float s0 = 0.f, s1 = 0.f;
-    int j = 0;
-    for (; j + 1 < topk; j += 2) {
-      const int J0 = min(max(row[j], 0), n_kb - 1);
-      const int J1 = min(max(row[j + 1], 0), n_kb - 1);
-      s0 += tile[J0 * xw + xi];
-      s1 += tile[J1 * xw + xi];
+  for (int I0 = w * ipw; I0 < n_qb; I0 += 16 * ipw) {
+    const int I = I0 + sub;
+    const bool iok = I < n_qb;
+    const size_t row = (size_t)bh * n_qb + (iok ? I : 0);
+    const int cnt = iok ? run_cnt[row] : 0;
+    const int2* rr = runs + row * topk;
+    float acc0 = 0.f, acc1 = 0.f;
+    int r = 0;
+    for (; r + 1 < cnt; r += 2) {
+      const int2 u = rr[r], v = rr[r + 1];
+      acc0 += P[u.y * xw + col] - P[u.x * xw + col];
+      acc1 += P[v.y * xw + col] - P[v.x * xw + col];
     }
-    if (j < topk) s0 += tile[min(max(row[j], 0), n_kb - 1) * xw + xi];
-    if (xok) state_m[((size_t)bh * n_qb + I) * kStateX + x] = total - (s0 + s1);
+    if (r < cnt) {
+      const int2 u = rr[r];
+      acc0 += P[u.y * xw + col] - P[u.x * xw + col];
+    }
+    if (iok && xok) state_m[row * kStateX + x] = total - (acc0 + acc1);
   }
 }
 
@@ -294,7 +345,7 @@ __global__ __launch_bounds__(BLKQ * 2) void k4_out(const uint16_t* __restrict__ 
   }
 }
 
-size_t gather_lds_bytes(int n_kb, int xw) { return ((size_t)n_kb * xw + 256 + xw) * sizeof(float); }
+size_t gather_lds_bytes(int n_kb, int xw) { return ((size_t)(n_kb + 1) * xw + 1024) * sizeof(float); }
 
 hipError_t launch_linear(const Plan& p, const uint16_t* q, const uint16_t* k, const uint16_t* v, hipStream_t s) {
   hipLaunchKernelGGL(k4_prep_wp, dim3(kD * kD / 256), dim3(256), 0, s, (const uint16_t*)p.w_proj, p.wpt);
@@ -310,8 +361,15 @@ hipError_t launch_linear(const Plan& p, const uint16_t* q, const uint16_t* k, co
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL(k4_gather, dim3(p.n_state_xt, p.BH), dim3(256), lds, s, p.state, p.block_idx, p.state_m,
-                     p.n_qb, p.n_kb, p.topk, p.state_xw, p.n_state_xt);
+  const int rows = p.BH * p.n_qb;
+  if (p.topk > 0) {
+    hipLaunchKernelGGL(k4_runs, dim3(rows), dim3(64), 0, s, p.block_idx, p.runs, p.run_cnt, p.n_kb, p.topk, rows);
+  } else {
+    hipLaunchKernelGGL(k_fill_i32, dim3((rows + 255) / 256), dim3(256), 0, s, p.run_cnt, rows, 0);
+  }
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(k4_gather, dim3(p.n_state_xt, p.BH), dim3(1024), lds, s, p.state, p.runs, p.run_cnt,
+                     p.state_m, p.n_qb, p.n_kb, p.topk, p.state_xw, p.n_state_xt);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int total = p.BH * p.n_qb;
   if (p.blk_q == 128)

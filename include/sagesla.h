@@ -44,6 +44,13 @@ typedef enum {
   SAGESLA_E_HIP = 6          /* a HIP call or launch failed; sagesla_last_hip_error() holds its code     */
 } sagesla_status;
 
+/* stages of sagesla_forward, in launch order (for the optional timing events) */
+#define SAGESLA_STAGE_QUANTIZE 0 /* K mean, smoothing, INT8 codes, scales, pooled means          */
+#define SAGESLA_STAGE_SELECT 1   /* block scores and top-k                                          */
+#define SAGESLA_STAGE_LINEAR 2   /* linear branch: block states, remaining-state gather, contraction */
+#define SAGESLA_STAGE_ATTN 3     /* block-sparse INT8 attention and the output epilogue (one kernel) */
+#define SAGESLA_NUM_STAGES 4
+
 /* flags */
 #define SAGESLA_LINEAR 0x1u         /* run the linear branch on the non-selected blocks (needs w_proj)      */
 #define SAGESLA_SMOOTH_K 0x2u       /* subtract the per-channel mean of K over all N tokens before quantizing */
@@ -69,6 +76,10 @@ typedef struct sagesla_params {
   double* k_pool;     /* [B][H][n_kb][D]   mean of the smoothed K rows of each key block                  */
   int32_t* block_idx; /* [B][H][n_qb][topk] selected key blocks, ascending (input with USE_GIVEN_MASK)     */
   float* o_lin;       /* [B][H][N][D]      linear-branch output after the projection (fp32)               */
+  /* Optional timing: NULL, or 2*SAGESLA_NUM_STAGES caller-created hipEvent_t handles (as void*). sagesla_forward
+     records events[2s] on `stream` just before stage s and events[2s+1] just after it (both at the same point
+     when the stage has nothing to do). The caller owns the events and reads them after synchronizing.       */
+  void* const* events;
 } sagesla_params;
 
 /* Bytes of workspace the three entry points need for these parameters (all intermediates kept inside).

@@ -14,7 +14,8 @@ from typing import Optional
 
 __all__ = [
     "LIB_PATH", "load", "Params", "SageSLAError", "topk_blocks", "n_blocks", "workspace_bytes", "validate",
-    "quantize", "select", "forward", "LINEAR", "SMOOTH_K", "USE_GIVEN_MASK", "STATUS",
+    "quantize", "select", "forward", "LINEAR", "SMOOTH_K", "USE_GIVEN_MASK", "STATUS", "STAGES", "stage_events",
+    "stage_ms", "Config",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsagesla.so")
@@ -24,6 +25,7 @@ SMOOTH_K = 0x2
 USE_GIVEN_MASK = 0x4
 
 STATUS = {0: "OK", 1: "E_NULL", 2: "E_SHAPE", 3: "E_UNSUPPORTED", 4: "E_WORKSPACE", 5: "E_ALIGN", 6: "E_HIP"}
+STAGES = ("quantize", "select", "linear", "attn")
 
 
 class SageSLAError(RuntimeError):
@@ -45,6 +47,7 @@ class Params(ctypes.Structure):
         ("q_i8", ctypes.c_void_p), ("q_scale", ctypes.c_void_p), ("k_i8", ctypes.c_void_p),
         ("k_scale", ctypes.c_void_p), ("k_mean", ctypes.c_void_p), ("q_pool", ctypes.c_void_p),
         ("k_pool", ctypes.c_void_p), ("block_idx", ctypes.c_void_p), ("o_lin", ctypes.c_void_p),
+        ("events", ctypes.POINTER(ctypes.c_void_p)),
     ]
 
 
@@ -58,6 +61,9 @@ def load():
         return _lib
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with `python -m int8_block_sparse_amd.build`")
+    # torch first: the library's HIP runtime dependency then binds to the runtime torch already loaded, so
+    # torch's device memory, streams and events are the library's too
+    import torch  # noqa: F401
     lib = ctypes.CDLL(LIB_PATH)
     P = ctypes.POINTER(Params)
     vp = ctypes.c_void_p
@@ -193,9 +199,23 @@ def _exports(cfg: Config, device):
     return ex
 
 
+def stage_events():
+    """2 * len(STAGES) timing events for forward(events=...); read them with stage_ms() after synchronizing."""
+    import torch
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * len(STAGES))]
+    for e in evs:
+        e.record()  # creates the underlying hipEvent_t
+    return evs
+
+
+def stage_ms(evs):
+    """Per-stage milliseconds from events recorded by forward(events=evs)."""
+    return {name: evs[2 * i].elapsed_time(evs[2 * i + 1]) for i, name in enumerate(STAGES)}
+
+
 def forward(q, k, v, w_proj=None, *, topk: int, blk_q: int = 128, blk_k: int = 64, linear: bool = True,
             smooth_k: bool = True, sm_scale: float = 0.0, mask=None, out=None, workspace=None,
-            export: bool = False):
+            export: bool = False, events=None):
     """SageSLA forward. q, k, v: bf16 [B, H, N, 128] CUDA tensors; w_proj: bf16 [128, 128] (needed with linear).
 
     mask: optional int32 [B, H, n_qb, topk] ascending block lists used instead of the selection.
@@ -216,6 +236,9 @@ def forward(q, k, v, w_proj=None, *, topk: int, blk_q: int = 128, blk_k: int = 6
     ptrs = {name: _ptr(t) for name, t in ex.items()}
     p = cfg.params(w_proj=_ptr(w_proj), workspace=ws.data_ptr(), workspace_bytes=ws.numel(),
                    given_mask=mask is not None, **ptrs)
+    if events is not None:
+        arr = (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
+        p.events = ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p))
     _check(load().sagesla_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), ctypes.byref(p),
                                   _stream(q.device)), "sagesla_forward")
     return (out, ex) if export else out

@@ -138,6 +138,14 @@ sagesla_status hip_status(hipError_t e) {
     if (st_ != SAGESLA_OK) return st_;            \
   } while (0)
 
+// records the caller's timing event of stage `stage` (begin: 0, end: 1) if events were given
+sagesla_status mark(const sagesla_params* p, int stage, int end, hipStream_t s) {
+  if (!p->events) return SAGESLA_OK;
+  void* ev = p->events[2 * stage + end];
+  if (!ev) return SAGESLA_OK;
+  return hip_status(hipEventRecord((hipEvent_t)ev, s));
+}
+
 sagesla_status run_quantize(const Plan& pl, const void* q, const void* k, hipStream_t s) {
   SAGESLA_TRY(launch_kmean(pl, (const uint16_t*)k, s));
   SAGESLA_TRY(launch_quant(pl, (const uint16_t*)q, (const uint16_t*)k, s));
@@ -197,15 +205,28 @@ sagesla_status sagesla_forward(const void* q, const void* k, const void* v, void
   if ((st = check_workspace(p, pl)) != SAGESLA_OK) return st;
   make_plan(p, (unsigned char*)p->workspace, &pl);
   const hipStream_t s = (hipStream_t)stream;
-  if ((st = run_quantize(pl, q, k, s)) != SAGESLA_OK) return st;
-  if (!pl.given_mask && (st = run_select(pl, s)) != SAGESLA_OK) return st;
+#define SAGESLA_STEP(expr)                                     \
+  do {                                                         \
+    if ((st = (expr)) != SAGESLA_OK) return st;                \
+  } while (0)
+  SAGESLA_STEP(mark(p, SAGESLA_STAGE_QUANTIZE, 0, s));
+  SAGESLA_STEP(run_quantize(pl, q, k, s));
+  SAGESLA_STEP(mark(p, SAGESLA_STAGE_QUANTIZE, 1, s));
+  SAGESLA_STEP(mark(p, SAGESLA_STAGE_SELECT, 0, s));
+  if (!pl.given_mask) SAGESLA_STEP(run_select(pl, s));
+  SAGESLA_STEP(mark(p, SAGESLA_STAGE_SELECT, 1, s));
+  SAGESLA_STEP(mark(p, SAGESLA_STAGE_LINEAR, 0, s));
   const bool lin_active = pl.linear && pl.topk < pl.n_kb;
   if (lin_active) {
     SAGESLA_TRY(launch_linear(pl, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, s));
   } else if (p->o_lin) {
     SAGESLA_TRY(launch_fill_f32(p->o_lin, (size_t)pl.BH * pl.N * kD, 0.f, s));
   }
+  SAGESLA_STEP(mark(p, SAGESLA_STAGE_LINEAR, 1, s));
+  SAGESLA_STEP(mark(p, SAGESLA_STAGE_ATTN, 0, s));
   SAGESLA_TRY(launch_attn(pl, (const uint16_t*)v, (uint16_t*)out, s));
+  SAGESLA_STEP(mark(p, SAGESLA_STAGE_ATTN, 1, s));
+#undef SAGESLA_STEP
   return SAGESLA_OK;
 }
 

@@ -97,6 +97,7 @@ void make_plan(const sagesla_params* p, unsigned char* ws, Plan* pl) {
   pl->q_pool = (double*)take(BH * nqb * D * sizeof(double));
   pl->k_pool = (double*)take(BH * nkb * D * sizeof(double));
   pl->scores = (double*)take(BH * nqb * nkb * sizeof(double));
+  pl->v_img = (unsigned char*)take(BH * nkb * 16384);
   pl->block_idx = (int32_t*)take(BH * nqb * (size_t)pl->topk * sizeof(int32_t));
   if (lin_active) {
     pl->wpt = (uint16_t*)take(D * D * sizeof(uint16_t));
@@ -146,9 +147,9 @@ sagesla_status mark(const sagesla_params* p, int stage, int end, hipStream_t s) 
   return hip_status(hipEventRecord((hipEvent_t)ev, s));
 }
 
-sagesla_status run_quantize(const Plan& pl, const void* q, const void* k, hipStream_t s) {
+sagesla_status run_quantize(const Plan& pl, const void* q, const void* k, const void* v, hipStream_t s) {
   SAGESLA_TRY(launch_kmean(pl, (const uint16_t*)k, s));
-  SAGESLA_TRY(launch_quant(pl, (const uint16_t*)q, (const uint16_t*)k, s));
+  SAGESLA_TRY(launch_quant(pl, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, s));
   return SAGESLA_OK;
 }
 
@@ -180,7 +181,7 @@ sagesla_status sagesla_quantize(const void* q, const void* k, const sagesla_para
   make_plan(p, nullptr, &pl);
   if ((st = check_workspace(p, pl)) != SAGESLA_OK) return st;
   make_plan(p, (unsigned char*)p->workspace, &pl);
-  return run_quantize(pl, q, k, (hipStream_t)stream);
+  return run_quantize(pl, q, k, nullptr, (hipStream_t)stream);
 }
 
 sagesla_status sagesla_select(const sagesla_params* p, void* stream) {
@@ -210,7 +211,7 @@ sagesla_status sagesla_forward(const void* q, const void* k, const void* v, void
     if ((st = (expr)) != SAGESLA_OK) return st;                \
   } while (0)
   SAGESLA_STEP(mark(p, SAGESLA_STAGE_QUANTIZE, 0, s));
-  SAGESLA_STEP(run_quantize(pl, q, k, s));
+  SAGESLA_STEP(run_quantize(pl, q, k, v, s));
   SAGESLA_STEP(mark(p, SAGESLA_STAGE_QUANTIZE, 1, s));
   SAGESLA_STEP(mark(p, SAGESLA_STAGE_SELECT, 0, s));
   if (!pl.given_mask) SAGESLA_STEP(run_select(pl, s));
@@ -224,7 +225,7 @@ sagesla_status sagesla_forward(const void* q, const void* k, const void* v, void
   }
   SAGESLA_STEP(mark(p, SAGESLA_STAGE_LINEAR, 1, s));
   SAGESLA_STEP(mark(p, SAGESLA_STAGE_ATTN, 0, s));
-  SAGESLA_TRY(launch_attn(pl, (const uint16_t*)v, (uint16_t*)out, s));
+  SAGESLA_TRY(launch_attn(pl, (uint16_t*)out, s));
   SAGESLA_STEP(mark(p, SAGESLA_STAGE_ATTN, 1, s));
 #undef SAGESLA_STEP
   return SAGESLA_OK;

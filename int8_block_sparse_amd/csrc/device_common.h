@@ -49,6 +49,10 @@ __device__ __forceinline__ float swap_halves_f32(float v) {
   return __int_as_float(swap_halves_i32(__float_as_int(v)));
 }
 
+// Key order inside each group of 16 keys of a V^T row in LDS: the bf16 MFMA lane half g, slot i (0..7) must
+// find key 8*(i/4) + 4*g + (i%4) at position 8*g + i, i.e. the middle two groups of 4 keys trade places.
+__device__ __forceinline__ int key_pos16(int off) { return (off & 3) | ((off & 4) << 1) | ((off & 8) >> 1); }
+
 // XOR swizzle of the 16-byte chunk index inside a 128-byte LDS row, so that both 8 consecutive rows read at
 // one chunk and rows 8 apart written at one chunk land in different banks.
 __device__ __forceinline__ int swz8(int row) { return (row ^ (row >> 3)) & 7; }

@@ -30,6 +30,7 @@ struct Plan {
   double* q_pool;       // [BH][n_qb][D]
   double* k_pool;       // [BH][n_kb][D]
   double* scores;       // [BH][n_qb][n_kb]
+  unsigned char* v_img; // [BH][n_kb][16384]    per key block: V^T in the attention kernel's LDS layout
   int32_t* block_idx;   // [BH][n_qb][topk]
   uint16_t* wpt;        // [D][D] bf16: W_p^T in MFMA slot order
   float* state;         // [BH][n_state_xt][n_kb][state_xw]
@@ -42,14 +43,15 @@ struct Plan {
 
 // K1: K-mean smoothing, per-block INT8 quantization and block mean pooling
 hipError_t launch_kmean(const Plan& p, const uint16_t* k, hipStream_t s);
-hipError_t launch_quant(const Plan& p, const uint16_t* q, const uint16_t* k, hipStream_t s);
+// (v may be null: then no V^T images are written)
+hipError_t launch_quant(const Plan& p, const uint16_t* q, const uint16_t* k, const uint16_t* v, hipStream_t s);
 // K2: pooled block scores and top-k selection
 hipError_t launch_scores(const Plan& p, hipStream_t s);
 hipError_t launch_topk(const Plan& p, hipStream_t s);
 // K4: linear branch (block states, total-minus-selected gather, contraction with phi(Q))
 hipError_t launch_linear(const Plan& p, const uint16_t* q, const uint16_t* k, const uint16_t* v, hipStream_t s);
 // K3: block-sparse INT8 attention, epilogue adds the linear branch and writes bf16
-hipError_t launch_attn(const Plan& p, const uint16_t* v, uint16_t* out, hipStream_t s);
+hipError_t launch_attn(const Plan& p, uint16_t* out, hipStream_t s);
 // fills (graph-capture friendly replacements for memset)
 hipError_t launch_fill_f32(float* dst, size_t n, float val, hipStream_t s);
 // dynamic LDS of the kernels that size it at run time

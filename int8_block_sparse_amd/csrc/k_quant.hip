@@ -152,13 +152,40 @@ __device__ __forceinline__ void quant_block(const uint16_t* __restrict__ src, in
   if (t == 0) *scale_out = (amax > 0.f) ? s : 0.f;
 }
 
-// grid (n_qb + n_kb, BH): x < n_qb quantizes query block x, otherwise key block x - n_qb.
+// V^T image of one key block for the attention kernel: [128 channels][64 keys] bf16, 16 KB, each channel row's
+// keys in MFMA slot order (key_pos16 within every 16) and its 16-byte chunks XOR-swizzled (swz8), exactly the
+// LDS layout the attention kernel reads; keys past a ragged block's end are zero. 256 threads: thread t takes
+// channels 8*(t%16)..+7 of keys 4*(t/16)..+3.
+__device__ __forceinline__ void write_v_image(const uint16_t* __restrict__ src, int nv, unsigned char* __restrict__ img) {
+  const int t = threadIdx.x, cg = t & 15, kg = t >> 4;
+  uint32_t wv[4][4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const int r = 4 * kg + b;
+    uint4 a = make_uint4(0, 0, 0, 0);
+    if (r < nv) a = *(const uint4*)(src + (size_t)r * kD + cg * 8);
+    wv[b][0] = a.x; wv[b][1] = a.y; wv[b][2] = a.z; wv[b][3] = a.w;
+  }
+  const int pos = 16 * (kg >> 2) + key_pos16(4 * (kg & 3));
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int row = cg * 8 + e, sh = (e & 1) * 16;
+    const uint32_t k0 = (wv[0][e >> 1] >> sh) & 0xffffu, k1 = (wv[1][e >> 1] >> sh) & 0xffffu;
+    const uint32_t k2 = (wv[2][e >> 1] >> sh) & 0xffffu, k3 = (wv[3][e >> 1] >> sh) & 0xffffu;
+    *(uint2*)(img + row * 128 + (((pos >> 3) ^ swz8(row)) << 4) + ((pos & 7) << 1)) =
+        make_uint2(k0 | (k1 << 16), k2 | (k3 << 16));
+  }
+}
+
+// grid (n_qb + n_kb, BH): x < n_qb quantizes query block x, otherwise key block x - n_qb (and, when v is given,
+// writes that key block's V^T image).
 template <int BLKQ>
 __global__ __launch_bounds__(256) void k1_quant(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                                const float* __restrict__ mu, int8_t* __restrict__ q8,
                                                int8_t* __restrict__ k8, float* __restrict__ qs,
                                                float* __restrict__ ks, double* __restrict__ qp,
-                                               double* __restrict__ kp, int N, int n_qb, int n_kb) {
+                                               double* __restrict__ kp, const uint16_t* __restrict__ v,
+                                               unsigned char* __restrict__ v_img, int N, int n_qb, int n_kb) {
   __shared__ float s_amax[4];
   __shared__ double s_red[16][kD + 1];
   const int bh = blockIdx.y;
@@ -174,6 +201,7 @@ __global__ __launch_bounds__(256) void k1_quant(const uint16_t* __restrict__ q, 
     quant_block<kBlkK>(k + base + (size_t)r0 * kD, min(kBlkK, N - r0), mu ? mu + bh * kD : nullptr,
                        k8 + base + (size_t)r0 * kD, ks + (size_t)bh * n_kb + j, kp + ((size_t)bh * n_kb + j) * kD,
                        s_amax, s_red);
+    if (v) write_v_image(v + base + (size_t)r0 * kD, min(kBlkK, N - r0), v_img + ((size_t)bh * n_kb + j) * 16384);
   }
 }
 
@@ -199,15 +227,15 @@ hipError_t launch_kmean(const Plan& p, const uint16_t* k, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_quant(const Plan& p, const uint16_t* q, const uint16_t* k, hipStream_t s) {
+hipError_t launch_quant(const Plan& p, const uint16_t* q, const uint16_t* k, const uint16_t* v, hipStream_t s) {
   const dim3 grid(p.n_qb + p.n_kb, p.BH);
   const float* mu = p.smooth ? p.k_mean : nullptr;
   if (p.blk_q == 128)
     hipLaunchKernelGGL(k1_quant<128>, grid, dim3(256), 0, s, q, k, mu, p.q_i8, p.k_i8, p.q_scale, p.k_scale,
-                       p.q_pool, p.k_pool, p.N, p.n_qb, p.n_kb);
+                       p.q_pool, p.k_pool, v, p.v_img, p.N, p.n_qb, p.n_kb);
   else
     hipLaunchKernelGGL(k1_quant<64>, grid, dim3(256), 0, s, q, k, mu, p.q_i8, p.k_i8, p.q_scale, p.k_scale,
-                       p.q_pool, p.k_pool, p.N, p.n_qb, p.n_kb);
+                       p.q_pool, p.k_pool, v, p.v_img, p.N, p.n_qb, p.n_kb);
   return hipGetLastError();
 }
 

@@ -102,7 +102,7 @@ void make_plan(const sagesla_params* p, unsigned char* ws, Plan* pl) {
   if (lin_active) {
     pl->wpt = (uint16_t*)take(D * D * sizeof(uint16_t));
     pl->state = (float*)take(BH * pl->n_state_xt * nkb * pl->state_xw * sizeof(float));
-    pl->runs = (int2*)take(BH * nqb * (size_t)pl->topk * sizeof(int2));
+    pl->runs = (int2*)take(BH * nqb * (size_t)run_stride(pl->topk) * sizeof(int2));
     pl->run_cnt = (int32_t*)take(BH * nqb * sizeof(int32_t));
     pl->state_m = (float*)take(BH * nqb * kStateX * sizeof(float));
     pl->o_lin = (float*)take(BH * N * D * sizeof(float));

@@ -34,7 +34,7 @@ struct Plan {
   int32_t* block_idx;   // [BH][n_qb][topk]
   uint16_t* wpt;        // [D][D] bf16: W_p^T in MFMA slot order
   float* state;         // [BH][n_state_xt][n_kb][state_xw]
-  int2* runs;           // [BH][n_qb][topk]      selection as runs [a, b) of consecutive key blocks
+  int2* runs;           // [BH][n_qb][run_stride(topk)]  selection as runs [a, b) (LDS byte offsets), zero-padded
   int32_t* run_cnt;     // [BH][n_qb]
   float* state_m;       // [BH][n_qb][kStateX]   remaining (non-selected) state per query block
   float* o_lin;         // [BH][N][D]
@@ -57,5 +57,6 @@ hipError_t launch_fill_f32(float* dst, size_t n, float val, hipStream_t s);
 // dynamic LDS of the kernels that size it at run time
 size_t topk_lds_bytes(int n_kb);
 size_t gather_lds_bytes(int n_kb, int xw);
+int run_stride(int topk);
 
 }  // namespace sagesla

@@ -36,6 +36,9 @@ __global__ __launch_bounds__(256) void k4_prep_wp(const uint16_t* __restrict__ w
 
 __device__ __forceinline__ float phi_f(float x) { return x > 0.f ? x + 1.f : expf(x); }
 
+constexpr int kRunUnroll = 8;              // runs per gather step
+constexpr int kRunPad = 2 * kRunUnroll;    // zero runs after each row's last run: covers the next-step prefetch
+
 __global__ void k_fill_i32(int32_t* __restrict__ d, int n, int v) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) d[i] = v;
@@ -53,7 +56,8 @@ __device__ __forceinline__ int lds_off(int row, int key) {  // byte offset of (r
 
 __global__ __launch_bounds__(256) void k4_states(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                                                 const uint16_t* __restrict__ wpt, float* __restrict__ table,
-                                                int N, int n_kb, int xw, int n_xt) {
+                                                int N, int n_kb, int lxw, int n_xt) {
+  const int xw = 1 << lxw;
   __shared__ __attribute__((aligned(16))) unsigned char s_pkh[kD * 128];
   __shared__ __attribute__((aligned(16))) unsigned char s_pkl[kD * 128];
   __shared__ __attribute__((aligned(16))) unsigned char s_vt[kD * 128];
@@ -155,7 +159,7 @@ __global__ __launch_bounds__(256) void k4_states(const uint16_t* __restrict__ k,
     for (int r = 0; r < 16; ++r) {
       const int f = 32 * mt + 8 * (r >> 2) + 4 * g + (r & 3);
       const int x = f * kD + c;
-      tb[((size_t)(x / xw) * n_kb + J) * xw + (x % xw)] = acc2[mt][r];
+      tb[((size_t)(x >> lxw) * n_kb + J) * xw + (x & (xw - 1))] = acc2[mt][r];
     }
   }
   if (t < kD) {
@@ -163,23 +167,25 @@ __global__ __launch_bounds__(256) void k4_states(const uint16_t* __restrict__ k,
 #pragma unroll
     for (int j = 0; j < 16; ++j) z += s_z[j][t];
     const int x = kD * kD + t;
-    tb[((size_t)(x / xw) * n_kb + J) * xw + (x % xw)] = z;
+    tb[((size_t)(x >> lxw) * n_kb + J) * xw + (x & (xw - 1))] = z;
   }
 }
 
 // ---------------------------------------------------------------------------------------------------------
 // k4_runs: the selected blocks of each query block as runs of consecutive indices [a, b). One wave per
 // (bh, I) row. For any list (sorted or not) the sum over its elements equals the sum over these runs of
-// P[b] - P[a] with P the exclusive prefix sum over blocks; for the ascending selections there are only a
-// third as many runs as blocks on structured video inputs.
+// P[b] - P[a] with P the exclusive prefix sum over blocks; for the ascending selections of structured video
+// inputs there are about a third as many runs as blocks. Runs are stored as LDS byte offsets of rows a and b
+// in the gather kernel's prefix table (row stride xw floats).
 // ---------------------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(64) void k4_runs(const int32_t* __restrict__ idx, int2* __restrict__ runs,
-                                             int32_t* __restrict__ run_cnt, int n_kb, int topk, int rows) {
+                                             int32_t* __restrict__ run_cnt, int n_kb, int topk, int rstride,
+                                             int rows, int row_bytes) {
   const int row = blockIdx.x;
   if (row >= rows) return;
   const int l = threadIdx.x;
   const int32_t* in = idx + (size_t)row * topk;
-  int2* out = runs + (size_t)row * topk;
+  int2* out = runs + (size_t)row * rstride;
   int ns = 0, ne = 0;
   for (int j0 = 0; j0 < topk; j0 += 64) {
     const int j = j0 + l;
@@ -191,95 +197,147 @@ __global__ __launch_bounds__(64) void k4_runs(const int32_t* __restrict__ idx, i
     const bool en = ok && next != cur + 1;
     const unsigned long long ms = __ballot(st), me = __ballot(en);
     const unsigned long long lt = l ? (~0ull >> (64 - l)) : 0ull;
-    if (st) out[ns + __popcll(ms & lt)].x = cur;
-    if (en) out[ne + __popcll(me & lt)].y = cur + 1;
+    if (st) out[ns + __popcll(ms & lt)].x = cur * row_bytes;
+    if (en) out[ne + __popcll(me & lt)].y = (cur + 1) * row_bytes;
     ns += __popcll(ms);
     ne += __popcll(me);
   }
+  // zero runs after the last one: the gather reads up to kRunPad - 1 entries past the count
+  if (l < kRunPad) out[ns + l] = make_int2(0, 0);
   if (l == 0) run_cnt[row] = ns;
 }
 
 // ---------------------------------------------------------------------------------------------------------
-// k4_gather: grid (n_xt, BH), 1024 threads (16 waves); LDS = (n_kb + 1) * xw floats + 1024 partials.
+// k4_gather: grid (n_xt, BH), 1024 threads (16 waves). LDS: the prefix table (n_kb + 1) * xw floats and 1024
+// scan partials. xw is a power of two from 4 to 64 and divides the state size 16512.
 // The state tile of all key blocks (xw columns) is loaded into LDS and turned in place into its exclusive
-// prefix sum over blocks, P[0..n_kb] (P[n_kb] = the total over all blocks). Segments of the scan and their
-// combination have a fixed order, so the result is deterministic.
-// Each wave then serves 64/xw query blocks at once (lane = (query block sub, column xi)):
+// prefix sum over blocks, P[0..n_kb] (P[n_kb] = the total over all blocks); the scan segments and their
+// combination have a fixed order, so the result is deterministic. Each wave then serves ipw = 64/xw query
+// blocks at once, each lane covering 4 consecutive columns:
 //   H_m[x] = P[n_kb][x] - sum over the runs [a, b) of the query block's selection of (P[b][x] - P[a][x]).
+// Run offsets are read 8 at a time into registers (one broadcast address per query block) with the next 8
+// prefetched; run rows end in 8 zero runs, so these loads need no bounds test.
 // ---------------------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void k4_gather(const float* __restrict__ table, const int2* __restrict__ runs,
-                                                 const int32_t* __restrict__ run_cnt, float* __restrict__ state_m,
-                                                 int n_qb, int n_kb, int topk, int xw, int n_xt) {
+constexpr int kGatherThreads = 1024;
+
+__global__ __launch_bounds__(kGatherThreads) void k4_gather(const float* __restrict__ table,
+                                                           const int2* __restrict__ runs,
+                                                           const int32_t* __restrict__ run_cnt,
+                                                           float* __restrict__ state_m, int n_qb, int n_kb,
+                                                           int rstride, int xw, int n_xt) {
   extern __shared__ __attribute__((aligned(16))) float lds[];
-  float* P = lds;                          // [(n_kb + 1) * xw]
-  float* seg = lds + (size_t)(n_kb + 1) * xw;  // [1024]
+  float* P = lds;                              // [(n_kb + 1) * xw]
+  float* seg = lds + (size_t)(n_kb + 1) * xw;  // [kGatherThreads]
   const int xt = blockIdx.x, bh = blockIdx.y;
   const int t = threadIdx.x;
   const float* src = table + ((size_t)bh * n_xt + xt) * n_kb * xw;
   const int nflt = n_kb * xw;
-  for (int i = 4 * t; i < nflt; i += 4 * 1024) *(float4*)(P + i) = *(const float4*)(src + i);
+  for (int i = 4 * t; i < nflt; i += 4 * kGatherThreads) *(float4*)(P + i) = *(const float4*)(src + i);
   __syncthreads();
-  // exclusive prefix over blocks: thread (sg, xi) scans rows [j0, j1) of column xi
-  const int nseg = 1024 / xw, sg = t / xw, xi = t % xw;
-  const int per = (n_kb + nseg - 1) / nseg;
-  const int j0 = min(n_kb, sg * per), j1 = min(n_kb, j0 + per);
-  float run = 0.f;
-  for (int j = j0; j < j1; ++j) run += P[j * xw + xi];
-  seg[t] = run;
-  __syncthreads();
-  float off = 0.f;
-  for (int s2 = 0; s2 < sg; ++s2) off += seg[s2 * xw + xi];
-  for (int j = j0; j < j1; ++j) {
-    const float v = P[j * xw + xi];
-    P[j * xw + xi] = off;
-    off += v;
+  {  // exclusive prefix over blocks: thread (sg, xi) scans rows [j0, j1) of column xi
+    const int nseg = kGatherThreads / xw, sg = t / xw, xi = t % xw;
+    const int per = (n_kb + nseg - 1) / nseg;
+    const int j0 = min(n_kb, sg * per), j1 = min(n_kb, j0 + per);
+    float run = 0.f;
+    for (int j = j0; j < j1; ++j) run += P[j * xw + xi];
+    seg[t] = run;
+    __syncthreads();
+    float off = 0.f;
+    for (int s2 = 0; s2 < sg; ++s2) off += seg[s2 * xw + xi];
+    for (int j = j0; j < j1; ++j) {
+      const float v = P[j * xw + xi];
+      P[j * xw + xi] = off;
+      off += v;
+    }
+    if (sg == nseg - 1) P[n_kb * xw + xi] = off;  // empty trailing segments pass their offset on
+    __syncthreads();
   }
-  if (sg == nseg - 1) P[n_kb * xw + xi] = off;  // last segment ends at n_kb (empty segments pass their offset on)
-  __syncthreads();
 
+  // gather: lane = (query block sub, 4 consecutive columns col4), one 16-byte LDS read per run endpoint
   const int w = t >> 6, l = t & 63;
-  const int ipw = 64 / xw, sub = l / xw, col = l % xw;
-  const float total = P[n_kb * xw + col];
-  const int x = xt * xw + col;
-  const bool xok = x < kStateX;
-  for (int I0 = w * ipw; I0 < n_qb; I0 += 16 * ipw) {
+  const int lpr = xw >> 2;  // lanes per query block
+  const int ipw = 64 / lpr, sub = l / lpr, col4 = (l % lpr) * 4;
+  const unsigned char* Pb = (const unsigned char*)P + col4 * 4;
+  const float4 total = *(const float4*)(P + n_kb * xw + col4);
+  const int x = xt * xw + col4;
+  for (int I0 = w * ipw; I0 < n_qb; I0 += (kGatherThreads / 64) * ipw) {
     const int I = I0 + sub;
-    const bool iok = I < n_qb;
-    const size_t row = (size_t)bh * n_qb + (iok ? I : 0);
-    const int cnt = iok ? run_cnt[row] : 0;
-    const int2* rr = runs + row * topk;
-    float acc0 = 0.f, acc1 = 0.f;
-    int r = 0;
-    for (; r + 1 < cnt; r += 2) {
-      const int2 u = rr[r], v = rr[r + 1];
-      acc0 += P[u.y * xw + col] - P[u.x * xw + col];
-      acc1 += P[v.y * xw + col] - P[v.x * xw + col];
+    if (I < n_qb) {
+      const size_t row = (size_t)bh * n_qb + I;
+      const int cnt = run_cnt[row];
+      const int4* rr = (const int4*)(runs + row * rstride);  // two runs per int4; rows padded with zero runs
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+      int4 cur[kRunUnroll / 2], nxt[kRunUnroll / 2];
+#pragma unroll
+      for (int i = 0; i < kRunUnroll / 2; ++i) cur[i] = rr[i];
+      for (int r = 0; r < cnt; r += kRunUnroll) {  // r <= cnt - 1: the prefetch stays below cnt + kRunPad
+#pragma unroll
+        for (int i = 0; i < kRunUnroll / 2; ++i) nxt[i] = rr[(r + kRunUnroll) / 2 + i];
+#pragma unroll
+        for (int i = 0; i < kRunUnroll / 2; ++i) {  // zero runs add P[0] - P[0] = 0
+          const float4 b0 = *(const float4*)(Pb + cur[i].y), a0 = *(const float4*)(Pb + cur[i].x);
+          const float4 b1 = *(const float4*)(Pb + cur[i].w), a1 = *(const float4*)(Pb + cur[i].z);
+          acc.x += (b0.x - a0.x) + (b1.x - a1.x);
+          acc.y += (b0.y - a0.y) + (b1.y - a1.y);
+          acc.z += (b0.z - a0.z) + (b1.z - a1.z);
+          acc.w += (b0.w - a0.w) + (b1.w - a1.w);
+        }
+#pragma unroll
+        for (int i = 0; i < kRunUnroll / 2; ++i) cur[i] = nxt[i];
+      }
+      *(float4*)(state_m + row * kStateX + x) =
+          make_float4(total.x - acc.x, total.y - acc.y, total.z - acc.z, total.w - acc.w);
     }
-    if (r < cnt) {
-      const int2 u = rr[r];
-      acc0 += P[u.y * xw + col] - P[u.x * xw + col];
-    }
-    if (iok && xok) state_m[row * kStateX + x] = total - (acc0 + acc1);
   }
 }
 
 // ---------------------------------------------------------------------------------------------------------
-// k4_out: one workgroup per (bh, I) query block, BLKQ/32 waves; lane (i = l%32, half g) of wave w owns row
-// I*BLKQ + 32w + i. O^T[e][i] = sum_c Hm'^T[e][c] phi(Q)^T[c][i]: A = state rows (fp32 -> hi/lo), B = phi(q)
-// (fp32 -> hi/lo); hi*hi + hi*lo + lo*hi. den[i] = phi(q_i) . Z_m.
+// k4_out: one workgroup (4 waves) per (bh, I) query block. O^T[e][i] = sum_c Hm'^T[e][c] phi(Q)^T[c][i], then
+// divided by den[i] = phi(q_i) . Z_m. The block's remaining state is loaded once into LDS as bf16 hi and lo
+// planes ([e][c] rows of 256 B, 16-byte chunks XOR-swizzled by e); wave w computes phi(q) (hi + lo) for its own
+// 32 rows and all 128 output channels, reading the A operands from LDS. Products hi*hi + hi*lo + lo*hi keep
+// ~16 significant bits.
 // ---------------------------------------------------------------------------------------------------------
+__device__ __forceinline__ int out_off(int e, int c) {  // byte offset of (e, c) in one [128][128] bf16 plane
+  return e * 256 + ((((c >> 3) ^ e) & 15) << 4) + ((c & 7) << 1);
+}
+
 template <int BLKQ>
 __global__ __launch_bounds__(BLKQ * 2) void k4_out(const uint16_t* __restrict__ q, const float* __restrict__ state_m,
                                                   float* __restrict__ o_lin, int N, int n_qb, int total) {
+  constexpr int NT = BLKQ * 2;
+  __shared__ __attribute__((aligned(16))) unsigned char s_hi[kD * 256];
+  __shared__ __attribute__((aligned(16))) unsigned char s_lo[kD * 256];
+  __shared__ float s_z[kD];
   const int item = xcd_remap(blockIdx.x, total);
   const int bh = item / n_qb, I = item % n_qb;
   const int t = threadIdx.x, w = t >> 6, l = t & 63, g = l >> 5, lr = l & 31;
+  const float* sm = state_m + ((size_t)bh * n_qb + I) * kStateX;
+
+  // stage: 8 consecutive floats of one row e per thread per step
+  for (int u = t; u < kD * kD / 8; u += NT) {
+    const int e = u >> 4, c0 = (u & 15) * 8;
+    const float4 a0 = *(const float4*)(sm + e * kD + c0);
+    const float4 a1 = *(const float4*)(sm + e * kD + c0 + 4);
+    const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+    uint32_t hw[4], lw[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float h0, l0, h1, l1;
+      split_bf16(av[2 * i], h0, l0);
+      split_bf16(av[2 * i + 1], h1, l1);
+      hw[i] = pack_bf16x2(h0, h1);
+      lw[i] = pack_bf16x2(l0, l1);
+    }
+    *(uint4*)(s_hi + out_off(e, c0)) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+    *(uint4*)(s_lo + out_off(e, c0)) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+  }
+  if (t < kD) s_z[t] = sm[kD * kD + t];
+  __syncthreads();
+
   const int row = I * BLKQ + 32 * w + lr;
   const bool rok = row < N;
-  const float* sm = state_m + ((size_t)bh * n_qb + I) * kStateX;
   const uint16_t* qrow = q + ((size_t)bh * N + (rok ? row : 0)) * kD;
-
-  // phi(q) of this lane's channels 16s + 8g + 0..7, split, and the partial denominator
   v8bf bqh[8], bql[8];
   float den = 0.f;
 #pragma unroll
@@ -288,15 +346,12 @@ __global__ __launch_bounds__(BLKQ * 2) void k4_out(const uint16_t* __restrict__ 
     uint4 wq = make_uint4(0, 0, 0, 0);
     if (rok) wq = *(const uint4*)(qrow + c0);
     const uint32_t ww[4] = {wq.x, wq.y, wq.z, wq.w};
-    const float4 z0 = *(const float4*)(sm + kD * kD + c0);
-    const float4 z1 = *(const float4*)(sm + kD * kD + c0 + 4);
-    const float zz[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
     uint32_t hw[4], lw[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const float p0 = phi_f(bf16_lo(ww[u])), p1 = phi_f(bf16_hi(ww[u]));
-      den = fmaf(p0, zz[2 * u], den);
-      den = fmaf(p1, zz[2 * u + 1], den);
+      den = fmaf(p0, s_z[c0 + 2 * u], den);
+      den = fmaf(p1, s_z[c0 + 2 * u + 1], den);
       float h0, l0, h1, l1;
       split_bf16(p0, h0, l0);
       split_bf16(p1, h1, l1);
@@ -308,27 +363,15 @@ __global__ __launch_bounds__(BLKQ * 2) void k4_out(const uint16_t* __restrict__ 
   }
   den += swap_halves_f32(den);
   const float inv = 1.f / den;
-
 #pragma unroll
   for (int et = 0; et < 4; ++et) {
     v16f acc = {};
     const int e = 32 * et + lr;
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      const float4 a0 = *(const float4*)(sm + e * kD + 16 * s + 8 * g);
-      const float4 a1 = *(const float4*)(sm + e * kD + 16 * s + 8 * g + 4);
-      const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-      uint32_t hw[4], lw[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        float h0, l0, h1, l1;
-        split_bf16(av[2 * u], h0, l0);
-        split_bf16(av[2 * u + 1], h1, l1);
-        hw[u] = pack_bf16x2(h0, h1);
-        lw[u] = pack_bf16x2(l0, l1);
-      }
-      const v8bf ah = __builtin_bit_cast(v8bf, make_uint4(hw[0], hw[1], hw[2], hw[3]));
-      const v8bf al = __builtin_bit_cast(v8bf, make_uint4(lw[0], lw[1], lw[2], lw[3]));
+      const int off = out_off(e, 16 * s + 8 * g);
+      const v8bf ah = *(const v8bf*)(s_hi + off);
+      const v8bf al = *(const v8bf*)(s_lo + off);
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bqh[s], acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bql[s], acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bqh[s], acc, 0, 0, 0);
@@ -345,13 +388,16 @@ __global__ __launch_bounds__(BLKQ * 2) void k4_out(const uint16_t* __restrict__ 
   }
 }
 
-size_t gather_lds_bytes(int n_kb, int xw) { return ((size_t)(n_kb + 1) * xw + 1024) * sizeof(float); }
+int run_stride(int topk) { return ((topk + 1) & ~1) + kRunPad; }
+
+size_t gather_lds_bytes(int n_kb, int xw) { return ((size_t)(n_kb + 1) * xw + kGatherThreads) * sizeof(float); }
 
 hipError_t launch_linear(const Plan& p, const uint16_t* q, const uint16_t* k, const uint16_t* v, hipStream_t s) {
   hipLaunchKernelGGL(k4_prep_wp, dim3(kD * kD / 256), dim3(256), 0, s, (const uint16_t*)p.w_proj, p.wpt);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k4_states, dim3(p.n_kb, p.BH), dim3(256), 0, s, k, v, p.wpt, p.state, p.N, p.n_kb, p.state_xw,
+  const int lxw = __builtin_ctz(p.state_xw);
+  hipLaunchKernelGGL(k4_states, dim3(p.n_kb, p.BH), dim3(256), 0, s, k, v, p.wpt, p.state, p.N, p.n_kb, lxw,
                      p.n_state_xt);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const size_t lds = gather_lds_bytes(p.n_kb, p.state_xw);
@@ -363,13 +409,17 @@ hipError_t launch_linear(const Plan& p, const uint16_t* q, const uint16_t* k, co
   }
   const int rows = p.BH * p.n_qb;
   if (p.topk > 0) {
-    hipLaunchKernelGGL(k4_runs, dim3(rows), dim3(64), 0, s, p.block_idx, p.runs, p.run_cnt, p.n_kb, p.topk, rows);
-  } else {
+    hipLaunchKernelGGL(k4_runs, dim3(rows), dim3(64), 0, s, p.block_idx, p.runs, p.run_cnt, p.n_kb, p.topk,
+                       run_stride(p.topk), rows, p.state_xw * (int)sizeof(float));
+  } else {  // nothing selected: every row has zero runs (and its padding must still read as zero runs)
     hipLaunchKernelGGL(k_fill_i32, dim3((rows + 255) / 256), dim3(256), 0, s, p.run_cnt, rows, 0);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(k_fill_i32, dim3((rows * 2 * run_stride(0) + 255) / 256), dim3(256), 0, s, (int32_t*)p.runs,
+                       rows * 2 * run_stride(0), 0);
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(k4_gather, dim3(p.n_state_xt, p.BH), dim3(1024), lds, s, p.state, p.runs, p.run_cnt,
-                     p.state_m, p.n_qb, p.n_kb, p.topk, p.state_xw, p.n_state_xt);
+  hipLaunchKernelGGL(k4_gather, dim3(p.n_state_xt, p.BH), dim3(kGatherThreads), lds, s, p.state, p.runs, p.run_cnt,
+                     p.state_m, p.n_qb, p.n_kb, run_stride(p.topk), p.state_xw, p.n_state_xt);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int total = p.BH * p.n_qb;
   if (p.blk_q == 128)

@@ -12,10 +12,15 @@
 // row (lane % 32) and half of the block's 64 keys: row max and row sum are in-lane work plus one exchange
 // between the two 32-lane halves. P (bf16) then feeds O^T = V^T P^T (v_mfma_f32_32x32x16_bf16) directly from
 // registers; V^T is staged in LDS with its keys ordered to match P's register order (the quantize kernel writes
-// each key block's V^T once as a ready LDS image). K codes and the V^T image of the next selected block are
-// loaded straight into the idle LDS buffer (global_load_lds) while the current one is computed.
+// each key block's V^T once as a ready LDS image). K codes and V^T images move through two three-slot LDS rings
+// with direct global->LDS loads (global_load_lds) issued two iterations ahead, and each barrier waits only for
+// the loads of two iterations back; each iteration computes the next block's scores while it runs this block's
+// softmax, and the scheduler interleaves those MFMAs (and the PV MFMAs) with the softmax VALU work so the matrix
+// core and the vector ALU of a wave overlap.
 // Softmax rescaling is lazy: the running max moves only when a block's max exceeds it by more than 2^8, which
 // keeps every exp2 argument <= 8 and skips the O rescale for almost every block.
+#include <type_traits>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -32,62 +37,194 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 // Stage key block J into one LDS buffer with direct global->LDS loads (no registers, no VALU work):
 // the K codes land row-major with 16-byte chunks XOR-swizzled per row, the V^T image is copied verbatim
-// (it was written in its LDS layout by the quantize kernel). Rows past the end of a ragged block re-read the
-// last valid row; their scores are masked and their V^T columns are zero.
+// (it was written in its LDS layout by the quantize kernel). Each lane's source offsets inside a block are
+// fixed (koffs for K, (blk*64 + l)*16 for V), so a load is a uniform block base plus a lane offset.
 template <int NW>
-__device__ __forceinline__ void attn_stage(const int8_t* __restrict__ kb, const unsigned char* __restrict__ vimg,
-                                           int nv, unsigned char* sk, unsigned char* sv) {
+struct StageOffsets {
+  uint32_t k[AttnTile<NW>::KPW];
+};
+
+template <int NW>
+__device__ __forceinline__ StageOffsets<NW> stage_offsets(int nv) {
   using T = AttnTile<NW>;
+  StageOffsets<NW> so;
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
 #pragma unroll
   for (int i = 0; i < T::KPW; ++i) {
-    const int blk = w * T::KPW + i;
-    const int p = blk * 64 + l;  // 16-byte position in the LDS image
+    const int p = (w * T::KPW + i) * 64 + l;  // 16-byte position in the LDS image
     const int r = p >> 3, ch = (p & 7) ^ swz8(r);
-    const int8_t* src = kb + min(r, nv - 1) * kD + ch * 16;
-    __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(sk + blk * 1024), 16, 0, 0);
+    so.k[i] = (uint32_t)(min(r, nv - 1) * kD + ch * 16);  // rows past a ragged end re-read the last valid row
   }
+  return so;
+}
+
+// Buffer descriptor over one (b, h) slab: raw addressing (stride 0), gfx9 descriptor word 3. The tile loads
+// are buffer loads to LDS: a uniform block offset in an SGPR plus a per-lane offset.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t slab_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+template <int NW>
+__device__ __forceinline__ void stage_k(__amdgpu_buffer_rsrc_t rk, uint32_t blk_off, const StageOffsets<NW>& so,
+                                        unsigned char* sk) {
+  using T = AttnTile<NW>;
+  const int w = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < T::KPW; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(sk + (w * T::KPW + i) * 1024), 16, so.k[i], blk_off, 0,
+                                             0);
+}
+
+template <int NW>
+__device__ __forceinline__ void stage_v(__amdgpu_buffer_rsrc_t rv, uint32_t blk_off, unsigned char* sv) {
+  using T = AttnTile<NW>;
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
 #pragma unroll
   for (int i = 0; i < T::VPW; ++i) {
     const int blk = w * T::VPW + i;
-    __builtin_amdgcn_global_load_lds((const void*)(vimg + (blk * 64 + l) * 16), (lds_void*)(sv + blk * 1024), 16, 0,
-                                     0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(sv + blk * 1024), 16, (uint32_t)((blk * 64 + l) * 16),
+                                             blk_off, 0, 0);
   }
+}
+
+template <int NW>
+__device__ __forceinline__ void attn_stage(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, int J,
+                                           const StageOffsets<NW>& so, unsigned char* sk, unsigned char* sv) {
+  stage_k<NW>(rk, (uint32_t)J * (kBlkK * kD), so, sk);
+  stage_v<NW>(rv, (uint32_t)J * 16384u, sv);
+}
+
+// Wait until at most N of this wave's vector-memory loads are still in flight and its LDS reads have returned,
+// then meet the other waves of the workgroup. The direct-to-LDS loads of a wave complete in issue order, so the
+// tiles issued before the last N loads have landed in every wave's share once all waves pass the barrier. The
+// empty asm statements keep the compiler from moving LDS accesses across the barrier.
+// The wait goes through the builtin (s_waitcnt simm16: vmcnt in bits 3:0 and 15:14, expcnt 6:4 left at its
+// maximum, lgkmcnt 11:8 = 0) so that the compiler's own counter tracking knows which loads have completed.
+template <int N>
+__device__ __forceinline__ void ring_sync() {
+  static_assert(N >= 0 && N < 64, "vmcnt has six bits");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 __device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// One selected key block: S^T on INT8 MFMA, online softmax update, O^T += V^T P^T on BF16 MFMA.
-// Lane (row lr, half g) holds key 32tt + 8(r/4) + 4g + (r%4) of the block in s[tt][r].
-template <bool RAGGED>
-__device__ __forceinline__ void attn_block(const unsigned char* sk, const unsigned char* sv, const v4i* bq,
-                                           const int (&koff)[2][4], const int (&voff)[4][4], float c, int nv,
-                                           int g, v16f* o, float& m_run, float& l_run) {
-  v16i sacc[2];
+// Scores of one key block (S^T = K Q^T, 8 INT8 MFMAs into two 32-key tiles). The int32 accumulators start at
+// kMagic, the bit pattern of 1.5 * 2^23: since |S| <= 127*127*128 < 2^22, the sum read as a float is exactly
+// 1.5 * 2^23 + S, so no int-to-float conversion is needed.
+constexpr int kMagic = 0x4B400000;
+constexpr float kMagicF = 12582912.0f;
+
+__device__ __forceinline__ void attn_scores(const unsigned char* __restrict__ sk, const v4i* bq, const int (&koff)[2][4],
+                                            v16i (&sacc)[2]) {
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt) {
-    sacc[tt] = (v16i){};
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sacc[tt][r] = kMagic;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const v4i a = *(const v4i*)(sk + koff[tt][s]);
       sacc[tt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, bq[s], sacc[tt], 0, 0, 0);
     }
   }
-  int mx = INT_MIN;
+}
+
+// One pair of probabilities: p = exp2(S*c - m) for scores r, r+1 of a 32-key tile, packed to bf16 in PV
+// B-operand order; the row sum is taken over the same bf16 values the PV product uses. s holds kMagic + S.
+// FAST: t = fma(1.5*2^23 + S, c, -kc) with kc = fl(1.5*2^23*c + m), one instruction; kc's rounding shifts every
+// t of the block by the same amount, at most half an ulp of kc (<= 2^-11 for c < 2^-10). Otherwise
+// t = fma(S, c, -m) exactly as written. Ragged keys carry INT_MIN and get p = 0.
+template <bool RAGGED, bool FAST>
+__device__ __forceinline__ void attn_exp_pair(const v16i& s, int r, float c, float m, float kc, uint32_t& pk,
+                                              float& ps) {
+  const float x0 = __int_as_float(s[r]), x1 = __int_as_float(s[r + 1]);
+  float p0 = __builtin_amdgcn_exp2f(FAST ? fmaf(x0, c, -kc) : fmaf(x0 - kMagicF, c, -m));
+  float p1 = __builtin_amdgcn_exp2f(FAST ? fmaf(x1, c, -kc) : fmaf(x1 - kMagicF, c, -m));
+  if (RAGGED) {
+    p0 = s[r] == INT_MIN ? 0.f : p0;
+    p1 = s[r + 1] == INT_MIN ? 0.f : p1;
+  }
+  pk = pack_bf16x2(p0, p1);
+  ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2bf, pk), (v2bf){(__bf16)1.0f, (__bf16)1.0f}, ps, false);
+}
+
+// One selected key block j whose scores are in scur. With HAS_NEXT the scores of block j+1 (K codes in sk_next)
+// are computed into snext in the same pass. Lane (row lr, half g) holds key 32tt + 8(r/4) + 4g + (r%4) of the
+// block in scur[tt][r].
+//
+// The pass is written as a fixed sequence of slots, one MFMA each: first the 8 score MFMAs of the next block
+// (S^T tiles tt = 0, 1, steps s = 0..3), then the 16 PV MFMAs of this block (steps s = 0..3, tiles ct = 0..3).
+// Each slot also issues the LDS operand read of the MFMA four slots later and one pair of this block's exps,
+// which run four pairs ahead of the PV steps that consume them. Scheduling barriers between the slots keep the
+// compiler from collapsing the read-ahead distance.
+template <bool RAGGED, bool HAS_NEXT, bool FAST>
+__device__ __forceinline__ void attn_iter(const unsigned char* __restrict__ sk_next,
+                                          const unsigned char* __restrict__ sv, const v4i* bq,
+                                          const int (&koff)[2][4], const int (&voff)[4][4], float c, int nv, int g,
+                                          v16f* o, float& m_run, float& l_run, v16i (&scur)[2], v16i (&snext)[2]) {
+  constexpr int NK = HAS_NEXT ? 8 : 0;  // score MFMAs of the next block
+  constexpr int NS = NK + 16;           // MFMAs of the pass
+  constexpr int AHEAD = 4;              // operand reads run this many MFMAs ahead
+  v4i ka[8];
+  v8bf va[16];
+  uint32_t pw[16];
+  auto read = [&](int i) {
+    if (i < NK) {
+      ka[i] = *(const v4i*)(sk_next + koff[i >> 2][i & 3]);
+    } else {
+      const int v = i - NK;
+      va[v] = *(const v8bf*)(sv + voff[v & 3][v >> 2]);
+    }
+  };
+  auto mfma = [&](int i) {
+    if (i < NK) {
+      const int tt = i >> 2, st = i & 3;
+      const v16i acc = st == 0 ? (v16i){kMagic, kMagic, kMagic, kMagic, kMagic, kMagic, kMagic, kMagic, kMagic,
+                                        kMagic, kMagic, kMagic, kMagic, kMagic, kMagic, kMagic}
+                               : snext[tt];
+      snext[tt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ka[i], bq[st], acc, 0, 0, 0);
+    } else {
+      const int v = i - NK, st = v >> 2, ct = v & 3;
+      const v8bf b = __builtin_bit_cast(v8bf, make_uint4(pw[4 * st], pw[4 * st + 1], pw[4 * st + 2], pw[4 * st + 3]));
+      o[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[v], b, o[ct], 0, 0, 0);
+    }
+  };
+  // block max over 8 registers of one tile half, ragged keys masked to INT_MIN
+  auto part_max = [&](int q) {
+    const int tt = q >> 1;
+    int mq = INT_MIN;
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
+    for (int r = 8 * (q & 1); r < 8 * (q & 1) + 8; ++r) {
       if (RAGGED) {
         const int key = 32 * tt + 8 * (r >> 2) + 4 * g + (r & 3);
-        if (key >= nv) sacc[tt][r] = INT_MIN;
+        if (key >= nv) scur[tt][r] = INT_MIN;
       }
-      mx = max(mx, sacc[tt][r]);
+      mq = max(mq, scur[tt][r]);
     }
+    return mq;
+  };
+
+  // region 1: first operand reads; with a next block, its first four score MFMAs overlap the block max
+#pragma unroll
+  for (int i = 0; i < AHEAD; ++i) read(i);
+  int mx = INT_MIN;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    if (HAS_NEXT) {
+      __builtin_amdgcn_sched_barrier(0);
+      read(q + AHEAD);
+      mfma(q);
+    }
+    mx = max(mx, part_max(q));
+  }
   mx = max(mx, swap_halves_i32(mx));
-  const float mblk = (float)mx * c;
+  const float mblk = (float)(mx - kMagic) * c;
   const bool need = mblk > m_run + 8.f;
   if (__ballot(need)) {
+    // rare: keep it a real branch (the marker has side effects, so the body is never executed speculatively)
+    asm volatile("; rescale running max" ::: "memory");
     const float m_new = need ? mblk : m_run;
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     l_run *= alpha;
@@ -97,37 +234,20 @@ __device__ __forceinline__ void attn_block(const unsigned char* sk, const unsign
       for (int r = 0; r < 16; ++r) o[ct][r] *= alpha;
     m_run = m_new;
   }
-  // p = exp2(s*c - m), packed to bf16 pairs in the order of the PV B operand; the row sum is taken over the
-  // same bf16 values the PV product uses
-  uint32_t pw[2][8];
+
+  // region 2: slot k runs MFMA k, the read for MFMA k + AHEAD and exp pair k - NK + 4
+  const float kc = FAST ? fmaf(kMagicF, c, m_run) : 0.f;
   float ps = 0.f;
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-      float p0 = __builtin_amdgcn_exp2f(fmaf((float)sacc[tt][r], c, -m_run));
-      float p1 = __builtin_amdgcn_exp2f(fmaf((float)sacc[tt][r + 1], c, -m_run));
-      if (RAGGED) {
-        p0 = sacc[tt][r] == INT_MIN ? 0.f : p0;
-        p1 = sacc[tt][r + 1] == INT_MIN ? 0.f : p1;
-      }
-      const uint32_t pk = pack_bf16x2(p0, p1);
-      pw[tt][r >> 1] = pk;
-      ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2bf, pk), (v2bf){(__bf16)1.0f, (__bf16)1.0f}, ps,
-                                           false);
-    }
-  l_run += ps;
-  // O^T += V^T P^T: step s covers keys 16s..16s+15 = registers 8(s%2)..+7 of tile s/2
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    const uint32_t* p = pw[s >> 1] + 4 * (s & 1);
-    const v8bf b = __builtin_bit_cast(v8bf, make_uint4(p[0], p[1], p[2], p[3]));
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-      const v8bf a = *(const v8bf*)(sv + voff[ct][s]);
-      o[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, o[ct], 0, 0, 0);
-    }
+  for (int k = HAS_NEXT ? 4 : -4; k < NS; ++k) {
+    __builtin_amdgcn_sched_barrier(0);
+    if (k >= 0 && k + AHEAD < NS && k + AHEAD >= (HAS_NEXT ? 8 : AHEAD)) read(k + AHEAD);
+    if (k >= 0) mfma(k);
+    const int e = k - NK + 4;
+    if (e >= 0 && e < 16) attn_exp_pair<RAGGED, FAST>(scur[e >> 3], 2 * (e & 7), c, m_run, kc, pw[e], ps);
   }
+  __builtin_amdgcn_sched_barrier(0);
+  l_run += ps;
 }
 
 template <int NW>
@@ -137,8 +257,10 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k3_attn(
     const float* __restrict__ o_lin, uint16_t* __restrict__ out, int N, int n_qb, int n_kb, int topk, float c0,
     int total) {
   constexpr int BLKQ = 32 * NW;
-  __shared__ __attribute__((aligned(1024))) unsigned char s_k[2][64 * 128];
-  __shared__ __attribute__((aligned(1024))) unsigned char s_v[2][128 * 128];
+  // two rings of three slots: K codes (64 keys x 128 B) and V^T images (128 x 64 bf16). Each slot is its own
+  // LDS object so that the compiler can tell the slot being filled from the slots being read.
+  __shared__ __attribute__((aligned(1024))) unsigned char s_k0[64 * 128], s_k1[64 * 128], s_k2[64 * 128];
+  __shared__ __attribute__((aligned(1024))) unsigned char s_v0[128 * 128], s_v1[128 * 128], s_v2[128 * 128];
 
   const int item = xcd_remap(blockIdx.x, total);
   const int bh = item / n_qb, I = item % n_qb;
@@ -169,72 +291,146 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k3_attn(
       voff[ct][s] = vr * 128 + (((2 * s + g) ^ swz8(vr)) << 4);
     }
   const float cq = qs[(size_t)bh * n_qb + I] * c0;
-  const int32_t* irow = idx + ((size_t)bh * n_qb + I) * topk;
-  const int8_t* kbase = k8 + (size_t)bh * N * kD;
-  const unsigned char* vbase = vt + (size_t)bh * n_kb * 16384;
-  const float* ksrow = ks + (size_t)bh * n_kb;
+  // The selection list and the key scales do not change during this kernel: reading them through the constant
+  // address space lets the uniform reads use scalar loads, which do not count against the vector-memory
+  // counter that the tile ring waits on.
+  typedef __attribute__((address_space(4))) const int32_t c_i32;
+  typedef __attribute__((address_space(4))) const float c_f32;
+  c_i32* irow = (c_i32*)(idx + ((size_t)bh * n_qb + I) * topk);
+  // descriptors over this (b, h)'s K codes and V^T images; every tile offset stays below their sizes (rows past
+  // a ragged end re-read the last valid row)
+  const __amdgpu_buffer_rsrc_t rk = slab_rsrc(k8 + (size_t)bh * N * kD, (uint32_t)N * kD);
+  const __amdgpu_buffer_rsrc_t rv = slab_rsrc(vt + (size_t)bh * n_kb * 16384, (uint32_t)n_kb * 16384u);
+  c_f32* ksrow = (c_f32*)(ks + (size_t)bh * n_kb);
+  const int last_kb = n_kb - 1;
+  const int nv_last = N - last_kb * kBlkK;  // valid keys of the last key block (64 unless ragged)
+  const StageOffsets<NW> so_full = stage_offsets<NW>(kBlkK);
+  const StageOffsets<NW> so_last = stage_offsets<NW>(nv_last);
 
   v16f o[4];
 #pragma unroll
   for (int ct = 0; ct < 4; ++ct) o[ct] = (v16f){};
   float m_run = -INFINITY, l_run = 0.f;
 
+  auto blk = [&](int j) { return min(max(irow[j], 0), last_kb); };
   auto stage = [&](int j, int buf) {
-    const int J = min(max(irow[j], 0), n_kb - 1);
-    attn_stage<NW>(kbase + (size_t)J * kBlkK * kD, vbase + (size_t)J * 16384, min(kBlkK, N - J * kBlkK), s_k[buf],
-                   s_v[buf]);
+    const int J = blk(j);
+    attn_stage<NW>(rk, rv, J, J == last_kb ? so_last : so_full,
+                   buf ? s_k1 : s_k0, buf ? s_v1 : s_v0);
   };
-  auto finish = [&]() {
+  auto sync = [&]() {
     wait_vmem_all();
     __syncthreads();
   };
   if (topk > 0) {
-    // Only the last key block can be ragged. Ascending lists hold it last, so the main loop runs the full-block
-    // body only and the ragged block (if selected) is peeled; a caller-given list that places it elsewhere
-    // takes the generic loop.
-    const int last_kb = n_kb - 1;
-    const bool has_ragged = (N % kBlkK) != 0;
-    bool tail_ragged = false, elsewhere = false;
-    if (has_ragged) {
-      tail_ragged = min(max(irow[topk - 1], 0), last_kb) == last_kb;
-      for (int j = 0; j < topk - 1; ++j) elsewhere |= min(max(irow[j], 0), last_kb) == last_kb;
+    // Only the last key block can be ragged. Ascending lists hold it last, so every iteration but the last
+    // runs the full-block body; a caller-given list that places it elsewhere takes the generic loop.
+    // One pass over the list, a lane per entry: the largest key scale and whether the ragged block occurs
+    // before the end.
+    const bool has_ragged = nv_last != kBlkK;
+    float kmax = 0.f;
+    bool early_ragged = false;
+    for (int j = l; j < topk; j += 64) {
+      const int J = blk(j);
+      kmax = fmaxf(kmax, ksrow[J]);
+      early_ragged |= has_ragged && j < topk - 1 && J == last_kb;
     }
-    stage(0, 0);
-    finish();
-    if (!elsewhere) {
-      const int nfull = topk - (tail_ragged ? 1 : 0);
+    kmax = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(wave_max_f32(kmax))));
+    const bool elsewhere = __ballot(early_ragged) != 0;
+    const bool tail_ragged = has_ragged && blk(topk - 1) == last_kb;
+    // one-instruction exponent argument when every block's scale product is below 2^-10 (see attn_exp_pair)
+    const bool fast = cq * kmax < 0x1p-10f;
+    v16i scur[2], snext[2];
+    using T = AttnTile<NW>;
+    using i0 = std::integral_constant<int, 0>;
+    using i1 = std::integral_constant<int, 1>;
+    using i2 = std::integral_constant<int, 2>;
+    // K codes and V^T images travel in separate three-slot rings, each tile issued two iterations before its
+    // use: iteration j reads K[j+1] (scores of the next block) and V[j], and issues K[j+3] and V[j+2] into the
+    // slots that K[j] and V[j-1] leave free. The slots are distinct restrict-qualified pointers so that the
+    // compiler can tell the loads in flight from the LDS reads of the current tiles.
+    auto ring = [&](auto fastc, unsigned char* __restrict__ k0, unsigned char* __restrict__ k1,
+                    unsigned char* __restrict__ k2, unsigned char* __restrict__ v0, unsigned char* __restrict__ v1,
+                    unsigned char* __restrict__ v2) {
+      constexpr bool F = decltype(fastc)::value;
+      unsigned char* const ks[3] = {k0, k1, k2};
+      unsigned char* const vs[3] = {v0, v1, v2};
+      auto put_k = [&](int j, unsigned char* dst) {
+        const int J = blk(j);
+        stage_k<NW>(rk, (uint32_t)J * (kBlkK * kD), J == last_kb ? so_last : so_full, dst);
+      };
+      auto put_v = [&](int j, unsigned char* dst) { stage_v<NW>(rv, (uint32_t)blk(j) * 16384u, dst); };
+      put_k(0, k0);
+      if (topk > 1) put_k(1, k1);
+      if (topk > 2) put_k(2, k2);
+      put_v(0, v0);
+      if (topk > 1) put_v(1, v1);
+      ring_sync<0>();
+      attn_scores(k0, bq, koff, scur);
+      auto pick = [&](int r, unsigned char* x0, unsigned char* x1, unsigned char* x2) {
+        return r == 0 ? x0 : r == 1 ? x1 : x2;
+      };
+      // Iteration j < topk - 1 waits for K[j+1] and V[j], issued two iterations back (the loads of iteration
+      // j-1 may stay in flight), issues K[j+3] and V[j+2], then runs block j with the scores of block j+1.
+      // Steady state, ring phase P = j % 3 known at compile time, both tiles issued:
+      auto iter_full = [&](int j, auto ph) {
+        constexpr int P = decltype(ph)::value;
+        ring_sync<T::KPW + T::VPW>();
+        put_k(j + 3, ks[P]);
+        put_v(j + 2, vs[(P + 2) % 3]);
+        attn_iter<false, true, F>(ks[(P + 1) % 3], vs[P], bq, koff, voff, cq * ksrow[blk(j)], kBlkK, g, o, m_run,
+                                  l_run, scur, snext);
+        scur[0] = snext[0];
+        scur[1] = snext[1];
+      };
+      // the last few iterations before the final block: slots picked at run time, tiles issued while they exist
+      auto iter_tail = [&](int j) {
+        const int P = j % 3;
+        if (j + 2 < topk)
+          ring_sync<T::KPW + T::VPW>();
+        else
+          ring_sync<T::VPW>();
+        if (j + 3 < topk) put_k(j + 3, pick(P, k0, k1, k2));
+        if (j + 2 < topk) put_v(j + 2, pick(P == 0 ? 2 : P - 1, v0, v1, v2));
+        attn_iter<false, true, F>(pick(P == 2 ? 0 : P + 1, k0, k1, k2), pick(P, v0, v1, v2), bq, koff, voff,
+                                  cq * ksrow[blk(j)], kBlkK, g, o, m_run, l_run, scur, snext);
+        scur[0] = snext[0];
+        scur[1] = snext[1];
+      };
       int j = 0;
-      for (; j + 1 < nfull; j += 2) {
-        stage(j + 1, 1);
-        attn_block<false>(s_k[0], s_v[0], bq, koff, voff, cq * ksrow[min(max(irow[j], 0), last_kb)], kBlkK, g, o,
-                          m_run, l_run);
-        finish();
-        if (j + 2 < topk) stage(j + 2, 0);
-        attn_block<false>(s_k[1], s_v[1], bq, koff, voff, cq * ksrow[min(max(irow[j + 1], 0), last_kb)], kBlkK, g,
-                          o, m_run, l_run);
-        finish();
+      for (; j + 5 < topk; j += 3) {
+        iter_full(j, i0{});
+        iter_full(j + 1, i1{});
+        iter_full(j + 2, i2{});
       }
-      if (j < nfull) {  // odd count of full blocks: buffer 0 holds block j
-        if (j + 1 < topk) stage(j + 1, 1);
-        attn_block<false>(s_k[0], s_v[0], bq, koff, voff, cq * ksrow[min(max(irow[j], 0), last_kb)], kBlkK, g, o,
-                          m_run, l_run);
-        finish();
-        ++j;
-      }
-      if (tail_ragged) {
-        const int buf = j & 1;
-        attn_block<true>(s_k[buf], s_v[buf], bq, koff, voff, cq * ksrow[last_kb], N - last_kb * kBlkK, g, o,
-                         m_run, l_run);
-      }
-    } else {
+      for (; j < topk - 1; ++j) iter_tail(j);
+      // last block (j == topk - 1), no successor
+      ring_sync<0>();
+      const int ph = j % 3;
+      unsigned char* const vl = ph == 0 ? v0 : ph == 1 ? v1 : v2;
+      if (tail_ragged)
+        attn_iter<true, false, F>(nullptr, vl, bq, koff, voff, cq * ksrow[last_kb], nv_last, g, o, m_run, l_run,
+                                  scur, snext);
+      else
+        attn_iter<false, false, F>(nullptr, vl, bq, koff, voff, cq * ksrow[blk(j)], kBlkK, g, o, m_run, l_run,
+                                   scur, snext);
+    };
+    if (elsewhere) {
+      stage(0, 0);
+      sync();
       for (int j = 0; j < topk; ++j) {
         const int buf = j & 1;
         if (j + 1 < topk) stage(j + 1, buf ^ 1);
-        const int J = min(max(irow[j], 0), last_kb);
-        attn_block<true>(s_k[buf], s_v[buf], bq, koff, voff, cq * ksrow[J], min(kBlkK, N - J * kBlkK), g, o, m_run,
-                         l_run);
-        finish();
+        const int J = blk(j);
+        attn_scores(buf ? s_k1 : s_k0, bq, koff, scur);
+        attn_iter<true, false, false>(nullptr, buf ? s_v1 : s_v0, bq, koff, voff, cq * ksrow[J], min(kBlkK, N - J * kBlkK),
+                                      g, o, m_run, l_run, scur, snext);
+        sync();
       }
+    } else if (fast) {
+      ring(std::true_type{}, s_k0, s_k1, s_k2, s_v0, s_v1, s_v2);
+    } else {
+      ring(std::false_type{}, s_k0, s_k1, s_k2, s_v0, s_v1, s_v2);
     }
   }
 

@@ -9,7 +9,7 @@ namespace sagesla {
 
 constexpr int kD = 128;       // head dim (the only one supported)
 constexpr int kBlkK = 64;     // key block
-constexpr int kStateX = kD * kD + kD;  // floats per linear-branch state: H^T W_p (D×D, e-major) then Z (D)
+constexpr int kStateX = kD * kD + kD;  // floats per linear-branch state: H^T (D×D, e-major) then Z (D)
 
 // Everything a launch needs, resolved from the parameter block: sizes and where each intermediate lives
 // (a caller's export buffer or a slice of the workspace).

@@ -5,15 +5,16 @@
 // on the raw bf16 q and k, per key block J the state is H_J = phi(K_J)^T V_J (D×D) and Z_J = sum phi(K_J) (D);
 // the totals over all blocks are formed once and each query block subtracts its selected blocks' states:
 //   O_l[i] = phi(q_i) H_m / (phi(q_i) . Z_m),  H_m = sum_J H_J - sum_{J selected} H_J,  out += O_l W_p.
-// Because the projection is linear and the denominator is a scalar per row, O_l W_p = phi(q_i) (H_m W_p) / den,
-// so the projection is applied to each block state once (k4_states) instead of to each output row.
+// The projection is linear and the denominator is a scalar per row, so O_l W_p = (phi(q_i) H_m W_p) / den: the
+// per-block states and their gather stay in the D×D state space and W_p is applied once per query block, to the
+// product phi(Q_I) H_m, in the output kernel.
 //
 // Kernels:
 //   k4_prep_wp   W_p^T with the MFMA key-slot order, bf16 (32 KB, once per call)
-//   k4_states    per key block: (H_J W_p)^T and Z_J into a column-tiled table (MFMA, HBM-bound)
+//   k4_states    per key block: H_J^T and Z_J into a column-tiled table (MFMA, HBM-bound)
 //   k4_gather    per (b,h) and column tile: the tile of all blocks' states sits in LDS; totals once, then for
 //                every query block H_m = total - sum over its selected blocks (LDS-bound)
-//   k4_out       per query block: O_lin = phi(Q) H_m / (phi(Q) . Z_m) (MFMA)
+//   k4_out       per query block: O_lin = (phi(Q) H_m) W_p / (phi(Q) . Z_m) (MFMA)
 // fp32 values enter the bf16 MFMAs as hi + lo bf16 pairs, so every product keeps ~16 significant bits.
 #include "device_common.h"
 #include "internal.h"
@@ -34,7 +35,17 @@ __global__ __launch_bounds__(256) void k4_prep_wp(const uint16_t* __restrict__ w
   wpt[f * kD + p] = wp[i];
 }
 
-__device__ __forceinline__ float phi_f(float x) { return x > 0.f ? x + 1.f : expf(x); }
+// phi(x) = elu(x) + 1: x + 1 for x > 0, e^x otherwise (hardware exp2 of x log2(e); the values then enter the
+// MFMAs as hi + lo bf16 pairs, ~16 significant bits)
+__device__ __forceinline__ float phi_f(float x) {
+  return x > 0.f ? x + 1.f : __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
+}
+
+// two fp32 values -> bf16 pairs hi = bf16(x) and lo = bf16(x - hi), packed as (x0, x1)
+__device__ __forceinline__ void split2(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+  hi = pack_bf16x2(x0, x1);
+  lo = pack_bf16x2(x0 - __uint_as_float(hi << 16), x1 - __uint_as_float(hi & 0xffff0000u));
+}
 
 constexpr int kRunUnroll = 8;              // runs per gather step
 constexpr int kRunPad = 2 * kRunUnroll;    // zero runs after each row's last run: covers the next-step prefetch
@@ -47,16 +58,16 @@ __global__ void k_fill_i32(int32_t* __restrict__ d, int n, int v) {
 // ---------------------------------------------------------------------------------------------------------
 // k4_states: grid (n_kb, BH), 256 threads (4 waves).
 // LDS holds phi(K)^T (hi, lo) and V^T as [channel][key] bf16 rows of 128 B, 16-byte chunks XOR-swizzled.
-// Wave w computes H^T[e][c] for all e and c in [32w, 32w+32) (A = V^T, B = phi(K)), then
-// (H W_p)^T[f][c] = sum_e W_p^T[f][e] H^T[e][c] with H^T taken straight from its accumulator registers.
+// Wave w computes H^T[e][c] = sum_key v[e] phi(k)[c] for all e and c in [32w, 32w+32) (A = V^T, B = phi(K)).
+// Table column x = e*128 + c; tile (x >> lxw) holds xw consecutive columns of every block: since xw <= 128 divides
+// 128, the address of (e, c) is a per-lane part (c, J) plus e * 128 * n_kb floats.
 // ---------------------------------------------------------------------------------------------------------
 __device__ __forceinline__ int lds_off(int row, int key) {  // byte offset of (row, key) in a [128][64] bf16 tile
   return row * 128 + (((key >> 3) ^ swz8(row)) << 4) + ((key & 7) << 1);
 }
 
 __global__ __launch_bounds__(256) void k4_states(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-                                                const uint16_t* __restrict__ wpt, float* __restrict__ table,
-                                                int N, int n_kb, int lxw, int n_xt) {
+                                                float* __restrict__ table, int N, int n_kb, int lxw, int n_xt) {
   const int xw = 1 << lxw;
   __shared__ __attribute__((aligned(16))) unsigned char s_pkh[kD * 128];
   __shared__ __attribute__((aligned(16))) unsigned char s_pkl[kD * 128];
@@ -69,7 +80,7 @@ __global__ __launch_bounds__(256) void k4_states(const uint16_t* __restrict__ k,
   const int nv = min(kBlkK, N - J * kBlkK);
 
   // ---- load, phi, split, transpose into LDS
-  float pk[4][8], vv[4][8];
+  uint32_t kw[4][4], vw[4][4];
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
     const int r = 4 * kg + b;
@@ -78,28 +89,29 @@ __global__ __launch_bounds__(256) void k4_states(const uint16_t* __restrict__ k,
       a = *(const uint4*)(k + base + (size_t)r * kD + cg * 8);
       c = *(const uint4*)(v + base + (size_t)r * kD + cg * 8);
     }
-    const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, cw[4] = {c.x, c.y, c.z, c.w};
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      pk[b][2 * u] = bf16_lo(aw[u]);
-      pk[b][2 * u + 1] = bf16_hi(aw[u]);
-      vv[b][2 * u] = bf16_lo(cw[u]);
-      vv[b][2 * u + 1] = bf16_hi(cw[u]);
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) pk[b][e] = (r < nv) ? phi_f(pk[b][e]) : 0.f;
+    kw[b][0] = a.x; kw[b][1] = a.y; kw[b][2] = a.z; kw[b][3] = a.w;
+    vw[b][0] = c.x; vw[b][1] = c.y; vw[b][2] = c.z; vw[b][3] = c.w;
   }
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const int row = cg * 8 + e;
-    float h[4], lo[4];
+    float pk[4];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) split_bf16(pk[b][e], h[b], lo[b]);
+    for (int b = 0; b < 4; ++b) {
+      const float x = (e & 1) ? bf16_hi(kw[b][e >> 1]) : bf16_lo(kw[b][e >> 1]);
+      pk[b] = (4 * kg + b < nv) ? phi_f(x) : 0.f;
+    }
+    uint32_t h01, l01, h23, l23;
+    split2(pk[0], pk[1], h01, l01);
+    split2(pk[2], pk[3], h23, l23);
     const int off = lds_off(row, 4 * kg);
-    *(uint2*)(s_pkh + off) = make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
-    *(uint2*)(s_pkl + off) = make_uint2(pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]));
-    *(uint2*)(s_vt + off) = make_uint2(pack_bf16x2(vv[0][e], vv[1][e]), pack_bf16x2(vv[2][e], vv[3][e]));
-    s_z[kg][row] = (pk[0][e] + pk[1][e]) + (pk[2][e] + pk[3][e]);
+    *(uint2*)(s_pkh + off) = make_uint2(h01, h23);
+    *(uint2*)(s_pkl + off) = make_uint2(l01, l23);
+    // V^T: channel e of keys 4kg..4kg+3, bf16 bits moved as they are
+    const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+    *(uint2*)(s_vt + off) = make_uint2(__builtin_amdgcn_perm(vw[1][e >> 1], vw[0][e >> 1], sel),
+                                       __builtin_amdgcn_perm(vw[3][e >> 1], vw[2][e >> 1], sel));
+    s_z[kg][row] = (pk[0] + pk[1]) + (pk[2] + pk[3]);
   }
   __syncthreads();
 
@@ -121,53 +133,21 @@ __global__ __launch_bounds__(256) void k4_states(const uint16_t* __restrict__ k,
     }
   }
 
-  // ---- (H W_p)^T = W_p^T H^T: m = f (4 tiles), n = c (tile w), k = e (8 steps of 16)
-  // B operand slot (g, i) of step s2 is e = 16 s2 + 8(i/4) + 4g + i%4 = accumulator register 8(s2%2)+i of
-  // tile s2/2 in this lane; the A operand reads W_p^T rows in the matching permuted order.
-  v16f acc2[4];
+  // ---- store H^T[e][c]: lane part (c, J, half g), row part e * 128 * n_kb floats
+  const int c = crow;
+  const size_t estride = (size_t)kD * n_kb;  // floats between rows e and e+1 of the table
+  float* tl = table + (size_t)bh * n_xt * n_kb * xw + ((size_t)(c >> lxw) * n_kb + J) * xw + (c & (xw - 1)) +
+              (size_t)(4 * g) * estride;
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) acc2[mt] = (v16f){};
+  for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-  for (int s2 = 0; s2 < 8; ++s2) {
-    const int src = s2 >> 1, r0 = 8 * (s2 & 1);
-    uint32_t hw[4], lw[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      float h0, l0, h1, l1;
-      split_bf16(acc[src][r0 + 2 * u], h0, l0);
-      split_bf16(acc[src][r0 + 2 * u + 1], h1, l1);
-      hw[u] = pack_bf16x2(h0, h1);
-      lw[u] = pack_bf16x2(l0, l1);
-    }
-    const v8bf bhi = __builtin_bit_cast(v8bf, make_uint4(hw[0], hw[1], hw[2], hw[3]));
-    const v8bf blo = __builtin_bit_cast(v8bf, make_uint4(lw[0], lw[1], lw[2], lw[3]));
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      const int f = 32 * mt + lr;
-      const v8bf a = *(const v8bf*)(wpt + f * kD + 16 * s2 + 8 * g);
-      acc2[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bhi, acc2[mt], 0, 0, 0);
-      acc2[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, blo, acc2[mt], 0, 0, 0);
-    }
-  }
-
-  // ---- store: x = f*128 + c for (H W_p)^T[f][c]; x = 16384 + c for Z[c]
-  float* tb = table + (size_t)bh * n_xt * n_kb * xw;
-  const int c = 32 * w + lr;
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int f = 32 * mt + 8 * (r >> 2) + 4 * g + (r & 3);
-      const int x = f * kD + c;
-      tb[((size_t)(x >> lxw) * n_kb + J) * xw + (x & (xw - 1))] = acc2[mt][r];
-    }
-  }
+    for (int r = 0; r < 16; ++r) tl[(size_t)(32 * mt + 8 * (r >> 2) + (r & 3)) * estride] = acc[mt][r];
   if (t < kD) {
     float z = 0.f;
 #pragma unroll
     for (int j = 0; j < 16; ++j) z += s_z[j][t];
     const int x = kD * kD + t;
-    tb[((size_t)(x >> lxw) * n_kb + J) * xw + (x & (xw - 1))] = z;
+    table[(size_t)bh * n_xt * n_kb * xw + ((size_t)(x >> lxw) * n_kb + J) * xw + (x & (xw - 1))] = z;
   }
 }
 
@@ -292,11 +272,12 @@ __global__ __launch_bounds__(kGatherThreads) void k4_gather(const float* __restr
 }
 
 // ---------------------------------------------------------------------------------------------------------
-// k4_out: one workgroup (4 waves) per (bh, I) query block. O^T[e][i] = sum_c Hm'^T[e][c] phi(Q)^T[c][i], then
-// divided by den[i] = phi(q_i) . Z_m. The block's remaining state is loaded once into LDS as bf16 hi and lo
-// planes ([e][c] rows of 256 B, 16-byte chunks XOR-swizzled by e); wave w computes phi(q) (hi + lo) for its own
-// 32 rows and all 128 output channels, reading the A operands from LDS. Products hi*hi + hi*lo + lo*hi keep
-// ~16 significant bits.
+// k4_out: one workgroup (4 waves) per (bh, I) query block.
+//   U^T[e][i] = sum_c H_m^T[e][c] phi(Q)^T[c][i]        (A = H_m^T hi/lo from LDS, B = phi(Q) hi/lo in registers)
+//   O^T[f][i] = sum_e W_p^T[f][e] U^T[e][i] / den[i]     (A = W_p^T from LDS, B = U^T hi/lo from the accumulators)
+// with den[i] = phi(q_i) . Z_m. The block's remaining state is loaded once into LDS as bf16 hi and lo planes
+// ([e][c] rows of 256 B, 16-byte chunks XOR-swizzled by e); after the first product the hi plane's space takes
+// W_p^T. Wave w handles its own 32 rows. Products hi*hi + hi*lo + lo*hi keep ~16 significant bits.
 // ---------------------------------------------------------------------------------------------------------
 __device__ __forceinline__ int out_off(int e, int c) {  // byte offset of (e, c) in one [128][128] bf16 plane
   return e * 256 + ((((c >> 3) ^ e) & 15) << 4) + ((c & 7) << 1);
@@ -304,7 +285,8 @@ __device__ __forceinline__ int out_off(int e, int c) {  // byte offset of (e, c)
 
 template <int BLKQ>
 __global__ __launch_bounds__(BLKQ * 2) void k4_out(const uint16_t* __restrict__ q, const float* __restrict__ state_m,
-                                                  float* __restrict__ o_lin, int N, int n_qb, int total) {
+                                                  const uint16_t* __restrict__ wpt, float* __restrict__ o_lin, int N,
+                                                  int n_qb, int total) {
   constexpr int NT = BLKQ * 2;
   __shared__ __attribute__((aligned(16))) unsigned char s_hi[kD * 256];
   __shared__ __attribute__((aligned(16))) unsigned char s_lo[kD * 256];
@@ -319,16 +301,11 @@ __global__ __launch_bounds__(BLKQ * 2) void k4_out(const uint16_t* __restrict__ 
     const int e = u >> 4, c0 = (u & 15) * 8;
     const float4 a0 = *(const float4*)(sm + e * kD + c0);
     const float4 a1 = *(const float4*)(sm + e * kD + c0 + 4);
-    const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
     uint32_t hw[4], lw[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float h0, l0, h1, l1;
-      split_bf16(av[2 * i], h0, l0);
-      split_bf16(av[2 * i + 1], h1, l1);
-      hw[i] = pack_bf16x2(h0, h1);
-      lw[i] = pack_bf16x2(l0, l1);
-    }
+    split2(a0.x, a0.y, hw[0], lw[0]);
+    split2(a0.z, a0.w, hw[1], lw[1]);
+    split2(a1.x, a1.y, hw[2], lw[2]);
+    split2(a1.z, a1.w, hw[3], lw[3]);
     *(uint4*)(s_hi + out_off(e, c0)) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
     *(uint4*)(s_lo + out_off(e, c0)) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
   }
@@ -352,39 +329,68 @@ __global__ __launch_bounds__(BLKQ * 2) void k4_out(const uint16_t* __restrict__ 
       const float p0 = phi_f(bf16_lo(ww[u])), p1 = phi_f(bf16_hi(ww[u]));
       den = fmaf(p0, s_z[c0 + 2 * u], den);
       den = fmaf(p1, s_z[c0 + 2 * u + 1], den);
-      float h0, l0, h1, l1;
-      split_bf16(p0, h0, l0);
-      split_bf16(p1, h1, l1);
-      hw[u] = pack_bf16x2(h0, h1);
-      lw[u] = pack_bf16x2(l0, l1);
+      split2(p0, p1, hw[u], lw[u]);
     }
     bqh[s] = __builtin_bit_cast(v8bf, make_uint4(hw[0], hw[1], hw[2], hw[3]));
     bql[s] = __builtin_bit_cast(v8bf, make_uint4(lw[0], lw[1], lw[2], lw[3]));
   }
   den += swap_halves_f32(den);
   const float inv = 1.f / den;
+
+  // ---- U^T = H_m^T phi(Q)^T
+  v16f acc[4];
 #pragma unroll
   for (int et = 0; et < 4; ++et) {
-    v16f acc = {};
+    acc[et] = (v16f){};
     const int e = 32 * et + lr;
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       const int off = out_off(e, 16 * s + 8 * g);
       const v8bf ah = *(const v8bf*)(s_hi + off);
       const v8bf al = *(const v8bf*)(s_lo + off);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bqh[s], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bql[s], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bqh[s], acc, 0, 0, 0);
+      acc[et] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bqh[s], acc[et], 0, 0, 0);
+      acc[et] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bql[s], acc[et], 0, 0, 0);
+      acc[et] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bqh[s], acc[et], 0, 0, 0);
     }
-    if (rok) {
-      float* orow = o_lin + ((size_t)bh * N + row) * kD;
+  }
+  __syncthreads();  // every wave is done with the state planes
+  // W_p^T (bf16, rows f of 256 B, already in MFMA slot order along e) into the hi plane's space, same swizzle
+  for (int u = t; u < kD * kD / 8; u += NT) {
+    const int f = u >> 4, e0 = (u & 15) * 8;
+    *(uint4*)(s_hi + out_off(f, e0)) = *(const uint4*)(wpt + f * kD + e0);
+  }
+  __syncthreads();
+
+  // ---- O^T = W_p^T U^T: B operand slot (g, i) of step s2 is e = 16 s2 + 8(i/4) + 4g + i%4, i.e. accumulator
+  // register 8(s2%2) + i of tile s2/2 in this lane; W_p^T rows hold e in the matching permuted order.
+  v16f acc2[4];
+#pragma unroll
+  for (int ft = 0; ft < 4; ++ft) acc2[ft] = (v16f){};
+#pragma unroll
+  for (int s2 = 0; s2 < 8; ++s2) {
+    const int src = s2 >> 1, r0 = 8 * (s2 & 1);
+    uint32_t hw[4], lw[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) split2(acc[src][r0 + 2 * u], acc[src][r0 + 2 * u + 1], hw[u], lw[u]);
+    const v8bf bhi = __builtin_bit_cast(v8bf, make_uint4(hw[0], hw[1], hw[2], hw[3]));
+    const v8bf blo = __builtin_bit_cast(v8bf, make_uint4(lw[0], lw[1], lw[2], lw[3]));
+#pragma unroll
+    for (int ft = 0; ft < 4; ++ft) {
+      const v8bf a = *(const v8bf*)(s_hi + out_off(32 * ft + lr, 16 * s2 + 8 * g));
+      acc2[ft] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bhi, acc2[ft], 0, 0, 0);
+      acc2[ft] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, blo, acc2[ft], 0, 0, 0);
+    }
+  }
+  if (rok) {
+    float* orow = o_lin + ((size_t)bh * N + row) * kD;
+#pragma unroll
+    for (int ft = 0; ft < 4; ++ft)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        const int e0 = 32 * et + 8 * r4 + 4 * g;
-        *(float4*)(orow + e0) = make_float4(acc[4 * r4] * inv, acc[4 * r4 + 1] * inv, acc[4 * r4 + 2] * inv,
-                                            acc[4 * r4 + 3] * inv);
+        const int f0 = 32 * ft + 8 * r4 + 4 * g;
+        *(float4*)(orow + f0) = make_float4(acc2[ft][4 * r4] * inv, acc2[ft][4 * r4 + 1] * inv,
+                                            acc2[ft][4 * r4 + 2] * inv, acc2[ft][4 * r4 + 3] * inv);
       }
-    }
   }
 }
 
@@ -397,7 +403,7 @@ hipError_t launch_linear(const Plan& p, const uint16_t* q, const uint16_t* k, co
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int lxw = __builtin_ctz(p.state_xw);
-  hipLaunchKernelGGL(k4_states, dim3(p.n_kb, p.BH), dim3(256), 0, s, k, v, p.wpt, p.state, p.N, p.n_kb, lxw,
+  hipLaunchKernelGGL(k4_states, dim3(p.n_kb, p.BH), dim3(256), 0, s, k, v, p.state, p.N, p.n_kb, lxw,
                      p.n_state_xt);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const size_t lds = gather_lds_bytes(p.n_kb, p.state_xw);
@@ -423,9 +429,11 @@ hipError_t launch_linear(const Plan& p, const uint16_t* q, const uint16_t* k, co
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int total = p.BH * p.n_qb;
   if (p.blk_q == 128)
-    hipLaunchKernelGGL(k4_out<128>, dim3(total), dim3(256), 0, s, q, p.state_m, p.o_lin, p.N, p.n_qb, total);
+    hipLaunchKernelGGL(k4_out<128>, dim3(total), dim3(256), 0, s, q, p.state_m, p.wpt, p.o_lin, p.N, p.n_qb,
+                       total);
   else
-    hipLaunchKernelGGL(k4_out<64>, dim3(total), dim3(128), 0, s, q, p.state_m, p.o_lin, p.N, p.n_qb, total);
+    hipLaunchKernelGGL(k4_out<64>, dim3(total), dim3(128), 0, s, q, p.state_m, p.wpt, p.o_lin, p.N, p.n_qb,
+                       total);
   return hipGetLastError();
 }
 

@@ -38,7 +38,7 @@ typedef enum {
   SAGESLA_E_NULL = 1,        /* a required pointer is NULL                                              */
   SAGESLA_E_SHAPE = 2,       /* B, H or N < 1, B*H > 65535, topk outside [0, n_kb], sm_scale < 0 or NaN   */
   SAGESLA_E_UNSUPPORTED = 3, /* D != 128, blk_k != 64, blk_q not in {64, 128}, unknown flag bits,
-                                N > 2^24, n_kb > 20480, or (linear branch) n_kb > 9983                    */
+                                N > 2^24 or n_kb > 20480                                                  */
   SAGESLA_E_WORKSPACE = 4,   /* workspace smaller than sagesla_workspace_bytes()                         */
   SAGESLA_E_ALIGN = 5,       /* a pointer is not 16-byte aligned (workspace: 256-byte aligned)           */
   SAGESLA_E_HIP = 6          /* a HIP call or launch failed; sagesla_last_hip_error() holds its code     */

@@ -16,15 +16,8 @@ constexpr size_t kAlign = 256;
 constexpr int kColsumChunk = 512;
 constexpr int kMaxKeyBlocks = 20480;
 constexpr int kMaxN = 1 << 24;
-constexpr size_t kMaxLds = 160 * 1024;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
-
-int state_tile_width(int n_kb) {
-  for (int xw = 64; xw >= 4; xw >>= 1)
-    if (gather_lds_bytes(n_kb, xw) <= kMaxLds) return xw;
-  return 0;
-}
 
 bool misaligned(const void* ptr, size_t a) { return ptr && ((uintptr_t)ptr % a) != 0; }
 
@@ -40,8 +33,6 @@ sagesla_status check_shape(const sagesla_params* p) {
   if (n_kb > kMaxKeyBlocks) return SAGESLA_E_UNSUPPORTED;
   if (p->topk < 0 || p->topk > n_kb) return SAGESLA_E_SHAPE;
   if (!(isfinite(p->sm_scale) && p->sm_scale >= 0.f)) return SAGESLA_E_SHAPE;
-  const bool linear = (p->flags & SAGESLA_LINEAR) && p->topk < n_kb;
-  if (linear && state_tile_width(n_kb) == 0) return SAGESLA_E_UNSUPPORTED;
   return SAGESLA_OK;
 }
 
@@ -77,10 +68,6 @@ void make_plan(const sagesla_params* p, unsigned char* ws, Plan* pl) {
   pl->n_colsum_chunks = (p->N + kColsumChunk - 1) / kColsumChunk;
   pl->w_proj = p->w_proj;
   const bool lin_active = pl->linear && pl->topk < pl->n_kb;
-  if (lin_active) {
-    pl->state_xw = state_tile_width(pl->n_kb);
-    pl->n_state_xt = (kStateX + pl->state_xw - 1) / pl->state_xw;
-  }
   const size_t BH = pl->BH, N = pl->N, D = kD, nqb = pl->n_qb, nkb = pl->n_kb;
   size_t off = 0;
   auto take = [&](size_t bytes) -> unsigned char* {
@@ -101,9 +88,8 @@ void make_plan(const sagesla_params* p, unsigned char* ws, Plan* pl) {
   pl->block_idx = (int32_t*)take(BH * nqb * (size_t)pl->topk * sizeof(int32_t));
   if (lin_active) {
     pl->wpt = (uint16_t*)take(D * D * sizeof(uint16_t));
-    pl->state = (float*)take(BH * pl->n_state_xt * nkb * pl->state_xw * sizeof(float));
-    pl->runs = (int2*)take(BH * nqb * (size_t)run_stride(pl->topk) * sizeof(int2));
-    pl->run_cnt = (int32_t*)take(BH * nqb * sizeof(int32_t));
+    pl->state = (float*)take(BH * nkb * kStateX * sizeof(float));
+    pl->keep_mask = (uint32_t*)take(BH * nqb * (size_t)((nkb + 31) / 32) * sizeof(uint32_t));
     pl->state_m = (float*)take(BH * nqb * kStateX * sizeof(float));
     pl->o_lin = (float*)take(BH * N * D * sizeof(float));
   }

@@ -18,7 +18,6 @@ struct Plan {
   bool smooth, linear, given_mask;
   float sm_scale;
   int colsum_chunk, n_colsum_chunks;
-  int state_xw, n_state_xt;     // linear-branch state gather: columns per tile, number of tiles
   const void* w_proj;
   // intermediates
   double* colsum_part;  // [BH][n_colsum_chunks][D]
@@ -33,9 +32,8 @@ struct Plan {
   unsigned char* v_img; // [BH][n_kb][16384]    per key block: V^T in the attention kernel's LDS layout
   int32_t* block_idx;   // [BH][n_qb][topk]
   uint16_t* wpt;        // [D][D] bf16: W_p^T in MFMA slot order
-  float* state;         // [BH][n_state_xt][n_kb][state_xw]
-  int2* runs;           // [BH][n_qb][run_stride(topk)]  selection as runs [a, b) (LDS byte offsets), zero-padded
-  int32_t* run_cnt;     // [BH][n_qb]
+  float* state;         // [BH][kStateX / 32][n_kb][32]   per-block states, tiles of 32 columns
+  uint32_t* keep_mask;  // [BH][n_qb][ceil(n_kb/32)]   bit J set iff key block J is not selected
   float* state_m;       // [BH][n_qb][kStateX]   remaining (non-selected) state per query block
   float* o_lin;         // [BH][N][D]
   size_t ws_bytes;
@@ -48,7 +46,7 @@ hipError_t launch_quant(const Plan& p, const uint16_t* q, const uint16_t* k, con
 // K2: pooled block scores and top-k selection
 hipError_t launch_scores(const Plan& p, hipStream_t s);
 hipError_t launch_topk(const Plan& p, hipStream_t s);
-// K4: linear branch (block states, total-minus-selected gather, contraction with phi(Q))
+// K4: linear branch (block states, sum over the unselected blocks, contraction with phi(Q) and W_p)
 hipError_t launch_linear(const Plan& p, const uint16_t* q, const uint16_t* k, const uint16_t* v, hipStream_t s);
 // K3: block-sparse INT8 attention, epilogue adds the linear branch and writes bf16
 hipError_t launch_attn(const Plan& p, uint16_t* out, hipStream_t s);
@@ -56,7 +54,5 @@ hipError_t launch_attn(const Plan& p, uint16_t* out, hipStream_t s);
 hipError_t launch_fill_f32(float* dst, size_t n, float val, hipStream_t s);
 // dynamic LDS of the kernels that size it at run time
 size_t topk_lds_bytes(int n_kb);
-size_t gather_lds_bytes(int n_kb, int xw);
-int run_stride(int topk);
 
 }  // namespace sagesla

@@ -68,7 +68,7 @@ template <int NW>
 __device__ __forceinline__ void stage_k(__amdgpu_buffer_rsrc_t rk, uint32_t blk_off, const StageOffsets<NW>& so,
                                         unsigned char* sk) {
   using T = AttnTile<NW>;
-  const int w = threadIdx.x >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: LDS bases stay scalar
 #pragma unroll
   for (int i = 0; i < T::KPW; ++i)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(sk + (w * T::KPW + i) * 1024), 16, so.k[i], blk_off, 0,
@@ -78,12 +78,13 @@ __device__ __forceinline__ void stage_k(__amdgpu_buffer_rsrc_t rk, uint32_t blk_
 template <int NW>
 __device__ __forceinline__ void stage_v(__amdgpu_buffer_rsrc_t rv, uint32_t blk_off, unsigned char* sv) {
   using T = AttnTile<NW>;
-  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t lane_off = (threadIdx.x & 63) * 16;
 #pragma unroll
   for (int i = 0; i < T::VPW; ++i) {
-    const int blk = w * T::VPW + i;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(sv + blk * 1024), 16, (uint32_t)((blk * 64 + l) * 16),
-                                             blk_off, 0, 0);
+    const int blk = w * T::VPW + i;  // 1 KB piece of the image: uniform part in the scalar offset
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(sv + blk * 1024), 16, lane_off, blk_off + blk * 1024, 0,
+                                             0);
   }
 }
 

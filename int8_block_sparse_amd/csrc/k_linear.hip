@@ -12,8 +12,9 @@
 // Kernels:
 //   k4_prep_wp   W_p^T with the MFMA key-slot order, bf16 (32 KB, once per call)
 //   k4_states    per key block: H_J^T and Z_J into a column-tiled table (MFMA, HBM-bound)
-//   k4_gather    per (b,h) and column tile: the tile of all blocks' states sits in LDS; totals once, then for
-//                every query block H_m = total - sum over its selected blocks (LDS-bound)
+//   k4_mask      per query block: bitmask of the key blocks it did not select
+//   k4_gemm      H_m = sum of the states of the unselected blocks, as the dense product keep-mask x table
+//                (bf16 MFMA; about 90% of the mask is ones at 10% top-k)
 //   k4_out       per query block: O_lin = (phi(Q) H_m) W_p / (phi(Q) . Z_m) (MFMA)
 // fp32 values enter the bf16 MFMAs as hi + lo bf16 pairs, so every product keeps ~16 significant bits.
 #include "device_common.h"
@@ -45,14 +46,6 @@ __device__ __forceinline__ float phi_f(float x) {
 __device__ __forceinline__ void split2(float x0, float x1, uint32_t& hi, uint32_t& lo) {
   hi = pack_bf16x2(x0, x1);
   lo = pack_bf16x2(x0 - __uint_as_float(hi << 16), x1 - __uint_as_float(hi & 0xffff0000u));
-}
-
-constexpr int kRunUnroll = 8;              // runs per gather step
-constexpr int kRunPad = 2 * kRunUnroll;    // zero runs after each row's last run: covers the next-step prefetch
-
-__global__ void k_fill_i32(int32_t* __restrict__ d, int n, int v) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) d[i] = v;
 }
 
 // ---------------------------------------------------------------------------------------------------------
@@ -152,121 +145,205 @@ __global__ __launch_bounds__(256) void k4_states(const uint16_t* __restrict__ k,
 }
 
 // ---------------------------------------------------------------------------------------------------------
-// k4_runs: the selected blocks of each query block as runs of consecutive indices [a, b). One wave per
-// (bh, I) row. For any list (sorted or not) the sum over its elements equals the sum over these runs of
-// P[b] - P[a] with P the exclusive prefix sum over blocks; for the ascending selections of structured video
-// inputs there are about a third as many runs as blocks. Runs are stored as LDS byte offsets of rows a and b
-// in the gather kernel's prefix table (row stride xw floats).
+// k4_mask: one wave per (bh, I) row. Bit J of word J/32 is 1 iff query block I did not select key block J
+// (bits past n_kb are 0). Built in LDS with atomic ANDs, so an index that occurs twice clears its bit once, as
+// a set would.
 // ---------------------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(64) void k4_runs(const int32_t* __restrict__ idx, int2* __restrict__ runs,
-                                             int32_t* __restrict__ run_cnt, int n_kb, int topk, int rstride,
-                                             int rows, int row_bytes) {
-  const int row = blockIdx.x;
-  if (row >= rows) return;
-  const int l = threadIdx.x;
-  const int32_t* in = idx + (size_t)row * topk;
-  int2* out = runs + (size_t)row * rstride;
-  int ns = 0, ne = 0;
-  for (int j0 = 0; j0 < topk; j0 += 64) {
-    const int j = j0 + l;
-    const bool ok = j < topk;
-    const int cur = ok ? min(max(in[j], 0), n_kb - 1) : 0;
-    const int prev = (ok && j > 0) ? min(max(in[j - 1], 0), n_kb - 1) : -2;
-    const int next = (ok && j + 1 < topk) ? min(max(in[j + 1], 0), n_kb - 1) : -2;
-    const bool st = ok && cur != prev + 1;
-    const bool en = ok && next != cur + 1;
-    const unsigned long long ms = __ballot(st), me = __ballot(en);
-    const unsigned long long lt = l ? (~0ull >> (64 - l)) : 0ull;
-    if (st) out[ns + __popcll(ms & lt)].x = cur * row_bytes;
-    if (en) out[ne + __popcll(me & lt)].y = (cur + 1) * row_bytes;
-    ns += __popcll(ms);
-    ne += __popcll(me);
+constexpr int kMaskMaxWords = 640;  // 20480 key blocks
+
+__global__ __launch_bounds__(64) void k4_mask(const int32_t* __restrict__ idx, uint32_t* __restrict__ mask,
+                                             int n_kb, int topk, int n_kbw) {
+  __shared__ uint32_t m[kMaskMaxWords];
+  const int row = blockIdx.x, l = threadIdx.x;
+  for (int w = l; w < n_kbw; w += 64) {
+    const int left = n_kb - 32 * w;
+    m[w] = left >= 32 ? 0xffffffffu : ((1u << left) - 1u);
   }
-  // zero runs after the last one: the gather reads up to kRunPad - 1 entries past the count
-  if (l < kRunPad) out[ns + l] = make_int2(0, 0);
-  if (l == 0) run_cnt[row] = ns;
+  __syncthreads();
+  const int32_t* in = idx + (size_t)row * topk;
+  for (int j = l; j < topk; j += 64) {
+    const int J = min(max(in[j], 0), n_kb - 1);
+    atomicAnd(&m[J >> 5], ~(1u << (J & 31)));
+  }
+  __syncthreads();
+  uint32_t* out = mask + (size_t)row * n_kbw;
+  for (int w = l; w < n_kbw; w += 64) out[w] = m[w];
+}
+
+// 8 keep bits -> 8 bf16 (0 or 1.0), element i = bit i
+__device__ __forceinline__ uint4 expand_bits8(uint32_t b) {
+  uint32_t r[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t p = (b >> (2 * k)) & 3u;
+    r[k] = ((p & 1u) | ((p & 2u) << 15)) * 0x3F80u;
+  }
+  return make_uint4(r[0], r[1], r[2], r[3]);
 }
 
 // ---------------------------------------------------------------------------------------------------------
-// k4_gather: grid (n_xt, BH), 1024 threads (16 waves). LDS: the prefix table (n_kb + 1) * xw floats and 1024
-// scan partials. xw is a power of two from 4 to 64 and divides the state size 16512.
-// The state tile of all key blocks (xw columns) is loaded into LDS and turned in place into its exclusive
-// prefix sum over blocks, P[0..n_kb] (P[n_kb] = the total over all blocks); the scan segments and their
-// combination have a fixed order, so the result is deterministic. Each wave then serves ipw = 64/xw query
-// blocks at once, each lane covering 4 consecutive columns:
-//   H_m[x] = P[n_kb][x] - sum over the runs [a, b) of the query block's selection of (P[b][x] - P[a][x]).
-// Run offsets are read 8 at a time into registers (one broadcast address per query block) with the next 8
-// prefetched; run rows end in 8 zero runs, so these loads need no bounds test.
+// k4_gemm: C[I][x] = sum_J keep[I][J] H[J][x] over all key blocks J (keep = the k4_mask bits), for the state
+// columns x of the table (H^T then Z). D = A B with A = keep (I x J, exact 0/1 in bf16) and B = the table
+// (J x x) as hi + lo bf16, fp32 accumulation.
+// grid (kStateX / 128 column groups, ceil(n_qb / 640) query-block chunks, BH), 512 threads (8 waves).
+// Step = 32 key blocks (two MFMA k-steps of 16), one mask word per query block. At the start of step s the
+// workgroup issues buffer loads to LDS of the [32][128] fp32 table slice of step s+2 (4 column tiles of 32,
+// 4 KB contiguous each) and register loads of the mask words of step s+2; during step s the waves run its
+// MFMAs and build step s+1's fragments: B (hi, lo) from its staged slice, A from its mask words through a
+// 256-entry table that maps a mask byte to its 16-byte fragment (8 bf16 of 0 or 1.0). One wait for all loads
+// plus one barrier per step orders everything; every buffer is double and its own LDS object, so the compiler
+// can tell the buffers being filled from those being read.
+// Wave w owns query tiles 5 (w / 2) .. +4 and column tiles 2 (w % 2), +1: 10 output tiles of 32 x 32, each A
+// fragment feeding 4 MFMAs.
 // ---------------------------------------------------------------------------------------------------------
-constexpr int kGatherThreads = 1024;
+constexpr int kGemmIT = 20;  // query-block tiles of 32 per workgroup
+constexpr int kGemmThreads = 512;
 
-__global__ __launch_bounds__(kGatherThreads) void k4_gather(const float* __restrict__ table,
-                                                           const int2* __restrict__ runs,
-                                                           const int32_t* __restrict__ run_cnt,
-                                                           float* __restrict__ state_m, int n_qb, int n_kb,
-                                                           int rstride, int xw, int n_xt) {
-  extern __shared__ __attribute__((aligned(16))) float lds[];
-  float* P = lds;                              // [(n_kb + 1) * xw]
-  float* seg = lds + (size_t)(n_kb + 1) * xw;  // [kGatherThreads]
-  const int xt = blockIdx.x, bh = blockIdx.y;
-  const int t = threadIdx.x;
-  const float* src = table + ((size_t)bh * n_xt + xt) * n_kb * xw;
-  const int nflt = n_kb * xw;
-  for (int i = 4 * t; i < nflt; i += 4 * kGatherThreads) *(float4*)(P + i) = *(const float4*)(src + i);
-  __syncthreads();
-  {  // exclusive prefix over blocks: thread (sg, xi) scans rows [j0, j1) of column xi
-    const int nseg = kGatherThreads / xw, sg = t / xw, xi = t % xw;
-    const int per = (n_kb + nseg - 1) / nseg;
-    const int j0 = min(n_kb, sg * per), j1 = min(n_kb, j0 + per);
-    float run = 0.f;
-    for (int j = j0; j < j1; ++j) run += P[j * xw + xi];
-    seg[t] = run;
-    __syncthreads();
-    float off = 0.f;
-    for (int s2 = 0; s2 < sg; ++s2) off += seg[s2 * xw + xi];
-    for (int j = j0; j < j1; ++j) {
-      const float v = P[j * xw + xi];
-      P[j * xw + xi] = off;
-      off += v;
+__device__ __forceinline__ void gemm_wait_sync() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((0 & 15) | (7 << 4));  // vmcnt(0) lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+__global__ __launch_bounds__(kGemmThreads, 1) void k4_gemm(const float* __restrict__ table,
+                                                          const uint32_t* __restrict__ mask,
+                                                          float* __restrict__ state_m, int n_qb, int n_kb,
+                                                          int n_kbw) {
+  __shared__ __attribute__((aligned(1024))) uint4 s_a0[2 * kGemmIT * 64], s_a1[2 * kGemmIT * 64];  // [sub][tile][lane]
+  __shared__ __attribute__((aligned(1024))) float s_st0[4 * 32 * 32], s_st1[4 * 32 * 32];          // [tile][row][32]
+  __shared__ __attribute__((aligned(1024))) uint4 s_bh0[2 * 4 * 64], s_bh1[2 * 4 * 64];            // [sub][tile][lane]
+  __shared__ __attribute__((aligned(1024))) uint4 s_bl0[2 * 4 * 64], s_bl1[2 * 4 * 64];
+  __shared__ __attribute__((aligned(16))) uint4 s_lut[256];
+  constexpr int n_xt = kStateX / 32;
+  const int xg = blockIdx.x, ic = blockIdx.y, bh = blockIdx.z;
+  const int t = threadIdx.x, w = __builtin_amdgcn_readfirstlane(t >> 6), l = t & 63, g = l >> 5, lr = l & 31;
+  const int I0 = ic * kGemmIT * 32;
+  const int n_it = min(kGemmIT, (n_qb - I0 + 31) >> 5);
+  const int nss = n_kbw;  // steps of 32 key blocks
+  const __amdgpu_buffer_rsrc_t rt = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(table + (size_t)bh * n_xt * n_kb * 32), (short)0, n_xt * n_kb * 32 * 4, 0x00020000);
+  if (t < 256) s_lut[t] = expand_bits8(t);
+
+  // Mask words of step ss: thread t builds the 4 fragments (sub-step, half) of row t and one fragment of row
+  // 512 + t/4, so it loads those two rows' words (0 past the chunk or n_qb).
+  const int ra = t, rb = 512 + (t >> 2);
+  const bool aok = ra < n_it * 32 && I0 + ra < n_qb, bok = rb < n_it * 32 && I0 + rb < n_qb;
+  const uint32_t* mrow = mask + ((size_t)bh * n_qb + I0) * n_kbw;
+  auto mload = [&](int ss, uint32_t& m0, uint32_t& m1) {
+    m0 = (aok && ss < nss) ? mrow[(size_t)ra * n_kbw + ss] : 0u;
+    m1 = (bok && ss < nss) ? mrow[(size_t)rb * n_kbw + ss] : 0u;
+  };
+  // A fragments of one step in 3 pieces: row t sub-step 0, row t sub-step 1, one fragment of row 512 + t/4;
+  // fragment (row r, sub-step, half g') = lut[byte 2 sub + g' of the row's word]
+  auto build_a = [&](int piece, uint32_t m0, uint32_t m1, uint4* dst) {
+    if (piece < 2) {
+#pragma unroll
+      for (int gg = 0; gg < 2; ++gg)
+        dst[(piece * kGemmIT + (ra >> 5)) * 64 + gg * 32 + (ra & 31)] = s_lut[(m0 >> (16 * piece + 8 * gg)) & 0xffu];
+    } else {
+      const int sub = (t >> 1) & 1, gg = t & 1;
+      dst[(sub * kGemmIT + (rb >> 5)) * 64 + gg * 32 + (rb & 31)] = s_lut[(m1 >> (16 * sub + 8 * gg)) & 0xffu];
     }
-    if (sg == nseg - 1) P[n_kb * xw + xi] = off;  // empty trailing segments pass their offset on
-    __syncthreads();
+  };
+  // table slice of step ss: column tile xt = w / 2, rows 32 ss + 16 (w % 2) .. +15 (clamped to n_kb - 1; the
+  // mask is 0 there), 8 rows per 1 KB load
+  auto dma_st = [&](int ss, float* dst) {
+    const int xt = w >> 1;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int row = 32 * ss + 16 * (w & 1) + 8 * h + (l >> 3);
+      const uint32_t off = (uint32_t)((((4 * xg + xt) * n_kb + min(row, n_kb - 1)) * 32 + (l & 7) * 4) * 4);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rt, (__attribute__((address_space(3))) void*)(dst + xt * 1024 + (16 * (w & 1) + 8 * h) * 32),
+                                               16, off, 0, 0, 0);
+    }
+  };
+  // B fragments of one step from a staging slice, in 2 pieces (sub-steps): thread = (column tile t>>7, half h,
+  // lane l) -> rows 16 sub + 8 g + 4 h .. +3 of column lr
+  auto build_b = [&](int sub, const float* __restrict__ st, uint4* bh_, uint4* bl_) {
+    const int xt = t >> 7, h = (t >> 6) & 1;
+    const float* c = st + xt * 1024 + (16 * sub + 8 * g + 4 * h) * 32 + lr;
+    uint32_t h01, l01, h23, l23;
+    split2(c[0], c[32], h01, l01);
+    split2(c[64], c[96], h23, l23);
+    const int fi = (sub * 4 + xt) * 64 + l;
+    ((uint2*)&bh_[fi])[h] = make_uint2(h01, h23);
+    ((uint2*)&bl_[fi])[h] = make_uint2(l01, l23);
+  };
+
+  // wave w: query tiles 5 (w / 2) .. +4, column tiles 2 (w % 2), +1; acc[2 q + c]
+  const int wit = 5 * (w >> 1), wxt = 2 * (w & 1);
+  v16f acc[10];
+#pragma unroll
+  for (int k = 0; k < 10; ++k) acc[k] = (v16f){};
+
+  // one step with static buffers
+  uint32_t mc0, mc1, mn0, mn1;  // mask words of the step being built / being loaded
+  auto step = [&](int ss, const uint4* __restrict__ A, const uint4* __restrict__ Bh, const uint4* __restrict__ Bl,
+                  const float* __restrict__ st_next, uint4* a_next, uint4* bh_next, uint4* bl_next, float* st_fill) {
+    gemm_wait_sync();  // slice ss+1 and words ss+1 landed; A(ss), B(ss) built; the buffers filled below are free
+    mc0 = mn0;
+    mc1 = mn1;
+    if (ss + 2 < nss) dma_st(ss + 2, st_fill);
+    mload(ss + 2, mn0, mn1);
+    const uint4* Aw = A + wit * 64 + l;
+    // 10 slots (sub, q): A fragment of tile wit + q read two slots ahead; 4 MFMAs (2 column tiles x hi/lo)
+    v8bf af[10];
+    v8bf bhi[2][2], blo[2][2];
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        bhi[sub][c] = __builtin_bit_cast(v8bf, Bh[(sub * 4 + wxt + c) * 64 + l]);
+        blo[sub][c] = __builtin_bit_cast(v8bf, Bl[(sub * 4 + wxt + c) * 64 + l]);
+      }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) af[i] = __builtin_bit_cast(v8bf, Aw[(i / 5) * (kGemmIT * 64) + (i % 5) * 64]);
+#pragma unroll
+    for (int i = 0; i < 10; ++i) {  // tiles past n_it hold stale data, never stored
+      __builtin_amdgcn_sched_barrier(0);
+      const int sub = i / 5, q = i % 5;
+      if (i + 2 < 10) af[i + 2] = __builtin_bit_cast(v8bf, Aw[((i + 2) / 5) * (kGemmIT * 64) + ((i + 2) % 5) * 64]);
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        acc[2 * q + c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bhi[sub][c], acc[2 * q + c], 0, 0, 0);
+        acc[2 * q + c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], blo[sub][c], acc[2 * q + c], 0, 0, 0);
+      }
+      // fragments of step ss+1 (past the end: unused)
+      if (i == 2 || i == 7) build_b(i / 5, st_next, bh_next, bl_next);
+      if (i == 1 || i == 4 || i == 8) build_a(i == 1 ? 0 : i == 4 ? 1 : 2, mc0, mc1, a_next);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // prologue: slices 0 and 1, words 0 and 1; fragments of step 0
+  dma_st(0, s_st0);
+  if (nss > 1) dma_st(1, s_st1);
+  mload(0, mc0, mc1);
+  mload(1, mn0, mn1);
+  gemm_wait_sync();
+  build_b(0, s_st0, s_bh0, s_bl0);
+  build_b(1, s_st0, s_bh0, s_bl0);
+#pragma unroll
+  for (int piece = 0; piece < 3; ++piece) build_a(piece, mc0, mc1, s_a0);
+  for (int ss = 0; ss < nss; ss += 2) {
+    step(ss, s_a0, s_bh0, s_bl0, s_st1, s_a1, s_bh1, s_bl1, s_st0);
+    if (ss + 1 < nss) step(ss + 1, s_a1, s_bh1, s_bl1, s_st0, s_a0, s_bh0, s_bl0, s_st1);
   }
 
-  // gather: lane = (query block sub, 4 consecutive columns col4), one 16-byte LDS read per run endpoint
-  const int w = t >> 6, l = t & 63;
-  const int lpr = xw >> 2;  // lanes per query block
-  const int ipw = 64 / lpr, sub = l / lpr, col4 = (l % lpr) * 4;
-  const unsigned char* Pb = (const unsigned char*)P + col4 * 4;
-  const float4 total = *(const float4*)(P + n_kb * xw + col4);
-  const int x = xt * xw + col4;
-  for (int I0 = w * ipw; I0 < n_qb; I0 += (kGatherThreads / 64) * ipw) {
-    const int I = I0 + sub;
-    if (I < n_qb) {
-      const size_t row = (size_t)bh * n_qb + I;
-      const int cnt = run_cnt[row];
-      const int4* rr = (const int4*)(runs + row * rstride);  // two runs per int4; rows padded with zero runs
-      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-      int4 cur[kRunUnroll / 2], nxt[kRunUnroll / 2];
+  // store: acc[2q + c][r] is C[I][x] with I = I0 + 32 (wit + q) + 8(r/4) + 4g + r%4, x = xg*128 + 32 (wxt + c) + lr
 #pragma unroll
-      for (int i = 0; i < kRunUnroll / 2; ++i) cur[i] = rr[i];
-      for (int r = 0; r < cnt; r += kRunUnroll) {  // r <= cnt - 1: the prefetch stays below cnt + kRunPad
+  for (int q = 0; q < 5; ++q) {
+    if (wit + q < n_it) {
 #pragma unroll
-        for (int i = 0; i < kRunUnroll / 2; ++i) nxt[i] = rr[(r + kRunUnroll) / 2 + i];
+      for (int c = 0; c < 2; ++c) {
+        const int x = xg * 128 + 32 * (wxt + c) + lr;
 #pragma unroll
-        for (int i = 0; i < kRunUnroll / 2; ++i) {  // zero runs add P[0] - P[0] = 0
-          const float4 b0 = *(const float4*)(Pb + cur[i].y), a0 = *(const float4*)(Pb + cur[i].x);
-          const float4 b1 = *(const float4*)(Pb + cur[i].w), a1 = *(const float4*)(Pb + cur[i].z);
-          acc.x += (b0.x - a0.x) + (b1.x - a1.x);
-          acc.y += (b0.y - a0.y) + (b1.y - a1.y);
-          acc.z += (b0.z - a0.z) + (b1.z - a1.z);
-          acc.w += (b0.w - a0.w) + (b1.w - a1.w);
+        for (int r = 0; r < 16; ++r) {
+          const int I = I0 + 32 * (wit + q) + 8 * (r >> 2) + 4 * g + (r & 3);
+          if (I < n_qb) state_m[((size_t)bh * n_qb + I) * kStateX + x] = acc[2 * q + c][r];
         }
-#pragma unroll
-        for (int i = 0; i < kRunUnroll / 2; ++i) cur[i] = nxt[i];
       }
-      *(float4*)(state_m + row * kStateX + x) =
-          make_float4(total.x - acc.x, total.y - acc.y, total.z - acc.z, total.w - acc.w);
     }
   }
 }
@@ -394,38 +471,17 @@ __global__ __launch_bounds__(BLKQ * 2) void k4_out(const uint16_t* __restrict__ 
   }
 }
 
-int run_stride(int topk) { return ((topk + 1) & ~1) + kRunPad; }
-
-size_t gather_lds_bytes(int n_kb, int xw) { return ((size_t)(n_kb + 1) * xw + kGatherThreads) * sizeof(float); }
-
 hipError_t launch_linear(const Plan& p, const uint16_t* q, const uint16_t* k, const uint16_t* v, hipStream_t s) {
   hipLaunchKernelGGL(k4_prep_wp, dim3(kD * kD / 256), dim3(256), 0, s, (const uint16_t*)p.w_proj, p.wpt);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int lxw = __builtin_ctz(p.state_xw);
-  hipLaunchKernelGGL(k4_states, dim3(p.n_kb, p.BH), dim3(256), 0, s, k, v, p.state, p.N, p.n_kb, lxw,
-                     p.n_state_xt);
+  hipLaunchKernelGGL(k4_states, dim3(p.n_kb, p.BH), dim3(256), 0, s, k, v, p.state, p.N, p.n_kb, 5, kStateX / 32);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const size_t lds = gather_lds_bytes(p.n_kb, p.state_xw);
-  static bool attr_set = false;  // raising the dynamic-LDS cap is idempotent; racing first calls are harmless
-  if (!attr_set) {
-    e = hipFuncSetAttribute((const void*)k4_gather, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
-  const int rows = p.BH * p.n_qb;
-  if (p.topk > 0) {
-    hipLaunchKernelGGL(k4_runs, dim3(rows), dim3(64), 0, s, p.block_idx, p.runs, p.run_cnt, p.n_kb, p.topk,
-                       run_stride(p.topk), rows, p.state_xw * (int)sizeof(float));
-  } else {  // nothing selected: every row has zero runs (and its padding must still read as zero runs)
-    hipLaunchKernelGGL(k_fill_i32, dim3((rows + 255) / 256), dim3(256), 0, s, p.run_cnt, rows, 0);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(k_fill_i32, dim3((rows * 2 * run_stride(0) + 255) / 256), dim3(256), 0, s, (int32_t*)p.runs,
-                       rows * 2 * run_stride(0), 0);
-  }
+  const int rows = p.BH * p.n_qb, n_kbw = (p.n_kb + 31) / 32;
+  hipLaunchKernelGGL(k4_mask, dim3(rows), dim3(64), 0, s, p.block_idx, p.keep_mask, p.n_kb, p.topk, n_kbw);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(k4_gather, dim3(p.n_state_xt, p.BH), dim3(kGatherThreads), lds, s, p.state, p.runs, p.run_cnt,
-                     p.state_m, p.n_qb, p.n_kb, run_stride(p.topk), p.state_xw, p.n_state_xt);
+  hipLaunchKernelGGL(k4_gemm, dim3(kStateX / 128, (p.n_qb + kGemmIT * 32 - 1) / (kGemmIT * 32), p.BH),
+                     dim3(kGemmThreads), 0, s, p.state, p.keep_mask, p.state_m, p.n_qb, p.n_kb, n_kbw);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int total = p.BH * p.n_qb;
   if (p.blk_q == 128)

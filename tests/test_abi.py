@@ -120,11 +120,13 @@ def test_workspace_bytes(lib):
     assert 0 < lib.sagesla_workspace_bytes(ctypes.byref(cfg_dense.params())) < n
     bad = sg.Config(B=1, H=1, N=100, D=64)
     assert lib.sagesla_workspace_bytes(ctypes.byref(bad.params())) == 0
-    # the linear branch's LDS-resident state tile limits the key-block count
+    # key-block count: up to 20480 with or without the linear branch
     big = sg.Config(B=1, H=1, N=64 * 12000, topk=10, linear=True)
-    assert lib.sagesla_validate(ctypes.byref(big.params(w_proj=FAKE))) == 3
+    assert lib.sagesla_validate(ctypes.byref(big.params(w_proj=FAKE))) == 0
     big.linear = False
     assert lib.sagesla_validate(ctypes.byref(big.params())) == 0
+    huge = sg.Config(B=1, H=1, N=64 * 20481, topk=10, linear=True)
+    assert lib.sagesla_validate(ctypes.byref(huge.params(w_proj=FAKE))) == 3
 
 
 def test_topk_blocks_matches_flag_reading():

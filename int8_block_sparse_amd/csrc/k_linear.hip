@@ -28,12 +28,17 @@ __device__ __forceinline__ int slot_pos16(int off) {  // off = index within the 
   return (off & 3) | ((off & 4) << 1) | ((off & 8) >> 1);
 }
 
-// W_p^T, positions permuted as above: wpt[f][p], p = slot_pos16 applied within each 16 of e.
+// A [128][128] bf16 plane as the output kernel keeps it in LDS (and the remaining state is stored): rows of
+// 256 B, 16-byte chunks XOR-swizzled by row. Byte offset of (row, col):
+__device__ __forceinline__ int out_off(int e, int c) { return e * 256 + ((((c >> 3) ^ e) & 15) << 4) + ((c & 7) << 1); }
+
+// W_p^T, positions permuted as above: wpt[f][p], p = slot_pos16 applied within each 16 of e, in the swizzled
+// plane layout (a straight copy into LDS)
 __global__ __launch_bounds__(256) void k4_prep_wp(const uint16_t* __restrict__ wp, uint16_t* __restrict__ wpt) {
   const int i = blockIdx.x * 256 + threadIdx.x;  // 16384 elements
   const int e = i >> 7, f = i & 127;             // wp[e][f]
   const int p = (e & ~15) | slot_pos16(e & 15);
-  wpt[f * kD + p] = wp[i];
+  wpt[out_off(f, p) >> 1] = wp[i];
 }
 
 // phi(x) = elu(x) + 1: x + 1 for x > 0, e^x otherwise (hardware exp2 of x log2(e); the values then enter the
@@ -331,18 +336,52 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k4_gemm(const float* __restri
     if (ss + 1 < nss) step(ss + 1, s_a1, s_bh1, s_bl1, s_st0, s_a0, s_bh0, s_bl0, s_st1);
   }
 
-  // store: acc[2q + c][r] is C[I][x] with I = I0 + 32 (wit + q) + 8(r/4) + 4g + r%4, x = xg*128 + 32 (wxt + c) + lr
+  // Store. acc[2q + c][r] is C[I][x] with I = I0 + 32 (wit + q) + 8(r/4) + 4g + r%4, x = 128 xg + 32 (wxt + c) + lr.
+  // Column group xg < 128 is row e = xg of H_m^T: written as the bf16 hi and lo plane rows (out_off layout) of
+  // each query block's state record [hi plane 32 KB][lo plane 32 KB][Z fp32 512 B]; five rounds, one query
+  // tile per wave pair, go through LDS so that every store is a contiguous 16 B piece of a plane row.
+  // Column group 128 is Z, stored as fp32.
+  unsigned char* const sm_bytes = (unsigned char*)state_m;
+  constexpr size_t kRec = (size_t)kStateX * 4;  // bytes per query block
+  if (xg == kD) {
 #pragma unroll
-  for (int q = 0; q < 5; ++q) {
-    if (wit + q < n_it) {
+    for (int q = 0; q < 5; ++q)
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const int x = xg * 128 + 32 * (wxt + c) + lr;
+      for (int c = 0; c < 2; ++c)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int I = I0 + 32 * (wit + q) + 8 * (r >> 2) + 4 * g + (r & 3);
-          if (I < n_qb) state_m[((size_t)bh * n_qb + I) * kStateX + x] = acc[2 * q + c][r];
+          if (wit + q < n_it && I < n_qb)
+            *(float*)(sm_bytes + ((size_t)bh * n_qb + I) * kRec + 65536 + 4 * (32 * (wxt + c) + lr)) = acc[2 * q + c][r];
         }
+    return;
+  }
+  float* const half0 = (float*)s_a0;  // [128 rows][64 cols] fp32: columns 0-63
+  float* const half1 = (float*)s_a1;  //                          columns 64-127
+#pragma unroll
+  for (int q = 0; q < 5; ++q) {
+    __syncthreads();  // the step buffers (first round) / the previous round's staging are free
+    float* hw_ = (w & 1) ? half1 : half0;
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) hw_[(32 * (w >> 1) + 8 * (r >> 2) + 4 * g + (r & 3)) * 64 + 32 * c + lr] = acc[2 * q + c][r];
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {  // 128 rows x 16 chunks of 8 columns
+      const int u = t + kGemmThreads * j, row = u >> 4, k8 = u & 15;
+      const int it = 5 * (row >> 5) + q, I = I0 + 32 * it + (row & 31);
+      const float* src = (k8 < 8 ? half0 : half1) + row * 64 + 8 * (k8 & 7);
+      const float4 x0 = *(const float4*)src, x1 = *(const float4*)(src + 4);
+      uint32_t hi[4], lo[4];
+      split2(x0.x, x0.y, hi[0], lo[0]);
+      split2(x0.z, x0.w, hi[1], lo[1]);
+      split2(x1.x, x1.y, hi[2], lo[2]);
+      split2(x1.z, x1.w, hi[3], lo[3]);
+      if (it < n_it && I < n_qb) {
+        unsigned char* rec = sm_bytes + ((size_t)bh * n_qb + I) * kRec + out_off(xg, 8 * k8);
+        *(uint4*)rec = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+        *(uint4*)(rec + 32768) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
       }
     }
   }
@@ -352,42 +391,38 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k4_gemm(const float* __restri
 // k4_out: one workgroup (4 waves) per (bh, I) query block.
 //   U^T[e][i] = sum_c H_m^T[e][c] phi(Q)^T[c][i]        (A = H_m^T hi/lo from LDS, B = phi(Q) hi/lo in registers)
 //   O^T[f][i] = sum_e W_p^T[f][e] U^T[e][i] / den[i]     (A = W_p^T from LDS, B = U^T hi/lo from the accumulators)
-// with den[i] = phi(q_i) . Z_m. The block's remaining state is loaded once into LDS as bf16 hi and lo planes
-// ([e][c] rows of 256 B, 16-byte chunks XOR-swizzled by e); after the first product the hi plane's space takes
-// W_p^T. Wave w handles its own 32 rows. Products hi*hi + hi*lo + lo*hi keep ~16 significant bits.
+// with den[i] = phi(q_i) . Z_m. The block's remaining state arrives as bf16 hi and lo planes already in the LDS
+// layout (k4_gemm wrote them so): buffer loads to LDS bring them in while phi(Q) is formed; after the first
+// product the hi plane's space takes W_p^T the same way. Wave w handles its own 32 rows. Products
+// hi*hi + hi*lo + lo*hi keep ~16 significant bits.
 // ---------------------------------------------------------------------------------------------------------
-__device__ __forceinline__ int out_off(int e, int c) {  // byte offset of (e, c) in one [128][128] bf16 plane
-  return e * 256 + ((((c >> 3) ^ e) & 15) << 4) + ((c & 7) << 1);
-}
-
 template <int BLKQ>
 __global__ __launch_bounds__(BLKQ * 2) void k4_out(const uint16_t* __restrict__ q, const float* __restrict__ state_m,
                                                   const uint16_t* __restrict__ wpt, float* __restrict__ o_lin, int N,
                                                   int n_qb, int total) {
-  constexpr int NT = BLKQ * 2;
-  __shared__ __attribute__((aligned(16))) unsigned char s_hi[kD * 256];
-  __shared__ __attribute__((aligned(16))) unsigned char s_lo[kD * 256];
+  constexpr int NW = BLKQ / 32;
+  __shared__ __attribute__((aligned(1024))) unsigned char s_hi[kD * 256];
+  __shared__ __attribute__((aligned(1024))) unsigned char s_lo[kD * 256];
   __shared__ float s_z[kD];
   const int item = xcd_remap(blockIdx.x, total);
   const int bh = item / n_qb, I = item % n_qb;
-  const int t = threadIdx.x, w = t >> 6, l = t & 63, g = l >> 5, lr = l & 31;
-  const float* sm = state_m + ((size_t)bh * n_qb + I) * kStateX;
-
-  // stage: 8 consecutive floats of one row e per thread per step
-  for (int u = t; u < kD * kD / 8; u += NT) {
-    const int e = u >> 4, c0 = (u & 15) * 8;
-    const float4 a0 = *(const float4*)(sm + e * kD + c0);
-    const float4 a1 = *(const float4*)(sm + e * kD + c0 + 4);
-    uint32_t hw[4], lw[4];
-    split2(a0.x, a0.y, hw[0], lw[0]);
-    split2(a0.z, a0.w, hw[1], lw[1]);
-    split2(a1.x, a1.y, hw[2], lw[2]);
-    split2(a1.z, a1.w, hw[3], lw[3]);
-    *(uint4*)(s_hi + out_off(e, c0)) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-    *(uint4*)(s_lo + out_off(e, c0)) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+  const int t = threadIdx.x, w = __builtin_amdgcn_readfirstlane(t >> 6), l = t & 63, g = l >> 5, lr = l & 31;
+  const size_t rec = ((size_t)bh * n_qb + I) * (size_t)kStateX * 4;
+  const unsigned char* srec = (const unsigned char*)state_m + rec;  // [hi plane 32 KB][lo plane 32 KB][Z fp32]
+  float4 zv = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (t < kD / 4) zv = *(const float4*)(srec + 65536 + 16 * t);  // issued before the plane loads: waited alone
+  {  // the planes: 64 buffer loads of 1 KB straight into LDS
+    const __amdgpu_buffer_rsrc_t rb =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(srec), (short)0, kStateX * 4, 0x00020000);
+#pragma unroll
+    for (int i = 0; i < 64 / NW; ++i) {
+      const int k = w + NW * i;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (__attribute__((address_space(3))) void*)((k < 32 ? s_hi : s_lo) + (k & 31) * 1024),
+                                               16, l * 16, k * 1024, 0, 0);
+    }
   }
-  if (t < kD) s_z[t] = sm[kD * kD + t];
-  __syncthreads();
+  if (t < kD / 4) *(float4*)(s_z + 4 * t) = zv;
+  __syncthreads();  // s_z
 
   const int row = I * BLKQ + 32 * w + lr;
   const bool rok = row < N;
@@ -412,6 +447,8 @@ __global__ __launch_bounds__(BLKQ * 2) void k4_out(const uint16_t* __restrict__ 
     bql[s] = __builtin_bit_cast(v8bf, make_uint4(lw[0], lw[1], lw[2], lw[3]));
   }
   den += swap_halves_f32(den);
+  __builtin_amdgcn_s_waitcnt(7 << 4);  // vmcnt(0) lgkmcnt(0): this wave's plane loads have landed
+  __syncthreads();                      // ... and every other wave's
   const float inv = 1.f / den;
 
   // ---- U^T = H_m^T phi(Q)^T
@@ -431,10 +468,14 @@ __global__ __launch_bounds__(BLKQ * 2) void k4_out(const uint16_t* __restrict__ 
     }
   }
   __syncthreads();  // every wave is done with the state planes
-  // W_p^T (bf16, rows f of 256 B, already in MFMA slot order along e) into the hi plane's space, same swizzle
-  for (int u = t; u < kD * kD / 8; u += NT) {
-    const int f = u >> 4, e0 = (u & 15) * 8;
-    *(uint4*)(s_hi + out_off(f, e0)) = *(const uint4*)(wpt + f * kD + e0);
+  {  // W_p^T (already in the plane layout) into the hi plane's space: 32 loads of 1 KB
+    const __amdgpu_buffer_rsrc_t rw =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(wpt), (short)0, kD * kD * 2, 0x00020000);
+#pragma unroll
+    for (int i = 0; i < 32 / NW; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (__attribute__((address_space(3))) void*)(s_hi + (w + NW * i) * 1024),
+                                               16, l * 16, (w + NW * i) * 1024, 0, 0);
+    __builtin_amdgcn_s_waitcnt(7 << 4);
   }
   __syncthreads();
 

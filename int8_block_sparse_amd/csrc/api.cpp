@@ -89,7 +89,7 @@ void make_plan(const sagesla_params* p, unsigned char* ws, Plan* pl) {
   if (lin_active) {
     pl->wpt = (uint16_t*)take(D * D * sizeof(uint16_t));
     pl->state = (float*)take(BH * nkb * kStateX * sizeof(float));
-    pl->keep_mask = (uint32_t*)take(BH * nqb * (size_t)((nkb + 31) / 32) * sizeof(uint32_t));
+    pl->keep_mask = (uint32_t*)take(BH * (size_t)mask_row_pad(pl->n_qb) * ((nkb + 31) / 32) * sizeof(uint32_t));
     pl->state_m = (float*)take(BH * nqb * kStateX * sizeof(float));
     pl->o_lin = (float*)take(BH * N * D * sizeof(float));
   }

@@ -33,7 +33,7 @@ struct Plan {
   int32_t* block_idx;   // [BH][n_qb][topk]
   uint16_t* wpt;        // [D][D] bf16: W_p^T in MFMA slot order
   float* state;         // [BH][kStateX / 32][n_kb][32]   per-block states, tiles of 32 columns
-  uint32_t* keep_mask;  // [BH][n_qb][ceil(n_kb/32)]   bit J set iff key block J is not selected
+  uint32_t* keep_mask;  // [BH][ceil(n_kb/32)][mask_row_pad(n_qb)]   bit J set iff key block J is not selected
   float* state_m;       // [BH][n_qb][kStateX]   remaining (non-selected) state per query block
   float* o_lin;         // [BH][N][D]
   size_t ws_bytes;
@@ -54,5 +54,7 @@ hipError_t launch_attn(const Plan& p, uint16_t* out, hipStream_t s);
 hipError_t launch_fill_f32(float* dst, size_t n, float val, hipStream_t s);
 // dynamic LDS of the kernels that size it at run time
 size_t topk_lds_bytes(int n_kb);
+// query-block rows of the keep mask, padded for the linear-branch product's chunks
+int mask_row_pad(int n_qb);
 
 }  // namespace sagesla

@@ -152,14 +152,15 @@ __global__ __launch_bounds__(256) void k4_states(const uint16_t* __restrict__ k,
 // ---------------------------------------------------------------------------------------------------------
 // k4_mask: one wave per (bh, I) row. Bit J of word J/32 is 1 iff query block I did not select key block J
 // (bits past n_kb are 0). Built in LDS with atomic ANDs, so an index that occurs twice clears its bit once, as
-// a set would.
+// a set would. Stored word-major per head, mask[bh][word][I] with rows padded to qpad, so that one word of a
+// run of query blocks is contiguous.
 // ---------------------------------------------------------------------------------------------------------
 constexpr int kMaskMaxWords = 640;  // 20480 key blocks
 
 __global__ __launch_bounds__(64) void k4_mask(const int32_t* __restrict__ idx, uint32_t* __restrict__ mask,
-                                             int n_kb, int topk, int n_kbw) {
+                                             int n_qb, int n_kb, int topk, int n_kbw, int qpad) {
   __shared__ uint32_t m[kMaskMaxWords];
-  const int row = blockIdx.x, l = threadIdx.x;
+  const int row = blockIdx.x, l = threadIdx.x, bh = row / n_qb, I = row % n_qb;
   for (int w = l; w < n_kbw; w += 64) {
     const int left = n_kb - 32 * w;
     m[w] = left >= 32 ? 0xffffffffu : ((1u << left) - 1u);
@@ -171,8 +172,7 @@ __global__ __launch_bounds__(64) void k4_mask(const int32_t* __restrict__ idx, u
     atomicAnd(&m[J >> 5], ~(1u << (J & 31)));
   }
   __syncthreads();
-  uint32_t* out = mask + (size_t)row * n_kbw;
-  for (int w = l; w < n_kbw; w += 64) out[w] = m[w];
+  for (int w = l; w < n_kbw; w += 64) mask[((size_t)bh * n_kbw + w) * qpad + I] = m[w];
 }
 
 // 8 keep bits -> 8 bf16 (0 or 1.0), element i = bit i
@@ -191,18 +191,20 @@ __device__ __forceinline__ uint4 expand_bits8(uint32_t b) {
 // columns x of the table (H^T then Z). D = A B with A = keep (I x J, exact 0/1 in bf16) and B = the table
 // (J x x) as hi + lo bf16, fp32 accumulation.
 // grid (kStateX / 128 column groups, ceil(n_qb / 640) query-block chunks, BH), 512 threads (8 waves).
-// Step = 32 key blocks (two MFMA k-steps of 16), one mask word per query block. At the start of step s the
+// Step = 32 key blocks (two MFMA k-steps of 16) = one mask word per query block. At the start of step s the
 // workgroup issues buffer loads to LDS of the [32][128] fp32 table slice of step s+2 (4 column tiles of 32,
-// 4 KB contiguous each) and register loads of the mask words of step s+2; during step s the waves run its
-// MFMAs and build step s+1's fragments: B (hi, lo) from its staged slice, A from its mask words through a
-// 256-entry table that maps a mask byte to its 16-byte fragment (8 bf16 of 0 or 1.0). One wait for all loads
-// plus one barrier per step orders everything; every buffer is double and its own LDS object, so the compiler
-// can tell the buffers being filled from those being read.
+// 4 KB contiguous each) and of the chunk's 640 mask words of step s+1; during step s the waves run its MFMAs
+// and rebuild slice s+1 into B fragments (hi, lo). Each wave forms its own A operands in registers: the byte
+// of its row's mask word for (sub-step, lane half) becomes 8 bf16 through two reads of a 16-entry nibble table
+// kept in 32 lane-private copies (conflict-free). One wait for all loads plus one barrier per step orders
+// everything; every buffer is double and its own LDS object, so the compiler can tell the buffers being filled
+// from those being read.
 // Wave w owns query tiles 5 (w / 2) .. +4 and column tiles 2 (w % 2), +1: 10 output tiles of 32 x 32, each A
-// fragment feeding 4 MFMAs.
+// operand feeding 4 MFMAs.
 // ---------------------------------------------------------------------------------------------------------
 constexpr int kGemmIT = 20;  // query-block tiles of 32 per workgroup
 constexpr int kGemmThreads = 512;
+constexpr int kGemmRows = kGemmIT * 32;  // query blocks per workgroup; mask rows are padded to a multiple
 
 __device__ __forceinline__ void gemm_wait_sync() {
   asm volatile("" ::: "memory");
@@ -214,42 +216,35 @@ __device__ __forceinline__ void gemm_wait_sync() {
 __global__ __launch_bounds__(kGemmThreads, 1) void k4_gemm(const float* __restrict__ table,
                                                           const uint32_t* __restrict__ mask,
                                                           float* __restrict__ state_m, int n_qb, int n_kb,
-                                                          int n_kbw) {
-  __shared__ __attribute__((aligned(1024))) uint4 s_a0[2 * kGemmIT * 64], s_a1[2 * kGemmIT * 64];  // [sub][tile][lane]
-  __shared__ __attribute__((aligned(1024))) float s_st0[4 * 32 * 32], s_st1[4 * 32 * 32];          // [tile][row][32]
-  __shared__ __attribute__((aligned(1024))) uint4 s_bh0[2 * 4 * 64], s_bh1[2 * 4 * 64];            // [sub][tile][lane]
+                                                          int n_kbw, int qpad) {
+  __shared__ __attribute__((aligned(1024))) float s_st0[4 * 32 * 32], s_st1[4 * 32 * 32];  // [tile][row][32]
+  __shared__ __attribute__((aligned(1024))) uint4 s_bh0[2 * 4 * 64], s_bh1[2 * 4 * 64];    // [sub][tile][lane]
   __shared__ __attribute__((aligned(1024))) uint4 s_bl0[2 * 4 * 64], s_bl1[2 * 4 * 64];
-  __shared__ __attribute__((aligned(16))) uint4 s_lut[256];
+  __shared__ __attribute__((aligned(1024))) uint32_t s_w0[kGemmRows + 128], s_w1[kGemmRows + 128];  // mask words
+  __shared__ __attribute__((aligned(1024))) uint2 s_nib[16 * 32];  // [nibble][copy]: 4 bf16 of 0 / 1.0
   constexpr int n_xt = kStateX / 32;
   const int xg = blockIdx.x, ic = blockIdx.y, bh = blockIdx.z;
   const int t = threadIdx.x, w = __builtin_amdgcn_readfirstlane(t >> 6), l = t & 63, g = l >> 5, lr = l & 31;
-  const int I0 = ic * kGemmIT * 32;
+  const int I0 = ic * kGemmRows;
   const int n_it = min(kGemmIT, (n_qb - I0 + 31) >> 5);
   const int nss = n_kbw;  // steps of 32 key blocks
   const __amdgpu_buffer_rsrc_t rt = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<float*>(table + (size_t)bh * n_xt * n_kb * 32), (short)0, n_xt * n_kb * 32 * 4, 0x00020000);
-  if (t < 256) s_lut[t] = expand_bits8(t);
+  const __amdgpu_buffer_rsrc_t rm = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint32_t*>(mask + (size_t)bh * n_kbw * qpad), (short)0, n_kbw * qpad * 4, 0x00020000);
+  {
+    const int n = t >> 5;  // 16 x 32 entries
+    const uint32_t lo = ((n & 1) ? 0x3F80u : 0u) | ((n & 2) ? 0x3F800000u : 0u);
+    const uint32_t hi = ((n & 4) ? 0x3F80u : 0u) | ((n & 8) ? 0x3F800000u : 0u);
+    s_nib[t] = make_uint2(lo, hi);
+  }
 
-  // Mask words of step ss: thread t builds the 4 fragments (sub-step, half) of row t and one fragment of row
-  // 512 + t/4, so it loads those two rows' words (0 past the chunk or n_qb).
-  const int ra = t, rb = 512 + (t >> 2);
-  const bool aok = ra < n_it * 32 && I0 + ra < n_qb, bok = rb < n_it * 32 && I0 + rb < n_qb;
-  const uint32_t* mrow = mask + ((size_t)bh * n_qb + I0) * n_kbw;
-  auto mload = [&](int ss, uint32_t& m0, uint32_t& m1) {
-    m0 = (aok && ss < nss) ? mrow[(size_t)ra * n_kbw + ss] : 0u;
-    m1 = (bok && ss < nss) ? mrow[(size_t)rb * n_kbw + ss] : 0u;
-  };
-  // A fragments of one step in 3 pieces: row t sub-step 0, row t sub-step 1, one fragment of row 512 + t/4;
-  // fragment (row r, sub-step, half g') = lut[byte 2 sub + g' of the row's word]
-  auto build_a = [&](int piece, uint32_t m0, uint32_t m1, uint4* dst) {
-    if (piece < 2) {
-#pragma unroll
-      for (int gg = 0; gg < 2; ++gg)
-        dst[(piece * kGemmIT + (ra >> 5)) * 64 + gg * 32 + (ra & 31)] = s_lut[(m0 >> (16 * piece + 8 * gg)) & 0xffu];
-    } else {
-      const int sub = (t >> 1) & 1, gg = t & 1;
-      dst[(sub * kGemmIT + (rb >> 5)) * 64 + gg * 32 + (rb & 31)] = s_lut[(m1 >> (16 * sub + 8 * gg)) & 0xffu];
-    }
+  // mask words of step ss for the chunk's rows: 3 loads of 1 KB (768 words; the last 128 are slack, and the
+  // descriptor bounds return 0 past the end)
+  auto dma_w = [&](int ss, uint32_t* dst) {
+    if (w < 3)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rm, (__attribute__((address_space(3))) void*)(dst + 256 * w), 16,
+                                               (uint32_t)(((size_t)ss * qpad + I0 + 256 * w) * 4 + l * 16), 0, 0, 0);
   };
   // table slice of step ss: column tile xt = w / 2, rows 32 ss + 16 (w % 2) .. +15 (clamped to n_kb - 1; the
   // mask is 0 there), 8 rows per 1 KB load
@@ -275,6 +270,13 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k4_gemm(const float* __restri
     ((uint2*)&bh_[fi])[h] = make_uint2(h01, h23);
     ((uint2*)&bl_[fi])[h] = make_uint2(l01, l23);
   };
+  // A operand: byte (2 sub + g) of the row's word -> 8 bf16 from the lane's copy of the nibble table
+  const uint2* nib = s_nib + lr;
+  auto a_frag = [&](uint32_t word, int sub) {
+    const uint32_t b = word >> (16 * sub + 8 * g);
+    const uint2 lo = nib[(b & 15u) * 32], hi = nib[((b >> 4) & 15u) * 32];
+    return __builtin_bit_cast(v8bf, make_uint4(lo.x, lo.y, hi.x, hi.y));
+  };
 
   // wave w: query tiles 5 (w / 2) .. +4, column tiles 2 (w % 2), +1; acc[2 q + c]
   const int wit = 5 * (w >> 1), wxt = 2 * (w & 1);
@@ -283,17 +285,14 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k4_gemm(const float* __restri
   for (int k = 0; k < 10; ++k) acc[k] = (v16f){};
 
   // one step with static buffers
-  uint32_t mc0, mc1, mn0, mn1;  // mask words of the step being built / being loaded
-  auto step = [&](int ss, const uint4* __restrict__ A, const uint4* __restrict__ Bh, const uint4* __restrict__ Bl,
-                  const float* __restrict__ st_next, uint4* a_next, uint4* bh_next, uint4* bl_next, float* st_fill) {
-    gemm_wait_sync();  // slice ss+1 and words ss+1 landed; A(ss), B(ss) built; the buffers filled below are free
-    mc0 = mn0;
-    mc1 = mn1;
+  auto step = [&](int ss, const uint32_t* __restrict__ W, const uint4* __restrict__ Bh, const uint4* __restrict__ Bl,
+                  const float* __restrict__ st_next, uint4* bh_next, uint4* bl_next, uint32_t* w_fill, float* st_fill) {
+    gemm_wait_sync();  // words ss, slice ss+1 landed; B(ss) built; the buffers filled below are free
     if (ss + 2 < nss) dma_st(ss + 2, st_fill);
-    mload(ss + 2, mn0, mn1);
-    const uint4* Aw = A + wit * 64 + l;
-    // 10 slots (sub, q): A fragment of tile wit + q read two slots ahead; 4 MFMAs (2 column tiles x hi/lo)
-    v8bf af[10];
+    if (ss + 1 < nss) dma_w(ss + 1, w_fill);
+    uint32_t wq[5];
+#pragma unroll
+    for (int q = 0; q < 5; ++q) wq[q] = W[32 * (wit + q) + lr];
     v8bf bhi[2][2], blo[2][2];
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub)
@@ -302,44 +301,42 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k4_gemm(const float* __restri
         bhi[sub][c] = __builtin_bit_cast(v8bf, Bh[(sub * 4 + wxt + c) * 64 + l]);
         blo[sub][c] = __builtin_bit_cast(v8bf, Bl[(sub * 4 + wxt + c) * 64 + l]);
       }
+    // 10 slots (sub, q): 4 MFMAs (2 column tiles x hi/lo) on the A operand formed two slots before
+    v8bf af[10];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) af[i] = __builtin_bit_cast(v8bf, Aw[(i / 5) * (kGemmIT * 64) + (i % 5) * 64]);
+    for (int i = 0; i < 2; ++i) af[i] = a_frag(wq[i % 5], i / 5);
 #pragma unroll
-    for (int i = 0; i < 10; ++i) {  // tiles past n_it hold stale data, never stored
+    for (int i = 0; i < 10; ++i) {  // tiles past n_it have zero words, never stored
       __builtin_amdgcn_sched_barrier(0);
       const int sub = i / 5, q = i % 5;
-      if (i + 2 < 10) af[i + 2] = __builtin_bit_cast(v8bf, Aw[((i + 2) / 5) * (kGemmIT * 64) + ((i + 2) % 5) * 64]);
+      if (i + 2 < 10) af[i + 2] = a_frag(wq[(i + 2) % 5], (i + 2) / 5);
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         acc[2 * q + c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bhi[sub][c], acc[2 * q + c], 0, 0, 0);
         acc[2 * q + c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], blo[sub][c], acc[2 * q + c], 0, 0, 0);
       }
-      // fragments of step ss+1 (past the end: unused)
+      // B fragments of step ss+1 (past the end: unused)
       if (i == 2 || i == 7) build_b(i / 5, st_next, bh_next, bl_next);
-      if (i == 1 || i == 4 || i == 8) build_a(i == 1 ? 0 : i == 4 ? 1 : 2, mc0, mc1, a_next);
     }
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // prologue: slices 0 and 1, words 0 and 1; fragments of step 0
+  // prologue: slices 0 and 1, words 0; B fragments of step 0
   dma_st(0, s_st0);
   if (nss > 1) dma_st(1, s_st1);
-  mload(0, mc0, mc1);
-  mload(1, mn0, mn1);
+  dma_w(0, s_w0);
   gemm_wait_sync();
   build_b(0, s_st0, s_bh0, s_bl0);
   build_b(1, s_st0, s_bh0, s_bl0);
-#pragma unroll
-  for (int piece = 0; piece < 3; ++piece) build_a(piece, mc0, mc1, s_a0);
   for (int ss = 0; ss < nss; ss += 2) {
-    step(ss, s_a0, s_bh0, s_bl0, s_st1, s_a1, s_bh1, s_bl1, s_st0);
-    if (ss + 1 < nss) step(ss + 1, s_a1, s_bh1, s_bl1, s_st0, s_a0, s_bh0, s_bl0, s_st1);
+    step(ss, s_w0, s_bh0, s_bl0, s_st1, s_bh1, s_bl1, s_w1, s_st0);
+    if (ss + 1 < nss) step(ss + 1, s_w1, s_bh1, s_bl1, s_st0, s_bh0, s_bl0, s_w0, s_st1);
   }
 
   // Store. acc[2q + c][r] is C[I][x] with I = I0 + 32 (wit + q) + 8(r/4) + 4g + r%4, x = 128 xg + 32 (wxt + c) + lr.
   // Column group xg < 128 is row e = xg of H_m^T: written as the bf16 hi and lo plane rows (out_off layout) of
-  // each query block's state record [hi plane 32 KB][lo plane 32 KB][Z fp32 512 B]; five rounds, one query
-  // tile per wave pair, go through LDS so that every store is a contiguous 16 B piece of a plane row.
+  // each query block's state record [hi plane 32 KB][lo plane 32 KB][Z fp32 512 B]; ten half-rounds of 64 query
+  // blocks go through LDS so that every store is a contiguous 16 B piece of a plane row.
   // Column group 128 is Z, stored as fp32.
   unsigned char* const sm_bytes = (unsigned char*)state_m;
   constexpr size_t kRec = (size_t)kStateX * 4;  // bytes per query block
@@ -356,35 +353,40 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k4_gemm(const float* __restri
         }
     return;
   }
-  float* const half0 = (float*)s_a0;  // [128 rows][64 cols] fp32: columns 0-63
-  float* const half1 = (float*)s_a1;  //                          columns 64-127
+  // staging per half-round: 64 rows (two wave pairs' query tiles) x 128 columns, columns 0-63 in s_st0 and
+  // 64-127 in s_st1 (16 KB each)
 #pragma unroll
-  for (int q = 0; q < 5; ++q) {
-    __syncthreads();  // the step buffers (first round) / the previous round's staging are free
-    float* hw_ = (w & 1) ? half1 : half0;
+  for (int q = 0; q < 5; ++q)
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
+    for (int hr = 0; hr < 2; ++hr) {
+      __syncthreads();  // the step buffers (first round) / the previous round's staging are free
+      if ((w >> 2) == hr) {
+        float* hw_ = (w & 1) ? s_st1 : s_st0;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) hw_[(32 * (w >> 1) + 8 * (r >> 2) + 4 * g + (r & 3)) * 64 + 32 * c + lr] = acc[2 * q + c][r];
-    __syncthreads();
+        for (int c = 0; c < 2; ++c)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {  // 128 rows x 16 chunks of 8 columns
-      const int u = t + kGemmThreads * j, row = u >> 4, k8 = u & 15;
-      const int it = 5 * (row >> 5) + q, I = I0 + 32 * it + (row & 31);
-      const float* src = (k8 < 8 ? half0 : half1) + row * 64 + 8 * (k8 & 7);
-      const float4 x0 = *(const float4*)src, x1 = *(const float4*)(src + 4);
-      uint32_t hi[4], lo[4];
-      split2(x0.x, x0.y, hi[0], lo[0]);
-      split2(x0.z, x0.w, hi[1], lo[1]);
-      split2(x1.x, x1.y, hi[2], lo[2]);
-      split2(x1.z, x1.w, hi[3], lo[3]);
-      if (it < n_it && I < n_qb) {
-        unsigned char* rec = sm_bytes + ((size_t)bh * n_qb + I) * kRec + out_off(xg, 8 * k8);
-        *(uint4*)rec = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-        *(uint4*)(rec + 32768) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+          for (int r = 0; r < 16; ++r)
+            hw_[(32 * ((w >> 1) & 1) + 8 * (r >> 2) + 4 * g + (r & 3)) * 64 + 32 * c + lr] = acc[2 * q + c][r];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {  // 64 rows x 16 chunks of 8 columns
+        const int u = t + kGemmThreads * j, row = u >> 4, k8 = u & 15;
+        const int it = 5 * (2 * hr + (row >> 5)) + q, I = I0 + 32 * it + (row & 31);
+        const float* src = (k8 < 8 ? s_st0 : s_st1) + row * 64 + 8 * (k8 & 7);
+        const float4 x0 = *(const float4*)src, x1 = *(const float4*)(src + 4);
+        uint32_t hi[4], lo[4];
+        split2(x0.x, x0.y, hi[0], lo[0]);
+        split2(x0.z, x0.w, hi[1], lo[1]);
+        split2(x1.x, x1.y, hi[2], lo[2]);
+        split2(x1.z, x1.w, hi[3], lo[3]);
+        if (it < n_it && I < n_qb) {
+          unsigned char* rec = sm_bytes + ((size_t)bh * n_qb + I) * kRec + out_off(xg, 8 * k8);
+          *(uint4*)rec = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+          *(uint4*)(rec + 32768) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+        }
       }
     }
-  }
 }
 
 // ---------------------------------------------------------------------------------------------------------
@@ -512,17 +514,20 @@ __global__ __launch_bounds__(BLKQ * 2) void k4_out(const uint16_t* __restrict__ 
   }
 }
 
+int mask_row_pad(int n_qb) { return (n_qb + kGemmRows - 1) / kGemmRows * kGemmRows; }
+
 hipError_t launch_linear(const Plan& p, const uint16_t* q, const uint16_t* k, const uint16_t* v, hipStream_t s) {
   hipLaunchKernelGGL(k4_prep_wp, dim3(kD * kD / 256), dim3(256), 0, s, (const uint16_t*)p.w_proj, p.wpt);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k4_states, dim3(p.n_kb, p.BH), dim3(256), 0, s, k, v, p.state, p.N, p.n_kb, 5, kStateX / 32);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const int rows = p.BH * p.n_qb, n_kbw = (p.n_kb + 31) / 32;
-  hipLaunchKernelGGL(k4_mask, dim3(rows), dim3(64), 0, s, p.block_idx, p.keep_mask, p.n_kb, p.topk, n_kbw);
+  const int rows = p.BH * p.n_qb, n_kbw = (p.n_kb + 31) / 32, qpad = mask_row_pad(p.n_qb);
+  hipLaunchKernelGGL(k4_mask, dim3(rows), dim3(64), 0, s, p.block_idx, p.keep_mask, p.n_qb, p.n_kb, p.topk, n_kbw,
+                     qpad);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(k4_gemm, dim3(kStateX / 128, (p.n_qb + kGemmIT * 32 - 1) / (kGemmIT * 32), p.BH),
-                     dim3(kGemmThreads), 0, s, p.state, p.keep_mask, p.state_m, p.n_qb, p.n_kb, n_kbw);
+  hipLaunchKernelGGL(k4_gemm, dim3(kStateX / 128, qpad / kGemmRows, p.BH), dim3(kGemmThreads), 0, s, p.state,
+                     p.keep_mask, p.state_m, p.n_qb, p.n_kb, n_kbw, qpad);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int total = p.BH * p.n_qb;
   if (p.blk_q == 128)

@@ -88,7 +88,10 @@ __device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {
 
 // One block of up to MAXROWS rows (valid: `rows`) × 128 channels, 256 threads. Thread t owns channels
 // 8*(t%16)..+7 of rows t/16 + 16*i.
-template <int MAXROWS>
+// One block of rows (<= MAXROWS) of D channels: thread (row group rl, 8-channel group cg) holds rows rl + 16 i.
+// Rows stay packed bf16 in registers (4 words per 8 values); with SMOOTH the fp32 value k - mu is formed again
+// where it is needed (the same single IEEE subtraction each time).
+template <int MAXROWS, bool SMOOTH>
 __device__ __forceinline__ void quant_block(const uint16_t* __restrict__ src, int rows, const float* __restrict__ mu,
                                             int8_t* __restrict__ dst, float* __restrict__ scale_out,
                                             double* __restrict__ pool_out, float* s_amax,
@@ -97,31 +100,30 @@ __device__ __forceinline__ void quant_block(const uint16_t* __restrict__ src, in
   const int t = threadIdx.x, cg = t & 15, rl = t >> 4;
   float m8[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) m8[e] = mu ? mu[cg * 8 + e] : 0.f;
-  float x[IT][8];
+  for (int e = 0; e < 8; ++e) m8[e] = SMOOTH ? mu[cg * 8 + e] : 0.f;
+  uint4 raw[IT];
+#pragma unroll
+  for (int i = 0; i < IT; ++i) {
+    const int r = rl + 16 * i;
+    raw[i] = (r < rows) ? *(const uint4*)(src + (size_t)r * kD + cg * 8) : make_uint4(0, 0, 0, 0);
+  }
+  auto value = [&](int i, int e) -> float {  // element e of row rl + 16 i, smoothed when SMOOTH (0 past rows)
+    const uint32_t wd = e < 2 ? raw[i].x : e < 4 ? raw[i].y : e < 6 ? raw[i].z : raw[i].w;
+    const float x = (e & 1) ? bf16_hi(wd) : bf16_lo(wd);
+    return SMOOTH ? (rl + 16 * i < rows ? x - m8[e] : 0.f) : x;  // one IEEE fp32 subtraction
+  };
   float amax = 0.f;
   double psum[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) psum[e] = 0.0;
 #pragma unroll
-  for (int i = 0; i < IT; ++i) {
-    const int r = rl + 16 * i;
-    uint4 w = make_uint4(0, 0, 0, 0);
-    if (r < rows) w = *(const uint4*)(src + (size_t)r * kD + cg * 8);
-    x[i][0] = bf16_lo(w.x); x[i][1] = bf16_hi(w.x);
-    x[i][2] = bf16_lo(w.y); x[i][3] = bf16_hi(w.y);
-    x[i][4] = bf16_lo(w.z); x[i][5] = bf16_hi(w.z);
-    x[i][6] = bf16_lo(w.w); x[i][7] = bf16_hi(w.w);
-    if (mu && r < rows) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[i][e] = x[i][e] - m8[e];  // one IEEE fp32 subtraction
-    }
+  for (int i = 0; i < IT; ++i)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      amax = fmaxf(amax, fabsf(x[i][e]));
-      psum[e] += (double)x[i][e];
+      const float x = value(i, e);
+      amax = fmaxf(amax, fabsf(x));
+      psum[e] += (double)x;
     }
-  }
   amax = wave_max_f32(amax);
   if ((t & 63) == 0) s_amax[t >> 6] = amax;
 #pragma unroll
@@ -136,7 +138,7 @@ __device__ __forceinline__ void quant_block(const uint16_t* __restrict__ src, in
     if (r < rows) {
       int c[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) c[e] = (amax > 0.f) ? quant_code(x[i][e], s, rcp) : 0;
+      for (int e = 0; e < 8; ++e) c[e] = (amax > 0.f) ? quant_code(value(i, e), s, rcp) : 0;
       uint2 o;
       o.x = pack4_i8(c[0], c[1], c[2], c[3]);
       o.y = pack4_i8(c[4], c[5], c[6], c[7]);
@@ -152,13 +154,10 @@ __device__ __forceinline__ void quant_block(const uint16_t* __restrict__ src, in
   if (t == 0) *scale_out = (amax > 0.f) ? s : 0.f;
 }
 
-// V^T image of one key block for the attention kernel: [128 channels][64 keys] bf16, 16 KB, each channel row's
-// keys in MFMA slot order (key_pos16 within every 16) and its 16-byte chunks XOR-swizzled (swz8), exactly the
-// LDS layout the attention kernel reads; keys past a ragged block's end are zero. 256 threads: thread t takes
-// channels 8*(t%16)..+7 of keys 4*(t/16)..+3.
-__device__ __forceinline__ void write_v_image(const uint16_t* __restrict__ src, int nv, unsigned char* __restrict__ img) {
+// rows of one key block of V as the V^T image writer takes them: thread (cg, kg) holds keys 4 kg .. +3,
+// channels 8 cg .. +7 (zeros past nv)
+__device__ __forceinline__ void load_v_rows(const uint16_t* __restrict__ src, int nv, uint32_t (&wv)[4][4]) {
   const int t = threadIdx.x, cg = t & 15, kg = t >> 4;
-  uint32_t wv[4][4];
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
     const int r = 4 * kg + b;
@@ -166,6 +165,14 @@ __device__ __forceinline__ void write_v_image(const uint16_t* __restrict__ src, 
     if (r < nv) a = *(const uint4*)(src + (size_t)r * kD + cg * 8);
     wv[b][0] = a.x; wv[b][1] = a.y; wv[b][2] = a.z; wv[b][3] = a.w;
   }
+}
+
+// V^T image of one key block for the attention kernel: [128 channels][64 keys] bf16, 16 KB, each channel row's
+// keys in MFMA slot order (key_pos16 within every 16) and its 16-byte chunks XOR-swizzled (swz8), exactly the
+// LDS layout the attention kernel reads; keys past a ragged block's end are zero. 256 threads: thread t holds
+// (load_v_rows) channels 8*(t%16)..+7 of keys 4*(t/16)..+3.
+__device__ __forceinline__ void write_v_image(const uint32_t (&wv)[4][4], unsigned char* __restrict__ img) {
+  const int t = threadIdx.x, cg = t & 15, kg = t >> 4;
   const int pos = 16 * (kg >> 2) + key_pos16(4 * (kg & 3));
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
@@ -193,15 +200,20 @@ __global__ __launch_bounds__(256) void k1_quant(const uint16_t* __restrict__ q, 
   const size_t base = (size_t)bh * N * kD;
   if (x < n_qb) {
     const int r0 = x * BLKQ;
-    quant_block<BLKQ>(q + base + (size_t)r0 * kD, min(BLKQ, N - r0), nullptr, q8 + base + (size_t)r0 * kD,
-                      qs + (size_t)bh * n_qb + x, qp + ((size_t)bh * n_qb + x) * kD, s_amax, s_red);
+    quant_block<BLKQ, false>(q + base + (size_t)r0 * kD, min(BLKQ, N - r0), nullptr, q8 + base + (size_t)r0 * kD,
+                             qs + (size_t)bh * n_qb + x, qp + ((size_t)bh * n_qb + x) * kD, s_amax, s_red);
   } else {
     const int j = x - n_qb;
-    const int r0 = j * kBlkK;
-    quant_block<kBlkK>(k + base + (size_t)r0 * kD, min(kBlkK, N - r0), mu ? mu + bh * kD : nullptr,
-                       k8 + base + (size_t)r0 * kD, ks + (size_t)bh * n_kb + j, kp + ((size_t)bh * n_kb + j) * kD,
-                       s_amax, s_red);
-    if (v) write_v_image(v + base + (size_t)r0 * kD, min(kBlkK, N - r0), v_img + ((size_t)bh * n_kb + j) * 16384);
+    const int r0 = j * kBlkK, nv = min(kBlkK, N - r0);
+    uint32_t wv[4][4];
+    if (v) load_v_rows(v + base + (size_t)r0 * kD, nv, wv);  // in flight while K is quantized
+    if (mu)
+      quant_block<kBlkK, true>(k + base + (size_t)r0 * kD, nv, mu + bh * kD, k8 + base + (size_t)r0 * kD,
+                               ks + (size_t)bh * n_kb + j, kp + ((size_t)bh * n_kb + j) * kD, s_amax, s_red);
+    else
+      quant_block<kBlkK, false>(k + base + (size_t)r0 * kD, nv, nullptr, k8 + base + (size_t)r0 * kD,
+                                ks + (size_t)bh * n_kb + j, kp + ((size_t)bh * n_kb + j) * kD, s_amax, s_red);
+    if (v) write_v_image(wv, v_img + ((size_t)bh * n_kb + j) * 16384);
   }
 }
 

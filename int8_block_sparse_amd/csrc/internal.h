@@ -32,7 +32,7 @@ struct Plan {
   unsigned char* v_img; // [BH][n_kb][16384]    per key block: V^T in the attention kernel's LDS layout
   int32_t* block_idx;   // [BH][n_qb][topk]
   uint16_t* wpt;        // [D][D] bf16: W_p^T in MFMA slot order
-  float* state;         // [BH][kStateX / 32][n_kb][32]   per-block states, tiles of 32 columns
+  float* state;         // [BH][kStateX / 128][n_kb][128]   per-block states, tiles of 128 columns
   uint32_t* keep_mask;  // [BH][ceil(n_kb/32)][mask_row_pad(n_qb)]   bit J set iff key block J is not selected
   float* state_m;       // [BH][n_qb][kStateX]   remaining (non-selected) state per query block
   float* o_lin;         // [BH][N][D]

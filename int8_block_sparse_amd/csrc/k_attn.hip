@@ -17,8 +17,8 @@
 // the loads of two iterations back; each iteration computes the next block's scores while it runs this block's
 // softmax, and the scheduler interleaves those MFMAs (and the PV MFMAs) with the softmax VALU work so the matrix
 // core and the vector ALU of a wave overlap.
-// Softmax rescaling is lazy: the running max moves only when a block's max exceeds it by more than 2^8, which
-// keeps every exp2 argument <= 8 and skips the O rescale for almost every block.
+// Softmax rescaling is lazy: the running max moves only when a block's max exceeds it by more than kLazy (log2
+// units), which keeps every exp2 argument <= kLazy and skips the O rescale for almost every block.
 #include <type_traits>
 
 #include "device_common.h"
@@ -116,6 +116,11 @@ __device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(
 // kMagic, the bit pattern of 1.5 * 2^23: since |S| <= 127*127*128 < 2^22, the sum read as a float is exactly
 // 1.5 * 2^23 + S, so no int-to-float conversion is needed.
 constexpr int kMagic = 0x4B400000;
+constexpr int kListCap = 1024;
+// Lazy-rescale slack in log2 units: probabilities stay <= 2^24, so a row sum over the largest key count stays
+// below 2^45, far inside fp32; on smooth video-like inputs a running max of 32 rows moves for under 1% of
+// blocks (about 6% with a slack of 8).
+constexpr float kLazy = 24.f;  // selection-list entries the attention kernel keeps in LDS
 constexpr float kMagicF = 12582912.0f;
 
 __device__ __forceinline__ void attn_scores(const unsigned char* __restrict__ sk, const v4i* bq, const int (&koff)[2][4],
@@ -222,7 +227,7 @@ __device__ __forceinline__ void attn_iter(const unsigned char* __restrict__ sk_n
   }
   mx = max(mx, swap_halves_i32(mx));
   const float mblk = (float)(mx - kMagic) * c;
-  const bool need = mblk > m_run + 8.f;
+  const bool need = mblk > m_run + kLazy;
   if (__ballot(need)) {
     // rare: keep it a real branch (the marker has side effects, so the body is never executed speculatively)
     asm volatile("; rescale running max" ::: "memory");
@@ -262,6 +267,10 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k3_attn(
   // LDS object so that the compiler can tell the slot being filled from the slots being read.
   __shared__ __attribute__((aligned(1024))) unsigned char s_k0[64 * 128], s_k1[64 * 128], s_k2[64 * 128];
   __shared__ __attribute__((aligned(1024))) unsigned char s_v0[128 * 128], s_v1[128 * 128], s_v2[128 * 128];
+  // the selection list as the steady loop consumes it: block index and scale product cq * k_scale per entry
+  // (lists of up to kListCap entries; longer ones are read through scalar loads)
+  __shared__ uint16_t s_lj[kListCap];
+  __shared__ float s_lc[kListCap];
 
   const int item = xcd_remap(blockIdx.x, total);
   const int bh = item / n_qb, I = item % n_qb;
@@ -328,13 +337,20 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k3_attn(
     // runs the full-block body; a caller-given list that places it elsewhere takes the generic loop.
     // One pass over the list, a lane per entry: the largest key scale and whether the ragged block occurs
     // before the end.
+    // Wave 0 also writes the list to LDS when it fits.
     const bool has_ragged = nv_last != kBlkK;
+    const bool listed = topk <= kListCap;
     float kmax = 0.f;
     bool early_ragged = false;
     for (int j = l; j < topk; j += 64) {
       const int J = blk(j);
-      kmax = fmaxf(kmax, ksrow[J]);
+      const float kv = ksrow[J];
+      kmax = fmaxf(kmax, kv);
       early_ragged |= has_ragged && j < topk - 1 && J == last_kb;
+      if (listed && w == 0) {
+        s_lj[j] = (uint16_t)J;
+        s_lc[j] = cq * kv;
+      }
     }
     kmax = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(wave_max_f32(kmax))));
     const bool elsewhere = __ballot(early_ragged) != 0;
@@ -350,17 +366,22 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k3_attn(
     // use: iteration j reads K[j+1] (scores of the next block) and V[j], and issues K[j+3] and V[j+2] into the
     // slots that K[j] and V[j-1] leave free. The slots are distinct restrict-qualified pointers so that the
     // compiler can tell the loads in flight from the LDS reads of the current tiles.
-    auto ring = [&](auto fastc, unsigned char* __restrict__ k0, unsigned char* __restrict__ k1,
+    // With the list in LDS (L), iteration j takes J[j+3] and the scale product of block j from LDS reads issued
+    // one iteration earlier, which the ring's barrier wait has already completed: the steady loop then has no
+    // scalar-memory waits (those would also drain the LDS operand reads in flight).
+    auto ring = [&](auto fastc, auto listc, unsigned char* __restrict__ k0, unsigned char* __restrict__ k1,
                     unsigned char* __restrict__ k2, unsigned char* __restrict__ v0, unsigned char* __restrict__ v1,
                     unsigned char* __restrict__ v2) {
       constexpr bool F = decltype(fastc)::value;
+      constexpr bool L = decltype(listc)::value;
       unsigned char* const ks[3] = {k0, k1, k2};
       unsigned char* const vs[3] = {v0, v1, v2};
-      auto put_k = [&](int j, unsigned char* dst) {
-        const int J = blk(j);
+      auto put_kJ = [&](int J, unsigned char* dst) {
         stage_k<NW>(rk, (uint32_t)J * (kBlkK * kD), J == last_kb ? so_last : so_full, dst);
       };
-      auto put_v = [&](int j, unsigned char* dst) { stage_v<NW>(rv, (uint32_t)blk(j) * 16384u, dst); };
+      auto put_vJ = [&](int J, unsigned char* dst) { stage_v<NW>(rv, (uint32_t)J * 16384u, dst); };
+      auto put_k = [&](int j, unsigned char* dst) { put_kJ(blk(j), dst); };
+      auto put_v = [&](int j, unsigned char* dst) { put_vJ(blk(j), dst); };
       put_k(0, k0);
       if (topk > 1) put_k(1, k1);
       if (topk > 2) put_k(2, k2);
@@ -374,13 +395,33 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k3_attn(
       // Iteration j < topk - 1 waits for K[j+1] and V[j], issued two iterations back (the loads of iteration
       // j-1 may stay in flight), issues K[j+3] and V[j+2], then runs block j with the scores of block j+1.
       // Steady state, ring phase P = j % 3 known at compile time, both tiles issued:
+      // (L: lj holds J[j+3] and lc the scale product of block j, both as read from LDS; jv = J[j+2])
+      int lj = 0, jv = 0;
+      float lc = 0.f;
+      if constexpr (L) {
+        lj = s_lj[min(3, topk - 1)];
+        lc = s_lc[0];
+        jv = __builtin_amdgcn_readfirstlane((int)s_lj[min(2, topk - 1)]);
+      }
       auto iter_full = [&](int j, auto ph) {
         constexpr int P = decltype(ph)::value;
         ring_sync<T::KPW + T::VPW>();
-        put_k(j + 3, ks[P]);
-        put_v(j + 2, vs[(P + 2) % 3]);
-        attn_iter<false, true, F>(ks[(P + 1) % 3], vs[P], bq, koff, voff, cq * ksrow[blk(j)], kBlkK, g, o, m_run,
-                                  l_run, scur, snext);
+        float c;
+        if constexpr (L) {
+          const int J3 = __builtin_amdgcn_readfirstlane(lj);
+          c = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(lc)));
+          put_kJ(J3, ks[P]);
+          put_vJ(jv, vs[(P + 2) % 3]);
+          lj = s_lj[min(j + 4, topk - 1)];
+          lc = s_lc[j + 1];
+          jv = J3;
+        } else {
+          put_k(j + 3, ks[P]);
+          put_v(j + 2, vs[(P + 2) % 3]);
+          c = cq * ksrow[blk(j)];
+        }
+        attn_iter<false, true, F>(ks[(P + 1) % 3], vs[P], bq, koff, voff, c, kBlkK, g, o, m_run, l_run, scur,
+                                  snext);
         scur[0] = snext[0];
         scur[1] = snext[1];
       };
@@ -429,9 +470,15 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k3_attn(
         sync();
       }
     } else if (fast) {
-      ring(std::true_type{}, s_k0, s_k1, s_k2, s_v0, s_v1, s_v2);
+      if (listed)
+        ring(std::true_type{}, std::true_type{}, s_k0, s_k1, s_k2, s_v0, s_v1, s_v2);
+      else
+        ring(std::true_type{}, std::false_type{}, s_k0, s_k1, s_k2, s_v0, s_v1, s_v2);
     } else {
-      ring(std::false_type{}, s_k0, s_k1, s_k2, s_v0, s_v1, s_v2);
+      if (listed)
+        ring(std::false_type{}, std::true_type{}, s_k0, s_k1, s_k2, s_v0, s_v1, s_v2);
+      else
+        ring(std::false_type{}, std::false_type{}, s_k0, s_k1, s_k2, s_v0, s_v1, s_v2);
     }
   }
 

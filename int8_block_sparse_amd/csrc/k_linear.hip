@@ -58,7 +58,8 @@ __device__ __forceinline__ void split2(float x0, float x1, uint32_t& hi, uint32_
 // LDS holds phi(K)^T (hi, lo) and V^T as [channel][key] bf16 rows of 128 B, 16-byte chunks XOR-swizzled.
 // Wave w computes H^T[e][c] = sum_key v[e] phi(k)[c] for all e and c in [32w, 32w+32) (A = V^T, B = phi(K)).
 // Table column x = e*128 + c; tile (x >> lxw) holds xw consecutive columns of every block: since xw <= 128 divides
-// 128, the address of (e, c) is a per-lane part (c, J) plus e * 128 * n_kb floats.
+// 128, the address of (e, c) is a per-lane part (c, J) plus e * 128 * n_kb floats. The forward uses xw = 128:
+// each block's state is 129 pieces of 512 B, and 32 consecutive blocks of one tile are 16 KB contiguous.
 // ---------------------------------------------------------------------------------------------------------
 __device__ __forceinline__ int lds_off(int row, int key) {  // byte offset of (row, key) in a [128][64] bf16 tile
   return row * 128 + (((key >> 3) ^ swz8(row)) << 4) + ((key & 7) << 1);
@@ -192,8 +193,8 @@ __device__ __forceinline__ uint4 expand_bits8(uint32_t b) {
 // (J x x) as hi + lo bf16, fp32 accumulation.
 // grid (kStateX / 128 column groups, ceil(n_qb / 640) query-block chunks, BH), 512 threads (8 waves).
 // Step = 32 key blocks (two MFMA k-steps of 16) = one mask word per query block. At the start of step s the
-// workgroup issues buffer loads to LDS of the [32][128] fp32 table slice of step s+2 (4 column tiles of 32,
-// 4 KB contiguous each) and of the chunk's 640 mask words of step s+1; during step s the waves run its MFMAs
+// workgroup issues buffer loads to LDS of the [32][128] fp32 table slice of step s+2 (16 KB contiguous) and of
+// the chunk's 640 mask words of step s+1; during step s the waves run its MFMAs
 // and rebuild slice s+1 into B fragments (hi, lo). Each wave forms its own A operands in registers: the byte
 // of its row's mask word for (sub-step, lane half) becomes 8 bf16 through two reads of a 16-entry nibble table
 // kept in 32 lane-private copies (conflict-free). One wait for all loads plus one barrier per step orders
@@ -222,14 +223,14 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k4_gemm(const float* __restri
   __shared__ __attribute__((aligned(1024))) uint4 s_bl0[2 * 4 * 64], s_bl1[2 * 4 * 64];
   __shared__ __attribute__((aligned(1024))) uint32_t s_w0[kGemmRows + 128], s_w1[kGemmRows + 128];  // mask words
   __shared__ __attribute__((aligned(1024))) uint2 s_nib[16 * 32];  // [nibble][copy]: 4 bf16 of 0 / 1.0
-  constexpr int n_xt = kStateX / 32;
+  constexpr int n_xt = kStateX / 128;
   const int xg = blockIdx.x, ic = blockIdx.y, bh = blockIdx.z;
   const int t = threadIdx.x, w = __builtin_amdgcn_readfirstlane(t >> 6), l = t & 63, g = l >> 5, lr = l & 31;
   const int I0 = ic * kGemmRows;
   const int n_it = min(kGemmIT, (n_qb - I0 + 31) >> 5);
   const int nss = n_kbw;  // steps of 32 key blocks
   const __amdgpu_buffer_rsrc_t rt = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<float*>(table + (size_t)bh * n_xt * n_kb * 32), (short)0, n_xt * n_kb * 32 * 4, 0x00020000);
+      const_cast<float*>(table + (size_t)bh * n_xt * n_kb * 128), (short)0, n_xt * n_kb * 128 * 4, 0x00020000);
   const __amdgpu_buffer_rsrc_t rm = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint32_t*>(mask + (size_t)bh * n_kbw * qpad), (short)0, n_kbw * qpad * 4, 0x00020000);
   {
@@ -246,15 +247,14 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k4_gemm(const float* __restri
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rm, (__attribute__((address_space(3))) void*)(dst + 256 * w), 16,
                                                (uint32_t)(((size_t)ss * qpad + I0 + 256 * w) * 4 + l * 16), 0, 0, 0);
   };
-  // table slice of step ss: column tile xt = w / 2, rows 32 ss + 16 (w % 2) .. +15 (clamped to n_kb - 1; the
-  // mask is 0 there), 8 rows per 1 KB load
+  // table slice of step ss: rows 32 ss .. +31 of column group xg ([row][128] fp32, 16 KB contiguous; rows past
+  // n_kb are clamped to n_kb - 1, where the mask is 0); wave w loads rows 4w .. 4w+3, two rows per 1 KB load
   auto dma_st = [&](int ss, float* dst) {
-    const int xt = w >> 1;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const int row = 32 * ss + 16 * (w & 1) + 8 * h + (l >> 3);
-      const uint32_t off = (uint32_t)((((4 * xg + xt) * n_kb + min(row, n_kb - 1)) * 32 + (l & 7) * 4) * 4);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rt, (__attribute__((address_space(3))) void*)(dst + xt * 1024 + (16 * (w & 1) + 8 * h) * 32),
+      const int row = 32 * ss + 4 * w + 2 * h + (l >> 5);
+      const uint32_t off = (uint32_t)((((size_t)xg * n_kb + min(row, n_kb - 1)) * 128 + (l & 31) * 4) * 4);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rt, (__attribute__((address_space(3))) void*)(dst + (4 * w + 2 * h) * 128),
                                                16, off, 0, 0, 0);
     }
   };
@@ -262,10 +262,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k4_gemm(const float* __restri
   // lane l) -> rows 16 sub + 8 g + 4 h .. +3 of column lr
   auto build_b = [&](int sub, const float* __restrict__ st, uint4* bh_, uint4* bl_) {
     const int xt = t >> 7, h = (t >> 6) & 1;
-    const float* c = st + xt * 1024 + (16 * sub + 8 * g + 4 * h) * 32 + lr;
+    const float* c = st + (16 * sub + 8 * g + 4 * h) * 128 + 32 * xt + lr;
     uint32_t h01, l01, h23, l23;
-    split2(c[0], c[32], h01, l01);
-    split2(c[64], c[96], h23, l23);
+    split2(c[0], c[128], h01, l01);
+    split2(c[256], c[384], h23, l23);
     const int fi = (sub * 4 + xt) * 64 + l;
     ((uint2*)&bh_[fi])[h] = make_uint2(h01, h23);
     ((uint2*)&bl_[fi])[h] = make_uint2(l01, l23);
@@ -520,7 +520,7 @@ hipError_t launch_linear(const Plan& p, const uint16_t* q, const uint16_t* k, co
   hipLaunchKernelGGL(k4_prep_wp, dim3(kD * kD / 256), dim3(256), 0, s, (const uint16_t*)p.w_proj, p.wpt);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k4_states, dim3(p.n_kb, p.BH), dim3(256), 0, s, k, v, p.state, p.N, p.n_kb, 5, kStateX / 32);
+  hipLaunchKernelGGL(k4_states, dim3(p.n_kb, p.BH), dim3(256), 0, s, k, v, p.state, p.N, p.n_kb, 7, kStateX / 128);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int rows = p.BH * p.n_qb, n_kbw = (p.n_kb + 31) / 32, qpad = mask_row_pad(p.n_qb);
   hipLaunchKernelGGL(k4_mask, dim3(rows), dim3(64), 0, s, p.block_idx, p.keep_mask, p.n_qb, p.n_kb, p.topk, n_kbw,

@@ -48,6 +48,11 @@ __device__ __forceinline__ int swap_halves_i32(int v) {
 __device__ __forceinline__ float swap_halves_f32(float v) {
   return __int_as_float(swap_halves_i32(__float_as_int(v)));
 }
+// max over lanes l and l ^ 32, on every lane: the swap leaves one half's value in both halves of each result
+__device__ __forceinline__ int max_halves_i32(int v) {
+  auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return max((int)r[0], (int)r[1]);
+}
 
 // Key order inside each group of 16 keys of a V^T row in LDS: the bf16 MFMA lane half g, slot i (0..7) must
 // find key 8*(i/4) + 4*g + (i%4) at position 8*g + i, i.e. the middle two groups of 4 keys trade places.
@@ -56,6 +61,11 @@ __device__ __forceinline__ int key_pos16(int off) { return (off & 3) | ((off & 4
 // XOR swizzle of the 16-byte chunk index inside a 128-byte LDS row, so that both 8 consecutive rows read at
 // one chunk and rows 8 apart written at one chunk land in different banks.
 __device__ __forceinline__ int swz8(int row) { return (row ^ (row >> 3)) & 7; }
+// The same pattern built from the low five row bits only, so that it repeats every 32 rows: operand reads of
+// 32-row MFMA tiles at rows 32t + lane then differ from tile 0's by the constant 4096 * t, which the LDS
+// instructions take as an immediate offset instead of a register per tile. Each read still touches 32 rows
+// that share bit 5, where the two patterns differ by a constant XOR, so it stays conflict-free.
+__device__ __forceinline__ int swz32(int row) { return (row ^ ((row >> 3) & 3)) & 7; }
 
 // Map a flat workgroup id to a work item so that each XCD (ids are dealt round-robin over 8 XCDs) gets one
 // contiguous range of work items: neighbouring query blocks of a head then share that XCD's L2.

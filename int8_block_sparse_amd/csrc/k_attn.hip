@@ -52,7 +52,7 @@ __device__ __forceinline__ StageOffsets<NW> stage_offsets(int nv) {
 #pragma unroll
   for (int i = 0; i < T::KPW; ++i) {
     const int p = (w * T::KPW + i) * 64 + l;  // 16-byte position in the LDS image
-    const int r = p >> 3, ch = (p & 7) ^ swz8(r);
+    const int r = p >> 3, ch = (p & 7) ^ swz32(r);
     so.k[i] = (uint32_t)(min(r, nv - 1) * kD + ch * 16);  // rows past a ragged end re-read the last valid row
   }
   return so;
@@ -113,15 +113,24 @@ __device__ __forceinline__ void ring_sync() {
 __device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Scores of one key block (S^T = K Q^T, 8 INT8 MFMAs into two 32-key tiles). The int32 accumulators start at
-// kMagic, the bit pattern of 1.5 * 2^23: since |S| <= 127*127*128 < 2^22, the sum read as a float is exactly
-// 1.5 * 2^23 + S, so no int-to-float conversion is needed.
-constexpr int kMagic = 0x4B400000;
-constexpr int kListCap = 1024;
+// kMagic is the fp32 bit pattern of 1/(2*pi), 0x3E22F983, whose mantissa field 0x22F983 = 2292099 leaves
+// 2292099 steps below it and 2^23 - 2292099 = 6096509 above it inside its binade. Since |S| <= 127*127*128 =
+// 2064512, the sum read as a float is exactly 2^-3 + (2292099 + S) * 2^-26 (no int-to-float conversion), and since
+// the pattern is an inline constant of the instruction set, the first MFMA of each tile takes it as its
+// accumulator operand without any register being set up.
+constexpr int kMagic = 0x3E22F983;
+constexpr int kMagicMant = kMagic & 0x7FFFFF;
+constexpr float kMagicF = __builtin_bit_cast(float, kMagic);  // 2^-3 * (1 + kMagicMant * 2^-23)
+constexpr float kMagicScale = 0x1p26f;                        // one unit of S in that float is 2^-26
+constexpr float kMagicUnits = kMagicF * kMagicScale;          // 2^23 + kMagicMant, exact
+static_assert(kMagicUnits == float((1 << 23) + kMagicMant), "the magic's float value in units of S");
+static_assert(127 * 127 * 128 < kMagicMant && 127 * 127 * 128 < (1 << 23) - kMagicMant,
+              "scores must stay in the binade");
+constexpr int kListCap = 1020;  // selection-list entries the attention kernel keeps in LDS
 // Lazy-rescale slack in log2 units: probabilities stay <= 2^24, so a row sum over the largest key count stays
 // below 2^45, far inside fp32; on smooth video-like inputs a running max of 32 rows moves for under 1% of
 // blocks (about 6% with a slack of 8).
-constexpr float kLazy = 24.f;  // selection-list entries the attention kernel keeps in LDS
-constexpr float kMagicF = 12582912.0f;
+constexpr float kLazy = 24.f;
 
 __device__ __forceinline__ void attn_scores(const unsigned char* __restrict__ sk, const v4i* bq, const int (&koff)[2][4],
                                             v16i (&sacc)[2]) {
@@ -138,16 +147,18 @@ __device__ __forceinline__ void attn_scores(const unsigned char* __restrict__ sk
 }
 
 // One pair of probabilities: p = exp2(S*c - m) for scores r, r+1 of a 32-key tile, packed to bf16 in PV
-// B-operand order; the row sum is taken over the same bf16 values the PV product uses. s holds kMagic + S.
-// FAST: t = fma(1.5*2^23 + S, c, -kc) with kc = fl(1.5*2^23*c + m), one instruction; kc's rounding shifts every
-// t of the block by the same amount, at most half an ulp of kc (<= 2^-11 for c < 2^-10). Otherwise
-// t = fma(S, c, -m) exactly as written. Ragged keys carry INT_MIN and get p = 0.
+// B-operand order; the row sum is taken over the same bf16 values the PV product uses. s holds kMagic + S, read as
+// the float x = kMagicF + S * 2^-26, and c26 = c * 2^26. FAST: t = fma(x, c26, -kc) = (kMagicUnits + S) * c - kc
+// with kc = fl(kMagicUnits * c + m), one instruction; kc's rounding shifts every t of the block by the same
+// amount, at most half an ulp of kc (<= 2^-11 for c < 2^-10). Otherwise t = fma(x - kMagicF, c26, -m), where the
+// subtraction is exact and the product is S * c: the same value as fma(S, c, -m). Ragged keys carry INT_MIN and
+// get p = 0.
 template <bool RAGGED, bool FAST>
-__device__ __forceinline__ void attn_exp_pair(const v16i& s, int r, float c, float m, float kc, uint32_t& pk,
+__device__ __forceinline__ void attn_exp_pair(const v16i& s, int r, float c26, float m, float kc, uint32_t& pk,
                                               float& ps) {
   const float x0 = __int_as_float(s[r]), x1 = __int_as_float(s[r + 1]);
-  float p0 = __builtin_amdgcn_exp2f(FAST ? fmaf(x0, c, -kc) : fmaf(x0 - kMagicF, c, -m));
-  float p1 = __builtin_amdgcn_exp2f(FAST ? fmaf(x1, c, -kc) : fmaf(x1 - kMagicF, c, -m));
+  float p0 = __builtin_amdgcn_exp2f(FAST ? fmaf(x0, c26, -kc) : fmaf(x0 - kMagicF, c26, -m));
+  float p1 = __builtin_amdgcn_exp2f(FAST ? fmaf(x1, c26, -kc) : fmaf(x1 - kMagicF, c26, -m));
   if (RAGGED) {
     p0 = s[r] == INT_MIN ? 0.f : p0;
     p1 = s[r + 1] == INT_MIN ? 0.f : p1;
@@ -187,10 +198,14 @@ __device__ __forceinline__ void attn_iter(const unsigned char* __restrict__ sk_n
   auto mfma = [&](int i) {
     if (i < NK) {
       const int tt = i >> 2, st = i & 3;
-      const v16i acc = st == 0 ? (v16i){kMagic, kMagic, kMagic, kMagic, kMagic, kMagic, kMagic, kMagic, kMagic,
-                                        kMagic, kMagic, kMagic, kMagic, kMagic, kMagic, kMagic}
-                               : snext[tt];
-      snext[tt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ka[i], bq[st], acc, 0, 0, 0);
+      if (st == 0)
+        snext[tt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
+            ka[i], bq[st],
+            (v16i){kMagic, kMagic, kMagic, kMagic, kMagic, kMagic, kMagic, kMagic, kMagic, kMagic, kMagic, kMagic,
+                   kMagic, kMagic, kMagic, kMagic},
+            0, 0, 0);
+      else
+        snext[tt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ka[i], bq[st], snext[tt], 0, 0, 0);
     } else {
       const int v = i - NK, st = v >> 2, ct = v & 3;
       const v8bf b = __builtin_bit_cast(v8bf, make_uint4(pw[4 * st], pw[4 * st + 1], pw[4 * st + 2], pw[4 * st + 3]));
@@ -225,7 +240,7 @@ __device__ __forceinline__ void attn_iter(const unsigned char* __restrict__ sk_n
     }
     mx = max(mx, part_max(q));
   }
-  mx = max(mx, swap_halves_i32(mx));
+  mx = max_halves_i32(mx);
   const float mblk = (float)(mx - kMagic) * c;
   const bool need = mblk > m_run + kLazy;
   if (__ballot(need)) {
@@ -242,7 +257,8 @@ __device__ __forceinline__ void attn_iter(const unsigned char* __restrict__ sk_n
   }
 
   // region 2: slot k runs MFMA k, the read for MFMA k + AHEAD and exp pair k - NK + 4
-  const float kc = FAST ? fmaf(kMagicF, c, m_run) : 0.f;
+  const float kc = FAST ? fmaf(kMagicUnits, c, m_run) : 0.f;
+  const float c26 = c * kMagicScale;
   float ps = 0.f;
 #pragma unroll
   for (int k = HAS_NEXT ? 4 : -4; k < NS; ++k) {
@@ -250,7 +266,7 @@ __device__ __forceinline__ void attn_iter(const unsigned char* __restrict__ sk_n
     if (k >= 0 && k + AHEAD < NS && k + AHEAD >= (HAS_NEXT ? 8 : AHEAD)) read(k + AHEAD);
     if (k >= 0) mfma(k);
     const int e = k - NK + 4;
-    if (e >= 0 && e < 16) attn_exp_pair<RAGGED, FAST>(scur[e >> 3], 2 * (e & 7), c, m_run, kc, pw[e], ps);
+    if (e >= 0 && e < 16) attn_exp_pair<RAGGED, FAST>(scur[e >> 3], 2 * (e & 7), c26, m_run, kc, pw[e], ps);
   }
   __builtin_amdgcn_sched_barrier(0);
   l_run += ps;
@@ -268,8 +284,9 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k3_attn(
   __shared__ __attribute__((aligned(1024))) unsigned char s_k0[64 * 128], s_k1[64 * 128], s_k2[64 * 128];
   __shared__ __attribute__((aligned(1024))) unsigned char s_v0[128 * 128], s_v1[128 * 128], s_v2[128 * 128];
   // the selection list as the steady loop consumes it: block index and scale product cq * k_scale per entry
-  // (lists of up to kListCap entries; longer ones are read through scalar loads)
-  __shared__ uint16_t s_lj[kListCap];
+  // (lists of up to kListCap entries, padded with four copies of the last index; longer lists are read through
+  // scalar loads)
+  __shared__ int s_lj[kListCap + 4];
   __shared__ float s_lc[kListCap];
 
   const int item = xcd_remap(blockIdx.x, total);
@@ -291,14 +308,14 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k3_attn(
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int kr = 32 * tt + lr;
-      koff[tt][s] = kr * 128 + (((2 * s + g) ^ swz8(kr)) << 4);
+      koff[tt][s] = kr * 128 + (((2 * s + g) ^ swz32(kr)) << 4);
     }
 #pragma unroll
   for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int vr = 32 * ct + lr;
-      voff[ct][s] = vr * 128 + (((2 * s + g) ^ swz8(vr)) << 4);
+      voff[ct][s] = vr * 128 + (((2 * s + g) ^ swz32(vr)) << 4);
     }
   const float cq = qs[(size_t)bh * n_qb + I] * c0;
   // The selection list and the key scales do not change during this kernel: reading them through the constant
@@ -348,10 +365,11 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k3_attn(
       kmax = fmaxf(kmax, kv);
       early_ragged |= has_ragged && j < topk - 1 && J == last_kb;
       if (listed && w == 0) {
-        s_lj[j] = (uint16_t)J;
+        s_lj[j] = J;
         s_lc[j] = cq * kv;
       }
     }
+    if (listed && w == 0 && l < 4) s_lj[topk + l] = blk(topk - 1);
     kmax = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(wave_max_f32(kmax))));
     const bool elsewhere = __ballot(early_ragged) != 0;
     const bool tail_ragged = has_ragged && blk(topk - 1) == last_kb;
@@ -376,9 +394,10 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k3_attn(
       constexpr bool L = decltype(listc)::value;
       unsigned char* const ks[3] = {k0, k1, k2};
       unsigned char* const vs[3] = {v0, v1, v2};
-      auto put_kJ = [&](int J, unsigned char* dst) {
-        stage_k<NW>(rk, (uint32_t)J * (kBlkK * kD), J == last_kb ? so_last : so_full, dst);
-      };
+      // K tiles use the full-block offsets even for a ragged last block: its rows past N lie beyond the
+      // descriptor's range, so those loads return zeros without touching memory, and the ragged pass masks the
+      // keys anyway
+      auto put_kJ = [&](int J, unsigned char* dst) { stage_k<NW>(rk, (uint32_t)J * (kBlkK * kD), so_full, dst); };
       auto put_vJ = [&](int J, unsigned char* dst) { stage_v<NW>(rv, (uint32_t)J * 16384u, dst); };
       auto put_k = [&](int j, unsigned char* dst) { put_kJ(blk(j), dst); };
       auto put_v = [&](int j, unsigned char* dst) { put_vJ(blk(j), dst); };
@@ -399,9 +418,9 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k3_attn(
       int lj = 0, jv = 0;
       float lc = 0.f;
       if constexpr (L) {
-        lj = s_lj[min(3, topk - 1)];
+        lj = s_lj[3];
         lc = s_lc[0];
-        jv = __builtin_amdgcn_readfirstlane((int)s_lj[min(2, topk - 1)]);
+        jv = __builtin_amdgcn_readfirstlane(s_lj[2]);
       }
       auto iter_full = [&](int j, auto ph) {
         constexpr int P = decltype(ph)::value;
@@ -412,7 +431,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k3_attn(
           c = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(lc)));
           put_kJ(J3, ks[P]);
           put_vJ(jv, vs[(P + 2) % 3]);
-          lj = s_lj[min(j + 4, topk - 1)];
+          lj = s_lj[j + 4];
           lc = s_lc[j + 1];
           jv = J3;
         } else {

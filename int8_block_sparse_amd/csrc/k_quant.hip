@@ -168,7 +168,7 @@ __device__ __forceinline__ void load_v_rows(const uint16_t* __restrict__ src, in
 }
 
 // V^T image of one key block for the attention kernel: [128 channels][64 keys] bf16, 16 KB, each channel row's
-// keys in MFMA slot order (key_pos16 within every 16) and its 16-byte chunks XOR-swizzled (swz8), exactly the
+// keys in MFMA slot order (key_pos16 within every 16) and its 16-byte chunks XOR-swizzled (swz32), exactly the
 // LDS layout the attention kernel reads; keys past a ragged block's end are zero. 256 threads: thread t holds
 // (load_v_rows) channels 8*(t%16)..+7 of keys 4*(t/16)..+3.
 __device__ __forceinline__ void write_v_image(const uint32_t (&wv)[4][4], unsigned char* __restrict__ img) {
@@ -179,7 +179,7 @@ __device__ __forceinline__ void write_v_image(const uint32_t (&wv)[4][4], unsign
     const int row = cg * 8 + e, sh = (e & 1) * 16;
     const uint32_t k0 = (wv[0][e >> 1] >> sh) & 0xffffu, k1 = (wv[1][e >> 1] >> sh) & 0xffffu;
     const uint32_t k2 = (wv[2][e >> 1] >> sh) & 0xffffu, k3 = (wv[3][e >> 1] >> sh) & 0xffffu;
-    *(uint2*)(img + row * 128 + (((pos >> 3) ^ swz8(row)) << 4) + ((pos & 7) << 1)) =
+    *(uint2*)(img + row * 128 + (((pos >> 3) ^ swz32(row)) << 4) + ((pos & 7) << 1)) =
         make_uint2(k0 | (k1 << 16), k2 | (k3 << 16));
   }
 }

@@ -193,13 +193,14 @@ __device__ __forceinline__ uint4 expand_bits8(uint32_t b) {
 // (J x x) as hi + lo bf16, fp32 accumulation.
 // grid (kStateX / 128 column groups, ceil(n_qb / 640) query-block chunks, BH), 512 threads (8 waves).
 // Step = 32 key blocks (two MFMA k-steps of 16) = one mask word per query block. At the start of step s the
-// workgroup issues buffer loads to LDS of the [32][128] fp32 table slice of step s+2 (16 KB contiguous) and of
-// the chunk's 640 mask words of step s+1; during step s the waves run its MFMAs
-// and rebuild slice s+1 into B fragments (hi, lo). Each wave forms its own A operands in registers: the byte
-// of its row's mask word for (sub-step, lane half) becomes 8 bf16 through two reads of a 16-entry nibble table
-// kept in 32 lane-private copies (conflict-free). One wait for all loads plus one barrier per step orders
-// everything; every buffer is double and its own LDS object, so the compiler can tell the buffers being filled
-// from those being read.
+// workgroup issues buffer loads to LDS of the [32][128] fp32 table slice of step s+3 (16 KB contiguous) and of
+// the chunk's 640 mask words of step s+2; during step s the waves run its MFMAs and rebuild slice s+1 into B
+// fragments (hi, lo). Each wave forms its own A operands in registers: the byte of its row's mask word for
+// (sub-step, lane half) becomes 8 bf16 through one read of a 256-entry byte table (at ~90% ones most lanes
+// read entry 0xFF, which the LDS broadcasts). One wait plus one barrier per step orders everything; the wait leaves the previous
+// step's loads in flight, so every load has two steps to land. Slices, words and B fragments each rotate
+// through three buffers, each its own LDS object, so the compiler can tell the buffers being filled from those
+// being read.
 // Wave w owns query tiles 5 (w / 2) .. +4 and column tiles 2 (w % 2), +1: 10 output tiles of 32 x 32, each A
 // operand feeding 4 MFMAs.
 // ---------------------------------------------------------------------------------------------------------
@@ -207,9 +208,12 @@ constexpr int kGemmIT = 20;  // query-block tiles of 32 per workgroup
 constexpr int kGemmThreads = 512;
 constexpr int kGemmRows = kGemmIT * 32;  // query blocks per workgroup; mask rows are padded to a multiple
 
-__device__ __forceinline__ void gemm_wait_sync() {
+// wait until at most N of this wave's vector-memory operations are in flight (and every LDS operation is done),
+// then a workgroup barrier
+template <int N> __device__ __forceinline__ void gemm_sync() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
   asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt((0 & 15) | (7 << 4));  // vmcnt(0) lgkmcnt(0)
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4));  // vmcnt(N) lgkmcnt(0)
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
@@ -218,11 +222,13 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k4_gemm(const float* __restri
                                                           const uint32_t* __restrict__ mask,
                                                           float* __restrict__ state_m, int n_qb, int n_kb,
                                                           int n_kbw, int qpad) {
-  __shared__ __attribute__((aligned(1024))) float s_st0[4 * 32 * 32], s_st1[4 * 32 * 32];  // [tile][row][32]
-  __shared__ __attribute__((aligned(1024))) uint4 s_bh0[2 * 4 * 64], s_bh1[2 * 4 * 64];    // [sub][tile][lane]
-  __shared__ __attribute__((aligned(1024))) uint4 s_bl0[2 * 4 * 64], s_bl1[2 * 4 * 64];
-  __shared__ __attribute__((aligned(1024))) uint32_t s_w0[kGemmRows + 128], s_w1[kGemmRows + 128];  // mask words
-  __shared__ __attribute__((aligned(1024))) uint2 s_nib[16 * 32];  // [nibble][copy]: 4 bf16 of 0 / 1.0
+  // three-slot rings: table slices [row][128] fp32, B fragments [sub][tile][lane], mask words
+  __shared__ __attribute__((aligned(1024))) float s_st0[32 * 128], s_st1[32 * 128], s_st2[32 * 128];
+  __shared__ __attribute__((aligned(1024))) uint4 s_bh0[2 * 4 * 64], s_bh1[2 * 4 * 64], s_bh2[2 * 4 * 64];
+  __shared__ __attribute__((aligned(1024))) uint4 s_bl0[2 * 4 * 64], s_bl1[2 * 4 * 64], s_bl2[2 * 4 * 64];
+  __shared__ __attribute__((aligned(1024))) uint32_t s_w0[kGemmRows + 128], s_w1[kGemmRows + 128],
+      s_w2[kGemmRows + 128];
+  __shared__ __attribute__((aligned(1024))) uint4 s_lut[256];  // byte -> 8 bf16 of 0 / 1.0, element i = bit i
   constexpr int n_xt = kStateX / 128;
   const int xg = blockIdx.x, ic = blockIdx.y, bh = blockIdx.z;
   const int t = threadIdx.x, w = __builtin_amdgcn_readfirstlane(t >> 6), l = t & 63, g = l >> 5, lr = l & 31;
@@ -233,49 +239,60 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k4_gemm(const float* __restri
       const_cast<float*>(table + (size_t)bh * n_xt * n_kb * 128), (short)0, n_xt * n_kb * 128 * 4, 0x00020000);
   const __amdgpu_buffer_rsrc_t rm = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint32_t*>(mask + (size_t)bh * n_kbw * qpad), (short)0, n_kbw * qpad * 4, 0x00020000);
-  {
-    const int n = t >> 5;  // 16 x 32 entries
-    const uint32_t lo = ((n & 1) ? 0x3F80u : 0u) | ((n & 2) ? 0x3F800000u : 0u);
-    const uint32_t hi = ((n & 4) ? 0x3F80u : 0u) | ((n & 8) ? 0x3F800000u : 0u);
-    s_nib[t] = make_uint2(lo, hi);
+  if (t < 256) {
+    uint32_t d[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) d[k] = ((t >> (2 * k)) & 1 ? 0x3F80u : 0u) | ((t >> (2 * k + 1)) & 1 ? 0x3F800000u : 0u);
+    s_lut[t] = make_uint4(d[0], d[1], d[2], d[3]);
   }
 
   // mask words of step ss for the chunk's rows: 3 loads of 1 KB (768 words; the last 128 are slack, and the
   // descriptor bounds return 0 past the end)
+  // (the lane part of every load offset is the loop-invariant l * 16; the rest is uniform and goes in soffset)
+  const uint32_t lane16 = (uint32_t)l * 16u;
   auto dma_w = [&](int ss, uint32_t* dst) {
     if (w < 3)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rm, (__attribute__((address_space(3))) void*)(dst + 256 * w), 16,
-                                               (uint32_t)(((size_t)ss * qpad + I0 + 256 * w) * 4 + l * 16), 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rm, (__attribute__((address_space(3))) void*)(dst + 256 * w), 16, lane16,
+                                               (uint32_t)((ss * qpad + I0 + 256 * w) * 4), 0, 0);
   };
-  // table slice of step ss: rows 32 ss .. +31 of column group xg ([row][128] fp32, 16 KB contiguous; rows past
-  // n_kb are clamped to n_kb - 1, where the mask is 0); wave w loads rows 4w .. 4w+3, two rows per 1 KB load
+  // table slice of step ss: rows 32 ss .. +31 of column group xg ([row][128] fp32, 16 KB contiguous); wave w loads
+  // rows 4w .. 4w+3, two adjacent rows per 1 KB load. Rows past n_kb, whose mask bits are 0, read the next column
+  // group's (finite) rows, or lie past the descriptor's range for the last group and read as zeros.
   auto dma_st = [&](int ss, float* dst) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const int row = 32 * ss + 4 * w + 2 * h + (l >> 5);
-      const uint32_t off = (uint32_t)((((size_t)xg * n_kb + min(row, n_kb - 1)) * 128 + (l & 31) * 4) * 4);
+      const uint32_t base = (uint32_t)((xg * n_kb + 32 * ss + 4 * w + 2 * h) * 512);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rt, (__attribute__((address_space(3))) void*)(dst + (4 * w + 2 * h) * 128),
-                                               16, off, 0, 0, 0);
+                                               16, lane16, base, 0, 0);
     }
   };
-  // B fragments of one step from a staging slice, in 2 pieces (sub-steps): thread = (column tile t>>7, half h,
-  // lane l) -> rows 16 sub + 8 g + 4 h .. +3 of column lr
-  auto build_b = [&](int sub, const float* __restrict__ st, uint4* bh_, uint4* bl_) {
-    const int xt = t >> 7, h = (t >> 6) & 1;
-    const float* c = st + (16 * sub + 8 * g + 4 * h) * 128 + 32 * xt + lr;
-    uint32_t h01, l01, h23, l23;
-    split2(c[0], c[128], h01, l01);
-    split2(c[256], c[384], h23, l23);
-    const int fi = (sub * 4 + xt) * 64 + l;
-    ((uint2*)&bh_[fi])[h] = make_uint2(h01, h23);
-    ((uint2*)&bl_[fi])[h] = make_uint2(l01, l23);
+  // B fragments of one step from a staging slice, in 2 pieces (sub-steps). Thread t = (column tile xt = t>>7,
+  // fragment lane fl = (t>>1)&63, half h = t&1) takes rows 16 sub + 8 (fl>>5) + 4 h .. +3 of column 32 xt +
+  // (fl&31) and writes 8 bytes of the hi and of the lo fragment: consecutive threads write consecutive 8-byte
+  // pieces. The reads (b_load) are issued two slots before the split and the writes (b_store).
+  const int b_xt = t >> 7, b_fl = (t >> 1) & 63, b_h = t & 1;
+  auto b_load = [&](int sub, const float* __restrict__ st, float (&v)[4]) {
+    const float* c = st + (16 * sub + 8 * (b_fl >> 5) + 4 * b_h) * 128 + 32 * b_xt + (b_fl & 31);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = c[128 * k];
   };
-  // A operand: byte (2 sub + g) of the row's word -> 8 bf16 from the lane's copy of the nibble table
-  const uint2* nib = s_nib + lr;
+  auto b_store = [&](int sub, const float (&v)[4], uint4* bh_, uint4* bl_) {
+    uint32_t h01, l01, h23, l23;
+    split2(v[0], v[1], h01, l01);
+    split2(v[2], v[3], h23, l23);
+    const int fi = (sub * 4 + b_xt) * 64 + b_fl;
+    ((uint2*)&bh_[fi])[b_h] = make_uint2(h01, h23);
+    ((uint2*)&bl_[fi])[b_h] = make_uint2(l01, l23);
+  };
+  auto build_b = [&](int sub, const float* __restrict__ st, uint4* bh_, uint4* bl_) {
+    float v[4];
+    b_load(sub, st, v);
+    b_store(sub, v, bh_, bl_);
+  };
+  // A operand: byte (2 sub + g) of the row's word -> 8 bf16 from the byte table (mostly 0xFF: broadcast reads)
   auto a_frag = [&](uint32_t word, int sub) {
-    const uint32_t b = word >> (16 * sub + 8 * g);
-    const uint2 lo = nib[(b & 15u) * 32], hi = nib[((b >> 4) & 15u) * 32];
-    return __builtin_bit_cast(v8bf, make_uint4(lo.x, lo.y, hi.x, hi.y));
+    const uint32_t b = (word >> (16 * sub + 8 * g)) & 0xFFu;
+    return __builtin_bit_cast(v8bf, s_lut[b]);
   };
 
   // wave w: query tiles 5 (w / 2) .. +4, column tiles 2 (w % 2), +1; acc[2 q + c]
@@ -287,9 +304,18 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k4_gemm(const float* __restri
   // one step with static buffers
   auto step = [&](int ss, const uint32_t* __restrict__ W, const uint4* __restrict__ Bh, const uint4* __restrict__ Bl,
                   const float* __restrict__ st_next, uint4* bh_next, uint4* bl_next, uint32_t* w_fill, float* st_fill) {
-    gemm_wait_sync();  // words ss, slice ss+1 landed; B(ss) built; the buffers filled below are free
-    if (ss + 2 < nss) dma_st(ss + 2, st_fill);
-    if (ss + 1 < nss) dma_w(ss + 1, w_fill);
+    // Words ss and slice ss+1 (issued two steps back) have landed and B(ss) is built; the loads this wave
+    // issued in step ss-1 (slice ss+2, words ss+1) may stay in flight. The buffers filled below are free. The
+    // loads are issued even past the last step (they then read zeros or finite rows that no mask bit selects),
+    // so that every wave has a fixed count in flight.
+    if (ss == 0)
+      gemm_sync<0>();
+    else if (w < 3)
+      gemm_sync<3>();
+    else
+      gemm_sync<2>();
+    dma_st(ss + 3, st_fill);
+    dma_w(ss + 2, w_fill);
     uint32_t wq[5];
 #pragma unroll
     for (int q = 0; q < 5; ++q) wq[q] = W[32 * (wit + q) + lr];
@@ -303,6 +329,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k4_gemm(const float* __restri
       }
     // 10 slots (sub, q): 4 MFMAs (2 column tiles x hi/lo) on the A operand formed two slots before
     v8bf af[10];
+    float bv[4];  // staging values of the B build in flight
 #pragma unroll
     for (int i = 0; i < 2; ++i) af[i] = a_frag(wq[i % 5], i / 5);
 #pragma unroll
@@ -315,22 +342,28 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k4_gemm(const float* __restri
         acc[2 * q + c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bhi[sub][c], acc[2 * q + c], 0, 0, 0);
         acc[2 * q + c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], blo[sub][c], acc[2 * q + c], 0, 0, 0);
       }
-      // B fragments of step ss+1 (past the end: unused)
-      if (i == 2 || i == 7) build_b(i / 5, st_next, bh_next, bl_next);
+      // B fragments of step ss+1 (past the end: unused): reads in slots 0 and 5, split and writes in 2 and 7
+      if (i == 0 || i == 5) b_load(i / 5, st_next, bv);
+      if (i == 2 || i == 7) b_store(i / 5, bv, bh_next, bl_next);
     }
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // prologue: slices 0 and 1, words 0; B fragments of step 0
+  // prologue: slices 0-2, words 0-1; B fragments of step 0. Step ss keeps words ss in s_w[ss % 3], slice ss in
+  // s_st[ss % 3] and B(ss) in s_b*[ss % 3]: it builds B(ss+1) from slice ss+1, and refills the slice slot of
+  // ss (slice ss+3) and the word slot of ss-1 (words ss+2).
   dma_st(0, s_st0);
-  if (nss > 1) dma_st(1, s_st1);
+  dma_st(1, s_st1);
+  dma_st(2, s_st2);
   dma_w(0, s_w0);
-  gemm_wait_sync();
+  dma_w(1, s_w1);
+  gemm_sync<0>();
   build_b(0, s_st0, s_bh0, s_bl0);
   build_b(1, s_st0, s_bh0, s_bl0);
-  for (int ss = 0; ss < nss; ss += 2) {
-    step(ss, s_w0, s_bh0, s_bl0, s_st1, s_bh1, s_bl1, s_w1, s_st0);
-    if (ss + 1 < nss) step(ss + 1, s_w1, s_bh1, s_bl1, s_st0, s_bh0, s_bl0, s_w0, s_st1);
+  for (int ss = 0; ss < nss; ss += 3) {
+    step(ss, s_w0, s_bh0, s_bl0, s_st1, s_bh1, s_bl1, s_w2, s_st0);
+    if (ss + 1 < nss) step(ss + 1, s_w1, s_bh1, s_bl1, s_st2, s_bh2, s_bl2, s_w0, s_st1);
+    if (ss + 2 < nss) step(ss + 2, s_w2, s_bh2, s_bl2, s_st0, s_bh0, s_bl0, s_w1, s_st2);
   }
 
   // Store. acc[2q + c][r] is C[I][x] with I = I0 + 32 (wit + q) + 8(r/4) + 4g + r%4, x = 128 xg + 32 (wxt + c) + lr.

@@ -265,3 +265,8 @@ def test_full_size_sla_480p():
 
 def test_full_size_sla_720p_pair():
     sampled_case(3, [(0, 0), (1, 39)])
+
+
+def test_full_size_sla_1080p_long():
+    # the largest layer shape (N = 269280 tokens, 4208 key blocks, top-k 210), two heads sampled
+    sampled_case(4, [(0, 0), (0, 39)])

@@ -47,8 +47,9 @@ typedef enum {
 /* stages of sagesla_forward, in launch order (for the optional timing events) */
 #define SAGESLA_STAGE_QUANTIZE 0 /* K mean, smoothing, INT8 codes, scales, pooled means          */
 #define SAGESLA_STAGE_SELECT 1   /* block scores and top-k                                          */
-#define SAGESLA_STAGE_LINEAR 2   /* linear branch: block states, remaining-state gather, contraction */
-#define SAGESLA_STAGE_ATTN 3     /* block-sparse INT8 attention and the output epilogue (one kernel) */
+#define SAGESLA_STAGE_LINEAR 2   /* linear branch: block states and the remaining state of each query block */
+#define SAGESLA_STAGE_ATTN 3     /* block-sparse INT8 attention, then per query block the linear branch's
+                                    contraction with phi(Q) and W_p and the output (one kernel) */
 #define SAGESLA_NUM_STAGES 4
 
 /* flags */

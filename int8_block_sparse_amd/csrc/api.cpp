@@ -91,7 +91,6 @@ void make_plan(const sagesla_params* p, unsigned char* ws, Plan* pl) {
     pl->state = (float*)take(BH * nkb * kStateX * sizeof(float));
     pl->keep_mask = (uint32_t*)take(BH * (size_t)mask_row_pad(pl->n_qb) * ((nkb + 31) / 32) * sizeof(uint32_t));
     pl->state_m = (float*)take(BH * nqb * kStateX * sizeof(float));
-    pl->o_lin = (float*)take(BH * N * D * sizeof(float));
   }
   pl->ws_bytes = off;
   // caller-owned exports replace their workspace slice
@@ -103,7 +102,7 @@ void make_plan(const sagesla_params* p, unsigned char* ws, Plan* pl) {
   if (p->q_pool) pl->q_pool = p->q_pool;
   if (p->k_pool) pl->k_pool = p->k_pool;
   if (p->block_idx) pl->block_idx = p->block_idx;
-  if (p->o_lin && lin_active) pl->o_lin = p->o_lin;
+  pl->o_lin = lin_active ? p->o_lin : nullptr;  // optional export
 }
 
 sagesla_status check_workspace(const sagesla_params* p, const Plan& pl) {
@@ -205,13 +204,13 @@ sagesla_status sagesla_forward(const void* q, const void* k, const void* v, void
   SAGESLA_STEP(mark(p, SAGESLA_STAGE_LINEAR, 0, s));
   const bool lin_active = pl.linear && pl.topk < pl.n_kb;
   if (lin_active) {
-    SAGESLA_TRY(launch_linear(pl, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, s));
+    SAGESLA_TRY(launch_linear(pl, (const uint16_t*)k, (const uint16_t*)v, s));
   } else if (p->o_lin) {
     SAGESLA_TRY(launch_fill_f32(p->o_lin, (size_t)pl.BH * pl.N * kD, 0.f, s));
   }
   SAGESLA_STEP(mark(p, SAGESLA_STAGE_LINEAR, 1, s));
   SAGESLA_STEP(mark(p, SAGESLA_STAGE_ATTN, 0, s));
-  SAGESLA_TRY(launch_attn(pl, (uint16_t*)out, s));
+  SAGESLA_TRY(launch_attn(pl, (const uint16_t*)q, (uint16_t*)out, s));
   SAGESLA_STEP(mark(p, SAGESLA_STAGE_ATTN, 1, s));
 #undef SAGESLA_STEP
   return SAGESLA_OK;

@@ -35,7 +35,7 @@ struct Plan {
   float* state;         // [BH][kStateX / 128][n_kb][128]   per-block states, tiles of 128 columns
   uint32_t* keep_mask;  // [BH][ceil(n_kb/32)][mask_row_pad(n_qb)]   bit J set iff key block J is not selected
   float* state_m;       // [BH][n_qb][kStateX]   remaining (non-selected) state per query block
-  float* o_lin;         // [BH][N][D]
+  float* o_lin;         // [BH][N][D] optional export (caller-owned), written by the attention kernel
   size_t ws_bytes;
 };
 
@@ -47,9 +47,9 @@ hipError_t launch_quant(const Plan& p, const uint16_t* q, const uint16_t* k, con
 hipError_t launch_scores(const Plan& p, hipStream_t s);
 hipError_t launch_topk(const Plan& p, hipStream_t s);
 // K4: linear branch (block states, sum over the unselected blocks, contraction with phi(Q) and W_p)
-hipError_t launch_linear(const Plan& p, const uint16_t* q, const uint16_t* k, const uint16_t* v, hipStream_t s);
+hipError_t launch_linear(const Plan& p, const uint16_t* k, const uint16_t* v, hipStream_t s);
 // K3: block-sparse INT8 attention, epilogue adds the linear branch and writes bf16
-hipError_t launch_attn(const Plan& p, uint16_t* out, hipStream_t s);
+hipError_t launch_attn(const Plan& p, const uint16_t* q, uint16_t* out, hipStream_t s);
 // fills (graph-capture friendly replacements for memset)
 hipError_t launch_fill_f32(float* dst, size_t n, float val, hipStream_t s);
 // dynamic LDS of the kernels that size it at run time

@@ -7,7 +7,7 @@
 //   O_l[i] = phi(q_i) H_m / (phi(q_i) . Z_m),  H_m = sum_J H_J - sum_{J selected} H_J,  out += O_l W_p.
 // The projection is linear and the denominator is a scalar per row, so O_l W_p = (phi(q_i) H_m W_p) / den: the
 // per-block states and their gather stay in the D×D state space and W_p is applied once per query block, to the
-// product phi(Q_I) H_m, in the output kernel.
+// product phi(Q_I) H_m, in the attention kernel's epilogue (k_attn.hip), which adds O_l W_p to the sparse part.
 //
 // Kernels:
 //   k4_prep_wp   W_p^T with the MFMA key-slot order, bf16 (32 KB, once per call)
@@ -15,42 +15,21 @@
 //   k4_mask      per query block: bitmask of the key blocks it did not select
 //   k4_gemm      H_m = sum of the states of the unselected blocks, as the dense product keep-mask x table
 //                (bf16 MFMA; about 90% of the mask is ones at 10% top-k)
-//   k4_out       per query block: O_lin = (phi(Q) H_m) W_p / (phi(Q) . Z_m) (MFMA)
+// (the attention kernel's epilogue then forms O_lin = (phi(Q) H_m) W_p / (phi(Q) . Z_m) per query block, MFMA)
 // fp32 values enter the bf16 MFMAs as hi + lo bf16 pairs, so every product keeps ~16 significant bits.
 #include "device_common.h"
 #include "internal.h"
+#include "lin_common.h"
 
 namespace sagesla {
 
-// position of key/channel slot inside a 16-group such that the MFMA 32x32x16 lane (half g, slot i) reads
-// 8 consecutive positions: slot (g, i) <-> index 8*(i/4) + 4*g + (i%4); position 8*g + 4*(i/4) + (i%4).
-__device__ __forceinline__ int slot_pos16(int off) {  // off = index within the 16-group
-  return (off & 3) | ((off & 4) << 1) | ((off & 8) >> 1);
-}
-
-// A [128][128] bf16 plane as the output kernel keeps it in LDS (and the remaining state is stored): rows of
-// 256 B, 16-byte chunks XOR-swizzled by row. Byte offset of (row, col):
-__device__ __forceinline__ int out_off(int e, int c) { return e * 256 + ((((c >> 3) ^ e) & 15) << 4) + ((c & 7) << 1); }
-
-// W_p^T, positions permuted as above: wpt[f][p], p = slot_pos16 applied within each 16 of e, in the swizzled
+// W_p^T, positions permuted by slot_pos16: wpt[f][p], p = slot_pos16 applied within each 16 of e, in the swizzled
 // plane layout (a straight copy into LDS)
 __global__ __launch_bounds__(256) void k4_prep_wp(const uint16_t* __restrict__ wp, uint16_t* __restrict__ wpt) {
   const int i = blockIdx.x * 256 + threadIdx.x;  // 16384 elements
   const int e = i >> 7, f = i & 127;             // wp[e][f]
   const int p = (e & ~15) | slot_pos16(e & 15);
   wpt[out_off(f, p) >> 1] = wp[i];
-}
-
-// phi(x) = elu(x) + 1: x + 1 for x > 0, e^x otherwise (hardware exp2 of x log2(e); the values then enter the
-// MFMAs as hi + lo bf16 pairs, ~16 significant bits)
-__device__ __forceinline__ float phi_f(float x) {
-  return x > 0.f ? x + 1.f : __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
-}
-
-// two fp32 values -> bf16 pairs hi = bf16(x) and lo = bf16(x - hi), packed as (x0, x1)
-__device__ __forceinline__ void split2(float x0, float x1, uint32_t& hi, uint32_t& lo) {
-  hi = pack_bf16x2(x0, x1);
-  lo = pack_bf16x2(x0 - __uint_as_float(hi << 16), x1 - __uint_as_float(hi & 0xffff0000u));
 }
 
 // ---------------------------------------------------------------------------------------------------------
@@ -422,134 +401,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k4_gemm(const float* __restri
     }
 }
 
-// ---------------------------------------------------------------------------------------------------------
-// k4_out: one workgroup (4 waves) per (bh, I) query block.
-//   U^T[e][i] = sum_c H_m^T[e][c] phi(Q)^T[c][i]        (A = H_m^T hi/lo from LDS, B = phi(Q) hi/lo in registers)
-//   O^T[f][i] = sum_e W_p^T[f][e] U^T[e][i] / den[i]     (A = W_p^T from LDS, B = U^T hi/lo from the accumulators)
-// with den[i] = phi(q_i) . Z_m. The block's remaining state arrives as bf16 hi and lo planes already in the LDS
-// layout (k4_gemm wrote them so): buffer loads to LDS bring them in while phi(Q) is formed; after the first
-// product the hi plane's space takes W_p^T the same way. Wave w handles its own 32 rows. Products
-// hi*hi + hi*lo + lo*hi keep ~16 significant bits.
-// ---------------------------------------------------------------------------------------------------------
-template <int BLKQ>
-__global__ __launch_bounds__(BLKQ * 2) void k4_out(const uint16_t* __restrict__ q, const float* __restrict__ state_m,
-                                                  const uint16_t* __restrict__ wpt, float* __restrict__ o_lin, int N,
-                                                  int n_qb, int total) {
-  constexpr int NW = BLKQ / 32;
-  __shared__ __attribute__((aligned(1024))) unsigned char s_hi[kD * 256];
-  __shared__ __attribute__((aligned(1024))) unsigned char s_lo[kD * 256];
-  __shared__ float s_z[kD];
-  const int item = xcd_remap(blockIdx.x, total);
-  const int bh = item / n_qb, I = item % n_qb;
-  const int t = threadIdx.x, w = __builtin_amdgcn_readfirstlane(t >> 6), l = t & 63, g = l >> 5, lr = l & 31;
-  const size_t rec = ((size_t)bh * n_qb + I) * (size_t)kStateX * 4;
-  const unsigned char* srec = (const unsigned char*)state_m + rec;  // [hi plane 32 KB][lo plane 32 KB][Z fp32]
-  float4 zv = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (t < kD / 4) zv = *(const float4*)(srec + 65536 + 16 * t);  // issued before the plane loads: waited alone
-  {  // the planes: 64 buffer loads of 1 KB straight into LDS
-    const __amdgpu_buffer_rsrc_t rb =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(srec), (short)0, kStateX * 4, 0x00020000);
-#pragma unroll
-    for (int i = 0; i < 64 / NW; ++i) {
-      const int k = w + NW * i;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (__attribute__((address_space(3))) void*)((k < 32 ? s_hi : s_lo) + (k & 31) * 1024),
-                                               16, l * 16, k * 1024, 0, 0);
-    }
-  }
-  if (t < kD / 4) *(float4*)(s_z + 4 * t) = zv;
-  __syncthreads();  // s_z
-
-  const int row = I * BLKQ + 32 * w + lr;
-  const bool rok = row < N;
-  const uint16_t* qrow = q + ((size_t)bh * N + (rok ? row : 0)) * kD;
-  v8bf bqh[8], bql[8];
-  float den = 0.f;
-#pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    const int c0 = 16 * s + 8 * g;
-    uint4 wq = make_uint4(0, 0, 0, 0);
-    if (rok) wq = *(const uint4*)(qrow + c0);
-    const uint32_t ww[4] = {wq.x, wq.y, wq.z, wq.w};
-    uint32_t hw[4], lw[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const float p0 = phi_f(bf16_lo(ww[u])), p1 = phi_f(bf16_hi(ww[u]));
-      den = fmaf(p0, s_z[c0 + 2 * u], den);
-      den = fmaf(p1, s_z[c0 + 2 * u + 1], den);
-      split2(p0, p1, hw[u], lw[u]);
-    }
-    bqh[s] = __builtin_bit_cast(v8bf, make_uint4(hw[0], hw[1], hw[2], hw[3]));
-    bql[s] = __builtin_bit_cast(v8bf, make_uint4(lw[0], lw[1], lw[2], lw[3]));
-  }
-  den += swap_halves_f32(den);
-  __builtin_amdgcn_s_waitcnt(7 << 4);  // vmcnt(0) lgkmcnt(0): this wave's plane loads have landed
-  __syncthreads();                      // ... and every other wave's
-  const float inv = 1.f / den;
-
-  // ---- U^T = H_m^T phi(Q)^T
-  v16f acc[4];
-#pragma unroll
-  for (int et = 0; et < 4; ++et) {
-    acc[et] = (v16f){};
-    const int e = 32 * et + lr;
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const int off = out_off(e, 16 * s + 8 * g);
-      const v8bf ah = *(const v8bf*)(s_hi + off);
-      const v8bf al = *(const v8bf*)(s_lo + off);
-      acc[et] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bqh[s], acc[et], 0, 0, 0);
-      acc[et] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bql[s], acc[et], 0, 0, 0);
-      acc[et] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bqh[s], acc[et], 0, 0, 0);
-    }
-  }
-  __syncthreads();  // every wave is done with the state planes
-  {  // W_p^T (already in the plane layout) into the hi plane's space: 32 loads of 1 KB
-    const __amdgpu_buffer_rsrc_t rw =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(wpt), (short)0, kD * kD * 2, 0x00020000);
-#pragma unroll
-    for (int i = 0; i < 32 / NW; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (__attribute__((address_space(3))) void*)(s_hi + (w + NW * i) * 1024),
-                                               16, l * 16, (w + NW * i) * 1024, 0, 0);
-    __builtin_amdgcn_s_waitcnt(7 << 4);
-  }
-  __syncthreads();
-
-  // ---- O^T = W_p^T U^T: B operand slot (g, i) of step s2 is e = 16 s2 + 8(i/4) + 4g + i%4, i.e. accumulator
-  // register 8(s2%2) + i of tile s2/2 in this lane; W_p^T rows hold e in the matching permuted order.
-  v16f acc2[4];
-#pragma unroll
-  for (int ft = 0; ft < 4; ++ft) acc2[ft] = (v16f){};
-#pragma unroll
-  for (int s2 = 0; s2 < 8; ++s2) {
-    const int src = s2 >> 1, r0 = 8 * (s2 & 1);
-    uint32_t hw[4], lw[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) split2(acc[src][r0 + 2 * u], acc[src][r0 + 2 * u + 1], hw[u], lw[u]);
-    const v8bf bhi = __builtin_bit_cast(v8bf, make_uint4(hw[0], hw[1], hw[2], hw[3]));
-    const v8bf blo = __builtin_bit_cast(v8bf, make_uint4(lw[0], lw[1], lw[2], lw[3]));
-#pragma unroll
-    for (int ft = 0; ft < 4; ++ft) {
-      const v8bf a = *(const v8bf*)(s_hi + out_off(32 * ft + lr, 16 * s2 + 8 * g));
-      acc2[ft] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bhi, acc2[ft], 0, 0, 0);
-      acc2[ft] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, blo, acc2[ft], 0, 0, 0);
-    }
-  }
-  if (rok) {
-    float* orow = o_lin + ((size_t)bh * N + row) * kD;
-#pragma unroll
-    for (int ft = 0; ft < 4; ++ft)
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int f0 = 32 * ft + 8 * r4 + 4 * g;
-        *(float4*)(orow + f0) = make_float4(acc2[ft][4 * r4] * inv, acc2[ft][4 * r4 + 1] * inv,
-                                            acc2[ft][4 * r4 + 2] * inv, acc2[ft][4 * r4 + 3] * inv);
-      }
-  }
-}
-
 int mask_row_pad(int n_qb) { return (n_qb + kGemmRows - 1) / kGemmRows * kGemmRows; }
 
-hipError_t launch_linear(const Plan& p, const uint16_t* q, const uint16_t* k, const uint16_t* v, hipStream_t s) {
+hipError_t launch_linear(const Plan& p, const uint16_t* k, const uint16_t* v, hipStream_t s) {
   hipLaunchKernelGGL(k4_prep_wp, dim3(kD * kD / 256), dim3(256), 0, s, (const uint16_t*)p.w_proj, p.wpt);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -561,14 +415,6 @@ hipError_t launch_linear(const Plan& p, const uint16_t* q, const uint16_t* k, co
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(k4_gemm, dim3(kStateX / 128, qpad / kGemmRows, p.BH), dim3(kGemmThreads), 0, s, p.state,
                      p.keep_mask, p.state_m, p.n_qb, p.n_kb, n_kbw, qpad);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  const int total = p.BH * p.n_qb;
-  if (p.blk_q == 128)
-    hipLaunchKernelGGL(k4_out<128>, dim3(total), dim3(256), 0, s, q, p.state_m, p.wpt, p.o_lin, p.N, p.n_qb,
-                       total);
-  else
-    hipLaunchKernelGGL(k4_out<64>, dim3(total), dim3(128), 0, s, q, p.state_m, p.wpt, p.o_lin, p.N, p.n_qb,
-                       total);
   return hipGetLastError();
 }
 

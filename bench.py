@@ -140,6 +140,10 @@ def main():
     units = wl.B * wl.H * wl.n_qb * wl.topk  # selected (query block, key block) pairs
     ops_i8 = units * 2.0 * wl.blk_q * wl.blk_k * wl.D  # S = Q K^T on INT8 MFMA
     ops_bf16 = units * 2.0 * wl.blk_q * wl.blk_k * wl.D  # O = P V on BF16 MFMA
+    if wl.linear and wl.topk < wl.n_kb:
+        # its epilogue contracts each query block with the linear branch's remaining state and W_p: phi(Q) H_m
+        # as 3 bf16 products (hi*hi + hi*lo + lo*hi) and (.) W_p as 2 (hi and lo of the first result)
+        ops_bf16 += wl.B * wl.H * wl.n_qb * 5 * 2.0 * wl.blk_q * wl.D * wl.D
     t_attn = st_avg["attn"] * 1e-3
     int8_equiv = (ops_i8 + ops_bf16 * PEAK_INT8_TOPS / PEAK_BF16_TFLOPS) / t_attn / 1e12
     traffic = read_counters()
@@ -162,7 +166,7 @@ def main():
                    "linear": wl.linear, "parallelism": "single GPU"},
         "stages_ms": {n: round(t, 4) for n, t in st_avg.items()},
         "roofline": {
-            "kernel": "k3_attn (block-sparse INT8 attention)",
+            "kernel": "k3_attn (block-sparse INT8 attention + linear-branch epilogue)",
             "bound": "mfma",
             "achieved": round(int8_equiv, 1),
             "peak": PEAK_INT8_TOPS,

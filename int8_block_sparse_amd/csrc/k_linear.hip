@@ -282,7 +282,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k4_gemm(const float* __restri
 
   // one step with static buffers
   auto step = [&](int ss, const uint32_t* __restrict__ W, const uint4* __restrict__ Bh, const uint4* __restrict__ Bl,
-                  const float* __restrict__ st_next, uint4* bh_next, uint4* bl_next, uint32_t* w_fill, float* st_fill) {
+                  const float* __restrict__ st_next, uint4* __restrict__ bh_next, uint4* __restrict__ bl_next,
+                  uint32_t* __restrict__ w_fill, float* __restrict__ st_fill) {
     // Words ss and slice ss+1 (issued two steps back) have landed and B(ss) is built; the loads this wave
     // issued in step ss-1 (slice ss+2, words ss+1) may stay in flight. The buffers filled below are free. The
     // loads are issued even past the last step (they then read zeros or finite rows that no mask bit selects),

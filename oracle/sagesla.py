@@ -187,25 +187,32 @@ def select_topk(scores: np.ndarray, k: int):
 # --------------------------------------------------------------------------------------------------------
 # 6. INT8 block-sparse attention over the selected blocks  ([TD-news] §三(一) item 3, §三(二) item 3)
 # --------------------------------------------------------------------------------------------------------
-def sparse_attention(q_codes, q_scales, k_codes, k_scales, V, idx, blk_q, blk_k, sm_scale, blocks=None):
+def sparse_attention(q_codes, q_scales, k_codes, k_scales, V, idx, blk_q, blk_k, sm_scale, blocks=None,
+                     q_group=None, k_group=None):
     """O_s[i] = sum_j softmax_j(z_ij) v_j over the keys j of the selected blocks of i's query block.
 
-    z_ij = (codeQ_i . codeK_j) * s_q(I) * s_k(J) * sm_scale; the integer dot product is exact in fp64.
+    z_ij = (codeQ_i . codeK_j) * s_q(i) * s_k(j) * sm_scale; the integer dot product is exact in fp64. s_q(i) is
+    the scale of the q_group rows that hold row i (default q_group = blk_q: one scale per query block) and s_k(j)
+    that of the k_group keys that hold key j (default blk_k). The finer "thread-level" variant ([TD-news]
+    §三(一) item 2) uses groups of 32 tokens, so every 32×32 tile of scores has its own pair of scales.
     The softmax is normalised over the selected keys only. A query block with no selected block gets 0.
     blocks: optional list of query blocks to compute (the rows of the others are left 0)."""
     N, D = V.shape
+    gq = blk_q if q_group is None else q_group
+    gk = blk_k if k_group is None else k_group
     V = np.asarray(V, np.float64)
     out = np.zeros((N, D), dtype=np.float64)
     qc = q_codes.astype(np.float64)
     kc = k_codes.astype(np.float64)
+    qs_row = np.repeat(np.asarray(q_scales, np.float64), gq)[:N]  # scale of each row
+    ks_row = np.repeat(np.asarray(k_scales, np.float64), gk)[:N]  # scale of each key
     for I in (range(n_blocks(N, blk_q)) if blocks is None else blocks):
         rows = block_rows(N, blk_q, I)
         sel = list(idx[I])
         if not sel:
             continue
         key_rows = np.concatenate([np.arange(N)[block_rows(N, blk_k, J)] for J in sel])
-        kscale = np.concatenate([np.full(block_rows(N, blk_k, J).stop - J * blk_k, k_scales[J]) for J in sel])
-        z = (qc[rows] @ kc[key_rows].T) * q_scales[I] * kscale[None, :] * sm_scale
+        z = (qc[rows] @ kc[key_rows].T) * qs_row[rows][:, None] * ks_row[key_rows][None, :] * sm_scale
         z = z - z.max(axis=1, keepdims=True)
         p = np.exp(z)
         out[rows] = (p @ V[key_rows]) / p.sum(axis=1, keepdims=True)
@@ -283,13 +290,14 @@ def project(O_l, W_p):
 # 8. the whole forward
 # --------------------------------------------------------------------------------------------------------
 def forward_head(Q, K, V, W_p, blk_q, blk_k, topk, *, linear=True, smooth_k=True, quant=True,
-                 sm_scale=None, mask=None, blocks=None):
+                 sm_scale=None, mask=None, blocks=None, quant_group=None):
     """SageSLA forward for one (b, h) slice. Q, K, V: [N, D] arrays of exact bf16 values; W_p: [D, D].
 
     Switches for the tests: smooth_k=False skips K-mean smoothing, quant=False attends with the unquantized
     fp32 values, mask (int [n_qb, k] ascending) replaces the selection (used to compare with a GPU's own
-    selection), blocks (list of query blocks) limits the attention outputs to those blocks. Returns a dict with
-    every intermediate and 'out' (fp64)."""
+    selection), blocks (list of query blocks) limits the attention outputs to those blocks, quant_group (rows
+    per INT8 scale, for Q and K alike) replaces the default of one scale per block with finer groups (32 for the
+    pages' thread-level granularity). Returns a dict with every intermediate and 'out' (fp64)."""
     Q = np.asarray(Q, np.float64)
     K = np.asarray(K, np.float64)
     V = np.asarray(V, np.float64)
@@ -304,8 +312,10 @@ def forward_head(Q, K, V, W_p, blk_q, blk_k, topk, *, linear=True, smooth_k=True
         r["exact_sum_ok"] = True
         r["mu"] = np.zeros(D)
     kp = smooth(K, r["mu"])
-    r["q_codes"], r["q_scales"] = quantize(Q, blk_q)
-    r["k_codes"], r["k_scales"] = quantize(kp, blk_k)
+    gq = blk_q if quant_group is None else quant_group
+    gk = blk_k if quant_group is None else quant_group
+    r["q_codes"], r["q_scales"] = quantize(Q, gq)
+    r["k_codes"], r["k_scales"] = quantize(kp, gk)
     r["q_pool"] = pool(Q, blk_q)
     r["k_pool"] = pool(kp, blk_k)
     r["scores"] = block_scores(r["q_pool"], r["k_pool"])
@@ -313,7 +323,7 @@ def forward_head(Q, K, V, W_p, blk_q, blk_k, topk, *, linear=True, smooth_k=True
     idx = r["idx"] if mask is None else np.asarray(mask)
     if quant:
         r["o_s"] = sparse_attention(r["q_codes"], r["q_scales"], r["k_codes"], r["k_scales"], V, idx,
-                                    blk_q, blk_k, sm_scale, blocks=blocks)
+                                    blk_q, blk_k, sm_scale, blocks=blocks, q_group=gq, k_group=gk)
     else:
         ones_q = np.ones(n_blocks(N, blk_q))
         ones_k = np.ones(n_blocks(N, blk_k))

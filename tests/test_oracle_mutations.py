@@ -71,6 +71,13 @@ def _sparse_drop_ragged_tail(q_codes, q_scales, k_codes, k_scales, V, idx, blk_q
     return _orig["sparse_attention"](q_codes, q_scales, k_codes, k_scales, V, idx2, blk_q, blk_k, sm_scale, **kw)
 
 
+def _sparse_ignore_groups(q_codes, q_scales, k_codes, k_scales, V, idx, blk_q, blk_k, sm_scale, blocks=None,
+                          q_group=None, k_group=None):
+    # indexes finer scales as if there were one per block
+    return _orig["sparse_attention"](q_codes, q_scales, k_codes, k_scales, V, idx, blk_q, blk_k, sm_scale,
+                                     blocks=blocks)
+
+
 def _pool_sum(X, blk):
     return _orig["pool"](X, blk) * blk
 
@@ -90,6 +97,7 @@ MUTATIONS = {
     "kmean_first_block": ("k_mean", _kmean_first_block),
     "sparse_no_scale": ("sparse_attention", _sparse_no_scale),
     "sparse_drop_ragged_tail": ("sparse_attention", _sparse_drop_ragged_tail),
+    "sparse_ignore_groups": ("sparse_attention", _sparse_ignore_groups),
     "project_transposed": ("project", _project_transposed),
     "pool_sum": ("pool", _pool_sum),
 }
@@ -108,6 +116,8 @@ def _run_pins():
         lambda: pins.test_select_constant_keys_and_full(),
         lambda: pins.test_block_score_is_mean_token_score(),
         lambda: pins.test_sparse_bruteforce(rng()),
+        lambda: pins.test_sparse_bruteforce_groups(rng()),
+        lambda: pins.test_dense_equivalence_quantized_groups(pins.SMALL[1]),
         lambda: pins.test_linear_closed_form_all_marginal(pins.SMALL[0]),
         lambda: pins.test_linear_bruteforce_marginal_keys(rng()),
         lambda: pins.test_phi_matches_library(rng()),

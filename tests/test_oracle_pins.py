@@ -69,6 +69,24 @@ def test_dense_equivalence_quantized():
     np.testing.assert_allclose(r["out"], ref, atol=1e-12, rtol=0)
 
 
+@pytest.mark.parametrize("wl", SMALL[:3], ids=lambda w: f"N{w.N}-bq{w.blk_q}")
+def test_dense_equivalence_quantized_groups(wl):
+    # thread-level granularity ([TD-news] §三(一) item 2): one scale per 32 tokens of Q and of K. Top-k 100 %
+    # then equals dense attention on Q and smoothed K dequantized group by group (ragged last groups included)
+    Q, K, V, W = head(wl)
+    r = orc.forward_head(Q, K, V, W, wl.blk_q, wl.blk_k, wl.n_kb, linear=False, quant_group=32)
+    ng = -(-wl.N // 32)
+    assert len(r["q_scales"]) == ng and len(r["k_scales"]) == ng
+    for codes, scales in ((r["q_codes"], r["q_scales"]), (r["k_codes"], r["k_scales"])):
+        for g in range(ng):  # each group's absmax element maps to +-127
+            if scales[g] > 0:
+                assert np.max(np.abs(codes[32 * g: 32 * g + 32].astype(int))) == 127
+    Qd = r["q_codes"].astype(np.float64) * np.repeat(r["q_scales"], 32)[: wl.N, None]
+    Kd = r["k_codes"].astype(np.float64) * np.repeat(r["k_scales"], 32)[: wl.N, None]
+    ref = sdpa64(Qd, Kd, V, 1 / math.sqrt(wl.D))
+    np.testing.assert_allclose(r["out"], ref, atol=1e-12, rtol=0)
+
+
 # ---------------------------------------------------------------------------------------------------------
 # K-mean smoothing
 # ---------------------------------------------------------------------------------------------------------
@@ -230,6 +248,32 @@ def test_sparse_bruteforce(rng):
             for j in range(J * bk, min(N, (J + 1) * bk)):
                 dot = sum(int(qc[i, c]) * int(kc[j, c]) for c in range(D))
                 zs.append(dot * qs[I] * ks[J] * 0.3)
+                vs.append(V[j])
+        m = max(zs)
+        w = [math.exp(z - m) for z in zs]
+        ref = sum(wi * vi for wi, vi in zip(w, vs)) / sum(w)
+        np.testing.assert_allclose(out[i], ref, atol=1e-12, rtol=0)
+
+
+def test_sparse_bruteforce_groups(rng):
+    # one scale per 16 rows of Q and per 16 keys, groups 2^g apart in magnitude so a scale taken from the wrong
+    # group shows; blocks of 48 queries / 32 keys, ragged tails
+    N, D, bq, bk, grp = 150, 16, 48, 32, 16
+    mag = np.repeat(2.0 ** (np.arange(-(-N // grp)) % 5), grp)[:N, None]
+    Q = rng.standard_normal((N, D)) * mag
+    K = (rng.standard_normal((N, D)) + 1.0) * mag[::-1]
+    V = rng.standard_normal((N, D))
+    qc, qs = orc.quantize(Q, grp)
+    kc, ks = orc.quantize(K, grp)
+    nqb, nkb = orc.n_blocks(N, bq), orc.n_blocks(N, bk)
+    idx = np.stack([np.sort(rng.choice(nkb, 2, replace=False)) for _ in range(nqb)])
+    out = orc.sparse_attention(qc, qs, kc, ks, V, idx, bq, bk, 0.05, q_group=grp, k_group=grp)
+    for i in range(N):
+        zs, vs = [], []
+        for J in idx[i // bq]:
+            for j in range(J * bk, min(N, (J + 1) * bk)):
+                dot = sum(int(qc[i, c]) * int(kc[j, c]) for c in range(D))
+                zs.append(dot * qs[i // grp] * ks[j // grp] * 0.05)
                 vs.append(V[j])
         m = max(zs)
         w = [math.exp(z - m) for z in zs]

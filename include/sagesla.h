@@ -56,6 +56,9 @@ typedef enum {
 #define SAGESLA_LINEAR 0x1u         /* run the linear branch on the non-selected blocks (needs w_proj)      */
 #define SAGESLA_SMOOTH_K 0x2u       /* subtract the per-channel mean of K over all N tokens before quantizing */
 #define SAGESLA_USE_GIVEN_MASK 0x4u /* sagesla_forward reads block_idx instead of selecting (block_idx required) */
+#define SAGESLA_QUANT_GROUP32 0x8u  /* one INT8 scale per 32 tokens of Q and of K instead of one per block: the
+                                       "thread-level" granularity of [TD-news] §三(一) item 2, each 32×32 tile of
+                                       scores with its own pair of scales (q_scale/k_scale then hold n_g values) */
 
 typedef struct sagesla_params {
   int32_t B, H, N, D;   /* batch, heads, tokens, head dim (D == 128)                                       */
@@ -69,9 +72,10 @@ typedef struct sagesla_params {
   /* Optional intermediates (device, caller-owned). NULL keeps an intermediate inside the workspace; a
      non-NULL pointer makes the library write it there (and read it back from there in later stages).     */
   int8_t* q_i8;       /* [B][H][N][D]      INT8 codes of Q                                                */
-  float* q_scale;     /* [B][H][n_qb]      per query block: fp32(absmax/127), 0 for an all-zero block      */
+  float* q_scale;     /* [B][H][n_qb]      per query block: fp32(absmax/127), 0 for an all-zero block;
+                         [B][H][n_g] per 32 tokens with SAGESLA_QUANT_GROUP32 (n_g = ceil(N / 32))        */
   int8_t* k_i8;       /* [B][H][N][D]      INT8 codes of the smoothed K                                   */
-  float* k_scale;     /* [B][H][n_kb]                                                                      */
+  float* k_scale;     /* [B][H][n_kb]      (or [B][H][n_g] with SAGESLA_QUANT_GROUP32)                      */
   float* k_mean;      /* [B][H][D]         fp32(sum_t K[t][c] / N), zeros without SAGESLA_SMOOTH_K         */
   double* q_pool;     /* [B][H][n_qb][D]   mean of the raw Q rows of each query block                     */
   double* k_pool;     /* [B][H][n_kb][D]   mean of the smoothed K rows of each key block                  */
@@ -96,8 +100,9 @@ sagesla_status sagesla_validate(const sagesla_params* p);
    Reads q, k (bf16 [B][H][N][D]). With SAGESLA_SMOOTH_K, k_mean = fp32(exact column sum / N) per (b, h) and
    K is smoothed to k' = fp32(K - k_mean); otherwise k' = K. Per block of blk_q query rows (blk_k key rows) × D
    channels, the last block holding only the remaining rows: scale = fp32(absmax/127) and
-   code = clamp(round-half-even(fp32(x / scale)), -127, 127) for Q and for k'. Also writes q_pool/k_pool, the
-   block means of raw Q and of k' (fp64). Codes, scales and k_mean are bit-exact functions of the inputs. */
+   code = clamp(round-half-even(fp32(x / scale)), -127, 127) for Q and for k'; with SAGESLA_QUANT_GROUP32 the
+   same per group of 32 rows (the last group holding the remaining rows). Also writes q_pool/k_pool, the block
+   means of raw Q and of k' (fp64). Codes, scales and k_mean are bit-exact functions of the inputs. */
 sagesla_status sagesla_quantize(const void* q, const void* k, const sagesla_params* p, void* stream);
 
 /* Select stage ([TD-news] §三(二) item 1; [TD-guide] --sla_topk).
@@ -110,8 +115,9 @@ sagesla_status sagesla_select(const sagesla_params* p, void* stream);
    attention on the rest). Runs quantize, select (or reads block_idx with SAGESLA_USE_GIVEN_MASK; indices are
    clamped to [0, n_kb)), the linear branch (SAGESLA_LINEAR) and the sparse attention, and writes
    out = bf16_rne(O_s + O_lin):
-     O_s[i]  = softmax over the selected keys j of z_ij = (codeQ_i · codeK_j) · scale_q(I) · scale_k(J) · sm_scale,
-               applied to the bf16 value rows (0 when topk == 0);
+     O_s[i]  = softmax over the selected keys j of z_ij = (codeQ_i · codeK_j) · scale_q(i) · scale_k(j) · sm_scale,
+               where scale_q(i) / scale_k(j) is the scale of the block (or, with SAGESLA_QUANT_GROUP32, of the
+               32-row group) holding row i / j, applied to the bf16 value rows (0 when topk == 0);
      O_lin   = O_l · W_p, O_l[i] = phi(q_i) H_m / (phi(q_i) · Z_m), phi = elu + 1 on the raw bf16 q and k,
                H_m / Z_m = the sum over all key blocks of phi(K_J)^T V_J / sum phi(K_J) minus the same sums over
                the selected blocks (0 when every key block is selected). */

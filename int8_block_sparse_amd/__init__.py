@@ -14,7 +14,8 @@ from typing import Optional
 
 __all__ = [
     "LIB_PATH", "load", "Params", "SageSLAError", "topk_blocks", "n_blocks", "workspace_bytes", "validate",
-    "quantize", "select", "forward", "LINEAR", "SMOOTH_K", "USE_GIVEN_MASK", "STATUS", "STAGES", "stage_events",
+    "quantize", "select", "forward", "LINEAR", "SMOOTH_K", "USE_GIVEN_MASK", "QUANT_GROUP32", "STATUS", "STAGES",
+    "stage_events",
     "stage_ms", "Config",
 ]
 
@@ -23,6 +24,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsagesla.
 LINEAR = 0x1
 SMOOTH_K = 0x2
 USE_GIVEN_MASK = 0x4
+QUANT_GROUP32 = 0x8  # one INT8 scale per 32 tokens of Q and of K (thread-level granularity)
 
 STATUS = {0: "OK", 1: "E_NULL", 2: "E_SHAPE", 3: "E_UNSUPPORTED", 4: "E_WORKSPACE", 5: "E_ALIGN", 6: "E_HIP"}
 STAGES = ("quantize", "select", "linear", "attn")
@@ -115,6 +117,7 @@ class Config:
     linear: bool = True
     smooth_k: bool = True
     sm_scale: float = 0.0
+    group32: bool = False  # one INT8 scale per 32 tokens instead of one per block
 
     @property
     def n_qb(self) -> int:
@@ -124,8 +127,16 @@ class Config:
     def n_kb(self) -> int:
         return n_blocks(self.N, self.blk_k)
 
+    @property
+    def n_qscale(self) -> int:
+        return n_blocks(self.N, 32) if self.group32 else self.n_qb
+
+    @property
+    def n_kscale(self) -> int:
+        return n_blocks(self.N, 32) if self.group32 else self.n_kb
+
     def params(self, **ptrs) -> Params:
-        flags = (LINEAR if self.linear else 0) | (SMOOTH_K if self.smooth_k else 0)
+        flags = (LINEAR if self.linear else 0) | (SMOOTH_K if self.smooth_k else 0) | (QUANT_GROUP32 if self.group32 else 0)
         if ptrs.pop("given_mask", False):
             flags |= USE_GIVEN_MASK
         p = Params(B=self.B, H=self.H, N=self.N, D=self.D, blk_q=self.blk_q, blk_k=self.blk_k, topk=self.topk,
@@ -185,9 +196,9 @@ def _exports(cfg: Config, device):
     f = dict(device=device)
     ex = {
         "q_i8": torch.empty(cfg.B, cfg.H, N, D, dtype=torch.int8, **f),
-        "q_scale": torch.empty(cfg.B, cfg.H, cfg.n_qb, dtype=torch.float32, **f),
+        "q_scale": torch.empty(cfg.B, cfg.H, cfg.n_qscale, dtype=torch.float32, **f),
         "k_i8": torch.empty(cfg.B, cfg.H, N, D, dtype=torch.int8, **f),
-        "k_scale": torch.empty(cfg.B, cfg.H, cfg.n_kb, dtype=torch.float32, **f),
+        "k_scale": torch.empty(cfg.B, cfg.H, cfg.n_kscale, dtype=torch.float32, **f),
         "k_mean": torch.empty(cfg.B, cfg.H, D, dtype=torch.float32, **f),
         "q_pool": torch.empty(cfg.B, cfg.H, cfg.n_qb, D, dtype=torch.float64, **f),
         "k_pool": torch.empty(cfg.B, cfg.H, cfg.n_kb, D, dtype=torch.float64, **f),
@@ -215,14 +226,15 @@ def stage_ms(evs):
 
 def forward(q, k, v, w_proj=None, *, topk: int, blk_q: int = 128, blk_k: int = 64, linear: bool = True,
             smooth_k: bool = True, sm_scale: float = 0.0, mask=None, out=None, workspace=None,
-            export: bool = False, events=None):
+            export: bool = False, events=None, group32: bool = False):
     """SageSLA forward. q, k, v: bf16 [B, H, N, 128] CUDA tensors; w_proj: bf16 [128, 128] (needed with linear).
 
     mask: optional int32 [B, H, n_qb, topk] ascending block lists used instead of the selection.
+    group32: one INT8 scale per 32 tokens of Q and of K instead of one per block.
     export=True also returns a dict of every intermediate (codes, scales, K mean, pooled means, block lists,
     and the linear-branch output). Runs asynchronously on the current stream."""
     B, H, N, D = q.shape
-    cfg = Config(B, H, N, D, blk_q, blk_k, topk, linear, smooth_k, sm_scale)
+    cfg = Config(B, H, N, D, blk_q, blk_k, topk, linear, smooth_k, sm_scale, group32)
     if out is None:
         import torch
         out = torch.empty_like(q)
@@ -244,11 +256,12 @@ def forward(q, k, v, w_proj=None, *, topk: int, blk_q: int = 128, blk_k: int = 6
     return (out, ex) if export else out
 
 
-def quantize(q, k, *, blk_q: int = 128, blk_k: int = 64, smooth_k: bool = True, workspace=None):
+def quantize(q, k, *, blk_q: int = 128, blk_k: int = 64, smooth_k: bool = True, workspace=None,
+             group32: bool = False):
     """Quantize stage alone: returns dict(q_i8, q_scale, k_i8, k_scale, k_mean, q_pool, k_pool) and the workspace
     (pass it to select())."""
     B, H, N, D = q.shape
-    cfg = Config(B, H, N, D, blk_q, blk_k, 0, False, smooth_k)
+    cfg = Config(B, H, N, D, blk_q, blk_k, 0, False, smooth_k, group32=group32)
     _shape_check(q, k, None, None, cfg)
     ws = _workspace(cfg, q.device, workspace)
     ex = _exports(cfg, q.device)

@@ -25,7 +25,8 @@ bool misaligned(const void* ptr, size_t a) { return ptr && ((uintptr_t)ptr % a) 
 sagesla_status check_shape(const sagesla_params* p) {
   if (!p) return SAGESLA_E_NULL;
   if (p->D != kD || p->blk_k != kBlkK || (p->blk_q != 64 && p->blk_q != 128)) return SAGESLA_E_UNSUPPORTED;
-  if (p->flags & ~(uint32_t)(SAGESLA_LINEAR | SAGESLA_SMOOTH_K | SAGESLA_USE_GIVEN_MASK)) return SAGESLA_E_UNSUPPORTED;
+  if (p->flags & ~(uint32_t)(SAGESLA_LINEAR | SAGESLA_SMOOTH_K | SAGESLA_USE_GIVEN_MASK | SAGESLA_QUANT_GROUP32))
+    return SAGESLA_E_UNSUPPORTED;
   if (p->B < 1 || p->H < 1 || p->N < 1) return SAGESLA_E_SHAPE;
   if ((int64_t)p->B * p->H > 65535) return SAGESLA_E_SHAPE;
   if (p->N > kMaxN) return SAGESLA_E_UNSUPPORTED;
@@ -63,6 +64,8 @@ void make_plan(const sagesla_params* p, unsigned char* ws, Plan* pl) {
   pl->smooth = (p->flags & SAGESLA_SMOOTH_K) != 0;
   pl->linear = (p->flags & SAGESLA_LINEAR) != 0;
   pl->given_mask = (p->flags & SAGESLA_USE_GIVEN_MASK) != 0;
+  pl->group32 = (p->flags & SAGESLA_QUANT_GROUP32) != 0;
+  pl->n_g = (p->N + 31) / 32;
   pl->sm_scale = p->sm_scale > 0.f ? p->sm_scale : 1.f / sqrtf((float)p->D);
   pl->colsum_chunk = kColsumChunk;
   pl->n_colsum_chunks = (p->N + kColsumChunk - 1) / kColsumChunk;
@@ -79,8 +82,8 @@ void make_plan(const sagesla_params* p, unsigned char* ws, Plan* pl) {
   pl->k_mean = (float*)take(BH * D * sizeof(float));
   pl->q_i8 = (int8_t*)take(BH * N * D);
   pl->k_i8 = (int8_t*)take(BH * N * D);
-  pl->q_scale = (float*)take(BH * nqb * sizeof(float));
-  pl->k_scale = (float*)take(BH * nkb * sizeof(float));
+  pl->q_scale = (float*)take(BH * (pl->group32 ? (size_t)pl->n_g : nqb) * sizeof(float));
+  pl->k_scale = (float*)take(BH * (pl->group32 ? (size_t)pl->n_g : nkb) * sizeof(float));
   pl->q_pool = (double*)take(BH * nqb * D * sizeof(double));
   pl->k_pool = (double*)take(BH * nkb * D * sizeof(double));
   pl->scores = (double*)take(BH * nqb * nkb * sizeof(double));

@@ -16,6 +16,8 @@ constexpr int kStateX = kD * kD + kD;  // floats per linear-branch state: H^T (D
 struct Plan {
   int B, H, BH, N, blk_q, n_qb, n_kb, topk;
   bool smooth, linear, given_mask;
+  bool group32;  // one INT8 scale per 32 tokens (n_g = ceil(N / 32) per (b, h)) instead of one per block
+  int n_g;
   float sm_scale;
   int colsum_chunk, n_colsum_chunks;
   const void* w_proj;
@@ -24,8 +26,8 @@ struct Plan {
   float* k_mean;        // [BH][D]
   int8_t* q_i8;         // [BH][N][D]
   int8_t* k_i8;
-  float* q_scale;       // [BH][n_qb]
-  float* k_scale;       // [BH][n_kb]
+  float* q_scale;       // [BH][n_qb] (or [BH][n_g] with group32)
+  float* k_scale;       // [BH][n_kb] (or [BH][n_g] with group32)
   double* q_pool;       // [BH][n_qb][D]
   double* k_pool;       // [BH][n_kb][D]
   double* scores;       // [BH][n_qb][n_kb]

@@ -65,7 +65,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t slab_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-template <int NW>
+// (TAG only gives each attention-kernel instantiation its own specialization: when two kernels with the same NW
+// share one, the host compilation pass rejects the call inside the second kernel's lambdas)
+template <int NW, int TAG = 0>
 __device__ __forceinline__ void stage_k(__amdgpu_buffer_rsrc_t rk, uint32_t blk_off, const StageOffsets<NW>& so,
                                         unsigned char* sk) {
   using T = AttnTile<NW>;
@@ -89,10 +91,10 @@ __device__ __forceinline__ void stage_v(__amdgpu_buffer_rsrc_t rv, uint32_t blk_
   }
 }
 
-template <int NW>
+template <int NW, int TAG = 0>
 __device__ __forceinline__ void attn_stage(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, int J,
                                            const StageOffsets<NW>& so, unsigned char* sk, unsigned char* sv) {
-  stage_k<NW>(rk, (uint32_t)J * (kBlkK * kD), so, sk);
+  stage_k<NW, TAG>(rk, (uint32_t)J * (kBlkK * kD), so, sk);
   stage_v<NW>(rv, (uint32_t)J * 16384u, sv);
 }
 
@@ -177,11 +179,14 @@ __device__ __forceinline__ void attn_exp_pair(const v16i& s, int r, float c26, f
 // Each slot also issues the LDS operand read of the MFMA four slots later and one pair of this block's exps,
 // which run four pairs ahead of the PV steps that consume them. Scheduling barriers between the slots keep the
 // compiler from collapsing the read-ahead distance.
-template <bool RAGGED, bool HAS_NEXT, bool FAST>
+// G (one scale per 32 keys): score tile 0 (keys 0-31) takes the scale product c and tile 1 (keys 32-63) c1;
+// otherwise both take c.
+template <bool RAGGED, bool HAS_NEXT, bool FAST, bool G = false>
 __device__ __forceinline__ void attn_iter(const unsigned char* __restrict__ sk_next,
                                           const unsigned char* __restrict__ sv, const v4i* bq,
-                                          const int (&koff)[2][4], const int (&voff)[4][4], float c, int nv, int g,
-                                          v16f* o, float& m_run, float& l_run, v16i (&scur)[2], v16i (&snext)[2]) {
+                                          const int (&koff)[2][4], const int (&voff)[4][4], float c, float c1, int nv,
+                                          int g, v16f* o, float& m_run, float& l_run, v16i (&scur)[2],
+                                          v16i (&snext)[2]) {
   constexpr int NK = HAS_NEXT ? 8 : 0;  // score MFMAs of the next block
   constexpr int NS = NK + 16;           // MFMAs of the pass
   constexpr int AHEAD = 4;              // operand reads run this many MFMAs ahead
@@ -231,7 +236,7 @@ __device__ __forceinline__ void attn_iter(const unsigned char* __restrict__ sk_n
   // region 1: first operand reads; with a next block, its first four score MFMAs overlap the block max
 #pragma unroll
   for (int i = 0; i < AHEAD; ++i) read(i);
-  int mx = INT_MIN;
+  int mx = INT_MIN, mx1 = INT_MIN;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     if (HAS_NEXT) {
@@ -239,10 +244,18 @@ __device__ __forceinline__ void attn_iter(const unsigned char* __restrict__ sk_n
       read(q + AHEAD);
       mfma(q);
     }
-    mx = max(mx, part_max(q));
+    if (G && q >= 2)
+      mx1 = max(mx1, part_max(q));
+    else
+      mx = max(mx, part_max(q));
   }
   mx = max_halves_i32(mx);
-  const float mblk = (float)(mx - kMagic) * c;
+  float mblk = (float)(mx - kMagic) * c;
+  if constexpr (G) {
+    // tile 1 of a ragged block may hold no valid key at all (its max then stays INT_MIN)
+    mx1 = max_halves_i32(mx1);
+    mblk = fmaxf(mblk, (RAGGED && mx1 == INT_MIN) ? -INFINITY : (float)(mx1 - kMagic) * c1);
+  }
   const bool need = mblk > m_run + kLazy;
   if (__ballot(need)) {
     // rare: keep it a real branch (the marker has side effects, so the body is never executed speculatively)
@@ -260,6 +273,8 @@ __device__ __forceinline__ void attn_iter(const unsigned char* __restrict__ sk_n
   // region 2: slot k runs MFMA k, the read for MFMA k + AHEAD and exp pair k - NK + 4
   const float kc = FAST ? fmaf(kMagicUnits, c, m_run) : 0.f;
   const float c26 = c * kMagicScale;
+  const float kc1 = G ? (FAST ? fmaf(kMagicUnits, c1, m_run) : 0.f) : kc;
+  const float c26_1 = G ? c1 * kMagicScale : c26;
   float ps = 0.f;
 #pragma unroll
   for (int k = HAS_NEXT ? 4 : -4; k < NS; ++k) {
@@ -267,7 +282,9 @@ __device__ __forceinline__ void attn_iter(const unsigned char* __restrict__ sk_n
     if (k >= 0 && k + AHEAD < NS && k + AHEAD >= (HAS_NEXT ? 8 : AHEAD)) read(k + AHEAD);
     if (k >= 0) mfma(k);
     const int e = k - NK + 4;
-    if (e >= 0 && e < 16) attn_exp_pair<RAGGED, FAST>(scur[e >> 3], 2 * (e & 7), c26, m_run, kc, pw[e], ps);
+    if (e >= 0 && e < 16)
+      attn_exp_pair<RAGGED, FAST>(scur[e >> 3], 2 * (e & 7), (e >> 3) ? c26_1 : c26, m_run, (e >> 3) ? kc1 : kc,
+                                  pw[e], ps);
   }
   __builtin_amdgcn_sched_barrier(0);
   l_run += ps;
@@ -394,7 +411,9 @@ __device__ __forceinline__ void lin_epilogue(const uint16_t* __restrict__ q, con
   }
 }
 
-template <int NW>
+// G: one INT8 scale per 32 tokens of Q and of K (q_scale and k_scale hold ceil(N / 32) values per (b, h)): each
+// wave's 32 rows are one group of Q, and each 32-key score tile one group of K.
+template <int NW, bool G>
 __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k3_attn(
     const int8_t* __restrict__ q8, const int8_t* __restrict__ k8, const unsigned char* __restrict__ vt,
     const float* __restrict__ qs, const float* __restrict__ ks, const int32_t* __restrict__ idx,
@@ -440,7 +459,18 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k3_attn(
       const int vr = 32 * ct + lr;
       voff[ct][s] = vr * 128 + (((2 * s + g) ^ swz32(vr)) << 4);
     }
-  const float cq = qs[(size_t)bh * n_qb + I] * c0;
+  const int n_g = (N + 31) / 32;
+  // this wave's query scale times sm_scale * log2(e); cq_max over the workgroup's waves decides the exponent form
+  // for all of them
+  float cq, cq_max;
+  if (G) {
+    cq = qs[(size_t)bh * n_g + min(I * NW + w, n_g - 1)] * c0;
+    cq_max = 0.f;
+#pragma unroll
+    for (int k = 0; k < NW; ++k) cq_max = fmaxf(cq_max, qs[(size_t)bh * n_g + min(I * NW + k, n_g - 1)] * c0);
+  } else {
+    cq = cq_max = qs[(size_t)bh * n_qb + I] * c0;
+  }
   // The selection list and the key scales do not change during this kernel: reading them through the constant
   // address space lets the uniform reads use scalar loads, which do not count against the vector-memory
   // counter that the tile ring waits on.
@@ -451,7 +481,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k3_attn(
   // a ragged end re-read the last valid row)
   const __amdgpu_buffer_rsrc_t rk = slab_rsrc(k8 + (size_t)bh * N * kD, (uint32_t)N * kD);
   const __amdgpu_buffer_rsrc_t rv = slab_rsrc(vt + (size_t)bh * n_kb * 16384, (uint32_t)n_kb * 16384u);
-  c_f32* ksrow = (c_f32*)(ks + (size_t)bh * n_kb);
+  c_f32* ksrow = (c_f32*)(ks + (size_t)bh * (G ? n_g : n_kb));
   const int last_kb = n_kb - 1;
   const int nv_last = N - last_kb * kBlkK;  // valid keys of the last key block (64 unless ragged)
   const StageOffsets<NW> so_full = stage_offsets<NW>(kBlkK);
@@ -463,9 +493,16 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k3_attn(
   float m_run = -INFINITY, l_run = 0.f;
 
   auto blk = [&](int j) { return min(max(irow[j], 0), last_kb); };
+  // key scales of block J for score tiles 0 and 1 (G: its two 32-key groups; the second group of a last block
+  // that ends inside its first half does not exist and is clamped, its keys are masked anyway)
+  auto kscale = [&](int J) -> float2 {
+    if (G) return make_float2(ksrow[2 * J], ksrow[min(2 * J + 1, n_g - 1)]);
+    const float k1 = ksrow[J];
+    return make_float2(k1, k1);
+  };
   auto stage = [&](int j, int buf) {
     const int J = blk(j);
-    attn_stage<NW>(rk, rv, J, J == last_kb ? so_last : so_full,
+    attn_stage<NW, G ? 1 : 0>(rk, rv, J, J == last_kb ? so_last : so_full,
                    buf ? s_k1 : s_k0, buf ? s_v1 : s_v0);
   };
   auto sync = [&]() {
@@ -479,17 +516,21 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k3_attn(
     // before the end.
     // Wave 0 also writes the list to LDS when it fits.
     const bool has_ragged = nv_last != kBlkK;
-    const bool listed = topk <= kListCap;
+    // (G: the list keeps the two raw key scales per entry, in half the entries; each wave multiplies by its cq)
+    const bool listed = topk <= (G ? kListCap / 2 : kListCap);
     float kmax = 0.f;
     bool early_ragged = false;
     for (int j = l; j < topk; j += 64) {
       const int J = blk(j);
-      const float kv = ksrow[J];
-      kmax = fmaxf(kmax, kv);
+      const float2 kv = kscale(J);
+      kmax = fmaxf(kmax, fmaxf(kv.x, kv.y));
       early_ragged |= has_ragged && j < topk - 1 && J == last_kb;
       if (listed && w == 0) {
         s_lj[j] = J;
-        s_lc[j] = cq * kv;
+        if (G)
+          ((float2*)s_lc)[j] = kv;
+        else
+          s_lc[j] = cq * kv.x;
       }
     }
     if (listed && w == 0 && l < 4) s_lj[topk + l] = blk(topk - 1);
@@ -497,7 +538,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k3_attn(
     const bool elsewhere = __ballot(early_ragged) != 0;
     const bool tail_ragged = has_ragged && blk(topk - 1) == last_kb;
     // one-instruction exponent argument when every block's scale product is below 2^-10 (see attn_exp_pair)
-    const bool fast = cq * kmax < 0x1p-10f;
+    const bool fast = cq_max * kmax < 0x1p-10f;
     v16i scur[2], snext[2];
     using T = AttnTile<NW>;
     using i0 = std::integral_constant<int, 0>;
@@ -520,7 +561,9 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k3_attn(
       // K tiles use the full-block offsets even for a ragged last block: its rows past N lie beyond the
       // descriptor's range, so those loads return zeros without touching memory, and the ragged pass masks the
       // keys anyway
-      auto put_kJ = [&](int J, unsigned char* dst) { stage_k<NW>(rk, (uint32_t)J * (kBlkK * kD), so_full, dst); };
+      auto put_kJ = [&](int J, unsigned char* dst) {
+        stage_k<NW, G ? 1 : 0>(rk, (uint32_t)J * (kBlkK * kD), so_full, dst);
+      };
       auto put_vJ = [&](int J, unsigned char* dst) { stage_v<NW>(rv, (uint32_t)J * 16384u, dst); };
       auto put_k = [&](int j, unsigned char* dst) { put_kJ(blk(j), dst); };
       auto put_v = [&](int j, unsigned char* dst) { put_vJ(blk(j), dst); };
@@ -537,33 +580,46 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k3_attn(
       // Iteration j < topk - 1 waits for K[j+1] and V[j], issued two iterations back (the loads of iteration
       // j-1 may stay in flight), issues K[j+3] and V[j+2], then runs block j with the scores of block j+1.
       // Steady state, ring phase P = j % 3 known at compile time, both tiles issued:
-      // (L: lj holds J[j+3] and lc the scale product of block j, both as read from LDS; jv = J[j+2])
+      // (L: lj holds J[j+3] and lc the scale product of block j (G: the two key scales of block j), both as
+      // read from LDS; jv = J[j+2])
       int lj = 0, jv = 0;
-      float lc = 0.f;
+      float2 lc = make_float2(0.f, 0.f);
+      auto list_c = [&](int j) { return G ? ((const float2*)s_lc)[j] : make_float2(s_lc[j], 0.f); };
       if constexpr (L) {
         lj = s_lj[3];
-        lc = s_lc[0];
+        lc = list_c(0);
         jv = __builtin_amdgcn_readfirstlane(s_lj[2]);
       }
+      // scale products of block j for tiles 0 and 1, from the scalar-load path
+      auto cpair = [&](int J, float& ca, float& cb) {
+        const float2 kv = kscale(J);
+        ca = cq * kv.x;
+        cb = G ? cq * kv.y : ca;
+      };
       auto iter_full = [&](int j, auto ph) {
         constexpr int P = decltype(ph)::value;
         ring_sync<T::KPW + T::VPW>();
-        float c;
+        float c, c1;
         if constexpr (L) {
           const int J3 = __builtin_amdgcn_readfirstlane(lj);
-          c = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(lc)));
+          if (G) {
+            c = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(cq * lc.x)));
+            c1 = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(cq * lc.y)));
+          } else {
+            c1 = c = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(lc.x)));
+          }
           put_kJ(J3, ks[P]);
           put_vJ(jv, vs[(P + 2) % 3]);
           lj = s_lj[j + 4];
-          lc = s_lc[j + 1];
+          lc = list_c(j + 1);
           jv = J3;
         } else {
           put_k(j + 3, ks[P]);
           put_v(j + 2, vs[(P + 2) % 3]);
-          c = cq * ksrow[blk(j)];
+          cpair(blk(j), c, c1);
         }
-        attn_iter<false, true, F>(ks[(P + 1) % 3], vs[P], bq, koff, voff, c, kBlkK, g, o, m_run, l_run, scur,
-                                  snext);
+        attn_iter<false, true, F, G>(ks[(P + 1) % 3], vs[P], bq, koff, voff, c, c1, kBlkK, g, o, m_run, l_run,
+                                     scur, snext);
         scur[0] = snext[0];
         scur[1] = snext[1];
       };
@@ -576,8 +632,10 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k3_attn(
           ring_sync<T::VPW>();
         if (j + 3 < topk) put_k(j + 3, pick(P, k0, k1, k2));
         if (j + 2 < topk) put_v(j + 2, pick(P == 0 ? 2 : P - 1, v0, v1, v2));
-        attn_iter<false, true, F>(pick(P == 2 ? 0 : P + 1, k0, k1, k2), pick(P, v0, v1, v2), bq, koff, voff,
-                                  cq * ksrow[blk(j)], kBlkK, g, o, m_run, l_run, scur, snext);
+        float c, c1;
+        cpair(blk(j), c, c1);
+        attn_iter<false, true, F, G>(pick(P == 2 ? 0 : P + 1, k0, k1, k2), pick(P, v0, v1, v2), bq, koff, voff, c,
+                                     c1, kBlkK, g, o, m_run, l_run, scur, snext);
         scur[0] = snext[0];
         scur[1] = snext[1];
       };
@@ -592,12 +650,12 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k3_attn(
       ring_sync<0>();
       const int ph = j % 3;
       unsigned char* const vl = ph == 0 ? v0 : ph == 1 ? v1 : v2;
+      float c, c1;
+      cpair(tail_ragged ? last_kb : blk(j), c, c1);
       if (tail_ragged)
-        attn_iter<true, false, F>(nullptr, vl, bq, koff, voff, cq * ksrow[last_kb], nv_last, g, o, m_run, l_run,
-                                  scur, snext);
+        attn_iter<true, false, F, G>(nullptr, vl, bq, koff, voff, c, c1, nv_last, g, o, m_run, l_run, scur, snext);
       else
-        attn_iter<false, false, F>(nullptr, vl, bq, koff, voff, cq * ksrow[blk(j)], kBlkK, g, o, m_run, l_run,
-                                   scur, snext);
+        attn_iter<false, false, F, G>(nullptr, vl, bq, koff, voff, c, c1, kBlkK, g, o, m_run, l_run, scur, snext);
     };
     if (elsewhere) {
       stage(0, 0);
@@ -606,9 +664,10 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k3_attn(
         const int buf = j & 1;
         if (j + 1 < topk) stage(j + 1, buf ^ 1);
         const int J = blk(j);
+        const float2 kv = kscale(J);
         attn_scores(buf ? s_k1 : s_k0, bq, koff, scur);
-        attn_iter<true, false, false>(nullptr, buf ? s_v1 : s_v0, bq, koff, voff, cq * ksrow[J], min(kBlkK, N - J * kBlkK),
-                                      g, o, m_run, l_run, scur, snext);
+        attn_iter<true, false, false, G>(nullptr, buf ? s_v1 : s_v0, bq, koff, voff, cq * kv.x, cq * kv.y,
+                                         min(kBlkK, N - J * kBlkK), g, o, m_run, l_run, scur, snext);
         sync();
       }
     } else if (fast) {
@@ -656,12 +715,15 @@ hipError_t launch_attn(const Plan& p, const uint16_t* q, uint16_t* out, hipStrea
   const bool lin = p.linear && p.topk < p.n_kb;
   const float* sm = lin ? p.state_m : nullptr;
   float* olin = lin ? p.o_lin : nullptr;  // optional export of the linear branch's output
-  if (p.blk_q == 128)
-    hipLaunchKernelGGL(k3_attn<4>, dim3(total), dim3(256), 0, s, p.q_i8, p.k_i8, p.v_img, p.q_scale, p.k_scale,
-                       p.block_idx, q, sm, p.wpt, olin, out, p.N, p.n_qb, p.n_kb, p.topk, c0, total);
-  else
-    hipLaunchKernelGGL(k3_attn<2>, dim3(total), dim3(128), 0, s, p.q_i8, p.k_i8, p.v_img, p.q_scale, p.k_scale,
-                       p.block_idx, q, sm, p.wpt, olin, out, p.N, p.n_qb, p.n_kb, p.topk, c0, total);
+#define SAGESLA_ATTN(NWV, G)                                                                                     \
+  hipLaunchKernelGGL((k3_attn<NWV, G>), dim3(total), dim3(64 * NWV), 0, s, p.q_i8, p.k_i8, p.v_img, p.q_scale,     \
+                     p.k_scale, p.block_idx, q, sm, p.wpt, olin, out, p.N, p.n_qb, p.n_kb, p.topk, c0, total)
+  if (p.blk_q == 128) {
+    if (p.group32) SAGESLA_ATTN(4, true); else SAGESLA_ATTN(4, false);
+  } else {
+    if (p.group32) SAGESLA_ATTN(2, true); else SAGESLA_ATTN(2, false);
+  }
+#undef SAGESLA_ATTN
   return hipGetLastError();
 }
 

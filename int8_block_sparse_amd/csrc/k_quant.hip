@@ -4,7 +4,8 @@
 // outliers before quantizing, item 2 gives every sub-block its own quantization parameters. Here:
 //   mu[c]   = fp32(exact sum over all N tokens of K[t][c] / N)     (per (b, h) channel mean of K)
 //   k'      = fp32(K - mu)                                          (Q and V are not smoothed)
-//   scale   = fp32(absmax / 127) per block of rows × all D channels (0 for an all-zero block)
+//   scale   = fp32(absmax / 127) per block of rows × all D channels (0 for an all-zero block), or per 32 rows
+//             (the pages' thread-level granularity, §三(一) item 2)
 //   code    = clamp(round-half-even(fp32(x / scale)), -127, 127)
 //   pool    = fp64 mean of the block's rows (raw Q; smoothed K)
 // The fp64 column sums are exact when every partial sum is representable, which holds for bf16 inputs whose
@@ -91,12 +92,15 @@ __device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {
 // One block of rows (<= MAXROWS) of D channels: thread (row group rl, 8-channel group cg) holds rows rl + 16 i.
 // Rows stay packed bf16 in registers (4 words per 8 values); with SMOOTH the fp32 value k - mu is formed again
 // where it is needed (the same single IEEE subtraction each time).
-template <int MAXROWS, bool SMOOTH>
+// With G32 the block's rows get one scale per 32 rows (group g = rows 32 g .. +31 = the rows of steps i = 2g, 2g+1
+// of every thread); scale_out then receives one value per group that holds a valid row.
+template <int MAXROWS, bool SMOOTH, bool G32>
 __device__ __forceinline__ void quant_block(const uint16_t* __restrict__ src, int rows, const float* __restrict__ mu,
                                             int8_t* __restrict__ dst, float* __restrict__ scale_out,
-                                            double* __restrict__ pool_out, float* s_amax,
+                                            double* __restrict__ pool_out, float (*s_amax)[4],
                                             double (*s_red)[kD + 1]) {
   constexpr int IT = MAXROWS / 16;
+  constexpr int NG = G32 ? MAXROWS / 32 : 1;  // scales in this block
   const int t = threadIdx.x, cg = t & 15, rl = t >> 4;
   float m8[8];
 #pragma unroll
@@ -112,7 +116,9 @@ __device__ __forceinline__ void quant_block(const uint16_t* __restrict__ src, in
     const float x = (e & 1) ? bf16_hi(wd) : bf16_lo(wd);
     return SMOOTH ? (rl + 16 * i < rows ? x - m8[e] : 0.f) : x;  // one IEEE fp32 subtraction
   };
-  float amax = 0.f;
+  float amax[NG];
+#pragma unroll
+  for (int gi = 0; gi < NG; ++gi) amax[gi] = 0.f;
   double psum[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) psum[e] = 0.0;
@@ -121,24 +127,31 @@ __device__ __forceinline__ void quant_block(const uint16_t* __restrict__ src, in
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float x = value(i, e);
-      amax = fmaxf(amax, fabsf(x));
+      amax[G32 ? i / 2 : 0] = fmaxf(amax[G32 ? i / 2 : 0], fabsf(x));
       psum[e] += (double)x;
     }
-  amax = wave_max_f32(amax);
-  if ((t & 63) == 0) s_amax[t >> 6] = amax;
+#pragma unroll
+  for (int gi = 0; gi < NG; ++gi) {
+    amax[gi] = wave_max_f32(amax[gi]);
+    if ((t & 63) == 0) s_amax[t >> 6][gi] = amax[gi];
+  }
 #pragma unroll
   for (int e = 0; e < 8; ++e) s_red[rl][cg * 8 + e] = psum[e];
   __syncthreads();
-  amax = fmaxf(fmaxf(s_amax[0], s_amax[1]), fmaxf(s_amax[2], s_amax[3]));
-  const float s = amax / 127.f;  // IEEE fp32 division (correctly rounded)
-  const float rcp = 1.f / s;
+  float s[NG], rcp[NG];
+#pragma unroll
+  for (int gi = 0; gi < NG; ++gi) {
+    amax[gi] = fmaxf(fmaxf(s_amax[0][gi], s_amax[1][gi]), fmaxf(s_amax[2][gi], s_amax[3][gi]));
+    s[gi] = amax[gi] / 127.f;  // IEEE fp32 division (correctly rounded)
+    rcp[gi] = 1.f / s[gi];
+  }
 #pragma unroll
   for (int i = 0; i < IT; ++i) {
-    const int r = rl + 16 * i;
+    const int r = rl + 16 * i, gi = G32 ? i / 2 : 0;
     if (r < rows) {
       int c[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) c[e] = (amax > 0.f) ? quant_code(value(i, e), s, rcp) : 0;
+      for (int e = 0; e < 8; ++e) c[e] = (amax[gi] > 0.f) ? quant_code(value(i, e), s[gi], rcp[gi]) : 0;
       uint2 o;
       o.x = pack4_i8(c[0], c[1], c[2], c[3]);
       o.y = pack4_i8(c[4], c[5], c[6], c[7]);
@@ -151,7 +164,7 @@ __device__ __forceinline__ void quant_block(const uint16_t* __restrict__ src, in
     for (int j = 0; j < 16; ++j) sum += s_red[j][t];
     pool_out[t] = sum / (double)rows;
   }
-  if (t == 0) *scale_out = (amax > 0.f) ? s : 0.f;
+  if (t < NG && 32 * t < rows) scale_out[t] = (amax[t] > 0.f) ? s[t] : 0.f;
 }
 
 // rows of one key block of V as the V^T image writer takes them: thread (cg, kg) holds keys 4 kg .. +3,
@@ -186,33 +199,37 @@ __device__ __forceinline__ void write_v_image(const uint32_t (&wv)[4][4], unsign
 
 // grid (n_qb + n_kb, BH): x < n_qb quantizes query block x, otherwise key block x - n_qb (and, when v is given,
 // writes that key block's V^T image).
-template <int BLKQ>
+template <int BLKQ, bool G32>
 __global__ __launch_bounds__(256) void k1_quant(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                                const float* __restrict__ mu, int8_t* __restrict__ q8,
                                                int8_t* __restrict__ k8, float* __restrict__ qs,
                                                float* __restrict__ ks, double* __restrict__ qp,
                                                double* __restrict__ kp, const uint16_t* __restrict__ v,
                                                unsigned char* __restrict__ v_img, int N, int n_qb, int n_kb) {
-  __shared__ float s_amax[4];
+  __shared__ float s_amax[4][4];
   __shared__ double s_red[16][kD + 1];
   const int bh = blockIdx.y;
   const int x = blockIdx.x;
   const size_t base = (size_t)bh * N * kD;
+  // scales per block, or per 32 tokens with G32 (n_g = ceil(N / 32) of them per (b, h))
+  const int n_g = (N + 31) / 32;
   if (x < n_qb) {
     const int r0 = x * BLKQ;
-    quant_block<BLKQ, false>(q + base + (size_t)r0 * kD, min(BLKQ, N - r0), nullptr, q8 + base + (size_t)r0 * kD,
-                             qs + (size_t)bh * n_qb + x, qp + ((size_t)bh * n_qb + x) * kD, s_amax, s_red);
+    float* so = G32 ? qs + (size_t)bh * n_g + x * (BLKQ / 32) : qs + (size_t)bh * n_qb + x;
+    quant_block<BLKQ, false, G32>(q + base + (size_t)r0 * kD, min(BLKQ, N - r0), nullptr,
+                                  q8 + base + (size_t)r0 * kD, so, qp + ((size_t)bh * n_qb + x) * kD, s_amax, s_red);
   } else {
     const int j = x - n_qb;
     const int r0 = j * kBlkK, nv = min(kBlkK, N - r0);
+    float* so = G32 ? ks + (size_t)bh * n_g + j * (kBlkK / 32) : ks + (size_t)bh * n_kb + j;
     uint32_t wv[4][4];
     if (v) load_v_rows(v + base + (size_t)r0 * kD, nv, wv);  // in flight while K is quantized
     if (mu)
-      quant_block<kBlkK, true>(k + base + (size_t)r0 * kD, nv, mu + bh * kD, k8 + base + (size_t)r0 * kD,
-                               ks + (size_t)bh * n_kb + j, kp + ((size_t)bh * n_kb + j) * kD, s_amax, s_red);
+      quant_block<kBlkK, true, G32>(k + base + (size_t)r0 * kD, nv, mu + bh * kD, k8 + base + (size_t)r0 * kD, so,
+                                    kp + ((size_t)bh * n_kb + j) * kD, s_amax, s_red);
     else
-      quant_block<kBlkK, false>(k + base + (size_t)r0 * kD, nv, nullptr, k8 + base + (size_t)r0 * kD,
-                                ks + (size_t)bh * n_kb + j, kp + ((size_t)bh * n_kb + j) * kD, s_amax, s_red);
+      quant_block<kBlkK, false, G32>(k + base + (size_t)r0 * kD, nv, nullptr, k8 + base + (size_t)r0 * kD, so,
+                                     kp + ((size_t)bh * n_kb + j) * kD, s_amax, s_red);
     if (v) write_v_image(wv, v_img + ((size_t)bh * n_kb + j) * 16384);
   }
 }
@@ -242,12 +259,15 @@ hipError_t launch_kmean(const Plan& p, const uint16_t* k, hipStream_t s) {
 hipError_t launch_quant(const Plan& p, const uint16_t* q, const uint16_t* k, const uint16_t* v, hipStream_t s) {
   const dim3 grid(p.n_qb + p.n_kb, p.BH);
   const float* mu = p.smooth ? p.k_mean : nullptr;
-  if (p.blk_q == 128)
-    hipLaunchKernelGGL(k1_quant<128>, grid, dim3(256), 0, s, q, k, mu, p.q_i8, p.k_i8, p.q_scale, p.k_scale,
-                       p.q_pool, p.k_pool, v, p.v_img, p.N, p.n_qb, p.n_kb);
-  else
-    hipLaunchKernelGGL(k1_quant<64>, grid, dim3(256), 0, s, q, k, mu, p.q_i8, p.k_i8, p.q_scale, p.k_scale,
-                       p.q_pool, p.k_pool, v, p.v_img, p.N, p.n_qb, p.n_kb);
+#define SAGESLA_QUANT(BQ, G)                                                                                   \
+  hipLaunchKernelGGL((k1_quant<BQ, G>), grid, dim3(256), 0, s, q, k, mu, p.q_i8, p.k_i8, p.q_scale, p.k_scale,     \
+                     p.q_pool, p.k_pool, v, p.v_img, p.N, p.n_qb, p.n_kb)
+  if (p.blk_q == 128) {
+    if (p.group32) SAGESLA_QUANT(128, true); else SAGESLA_QUANT(128, false);
+  } else {
+    if (p.group32) SAGESLA_QUANT(64, true); else SAGESLA_QUANT(64, false);
+  }
+#undef SAGESLA_QUANT
   return hipGetLastError();
 }
 

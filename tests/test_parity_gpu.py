@@ -109,7 +109,7 @@ def check_out(out, r, rows=None, lin=None, bf16_bound=False):
     return err, c
 
 
-def full_case(wl, seed=0, topk=None, linear=None, smooth_k=True, w_mul=1.0, prep=None):
+def full_case(wl, seed=0, topk=None, linear=None, smooth_k=True, w_mul=1.0, prep=None, group32=False):
     topk = wl.topk if topk is None else topk
     linear = wl.linear if linear is None else linear
     q, k, v, w = synth.make(wl, seed)
@@ -117,8 +117,10 @@ def full_case(wl, seed=0, topk=None, linear=None, smooth_k=True, w_mul=1.0, prep
         q, k, v = prep(q, k, v)
     w = (w.float() * w_mul).to(torch.bfloat16)
     dq, dk, dv, dw = (t.cuda() for t in (q, k, v, w))
-    say(f"case {wl.name} B{wl.B} H{wl.H} N{wl.N} bq{wl.blk_q} topk{topk} linear{linear} smooth{smooth_k}")
-    out, ex = run_gpu(dq, dk, dv, dw, wl, topk, linear=linear, smooth_k=smooth_k)
+    say(f"case {wl.name} B{wl.B} H{wl.H} N{wl.N} bq{wl.blk_q} topk{topk} linear{linear} smooth{smooth_k}"
+        f" group32{group32}")
+    out, ex = run_gpu(dq, dk, dv, dw, wl, topk, linear=linear, smooth_k=smooth_k, group32=group32)
+    qg = 32 if group32 else None
     outn = to_np(out)
     W = to_np(w)
     flagged = 0
@@ -126,12 +128,14 @@ def full_case(wl, seed=0, topk=None, linear=None, smooth_k=True, w_mul=1.0, prep
         for h in range(wl.H):
             Q, K, V = to_np(q[b, h]), to_np(k[b, h]), to_np(v[b, h])
             gidx = ex["block_idx"][b, h].cpu().numpy()
-            r = orc.forward_head(Q, K, V, W, wl.blk_q, wl.blk_k, topk, linear=linear, smooth_k=smooth_k)
+            r = orc.forward_head(Q, K, V, W, wl.blk_q, wl.blk_k, topk, linear=linear, smooth_k=smooth_k,
+                                 quant_group=qg)
             assert r["exact_sum_ok"]
             check_quant(ex, r, b, h)
             flagged += check_mask(gidx, r, topk)
             rg = orc.forward_head(Q, K, V, W, wl.blk_q, wl.blk_k, topk, linear=linear, smooth_k=smooth_k,
-                                  mask=gidx[:, :topk] if topk else np.zeros((wl.n_qb, 0), np.int32))
+                                  mask=gidx[:, :topk] if topk else np.zeros((wl.n_qb, 0), np.int32),
+                                  quant_group=qg)
             lin = to_np(ex["o_lin"][b, h]) if linear else None
             err, c = check_out(outn[b, h], rg, lin=lin, bf16_bound=w_mul != 1.0)
             say(f"  b{b} h{h}: out max-abs {err:.2e} cos {c:.6f}")
@@ -149,6 +153,12 @@ SMALL = {
 @pytest.mark.parametrize("name", list(SMALL))
 def test_forward_small(name):
     assert full_case(SMALL[name]) == 0
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_forward_small_group32(name):
+    # one INT8 scale per 32 tokens of Q and of K (thread-level granularity)
+    assert full_case(SMALL[name], group32=True) == 0
 
 
 def test_topk_zero_linear_only():
@@ -200,6 +210,27 @@ def test_given_mask_matches_oracle_with_same_mask():
         check_out(to_np(out[0, h]), r, lin=to_np(ex["o_lin"][0, h]))
 
 
+@pytest.mark.parametrize("group32", [False, True], ids=["block", "group32"])
+def test_given_mask_ragged_block_first(group32):
+    # caller-given lists in descending order that hold the ragged last key block first: the attention kernel's
+    # generic loop (the ring assumes the ragged block can only come last)
+    wl = SMALL["ragged128"]
+    q, k, v, w = synth.make(wl, 4)
+    rng = np.random.default_rng(6)
+    topk = 5
+    rows = []
+    for _ in range(wl.B * wl.H * wl.n_qb):
+        others = rng.choice(wl.n_kb - 1, topk - 1, replace=False)
+        rows.append(np.sort(np.append(others, wl.n_kb - 1))[::-1])
+    mask = np.stack(rows).reshape(wl.B, wl.H, wl.n_qb, topk).astype(np.int32)
+    out, ex = run_gpu(q.cuda(), k.cuda(), v.cuda(), w.cuda(), wl, topk, mask=torch.from_numpy(mask).cuda(),
+                      group32=group32)
+    for h in range(wl.H):
+        r = orc.forward_head(to_np(q[0, h]), to_np(k[0, h]), to_np(v[0, h]), to_np(w), wl.blk_q, wl.blk_k, topk,
+                             mask=mask[0, h], quant_group=32 if group32 else None)
+        check_out(to_np(out[0, h]), r, lin=to_np(ex["o_lin"][0, h]))
+
+
 def test_deterministic():
     wl = SMALL["grid"]
     q, k, v, w = (t.cuda() for t in synth.make(wl, 1))
@@ -226,13 +257,13 @@ def test_stage_entry_points_agree_with_forward():
 # the real layer shapes, in the launch configuration the benchmark times, checked on sampled (b, h) heads
 # and sampled query blocks (quantization and selection of a sampled head are checked in full)
 # ---------------------------------------------------------------------------------------------------------
-def sampled_case(cfg_id, heads, n_blocks_sample=6, seed=0):
+def sampled_case(cfg_id, heads, n_blocks_sample=6, seed=0, group32=False):
     wl = synth.workload(cfg_id)
     say(f"full-size {wl.name}: generating")
     q, k, v, w = synth.make(wl, seed, device="cuda")
     torch.cuda.synchronize()
     say(f"full-size {wl.name}: forward")
-    out, ex = run_gpu(q, k, v, w, wl, wl.topk, linear=wl.linear)
+    out, ex = run_gpu(q, k, v, w, wl, wl.topk, linear=wl.linear, group32=group32)
     W = to_np(w)
     rng = np.random.default_rng(cfg_id)
     flagged = 0
@@ -240,7 +271,8 @@ def sampled_case(cfg_id, heads, n_blocks_sample=6, seed=0):
         Q, K, V = to_np(q[b, h]), to_np(k[b, h]), to_np(v[b, h])
         gidx = ex["block_idx"][b, h].cpu().numpy()[:, :wl.topk]
         blocks = sorted(set([0, wl.n_qb - 1] + list(rng.choice(wl.n_qb, n_blocks_sample, replace=False))))
-        r = orc.forward_head(Q, K, V, W, wl.blk_q, wl.blk_k, wl.topk, linear=wl.linear, mask=gidx, blocks=blocks)
+        r = orc.forward_head(Q, K, V, W, wl.blk_q, wl.blk_k, wl.topk, linear=wl.linear, mask=gidx, blocks=blocks,
+                             quant_group=32 if group32 else None)
         assert r["exact_sum_ok"]
         check_quant(ex, r, b, h)
         flagged_h = check_mask(gidx, r, wl.topk)
@@ -270,3 +302,8 @@ def test_full_size_sla_720p_pair():
 def test_full_size_sla_1080p_long():
     # the largest layer shape (N = 269280 tokens, 4208 key blocks, top-k 210), two heads sampled
     sampled_case(4, [(0, 0), (0, 39)])
+
+
+def test_full_size_sla_720p_pair_group32():
+    # the benchmarked layer with one INT8 scale per 32 tokens of Q and of K
+    sampled_case(3, [(0, 0), (1, 39)], group32=True)

@@ -1,7 +1,7 @@
 """SageSLA attention forward for AMD Instinct MI355X (gfx950): thin Python binding of libsagesla.so.
 
 Every step of the forward runs in the library's HIP kernels; this module only marshals arguments through the
-C ABI declared in include/sagesla.h. PyTorch provides device memory and the current stream. There is no CPU
+C ABI declared in include/sagesla.h (the W8A8 linear layer of include/w8a8.h is bound in w8a8.py). PyTorch provides device memory and the current stream. There is no CPU
 fallback: calls fail loudly if the library is missing or no GPU is present.
 """
 from __future__ import annotations
@@ -83,6 +83,15 @@ def load():
     lib.sagesla_status_str.restype = ctypes.c_char_p
     lib.sagesla_last_hip_error.argtypes = []
     lib.sagesla_last_hip_error.restype = ctypes.c_int
+    i32, f32 = ctypes.c_int32, ctypes.c_float
+    lib.w8a8_quantize.argtypes = [vp, i32, i32, f32, vp, vp, vp]
+    lib.w8a8_quantize.restype = ctypes.c_int
+    lib.w8a8_gemm.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, vp]
+    lib.w8a8_gemm.restype = ctypes.c_int
+    lib.w8a8_workspace_bytes.argtypes = [i32, i32]
+    lib.w8a8_workspace_bytes.restype = ctypes.c_size_t
+    lib.w8a8_linear.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, f32, vp, ctypes.c_size_t, vp]
+    lib.w8a8_linear.restype = ctypes.c_int
     _lib = lib
     return lib
 

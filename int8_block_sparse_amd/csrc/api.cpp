@@ -5,6 +5,7 @@
 
 #include "internal.h"
 #include "sagesla.h"
+#include "w8a8.h"
 
 using namespace sagesla;
 
@@ -216,6 +217,85 @@ sagesla_status sagesla_forward(const void* q, const void* k, const void* v, void
   SAGESLA_TRY(launch_attn(pl, (const uint16_t*)q, (uint16_t*)out, s));
   SAGESLA_STEP(mark(p, SAGESLA_STAGE_ATTN, 1, s));
 #undef SAGESLA_STEP
+  return SAGESLA_OK;
+}
+
+// ---------------------------------------------------------------------------------------------------------
+// W8A8 linear layer (include/w8a8.h)
+// ---------------------------------------------------------------------------------------------------------
+}  // extern "C"
+
+namespace {
+
+constexpr int32_t kW8a8MaxK = 32768;
+constexpr int32_t kW8a8MaxRows = 1 << 24;
+
+// rows × cols matrix cut into 128×128 blocks: sizes and limits
+sagesla_status w8a8_check_matrix(int32_t rows, int32_t cols) {
+  if (rows < 1 || cols < 1) return SAGESLA_E_SHAPE;
+  if (cols % 128 != 0 || rows > kW8a8MaxRows || (int64_t)rows * cols >= ((int64_t)1 << 31))
+    return SAGESLA_E_UNSUPPORTED;
+  return SAGESLA_OK;
+}
+
+sagesla_status w8a8_check_gemm(int32_t M, int32_t N, int32_t K) {
+  sagesla_status st;
+  if ((st = w8a8_check_matrix(M, K)) != SAGESLA_OK) return st;
+  if ((st = w8a8_check_matrix(N, K)) != SAGESLA_OK) return st;
+  if (N % 128 != 0 || K > kW8a8MaxK) return SAGESLA_E_UNSUPPORTED;
+  return SAGESLA_OK;
+}
+
+size_t w8a8_scale_count(int32_t rows, int32_t cols) { return (size_t)((rows + 127) / 128) * (cols / 128); }
+
+}  // namespace
+
+extern "C" {
+
+sagesla_status w8a8_quantize(const void* x, int32_t rows, int32_t cols, float clip, int8_t* codes,
+                             float* scales, void* stream) {
+  sagesla_status st = w8a8_check_matrix(rows, cols);
+  if (st != SAGESLA_OK) return st;
+  if (!(clip > 0.f && clip <= 1.f)) return SAGESLA_E_SHAPE;
+  if (!x || !codes || !scales) return SAGESLA_E_NULL;
+  if (misaligned(x, 16) || misaligned(codes, 16) || misaligned(scales, 16)) return SAGESLA_E_ALIGN;
+  return hip_status(launch_w8a8_quant((const uint16_t*)x, rows, cols, clip, codes, scales, (hipStream_t)stream));
+}
+
+sagesla_status w8a8_gemm(const int8_t* x_i8, const float* x_scale, const int8_t* w_i8, const float* w_scale,
+                         const void* bias, void* y, int32_t M, int32_t N, int32_t K, void* stream) {
+  sagesla_status st = w8a8_check_gemm(M, N, K);
+  if (st != SAGESLA_OK) return st;
+  if (!x_i8 || !x_scale || !w_i8 || !w_scale || !y) return SAGESLA_E_NULL;
+  if (misaligned(x_i8, 16) || misaligned(x_scale, 16) || misaligned(w_i8, 16) || misaligned(w_scale, 16) ||
+      misaligned(bias, 16) || misaligned(y, 16))
+    return SAGESLA_E_ALIGN;
+  return hip_status(launch_w8a8_gemm(x_i8, x_scale, w_i8, w_scale, (const uint16_t*)bias, (uint16_t*)y, M, N, K,
+                                     (hipStream_t)stream));
+}
+
+size_t w8a8_workspace_bytes(int32_t M, int32_t K) {
+  if (w8a8_check_matrix(M, K) != SAGESLA_OK || K > kW8a8MaxK) return 0;
+  return align_up((size_t)M * K) + align_up(w8a8_scale_count(M, K) * sizeof(float));
+}
+
+sagesla_status w8a8_linear(const void* x, const int8_t* w_i8, const float* w_scale, const void* bias, void* y,
+                           int32_t M, int32_t N, int32_t K, float clip, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  sagesla_status st = w8a8_check_gemm(M, N, K);
+  if (st != SAGESLA_OK) return st;
+  if (!(clip > 0.f && clip <= 1.f)) return SAGESLA_E_SHAPE;
+  if (!x || !w_i8 || !w_scale || !y) return SAGESLA_E_NULL;
+  if (misaligned(x, 16) || misaligned(w_i8, 16) || misaligned(w_scale, 16) || misaligned(bias, 16) ||
+      misaligned(y, 16))
+    return SAGESLA_E_ALIGN;
+  if (!workspace || workspace_bytes < w8a8_workspace_bytes(M, K)) return SAGESLA_E_WORKSPACE;
+  if (misaligned(workspace, kAlign)) return SAGESLA_E_ALIGN;
+  int8_t* x8 = (int8_t*)workspace;
+  float* xs = (float*)((unsigned char*)workspace + align_up((size_t)M * K));
+  const hipStream_t s = (hipStream_t)stream;
+  SAGESLA_TRY(launch_w8a8_quant((const uint16_t*)x, M, K, clip, x8, xs, s));
+  SAGESLA_TRY(launch_w8a8_gemm(x8, xs, w_i8, w_scale, (const uint16_t*)bias, (uint16_t*)y, M, N, K, s));
   return SAGESLA_OK;
 }
 

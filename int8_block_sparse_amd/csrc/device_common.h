@@ -67,6 +67,27 @@ __device__ __forceinline__ int swz8(int row) { return (row ^ (row >> 3)) & 7; }
 // that share bit 5, where the two patterns differ by a constant XOR, so it stays conflict-free.
 __device__ __forceinline__ int swz32(int row) { return (row ^ ((row >> 3) & 3)) & 7; }
 
+// The INT8 code clamp(round-half-even(fp32(x / s)), -127, 127) of x for a scale s > 0 and r = fp32(1/s):
+// q = fp32(x * r) differs from the correctly rounded quotient f = fp32(x / s) by at most 2.3e-5 when |q| < 128
+// (two roundings of relative 2^-24 each on a value below 128.0001, plus f's own half ulp, at most 2^-17), less
+// than the 2^-15 margin tested below. round(q) can
+// differ from round(f) only if a half-integer lies within that distance of q, so such rare elements (and
+// non-finite q) are recomputed with the IEEE division. When |q| >= 128 (only under clipping), |f| > 127.5 and
+// both round to a value that the clamp takes to +-127; the check then also sends q to the division unless it
+// happens to be near an integer, which changes nothing.
+__device__ __forceinline__ int quant_code(float x, float s, float r) {
+#pragma clang fp contract(off)
+  const float qv = x * r;
+  float c = rintf(qv);
+  if (!(fabsf(qv - c) < 0.5f - 0x1p-15f)) c = rintf(x / s);
+  c = fminf(fmaxf(c, -127.f), 127.f);
+  return (int)c;
+}
+
+__device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {
+  return (uint32_t)(a & 0xff) | ((uint32_t)(b & 0xff) << 8) | ((uint32_t)(c & 0xff) << 16) | ((uint32_t)d << 24);
+}
+
 // Map a flat workgroup id to a work item so that each XCD (ids are dealt round-robin over 8 XCDs) gets one
 // contiguous range of work items: neighbouring query blocks of a head then share that XCD's L2.
 __device__ __forceinline__ int xcd_remap(int id, int total) {

@@ -52,6 +52,11 @@ hipError_t launch_topk(const Plan& p, hipStream_t s);
 hipError_t launch_linear(const Plan& p, const uint16_t* k, const uint16_t* v, hipStream_t s);
 // K3: block-sparse INT8 attention, epilogue adds the linear branch and writes bf16
 hipError_t launch_attn(const Plan& p, const uint16_t* q, uint16_t* out, hipStream_t s);
+// W8A8 linear layer: 128×128 block quantizer and the block-scaled INT8 product (Y bf16 [M][N])
+hipError_t launch_w8a8_quant(const uint16_t* x, int rows, int cols, float clip, int8_t* codes, float* scales,
+                             hipStream_t s);
+hipError_t launch_w8a8_gemm(const int8_t* x8, const float* xs, const int8_t* w8, const float* ws,
+                            const uint16_t* bias, uint16_t* y, int M, int N, int K, hipStream_t s);
 // fills (graph-capture friendly replacements for memset)
 hipError_t launch_fill_f32(float* dst, size_t n, float val, hipStream_t s);
 // dynamic LDS of the kernels that size it at run time

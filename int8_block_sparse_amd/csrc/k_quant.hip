@@ -69,24 +69,6 @@ __global__ __launch_bounds__(128) void k1_colsum_final(const double* __restrict_
   mu[bh * kD + c] = (float)(s / (double)N);
 }
 
-// The INT8 code of x for a block with scale s > 0 and r = fp32(1/s):
-// q = fp32(x * r) differs from the correctly rounded quotient f = fp32(x / s) by at most 1.9e-5 when |x/s| <= 127
-// (two roundings of relative 2^-24 each on a value below 127.00001, plus f's own half ulp 2^-18). round(q)
-// can differ from round(f) only if a half-integer lies within that distance of q, so such rare elements (and
-// non-finite q) are recomputed with the IEEE division.
-__device__ __forceinline__ int quant_code(float x, float s, float r) {
-#pragma clang fp contract(off)
-  const float qv = x * r;
-  float c = rintf(qv);
-  if (!(fabsf(qv - c) < 0.5f - 0x1p-15f)) c = rintf(x / s);
-  c = fminf(fmaxf(c, -127.f), 127.f);
-  return (int)c;
-}
-
-__device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {
-  return (uint32_t)(a & 0xff) | ((uint32_t)(b & 0xff) << 8) | ((uint32_t)(c & 0xff) << 16) | ((uint32_t)d << 24);
-}
-
 // One block of up to MAXROWS rows (valid: `rows`) × 128 channels, 256 threads. Thread t owns channels
 // 8*(t%16)..+7 of rows t/16 + 16*i.
 // One block of rows (<= MAXROWS) of D channels: thread (row group rl, 8-channel group cg) holds rows rl + 16 i.

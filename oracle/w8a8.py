@@ -23,8 +23,8 @@ Readings where the pages stop (the plainest ones the rest supports):
     last row block of X holds only its valid rows; N and K are multiples of 128.
   * Per block: t = fp32(alpha * absmax), s = fp32(t / 127), code = clamp(round-half-even(fp32(x / s)), -127,
     127). alpha in (0, 1] is the clip ratio: values beyond the threshold t saturate at +-127. Weights use
-    alpha = 1 (no clipping); activations take alpha from the caller. A block whose absmax is 0 gets s = 0 and
-    all-zero codes.
+    alpha = 1 (no clipping); activations take alpha from the caller. A block whose s is 0 (absmax 0, or a
+    threshold so small that s underflows) gets s = 0 and all-zero codes.
   * The product: Y[m, n] = sum over k-blocks kb of s_x(mb, kb) * s_w(nb, kb) * P_kb[m, n] + b[n], with
     P_kb = sum over the 128 columns of the k-block of code_x * code_w (an exact integer).
 The fp32(.) points are single IEEE operations on fp32/bf16 operands; computing each in fp64 and rounding to
@@ -72,6 +72,8 @@ def quantize_blocks(X: np.ndarray, clip: float = 1.0):
                 continue
             t = float(_f32(alpha * amax))
             s = float(_f32(t / QMAX))
+            if s == 0.0:  # the threshold underflowed: treated as an all-zero block
+                continue
             q = np.rint(_f32(blk / s))  # fp32 quotient, then round half to even
             codes[r0:r1, kb * BLK:(kb + 1) * BLK] = np.clip(q, -QMAX, QMAX).astype(np.int8)
             scales[mb, kb] = s

@@ -29,7 +29,8 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "workload", "custom", "make", "topk_blocks", "n_blocks"]
+__all__ = ["Workload", "WORKLOADS", "workload", "custom", "make", "topk_blocks", "n_blocks", "LinearWorkload",
+           "LINEAR_WORKLOADS", "make_linear"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -170,3 +171,59 @@ def make(wl: Workload, seed: int = 0, device="cpu"):
         v[b].copy_(vb.to(torch.bfloat16))
         del qb, kb, vb
     return q, k, v, w_p.to(torch.bfloat16).contiguous()
+
+
+# ---------------------------------------------------------------------------------------------------------
+# W8A8 linear layers
+# ---------------------------------------------------------------------------------------------------------
+# The pages quantize the linear layers around attention with 8-bit weights and activations ("Turbo Diffusion",
+# lanhy.cn, §三(四) item 1). Their shapes here are those of the Wan DiTs the pages accelerate: tokens M of one
+# layer's input (the 14B 720P pair: 2 × 75600; the 1.3B 480P layer: 32760), model width 5120 (14B) or 1536
+# (1.3B), FFN width 13824 (14B).
+#
+# Recipe (one torch.Generator seeded with ``seed``, in this order):
+#   * chan[K]   = 1, except 1% of the input channels (chosen by a random permutation) set to 16: activation
+#                 outlier channels, which make block absmax and clipping matter
+#   * W[N, K]   = N(0,1) / sqrt(K)
+#   * b[N]      = 0.1 N(0,1)
+#   * X[M, K]   = N(0,1) * chan (drawn in row chunks to bound host memory)
+#   * everything drawn in fp32 and rounded once to bf16.
+@dataclasses.dataclass(frozen=True)
+class LinearWorkload:
+    name: str
+    M: int  # tokens
+    N: int  # output features
+    K: int  # input features
+
+    @property
+    def ops(self) -> float:
+        """2·M·N·K: multiply-adds of the product, counted as two operations each."""
+        return 2.0 * self.M * self.N * self.K
+
+
+LINEAR_WORKLOADS = {
+    "small-ragged": LinearWorkload("small-ragged", 300, 384, 640),
+    "wan1.3b-480p-proj": LinearWorkload("wan1.3b-480p-proj", 32760, 1536, 1536),
+    "wan14b-720p-proj": LinearWorkload("wan14b-720p-proj", 151200, 5120, 5120),
+    "wan14b-720p-ffn-up": LinearWorkload("wan14b-720p-ffn-up", 151200, 13824, 5120),
+    "wan14b-720p-ffn-down": LinearWorkload("wan14b-720p-ffn-down", 151200, 5120, 13824),
+}
+
+
+def make_linear(wl: LinearWorkload, seed: int = 0, device="cpu", bias: bool = True):
+    """Draw (x [M, K], w [N, K], b [N] or None): contiguous bf16 tensors."""
+    dev = torch.device(device)
+    g = torch.Generator(device=dev)
+    g.manual_seed(int(seed))
+    M, N, K = wl.M, wl.N, wl.K
+    chan = torch.ones(K, device=dev)
+    n_out = max(1, K // 100)
+    chan[torch.randperm(K, generator=g, device=dev)[:n_out]] = 16.0
+    w = (torch.randn(N, K, generator=g, device=dev) / math.sqrt(K)).to(torch.bfloat16)
+    b = (0.1 * torch.randn(N, generator=g, device=dev)).to(torch.bfloat16)
+    x = torch.empty(M, K, dtype=torch.bfloat16, device=dev)
+    step = max(1, (1 << 26) // K)
+    for r0 in range(0, M, step):
+        r1 = min(M, r0 + step)
+        x[r0:r1] = (torch.randn(r1 - r0, K, generator=g, device=dev) * chan).to(torch.bfloat16)
+    return x, w, (b if bias else None)

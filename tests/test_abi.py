@@ -23,16 +23,24 @@ def lib():
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(sagesla_[a-z_]+)\s*\(", text)))
+    """Every function declared by the headers under include/ (prototypes: a return type, a name, a parameter
+    list ending in ';')."""
+    names = set()
+    for h in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if not h.endswith(".h"):
+            continue
+        text = open(os.path.join(ROOT, "include", h)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names |= set(re.findall(r"\b((?:sagesla|w8a8)_[a-z0-9_]+)\s*\([^;{]*\)\s*;", text))
+    return sorted(names)
 
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert {"sagesla_quantize", "sagesla_select", "sagesla_forward", "sagesla_workspace_bytes"} <= set(names)
+    assert {"sagesla_quantize", "sagesla_select", "sagesla_forward", "sagesla_workspace_bytes", "w8a8_quantize",
+            "w8a8_gemm", "w8a8_linear", "w8a8_workspace_bytes"} <= set(names)
     for n in names:
-        assert hasattr(lib, n), f"{n} declared in sagesla.h but not exported"
+        assert hasattr(lib, n), f"{n} declared in include/ but not exported"
 
 
 @pytest.mark.skipif(shutil.which("gcc") is None, reason="needs gcc")
@@ -132,3 +140,35 @@ def test_workspace_bytes(lib):
 def test_topk_blocks_matches_flag_reading():
     assert [sg.topk_blocks(f, n) for f, n in [(0.25, 16), (1.0, 512), (0.1, 512), (0.1, 1182), (0.05, 4208)]] == \
         [4, 512, 51, 118, 210]
+
+
+# ---------------------------------------------------------------------------------------------------------
+# W8A8 linear layer (include/w8a8.h): host-side validation only
+# ---------------------------------------------------------------------------------------------------------
+@cpu_only
+@pytest.mark.parametrize("rows,cols,clip,status", [
+    (0, 128, 1.0, 2), (4, 0, 1.0, 2), (4, 128, 0.0, 2), (4, 128, 1.5, 2), (4, 128, float("nan"), 2),
+    (4, 100, 1.0, 3), ((1 << 24) + 1, 128, 1.0, 3), (1 << 17, 1 << 14, 1.0, 3),
+])
+def test_w8a8_quantize_validation(lib, rows, cols, clip, status):
+    assert lib.w8a8_quantize(FAKE, rows, cols, clip, FAKE, FAKE, None) == status
+
+
+@cpu_only
+def test_w8a8_pointer_validation(lib):
+    assert lib.w8a8_quantize(None, 4, 128, 1.0, FAKE, FAKE, None) == 1
+    assert lib.w8a8_quantize(FAKE + 2, 4, 128, 1.0, FAKE, FAKE, None) == 5
+    g = lambda **kw: lib.w8a8_gemm(kw.get("x", FAKE), FAKE, FAKE, FAKE, kw.get("b", None), kw.get("y", FAKE),
+                                   kw.get("M", 300), kw.get("N", 256), kw.get("K", 384), None)
+    assert g(x=None) == 1 and g(y=None) == 1 and g(b=FAKE + 8) == 5 and g(y=FAKE + 4) == 5
+    assert g(N=200) == 3 and g(K=200) == 3 and g(K=32768 + 128) == 3 and g(M=0) == 2
+    lin = lambda **kw: lib.w8a8_linear(FAKE, FAKE, FAKE, None, FAKE, 300, 256, 384, kw.get("clip", 1.0),
+                                       kw.get("ws", FAKE), kw.get("wsb", 1 << 30), None)
+    assert lin(clip=0.0) == 2 and lin(ws=None) == 4 and lin(wsb=1000) == 4 and lin(ws=FAKE + 16) == 5
+    assert lib.sagesla_last_hip_error() == 0
+
+
+def test_w8a8_workspace_bytes(lib):
+    assert lib.w8a8_workspace_bytes(300, 384) == 115200 + 256  # codes (aligned) + 3 x 3 scales (aligned)
+    assert lib.w8a8_workspace_bytes(151200, 5120) >= 151200 * 5120
+    assert lib.w8a8_workspace_bytes(0, 128) == 0 and lib.w8a8_workspace_bytes(10, 100) == 0

@@ -9,6 +9,11 @@ roofline (its duration measured with HIP events recorded by the library around i
 the CPU oracle timed on a bounded sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--calib-copy-mib M]
+
+The second workload, the W8A8 block-quantized linear layer ("Turbo Diffusion", lanhy.cn, §三(四) item 1), is
+measured with --workload w8a8-<shape> (shapes: the synth module's LINEAR_WORKLOADS, e.g. w8a8-wan14b-720p-proj):
+a step is one whole layer (activation quantization, then the block-scaled INT8 product with the pre-quantized
+weights) and the line carries the product kernel's roofline.
 """
 from __future__ import annotations
 
@@ -29,6 +34,8 @@ PEAK_INT8_TOPS = 5000.0  # MI355X dense INT8 MFMA
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense BF16 MFMA
 COUNTERS = os.path.join(ROOT, "profiles", "k3_attn_wan14b-720p-sla-pair_counters.txt")
 K3_SOURCE = os.path.join(ROOT, "int8_block_sparse_amd", "csrc", "k_attn.hip")
+W8A8_COUNTERS = os.path.join(ROOT, "profiles", "k5_gemm_wan14b-720p-proj_counters.txt")
+W8A8_SOURCE = os.path.join(ROOT, "int8_block_sparse_amd", "csrc", "k_w8a8.hip")
 
 
 def log(*a):
@@ -40,17 +47,17 @@ def source_sha(path):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def read_counters():
-    """HBM bytes per launch of the sparse-attention kernel from the committed rocprofv3 counter summary, or
+def read_counters(path=COUNTERS, source=K3_SOURCE):
+    """HBM bytes per launch of a workload's dominant kernel from its committed rocprofv3 counter summary, or
     None when absent or taken on a different kernel source."""
-    if not os.path.exists(COUNTERS):
+    if not os.path.exists(path):
         return None
     kv = {}
-    for line in open(COUNTERS):
-        if ":" in line and not line.startswith("#"):
-            k, v = line.split(":", 1)
+    for line in open(path):
+        if ": " in line and not line.startswith("#"):
+            k, v = line.rsplit(": ", 1)  # keys may hold ':' themselves ("sha256[:16]")
             kv[k.strip()] = v.strip()
-    if kv.get("k_attn.hip sha256[:16]") != source_sha(K3_SOURCE):
+    if kv.get(f"{os.path.basename(source)} sha256[:16]") != source_sha(source):
         return None
     try:
         return float(kv["hbm bytes per launch (fetch+write, copy-calibrated)"])
@@ -84,6 +91,118 @@ def cpu_baseline(q, k, v, w, wl, heads, budget_s=30.0):
             "seconds": round(dt, 2)}
 
 
+def cpu_baseline_w8a8(x, w, bias, wl, rows, budget_s=30.0):
+    """The fp64 W8A8 oracle (unchanged, untuned) on whole 128-token blocks of the same layer; TOPS."""
+    import numpy as np
+    from oracle import w8a8 as ow
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # noqa: BLE001
+        cores = len(os.sched_getaffinity(0))
+    W = w.float().cpu().double().numpy()
+    b = bias.float().cpu().double().numpy()
+    wq, ws = ow.quantize_blocks(W)  # one-time weight quantization: not timed
+    done, t0 = 0, time.perf_counter()
+    for r0 in range(0, rows, 128):
+        X = x[r0:r0 + 128].float().cpu().double().numpy()
+        xq, xs = ow.quantize_blocks(X)
+        ow.block_gemm(xq, xs, wq, ws, b)
+        done += X.shape[0]
+        log(f"cpu baseline: {done}/{rows} tokens at {time.perf_counter() - t0:.1f} s")
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    del np
+    return {"value": done * 2.0 * wl.N * wl.K / dt / 1e12, "unit": "TOPS (2*M*N*K per layer)", "cores": int(cores),
+            "kind": "oracle", "sample": f"{done} of {wl.M} tokens (whole 128-token blocks), all {wl.N} outputs",
+            "seconds": round(dt, 2)}
+
+
+def main_w8a8(args, name):
+    import torch
+    import int8_block_sparse_amd as sg
+    import int8_block_sparse_amd.w8a8 as w8
+    import synth
+
+    if name not in synth.LINEAR_WORKLOADS:
+        sys.exit(f"unknown W8A8 shape {name}; one of {sorted(synth.LINEAR_WORKLOADS)}")
+    if not torch.cuda.is_available():
+        sys.exit("bench.py needs a GPU")
+    sg.load()
+    dev = torch.device("cuda:0")
+    wl = synth.LINEAR_WORKLOADS[name]
+    log(f"generating {wl.name} inputs on the GPU")
+    x, w, bias = synth.make_linear(wl, 0, device=dev)
+    wq, wsc = w8.quantize(w)  # weights are quantized once, outside the timed steps
+    y = torch.empty(wl.M, wl.N, dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(w8.workspace_bytes(wl.M, wl.K), dtype=torch.uint8, device=dev)
+    x8 = ws[:wl.M * wl.K].view(torch.int8).view(wl.M, wl.K)  # the layer's activation codes live in the workspace
+    off = (wl.M * wl.K + 255) // 256 * 256
+    xs = ws[off:off + 4 * w8.n_blocks(wl.M) * (wl.K // 128)].view(torch.float32).view(w8.n_blocks(wl.M), wl.K // 128)
+    step = lambda: w8.linear(x, wq, wsc, bias, clip=1.0, out=y, workspace=ws)
+    for _ in range(args.warmup):
+        step()
+    # per-kernel times: the two launches of one step, bracketed by events on the launch stream
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record()
+        w8.quantize(x, 1.0, x8, xs)
+        ev[i][1].record()
+        w8.gemm(x8, xs, wq, wsc, bias, out=y)
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    ms = dt * 1e3 / args.steps
+    t_q = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
+    t_g = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
+    log(f"{ms:.3f} ms/layer; quantize {t_q:.3f} ms, gemm {t_g:.3f} ms")
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib << 20
+        a = torch.empty(n, dtype=torch.uint8, device=dev)
+        a2 = torch.empty_like(a)
+        a2.copy_(a)
+        torch.cuda.synchronize()
+    ops = wl.ops
+    gemm_tops = ops / (t_g * 1e-3) / 1e12
+    result = {
+        "metric": "W8A8 block-quantized linear layer TOPS (2*M*N*K per layer, INT8 MFMA)",
+        "value": round(ops / (ms * 1e-3) / 1e12, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "M": wl.M, "N": wl.N, "K": wl.K, "block": 128, "clip": 1.0, "bias": True,
+                   "parallelism": "single GPU"},
+        "stages_ms": {"quantize": round(t_q, 4), "gemm": round(t_g, 4)},
+        "roofline": {
+            "kernel": "k5_gemm (block-scaled INT8 product)",
+            "bound": "mfma",
+            "achieved": round(gemm_tops, 1),
+            "peak": PEAK_INT8_TOPS,
+            "unit": "TOPS (INT8)",
+            "frac": round(gemm_tops / PEAK_INT8_TOPS, 4),
+            "traffic": read_counters(W8A8_COUNTERS, W8A8_SOURCE) if name == "wan14b-720p-proj" else None,
+            "avg_launch_ms": round(t_g, 4),
+            "ops_i8_per_launch": ops,
+        },
+    }
+    if not args.no_cpu_baseline:
+        del ws, x8, xs
+        result["cpu_baseline"] = cpu_baseline_w8a8(x, w, bias, wl, rows=1024)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -92,12 +211,18 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (HBM-counter calibration under rocprofv3)")
+    ap.add_argument("--workload", default="sagesla",
+                    help="sagesla (the headline attention layer) or w8a8-<shape> (the W8A8 linear layer)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the forward shards by "
               f"(batch, head) with no exchange, so N GPUs would each run this same kernel set on B*H/N heads.",
               file=sys.stderr)
         sys.exit(2)
+    if args.workload.startswith("w8a8-"):
+        return main_w8a8(args, args.workload[len("w8a8-"):])
+    if args.workload != "sagesla":
+        sys.exit(f"unknown workload {args.workload}")
 
     import torch
     import int8_block_sparse_amd as sg

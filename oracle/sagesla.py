@@ -18,6 +18,8 @@ Sources are the TurboDiffusion pages:
 The pages describe the method only in prose. Every step they leave open is fixed here by the plainest
 reading, stated at the function that applies it.
 
+Optionally first, per token over all heads: Q, K <- RMSNorm with a per-channel weight (qk_rmsnorm; [TD-news]
+§三(四) item 2, point 1).
 Per (batch b, head h), with Q, K, V the [N, D] slices, bq/bk the query/key block sizes:
   1. mu     = fp32(sum_t K[t] / N)                       K-mean over all N tokens (smoothing)
   2. k'     = fp32(K - mu)                               smoothed keys; Q and V are not smoothed
@@ -42,7 +44,7 @@ import math
 import numpy as np
 
 __all__ = [
-    "topk_count", "n_blocks", "block_rows", "exact_sum_ok", "k_mean", "smooth", "quantize", "dequantize",
+    "bf16_round", "qk_rmsnorm", "topk_count", "n_blocks", "block_rows", "exact_sum_ok", "k_mean", "smooth", "quantize", "dequantize",
     "pool", "block_scores", "select_topk", "sparse_attention", "phi", "linear_states", "linear_branch",
     "project", "forward_head", "forward", "dense_attention",
 ]
@@ -69,6 +71,39 @@ def topk_count(frac: float, n_kb: int) -> int:
     if frac >= 1.0:
         return n_kb
     return max(1, int(math.floor(frac * n_kb + 0.5)))
+
+
+# --------------------------------------------------------------------------------------------------------
+# 0. RMSNorm of Q and K before the path  ([TD-news] §三(四) item 2, point 1: LayerNorm and RMSNorm operators
+#    rewritten for the GPU; §四 step 4: the sampler calls them)
+# --------------------------------------------------------------------------------------------------------
+def bf16_round(x):
+    """Round values that are exact fp32 numbers (held in fp64) to bf16, round-to-nearest-even (finite inputs)."""
+    u = np.asarray(x, dtype=np.float64).astype(np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return u.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def qk_rmsnorm(X, gamma, eps):
+    """RMSNorm of every token over all H*D channels of its heads, with a per-channel weight.
+
+    Reading: the pages name the RMSNorm/LayerNorm operators of the video DiTs they accelerate without their
+    formula; those models normalize the projected queries and keys by RMSNorm over the model width (all heads
+    of a token) with a learned weight, so: X [H, N, D] (one batch entry), gamma [H*D] (bf16 values), eps.
+    Per token: S = sum of x^2 over the H*D channels (exact in fp64 when exact_sum_ok holds for the squares),
+    m = S / (H*D), r = fp32(1 / sqrt(m + eps)) (three fp64 operations, each correctly rounded, then fp32);
+    the output is y = bf16(fp32(bf16(fp32(x * r)) * gamma)): the normalized value rounded to bf16 before the
+    weight, as the models compute it. Returns (Y [H, N, D], r [N], exact flag)."""
+    X = np.asarray(X, np.float64)
+    H, N, D = X.shape
+    sq = (X * X).transpose(0, 2, 1).reshape(H * D, N)  # squares of bf16 values: exact in fp64
+    exact = exact_sum_ok(sq)
+    S = sq.sum(axis=0)
+    m = S / float(H * D)
+    r = (1.0 / np.sqrt(m + float(np.float32(eps)))).astype(np.float32).astype(np.float64)
+    g = np.asarray(gamma, np.float64).reshape(H, 1, D)
+    n = bf16_round(X * r[None, :, None])  # the fp32 product rounds exactly like its fp64 value: 8 + 24 bits
+    return bf16_round(n * g), r, exact
 
 
 # --------------------------------------------------------------------------------------------------------
@@ -355,9 +390,27 @@ def _sparse_float(Q, Kp, V, idx, blk_q, blk_k, sm_scale, sq, sk):
     return out
 
 
-def forward(q, k, v, w_p, blk_q, blk_k, topk, **kw):
-    """Batched wrapper: q, k, v [B, H, N, D]; returns a list (over b, h) of forward_head results."""
+def forward(q, k, v, w_p, blk_q, blk_k, topk, qk_norm=None, **kw):
+    """Batched wrapper: q, k, v [B, H, N, D]; returns a list (over b, h) of forward_head results.
+
+    qk_norm = (gamma_q [H*D], gamma_k [H*D], eps) first normalizes Q and K with qk_rmsnorm per batch entry; the
+    whole path then sees the normalized values (each head's result also carries them as 'q_hat', 'k_hat')."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
     B, H = q.shape[:2]
-    return [[forward_head(q[b, h], k[b, h], v[b, h], w_p, blk_q, blk_k, topk,
-                          **{**kw, "mask": (kw.get("mask")[b][h] if kw.get("mask") is not None else None)})
-             for h in range(H)] for b in range(B)]
+    out = []
+    for b in range(B):
+        qb, kb = q[b], k[b]
+        if qk_norm is not None:
+            gq, gk, eps = qk_norm
+            qb = qk_rmsnorm(qb, gq, eps)[0]
+            kb = qk_rmsnorm(kb, gk, eps)[0]
+        row = []
+        for h in range(H):
+            r = forward_head(qb[h], kb[h], v[b, h], w_p, blk_q, blk_k, topk,
+                             **{**kw, "mask": (kw.get("mask")[b][h] if kw.get("mask") is not None else None)})
+            if qk_norm is not None:
+                r["q_hat"], r["k_hat"] = qb[h], kb[h]
+            row.append(r)
+        out.append(row)
+    return out

@@ -30,7 +30,7 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = ["Workload", "WORKLOADS", "workload", "custom", "make", "topk_blocks", "n_blocks", "LinearWorkload",
-           "LINEAR_WORKLOADS", "make_linear"]
+           "LINEAR_WORKLOADS", "make_linear", "make_norm_weights", "NORM_EPS"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -227,3 +227,20 @@ def make_linear(wl: LinearWorkload, seed: int = 0, device="cpu", bias: bool = Tr
         r1 = min(M, r0 + step)
         x[r0:r1] = (torch.randn(r1 - r0, K, generator=g, device=dev) * chan).to(torch.bfloat16)
     return x, w, (b if bias else None)
+
+
+# ---------------------------------------------------------------------------------------------------------
+# RMSNorm weights of Q and K (the norm before the attention path)
+# ---------------------------------------------------------------------------------------------------------
+NORM_EPS = 1e-6  # the epsilon of the Wan DiTs' RMSNorm
+
+
+def make_norm_weights(H: int, D: int, seed: int = 0, device="cpu"):
+    """(gamma_q, gamma_k): bf16 [H*D] each, 1 + 0.1 N(0,1) drawn in fp32 from one generator seeded with
+    ``seed`` (gamma_q first), rounded once to bf16."""
+    dev = torch.device(device)
+    g = torch.Generator(device=dev)
+    g.manual_seed(int(seed) + 7919)
+    gq = (1.0 + 0.1 * torch.randn(H * D, generator=g, device=dev)).to(torch.bfloat16)
+    gk = (1.0 + 0.1 * torch.randn(H * D, generator=g, device=dev)).to(torch.bfloat16)
+    return gq, gk

@@ -86,7 +86,37 @@ def _project_transposed(O_l, W_p):
     return _orig["project"](O_l, np.asarray(W_p).T)
 
 
+def _rmsnorm_per_head(X, gamma, eps):
+    # normalizes each head's D channels alone instead of all H*D channels of the token
+    X = np.asarray(X, np.float64)
+    H, N, D = X.shape
+    g = np.asarray(gamma, np.float64).reshape(H, D)
+    outs, rs = [], []
+    for h in range(H):
+        y, r, ex = _orig["qk_rmsnorm"](X[h:h + 1], g[h], eps)
+        outs.append(y[0])
+        rs.append(r)
+    return np.stack(outs), rs[0], True
+
+
+def _rmsnorm_no_weight(X, gamma, eps):
+    return _orig["qk_rmsnorm"](X, np.ones_like(np.asarray(gamma, np.float64)), eps)
+
+
+def _rmsnorm_sum_not_mean(X, gamma, eps):
+    # divides by the root of the sum of squares instead of their mean
+    X = np.asarray(X, np.float64)
+    H, N, D = X.shape
+    S = (X * X).sum(axis=(0, 2))
+    r = (1.0 / np.sqrt(S + float(np.float32(eps)))).astype(np.float32).astype(np.float64)
+    n = orc.bf16_round(X * r[None, :, None])
+    return orc.bf16_round(n * np.asarray(gamma, np.float64).reshape(H, 1, D)), r, True
+
+
 MUTATIONS = {
+    "rmsnorm_per_head": ("qk_rmsnorm", _rmsnorm_per_head),
+    "rmsnorm_no_weight": ("qk_rmsnorm", _rmsnorm_no_weight),
+    "rmsnorm_sum_not_mean": ("qk_rmsnorm", _rmsnorm_sum_not_mean),
     "phi_no_plus_one": ("phi", _phi_no_plus_one),
     "quantize_div128": ("quantize", _quantize_div128),
     "quantize_floor": ("quantize", _quantize_floor),
@@ -122,6 +152,8 @@ def _run_pins():
         lambda: pins.test_linear_bruteforce_marginal_keys(rng()),
         lambda: pins.test_phi_matches_library(rng()),
         lambda: pins.test_combine_special_cases(),
+        lambda: pins.test_rmsnorm_matches_library(),
+        lambda: pins.test_rmsnorm_unit_rms_with_unit_weight(),
     ]
     failed = 0
     for c in checks:

@@ -360,3 +360,66 @@ def test_combine_special_cases():
     assert not r["out"].any()
     r = orc.forward_head(Q, K, V, np.eye(wl.D), wl.blk_q, wl.blk_k, 4)
     np.testing.assert_allclose(r["out"], r["o_s"] + r["o_l"], atol=1e-15, rtol=0)
+
+
+# ---------------------------------------------------------------------------------------------------------
+# RMSNorm of Q and K over all heads of a token (the optional step before the path)
+# ---------------------------------------------------------------------------------------------------------
+def _norm_inputs(H=3, N=50, D=128, seed=0):
+    rng = np.random.default_rng(seed)
+    X = rng.standard_normal((H, N, D)) * np.exp(rng.standard_normal((1, N, 1)))
+    X = orc.bf16_round(X)
+    gamma = orc.bf16_round(1 + 0.1 * rng.standard_normal(H * D))
+    return X, gamma
+
+
+def test_rmsnorm_matches_library():
+    # torch's fp64 rms_norm over the H*D channels of each token, weight applied: the oracle differs only by its
+    # two bf16 roundings (relative 2^-8 each at most) and r's fp32 rounding (2^-24): y = x r g (1+d1)(1+d2)(1+d3)
+    X, gamma = _norm_inputs()
+    H, N, D = X.shape
+    Y, r, exact = orc.qk_rmsnorm(X, gamma, 1e-6)
+    assert exact
+    t = torch.from_numpy(X.transpose(1, 0, 2).reshape(N, H * D))
+    ref = torch.nn.functional.rms_norm(t, (H * D,), torch.from_numpy(gamma), eps=float(np.float32(1e-6)))
+    ref = ref.numpy().reshape(N, H, D).transpose(1, 0, 2)
+    np.testing.assert_allclose(Y, ref, rtol=2.0 ** -7 + 2.0 ** -15, atol=0)
+    assert np.max(np.abs(Y / ref - 1)) > 2.0 ** -9  # both roundings are really there
+    # r itself: the fp32 rounding of the exact reciprocal root
+    np.testing.assert_allclose(r, 1 / np.sqrt((X ** 2).mean(axis=(0, 2)) + float(np.float32(1e-6))), rtol=2.0 ** -24)
+
+
+def test_rmsnorm_scale_invariance_and_zero_token():
+    X, gamma = _norm_inputs(seed=1)
+    X[:, 7] = 0.0
+    Y, r, _ = orc.qk_rmsnorm(X, gamma, 0.0 + 1e-30)  # eps far below every mean square
+    X2 = X.copy()
+    X2[:, 3] *= 2.0 ** 5
+    X2[:, 4] *= 2.0 ** -7
+    Y2, r2, _ = orc.qk_rmsnorm(X2, gamma, 1e-30)
+    np.testing.assert_array_equal(Y2[:, 3], Y[:, 3])
+    np.testing.assert_array_equal(Y2[:, 4], Y[:, 4])
+    assert r2[3] == r[3] * 2.0 ** -5 and r2[4] == r[4] * 2.0 ** 7
+    assert not Y[:, 7].any()
+
+
+def test_rmsnorm_unit_rms_with_unit_weight():
+    X, _ = _norm_inputs(seed=2)
+    Y, _, _ = orc.qk_rmsnorm(X, np.ones(X.shape[0] * X.shape[2]), 1e-6)
+    ms = (Y ** 2).mean(axis=(0, 2))
+    np.testing.assert_allclose(ms, 1.0, rtol=2.0 ** -7)
+
+
+def test_forward_with_norm_equals_forward_on_normalized_inputs():
+    wl = SMALL[1]
+    q, k, v, w = synth.make(synth.custom(1, 2, 1000, blk_q=128, blk_k=64), 0)
+    gq, gk = synth.make_norm_weights(2, 128, 0)
+    Q, K, V, W = to_np(q), to_np(k), to_np(v), to_np(w)
+    res = orc.forward(Q, K, V, W, 128, 64, 3, qk_norm=(to_np(gq), to_np(gk), synth.NORM_EPS))
+    qh = orc.qk_rmsnorm(Q[0], to_np(gq), synth.NORM_EPS)[0]
+    kh = orc.qk_rmsnorm(K[0], to_np(gk), synth.NORM_EPS)[0]
+    for h in range(2):
+        r = orc.forward_head(qh[h], kh[h], V[0, h], W, 128, 64, 3)
+        np.testing.assert_array_equal(res[0][h]["out"], r["out"])
+        np.testing.assert_array_equal(res[0][h]["q_hat"], qh[h])
+    del wl

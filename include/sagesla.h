@@ -36,7 +36,8 @@ extern "C" {
 typedef enum {
   SAGESLA_OK = 0,
   SAGESLA_E_NULL = 1,        /* a required pointer is NULL                                              */
-  SAGESLA_E_SHAPE = 2,       /* B, H or N < 1, B*H > 65535, topk outside [0, n_kb], sm_scale < 0 or NaN   */
+  SAGESLA_E_SHAPE = 2,       /* B, H or N < 1, B*H > 65535, topk outside [0, n_kb], sm_scale < 0 or NaN,
+                                norm_eps negative or not finite (with SAGESLA_QK_RMSNORM)                    */
   SAGESLA_E_UNSUPPORTED = 3, /* D != 128, blk_k != 64, blk_q not in {64, 128}, unknown flag bits,
                                 N > 2^24 or n_kb > 20480                                                  */
   SAGESLA_E_WORKSPACE = 4,   /* workspace smaller than sagesla_workspace_bytes()                         */
@@ -45,7 +46,7 @@ typedef enum {
 } sagesla_status;
 
 /* stages of sagesla_forward, in launch order (for the optional timing events) */
-#define SAGESLA_STAGE_QUANTIZE 0 /* K mean, smoothing, INT8 codes, scales, pooled means          */
+#define SAGESLA_STAGE_QUANTIZE 0 /* (RMSNorm of Q and K,) K mean, smoothing, INT8 codes, scales, pooled means */
 #define SAGESLA_STAGE_SELECT 1   /* block scores and top-k                                          */
 #define SAGESLA_STAGE_LINEAR 2   /* linear branch: block states and the remaining state of each query block */
 #define SAGESLA_STAGE_ATTN 3     /* block-sparse INT8 attention, then per query block the linear branch's
@@ -59,6 +60,9 @@ typedef enum {
 #define SAGESLA_QUANT_GROUP32 0x8u  /* one INT8 scale per 32 tokens of Q and of K instead of one per block: the
                                        "thread-level" granularity of [TD-news] §三(一) item 2, each 32×32 tile of
                                        scores with its own pair of scales (q_scale/k_scale then hold n_g values) */
+#define SAGESLA_QK_RMSNORM 0x10u    /* first normalize Q and K, per token over all H*D channels of its heads, by
+                                       RMSNorm with the weights q_norm_w / k_norm_w ([TD-news] §三(四) item 2,
+                                       point 1); every later step sees the normalized values (see sagesla_quantize) */
 
 typedef struct sagesla_params {
   int32_t B, H, N, D;   /* batch, heads, tokens, head dim (D == 128)                                       */
@@ -85,6 +89,13 @@ typedef struct sagesla_params {
      records events[2s] on `stream` just before stage s and events[2s+1] just after it (both at the same point
      when the stage has nothing to do). The caller owns the events and reads them after synchronizing.       */
   void* const* events;
+  /* RMSNorm of Q and K (SAGESLA_QK_RMSNORM): bf16 [H*D] weights, indexed h*D + d (required with the flag), and
+     eps (finite, >= 0). q_hat / k_hat: optional exports [B][H][N][D] bf16 of the normalized Q and K. */
+  const void* q_norm_w;
+  const void* k_norm_w;
+  void* q_hat;
+  void* k_hat;
+  float norm_eps;
 } sagesla_params;
 
 /* Bytes of workspace the three entry points need for these parameters (all intermediates kept inside).
@@ -97,7 +108,13 @@ size_t sagesla_workspace_bytes(const sagesla_params* p);
 sagesla_status sagesla_validate(const sagesla_params* p);
 
 /* Quantize stage ([TD-news] §三(一) items 1–2).
-   Reads q, k (bf16 [B][H][N][D]). With SAGESLA_SMOOTH_K, k_mean = fp32(exact column sum / N) per (b, h) and
+   Reads q, k (bf16 [B][H][N][D]). With SAGESLA_QK_RMSNORM these are first replaced by their normalized
+   values: per (b, token n), S = the sum of x^2 over the H*D channels of q[b][:][n][:] (fp64; exact, and so
+   order-independent, when every partial sum is representable), r = fp32(1 / sqrt(S / (H*D) + eps)) (fp64
+   division, addition, square root and reciprocal, each correctly rounded, then one rounding to fp32), and
+   x_hat = bf16_rne(fp32(bf16_rne(fp32(x * r)) * w[h*D + d])); likewise k with k_norm_w. Everything below then
+   applies to q_hat and k_hat (the K mean, codes and pooled means here; the selection, both attention branches
+   in sagesla_forward). With SAGESLA_SMOOTH_K, k_mean = fp32(exact column sum / N) per (b, h) and
    K is smoothed to k' = fp32(K - k_mean); otherwise k' = K. Per block of blk_q query rows (blk_k key rows) × D
    channels, the last block holding only the remaining rows: scale = fp32(absmax/127) and
    code = clamp(round-half-even(fp32(x / scale)), -127, 127) for Q and for k'; with SAGESLA_QUANT_GROUP32 the

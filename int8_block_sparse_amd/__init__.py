@@ -14,7 +14,7 @@ from typing import Optional
 
 __all__ = [
     "LIB_PATH", "load", "Params", "SageSLAError", "topk_blocks", "n_blocks", "workspace_bytes", "validate",
-    "quantize", "select", "forward", "LINEAR", "SMOOTH_K", "USE_GIVEN_MASK", "QUANT_GROUP32", "STATUS", "STAGES",
+    "quantize", "select", "forward", "LINEAR", "SMOOTH_K", "USE_GIVEN_MASK", "QUANT_GROUP32", "QK_RMSNORM", "STATUS", "STAGES",
     "stage_events",
     "stage_ms", "Config",
 ]
@@ -25,6 +25,7 @@ LINEAR = 0x1
 SMOOTH_K = 0x2
 USE_GIVEN_MASK = 0x4
 QUANT_GROUP32 = 0x8  # one INT8 scale per 32 tokens of Q and of K (thread-level granularity)
+QK_RMSNORM = 0x10  # RMSNorm of Q and K over all heads of each token first
 
 STATUS = {0: "OK", 1: "E_NULL", 2: "E_SHAPE", 3: "E_UNSUPPORTED", 4: "E_WORKSPACE", 5: "E_ALIGN", 6: "E_HIP"}
 STAGES = ("quantize", "select", "linear", "attn")
@@ -50,6 +51,8 @@ class Params(ctypes.Structure):
         ("k_scale", ctypes.c_void_p), ("k_mean", ctypes.c_void_p), ("q_pool", ctypes.c_void_p),
         ("k_pool", ctypes.c_void_p), ("block_idx", ctypes.c_void_p), ("o_lin", ctypes.c_void_p),
         ("events", ctypes.POINTER(ctypes.c_void_p)),
+        ("q_norm_w", ctypes.c_void_p), ("k_norm_w", ctypes.c_void_p), ("q_hat", ctypes.c_void_p),
+        ("k_hat", ctypes.c_void_p), ("norm_eps", ctypes.c_float),
     ]
 
 
@@ -127,6 +130,7 @@ class Config:
     smooth_k: bool = True
     sm_scale: float = 0.0
     group32: bool = False  # one INT8 scale per 32 tokens instead of one per block
+    qk_norm: bool = False  # RMSNorm of Q and K first (weights and eps passed as pointers / norm_eps)
 
     @property
     def n_qb(self) -> int:
@@ -145,7 +149,8 @@ class Config:
         return n_blocks(self.N, 32) if self.group32 else self.n_kb
 
     def params(self, **ptrs) -> Params:
-        flags = (LINEAR if self.linear else 0) | (SMOOTH_K if self.smooth_k else 0) | (QUANT_GROUP32 if self.group32 else 0)
+        flags = ((LINEAR if self.linear else 0) | (SMOOTH_K if self.smooth_k else 0) |
+                 (QUANT_GROUP32 if self.group32 else 0) | (QK_RMSNORM if self.qk_norm else 0))
         if ptrs.pop("given_mask", False):
             flags |= USE_GIVEN_MASK
         p = Params(B=self.B, H=self.H, N=self.N, D=self.D, blk_q=self.blk_q, blk_k=self.blk_k, topk=self.topk,
@@ -215,6 +220,9 @@ def _exports(cfg: Config, device):
     }
     if cfg.linear:
         ex["o_lin"] = torch.empty(cfg.B, cfg.H, N, D, dtype=torch.float32, **f)
+    if cfg.qk_norm:
+        ex["q_hat"] = torch.empty(cfg.B, cfg.H, N, D, dtype=torch.bfloat16, **f)
+        ex["k_hat"] = torch.empty(cfg.B, cfg.H, N, D, dtype=torch.bfloat16, **f)
     del BH
     return ex
 
@@ -233,17 +241,30 @@ def stage_ms(evs):
     return {name: evs[2 * i].elapsed_time(evs[2 * i + 1]) for i, name in enumerate(STAGES)}
 
 
+def _norm_args(norm, H, D):
+    """(gamma_q, gamma_k, eps) -> Params fields; gammas bf16 [H*D] CUDA tensors."""
+    import torch
+    if norm is None:
+        return {}
+    gq, gk, eps = norm
+    for name, t in (("gamma_q", gq), ("gamma_k", gk)):
+        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous() or t.numel() != H * D:
+            raise ValueError(f"{name} must be a contiguous bf16 CUDA tensor of H*D elements")
+    return {"q_norm_w": gq.data_ptr(), "k_norm_w": gk.data_ptr(), "norm_eps": float(eps)}
+
+
 def forward(q, k, v, w_proj=None, *, topk: int, blk_q: int = 128, blk_k: int = 64, linear: bool = True,
             smooth_k: bool = True, sm_scale: float = 0.0, mask=None, out=None, workspace=None,
-            export: bool = False, events=None, group32: bool = False):
+            export: bool = False, events=None, group32: bool = False, norm=None):
     """SageSLA forward. q, k, v: bf16 [B, H, N, 128] CUDA tensors; w_proj: bf16 [128, 128] (needed with linear).
 
     mask: optional int32 [B, H, n_qb, topk] ascending block lists used instead of the selection.
     group32: one INT8 scale per 32 tokens of Q and of K instead of one per block.
+    norm: (gamma_q, gamma_k, eps) normalizes Q and K first (RMSNorm over the H*D channels of each token).
     export=True also returns a dict of every intermediate (codes, scales, K mean, pooled means, block lists,
     and the linear-branch output). Runs asynchronously on the current stream."""
     B, H, N, D = q.shape
-    cfg = Config(B, H, N, D, blk_q, blk_k, topk, linear, smooth_k, sm_scale, group32)
+    cfg = Config(B, H, N, D, blk_q, blk_k, topk, linear, smooth_k, sm_scale, group32, norm is not None)
     if out is None:
         import torch
         out = torch.empty_like(q)
@@ -256,7 +277,7 @@ def forward(q, k, v, w_proj=None, *, topk: int, blk_q: int = 128, blk_k: int = 6
         ex["block_idx"] = mask
     ptrs = {name: _ptr(t) for name, t in ex.items()}
     p = cfg.params(w_proj=_ptr(w_proj), workspace=ws.data_ptr(), workspace_bytes=ws.numel(),
-                   given_mask=mask is not None, **ptrs)
+                   given_mask=mask is not None, **ptrs, **_norm_args(norm, H, D))
     if events is not None:
         arr = (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
         p.events = ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p))
@@ -266,16 +287,17 @@ def forward(q, k, v, w_proj=None, *, topk: int, blk_q: int = 128, blk_k: int = 6
 
 
 def quantize(q, k, *, blk_q: int = 128, blk_k: int = 64, smooth_k: bool = True, workspace=None,
-             group32: bool = False):
+             group32: bool = False, norm=None):
     """Quantize stage alone: returns dict(q_i8, q_scale, k_i8, k_scale, k_mean, q_pool, k_pool) and the workspace
     (pass it to select())."""
     B, H, N, D = q.shape
-    cfg = Config(B, H, N, D, blk_q, blk_k, 0, False, smooth_k, group32=group32)
+    cfg = Config(B, H, N, D, blk_q, blk_k, 0, False, smooth_k, group32=group32, qk_norm=norm is not None)
     _shape_check(q, k, None, None, cfg)
     ws = _workspace(cfg, q.device, workspace)
     ex = _exports(cfg, q.device)
     ex.pop("block_idx")
-    p = cfg.params(workspace=ws.data_ptr(), workspace_bytes=ws.numel(), **{n: _ptr(t) for n, t in ex.items()})
+    p = cfg.params(workspace=ws.data_ptr(), workspace_bytes=ws.numel(), **{n: _ptr(t) for n, t in ex.items()},
+                   **_norm_args(norm, H, D))
     _check(load().sagesla_quantize(q.data_ptr(), k.data_ptr(), ctypes.byref(p), _stream(q.device)),
            "sagesla_quantize")
     return ex, ws

@@ -26,7 +26,8 @@ bool misaligned(const void* ptr, size_t a) { return ptr && ((uintptr_t)ptr % a) 
 sagesla_status check_shape(const sagesla_params* p) {
   if (!p) return SAGESLA_E_NULL;
   if (p->D != kD || p->blk_k != kBlkK || (p->blk_q != 64 && p->blk_q != 128)) return SAGESLA_E_UNSUPPORTED;
-  if (p->flags & ~(uint32_t)(SAGESLA_LINEAR | SAGESLA_SMOOTH_K | SAGESLA_USE_GIVEN_MASK | SAGESLA_QUANT_GROUP32))
+  if (p->flags & ~(uint32_t)(SAGESLA_LINEAR | SAGESLA_SMOOTH_K | SAGESLA_USE_GIVEN_MASK | SAGESLA_QUANT_GROUP32 |
+                             SAGESLA_QK_RMSNORM))
     return SAGESLA_E_UNSUPPORTED;
   if (p->B < 1 || p->H < 1 || p->N < 1) return SAGESLA_E_SHAPE;
   if ((int64_t)p->B * p->H > 65535) return SAGESLA_E_SHAPE;
@@ -35,6 +36,7 @@ sagesla_status check_shape(const sagesla_params* p) {
   if (n_kb > kMaxKeyBlocks) return SAGESLA_E_UNSUPPORTED;
   if (p->topk < 0 || p->topk > n_kb) return SAGESLA_E_SHAPE;
   if (!(isfinite(p->sm_scale) && p->sm_scale >= 0.f)) return SAGESLA_E_SHAPE;
+  if ((p->flags & SAGESLA_QK_RMSNORM) && !(isfinite(p->norm_eps) && p->norm_eps >= 0.f)) return SAGESLA_E_SHAPE;
   return SAGESLA_OK;
 }
 
@@ -43,10 +45,12 @@ sagesla_status check_params(const sagesla_params* p) {
   const sagesla_status st = check_shape(p);
   if (st != SAGESLA_OK) return st;
   if ((p->flags & SAGESLA_LINEAR) && !p->w_proj) return SAGESLA_E_NULL;
+  if ((p->flags & SAGESLA_QK_RMSNORM) && (!p->q_norm_w || !p->k_norm_w)) return SAGESLA_E_NULL;
   if (misaligned(p->w_proj, 16) || misaligned(p->q_i8, 16) || misaligned(p->k_i8, 16) ||
       misaligned(p->q_scale, 16) || misaligned(p->k_scale, 16) || misaligned(p->k_mean, 16) ||
       misaligned(p->q_pool, 16) || misaligned(p->k_pool, 16) || misaligned(p->block_idx, 16) ||
-      misaligned(p->o_lin, 16))
+      misaligned(p->o_lin, 16) || misaligned(p->q_norm_w, 16) || misaligned(p->k_norm_w, 16) ||
+      misaligned(p->q_hat, 16) || misaligned(p->k_hat, 16))
     return SAGESLA_E_ALIGN;
   return SAGESLA_OK;
 }
@@ -67,6 +71,10 @@ void make_plan(const sagesla_params* p, unsigned char* ws, Plan* pl) {
   pl->given_mask = (p->flags & SAGESLA_USE_GIVEN_MASK) != 0;
   pl->group32 = (p->flags & SAGESLA_QUANT_GROUP32) != 0;
   pl->n_g = (p->N + 31) / 32;
+  pl->qk_norm = (p->flags & SAGESLA_QK_RMSNORM) != 0;
+  pl->norm_eps = p->norm_eps;
+  pl->q_norm_w = p->q_norm_w;
+  pl->k_norm_w = p->k_norm_w;
   pl->sm_scale = p->sm_scale > 0.f ? p->sm_scale : 1.f / sqrtf((float)p->D);
   pl->colsum_chunk = kColsumChunk;
   pl->n_colsum_chunks = (p->N + kColsumChunk - 1) / kColsumChunk;
@@ -79,6 +87,10 @@ void make_plan(const sagesla_params* p, unsigned char* ws, Plan* pl) {
     off += align_up(bytes);
     return r;
   };
+  if (pl->qk_norm) {
+    pl->q_hat = (uint16_t*)take(BH * N * D * sizeof(uint16_t));
+    pl->k_hat = (uint16_t*)take(BH * N * D * sizeof(uint16_t));
+  }
   pl->colsum_part = (double*)take(BH * pl->n_colsum_chunks * D * sizeof(double));
   pl->k_mean = (float*)take(BH * D * sizeof(float));
   pl->q_i8 = (int8_t*)take(BH * N * D);
@@ -106,6 +118,8 @@ void make_plan(const sagesla_params* p, unsigned char* ws, Plan* pl) {
   if (p->q_pool) pl->q_pool = p->q_pool;
   if (p->k_pool) pl->k_pool = p->k_pool;
   if (p->block_idx) pl->block_idx = p->block_idx;
+  if (pl->qk_norm && p->q_hat) pl->q_hat = (uint16_t*)p->q_hat;
+  if (pl->qk_norm && p->k_hat) pl->k_hat = (uint16_t*)p->k_hat;
   pl->o_lin = lin_active ? p->o_lin : nullptr;  // optional export
 }
 
@@ -136,7 +150,14 @@ sagesla_status mark(const sagesla_params* p, int stage, int end, hipStream_t s) 
   return hip_status(hipEventRecord((hipEvent_t)ev, s));
 }
 
-sagesla_status run_quantize(const Plan& pl, const void* q, const void* k, const void* v, hipStream_t s) {
+// the Q and K every step after the optional norm reads: the caller's, or their normalized copies
+const void* eff_q(const Plan& pl, const void* q) { return pl.qk_norm ? (const void*)pl.q_hat : q; }
+const void* eff_k(const Plan& pl, const void* k) { return pl.qk_norm ? (const void*)pl.k_hat : k; }
+
+sagesla_status run_quantize(const Plan& pl, const void* q_in, const void* k_in, const void* v, hipStream_t s) {
+  if (pl.qk_norm) SAGESLA_TRY(launch_qk_norm(pl, (const uint16_t*)q_in, (const uint16_t*)k_in, s));
+  const void* q = eff_q(pl, q_in);
+  const void* k = eff_k(pl, k_in);
   SAGESLA_TRY(launch_kmean(pl, (const uint16_t*)k, s));
   SAGESLA_TRY(launch_quant(pl, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, s));
   return SAGESLA_OK;
@@ -208,13 +229,13 @@ sagesla_status sagesla_forward(const void* q, const void* k, const void* v, void
   SAGESLA_STEP(mark(p, SAGESLA_STAGE_LINEAR, 0, s));
   const bool lin_active = pl.linear && pl.topk < pl.n_kb;
   if (lin_active) {
-    SAGESLA_TRY(launch_linear(pl, (const uint16_t*)k, (const uint16_t*)v, s));
+    SAGESLA_TRY(launch_linear(pl, (const uint16_t*)eff_k(pl, k), (const uint16_t*)v, s));
   } else if (p->o_lin) {
     SAGESLA_TRY(launch_fill_f32(p->o_lin, (size_t)pl.BH * pl.N * kD, 0.f, s));
   }
   SAGESLA_STEP(mark(p, SAGESLA_STAGE_LINEAR, 1, s));
   SAGESLA_STEP(mark(p, SAGESLA_STAGE_ATTN, 0, s));
-  SAGESLA_TRY(launch_attn(pl, (const uint16_t*)q, (uint16_t*)out, s));
+  SAGESLA_TRY(launch_attn(pl, (const uint16_t*)eff_q(pl, q), (uint16_t*)out, s));
   SAGESLA_STEP(mark(p, SAGESLA_STAGE_ATTN, 1, s));
 #undef SAGESLA_STEP
   return SAGESLA_OK;

@@ -18,6 +18,12 @@ struct Plan {
   bool smooth, linear, given_mask;
   bool group32;  // one INT8 scale per 32 tokens (n_g = ceil(N / 32) per (b, h)) instead of one per block
   int n_g;
+  bool qk_norm;  // RMSNorm of Q and K over all heads of each token before everything else
+  float norm_eps;
+  const void* q_norm_w;  // bf16 [H * D]
+  const void* k_norm_w;
+  uint16_t* q_hat;  // [BH][N][D] bf16 normalized Q and K (workspace or caller export)
+  uint16_t* k_hat;
   float sm_scale;
   int colsum_chunk, n_colsum_chunks;
   const void* w_proj;
@@ -41,6 +47,8 @@ struct Plan {
   size_t ws_bytes;
 };
 
+// K0: RMSNorm of Q and K per token over all heads (writes p.q_hat, p.k_hat)
+hipError_t launch_qk_norm(const Plan& p, const uint16_t* q, const uint16_t* k, hipStream_t s);
 // K1: K-mean smoothing, per-block INT8 quantization and block mean pooling
 hipError_t launch_kmean(const Plan& p, const uint16_t* k, hipStream_t s);
 // (v may be null: then no V^T images are written)

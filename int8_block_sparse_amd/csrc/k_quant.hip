@@ -16,6 +16,99 @@
 
 namespace sagesla {
 
+// K0: RMSNorm of Q and K over all H*D channels of each token. grid (ceil(N / 8), B, 2: Q then K), 512 threads:
+// wave w takes token 8 blockIdx.x + w; lane l holds channels 8 (l % 16) .. +7 of heads 4 i + l / 16, so one
+// 16-byte load per lane covers four whole 256-byte head rows, and all of a token's loads are in flight at once
+// (up to 64 heads held in registers; more heads are read again for the output). The sum of squares (each square
+// of a bf16 value is exact in fp64) is kept as a double-double (Knuth's error-free TwoSum) per lane and through
+// the lane-exchange tree, so it is within n^2 2^-106 of the exact sum before its single rounding to fp64; TwoSum
+// is symmetric in its operands, so every lane of the tree ends with the same value. Output:
+// x_hat = bf16(fp32(bf16(fp32(x * r)) * w)).
+__device__ __forceinline__ void two_sum(double a, double b, double& s, double& e) {
+  s = a + b;
+  const double bb = s - a;
+  e = (a - (s - bb)) + (b - bb);
+}
+
+constexpr int kNormRegLoads = 16;  // head groups of 4 kept in registers (H <= 64)
+
+__global__ __launch_bounds__(512) void k0_rmsnorm(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                                                  const uint16_t* __restrict__ wq, const uint16_t* __restrict__ wk,
+                                                  uint16_t* __restrict__ q_hat, uint16_t* __restrict__ k_hat, int H,
+                                                  int N, float eps) {
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int n = blockIdx.x * 8 + w, b = blockIdx.y;
+  if (n >= N) return;  // whole wave: no barrier in this kernel
+  const bool isk = blockIdx.z != 0;
+  const uint16_t* src = isk ? k : q;
+  const uint16_t* wt = isk ? wk : wq;
+  uint16_t* dst = isk ? k_hat : q_hat;
+  const int hs = l >> 4, c0 = 8 * (l & 15);
+  const size_t plane = (size_t)N * kD;  // elements per (b, h) plane
+  const size_t base = (size_t)b * H * plane + (size_t)n * kD + c0;
+  const int ng = (H + 3) >> 2;  // head groups of 4
+  auto row = [&](int i) { return base + (size_t)(4 * i + hs) * plane; };
+  auto live = [&](int i) { return 4 * i + hs < H; };
+
+  uint4 x[kNormRegLoads];
+#pragma unroll
+  for (int i = 0; i < kNormRegLoads; ++i)
+    x[i] = (i < ng && live(i)) ? *(const uint4*)(src + row(i)) : make_uint4(0, 0, 0, 0);
+  double hi = 0.0, lo = 0.0, e;
+  auto acc8 = [&](const uint4& v) {
+    const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const double a = (double)bf16_lo(wd[j]), c = (double)bf16_hi(wd[j]);
+      two_sum(hi, a * a, hi, e);
+      lo += e;
+      two_sum(hi, c * c, hi, e);
+      lo += e;
+    }
+  };
+#pragma unroll
+  for (int i = 0; i < kNormRegLoads; ++i)
+    if (i < ng) acc8(x[i]);
+  for (int i = kNormRegLoads; i < ng; ++i)
+    if (live(i)) acc8(*(const uint4*)(src + row(i)));
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const double ho = __shfl_xor(hi, o), lw = __shfl_xor(lo, o);
+    two_sum(hi, ho, hi, e);
+    lo = (lo + lw) + e;
+  }
+  const double m = (hi + lo) / (double)(H * kD);
+  const float r = (float)(1.0 / sqrt(m + (double)eps));
+  auto norm8 = [&](int i, const uint4& v) {
+    const int h = 4 * i + hs;
+    const uint4 g = *(const uint4*)(wt + h * kD + c0);
+    const uint32_t wd[4] = {v.x, v.y, v.z, v.w}, gw[4] = {g.x, g.y, g.z, g.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float n0, n1, y0, y1;
+      {
+#pragma clang fp contract(off)
+        n0 = bf16_lo(wd[j]) * r;
+        n1 = bf16_hi(wd[j]) * r;
+      }
+      const uint32_t nb = pack_bf16x2(n0, n1);
+      {
+#pragma clang fp contract(off)
+        y0 = bf16_lo(nb) * bf16_lo(gw[j]);
+        y1 = bf16_hi(nb) * bf16_hi(gw[j]);
+      }
+      o[j] = pack_bf16x2(y0, y1);
+    }
+    *(uint4*)(dst + row(i)) = make_uint4(o[0], o[1], o[2], o[3]);
+  };
+#pragma unroll
+  for (int i = 0; i < kNormRegLoads; ++i)
+    if (i < ng && live(i)) norm8(i, x[i]);
+  for (int i = kNormRegLoads; i < ng; ++i)
+    if (live(i)) norm8(i, *(const uint4*)(src + row(i)));
+}
+
 // Partial column sums of K over row chunks, fp64. grid (n_chunks, BH), 256 threads:
 // thread t reads channels 8*(t%16)..+7 of rows t/16, t/16+16, ... (a wave reads 4 whole rows per load).
 __global__ __launch_bounds__(256) void k1_colsum_partial(const uint16_t* __restrict__ k, double* __restrict__ part,
@@ -225,6 +318,12 @@ hipError_t launch_fill_f32(float* dst, size_t n, float val, hipStream_t s) {
   size_t blocks = (n + 255) / 256;
   if (blocks > 65536) blocks = 65536;
   hipLaunchKernelGGL(k_fill_f32, dim3((unsigned)blocks), dim3(256), 0, s, dst, n, val);
+  return hipGetLastError();
+}
+
+hipError_t launch_qk_norm(const Plan& p, const uint16_t* q, const uint16_t* k, hipStream_t s) {
+  hipLaunchKernelGGL(k0_rmsnorm, dim3((p.N + 7) / 8, p.B, 2), dim3(512), 0, s, q, k, (const uint16_t*)p.q_norm_w,
+                     (const uint16_t*)p.k_norm_w, p.q_hat, p.k_hat, p.H, p.N, p.norm_eps);
   return hipGetLastError();
 }
 

@@ -91,7 +91,7 @@ def fwd(lib, p, q=FAKE, k=FAKE, v=FAKE, out=FAKE):
 
 @cpu_only
 @pytest.mark.parametrize("field,value,status", [
-    ("D", 64, 3), ("blk_k", 128, 3), ("blk_q", 32, 3), ("flags", 0x10, 3), ("N", (1 << 24) + 1, 3),
+    ("D", 64, 3), ("blk_k", 128, 3), ("blk_q", 32, 3), ("flags", 0x20, 3), ("N", (1 << 24) + 1, 3),
     ("B", 0, 2), ("H", 0, 2), ("N", 0, 2), ("topk", -1, 2), ("topk", 17, 2), ("B", 300, 2),
     ("sm_scale", float("nan"), 2), ("sm_scale", -1.0, 2),
     ("w_proj", None, 1), ("workspace", None, 4), ("workspace_bytes", 100, 4),
@@ -102,6 +102,24 @@ def test_forward_validation(lib, field, value, status):
     if field == "B":
         p.H = 300 if value == 300 else p.H
     assert fwd(lib, p) == status
+
+
+@cpu_only
+def test_norm_validation(lib):
+    p = good(flags=sg.LINEAR | sg.QK_RMSNORM, q_norm_w=FAKE, k_norm_w=FAKE, norm_eps=1e-6)
+    assert lib.sagesla_validate(ctypes.byref(p)) == 0
+    assert lib.sagesla_validate(ctypes.byref(good(flags=sg.LINEAR | sg.QK_RMSNORM, k_norm_w=FAKE))) == 1
+    assert lib.sagesla_validate(ctypes.byref(good(flags=sg.LINEAR | sg.QK_RMSNORM, q_norm_w=FAKE,
+                                                  k_norm_w=FAKE, norm_eps=-1.0))) == 2
+    assert lib.sagesla_validate(ctypes.byref(good(flags=sg.LINEAR | sg.QK_RMSNORM, q_norm_w=FAKE + 2,
+                                                  k_norm_w=FAKE))) == 5
+    assert lib.sagesla_validate(ctypes.byref(good(flags=sg.LINEAR | sg.QK_RMSNORM, q_norm_w=FAKE, k_norm_w=FAKE,
+                                                  q_hat=FAKE + 8))) == 5
+    # the norm's two [B][H][N][D] bf16 copies live in the workspace
+    cfg = sg.Config(B=1, H=2, N=1000, topk=2, linear=True)
+    plain = lib.sagesla_workspace_bytes(ctypes.byref(cfg.params()))
+    cfg.qk_norm = True
+    assert lib.sagesla_workspace_bytes(ctypes.byref(cfg.params())) >= plain + 2 * 2 * 1000 * 128 * 2
 
 
 @cpu_only

@@ -96,7 +96,7 @@ def _rmsnorm_per_head(X, gamma, eps):
         y, r, ex = _orig["qk_rmsnorm"](X[h:h + 1], g[h], eps)
         outs.append(y[0])
         rs.append(r)
-    return np.stack(outs), rs[0], True
+    return np.stack(outs), rs[0], np.zeros(N, dtype=bool)
 
 
 def _rmsnorm_no_weight(X, gamma, eps):
@@ -110,7 +110,7 @@ def _rmsnorm_sum_not_mean(X, gamma, eps):
     S = (X * X).sum(axis=(0, 2))
     r = (1.0 / np.sqrt(S + float(np.float32(eps)))).astype(np.float32).astype(np.float64)
     n = orc.bf16_round(X * r[None, :, None])
-    return orc.bf16_round(n * np.asarray(gamma, np.float64).reshape(H, 1, D)), r, True
+    return orc.bf16_round(n * np.asarray(gamma, np.float64).reshape(H, 1, D)), r, np.zeros(N, dtype=bool)
 
 
 MUTATIONS = {

@@ -378,8 +378,8 @@ def test_rmsnorm_matches_library():
     # two bf16 roundings (relative 2^-8 each at most) and r's fp32 rounding (2^-24): y = x r g (1+d1)(1+d2)(1+d3)
     X, gamma = _norm_inputs()
     H, N, D = X.shape
-    Y, r, exact = orc.qk_rmsnorm(X, gamma, 1e-6)
-    assert exact
+    Y, r, amb = orc.qk_rmsnorm(X, gamma, 1e-6)
+    assert not amb.any()
     t = torch.from_numpy(X.transpose(1, 0, 2).reshape(N, H * D))
     ref = torch.nn.functional.rms_norm(t, (H * D,), torch.from_numpy(gamma), eps=float(np.float32(1e-6)))
     ref = ref.numpy().reshape(N, H, D).transpose(1, 0, 2)
@@ -387,6 +387,15 @@ def test_rmsnorm_matches_library():
     assert np.max(np.abs(Y / ref - 1)) > 2.0 ** -9  # both roundings are really there
     # r itself: the fp32 rounding of the exact reciprocal root
     np.testing.assert_allclose(r, 1 / np.sqrt((X ** 2).mean(axis=(0, 2)) + float(np.float32(1e-6))), rtol=2.0 ** -24)
+
+
+def test_rmsnorm_sum_of_squares_is_exact():
+    # the double-double sum against Python's exactly rounded math.fsum, on values spanning 2^-60 .. 2^20
+    rng = np.random.default_rng(9)
+    v = orc.bf16_round(rng.standard_normal((3000, 7)) * 2.0 ** rng.integers(-30, 10, size=(3000, 7)))
+    sq = v * v
+    S = orc._sum_squares(sq)
+    assert all(S[j] == math.fsum(sq[:, j]) for j in range(7))
 
 
 def test_rmsnorm_scale_invariance_and_zero_token():

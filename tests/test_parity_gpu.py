@@ -109,7 +109,26 @@ def check_out(out, r, rows=None, lin=None, bf16_bound=False):
     return err, c
 
 
-def full_case(wl, seed=0, topk=None, linear=None, smooth_k=True, w_mul=1.0, prep=None, group32=False):
+def oracle_norm(x, b, gamma, chunk=4096):
+    """The oracle's RMSNorm of batch entry b of x ([B, H, N, D], any device), token chunk by token chunk (each
+    token's scale depends on all its heads only). Returns (normalized [H, N, D] fp64, True when no token's scale
+    rounding is ambiguous: the seeded inputs are checked to have none)."""
+    H, N, D = x.shape[1:]
+    y = np.empty((H, N, D))
+    clear = True
+    for n0 in range(0, N, chunk):
+        yc, _, amb = orc.qk_rmsnorm(to_np(x[b, :, n0:n0 + chunk]), to_np(gamma), synth.NORM_EPS)
+        y[:, n0:n0 + chunk] = yc
+        clear &= not amb.any()
+    return y, clear
+
+
+def check_hat(ex, b, h, want, name):
+    got = to_np(ex[name][b, h])
+    assert np.array_equal(got, want), f"{name}: {np.sum(got != want)} normalized values differ"
+
+
+def full_case(wl, seed=0, topk=None, linear=None, smooth_k=True, w_mul=1.0, prep=None, group32=False, norm=False):
     topk = wl.topk if topk is None else topk
     linear = wl.linear if linear is None else linear
     q, k, v, w = synth.make(wl, seed)
@@ -118,15 +137,25 @@ def full_case(wl, seed=0, topk=None, linear=None, smooth_k=True, w_mul=1.0, prep
     w = (w.float() * w_mul).to(torch.bfloat16)
     dq, dk, dv, dw = (t.cuda() for t in (q, k, v, w))
     say(f"case {wl.name} B{wl.B} H{wl.H} N{wl.N} bq{wl.blk_q} topk{topk} linear{linear} smooth{smooth_k}"
-        f" group32{group32}")
-    out, ex = run_gpu(dq, dk, dv, dw, wl, topk, linear=linear, smooth_k=smooth_k, group32=group32)
+        f" group32{group32} norm{norm}")
+    nw = synth.make_norm_weights(wl.H, wl.D, seed) if norm else None
+    out, ex = run_gpu(dq, dk, dv, dw, wl, topk, linear=linear, smooth_k=smooth_k, group32=group32,
+                      norm=(nw[0].cuda(), nw[1].cuda(), synth.NORM_EPS) if norm else None)
     qg = 32 if group32 else None
     outn = to_np(out)
     W = to_np(w)
     flagged = 0
     for b in range(wl.B):
+        if norm:
+            qh, eq = oracle_norm(q, b, nw[0])
+            kh, ek = oracle_norm(k, b, nw[1])
+            assert eq and ek
         for h in range(wl.H):
             Q, K, V = to_np(q[b, h]), to_np(k[b, h]), to_np(v[b, h])
+            if norm:
+                Q, K = qh[h], kh[h]
+                check_hat(ex, b, h, Q, "q_hat")
+                check_hat(ex, b, h, K, "k_hat")
             gidx = ex["block_idx"][b, h].cpu().numpy()
             r = orc.forward_head(Q, K, V, W, wl.blk_q, wl.blk_k, topk, linear=linear, smooth_k=smooth_k,
                                  quant_group=qg)
@@ -159,6 +188,12 @@ def test_forward_small(name):
 def test_forward_small_group32(name):
     # one INT8 scale per 32 tokens of Q and of K (thread-level granularity)
     assert full_case(SMALL[name], group32=True) == 0
+
+
+@pytest.mark.parametrize("name", ["tiny", "ragged128", "ragged64"])
+def test_forward_small_qk_norm(name):
+    # Q and K first normalized by RMSNorm over all heads of each token
+    assert full_case(SMALL[name], norm=True) == 0
 
 
 def test_topk_zero_linear_only():
@@ -257,18 +292,28 @@ def test_stage_entry_points_agree_with_forward():
 # the real layer shapes, in the launch configuration the benchmark times, checked on sampled (b, h) heads
 # and sampled query blocks (quantization and selection of a sampled head are checked in full)
 # ---------------------------------------------------------------------------------------------------------
-def sampled_case(cfg_id, heads, n_blocks_sample=6, seed=0, group32=False):
+def sampled_case(cfg_id, heads, n_blocks_sample=6, seed=0, group32=False, norm=False):
     wl = synth.workload(cfg_id)
     say(f"full-size {wl.name}: generating")
     q, k, v, w = synth.make(wl, seed, device="cuda")
+    nw = synth.make_norm_weights(wl.H, wl.D, seed, device="cuda") if norm else None
     torch.cuda.synchronize()
-    say(f"full-size {wl.name}: forward")
-    out, ex = run_gpu(q, k, v, w, wl, wl.topk, linear=wl.linear, group32=group32)
+    say(f"full-size {wl.name}: forward (group32 {group32}, norm {norm})")
+    out, ex = run_gpu(q, k, v, w, wl, wl.topk, linear=wl.linear, group32=group32,
+                      norm=(nw[0], nw[1], synth.NORM_EPS) if norm else None)
     W = to_np(w)
     rng = np.random.default_rng(cfg_id)
     flagged = 0
     for (b, h) in heads:
         Q, K, V = to_np(q[b, h]), to_np(k[b, h]), to_np(v[b, h])
+        if norm:
+            qh, eq = oracle_norm(q, b, nw[0])
+            kh, ek = oracle_norm(k, b, nw[1])
+            assert eq and ek
+            Q, K = qh[h], kh[h]
+            del qh, kh
+            check_hat(ex, b, h, Q, "q_hat")
+            check_hat(ex, b, h, K, "k_hat")
         gidx = ex["block_idx"][b, h].cpu().numpy()[:, :wl.topk]
         blocks = sorted(set([0, wl.n_qb - 1] + list(rng.choice(wl.n_qb, n_blocks_sample, replace=False))))
         r = orc.forward_head(Q, K, V, W, wl.blk_q, wl.blk_k, wl.topk, linear=wl.linear, mask=gidx, blocks=blocks,
@@ -307,3 +352,13 @@ def test_full_size_sla_1080p_long():
 def test_full_size_sla_720p_pair_group32():
     # the benchmarked layer with one INT8 scale per 32 tokens of Q and of K
     sampled_case(3, [(0, 0), (1, 39)], group32=True)
+
+
+def test_full_size_sla_480p_qk_norm():
+    # the 1.3B 480P layer with the RMSNorm of Q and K before the path
+    sampled_case(2, [(0, 0), (0, 11)], norm=True)
+
+
+def test_full_size_sla_720p_pair_qk_norm():
+    # the benchmarked layer with the RMSNorm of Q and K before the path
+    sampled_case(3, [(0, 0), (1, 39)], norm=True)

@@ -84,26 +84,47 @@ def bf16_round(x):
     return u.astype(np.uint32).view(np.float32).astype(np.float64)
 
 
+NORM_AMBIGUOUS = 2.0 ** -48  # relative band around r's fp32 rounding points within which a token is flagged
+
+
+def _sum_squares(sq):
+    """Sum over axis 0 of non-negative fp64 values (exact squares), nearly exactly: a double-double accumulator
+    (Knuth's error-free TwoSum, The Art of Computer Programming vol. 2, §4.2.2) whose error stays below
+    n^2 2^-106 of the sum, then rounded once to fp64."""
+    hi = np.zeros(sq.shape[1:])
+    lo = np.zeros(sq.shape[1:])
+    for v in sq:
+        s = hi + v
+        bb = s - hi
+        lo += (hi - (s - bb)) + (v - bb)
+        hi = s
+    return hi + lo
+
+
 def qk_rmsnorm(X, gamma, eps):
     """RMSNorm of every token over all H*D channels of its heads, with a per-channel weight.
 
     Reading: the pages name the RMSNorm/LayerNorm operators of the video DiTs they accelerate without their
     formula; those models normalize the projected queries and keys by RMSNorm over the model width (all heads
     of a token) with a learned weight, so: X [H, N, D] (one batch entry), gamma [H*D] (bf16 values), eps.
-    Per token: S = sum of x^2 over the H*D channels (exact in fp64 when exact_sum_ok holds for the squares),
-    m = S / (H*D), r = fp32(1 / sqrt(m + eps)) (three fp64 operations, each correctly rounded, then fp32);
-    the output is y = bf16(fp32(bf16(fp32(x * r)) * gamma)): the normalized value rounded to bf16 before the
-    weight, as the models compute it. Returns (Y [H, N, D], r [N], exact flag)."""
+    Per token: S = the sum of x^2 over the H*D channels, rounded once to fp64 (squares of bf16 values are exact;
+    the sum is taken nearly exactly), m = S / (H*D), r = fp32(1 / sqrt(m + eps)) (three fp64 operations, each
+    correctly rounded, then fp32); the output is y = bf16(fp32(bf16(fp32(x * r)) * gamma)): the normalized value
+    rounded to bf16 before the weight, as the models compute it.
+    A token is flagged ambiguous when r's fp32 rounding changes within a relative 2^-48 of its fp64 value: any
+    other faithful evaluation of S (within a few fp64 units) may then round r the other way. Returns
+    (Y [H, N, D], r [N], ambiguous [N] bool)."""
     X = np.asarray(X, np.float64)
     H, N, D = X.shape
     sq = (X * X).transpose(0, 2, 1).reshape(H * D, N)  # squares of bf16 values: exact in fp64
-    exact = exact_sum_ok(sq)
-    S = sq.sum(axis=0)
+    S = _sum_squares(sq)
     m = S / float(H * D)
-    r = (1.0 / np.sqrt(m + float(np.float32(eps)))).astype(np.float32).astype(np.float64)
+    r64 = 1.0 / np.sqrt(m + float(np.float32(eps)))
+    r = r64.astype(np.float32).astype(np.float64)
+    amb = (r64 * (1 - NORM_AMBIGUOUS)).astype(np.float32) != (r64 * (1 + NORM_AMBIGUOUS)).astype(np.float32)
     g = np.asarray(gamma, np.float64).reshape(H, 1, D)
     n = bf16_round(X * r[None, :, None])  # the fp32 product rounds exactly like its fp64 value: 8 + 24 bits
-    return bf16_round(n * g), r, exact
+    return bf16_round(n * g), r, amb
 
 
 # --------------------------------------------------------------------------------------------------------

@@ -1,0 +1,86 @@
+"""Plain fp64 CPU oracle of the SLA backward for a fixed block selection.
+
+TEST INFRASTRUCTURE ONLY. Nothing in the product path may import, call or execute this module: only the
+tests use it. It shares no code with the HIP library; both sides only consume the same seeded inputs.
+
+What is differentiated, and where the pages say so
+--------------------------------------------------
+[TD-news] ("Turbo Diffusion：秒级生成与高清保真的视频扩散技术突破", lanhy.cn) calls SLA trainable: §三(二)
+describes the sparse-plus-linear attention, and §四 step 1 fine-tunes the model with it before distillation.
+The pages give no backward. Reading (the plainest one): the gradient of the float forward for a fixed
+selection,
+    F(Q, K, V, W_p) = O_s + O_l W_p
+    O_s[i] = sum_j softmax_j(q_i . k_j * sm_scale) v_j over the keys j of the selected blocks of i's query block
+    O_l[i] = phi(q_i) H_m / (phi(q_i) . Z_m), H_m, Z_m = sum over the unselected key blocks of phi(K_J)^T V_J and
+             of the rows of phi(K_J); phi = elu + 1; O_l = 0 when every block is selected or linear is off,
+with INT8 quantization passed straight through (the codes dequantize to the inputs) and K-mean smoothing
+dropped (it shifts every score of a row by the same amount, so no softmax row, and no gradient, changes).
+Given dY = dL/dF, the backward returns dQ, dK, dV of each head and dW_p summed over the heads (W_p is shared).
+
+The gradient is computed by torch's reverse-mode differentiation (fp64, CPU) of that forward written out
+plainly below, one query block at a time; the tests pin it against central finite differences of the same
+forward and, for the dense special case, against torch's scaled_dot_product_attention.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+__all__ = ["forward_float_head", "backward_head", "backward"]
+
+
+def _blocks(n, blk):
+    return [(i * blk, min(n, (i + 1) * blk)) for i in range((n + blk - 1) // blk)]
+
+
+def forward_float_head(Q, K, V, W_p, idx, blk_q, blk_k, sm_scale=None, linear=True):
+    """F for one (b, h) head as fp64 torch tensors (differentiable); idx [n_qb][k] selected key blocks."""
+    N, D = Q.shape
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    kblocks = _blocks(N, blk_k)
+    phiQ = torch.where(Q > 0, Q + 1.0, torch.exp(torch.clamp(Q, max=0.0)))
+    phiK = torch.where(K > 0, K + 1.0, torch.exp(torch.clamp(K, max=0.0)))
+    rows_out = []
+    for I, (r0, r1) in enumerate(_blocks(N, blk_q)):
+        sel = sorted(set(int(J) for J in idx[I]))
+        o = torch.zeros(r1 - r0, D, dtype=Q.dtype)
+        if sel:
+            keys = torch.cat([torch.arange(*kblocks[J]) for J in sel])
+            p = torch.softmax((Q[r0:r1] @ K[keys].T) * sm_scale, dim=1)
+            o = o + p @ V[keys]
+        uns = [J for J in range(len(kblocks)) if J not in sel]
+        if linear and uns:
+            keys = torch.cat([torch.arange(*kblocks[J]) for J in uns])
+            Hm = phiK[keys].T @ V[keys]
+            Zm = phiK[keys].sum(dim=0)
+            o = o + ((phiQ[r0:r1] @ Hm) / (phiQ[r0:r1] @ Zm)[:, None]) @ W_p
+        rows_out.append(o)
+    return torch.cat(rows_out, dim=0)
+
+
+def backward_head(Q, K, V, W_p, idx, dY, blk_q, blk_k, sm_scale=None, linear=True):
+    """dQ, dK, dV (fp64 [N, D]) and this head's dW_p ([D, D]) for one head; inputs are arrays of exact values."""
+    t = lambda a: torch.tensor(np.asarray(a, np.float64), dtype=torch.float64, requires_grad=True)
+    Qt, Kt, Vt, Wt = t(Q), t(K), t(V), t(W_p)
+    F = forward_float_head(Qt, Kt, Vt, Wt, idx, blk_q, blk_k, sm_scale, linear)
+    (F * torch.as_tensor(np.asarray(dY, np.float64))).sum().backward()
+    return (Qt.grad.numpy(), Kt.grad.numpy(), Vt.grad.numpy(),
+            (Wt.grad.numpy() if Wt.grad is not None else np.zeros_like(np.asarray(W_p, np.float64))))
+
+
+def backward(q, k, v, w_p, idx, dy, blk_q, blk_k, sm_scale=None, linear=True, heads=None):
+    """Batched: q, k, v, dy [B, H, N, D], idx [B, H, n_qb, k]. Returns (dq, dk, dv) dicts keyed by (b, h) for
+    the requested heads (all by default) and dW_p summed over those heads."""
+    B, H = np.asarray(q).shape[:2]
+    heads = [(b, h) for b in range(B) for h in range(H)] if heads is None else heads
+    dq, dk, dv = {}, {}, {}
+    dW = np.zeros_like(np.asarray(w_p, np.float64))
+    for (b, h) in heads:
+        gq, gk, gv, gw = backward_head(q[b][h], k[b][h], v[b][h], w_p, idx[b][h], dy[b][h], blk_q, blk_k,
+                                       sm_scale, linear)
+        dq[b, h], dk[b, h], dv[b, h] = gq, gk, gv
+        dW += gw
+    return dq, dk, dv, dW

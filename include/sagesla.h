@@ -141,6 +141,21 @@ sagesla_status sagesla_select(const sagesla_params* p, void* stream);
 sagesla_status sagesla_forward(const void* q, const void* k, const void* v, void* out, const sagesla_params* p,
                                void* stream);
 
+/* SLA backward for a fixed selection (SLA is trainable: [TD-news] §三(二), fine-tuned with the model in §四).
+   Computes the gradient of the float forward
+     out = O_s + O_lin, O_s = softmax over the listed key blocks of q . k * sm_scale applied to v, O_lin as above,
+   with INT8 quantization passed straight through and the K-mean shift dropped (it changes no softmax row), for
+   the selection in block_idx (required when topk > 0; each row's blocks are a set: order and repeats do not
+   matter). dout: bf16 [B][H][N][D] = dL/d(out). Writes dq, dk, dv: fp32 [B][H][N][D], and with SAGESLA_LINEAR
+   dw_proj: fp32 [D][D], dL/dW_p summed over every (b, h) (zeros when every block is selected). Accumulation is
+   fp32 in a fixed order (deterministic); the score products run on bf16 MFMA with P and dS split into bf16
+   hi + lo pairs, the linear branch on fp32 vector arithmetic from the forward's remaining state (bf16 hi + lo).
+   SAGESLA_QK_RMSNORM is not differentiated (SAGESLA_E_UNSUPPORTED); SAGESLA_SMOOTH_K and SAGESLA_QUANT_GROUP32
+   do not change the result. The workspace must hold sagesla_backward_workspace_bytes(p) bytes. */
+size_t sagesla_backward_workspace_bytes(const sagesla_params* p);
+sagesla_status sagesla_backward(const void* q, const void* k, const void* v, const void* dout, float* dq, float* dk,
+                                float* dv, float* dw_proj, const sagesla_params* p, void* stream);
+
 /* Text of a status code (static storage). */
 const char* sagesla_status_str(sagesla_status s);
 

@@ -16,7 +16,7 @@ __all__ = [
     "LIB_PATH", "load", "Params", "SageSLAError", "topk_blocks", "n_blocks", "workspace_bytes", "validate",
     "quantize", "select", "forward", "LINEAR", "SMOOTH_K", "USE_GIVEN_MASK", "QUANT_GROUP32", "QK_RMSNORM", "STATUS", "STAGES",
     "stage_events",
-    "stage_ms", "Config",
+    "stage_ms", "Config", "backward",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsagesla.so")
@@ -82,6 +82,10 @@ def load():
     lib.sagesla_select.restype = ctypes.c_int
     lib.sagesla_forward.argtypes = [vp, vp, vp, vp, P, vp]
     lib.sagesla_forward.restype = ctypes.c_int
+    lib.sagesla_backward_workspace_bytes.argtypes = [P]
+    lib.sagesla_backward_workspace_bytes.restype = ctypes.c_size_t
+    lib.sagesla_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, P, vp]
+    lib.sagesla_backward.restype = ctypes.c_int
     lib.sagesla_status_str.argtypes = [ctypes.c_int]
     lib.sagesla_status_str.restype = ctypes.c_char_p
     lib.sagesla_last_hip_error.argtypes = []
@@ -315,3 +319,33 @@ def select(q_pool, k_pool, *, N: int, topk: int, blk_q: int = 128, blk_k: int = 
                    k_pool=kp.data_ptr(), block_idx=idx.data_ptr())
     _check(load().sagesla_select(ctypes.byref(p), _stream(q_pool.device)), "sagesla_select")
     return idx[..., :topk]
+
+
+def backward(q, k, v, w_proj, dout, mask, *, topk: int, blk_q: int = 128, blk_k: int = 64, linear: bool = True,
+             sm_scale: float = 0.0, workspace=None):
+    """SLA backward for the fixed selection `mask` (int32 [B, H, n_qb, topk]): gradient of the float forward
+    (INT8 quantization straight through) given dout = dL/d(out) (bf16 [B, H, N, 128]). Returns fp32 (dq, dk, dv)
+    and dW_p (fp32 [128, 128], summed over every head; None without the linear branch). Runs on the current
+    stream."""
+    import torch
+    B, H, N, D = q.shape
+    cfg = Config(B, H, N, D, blk_q, blk_k, topk, linear, True, sm_scale)
+    _shape_check(q, k, v, dout, cfg)
+    if topk > 0 and (mask is None or mask.dtype != torch.int32 or not mask.is_contiguous()
+                     or tuple(mask.shape) != (B, H, cfg.n_qb, topk)):
+        raise ValueError("mask must be a contiguous int32 CUDA tensor [B, H, n_qb, topk]")
+    p0 = cfg.params(w_proj=_ptr(w_proj))
+    need = load().sagesla_backward_workspace_bytes(ctypes.byref(p0))
+    if need == 0:
+        _check(validate(cfg) or 3, "sagesla_backward_workspace_bytes")
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    f32 = dict(dtype=torch.float32, device=q.device)
+    dq, dk, dv = (torch.empty(B, H, N, D, **f32) for _ in range(3))
+    dw = torch.empty(D, D, **f32) if linear else None
+    p = cfg.params(w_proj=_ptr(w_proj), workspace=workspace.data_ptr(), workspace_bytes=workspace.numel(),
+                   block_idx=_ptr(mask) if topk > 0 else None)
+    _check(load().sagesla_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(), dq.data_ptr(),
+                                   dk.data_ptr(), dv.data_ptr(), _ptr(dw), ctypes.byref(p), _stream(q.device)),
+           "sagesla_backward")
+    return dq, dk, dv, dw

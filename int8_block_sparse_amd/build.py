@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libsagesla.so")
 BUILD = os.path.join(ROOT, "_build")
-SOURCES = ["api.cpp", "k_quant.hip", "k_select.hip", "k_linear.hip", "k_attn.hip", "k_w8a8.hip"]
+SOURCES = ["api.cpp", "k_quant.hip", "k_select.hip", "k_linear.hip", "k_attn.hip", "k_w8a8.hip", "k_backward.hip"]
 ARCH = "gfx950"
 
 

@@ -320,6 +320,93 @@ sagesla_status w8a8_linear(const void* x, const int8_t* w_i8, const float* w_sca
   return SAGESLA_OK;
 }
 
+// ---------------------------------------------------------------------------------------------------------
+// SLA backward for a fixed selection (include/sagesla.h)
+// ---------------------------------------------------------------------------------------------------------
+}  // extern "C"
+
+namespace {
+
+// the backward's buffers after the forward plan's (ws == nullptr: sizes only); returns the total bytes
+size_t plan_backward(const Plan& pl, unsigned char* ws, BwdPlan* b) {
+  size_t off = pl.ws_bytes;
+  auto take = [&](size_t bytes) -> unsigned char* {
+    unsigned char* r = ws ? ws + off : nullptr;
+    off += align_up(bytes);
+    return r;
+  };
+  const size_t BH = pl.BH, N = pl.N;
+  const bool lin_active = pl.linear && pl.topk < pl.n_kb;
+  b->lse = (float*)take(BH * N * sizeof(float));
+  b->dd = (float*)take(BH * N * sizeof(float));
+  b->sel_bits = (uint32_t*)take(BH * pl.n_kb * (size_t)((pl.n_qb + 31) / 32) * sizeof(uint32_t));
+  if (lin_active) {
+    b->o_l = (float*)take(BH * N * kD * sizeof(float));
+    b->dhm = (float*)take(BH * pl.n_qb * (size_t)kStateX * sizeof(float));
+    b->dhj = (float*)take(BH * pl.n_kb * (size_t)kStateX * sizeof(float));
+    b->dw_part = (float*)take(BH * backward_dw_chunks(pl.N) * kD * kD * sizeof(float));
+  }
+  return off;
+}
+
+sagesla_status check_backward(const sagesla_params* p) {
+  sagesla_status st = check_params(p);
+  if (st != SAGESLA_OK) return st;
+  if (p->flags & SAGESLA_QK_RMSNORM) return SAGESLA_E_UNSUPPORTED;
+  if (p->topk > 0 && !p->block_idx) return SAGESLA_E_NULL;
+  return SAGESLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t sagesla_backward_workspace_bytes(const sagesla_params* p) {
+  if (check_shape(p) != SAGESLA_OK || (p->flags & SAGESLA_QK_RMSNORM)) return 0;
+  Plan pl;
+  make_plan(p, nullptr, &pl);
+  BwdPlan b{};
+  return plan_backward(pl, nullptr, &b);
+}
+
+sagesla_status sagesla_backward(const void* q, const void* k, const void* v, const void* dout, float* dq, float* dk,
+                                float* dv, float* dw_proj, const sagesla_params* p, void* stream) {
+  sagesla_status st = check_backward(p);
+  if (st != SAGESLA_OK) return st;
+  if (!q || !k || !v || !dout || !dq || !dk || !dv) return SAGESLA_E_NULL;
+  if ((p->flags & SAGESLA_LINEAR) && !dw_proj) return SAGESLA_E_NULL;
+  if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(dout, 16) || misaligned(dq, 16) ||
+      misaligned(dk, 16) || misaligned(dv, 16) || misaligned(dw_proj, 16))
+    return SAGESLA_E_ALIGN;
+  Plan pl;
+  make_plan(p, nullptr, &pl);
+  BwdPlan b{};
+  const size_t need = plan_backward(pl, nullptr, &b);
+  if (p->workspace_bytes < need || !p->workspace) return SAGESLA_E_WORKSPACE;
+  if (misaligned(p->workspace, kAlign)) return SAGESLA_E_ALIGN;
+  make_plan(p, (unsigned char*)p->workspace, &pl);
+  plan_backward(pl, (unsigned char*)p->workspace, &b);
+  b.fwd = &pl;
+  b.q = (const uint16_t*)q;
+  b.k = (const uint16_t*)k;
+  b.v = (const uint16_t*)v;
+  b.dy = (const uint16_t*)dout;
+  b.dq = dq;
+  b.dk = dk;
+  b.dv = dv;
+  b.dw = dw_proj;
+  const hipStream_t s = (hipStream_t)stream;
+  const bool lin_active = pl.linear && pl.topk < pl.n_kb;
+  if (lin_active) SAGESLA_TRY(launch_linear(pl, (const uint16_t*)k, (const uint16_t*)v, s));
+  SAGESLA_TRY(launch_backward_sparse(b, s));
+  if (lin_active) {
+    SAGESLA_TRY(launch_backward_linear(b, s));
+  } else if (dw_proj) {
+    SAGESLA_TRY(launch_fill_f32(dw_proj, (size_t)kD * kD, 0.f, s));
+  }
+  return SAGESLA_OK;
+}
+
 const char* sagesla_status_str(sagesla_status s) {
   switch (s) {
     case SAGESLA_OK: return "ok";

@@ -65,6 +65,22 @@ hipError_t launch_w8a8_quant(const uint16_t* x, int rows, int cols, float clip, 
                              hipStream_t s);
 hipError_t launch_w8a8_gemm(const int8_t* x8, const float* xs, const int8_t* w8, const float* ws,
                             const uint16_t* bias, uint16_t* y, int M, int N, int K, hipStream_t s);
+// SLA backward for a fixed selection: buffers on top of a forward Plan (whose linear-branch state it reuses)
+struct BwdPlan {
+  const Plan* fwd;
+  const uint16_t *q, *k, *v, *dy;  // bf16 [BH][N][D]
+  float *dq, *dk, *dv, *dw;        // outputs: fp32 [BH][N][D], dW_p fp32 [D][D]
+  float* lse;                      // [BH][N] base-2 log-sum-exp of each row's selected scores
+  float* dd;                       // [BH][N] D_i = sum_j P_ij dP_ij
+  uint32_t* sel_bits;              // [BH][n_kb][ceil(n_qb/32)]
+  float* o_l;                      // [BH][N][D] linear-branch output before W_p
+  float* dhm;                      // [BH][n_qb][kStateX] per query block dH_m (c-major) then dZ_m
+  float* dhj;                      // [BH][n_kb][kStateX] per key block dH_J then dZ_J
+  float* dw_part;                  // [BH][n_chunks][D][D]
+};
+hipError_t launch_backward_sparse(const BwdPlan& b, hipStream_t s);
+hipError_t launch_backward_linear(const BwdPlan& b, hipStream_t s);
+size_t backward_dw_chunks(int N);
 // fills (graph-capture friendly replacements for memset)
 hipError_t launch_fill_f32(float* dst, size_t n, float val, hipStream_t s);
 // dynamic LDS of the kernels that size it at run time

@@ -28,7 +28,7 @@ import math
 import numpy as np
 import torch
 
-__all__ = ["forward_float_head", "backward_head", "backward"]
+__all__ = ["forward_float_head", "backward_head", "backward", "dq_blocks"]
 
 
 def _blocks(n, blk):
@@ -84,3 +84,44 @@ def backward(q, k, v, w_p, idx, dy, blk_q, blk_k, sm_scale=None, linear=True, he
         dq[b, h], dk[b, h], dv[b, h] = gq, gk, gv
         dW += gw
     return dq, dk, dv, dW
+
+
+def dq_blocks(Q, K, V, W_p, idx, dY, blk_q, blk_k, blocks, sm_scale=None, linear=True):
+    """The rows of dQ for the query blocks `blocks` alone: the output of a query block depends on Q only through
+    that block's own rows, so the gradient of the forward restricted to those blocks gives these rows exactly.
+    Returns {I: dQ rows [rows of I, D]}."""
+    N, D = np.asarray(Q).shape
+    out = {}
+    Kt = torch.as_tensor(np.asarray(K, np.float64))
+    Vt = torch.as_tensor(np.asarray(V, np.float64))
+    Wt = torch.as_tensor(np.asarray(W_p, np.float64))
+    for I in blocks:
+        r0, r1 = I * blk_q, min(N, (I + 1) * blk_q)
+        Qb = torch.tensor(np.asarray(Q, np.float64)[r0:r1], requires_grad=True)
+        # the block's rows as a query block of its own, against all keys (its selection unchanged)
+        Qfull = torch.cat([torch.zeros(r0, D, dtype=torch.float64), Qb,
+                           torch.zeros(N - r1, D, dtype=torch.float64)]) if (r0 or r1 < N) else Qb
+        nq = (N + blk_q - 1) // blk_q
+        sel = [idx[J] if J == I else [] for J in range(nq)]
+        F = forward_float_head(Qfull, Kt, Vt, Wt, sel, blk_q, blk_k, sm_scale, linear=False)[r0:r1]
+        if linear:
+            F = F + _linear_rows(Qb, Kt, Vt, Wt, idx[I], blk_k)
+        (F * torch.as_tensor(np.asarray(dY, np.float64)[r0:r1])).sum().backward()
+        out[I] = Qb.grad.numpy()
+    return out
+
+
+def _linear_rows(Qb, K, V, W_p, sel, blk_k):
+    """The linear branch of one query block's rows (phi(q) H_m / phi(q) . Z_m over its unselected key blocks)."""
+    N = K.shape[0]
+    kb = _blocks(N, blk_k)
+    s = set(int(J) for J in sel)
+    uns = [J for J in range(len(kb)) if J not in s]
+    if not uns:
+        return torch.zeros_like(Qb)
+    keys = torch.cat([torch.arange(*kb[J]) for J in uns])
+    phiK = torch.where(K[keys] > 0, K[keys] + 1.0, torch.exp(torch.clamp(K[keys], max=0.0)))
+    phiQ = torch.where(Qb > 0, Qb + 1.0, torch.exp(torch.clamp(Qb, max=0.0)))
+    Hm = phiK.T @ V[keys]
+    Zm = phiK.sum(dim=0)
+    return ((phiQ @ Hm) / (phiQ @ Zm)[:, None]) @ W_p

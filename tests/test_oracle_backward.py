@@ -91,3 +91,11 @@ def test_planted_forward_mistakes_are_caught(mut, monkeypatch):
     monkeypatch.setattr(ob, "forward_float_head", mut)
     with pytest.raises(AssertionError):
         test_forward_float_matches_quantization_free_forward()
+
+
+def test_dq_blocks_equals_full_backward():
+    Q, K, V, W, idx, dY = _case(N=330, k=2)
+    gQ, _, _, _ = ob.backward_head(Q, K, V, W, idx, dY, 64, 64)
+    part = ob.dq_blocks(Q, K, V, W, idx, dY, 64, 64, [0, 2, 5])
+    for I, rows in part.items():
+        np.testing.assert_allclose(rows, gQ[I * 64:min(330, I * 64 + 64)], rtol=1e-11, atol=1e-13)

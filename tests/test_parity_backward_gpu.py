@@ -105,3 +105,46 @@ def test_backward_deterministic():
     torch.cuda.synchronize()
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+
+
+# ---------------------------------------------------------------------------------------------------------
+# the 720P layer at full size, with the forward's own selection: exact dQ rows on sampled query blocks of two
+# heads; with the linear branch off, the invariants of softmax attention (sum_j dK_j = 0 because every row of dS
+# sums to zero; sum_j dV_j = sum_i dY_i because every row of P sums to one)
+# ---------------------------------------------------------------------------------------------------------
+def full_720p(linear):
+    wl = synth.workload(3)
+    q, k, v, w = synth.make(wl, 0, device="cuda")
+    say(f"full-size {wl.name}: forward for the selection")
+    _, ex = sg.forward(q, k, v, w, topk=wl.topk, export=True)
+    mask = ex["block_idx"][..., :wl.topk].contiguous()
+    del ex
+    dy = torch.randn(q.shape, device="cuda", generator=torch.Generator(device="cuda").manual_seed(1)).to(torch.bfloat16)
+    say(f"full-size {wl.name}: backward (linear {linear})")
+    grads = sg.backward(q, k, v, w, dy, mask, topk=wl.topk, linear=linear)
+    torch.cuda.synchronize()
+    return wl, q, k, v, w, dy, mask, grads
+
+
+def test_backward_full_size_720p_dq_blocks():
+    wl, q, k, v, w, dy, mask, (dq, dk, dv, dw) = full_720p(True)
+    rng = np.random.default_rng(3)
+    for (b, h) in [(0, 0), (1, 39)]:
+        blocks = sorted({0, wl.n_qb - 1, *rng.choice(wl.n_qb, 3, replace=False).tolist()})
+        ref = ob.dq_blocks(to_np(q[b, h]), to_np(k[b, h]), to_np(v[b, h]), to_np(w), mask[b, h].cpu().numpy(),
+                           to_np(dy[b, h]), wl.blk_q, wl.blk_k, blocks)
+        for I in blocks:
+            r0, r1 = I * wl.blk_q, min(wl.N, (I + 1) * wl.blk_q)
+            close(f"b{b} h{h} dq block {I}", to_np(dq[b, h, r0:r1]), ref[I])
+    assert torch.isfinite(dk).all() and torch.isfinite(dv).all() and torch.isfinite(dw).all()
+
+
+def test_backward_full_size_720p_softmax_invariants():
+    wl, q, k, v, w, dy, mask, (dq, dk, dv, dw) = full_720p(False)
+    for (b, h) in [(0, 0), (0, 17), (1, 39)]:
+        sk = to_np(dk[b, h]).sum(axis=0)
+        scale = np.abs(to_np(dk[b, h])).sum(axis=0).max()
+        say(f"  b{b} h{h}: |sum dK| / sum |dK| = {np.abs(sk).max() / scale:.2e}")
+        assert np.abs(sk).max() <= 1e-4 * scale
+        sv, sy = to_np(dv[b, h]).sum(axis=0), to_np(dy[b, h]).sum(axis=0)
+        close(f"b{b} h{h} sum dV vs sum dY", sv, sy)

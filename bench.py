@@ -203,6 +203,61 @@ def main_w8a8(args, name):
     print(json.dumps(result), flush=True)
 
 
+def main_backward(args):
+    """The SLA backward for the forward's own selection on the 720P pair: a step is one sagesla_backward."""
+    import torch
+    import int8_block_sparse_amd as sg
+    import synth
+
+    if not torch.cuda.is_available():
+        sys.exit("bench.py needs a GPU")
+    sg.load()
+    dev = torch.device("cuda:0")
+    wl = synth.workload(WORKLOAD)
+    log(f"generating {wl.name} inputs on the GPU")
+    q, k, v, w = synth.make(wl, 0, device=dev)
+    _, ex = sg.forward(q, k, v, w, topk=wl.topk, export=True)
+    mask = ex["block_idx"][..., :wl.topk].contiguous()
+    del ex
+    dy = torch.randn(q.shape, device=dev, generator=torch.Generator(device=dev).manual_seed(1)).to(torch.bfloat16)
+    cfg = sg.Config(wl.B, wl.H, wl.N, wl.D, wl.blk_q, wl.blk_k, wl.topk, wl.linear)
+    import ctypes
+    ws = torch.empty(sg.load().sagesla_backward_workspace_bytes(ctypes.byref(cfg.params(w_proj=w.data_ptr()))),
+                     dtype=torch.uint8, device=dev)
+    step = lambda: sg.backward(q, k, v, w, dy, mask, topk=wl.topk, workspace=ws)
+    for _ in range(args.warmup):
+        step()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev[0].record()
+    for _ in range(args.steps):
+        step()
+    ev[1].record()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    ms_ev = ev[0].elapsed_time(ev[1]) / args.steps
+    log(f"{ms:.3f} ms per backward (events {ms_ev:.3f})")
+    # algorithmic bf16 work of the sparse branch: S, dP, dV, dK, dQ per selected block pair (2 bq bk D each)
+    pairs = wl.B * wl.H * wl.n_qb * wl.topk
+    flops = pairs * 5 * 2.0 * wl.blk_q * wl.blk_k * wl.D
+    tflops = flops / (ms * 1e-3) / 1e12
+    result = {
+        "metric": "SLA backward ms/layer (fixed selection), sparse-branch bf16 TFLOP/s",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s (5 products of 2*bq*bk*D per selected block pair)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16+f32", "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "N": wl.N, "D": wl.D, "blk_q": wl.blk_q,
+                   "blk_k": wl.blk_k, "topk": wl.topk, "linear": wl.linear, "parallelism": "single GPU"},
+        "roofline": {"kernel": "sagesla_backward (all kernels)", "bound": "mfma", "achieved": round(tflops, 1),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s (bf16)", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "avg_launch_ms": round(ms_ev, 4), "flops_per_step": flops},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -212,7 +267,8 @@ def main():
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (HBM-counter calibration under rocprofv3)")
     ap.add_argument("--workload", default="sagesla",
-                    help="sagesla (the headline attention layer) or w8a8-<shape> (the W8A8 linear layer)")
+                    help="sagesla (the headline attention layer), sla-backward (its backward for the forward's "
+                         "selection) or w8a8-<shape> (the W8A8 linear layer)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the forward shards by "
@@ -221,6 +277,8 @@ def main():
         sys.exit(2)
     if args.workload.startswith("w8a8-"):
         return main_w8a8(args, args.workload[len("w8a8-"):])
+    if args.workload == "sla-backward":
+        return main_backward(args)
     if args.workload != "sagesla":
         sys.exit(f"unknown workload {args.workload}")
 

@@ -8,8 +8,8 @@
 //
 // Sparse branch (bf16 MFMA, fp32 accumulation; P and dS enter the products as bf16 hi + lo pairs):
 //   kb_sel     bitmap [BH][n_kb][ceil(n_qb/32)]: bit I of key block J = J is selected by query block I
-//   kb_q       per query block: pass 1 the log-sum-exp of every row (base 2), pass 2 D_i = sum_j P_ij dP_ij,
-//              pass 3 dS = P (dP - D) and dQ = dS K sm_scale; writes LSE, D and dQ
+//   kb_q       per query block: pass 1 the log-sum-exp of every row (base 2) and D_i = sum_j P_ij dP_ij, both
+//              online; pass 2 dS = P (dP - D) and dQ = dS K sm_scale; writes LSE, D and dQ
 //   kb_kv      per key block, over the query blocks that selected it: dV = P^T dY, dK = dS^T Q sm_scale
 // Linear branch (fp32 VALU tiles), after the forward's remaining-state product (H_m, Z_m per query block):
 //   kb_lin_q   per query block: O_l, dO_l = dY W_p^T, dnum = dO_l / den, dden = -(dO_l . O_l) / den,
@@ -146,14 +146,16 @@ __global__ __launch_bounds__(256) void kb_q(const uint16_t* __restrict__ q, cons
   };
   __syncthreads();
 
-  // pass 1: m (max of s * c2) and l (sum of 2^(s c2 - m)) per row, online
-  float m = -INFINITY, lsum = 0.f;
+  // pass 1, online per row: m = max of s * c2, l = sum of 2^(s c2 - m) and u = sum of 2^(s c2 - m) dP, both rescaled
+  // when m grows; then LSE = m + log2(l) and D = u / l = sum_j P_ij dP_ij
+  float m = -INFINITY, lsum = 0.f, usum = 0.f;
   for (int t = 0; t < topk; ++t) {
     const int J = min(max(row[t], 0), n_kb - 1);
     if (listed_before(t, J)) continue;
-    const int nv = load_kv(J, false, false);
-    v16f st[2];
+    const int nv = load_kv(J, true, false);
+    v16f st[2], dp[2];
     scores(st);
+    dpt(dp);
     if (!wave_live) continue;
     float bm = -INFINITY;
 #pragma unroll
@@ -163,41 +165,31 @@ __global__ __launch_bounds__(256) void kb_q(const uint16_t* __restrict__ q, cons
         if (32 * tt + acc_row(r) < nv) bm = fmaxf(bm, st[tt][r] * c2);
     bm = fmaxf(bm, __shfl_xor(bm, 32));
     const float mn = fmaxf(m, bm);
-    float ps = 0.f;
+    float ps = 0.f, pu = 0.f;
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        if (32 * tt + acc_row(r) < nv) ps += __builtin_amdgcn_exp2f(st[tt][r] * c2 - mn);
+        if (32 * tt + acc_row(r) < nv) {
+          const float e = __builtin_amdgcn_exp2f(st[tt][r] * c2 - mn);
+          ps += e;
+          pu = fmaf(e, dp[tt][r], pu);
+        }
     ps += __shfl_xor(ps, 32);
-    lsum = (m == -INFINITY ? 0.f : lsum * __builtin_amdgcn_exp2f(m - mn)) + ps;
+    pu += __shfl_xor(pu, 32);
+    const float sc = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mn);
+    lsum = lsum * sc + ps;
+    usum = usum * sc + pu;
     m = mn;
   }
   const float lse = (lsum > 0.f) ? m + __log2f(lsum) : 0.f;  // no selected key: every P is 0 below
-
-  // pass 2: D_i = sum_j P_ij dP_ij
-  float dsum = 0.f;
-  for (int t = 0; t < topk; ++t) {
-    const int J = min(max(row[t], 0), n_kb - 1);
-    if (listed_before(t, J)) continue;
-    const int nv = load_kv(J, true, false);
-    v16f st[2], dp[2];
-    scores(st);
-    dpt(dp);
-    if (!wave_live) continue;
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (32 * tt + acc_row(r) < nv) dsum += __builtin_amdgcn_exp2f(st[tt][r] * c2 - lse) * dp[tt][r];
-  }
-  dsum += __shfl_xor(dsum, 32);
+  const float dsum = (lsum > 0.f) ? usum / lsum : 0.f;
   if (wave_live && l < 32 && i_loc < nq) {
     lse_out[(size_t)bh * N + r0 + i_loc] = lse;
     d_out[(size_t)bh * N + r0 + i_loc] = dsum;
   }
 
-  // pass 3: dS = P (dP - D) into LDS (rows i, keys j) as hi + lo, then dQ^T tiles += K^T-rows . dS-rows
+  // pass 2: dS = P (dP - D) into LDS (rows i, keys j) as hi + lo, then dQ^T tiles += K^T-rows . dS-rows
   v16f acc[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) acc[u] = (v16f){};
@@ -250,11 +242,13 @@ __global__ __launch_bounds__(256) void kb_q(const uint16_t* __restrict__ q, cons
 }
 
 // ---------------------------------------------------------------------------------------------------------
-// kb_kv: grid (n_kb, BH), 128 threads (2 waves x 32 keys). For every query block I that selected J (bitmap), in
-// halves of 64 rows: S = Q K^T and dP = dY V^T tiles with the keys as columns (lane = key), P and dS written
-// transposed (rows = keys) to LDS as hi + lo, then dV^T += dY^T-rows . P^T-rows and dK^T += Q^T-rows . dS^T-rows.
+// kb_kv: grid (n_kb, BH), 256 threads: wave w takes keys 32 (w % 2) .. +31 and rows 32 (w / 2) .. +31 of each
+// 64-row half of a query block. For every query block I that selected J (bitmap): S = Q K^T and dP = dY V^T
+// tiles with the keys as columns (lane = key), P and dS written transposed (rows = keys) to LDS as hi + lo, then
+// dV^T += dY^T-rows . P^T-rows and dK^T += Q^T-rows . dS^T-rows over the wave's 32 rows. The two waves of a key
+// tile then hold partial sums over complementary rows, added in a fixed order at the end.
 // ---------------------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(128) void kb_kv(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+__global__ __launch_bounds__(256) void kb_kv(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                              const uint16_t* __restrict__ v, const uint16_t* __restrict__ dy,
                                              const uint32_t* __restrict__ bits, const float* __restrict__ lse_in,
                                              const float* __restrict__ d_in, float* __restrict__ dk,
@@ -275,13 +269,14 @@ __global__ __launch_bounds__(128) void kb_kv(const uint16_t* __restrict__ q, con
   float* sDd = sL + 64;                    // [64] D of the rows
   const int J = blockIdx.x, bh = blockIdx.y;
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63, lr = l & 31;
+  const int kt = w & 1, ch = w >> 1;  // key tile, row chunk
   const int nk = min(64, N - J * 64);
   const uint16_t* qh = q + (size_t)bh * N * kD;
   const uint16_t* dyh = dy + (size_t)bh * N * kD;
-  load_rows<128>(k + (size_t)bh * N * kD, J * 64, 64, nk, sK, kLd128);
-  load_rows<128>(v + (size_t)bh * N * kD, J * 64, 64, nk, sV, kLd128);
+  load_rows<256>(k + (size_t)bh * N * kD, J * 64, 64, nk, sK, kLd128);
+  load_rows<256>(v + (size_t)bh * N * kD, J * 64, 64, nk, sV, kLd128);
   const float c2 = sm_scale * kLog2e;
-  const int j_loc = 32 * w + lr;
+  const int j_loc = 32 * kt + lr;
   v16f accv[4], acck[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) accv[u] = acck[u] = (v16f){};
@@ -295,61 +290,78 @@ __global__ __launch_bounds__(128) void kb_kv(const uint16_t* __restrict__ q, con
       for (int h0 = 0; h0 < nq; h0 += 64) {
         const int nh = min(64, nq - h0);
         __syncthreads();  // the previous half's tiles are no longer read
-        load_rows<128>(qh, q0 + h0, 64, nh, sQ, kLd128);
-        load_rows<128>(dyh, q0 + h0, 64, nh, sdY, kLd128);
-        load_rows_t<128>(qh, q0 + h0, 64, nh, sQt, kLd64);
-        load_rows_t<128>(dyh, q0 + h0, 64, nh, sdYt, kLd64);
+        load_rows<256>(qh, q0 + h0, 64, nh, sQ, kLd128);
+        load_rows<256>(dyh, q0 + h0, 64, nh, sdY, kLd128);
+        load_rows_t<256>(qh, q0 + h0, 64, nh, sQt, kLd64);
+        load_rows_t<256>(dyh, q0 + h0, 64, nh, sdYt, kLd64);
         if (threadIdx.x < 64) {
           const int ii = threadIdx.x;
           sL[ii] = ii < nh ? lse_in[(size_t)bh * N + q0 + h0 + ii] : 0.f;
           sDd[ii] = ii < nh ? d_in[(size_t)bh * N + q0 + h0 + ii] : 0.f;
         }
         __syncthreads();
+        const v16f s = mma_nt(sQ + 32 * ch * kLd128, kLd128, sK + 32 * kt * kLd128, kLd128, kD, (v16f){});
+        const v16f dp = mma_nt(sdY + 32 * ch * kLd128, kLd128, sV + 32 * kt * kLd128, kLd128, kD, (v16f){});
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {  // 32-row chunks of the half
-          const v16f s = mma_nt(sQ + 32 * c * kLd128, kLd128, sK + 32 * w * kLd128, kLd128, kD, (v16f){});
-          const v16f dp = mma_nt(sdY + 32 * c * kLd128, kLd128, sV + 32 * w * kLd128, kLd128, kD, (v16f){});
-#pragma unroll
-          for (int r = 0; r < 16; r += 4) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int ii = 32 * c + acc_row(r + e);
-              const bool ok = ii < nh;
-              const float p = ok ? __builtin_amdgcn_exp2f(s[r + e] * c2 - sL[ii]) : 0.f;
-              const float ds = p * (dp[r + e] - sDd[ii]);
-              const float ph = from_bf16(to_bf16(p)), dh = from_bf16(to_bf16(ds));
-              sPh[j_loc * kLd64 + ii] = to_bf16(ph);
-              sPl[j_loc * kLd64 + ii] = to_bf16(p - ph);
-              sDh[j_loc * kLd64 + ii] = to_bf16(dh);
-              sDl[j_loc * kLd64 + ii] = to_bf16(ds - dh);
-            }
-          }
+        for (int r = 0; r < 16; ++r) {
+          const int ii = 32 * ch + acc_row(r);
+          const bool ok = ii < nh;
+          const float p = ok ? __builtin_amdgcn_exp2f(s[r] * c2 - sL[ii]) : 0.f;
+          const float ds = p * (dp[r] - sDd[ii]);
+          const float ph = from_bf16(to_bf16(p)), dh = from_bf16(to_bf16(ds));
+          sPh[j_loc * kLd64 + ii] = to_bf16(ph);
+          sPl[j_loc * kLd64 + ii] = to_bf16(p - ph);
+          sDh[j_loc * kLd64 + ii] = to_bf16(dh);
+          sDl[j_loc * kLd64 + ii] = to_bf16(ds - dh);
         }
-        // each wave reads back only its own 32 key rows of P^T and dS^T
+        // each wave reads back only the P^T / dS^T entries it wrote (its keys, its 32 rows)
         __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
         __builtin_amdgcn_wave_barrier();
+        const int i0 = 32 * ch;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          accv[u] = mma_nt(sdYt + 32 * u * kLd64, kLd64, sPh + 32 * w * kLd64, kLd64, 64, accv[u]);
-          accv[u] = mma_nt(sdYt + 32 * u * kLd64, kLd64, sPl + 32 * w * kLd64, kLd64, 64, accv[u]);
-          acck[u] = mma_nt(sQt + 32 * u * kLd64, kLd64, sDh + 32 * w * kLd64, kLd64, 64, acck[u]);
-          acck[u] = mma_nt(sQt + 32 * u * kLd64, kLd64, sDl + 32 * w * kLd64, kLd64, 64, acck[u]);
+          accv[u] = mma_nt(sdYt + 32 * u * kLd64 + i0, kLd64, sPh + 32 * kt * kLd64 + i0, kLd64, 32, accv[u]);
+          accv[u] = mma_nt(sdYt + 32 * u * kLd64 + i0, kLd64, sPl + 32 * kt * kLd64 + i0, kLd64, 32, accv[u]);
+          acck[u] = mma_nt(sQt + 32 * u * kLd64 + i0, kLd64, sDh + 32 * kt * kLd64 + i0, kLd64, 32, acck[u]);
+          acck[u] = mma_nt(sQt + 32 * u * kLd64 + i0, kLd64, sDl + 32 * kt * kLd64 + i0, kLd64, 32, acck[u]);
         }
       }
     }
   }
-  // acc[u][r] = X^T[d = 32 u + acc_row(r)][key j_loc]
-  if (j_loc < nk) {
-    float* dvr = dv + ((size_t)bh * N + J * 64 + j_loc) * kD;
-    float* dkr = dk + ((size_t)bh * N + J * 64 + j_loc) * kD;
+  // acc[u][r] = partial X^T[d = 32 u + acc_row(r)][key j_loc] over the rows of chunk ch: chunk 1 hands its sums
+  // to chunk 0 through LDS (the row tiles are free now), which adds them (chunk 0 first) and stores
+  __syncthreads();
+  float* sX = (float*)smem;  // [2 key tiles][2 (dV, dK)][4 u][16 r][64 lanes]
+  if (ch == 1) {
 #pragma unroll
     for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int r = 0; r < 16; r += 4) {
-        *(float4*)(dvr + 32 * u + acc_row(r)) = make_float4(accv[u][r], accv[u][r + 1], accv[u][r + 2], accv[u][r + 3]);
-        *(float4*)(dkr + 32 * u + acc_row(r)) = make_float4(acck[u][r] * sm_scale, acck[u][r + 1] * sm_scale,
-                                                            acck[u][r + 2] * sm_scale, acck[u][r + 3] * sm_scale);
+      for (int r = 0; r < 16; ++r) {
+        sX[(((kt * 2 + 0) * 4 + u) * 16 + r) * 64 + l] = accv[u][r];
+        sX[(((kt * 2 + 1) * 4 + u) * 16 + r) * 64 + l] = acck[u][r];
       }
+  }
+  __syncthreads();
+  if (ch == 0) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        accv[u][r] += sX[(((kt * 2 + 0) * 4 + u) * 16 + r) * 64 + l];
+        acck[u][r] += sX[(((kt * 2 + 1) * 4 + u) * 16 + r) * 64 + l];
+      }
+    if (j_loc < nk) {
+      float* dvr = dv + ((size_t)bh * N + J * 64 + j_loc) * kD;
+      float* dkr = dk + ((size_t)bh * N + J * 64 + j_loc) * kD;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int r = 0; r < 16; r += 4) {
+          *(float4*)(dvr + 32 * u + acc_row(r)) = make_float4(accv[u][r], accv[u][r + 1], accv[u][r + 2], accv[u][r + 3]);
+          *(float4*)(dkr + 32 * u + acc_row(r)) = make_float4(acck[u][r] * sm_scale, acck[u][r + 1] * sm_scale,
+                                                              acck[u][r + 2] * sm_scale, acck[u][r + 3] * sm_scale);
+        }
+    }
   }
 }
 
@@ -667,7 +679,7 @@ hipError_t launch_backward_sparse(const BwdPlan& b, hipStream_t s) {
   hipLaunchKernelGGL(kb_q, dim3(p.n_qb, p.BH), dim3(256), kbq_lds_bytes(), s, b.q, b.k, b.v, b.dy, p.block_idx,
                      b.lse, b.dd, b.dq, p.N, p.n_qb, p.n_kb, p.topk, p.blk_q, p.sm_scale);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(kb_kv, dim3(p.n_kb, p.BH), dim3(128), kbkv_lds_bytes(), s, b.q, b.k, b.v, b.dy, b.sel_bits,
+  hipLaunchKernelGGL(kb_kv, dim3(p.n_kb, p.BH), dim3(256), kbkv_lds_bytes(), s, b.q, b.k, b.v, b.dy, b.sel_bits,
                      b.lse, b.dd, b.dk, b.dv, p.N, p.n_qb, p.n_kb, n_qbw, p.blk_q, p.sm_scale);
   return hipGetLastError();
 }

@@ -340,6 +340,7 @@ size_t plan_backward(const Plan& pl, unsigned char* ws, BwdPlan* b) {
   b->lse = (float*)take(BH * N * sizeof(float));
   b->dd = (float*)take(BH * N * sizeof(float));
   b->sel_bits = (uint32_t*)take(BH * pl.n_kb * (size_t)((pl.n_qb + 31) / 32) * sizeof(uint32_t));
+  b->sel_bits_q = (uint32_t*)take(BH * pl.n_qb * (size_t)((pl.n_kb + 31) / 32) * sizeof(uint32_t));
   if (lin_active) {
     b->o_l = (float*)take(BH * N * kD * sizeof(float));
     b->dhm = (float*)take(BH * pl.n_qb * (size_t)kStateX * sizeof(float));

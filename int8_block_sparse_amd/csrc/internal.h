@@ -72,7 +72,8 @@ struct BwdPlan {
   float *dq, *dk, *dv, *dw;        // outputs: fp32 [BH][N][D], dW_p fp32 [D][D]
   float* lse;                      // [BH][N] base-2 log-sum-exp of each row's selected scores
   float* dd;                       // [BH][N] D_i = sum_j P_ij dP_ij
-  uint32_t* sel_bits;              // [BH][n_kb][ceil(n_qb/32)]
+  uint32_t* sel_bits;              // [BH][n_kb][ceil(n_qb/32)]: bit I of key block J = I selected J
+  uint32_t* sel_bits_q;            // [BH][n_qb][ceil(n_kb/32)]: bit J of query block I = I selected J
   float* o_l;                      // [BH][N][D] linear-branch output before W_p
   float* dhm;                      // [BH][n_qb][kStateX] per query block dH_m (c-major) then dZ_m
   float* dhj;                      // [BH][n_kb][kStateX] per key block dH_J then dZ_J

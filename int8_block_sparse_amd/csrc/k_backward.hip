@@ -27,160 +27,223 @@ namespace sagesla {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kLd128 = kD + 8;  // LDS row stride (bf16 elements) of 128-wide rows: 272 B, conflict-free reads
-constexpr int kLd64 = 64 + 8;   // of 64-wide rows: 144 B
 
-// acc[32x32] += A[32 rows][K] . B[32 rows][K]^T with A, B bf16 row-major in LDS (row strides lda, ldb elements).
-// Result layout: lane l holds column l % 32 (a row of B) and rows 8 (r/4) + 4 (l/32) + r%4 (rows of A).
-__device__ __forceinline__ v16f mma_nt(const __bf16* A, int lda, const __bf16* B, int ldb, int K, v16f c) {
-  const int l = threadIdx.x & 63, r = l & 31, g = l >> 5;
-  for (int k0 = 0; k0 < K; k0 += 16) {
-    const v8bf a = *(const v8bf*)(A + r * lda + k0 + 8 * g);
-    const v8bf b = *(const v8bf*)(B + r * ldb + k0 + 8 * g);
-    c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-  }
-  return c;
-}
-
+// accumulator row of register r of a 32x32 MFMA tile (lane l holds column l % 32)
 __device__ __forceinline__ int acc_row(int r) { return 8 * (r >> 2) + 4 * ((threadIdx.x & 63) >> 5) + (r & 3); }
 
-__device__ __forceinline__ __bf16 to_bf16(float x) { return __builtin_bit_cast(__bf16, (uint16_t)(pack_bf16x2(x, 0.f) & 0xffffu)); }
-__device__ __forceinline__ float from_bf16(__bf16 x) { return __uint_as_float((uint32_t)__builtin_bit_cast(uint16_t, x) << 16); }
+typedef __attribute__((address_space(3))) void bw_lds_void;
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef short v8s __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) v4s lds_v4s;
 
-// rows [r0, r0 + nrows) of a [N][128] bf16 head into LDS rows of stride ld (rows past nvalid are zero); 256 threads
-template <int NT>
-__device__ __forceinline__ void load_rows(const uint16_t* __restrict__ src, int r0, int nrows, int nvalid,
-                                          __bf16* dst, int ld) {
-  for (int u = threadIdx.x; u < nrows * 16; u += NT) {
-    const int rr = u >> 4, c8 = (u & 15) * 8;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (rr < nvalid) v = *(const uint4*)(src + (size_t)(r0 + rr) * kD + c8);
-    *(uint4*)(dst + rr * ld + c8) = v;
-  }
+constexpr int kTileBytes = 64 * 256;  // a swizzled tile: 64 rows of 128 bf16
+
+// Swizzled tiles hold 64 rows of 256 B; the 16-byte chunk c of row r sits at chunk position c ^ tswz(r). Sixteen
+// consecutive rows at one chunk fall on sixteen distinct positions (the row reads of an MFMA operand), and four
+// rows from a multiple of 4 over four aligned chunks fall on sixteen distinct positions (transposing reads).
+__device__ __forceinline__ int tswz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+// byte offset of the 8-byte unit that holds columns col .. col + 3 (col a multiple of 4) of row r
+__device__ __forceinline__ int toff(int r, int col) { return r * 256 + (((col >> 3) ^ tswz(r)) << 4) + ((col & 4) << 1); }
+
+// operand of a 32x32x16 MFMA from a swizzled tile: row r0 + l % 32, columns k0 + 8 (l / 32) .. + 7 (l = lane)
+__device__ __forceinline__ v8bf row_op(const unsigned char* t, int r0, int k0, int l) {
+  return *(const v8bf*)(t + toff(r0 + (l & 31), k0 + 8 * (l >> 5)));
 }
 
-// the same rows transposed: dst[c][rr] (row stride ld), c < 128
-template <int NT>
-__device__ __forceinline__ void load_rows_t(const uint16_t* __restrict__ src, int r0, int nrows, int nvalid,
-                                            __bf16* dst, int ld) {
-  for (int u = threadIdx.x; u < nrows * 16; u += NT) {
-    const int rr = u >> 4, c8 = (u & 15) * 8;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (rr < nvalid) v = *(const uint4*)(src + (size_t)(r0 + rr) * kD + c8);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+// Transposed operand: the MFMA row is tile column m0 + l % 32, and contraction slot s (0..7) of lane half g is tile
+// row i0 + 8 (s / 4) + 4 g + s % 4, the order in which an accumulator tile holds its rows, so that a tile of
+// results serves as the other operand where it stands. Two transposing reads: within each group of 16 lanes,
+// lane i receives element i % 4 of the 8-byte units addressed by lanes 4 c + i / 4, c = 0..3.
+__device__ __forceinline__ v8bf tr_op(const unsigned char* t, int i0, int m0, int l) {
+  const int j = l & 15;
+  const int r = i0 + 4 * (l >> 5) + (j >> 2);
+  const int col = m0 + 16 * ((l >> 4) & 1) + 4 * (j & 3);
+  const v4s a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(t + toff(r, col)));
+  const v4s b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(t + toff(r + 8, col)));
+  const v8s ab = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return __builtin_bit_cast(v8bf, ab);
+}
+
+// accumulator rows 8 s .. 8 s + 7 of a lane as bf16 hi and lo operands (hi = bf16(x), lo = bf16(x - hi))
+__device__ __forceinline__ void split8(const v16f& x, int s, v8bf& hi, v8bf& lo) {
+  uint32_t h[4], o[4];
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      dst[(c8 + e) * ld + rr] = __builtin_bit_cast(__bf16, (uint16_t)((e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xffffu)));
+  for (int e = 0; e < 4; ++e) {
+    const float a = x[8 * s + 2 * e], b = x[8 * s + 2 * e + 1];
+    h[e] = pack_bf16x2(a, b);
+    o[e] = pack_bf16x2(a - __uint_as_float(h[e] << 16), b - __uint_as_float(h[e] & 0xffff0000u));
   }
+  hi = __builtin_bit_cast(v8bf, make_uint4(h[0], h[1], h[2], h[3]));
+  lo = __builtin_bit_cast(v8bf, make_uint4(o[0], o[1], o[2], o[3]));
+}
+
+__device__ __forceinline__ v16f mfma(v8bf a, v8bf b, v16f c) { return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0); }
+
+// Wait for this wave's direct-to-LDS loads and LDS accesses, then meet the other waves: the tiles the workgroup
+// staged before are complete once every wave passes. The empty asm statements keep LDS accesses on their side.
+__device__ __forceinline__ void dma_sync() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(7 << 4);  // vmcnt(0), lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Direct-to-LDS staging of one 64-row tile of a [rows][128] bf16 matrix: wave w issues four loads of 1 KB (tile
+// rows 16 e + 4 w .. + 3); lane l fills row 16 e + 4 w + l / 16 at chunk position l % 16 with the chunk
+// (l % 16) ^ tswz(row). Tile rows at or past nvalid re-read the last valid row (finite values that the kernels
+// weight by zero), so no load leaves the matrix.
+struct TileLoader {
+  int row[4];
+  uint32_t chunk[4];
+  __device__ __forceinline__ TileLoader() {
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      row[e] = 16 * e + 4 * w + (l >> 4);
+      chunk[e] = (uint32_t)(16 * ((l & 15) ^ tswz(row[e])));
+    }
+  }
+  __device__ __forceinline__ void operator()(__amdgpu_buffer_rsrc_t src, int row0, int nvalid, unsigned char* tile) const {
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t off = (uint32_t)(row0 + min(row[e], nvalid - 1)) * 256u + chunk[e];
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (bw_lds_void*)(tile + (4 * e + w) * 1024), 16, off, 0, 0, 0);
+    }
+  }
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const uint16_t* base, int N) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), (short)0, N * kD * 2, 0x00020000);
 }
 
 }  // namespace
 
 // ---------------------------------------------------------------------------------------------------------
-// kb_sel: grid (n_qb, BH), 64 threads. Sets bit I of word [bh][J][I / 32] for every listed J (atomic OR: the
-// result does not depend on the order).
+// kb_sel: grid (n_qb, BH), 64 threads. Sets bit I of word [bh][J][I / 32] and bit J of word [bh][I][J / 32] for
+// every listed J (atomic OR: the result does not depend on the order; a block listed twice sets its bits once).
 // ---------------------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(64) void kb_sel(const int32_t* __restrict__ idx, uint32_t* __restrict__ bits, int n_qb,
-                                             int n_kb, int topk, int n_qbw) {
+__global__ __launch_bounds__(64) void kb_sel(const int32_t* __restrict__ idx, uint32_t* __restrict__ bits,
+                                             uint32_t* __restrict__ bits_q, int n_qb, int n_kb, int topk, int n_qbw,
+                                             int n_kbw) {
   const int I = blockIdx.x, bh = blockIdx.y;
   const int32_t* row = idx + ((size_t)bh * n_qb + I) * topk;
   for (int t = threadIdx.x; t < topk; t += 64) {
     const int J = min(max(row[t], 0), n_kb - 1);
     atomicOr(&bits[((size_t)bh * n_kb + J) * n_qbw + (I >> 5)], 1u << (I & 31));
+    atomicOr(&bits_q[((size_t)bh * n_qb + I) * n_kbw + (J >> 5)], 1u << (J & 31));
   }
 }
 
 // ---------------------------------------------------------------------------------------------------------
-// kb_q: grid (n_qb, BH), 256 threads (4 waves x 32 query rows). Scores are computed transposed, S^T = K Q^T, so
-// each lane owns one query row: row maxima and sums are in-lane plus the partner lane l ^ 32.
+// kb_q: grid (n_qb, BH), 256 threads (4 waves x 32 query rows), two workgroups per CU. Scores are computed
+// transposed, S^T = K Q^T, so each lane owns one query row (with its partner lane l ^ 32); the wave's Q and dY
+// rows stay in registers as the B operands. The selected key blocks (ascending, each once, from the bitmap)
+// stream through a two-slot ring of swizzled K and V tiles filled by direct-to-LDS loads one block ahead.
 // ---------------------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void kb_q(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-                                            const uint16_t* __restrict__ v, const uint16_t* __restrict__ dy,
-                                            const int32_t* __restrict__ idx, float* __restrict__ lse_out,
-                                            float* __restrict__ d_out, float* __restrict__ dq, int N, int n_qb,
-                                            int n_kb, int topk, int blk_q, float sm_scale) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  __bf16* sQ = (__bf16*)smem;             // [128][kLd128]
-  __bf16* sdY = sQ + 128 * kLd128;        // [128][kLd128]
-  __bf16* sK = sdY + 128 * kLd128;        // [64][kLd128]
-  __bf16* sV = sK + 64 * kLd128;          // [64][kLd128]
-  __bf16* sKt = sV + 64 * kLd128;         // [128][kLd64]   K_J^T
-  __bf16* sSh = sKt + 128 * kLd64;        // [128][kLd64]   dS hi
-  __bf16* sSl = sSh + 128 * kLd64;        // [128][kLd64]   dS lo
+__global__ __launch_bounds__(256, 2) void kb_q(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                                               const uint16_t* __restrict__ v, const uint16_t* __restrict__ dy,
+                                               const uint32_t* __restrict__ bits_q, float* __restrict__ lse_out,
+                                               float* __restrict__ d_out, float* __restrict__ dq, int N, int n_qb,
+                                               int n_kbw, int blk_q, float sm_scale) {
+  extern __shared__ __align__(1024) unsigned char smem[];  // [slot][K tile, V tile]
   const int I = blockIdx.x, bh = blockIdx.y;
-  const int w = threadIdx.x >> 6, l = threadIdx.x & 63, lr = l & 31;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = threadIdx.x & 63, g = l >> 5;
   const int r0 = I * blk_q, nq = min(blk_q, N - r0);
-  const uint16_t* qh = q + (size_t)bh * N * kD;
-  const uint16_t* kh = k + (size_t)bh * N * kD;
-  const uint16_t* vh = v + (size_t)bh * N * kD;
-  const uint16_t* dyh = dy + (size_t)bh * N * kD;
-  const int32_t* row = idx + ((size_t)bh * n_qb + I) * topk;
-  load_rows<256>(qh, r0, 128, min(nq, 128), sQ, kLd128);
-  load_rows<256>(dyh, r0, 128, min(nq, 128), sdY, kLd128);
-  const bool wave_live = 32 * w < nq;  // the wave's rows exist (blk_q 64: waves 2, 3 idle but still sync)
+  const bool wave_live = 32 * w < nq;  // blk_q 64: waves 2, 3 hold no rows but still stage and meet
+  const int i_loc = 32 * w + (l & 31);
   const float c2 = sm_scale * kLog2e;
-  const int i_loc = 32 * w + lr;  // this lane's query row in the block
-  // a key block appears once even if listed twice
-  auto listed_before = [&](int t, int J) {
-    for (int u = 0; u < t; ++u)
-      if (min(max(row[u], 0), n_kb - 1) == J) return true;
-    return false;
+  v8bf qb[8], yb[8];
+  {
+    const bool iv = i_loc < nq;
+    const uint16_t* qr = q + ((size_t)bh * N + r0 + (iv ? i_loc : 0)) * kD + 8 * g;
+    const uint16_t* yr = dy + ((size_t)bh * N + r0 + (iv ? i_loc : 0)) * kD + 8 * g;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      qb[s] = iv ? *(const v8bf*)(qr + 16 * s) : (v8bf){};
+      yb[s] = iv ? *(const v8bf*)(yr + 16 * s) : (v8bf){};
+    }
+  }
+  const __amdgpu_buffer_rsrc_t rk = head_rsrc(k + (size_t)bh * N * kD, N);
+  const __amdgpu_buffer_rsrc_t rv = head_rsrc(v + (size_t)bh * N * kD, N);
+  const TileLoader load;
+  const uint32_t* sb = bits_q + ((size_t)bh * n_qb + I) * n_kbw;
+  // the selected blocks in ascending order: a cursor over the bitmap words (uniform across the workgroup)
+  auto next_block = [&](int& wi, uint32_t& cw) -> int {
+    while (cw == 0) {
+      if (++wi >= n_kbw) return -1;
+      cw = sb[wi];
+    }
+    const int J = 32 * wi + __builtin_ctz(cw);
+    cw &= cw - 1;
+    return J;
   };
-  auto load_kv = [&](int J, bool with_v, bool with_kt) {
-    __syncthreads();  // the previous block's tiles are no longer read
+  auto stage = [&](int J, int slot) {
+    unsigned char* t = smem + slot * 2 * kTileBytes;
     const int nv = min(64, N - J * 64);
-    load_rows<256>(kh, J * 64, 64, nv, sK, kLd128);
-    if (with_v) load_rows<256>(vh, J * 64, 64, nv, sV, kLd128);
-    if (with_kt) load_rows_t<256>(kh, J * 64, 64, nv, sKt, kLd64);
-    __syncthreads();
-    return nv;
+    load(rk, J * 64, nv, t);
+    load(rv, J * 64, nv, t + kTileBytes);
   };
-  // S^T (and dP^T) tiles of this wave: st[t] holds keys 32 t + acc_row(r) of query i_loc
-  auto scores = [&](v16f (&st)[2]) {
+  // S^T and dP^T of one 32-key tile tt of the block in slot `t`
+  // (lx: the lane index through an opaque copy per block, so that tile addresses are recomputed where used)
+  auto tile_sdp = [&](const unsigned char* t, int tt, int lx, v16f& st, v16f& dp) {
+    st = (v16f){};
+    dp = (v16f){};
 #pragma unroll
-    for (int t = 0; t < 2; ++t) st[t] = mma_nt(sK + 32 * t * kLd128, kLd128, sQ + 32 * w * kLd128, kLd128, kD, (v16f){});
+    for (int s = 0; s < 8; ++s) {
+      st = mfma(row_op(t, 32 * tt, 16 * s, lx), qb[s], st);
+      dp = mfma(row_op(t + kTileBytes, 32 * tt, 16 * s, lx), yb[s], dp);
+    }
   };
-  auto dpt = [&](v16f (&dp)[2]) {
-#pragma unroll
-    for (int t = 0; t < 2; ++t) dp[t] = mma_nt(sV + 32 * t * kLd128, kLd128, sdY + 32 * w * kLd128, kLd128, kD, (v16f){});
-  };
-  __syncthreads();
 
-  // pass 1, online per row: m = max of s * c2, l = sum of 2^(s c2 - m) and u = sum of 2^(s c2 - m) dP, both rescaled
-  // when m grows; then LSE = m + log2(l) and D = u / l = sum_j P_ij dP_ij
+  // pass 1, online per row: m = max of s * c2, l = sum of 2^(s c2 - m) and u = sum of 2^(s c2 - m) dP, both
+  // rescaled when m grows; then LSE = m + log2(l) and D = u / l = sum_j P_ij dP_ij
   float m = -INFINITY, lsum = 0.f, usum = 0.f;
-  for (int t = 0; t < topk; ++t) {
-    const int J = min(max(row[t], 0), n_kb - 1);
-    if (listed_before(t, J)) continue;
-    const int nv = load_kv(J, true, false);
-    v16f st[2], dp[2];
-    scores(st);
-    dpt(dp);
-    if (!wave_live) continue;
-    float bm = -INFINITY;
+  {
+    int wi = 0;
+    uint32_t cw = sb[0];
+    int cur = next_block(wi, cw), slot = 0;
+    if (cur >= 0) stage(cur, 0);
+    while (cur >= 0) {
+      const int nxt = next_block(wi, cw);
+      dma_sync();
+      if (nxt >= 0) stage(nxt, slot ^ 1);
+      if (wave_live) {
+        const unsigned char* t = smem + slot * 2 * kTileBytes;
+        const int nv = min(64, N - cur * 64);
+        int lx = l;
+        asm volatile("" : "+v"(lx));
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
+        for (int tt = 0; tt < 2; ++tt) {
+          v16f st, dp;
+          tile_sdp(t, tt, lx, st, dp);
+          float bm = -INFINITY;
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (32 * tt + acc_row(r) < nv) bm = fmaxf(bm, st[tt][r] * c2);
-    bm = fmaxf(bm, __shfl_xor(bm, 32));
-    const float mn = fmaxf(m, bm);
-    float ps = 0.f, pu = 0.f;
+          for (int r = 0; r < 16; ++r)
+            if (32 * tt + acc_row(r) < nv) bm = fmaxf(bm, st[r] * c2);
+          bm = fmaxf(bm, swap_halves_f32(bm));
+          const float mn = fmaxf(m, bm);
+          float ps = 0.f, pu = 0.f;
+          if (mn != -INFINITY) {
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (32 * tt + acc_row(r) < nv) {
-          const float e = __builtin_amdgcn_exp2f(st[tt][r] * c2 - mn);
-          ps += e;
-          pu = fmaf(e, dp[tt][r], pu);
+            for (int r = 0; r < 16; ++r)
+              if (32 * tt + acc_row(r) < nv) {
+                const float e = __builtin_amdgcn_exp2f(st[r] * c2 - mn);
+                ps += e;
+                pu = fmaf(e, dp[r], pu);
+              }
+          }
+          ps += swap_halves_f32(ps);
+          pu += swap_halves_f32(pu);
+          const float sc = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mn);
+          lsum = lsum * sc + ps;
+          usum = usum * sc + pu;
+          m = mn;
         }
-    ps += __shfl_xor(ps, 32);
-    pu += __shfl_xor(pu, 32);
-    const float sc = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mn);
-    lsum = lsum * sc + ps;
-    usum = usum * sc + pu;
-    m = mn;
+      }
+      cur = nxt;
+      slot ^= 1;
+    }
   }
   const float lse = (lsum > 0.f) ? m + __log2f(lsum) : 0.f;  // no selected key: every P is 0 below
   const float dsum = (lsum > 0.f) ? usum / lsum : 0.f;
@@ -189,44 +252,49 @@ __global__ __launch_bounds__(256) void kb_q(const uint16_t* __restrict__ q, cons
     d_out[(size_t)bh * N + r0 + i_loc] = dsum;
   }
 
-  // pass 2: dS = P (dP - D) into LDS (rows i, keys j) as hi + lo, then dQ^T tiles += K^T-rows . dS-rows
+  // pass 2: dS^T = P (dP - D) per tile in registers, dQ^T += K^T dS^T with K^T read transposed from the K tile
   v16f acc[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) acc[u] = (v16f){};
-  for (int t = 0; t < topk; ++t) {
-    const int J = min(max(row[t], 0), n_kb - 1);
-    if (listed_before(t, J)) continue;
-    const int nv = load_kv(J, true, true);
-    v16f st[2], dp[2];
-    scores(st);
-    dpt(dp);
+  {
+    int wi = 0;
+    uint32_t cw = sb[0];
+    int cur = next_block(wi, cw), slot = 0;
+    __syncthreads();  // pass 1's reads of both slots are done
+    if (cur >= 0) stage(cur, 0);
+    while (cur >= 0) {
+      const int nxt = next_block(wi, cw);
+      dma_sync();
+      if (nxt >= 0) stage(nxt, slot ^ 1);
+      if (wave_live) {
+        const unsigned char* t = smem + slot * 2 * kTileBytes;
+        const int nv = min(64, N - cur * 64);
+        int lx = l;
+        asm volatile("" : "+v"(lx));
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
+        for (int tt = 0; tt < 2; ++tt) {
+          v16f st, dp;
+          tile_sdp(t, tt, lx, st, dp);
 #pragma unroll
-      for (int r = 0; r < 16; r += 4) {
-        float hv[4], lv[4];
+          for (int r = 0; r < 16; ++r) {
+            const float p = (32 * tt + acc_row(r) < nv) ? __builtin_amdgcn_exp2f(st[r] * c2 - lse) : 0.f;
+            st[r] = p * (dp[r] - dsum);
+          }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const bool ok = wave_live && 32 * tt + acc_row(r + e) < nv;
-          const float p = ok ? __builtin_amdgcn_exp2f(st[tt][r + e] * c2 - lse) : 0.f;
-          const float ds = p * (dp[tt][r + e] - dsum);
-          hv[e] = from_bf16(to_bf16(ds));
-          lv[e] = ds - hv[e];
-        }
-        const int j0 = 32 * tt + acc_row(r);
+          for (int s = 0; s < 2; ++s) {
+            v8bf hi, lo;
+            split8(st, s, hi, lo);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          sSh[i_loc * kLd64 + j0 + e] = to_bf16(hv[e]);
-          sSl[i_loc * kLd64 + j0 + e] = to_bf16(lv[e]);
+            for (int u = 0; u < 4; ++u) {
+              const v8bf a = tr_op(t, 32 * tt + 16 * s, 32 * u, lx);
+              acc[u] = mfma(a, hi, acc[u]);
+              acc[u] = mfma(a, lo, acc[u]);
+            }
+          }
         }
       }
-    // this wave reads back only its own dS rows: a wave-level ordering of its LDS writes suffices
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
-    __builtin_amdgcn_wave_barrier();
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      acc[u] = mma_nt(sKt + 32 * u * kLd64, kLd64, sSh + 32 * w * kLd64, kLd64, 64, acc[u]);
-      acc[u] = mma_nt(sKt + 32 * u * kLd64, kLd64, sSl + 32 * w * kLd64, kLd64, 64, acc[u]);
+      cur = nxt;
+      slot ^= 1;
     }
   }
   // acc[u][r] = dQ^T[d = 32 u + acc_row(r)][i = i_loc] (unscaled)
@@ -242,41 +310,38 @@ __global__ __launch_bounds__(256) void kb_q(const uint16_t* __restrict__ q, cons
 }
 
 // ---------------------------------------------------------------------------------------------------------
-// kb_kv: grid (n_kb, BH), 256 threads: wave w takes keys 32 (w % 2) .. +31 and rows 32 (w / 2) .. +31 of each
-// 64-row half of a query block. For every query block I that selected J (bitmap): S = Q K^T and dP = dY V^T
-// tiles with the keys as columns (lane = key), P and dS written transposed (rows = keys) to LDS as hi + lo, then
-// dV^T += dY^T-rows . P^T-rows and dK^T += Q^T-rows . dS^T-rows over the wave's 32 rows. The two waves of a key
-// tile then hold partial sums over complementary rows, added in a fixed order at the end.
+// kb_kv: grid (n_kb, BH), 256 threads, two workgroups per CU: wave w takes keys 32 (w % 2) .. +31 and rows
+// 32 (w / 2) .. +31 of each 64-row half of a query block. K and V of the block are staged once; for every query
+// block I that selected J (bitmap) the halves of Q and dY are staged as swizzled tiles, S = Q K^T and
+// dP = dY V^T are formed with the keys as columns (lane = key), and P and dS, still in their accumulator
+// registers, are the B operands of dV^T += dY^T P and dK^T += Q^T dS, whose A operands are read transposed
+// from the Q and dY tiles. The two waves of a key tile then hold partial sums over complementary rows, added in a
+// fixed order at the end.
 // ---------------------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void kb_kv(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-                                             const uint16_t* __restrict__ v, const uint16_t* __restrict__ dy,
-                                             const uint32_t* __restrict__ bits, const float* __restrict__ lse_in,
-                                             const float* __restrict__ d_in, float* __restrict__ dk,
-                                             float* __restrict__ dv, int N, int n_qb, int n_kb, int n_qbw, int blk_q,
-                                             float sm_scale) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  __bf16* sQ = (__bf16*)smem;       // [64][kLd128]   64 query rows
-  __bf16* sdY = sQ + 64 * kLd128;   // [64][kLd128]
-  __bf16* sQt = sdY + 64 * kLd128;  // [128][kLd64]   Q^T of those rows
-  __bf16* sdYt = sQt + 128 * kLd64; // [128][kLd64]
-  __bf16* sK = sdYt + 128 * kLd64;  // [64][kLd128]
-  __bf16* sV = sK + 64 * kLd128;    // [64][kLd128]
-  __bf16* sPh = sV + 64 * kLd128;   // [64 keys][kLd64] P^T hi
-  __bf16* sPl = sPh + 64 * kLd64;
-  __bf16* sDh = sPl + 64 * kLd64;   // dS^T hi
-  __bf16* sDl = sDh + 64 * kLd64;
-  float* sL = (float*)(sDl + 64 * kLd64);  // [64] LSE of the rows
-  float* sDd = sL + 64;                    // [64] D of the rows
+__global__ __launch_bounds__(256, 2) void kb_kv(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                                                const uint16_t* __restrict__ v, const uint16_t* __restrict__ dy,
+                                                const uint32_t* __restrict__ bits, const float* __restrict__ lse_in,
+                                                const float* __restrict__ d_in, float* __restrict__ dk,
+                                                float* __restrict__ dv, int N, int n_qb, int n_kb, int n_qbw,
+                                                int blk_q, float sm_scale) {
+  extern __shared__ __align__(1024) unsigned char smem[];
+  unsigned char* sK = smem;
+  unsigned char* sV = smem + kTileBytes;
+  unsigned char* sQ = smem + 2 * kTileBytes;
+  unsigned char* sdY = smem + 3 * kTileBytes;
+  float* sL = (float*)(smem + 4 * kTileBytes);  // [64] LSE of the half's rows
+  float* sDd = sL + 64;                          // [64] D of the half's rows
   const int J = blockIdx.x, bh = blockIdx.y;
-  const int w = threadIdx.x >> 6, l = threadIdx.x & 63, lr = l & 31;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = threadIdx.x & 63;
   const int kt = w & 1, ch = w >> 1;  // key tile, row chunk
   const int nk = min(64, N - J * 64);
-  const uint16_t* qh = q + (size_t)bh * N * kD;
-  const uint16_t* dyh = dy + (size_t)bh * N * kD;
-  load_rows<256>(k + (size_t)bh * N * kD, J * 64, 64, nk, sK, kLd128);
-  load_rows<256>(v + (size_t)bh * N * kD, J * 64, 64, nk, sV, kLd128);
   const float c2 = sm_scale * kLog2e;
-  const int j_loc = 32 * kt + lr;
+  const TileLoader load;
+  const __amdgpu_buffer_rsrc_t rq = head_rsrc(q + (size_t)bh * N * kD, N);
+  const __amdgpu_buffer_rsrc_t ry = head_rsrc(dy + (size_t)bh * N * kD, N);
+  load(head_rsrc(k + (size_t)bh * N * kD, N), J * 64, nk, sK);
+  load(head_rsrc(v + (size_t)bh * N * kD, N), J * 64, nk, sV);
+  const int j_loc = 32 * kt + (l & 31);
   v16f accv[4], acck[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) accv[u] = acck[u] = (v16f){};
@@ -290,48 +355,58 @@ __global__ __launch_bounds__(256) void kb_kv(const uint16_t* __restrict__ q, con
       for (int h0 = 0; h0 < nq; h0 += 64) {
         const int nh = min(64, nq - h0);
         __syncthreads();  // the previous half's tiles are no longer read
-        load_rows<256>(qh, q0 + h0, 64, nh, sQ, kLd128);
-        load_rows<256>(dyh, q0 + h0, 64, nh, sdY, kLd128);
-        load_rows_t<256>(qh, q0 + h0, 64, nh, sQt, kLd64);
-        load_rows_t<256>(dyh, q0 + h0, 64, nh, sdYt, kLd64);
+        load(rq, q0 + h0, nh, sQ);
+        load(ry, q0 + h0, nh, sdY);
         if (threadIdx.x < 64) {
           const int ii = threadIdx.x;
           sL[ii] = ii < nh ? lse_in[(size_t)bh * N + q0 + h0 + ii] : 0.f;
           sDd[ii] = ii < nh ? d_in[(size_t)bh * N + q0 + h0 + ii] : 0.f;
         }
-        __syncthreads();
-        const v16f s = mma_nt(sQ + 32 * ch * kLd128, kLd128, sK + 32 * kt * kLd128, kLd128, kD, (v16f){});
-        const v16f dp = mma_nt(sdY + 32 * ch * kLd128, kLd128, sV + 32 * kt * kLd128, kLd128, kD, (v16f){});
+        dma_sync();
+        // the lane index goes through an opaque copy each half, so that the tile addresses derived from it are
+        // recomputed where they are used instead of being held in registers across the loop
+        int lx = l;
+        asm volatile("" : "+v"(lx));
+        v16f s = (v16f){}, dp = (v16f){};
+#pragma unroll
+        for (int sd = 0; sd < 8; ++sd) {
+          s = mfma(row_op(sQ, 32 * ch, 16 * sd, lx), row_op(sK, 32 * kt, 16 * sd, lx), s);
+          dp = mfma(row_op(sdY, 32 * ch, 16 * sd, lx), row_op(sV, 32 * kt, 16 * sd, lx), dp);
+        }
+        // s[r] -> P, dp[r] -> dS for row 32 ch + acc_row(r) and key j_loc (the fences keep the row statistics'
+        // reads and the transposed operand reads from being hoisted while every accumulator is live)
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int ii = 32 * ch + acc_row(r);
-          const bool ok = ii < nh;
-          const float p = ok ? __builtin_amdgcn_exp2f(s[r] * c2 - sL[ii]) : 0.f;
-          const float ds = p * (dp[r] - sDd[ii]);
-          const float ph = from_bf16(to_bf16(p)), dh = from_bf16(to_bf16(ds));
-          sPh[j_loc * kLd64 + ii] = to_bf16(ph);
-          sPl[j_loc * kLd64 + ii] = to_bf16(p - ph);
-          sDh[j_loc * kLd64 + ii] = to_bf16(dh);
-          sDl[j_loc * kLd64 + ii] = to_bf16(ds - dh);
+          const float p = ii < nh ? __builtin_amdgcn_exp2f(s[r] * c2 - sL[ii]) : 0.f;
+          dp[r] = p * (dp[r] - sDd[ii]);
+          s[r] = p;
         }
-        // each wave reads back only the P^T / dS^T entries it wrote (its keys, its 32 rows)
-        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
-        __builtin_amdgcn_wave_barrier();
-        const int i0 = 32 * ch;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          accv[u] = mma_nt(sdYt + 32 * u * kLd64 + i0, kLd64, sPh + 32 * kt * kLd64 + i0, kLd64, 32, accv[u]);
-          accv[u] = mma_nt(sdYt + 32 * u * kLd64 + i0, kLd64, sPl + 32 * kt * kLd64 + i0, kLd64, 32, accv[u]);
-          acck[u] = mma_nt(sQt + 32 * u * kLd64 + i0, kLd64, sDh + 32 * kt * kLd64 + i0, kLd64, 32, acck[u]);
-          acck[u] = mma_nt(sQt + 32 * u * kLd64 + i0, kLd64, sDl + 32 * kt * kLd64 + i0, kLd64, 32, acck[u]);
+        for (int st = 0; st < 2; ++st) {
+          __builtin_amdgcn_sched_barrier(0);
+          v8bf ph, pl, dh, dl;
+          split8(s, st, ph, pl);
+          split8(dp, st, dh, dl);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const v8bf ay = tr_op(sdY, 32 * ch + 16 * st, 32 * u, lx);
+            accv[u] = mfma(ay, ph, accv[u]);
+            accv[u] = mfma(ay, pl, accv[u]);
+            const v8bf aq = tr_op(sQ, 32 * ch + 16 * st, 32 * u, lx);
+            acck[u] = mfma(aq, dh, acck[u]);
+            acck[u] = mfma(aq, dl, acck[u]);
+          }
         }
       }
     }
   }
   // acc[u][r] = partial X^T[d = 32 u + acc_row(r)][key j_loc] over the rows of chunk ch: chunk 1 hands its sums
-  // to chunk 0 through LDS (the row tiles are free now), which adds them (chunk 0 first) and stores
-  __syncthreads();
-  float* sX = (float*)smem;  // [2 key tiles][2 (dV, dK)][4 u][16 r][64 lanes]
+  // to chunk 0 through LDS (the tiles are free now, and the K and V loads have landed even when no query block
+  // selected J), which adds them (chunk 0 first) and stores
+  dma_sync();
+  float* sX = (float*)smem;  // [2 key tiles][2 (dV, dK)][4 u][16 r][64 lanes] = 64 KB
   if (ch == 1) {
 #pragma unroll
     for (int u = 0; u < 4; ++u)
@@ -650,10 +725,8 @@ __global__ __launch_bounds__(256) void kb_dw_sum(const float* __restrict__ part,
 // ---------------------------------------------------------------------------------------------------------
 // launches
 // ---------------------------------------------------------------------------------------------------------
-size_t kbq_lds_bytes() { return (size_t)(2 * 128 * kLd128 + 2 * 64 * kLd128 + 3 * 128 * kLd64) * 2; }
-size_t kbkv_lds_bytes() {
-  return (size_t)(2 * 64 * kLd128 + 2 * 128 * kLd64 + 2 * 64 * kLd128 + 4 * 64 * kLd64) * 2 + 2 * 64 * 4;
-}
+size_t kbq_lds_bytes() { return (size_t)4 * kTileBytes; }
+size_t kbkv_lds_bytes() { return (size_t)4 * kTileBytes + 2 * 64 * 4; }
 size_t kblinq_lds_bytes() { return (size_t)(2 * kD * kD + 3 * kD + 16 * kD) * 4; }
 size_t kblink_lds_bytes() { return (size_t)(kD * kD + 2 * 64 * kD + kD) * 4; }
 
@@ -668,16 +741,17 @@ hipError_t launch_backward_sparse(const BwdPlan& b, hipStream_t s) {
   hipError_t e0 = allow_lds(kb_q, kbq_lds_bytes());
   if (e0 == hipSuccess) e0 = allow_lds(kb_kv, kbkv_lds_bytes());
   if (e0 != hipSuccess) return e0;
-  const int n_qbw = (p.n_qb + 31) / 32;
+  const int n_qbw = (p.n_qb + 31) / 32, n_kbw = (p.n_kb + 31) / 32;
   hipError_t e = launch_fill_f32((float*)b.sel_bits, (size_t)p.BH * p.n_kb * n_qbw, 0.f, s);
+  if (e == hipSuccess) e = launch_fill_f32((float*)b.sel_bits_q, (size_t)p.BH * p.n_qb * n_kbw, 0.f, s);
   if (e != hipSuccess) return e;
   if (p.topk > 0) {
-    hipLaunchKernelGGL(kb_sel, dim3(p.n_qb, p.BH), dim3(64), 0, s, p.block_idx, b.sel_bits, p.n_qb, p.n_kb, p.topk,
-                       n_qbw);
+    hipLaunchKernelGGL(kb_sel, dim3(p.n_qb, p.BH), dim3(64), 0, s, p.block_idx, b.sel_bits, b.sel_bits_q, p.n_qb,
+                       p.n_kb, p.topk, n_qbw, n_kbw);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(kb_q, dim3(p.n_qb, p.BH), dim3(256), kbq_lds_bytes(), s, b.q, b.k, b.v, b.dy, p.block_idx,
-                     b.lse, b.dd, b.dq, p.N, p.n_qb, p.n_kb, p.topk, p.blk_q, p.sm_scale);
+  hipLaunchKernelGGL(kb_q, dim3(p.n_qb, p.BH), dim3(256), kbq_lds_bytes(), s, b.q, b.k, b.v, b.dy, b.sel_bits_q,
+                     b.lse, b.dd, b.dq, p.N, p.n_qb, n_kbw, p.blk_q, p.sm_scale);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(kb_kv, dim3(p.n_kb, p.BH), dim3(256), kbkv_lds_bytes(), s, b.q, b.k, b.v, b.dy, b.sel_bits,
                      b.lse, b.dd, b.dk, b.dv, p.N, p.n_qb, p.n_kb, n_qbw, p.blk_q, p.sm_scale);

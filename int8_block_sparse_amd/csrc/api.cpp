@@ -344,6 +344,7 @@ size_t plan_backward(const Plan& pl, unsigned char* ws, BwdPlan* b) {
   if (lin_active) {
     b->o_l = (float*)take(BH * N * kD * sizeof(float));
     b->dhm = (float*)take(BH * pl.n_qb * (size_t)kStateX * sizeof(float));
+    b->keep_t = (uint32_t*)take(BH * (size_t)((pl.n_qb + 31) / 32) * mask_row_pad(pl.n_kb) * sizeof(uint32_t));
     b->dhj = (float*)take(BH * pl.n_kb * (size_t)kStateX * sizeof(float));
     b->dw_part = (float*)take(BH * backward_dw_chunks(pl.N) * kD * kD * sizeof(float));
   }

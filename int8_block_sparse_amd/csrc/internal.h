@@ -75,8 +75,9 @@ struct BwdPlan {
   uint32_t* sel_bits;              // [BH][n_kb][ceil(n_qb/32)]: bit I of key block J = I selected J
   uint32_t* sel_bits_q;            // [BH][n_qb][ceil(n_kb/32)]: bit J of query block I = I selected J
   float* o_l;                      // [BH][N][D] linear-branch output before W_p
-  float* dhm;                      // [BH][n_qb][kStateX] per query block dH_m (c-major) then dZ_m
-  float* dhj;                      // [BH][n_kb][kStateX] per key block dH_J then dZ_J
+  float* dhm;                      // [BH][kStateX / 128][n_qb][128] per query block dH_m (row c = column group c) then dZ_m
+  uint32_t* keep_t;                // [BH][ceil(n_qb/32)][mask_row_pad(n_kb)]: bit I of key block J = I did not select J
+  float* dhj;                      // [BH][n_kb] records: dH_J as bf16 hi and lo planes (row c), then dZ_J fp32
   float* dw_part;                  // [BH][n_chunks][D][D]
 };
 hipError_t launch_backward_sparse(const BwdPlan& b, hipStream_t s);
@@ -88,5 +89,10 @@ hipError_t launch_fill_f32(float* dst, size_t n, float val, hipStream_t s);
 size_t topk_lds_bytes(int n_kb);
 // query-block rows of the keep mask, padded for the linear-branch product's chunks
 int mask_row_pad(int n_qb);
+// out[r] = sum over i of mask bit (r, i) times table row i, for every record column: table fp32
+// [BH][kStateX / 128][n_in][128], mask [BH][ceil(n_in/32)][pad] (bit i % 32 of word i / 32 of row r), out in the
+// remaining-state record format (bf16 hi and lo planes of the first D*D columns, then fp32 columns), [BH][n_out]
+hipError_t launch_state_sum(const float* table, const uint32_t* mask, float* out, int n_out, int n_in, int pad, int BH,
+                            hipStream_t s);
 
 }  // namespace sagesla

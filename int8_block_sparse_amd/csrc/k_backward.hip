@@ -14,7 +14,8 @@
 // Linear branch (fp32 VALU tiles), after the forward's remaining-state product (H_m, Z_m per query block):
 //   kb_lin_q   per query block: O_l, dO_l = dY W_p^T, dnum = dO_l / den, dden = -(dO_l . O_l) / den,
 //              dQ += (dnum H_m^T + dden Z_m) * phi'(q), and the block's dH_m = phi(Q)^T dnum, dZ_m = phi(Q)^T dden
-//   kb_lin_sum per key block J: dH_J, dZ_J = the sums of dH_m, dZ_m over the query blocks that did not select J
+//   kb_keep_t  the keep mask transposed; dH_J, dZ_J = the sums of dH_m, dZ_m over the query blocks that did not
+//              select J, as the forward's dense mask x table product (k4_gemm, bf16 hi + lo MFMA)
 //   kb_lin_k   per key block: dK += (V dH_J^T + dZ_J) * phi'(k), dV += phi(K) dH_J
 //   kb_dw      dW_p = sum over all rows of O_l^T dY (per-chunk partials, then a fixed-order sum)
 // Every sum has a fixed order; no atomics touch floating-point data.
@@ -599,44 +600,39 @@ __global__ __launch_bounds__(256) void kb_lin_q(const uint16_t* __restrict__ q, 
   VTile<128> dh;
   vzero(dh);
   vgemm(dh, pB, 1, kD, pA, kD, 1, kD);  // A[row = c][kk = i] = phi(Q)[i][c]
-  float* out = dhm + ((size_t)bh * n_qb + I) * kStateX;
+  // column-tiled table: dH_m[c][e] at column group c, column e; dZ_m at column group D
+  auto tbl = [&](int xg, int col) -> float& { return dhm[(((size_t)bh * (kStateX / 128) + xg) * n_qb + I) * 128 + col]; };
 #pragma unroll
   for (int a = 0; a < 8; ++a)
 #pragma unroll
-    for (int b = 0; b < 8; ++b) out[(ty + 16 * a) * kD + tx + 16 * b] = dh.c[a][b];
+    for (int b = 0; b < 8; ++b) tbl(ty + 16 * a, tx + 16 * b) = dh.c[a][b];
   if (t < kD) {
     float s = 0.f;
     for (int i = 0; i < kD; ++i) s = fmaf(pB[i * kD + t], sDd[i], s);
-    out[kD * kD + t] = s;
+    tbl(kD, t) = s;
   }
 }
 
 // ---------------------------------------------------------------------------------------------------------
-// kb_lin_sum: grid (ceil(kStateX / 256), ceil(n_kb / 64), BH), 256 threads. Thread t owns column x = 256 bx + t
-// of the key blocks J0 .. J0+63 and adds dH_m[I][x] over the query blocks I in ascending order whenever J is not
-// selected by I (the keep mask of the forward's linear stage).
+// kb_keep_t: the keep mask transposed for the sum over query blocks, keep_t[bh][w][J] (rows padded to kpad):
+// bit i = 1 iff query block 32 w + i exists and did not select key block J (the complement of the selection
+// bitmap); padding rows are 0. The sums dH_J = sum over those query blocks of dH_m then run as the same dense
+// mask x table product as the forward's remaining states.
 // ---------------------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void kb_lin_sum(const float* __restrict__ dhm, const uint32_t* __restrict__ keep,
-                                                  float* __restrict__ dhj, int n_qb, int n_kb, int n_kbw, int qpad) {
-  const int x = blockIdx.x * 256 + threadIdx.x, J0 = blockIdx.y * 64, bh = blockIdx.z;
-  float acc[64];
-#pragma unroll
-  for (int j = 0; j < 64; ++j) acc[j] = 0.f;
-  const uint32_t* km = keep + (size_t)bh * n_kbw * qpad;
-  const int w0 = J0 >> 5;
-  for (int I = 0; I < n_qb; ++I) {
-    const float vx = x < kStateX ? dhm[((size_t)bh * n_qb + I) * kStateX + x] : 0.f;
-    const uint32_t m0 = km[(size_t)w0 * qpad + I];
-    const uint32_t m1 = (w0 + 1 < n_kbw) ? km[(size_t)(w0 + 1) * qpad + I] : 0u;
-#pragma unroll
-    for (int j = 0; j < 32; ++j) {
-      if ((m0 >> j) & 1u) acc[j] += vx;
-      if ((m1 >> j) & 1u) acc[32 + j] += vx;
-    }
+__global__ __launch_bounds__(256) void kb_keep_t(const uint32_t* __restrict__ sel_bits, uint32_t* __restrict__ keep_t,
+                                                 int n_qb, int n_kb, int n_qbw, int kpad, size_t total) {
+  const size_t x = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (x >= total) return;
+  const int J = (int)(x % kpad);
+  const size_t r = x / kpad;
+  const int w = (int)(r % n_qbw), bh = (int)(r / n_qbw);
+  uint32_t v = 0u;
+  if (J < n_kb) {
+    const int left = n_qb - 32 * w;
+    const uint32_t valid = left >= 32 ? 0xffffffffu : ((1u << left) - 1u);
+    v = ~sel_bits[((size_t)bh * n_kb + J) * n_qbw + w] & valid;
   }
-  if (x < kStateX)
-    for (int j = 0; j < 64; ++j)
-      if (J0 + j < n_kb) dhj[((size_t)bh * n_kb + J0 + j) * kStateX + x] = acc[j];
+  keep_t[x] = v;
 }
 
 // ---------------------------------------------------------------------------------------------------------
@@ -652,9 +648,15 @@ __global__ __launch_bounds__(256) void kb_lin_k(const uint16_t* __restrict__ k, 
   float* sZ = sP + 64 * kD;     // [128]
   const int J = blockIdx.x, bh = blockIdx.y, t = threadIdx.x, ty = t >> 4, tx = t & 15;
   const int j0 = J * 64, nk = min(64, N - j0);
-  const float* h = dhj + ((size_t)bh * n_kb + J) * kStateX;
-  for (int u = t; u < kD * kD; u += 256) sH[u] = h[u];
-  for (int u = t; u < kD; u += 256) sZ[u] = h[kD * kD + u];
+  // dH_J[c][e] = hi + lo of the record's plane row c, column e; dZ_J fp32 after the planes
+  const unsigned char* h = (const unsigned char*)(dhj + ((size_t)bh * n_kb + J) * kStateX);
+  for (int u = t; u < kD * kD; u += 256) {
+    const int c = u >> 7, e = u & 127;
+    const uint16_t hi = *(const uint16_t*)(h + out_off(c, e));
+    const uint16_t lo = *(const uint16_t*)(h + 32768 + out_off(c, e));
+    sH[u] = __uint_as_float((uint32_t)hi << 16) + __uint_as_float((uint32_t)lo << 16);
+  }
+  for (int u = t; u < kD; u += 256) sZ[u] = *(const float*)(h + 65536 + 4 * u);
   const uint16_t* kr = k + ((size_t)bh * N + j0) * kD;
   const uint16_t* vr = v + ((size_t)bh * N + j0) * kD;
   for (int u = t; u < 64 * kD; u += 256) {
@@ -767,10 +769,12 @@ hipError_t launch_backward_linear(const BwdPlan& b, hipStream_t s) {
                      (const uint16_t*)p.w_proj, p.state_m, b.o_l, b.dq, b.dhm, p.N, p.n_qb, p.blk_q);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int n_kbw = (p.n_kb + 31) / 32, qpad = mask_row_pad(p.n_qb);
-  hipLaunchKernelGGL(kb_lin_sum, dim3((kStateX + 255) / 256, (p.n_kb + 63) / 64, p.BH), dim3(256), 0, s, b.dhm,
-                     p.keep_mask, b.dhj, p.n_qb, p.n_kb, n_kbw, qpad);
+  const int n_qbw = (p.n_qb + 31) / 32, kpad = mask_row_pad(p.n_kb);
+  const size_t n_keep = (size_t)p.BH * n_qbw * kpad;
+  hipLaunchKernelGGL(kb_keep_t, dim3((unsigned)((n_keep + 255) / 256)), dim3(256), 0, s, b.sel_bits, b.keep_t, p.n_qb,
+                     p.n_kb, n_qbw, kpad, n_keep);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = launch_state_sum(b.dhm, b.keep_t, b.dhj, p.n_kb, p.n_qb, kpad, p.BH, s)) != hipSuccess) return e;
   hipLaunchKernelGGL(kb_lin_k, dim3(p.n_kb, p.BH), dim3(256), kblink_lds_bytes(), s, b.k, b.v, b.dhj, b.dk, b.dv,
                      p.N, p.n_kb);
   if ((e = hipGetLastError()) != hipSuccess) return e;

@@ -414,8 +414,13 @@ hipError_t launch_linear(const Plan& p, const uint16_t* k, const uint16_t* v, hi
   hipLaunchKernelGGL(k4_mask, dim3(rows), dim3(64), 0, s, p.block_idx, p.keep_mask, p.n_qb, p.n_kb, p.topk, n_kbw,
                      qpad);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(k4_gemm, dim3(kStateX / 128, qpad / kGemmRows, p.BH), dim3(kGemmThreads), 0, s, p.state,
-                     p.keep_mask, p.state_m, p.n_qb, p.n_kb, n_kbw, qpad);
+  return launch_state_sum(p.state, p.keep_mask, p.state_m, p.n_qb, p.n_kb, qpad, p.BH, s);
+}
+
+hipError_t launch_state_sum(const float* table, const uint32_t* mask, float* out, int n_out, int n_in, int pad, int BH,
+                            hipStream_t s) {
+  hipLaunchKernelGGL(k4_gemm, dim3(kStateX / 128, pad / kGemmRows, BH), dim3(kGemmThreads), 0, s, table, mask, out,
+                     n_out, n_in, (n_in + 31) / 32, pad);
   return hipGetLastError();
 }
 

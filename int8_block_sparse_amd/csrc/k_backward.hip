@@ -16,7 +16,7 @@
 //              dQ += (dnum H_m^T + dden Z_m) * phi'(q), and the block's dH_m = phi(Q)^T dnum, dZ_m = phi(Q)^T dden
 //   kb_keep_t  the keep mask transposed; dH_J, dZ_J = the sums of dH_m, dZ_m over the query blocks that did not
 //              select J, as the forward's dense mask x table product (k4_gemm, bf16 hi + lo MFMA)
-//   kb_lin_k   per key block: dK += (V dH_J^T + dZ_J) * phi'(k), dV += phi(K) dH_J
+//   kb_lin_k   per key block: dK += (V dH_J^T + dZ_J) * phi'(k), dV += phi(K) dH_J (bf16 MFMA, hi + lo)
 //   kb_dw      dW_p = sum over all rows of O_l^T dY (per-chunk partials, then a fixed-order sum)
 // Every sum has a fixed order; no atomics touch floating-point data.
 #include "device_common.h"
@@ -51,16 +51,18 @@ __device__ __forceinline__ v8bf row_op(const unsigned char* t, int r0, int k0, i
   return *(const v8bf*)(t + toff(r0 + (l & 31), k0 + 8 * (l >> 5)));
 }
 
-// Transposed operand: the MFMA row is tile column m0 + l % 32, and contraction slot s (0..7) of lane half g is tile
-// row i0 + 8 (s / 4) + 4 g + s % 4, the order in which an accumulator tile holds its rows, so that a tile of
-// results serves as the other operand where it stands. Two transposing reads: within each group of 16 lanes,
-// lane i receives element i % 4 of the 8-byte units addressed by lanes 4 c + i / 4, c = 0..3.
+// Transposed operand: the MFMA row is tile column m0 + l % 32, and the contraction runs over tile rows i0 .. i0 + 15.
+// With AccOrder, slot s (0..7) of lane half g is row i0 + 8 (s / 4) + 4 g + s % 4, the order in which an
+// accumulator tile holds its rows, so that a tile of results serves as the other operand where it stands;
+// otherwise slot s is row i0 + 8 g + s, the order of an operand read along a row. Two transposing reads: within
+// each group of 16 lanes, lane i receives element i % 4 of the 8-byte units addressed by lanes 4 c + i / 4.
+template <bool AccOrder = true>
 __device__ __forceinline__ v8bf tr_op(const unsigned char* t, int i0, int m0, int l) {
   const int j = l & 15;
-  const int r = i0 + 4 * (l >> 5) + (j >> 2);
+  const int r = i0 + (AccOrder ? 4 : 8) * (l >> 5) + (j >> 2);
   const int col = m0 + 16 * ((l >> 4) & 1) + 4 * (j & 3);
   const v4s a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(t + toff(r, col)));
-  const v4s b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(t + toff(r + 8, col)));
+  const v4s b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(t + toff(r + (AccOrder ? 8 : 4), col)));
   const v8s ab = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
   return __builtin_bit_cast(v8bf, ab);
 }
@@ -636,51 +638,78 @@ __global__ __launch_bounds__(256) void kb_keep_t(const uint32_t* __restrict__ se
 }
 
 // ---------------------------------------------------------------------------------------------------------
-// kb_lin_k: grid (n_kb, BH), 256 threads. dphi_k = V dH_J^T + dZ_J; dK += dphi_k * phi'(k); dV += phi(K) dH_J.
+// kb_lin_k: grid (n_kb, BH), 512 threads (8 waves). For key block J with its dH_J (the record's bf16 hi + lo
+// planes, row c) and dZ_J:
+//   dphi_k[j][c] = sum_e V[j][e] dH[c][e] + dZ[c];  dK[j][c] += dphi_k[j][c] phi'(K[j][c])
+//   dV[j][e] += sum_c phi(K)[j][c] dH[c][e]
+// on bf16 MFMA: V is exact, dH enters as hi + lo, phi(K) is split into hi + lo in registers (three products,
+// hi.hi + hi.lo + lo.hi). The planes are re-swizzled into LDS; K and V arrive by direct-to-LDS loads. Wave w owns
+// key tile w / 4 and column tile w % 4 (c for dK, e for dV).
 // ---------------------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void kb_lin_k(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+__global__ __launch_bounds__(512) void kb_lin_k(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                                                 const float* __restrict__ dhj, float* __restrict__ dk,
                                                 float* __restrict__ dv, int N, int n_kb) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  float* sH = (float*)smem;     // [128 c][128 e]
-  float* sV = sH + kD * kD;     // [64][128]
-  float* sP = sV + 64 * kD;     // [64][128] phi(K)
-  float* sZ = sP + 64 * kD;     // [128]
-  const int J = blockIdx.x, bh = blockIdx.y, t = threadIdx.x, ty = t >> 4, tx = t & 15;
+  extern __shared__ __align__(1024) unsigned char smem[];
+  unsigned char* sK = smem;                      // 64-row tiles
+  unsigned char* sV = smem + kTileBytes;
+  unsigned char* sHh = smem + 2 * kTileBytes;    // 128-row tiles: dH hi, lo (row c, column e)
+  unsigned char* sHl = sHh + 2 * kTileBytes;
+  float* sZ = (float*)(sHl + 2 * kTileBytes);    // [128]
+  const int J = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6), l = t & 63;
+  const int jt = w >> 2, ct = w & 3;
   const int j0 = J * 64, nk = min(64, N - j0);
-  // dH_J[c][e] = hi + lo of the record's plane row c, column e; dZ_J fp32 after the planes
-  const unsigned char* h = (const unsigned char*)(dhj + ((size_t)bh * n_kb + J) * kStateX);
-  for (int u = t; u < kD * kD; u += 256) {
-    const int c = u >> 7, e = u & 127;
-    const uint16_t hi = *(const uint16_t*)(h + out_off(c, e));
-    const uint16_t lo = *(const uint16_t*)(h + 32768 + out_off(c, e));
-    sH[u] = __uint_as_float((uint32_t)hi << 16) + __uint_as_float((uint32_t)lo << 16);
+  if (w < 4) {  // the loader's wave layout covers 4 waves
+    const TileLoader load;
+    load(head_rsrc(k + (size_t)bh * N * kD, N), j0, nk, sK);
+    load(head_rsrc(v + (size_t)bh * N * kD, N), j0, nk, sV);
   }
-  for (int u = t; u < kD; u += 256) sZ[u] = *(const float*)(h + 65536 + 4 * u);
-  const uint16_t* kr = k + ((size_t)bh * N + j0) * kD;
-  const uint16_t* vr = v + ((size_t)bh * N + j0) * kD;
-  for (int u = t; u < 64 * kD; u += 256) {
-    const bool ok = (u >> 7) < nk;
-    sV[u] = ok ? bf16_lo(vr[u]) : 0.f;
-    sP[u] = ok ? phi_f(bf16_lo(kr[u])) : 0.f;
+  const unsigned char* rec = (const unsigned char*)(dhj + ((size_t)bh * n_kb + J) * kStateX);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {  // 2 planes x 128 rows x 16 chunks
+    const int u = t + 512 * i, pl = u >> 11, c = (u >> 4) & 127, q = u & 15;
+    const uint4 x = *(const uint4*)(rec + 32768 * pl + out_off(c, 8 * q));
+    *(uint4*)((pl ? sHl : sHh) + toff(c, 8 * q)) = x;
   }
-  __syncthreads();
-  VTile<64> dpk, dvl;
-  vzero(dpk);
-  vzero(dvl);
-  vgemm(dpk, sV, kD, 1, sH, 1, kD, kD);  // A[j][e] = V; B[kk = e][col = c] = dH[c][e]
-  vgemm(dvl, sP, kD, 1, sH, kD, 1, kD);  // A[j][c] = phi(K); B[kk = c][col = e] = dH[c][e]
+  if (t < kD) sZ[t] = *(const float*)(rec + 65536 + 4 * t);
+  dma_sync();
+  v16f acck = (v16f){}, accv = (v16f){};
 #pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    const int j = ty + 16 * a;
-    if (j < nk)
+  for (int s = 0; s < 8; ++s) {
+    // dphi_k^T... as D[j][c]: A = V rows j (k = e), B = dH rows c (k = e)
+    const v8bf av = row_op(sV, 32 * jt, 16 * s, l);
+    acck = mfma(av, row_op(sHh, 32 * ct, 16 * s, l), acck);
+    acck = mfma(av, row_op(sHl, 32 * ct, 16 * s, l), acck);
+    // dV as D[j][e]: A = phi(K) rows j (k = c) as hi + lo, B = dH^T (column e, k = c) read transposed
+    const v8bf kr = row_op(sK, 32 * jt, 16 * s, l);
+    uint32_t ph[4], plo[4];
 #pragma unroll
-      for (int b = 0; b < 8; ++b) {
-        const int c = tx + 16 * b;
-        const size_t o = ((size_t)bh * N + j0 + j) * kD + c;
-        dk[o] += (dpk.c[a][b] + sZ[c]) * dphi(bf16_lo(kr[j * kD + c]));
-        dv[o] += dvl.c[a][b];
-      }
+    for (int e2 = 0; e2 < 4; ++e2) {
+      const uint32_t wv = __builtin_bit_cast(uint4, kr)[e2];
+      const float x0 = phi_f(bf16_lo(wv)), x1 = phi_f(bf16_lo(wv >> 16));
+      ph[e2] = pack_bf16x2(x0, x1);
+      plo[e2] = pack_bf16x2(x0 - __uint_as_float(ph[e2] << 16), x1 - __uint_as_float(ph[e2] & 0xffff0000u));
+    }
+    const v8bf ah = __builtin_bit_cast(v8bf, make_uint4(ph[0], ph[1], ph[2], ph[3]));
+    const v8bf al = __builtin_bit_cast(v8bf, make_uint4(plo[0], plo[1], plo[2], plo[3]));
+    const v8bf bh_ = tr_op<false>(sHh, 16 * s, 32 * ct, l);
+    const v8bf bl_ = tr_op<false>(sHl, 16 * s, 32 * ct, l);
+    accv = mfma(ah, bh_, accv);
+    accv = mfma(ah, bl_, accv);
+    accv = mfma(al, bh_, accv);
+  }
+  // acc[r]: key j = 32 jt + acc_row(r), column 32 ct + l % 32 (c for dK, e for dV)
+  const int col = 32 * ct + (l & 31);
+  const float zc = sZ[col];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int j = 32 * jt + acc_row(r);
+    if (j < nk) {
+      const size_t o = ((size_t)bh * N + j0 + j) * kD + col;
+      const float kv = bf16_lo(*(const uint16_t*)(sK + toff(j, col & ~3) + 2 * (col & 3)));
+      dk[o] += (acck[r] + zc) * dphi(kv);
+      dv[o] += accv[r];
+    }
   }
 }
 
@@ -730,7 +759,7 @@ __global__ __launch_bounds__(256) void kb_dw_sum(const float* __restrict__ part,
 size_t kbq_lds_bytes() { return (size_t)4 * kTileBytes; }
 size_t kbkv_lds_bytes() { return (size_t)4 * kTileBytes + 2 * 64 * 4; }
 size_t kblinq_lds_bytes() { return (size_t)(2 * kD * kD + 3 * kD + 16 * kD) * 4; }
-size_t kblink_lds_bytes() { return (size_t)(kD * kD + 2 * 64 * kD + kD) * 4; }
+size_t kblink_lds_bytes() { return (size_t)6 * kTileBytes + kD * 4; }
 
 // dynamic LDS above the default limit is requested once per kernel (gfx950 has 160 KB per workgroup)
 template <typename F>
@@ -775,7 +804,7 @@ hipError_t launch_backward_linear(const BwdPlan& b, hipStream_t s) {
                      p.n_kb, n_qbw, kpad, n_keep);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if ((e = launch_state_sum(b.dhm, b.keep_t, b.dhj, p.n_kb, p.n_qb, kpad, p.BH, s)) != hipSuccess) return e;
-  hipLaunchKernelGGL(kb_lin_k, dim3(p.n_kb, p.BH), dim3(256), kblink_lds_bytes(), s, b.k, b.v, b.dhj, b.dk, b.dv,
+  hipLaunchKernelGGL(kb_lin_k, dim3(p.n_kb, p.BH), dim3(512), kblink_lds_bytes(), s, b.k, b.v, b.dhj, b.dk, b.dv,
                      p.N, p.n_kb);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int n_chunks = (p.N + kDwChunk - 1) / kDwChunk;

@@ -12,8 +12,9 @@
 //              online; pass 2 dS = P (dP - D) and dQ = dS K sm_scale; writes LSE, D and dQ
 //   kb_kv      per key block, over the query blocks that selected it: dV = P^T dY, dK = dS^T Q sm_scale
 // Linear branch (fp32 VALU tiles), after the forward's remaining-state product (H_m, Z_m per query block):
-//   kb_lin_q   per query block: O_l, dO_l = dY W_p^T, dnum = dO_l / den, dden = -(dO_l . O_l) / den,
-//              dQ += (dnum H_m^T + dden Z_m) * phi'(q), and the block's dH_m = phi(Q)^T dnum, dZ_m = phi(Q)^T dden
+//   kb_lin_q   per query block (bf16 MFMA, hi + lo): O_l, dO_l = dY W_p^T, dnum = dO_l / den,
+//              dden = -(dO_l . O_l) / den, dQ += (dnum H_m^T + dden Z_m) * phi'(q), and the block's
+//              dH_m = phi(Q)^T dnum, dZ_m = phi(Q)^T dden
 //   kb_keep_t  the keep mask transposed; dH_J, dZ_J = the sums of dH_m, dZ_m over the query blocks that did not
 //              select J, as the forward's dense mask x table product (k4_gemm, bf16 hi + lo MFMA)
 //   kb_lin_k   per key block: dK += (V dH_J^T + dZ_J) * phi'(k), dV += phi(K) dH_J (bf16 MFMA, hi + lo)
@@ -480,138 +481,221 @@ __device__ __forceinline__ void vzero(VTile<M>& C) {
 
 __device__ __forceinline__ float dphi(float x) { return x > 0.f ? 1.f : __builtin_amdgcn_exp2f(x * kLog2e); }
 
-// H_m[c][e] of query block I from the remaining-state record (bf16 hi + lo planes of H_m^T, then Z_m fp32)
-__device__ __forceinline__ void load_state(const float* state_m, size_t rec, float* sH, float* sZ) {
-  const unsigned char* base = (const unsigned char*)state_m + rec;
-  for (int u = threadIdx.x; u < kD * kD; u += 256) {
-    const int e = u >> 7, c = u & 127;
-    const uint16_t hi = *(const uint16_t*)(base + out_off(e, c));
-    const uint16_t lo = *(const uint16_t*)(base + 32768 + out_off(e, c));
-    sH[c * kD + e] = __uint_as_float((uint32_t)hi << 16) + __uint_as_float((uint32_t)lo << 16);
-  }
-  for (int u = threadIdx.x; u < kD; u += 256) sZ[u] = *(const float*)(base + 65536 + 4 * u);
-}
-
 // ---------------------------------------------------------------------------------------------------------
-// kb_lin_q: grid (n_qb, BH), 256 threads; dynamic LDS: two 128x128 fp32 planes (A, B) + vectors.
+// kb_lin_q: grid (n_qb, BH), 256 threads (4 waves); bf16 MFMA with hi + lo splits of every non-bf16 operand.
+// For query block I with its remaining state H_m (record planes of H_m^T, row e) and Z_m:
+//   num = phi(Q) H_m, den = phi(Q) . Z_m, O_l = num / den (stored for dW_p)
+//   dO_l = dY W_p^T, dnum = dO_l / den
+//   dH_m = phi(Q)^T dnum                                    (wave w: columns e of tile w, contraction over rows)
+//   G = dnum H_m^T, dden = -(phi(Q) . G) / den              (= -(dO_l . O_l) / den; wave w: rows i of tile w)
+//   dQ += (G + dden Z_m) phi'(Q), dZ_m = phi(Q)^T dden
+// LDS: phi(Q) as hi + lo tiles (later dnum^T), the planes of H_m^T as hi + lo tiles.
 // ---------------------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void kb_lin_q(const uint16_t* __restrict__ q, const uint16_t* __restrict__ dy,
                                                 const uint16_t* __restrict__ w_proj, const float* __restrict__ state_m,
                                                 float* __restrict__ o_l, float* __restrict__ dq,
                                                 float* __restrict__ dhm, int N, int n_qb, int blk_q) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  float* pA = (float*)smem;      // [128][128]
-  float* pB = pA + kD * kD;      // [128][128]
-  float* sZ = pB + kD * kD;      // [128]
-  float* sDen = sZ + kD;         // [128]
-  float* sDd = sDen + kD;        // [128]
-  float* sRed = sDd + kD;        // [16][128]
-  const int I = blockIdx.x, bh = blockIdx.y, t = threadIdx.x, ty = t >> 4, tx = t & 15;
+  extern __shared__ __align__(1024) unsigned char smem[];
+  unsigned char* sPh = smem;                    // 128-row tiles: phi(Q) [i][c] hi, lo; later dnum^T [e][i]
+  unsigned char* sPl = smem + 2 * kTileBytes;
+  unsigned char* sHh = smem + 4 * kTileBytes;   // H_m^T [e][c] hi, lo
+  unsigned char* sHl = smem + 6 * kTileBytes;
+  float* sZ = (float*)(smem + 8 * kTileBytes);  // [128]
+  float* sDen = sZ + kD;                        // [128]
+  float* sDd = sDen + kD;                       // [128] dden
+  const int I = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6), l = t & 63, g = l >> 5;
   const int r0 = I * blk_q, nq = min(blk_q, N - r0);
-  const size_t rec = ((size_t)bh * n_qb + I) * (size_t)kStateX * 4;
+  const unsigned char* rec = (const unsigned char*)state_m + ((size_t)bh * n_qb + I) * (size_t)kStateX * 4;
   const uint16_t* qr = q + ((size_t)bh * N + r0) * kD;
   const uint16_t* dyr = dy + ((size_t)bh * N + r0) * kD;
-  // phase A: pA = phi(Q) [i][c] (rows past nq are 0), pB = H_m [c][e]; num = phi(Q) H_m, den = phi(Q) . Z_m
-  for (int u = t; u < kD * kD; u += 256) {
-    const int i = u >> 7;
-    pA[u] = i < nq ? phi_f(bf16_lo(qr[u])) : 0.f;
-  }
-  load_state(state_m, rec, pB, sZ);
-  __syncthreads();
-  for (int i = t; i < kD; i += 256) {
-    float s = 0.f;
-    for (int c = 0; c < kD; ++c) s = fmaf(pA[i * kD + c], sZ[c], s);
-    sDen[i] = s;
-  }
-  VTile<128> num;
-  vzero(num);
-  vgemm(num, pA, kD, 1, pB, kD, 1, kD);
-  __syncthreads();
-  float ol[8][8];
+  const float* zg = (const float*)(rec + 65536);
+
+  // staging: thread t takes row i = t / 2, columns 64 (t % 2) .. +63 of phi(Q) (zero past nq) and its part of
+  // den[i]; the two halves are added through the neighbouring lane (fixed order)
+  {
+    const int i = t >> 1, hc = t & 1;
+    float dpart = 0.f;
+#pragma unroll 2
+    for (int qq = 0; qq < 8; ++qq) {
+      const int c0 = 64 * hc + 8 * qq;
+      uint4 raw = make_uint4(0, 0, 0, 0);
+      if (i < nq) raw = *(const uint4*)(qr + i * kD + c0);
+      const uint32_t wv[4] = {raw.x, raw.y, raw.z, raw.w};
+      const float4 z0 = *(const float4*)(zg + c0), z1 = *(const float4*)(zg + c0 + 4);
+      const float zz[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
+      uint32_t h[4], o[4];
 #pragma unroll
-  for (int a = 0; a < 8; ++a)
-#pragma unroll
-    for (int b = 0; b < 8; ++b) {
-      const int i = ty + 16 * a;
-      ol[a][b] = i < nq ? num.c[a][b] / sDen[i] : 0.f;
+      for (int e2 = 0; e2 < 4; ++e2) {
+        const float x0 = i < nq ? phi_f(bf16_lo(wv[e2])) : 0.f, x1 = i < nq ? phi_f(bf16_lo(wv[e2] >> 16)) : 0.f;
+        dpart = fmaf(x0, zz[2 * e2], dpart);
+        dpart = fmaf(x1, zz[2 * e2 + 1], dpart);
+        h[e2] = pack_bf16x2(x0, x1);
+        o[e2] = pack_bf16x2(x0 - __uint_as_float(h[e2] << 16), x1 - __uint_as_float(h[e2] & 0xffff0000u));
+      }
+      *(uint4*)(sPh + toff(i, c0)) = make_uint4(h[0], h[1], h[2], h[3]);
+      *(uint4*)(sPl + toff(i, c0)) = make_uint4(o[0], o[1], o[2], o[3]);
     }
-#pragma unroll
-  for (int a = 0; a < 8; ++a) {
-    const int i = ty + 16 * a;
-    if (i < nq)
-#pragma unroll
-      for (int b = 0; b < 8; ++b) o_l[((size_t)bh * N + r0 + i) * kD + tx + 16 * b] = ol[a][b];
+    const float other = __shfl_xor(dpart, 1);
+    if (hc == 0) sDen[i] = dpart + other;
   }
-  __syncthreads();
-  // phase B: pA = dY [i][f], pB = W_p [e][f]; dO_l = dY W_p^T; dnum = dO_l / den; dden = -(dO_l . O_l) / den
-  for (int u = t; u < kD * kD; u += 256) {
-    pA[u] = (u >> 7) < nq ? bf16_lo(dyr[u]) : 0.f;
-    pB[u] = bf16_lo(w_proj[u]);
+#pragma unroll 4
+  for (int it = 0; it < 16; ++it) {  // the planes of H_m^T, re-swizzled: 2 planes x 128 rows x 16 chunks
+    const int u = t + 256 * it, pl = u >> 11, e = (u >> 4) & 127, qq = u & 15;
+    const uint4 x = *(const uint4*)(rec + 32768 * pl + out_off(e, 8 * qq));
+    *(uint4*)((pl ? sHl : sHh) + toff(e, 8 * qq)) = x;
   }
+  if (t < kD) sZ[t] = zg[t];
   __syncthreads();
-  VTile<128> dol;
-  vzero(dol);
-  vgemm(dol, pA, kD, 1, pB, 1, kD, kD);  // B[kk = f][col = e] = W_p[e][f]
-  float part[8];
+
+  // num (wave w: columns e of tile w, all rows): D[i][e] = sum_c phi(Q)[i][c] H_m[c][e]
+  const int ecol = 32 * w + (l & 31);
+  v16f acc[4];
 #pragma unroll
-  for (int a = 0; a < 8; ++a) {
-    part[a] = 0.f;
+  for (int a = 0; a < 4; ++a) acc[a] = (v16f){};
+#pragma unroll 2
+  for (int s = 0; s < 8; ++s) {
+    const v8bf bh_ = row_op(sHh, 32 * w, 16 * s, l), bl_ = row_op(sHl, 32 * w, 16 * s, l);
 #pragma unroll
-    for (int b = 0; b < 8; ++b) part[a] = fmaf(dol.c[a][b], ol[a][b], part[a]);
-  }
-#pragma unroll
-  for (int a = 0; a < 8; ++a) sRed[tx * kD + ty + 16 * a] = part[a];
-  __syncthreads();
-  if (t < kD) {
-    float s = 0.f;
-    for (int x = 0; x < 16; ++x) s += sRed[x * kD + t];
-    sDd[t] = t < nq ? -s / sDen[t] : 0.f;
-  }
-  __syncthreads();
-  // phase C: pA = dnum [i][e]; pB = H_m [c][e] again; dphi_q = dnum H_m^T + dden Z_m; dQ += dphi_q * phi'(q)
-#pragma unroll
-  for (int a = 0; a < 8; ++a)
-#pragma unroll
-    for (int b = 0; b < 8; ++b) {
-      const int i = ty + 16 * a;
-      pA[i * kD + tx + 16 * b] = i < nq ? dol.c[a][b] / sDen[i] : 0.f;
+    for (int a = 0; a < 4; ++a) {
+      const v8bf ah = row_op(sPh, 32 * a, 16 * s, l), al = row_op(sPl, 32 * a, 16 * s, l);
+      acc[a] = mfma(ah, bh_, acc[a]);
+      acc[a] = mfma(ah, bl_, acc[a]);
+      acc[a] = mfma(al, bh_, acc[a]);
     }
-  load_state(state_m, rec, pB, sZ);
+  }
+  // O_l = num / den, stored for dW_p
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int i = 32 * a + acc_row(r);
+      if (i < nq) o_l[((size_t)bh * N + r0 + i) * kD + ecol] = acc[a][r] / sDen[i];
+    }
+
+  // dO_l (same tiles): D[i][e] = sum_f dY[i][f] W_p[e][f]; A read from global rows of dY, B from rows of W_p
+  v8bf wb[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) wb[s] = *(const v8bf*)(w_proj + (size_t)ecol * kD + 16 * s + 8 * g);
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    acc[a] = (v16f){};
+    const int i = 32 * a + (l & 31);
+    const uint16_t* yrow = dyr + (size_t)min(i, nq - 1) * kD + 8 * g;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) acc[a] = mfma(*(const v8bf*)(yrow + 16 * s), wb[s], acc[a]);
+  }
+  // dnum = dO_l / den (0 on rows past nq)
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int i = 32 * a + acc_row(r);
+      acc[a][r] = i < nq ? acc[a][r] / sDen[i] : 0.f;
+    }
+
+  // dH_m (wave w: columns e of tile w): D[c][e] = sum_i phi(Q)^T[c][i] dnum[i][e], phi(Q)^T read transposed in
+  // accumulator row order so that dnum serves as B from its registers
+  {
+    v16f dh[4];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) dh[ct] = (v16f){};
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      v8bf nh, nl;
+      split8(acc[s >> 1], s & 1, nh, nl);
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        const v8bf ah = tr_op(sPh, 16 * s, 32 * ct, l), al = tr_op(sPl, 16 * s, 32 * ct, l);
+        dh[ct] = mfma(ah, nh, dh[ct]);
+        dh[ct] = mfma(ah, nl, dh[ct]);
+        dh[ct] = mfma(al, nh, dh[ct]);
+      }
+    }
+    // column-tiled table: dH_m[c][e] at column group c, column e
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int c = 32 * ct + acc_row(r);
+        dhm[(((size_t)bh * (kStateX / 128) + c) * n_qb + I) * 128 + ecol] = dh[ct][r];
+      }
+  }
+  __syncthreads();  // phi(Q) tiles no longer read
+  // dnum^T [e][i] as hi + lo into the phi(Q) tiles: lane e, runs of four rows i -> 8-byte pieces
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int r = 0; r < 16; r += 4) {
+      const int i0 = 32 * a + acc_row(r);
+      uint32_t h0 = pack_bf16x2(acc[a][r], acc[a][r + 1]), h1 = pack_bf16x2(acc[a][r + 2], acc[a][r + 3]);
+      uint32_t o0 = pack_bf16x2(acc[a][r] - __uint_as_float(h0 << 16), acc[a][r + 1] - __uint_as_float(h0 & 0xffff0000u));
+      uint32_t o1 = pack_bf16x2(acc[a][r + 2] - __uint_as_float(h1 << 16), acc[a][r + 3] - __uint_as_float(h1 & 0xffff0000u));
+      *(uint2*)(sPh + toff(ecol, i0)) = make_uint2(h0, h1);
+      *(uint2*)(sPl + toff(ecol, i0)) = make_uint2(o0, o1);
+    }
   __syncthreads();
-  VTile<128> dpq;
-  vzero(dpq);
-  vgemm(dpq, pA, kD, 1, pB, 1, kD, kD);  // B[kk = e][col = c] = H_m[c][e]
+
+  // G (wave w: rows i of tile w, all columns c): D[c][i] = sum_e H_m[c][e] dnum[i][e], both operands read
+  // transposed (contraction over the rows e of the H_m^T and dnum^T tiles)
+  const int irow = 32 * w + (l & 31);
 #pragma unroll
-  for (int a = 0; a < 8; ++a) {
-    const int i = ty + 16 * a;
-    if (i < nq)
+  for (int ct = 0; ct < 4; ++ct) acc[ct] = (v16f){};
+#pragma unroll 2
+  for (int s = 0; s < 8; ++s) {
+    const v8bf bh_ = tr_op<false>(sPh, 16 * s, 32 * w, l), bl_ = tr_op<false>(sPl, 16 * s, 32 * w, l);
 #pragma unroll
-      for (int b = 0; b < 8; ++b) {
-        const int c = tx + 16 * b;
-        float* d = dq + ((size_t)bh * N + r0 + i) * kD + c;
-        *d += (dpq.c[a][b] + sDd[i] * sZ[c]) * dphi(bf16_lo(qr[i * kD + c]));
+    for (int ct = 0; ct < 4; ++ct) {
+      const v8bf ah = tr_op<false>(sHh, 16 * s, 32 * ct, l), al = tr_op<false>(sHl, 16 * s, 32 * ct, l);
+      acc[ct] = mfma(ah, bh_, acc[ct]);
+      acc[ct] = mfma(ah, bl_, acc[ct]);
+      acc[ct] = mfma(al, bh_, acc[ct]);
+    }
+  }
+  // dden[i] = -(phi(Q)[i] . G[i]) / den[i]; lane i holds c = 32 ct + acc_row(r), the partner lane the rest
+  const bool iv = irow < nq;
+  const uint16_t* qrow = qr + (size_t)(iv ? irow : 0) * kD;
+  float dot = 0.f;
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+    for (int r = 0; r < 16; r += 4) {
+      const uint2 raw = iv ? *(const uint2*)(qrow + 32 * ct + acc_row(r)) : make_uint2(0, 0);
+      const uint32_t wv[2] = {raw.x, raw.y};
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        const float x = bf16_lo(e2 & 1 ? wv[e2 >> 1] >> 16 : wv[e2 >> 1]);
+        dot = fmaf(iv ? phi_f(x) : 0.f, acc[ct][r + e2], dot);
+      }
+    }
+  dot += swap_halves_f32(dot);
+  const float dden = iv ? -dot / sDen[irow] : 0.f;
+  if (l < 32) sDd[irow] = dden;
+  if (iv) {
+    float* dst = dq + ((size_t)bh * N + r0 + irow) * kD;
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+      for (int r = 0; r < 16; r += 4) {
+        const int c0 = 32 * ct + acc_row(r);
+        const uint2 raw = *(const uint2*)(qrow + c0);
+        const uint32_t wv[2] = {raw.x, raw.y};
+        float4 d = *(float4*)(dst + c0);
+        float* dd = (float*)&d;
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+          const float x = bf16_lo(e2 & 1 ? wv[e2 >> 1] >> 16 : wv[e2 >> 1]);
+          dd[e2] += (acc[ct][r + e2] + dden * sZ[c0 + e2]) * dphi(x);
+        }
+        *(float4*)(dst + c0) = d;
       }
   }
   __syncthreads();
-  // phase D: pB = phi(Q) [i][c]; dH_m = phi(Q)^T dnum -> C[c][e] = sum_i pB[i][c] pA[i][e]; dZ_m = phi(Q)^T dden
-  for (int u = t; u < kD * kD; u += 256) {
-    const int i = u >> 7;
-    pB[u] = i < nq ? phi_f(bf16_lo(qr[u])) : 0.f;
-  }
-  __syncthreads();
-  VTile<128> dh;
-  vzero(dh);
-  vgemm(dh, pB, 1, kD, pA, kD, 1, kD);  // A[row = c][kk = i] = phi(Q)[i][c]
-  // column-tiled table: dH_m[c][e] at column group c, column e; dZ_m at column group D
-  auto tbl = [&](int xg, int col) -> float& { return dhm[(((size_t)bh * (kStateX / 128) + xg) * n_qb + I) * 128 + col]; };
-#pragma unroll
-  for (int a = 0; a < 8; ++a)
-#pragma unroll
-    for (int b = 0; b < 8; ++b) tbl(ty + 16 * a, tx + 16 * b) = dh.c[a][b];
+  // dZ_m[c] = sum_i phi(Q)[i][c] dden[i] (rows in ascending order)
   if (t < kD) {
-    float s = 0.f;
-    for (int i = 0; i < kD; ++i) s = fmaf(pB[i * kD + t], sDd[i], s);
-    tbl(kD, t) = s;
+    float sz = 0.f;
+    for (int i = 0; i < nq; ++i) sz = fmaf(phi_f(bf16_lo(qr[(size_t)i * kD + t])), sDd[i], sz);
+    dhm[(((size_t)bh * (kStateX / 128) + kD) * n_qb + I) * 128 + t] = sz;
   }
 }
 
@@ -758,7 +842,7 @@ __global__ __launch_bounds__(256) void kb_dw_sum(const float* __restrict__ part,
 // ---------------------------------------------------------------------------------------------------------
 size_t kbq_lds_bytes() { return (size_t)4 * kTileBytes; }
 size_t kbkv_lds_bytes() { return (size_t)4 * kTileBytes + 2 * 64 * 4; }
-size_t kblinq_lds_bytes() { return (size_t)(2 * kD * kD + 3 * kD + 16 * kD) * 4; }
+size_t kblinq_lds_bytes() { return (size_t)8 * kTileBytes + 3 * kD * 4; }
 size_t kblink_lds_bytes() { return (size_t)6 * kTileBytes + kD * 4; }
 
 // dynamic LDS above the default limit is requested once per kernel (gfx950 has 160 KB per workgroup)

@@ -68,6 +68,30 @@ __device__ __forceinline__ v8bf tr_op(const unsigned char* t, int i0, int m0, in
   return __builtin_bit_cast(v8bf, ab);
 }
 
+// Lane parts of operand addresses in a swizzled tile. Every read is then a lane register plus a compile-time
+// offset (tile base, 32-row tile step, 16-row step), with no address arithmetic in the loops.
+// row_op(t, r0, 16 s, l) = t + 256 r0 + row_lane_off(l, s) for r0 a multiple of 16
+__device__ __forceinline__ uint32_t row_lane_off(int l, int s) {
+  const int lr = l & 31, g = l >> 5;
+  return (uint32_t)(lr * 256 + 16 * ((2 * s + g) ^ tswz(lr)));
+}
+// read h of tr_op<true>(t, i0, 32 u, l) = t + 256 i0 + tr_lane_off(l, u, h) for i0 a multiple of 16: the row is
+// i0 + 4 g + j / 4 + 8 h, whose tswz is 4 (j / 4) + (g + 2 h) % 4
+__device__ __forceinline__ uint32_t tr_lane_off(int l, int u, int h) {
+  const int g = l >> 5, j = l & 15, grp = (l >> 4) & 1;
+  const int rl = 4 * g + (j >> 2) + 8 * h;
+  const int sw = 4 * (j >> 2) + ((g + 2 * h) & 3);
+  const int chunk = 4 * u + 2 * grp + ((j & 3) >> 1);
+  return (uint32_t)(rl * 256 + 16 * (chunk ^ sw) + 8 * (j & 1));
+}
+__device__ __forceinline__ v8bf ld_row(const unsigned char* p) { return *(const v8bf*)p; }
+__device__ __forceinline__ v8bf ld_tr(const unsigned char* p0, const unsigned char* p1) {
+  const v4s a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)p0);
+  const v4s b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)p1);
+  const v8s ab = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return __builtin_bit_cast(v8bf, ab);
+}
+
 // accumulator rows 8 s .. 8 s + 7 of a lane as bf16 hi and lo operands (hi = bf16(x), lo = bf16(x - hi))
 __device__ __forceinline__ void split8(const v16f& x, int s, v8bf& hi, v8bf& lo) {
   uint32_t h[4], o[4];
@@ -172,6 +196,21 @@ __global__ __launch_bounds__(256, 2) void kb_q(const uint16_t* __restrict__ q, c
   const __amdgpu_buffer_rsrc_t rv = head_rsrc(v + (size_t)bh * N * kD, N);
   const TileLoader load;
   const uint32_t* sb = bits_q + ((size_t)bh * n_qb + I) * n_kbw;
+  // lane parts of the tile addresses, opaque so that the compiler keeps these 16 registers rather than
+  // materializing one address per read
+  uint32_t ro[8], to[4][2];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    ro[s] = row_lane_off(l, s);
+    asm volatile("" : "+v"(ro[s]));
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      to[u][h] = tr_lane_off(l, u, h);
+      asm volatile("" : "+v"(to[u][h]));
+    }
   // the selected blocks in ascending order: a cursor over the bitmap words (uniform across the workgroup)
   auto next_block = [&](int& wi, uint32_t& cw) -> int {
     while (cw == 0) {
@@ -188,67 +227,69 @@ __global__ __launch_bounds__(256, 2) void kb_q(const uint16_t* __restrict__ q, c
     load(rk, J * 64, nv, t);
     load(rv, J * 64, nv, t + kTileBytes);
   };
-  // S^T and dP^T of one 32-key tile tt of the block in slot `t`
-  // (lx: the lane index through an opaque copy per block, so that tile addresses are recomputed where used)
-  auto tile_sdp = [&](const unsigned char* t, int tt, int lx, v16f& st, v16f& dp) {
+  // Runs body(J, K tile, V tile) over the selected blocks through the two-slot ring; the loop is unrolled by
+  // two so that each slot's tile addresses are constants.
+  auto ring = [&](auto&& body) {
+    int wi = 0;
+    uint32_t cw = sb[0];
+    int cur = next_block(wi, cw);
+    if (cur >= 0) stage(cur, 0);
+    while (cur >= 0) {
+      int nxt = next_block(wi, cw);
+      dma_sync();
+      if (nxt >= 0) stage(nxt, 1);
+      if (wave_live) body(cur, smem, smem + kTileBytes);
+      cur = nxt;
+      if (cur < 0) break;
+      nxt = next_block(wi, cw);
+      dma_sync();
+      if (nxt >= 0) stage(nxt, 0);
+      if (wave_live) body(cur, smem + 2 * kTileBytes, smem + 3 * kTileBytes);
+      cur = nxt;
+    }
+  };
+  // S^T and dP^T of one 32-key tile tt of the block in tiles tk (K), tv (V)
+  auto tile_sdp = [&](const unsigned char* tk, const unsigned char* tv, int tt, v16f& st, v16f& dp) {
     st = (v16f){};
     dp = (v16f){};
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      st = mfma(row_op(t, 32 * tt, 16 * s, lx), qb[s], st);
-      dp = mfma(row_op(t + kTileBytes, 32 * tt, 16 * s, lx), yb[s], dp);
+      st = mfma(ld_row(tk + 8192 * tt + ro[s]), qb[s], st);
+      dp = mfma(ld_row(tv + 8192 * tt + ro[s]), yb[s], dp);
     }
   };
 
   // pass 1, online per row: m = max of s * c2, l = sum of 2^(s c2 - m) and u = sum of 2^(s c2 - m) dP, both
   // rescaled when m grows; then LSE = m + log2(l) and D = u / l = sum_j P_ij dP_ij
   float m = -INFINITY, lsum = 0.f, usum = 0.f;
-  {
-    int wi = 0;
-    uint32_t cw = sb[0];
-    int cur = next_block(wi, cw), slot = 0;
-    if (cur >= 0) stage(cur, 0);
-    while (cur >= 0) {
-      const int nxt = next_block(wi, cw);
-      dma_sync();
-      if (nxt >= 0) stage(nxt, slot ^ 1);
-      if (wave_live) {
-        const unsigned char* t = smem + slot * 2 * kTileBytes;
-        const int nv = min(64, N - cur * 64);
-        int lx = l;
-        asm volatile("" : "+v"(lx));
+  ring([&](int J, const unsigned char* tk, const unsigned char* tv) {
+    const int nv = min(64, N - J * 64);
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          v16f st, dp;
-          tile_sdp(t, tt, lx, st, dp);
-          float bm = -INFINITY;
+    for (int tt = 0; tt < 2; ++tt) {
+      v16f st, dp;
+      tile_sdp(tk, tv, tt, st, dp);
+      // keys past nv (rows re-read from the last valid key) are excluded by selects, not branches
+      float bm = -INFINITY;
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (32 * tt + acc_row(r) < nv) bm = fmaxf(bm, st[r] * c2);
-          bm = fmaxf(bm, swap_halves_f32(bm));
-          const float mn = fmaxf(m, bm);
-          float ps = 0.f, pu = 0.f;
-          if (mn != -INFINITY) {
+      for (int r = 0; r < 16; ++r) bm = fmaxf(bm, 32 * tt + acc_row(r) < nv ? st[r] * c2 : -INFINITY);
+      bm = fmaxf(bm, swap_halves_f32(bm));
+      const float mn = fmaxf(m, bm);
+      float ps = 0.f, pu = 0.f;
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-              if (32 * tt + acc_row(r) < nv) {
-                const float e = __builtin_amdgcn_exp2f(st[r] * c2 - mn);
-                ps += e;
-                pu = fmaf(e, dp[r], pu);
-              }
-          }
-          ps += swap_halves_f32(ps);
-          pu += swap_halves_f32(pu);
-          const float sc = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mn);
-          lsum = lsum * sc + ps;
-          usum = usum * sc + pu;
-          m = mn;
-        }
+      for (int r = 0; r < 16; ++r) {
+        const float e = __builtin_amdgcn_exp2f(fmaf(st[r], c2, -mn));
+        const float ev = 32 * tt + acc_row(r) < nv ? e : 0.f;
+        ps += ev;
+        pu = fmaf(ev, dp[r], pu);
       }
-      cur = nxt;
-      slot ^= 1;
+      ps += swap_halves_f32(ps);
+      pu += swap_halves_f32(pu);
+      const float sc = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mn);
+      lsum = lsum * sc + ps;
+      usum = usum * sc + pu;
+      m = mn;
     }
-  }
+  });
   const float lse = (lsum > 0.f) ? m + __log2f(lsum) : 0.f;  // no selected key: every P is 0 below
   const float dsum = (lsum > 0.f) ? usum / lsum : 0.f;
   if (wave_live && l < 32 && i_loc < nq) {
@@ -260,47 +301,34 @@ __global__ __launch_bounds__(256, 2) void kb_q(const uint16_t* __restrict__ q, c
   v16f acc[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) acc[u] = (v16f){};
-  {
-    int wi = 0;
-    uint32_t cw = sb[0];
-    int cur = next_block(wi, cw), slot = 0;
-    __syncthreads();  // pass 1's reads of both slots are done
-    if (cur >= 0) stage(cur, 0);
-    while (cur >= 0) {
-      const int nxt = next_block(wi, cw);
-      dma_sync();
-      if (nxt >= 0) stage(nxt, slot ^ 1);
-      if (wave_live) {
-        const unsigned char* t = smem + slot * 2 * kTileBytes;
-        const int nv = min(64, N - cur * 64);
-        int lx = l;
-        asm volatile("" : "+v"(lx));
+  __syncthreads();  // pass 1's reads of both slots are done
+  ring([&](int J, const unsigned char* tk, const unsigned char* tv) {
+    const int nv = min(64, N - J * 64);
+    const float nl2 = -lse;
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          v16f st, dp;
-          tile_sdp(t, tt, lx, st, dp);
+    for (int tt = 0; tt < 2; ++tt) {
+      v16f st, dp;
+      tile_sdp(tk, tv, tt, st, dp);
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float p = (32 * tt + acc_row(r) < nv) ? __builtin_amdgcn_exp2f(st[r] * c2 - lse) : 0.f;
-            st[r] = p * (dp[r] - dsum);
-          }
+      for (int r = 0; r < 16; ++r) {
+        const float e = __builtin_amdgcn_exp2f(fmaf(st[r], c2, nl2));
+        const float p = 32 * tt + acc_row(r) < nv ? e : 0.f;
+        st[r] = p * (dp[r] - dsum);
+      }
 #pragma unroll
-          for (int s = 0; s < 2; ++s) {
-            v8bf hi, lo;
-            split8(st, s, hi, lo);
+      for (int s = 0; s < 2; ++s) {
+        v8bf hi, lo;
+        split8(st, s, hi, lo);
+        const unsigned char* rb = tk + 8192 * tt + 4096 * s;
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-              const v8bf a = tr_op(t, 32 * tt + 16 * s, 32 * u, lx);
-              acc[u] = mfma(a, hi, acc[u]);
-              acc[u] = mfma(a, lo, acc[u]);
-            }
-          }
+        for (int u = 0; u < 4; ++u) {
+          const v8bf a = ld_tr(rb + to[u][0], rb + to[u][1]);
+          acc[u] = mfma(a, hi, acc[u]);
+          acc[u] = mfma(a, lo, acc[u]);
         }
       }
-      cur = nxt;
-      slot ^= 1;
     }
-  }
+  });
   // acc[u][r] = dQ^T[d = 32 u + acc_row(r)][i = i_loc] (unscaled)
   if (wave_live && i_loc < nq) {
     float* dst = dq + ((size_t)bh * N + r0 + i_loc) * kD;
@@ -346,6 +374,19 @@ __global__ __launch_bounds__(256, 2) void kb_kv(const uint16_t* __restrict__ q, 
   load(head_rsrc(k + (size_t)bh * N * kD, N), J * 64, nk, sK);
   load(head_rsrc(v + (size_t)bh * N * kD, N), J * 64, nk, sV);
   const int j_loc = 32 * kt + (l & 31);
+  // lane parts of the tile addresses (the wave's row chunk folded in), kept opaque so that the compiler holds
+  // three registers rather than one address per read. Row reads of k-step sd use the lane part of step 0 with
+  // bits 5-7 flipped by sd; the transposed reads of column tile u the lane part of tile 0 with bits 6-7 flipped
+  // by u (no other bit of a lane part reaches those bits). The K and V rows of the wave's key tile are the Q and
+  // dY lane parts shifted by the wave-uniform 8192 (kt - ch).
+  uint32_t oq = row_lane_off(l, 0) + 8192u * ch, tq[2];
+  asm volatile("" : "+v"(oq));
+  const int dkv = 8192 * (kt - ch);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    tq[h] = tr_lane_off(l, 0, h) + 8192u * ch;
+    asm volatile("" : "+v"(tq[h]));
+  }
   v16f accv[4], acck[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) accv[u] = acck[u] = (v16f){};
@@ -367,23 +408,21 @@ __global__ __launch_bounds__(256, 2) void kb_kv(const uint16_t* __restrict__ q, 
           sDd[ii] = ii < nh ? d_in[(size_t)bh * N + q0 + h0 + ii] : 0.f;
         }
         dma_sync();
-        // the lane index goes through an opaque copy each half, so that the tile addresses derived from it are
-        // recomputed where they are used instead of being held in registers across the loop
-        int lx = l;
-        asm volatile("" : "+v"(lx));
         v16f s = (v16f){}, dp = (v16f){};
 #pragma unroll
         for (int sd = 0; sd < 8; ++sd) {
-          s = mfma(row_op(sQ, 32 * ch, 16 * sd, lx), row_op(sK, 32 * kt, 16 * sd, lx), s);
-          dp = mfma(row_op(sdY, 32 * ch, 16 * sd, lx), row_op(sV, 32 * kt, 16 * sd, lx), dp);
+          const uint32_t o = oq ^ (32u * sd), okv = o + dkv;
+          s = mfma(ld_row(sQ + o), ld_row(sK + okv), s);
+          dp = mfma(ld_row(sdY + o), ld_row(sV + okv), dp);
         }
         // s[r] -> P, dp[r] -> dS for row 32 ch + acc_row(r) and key j_loc (the fences keep the row statistics'
         // reads and the transposed operand reads from being hoisted while every accumulator is live)
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int ii = 32 * ch + acc_row(r);
-          const float p = ii < nh ? __builtin_amdgcn_exp2f(s[r] * c2 - sL[ii]) : 0.f;
+          const int ii = 32 * ch + acc_row(r);  // < 64: the row statistics are read unconditionally
+          const float e = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -sL[ii]));
+          const float p = ii < nh ? e : 0.f;
           dp[r] = p * (dp[r] - sDd[ii]);
           s[r] = p;
         }
@@ -395,10 +434,11 @@ __global__ __launch_bounds__(256, 2) void kb_kv(const uint16_t* __restrict__ q, 
           split8(dp, st, dh, dl);
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
-            const v8bf ay = tr_op(sdY, 32 * ch + 16 * st, 32 * u, lx);
+            const uint32_t t0 = tq[0] ^ (64u * u), t1 = tq[1] ^ (64u * u);
+            const v8bf ay = ld_tr(sdY + 4096 * st + t0, sdY + 4096 * st + t1);
             accv[u] = mfma(ay, ph, accv[u]);
             accv[u] = mfma(ay, pl, accv[u]);
-            const v8bf aq = tr_op(sQ, 32 * ch + 16 * st, 32 * u, lx);
+            const v8bf aq = ld_tr(sQ + 4096 * st + t0, sQ + 4096 * st + t1);
             acck[u] = mfma(aq, dh, acck[u]);
             acck[u] = mfma(aq, dl, acck[u]);
           }

@@ -347,6 +347,7 @@ size_t plan_backward(const Plan& pl, unsigned char* ws, BwdPlan* b) {
     b->keep_t = (uint32_t*)take(BH * (size_t)((pl.n_qb + 31) / 32) * mask_row_pad(pl.n_kb) * sizeof(uint32_t));
     b->dhj = (float*)take(BH * pl.n_kb * (size_t)kStateX * sizeof(float));
     b->dw_part = (float*)take(BH * backward_dw_chunks(pl.N) * kD * kD * sizeof(float));
+    b->dw_seg = (float*)take(backward_dw_segments() * kD * kD * sizeof(float));
   }
   return off;
 }

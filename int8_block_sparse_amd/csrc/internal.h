@@ -79,10 +79,12 @@ struct BwdPlan {
   uint32_t* keep_t;                // [BH][ceil(n_qb/32)][mask_row_pad(n_kb)]: bit I of key block J = I did not select J
   float* dhj;                      // [BH][n_kb] records: dH_J as bf16 hi and lo planes (row c), then dZ_J fp32
   float* dw_part;                  // [BH][n_chunks][D][D]
+  float* dw_seg;                   // [backward_dw_segments()][D][D]
 };
 hipError_t launch_backward_sparse(const BwdPlan& b, hipStream_t s);
 hipError_t launch_backward_linear(const BwdPlan& b, hipStream_t s);
 size_t backward_dw_chunks(int N);
+size_t backward_dw_segments();
 // fills (graph-capture friendly replacements for memset)
 hipError_t launch_fill_f32(float* dst, size_t n, float val, hipStream_t s);
 // dynamic LDS of the kernels that size it at run time

@@ -18,7 +18,8 @@
 //   kb_keep_t  the keep mask transposed; dH_J, dZ_J = the sums of dH_m, dZ_m over the query blocks that did not
 //              select J, as the forward's dense mask x table product (k4_gemm, bf16 hi + lo MFMA)
 //   kb_lin_k   per key block: dK += (V dH_J^T + dZ_J) * phi'(k), dV += phi(K) dH_J (bf16 MFMA, hi + lo)
-//   kb_dw      dW_p = sum over all rows of O_l^T dY (per-chunk partials, then a fixed-order sum)
+//   kb_dw      dW_p = sum over all rows of O_l^T dY (bf16 MFMA, O_l as hi + lo; per-chunk partials, then a
+//              fixed-order sum in segments)
 // Every sum has a fixed order; no atomics touch floating-point data.
 #include "device_common.h"
 #include "internal.h"
@@ -484,41 +485,6 @@ __global__ __launch_bounds__(256, 2) void kb_kv(const uint16_t* __restrict__ q, 
   }
 }
 
-// ---------------------------------------------------------------------------------------------------------
-// fp32 VALU tile products for the linear branch: C[M][128] (+)= A[M][K] B[K][128], A and B in LDS with arbitrary
-// strides (so transposed operands are read in place). 256 threads: thread (ty = t / 16, tx = t % 16) computes rows
-// ty + 16 a (a < M / 16) and columns tx + 16 b (b < 8).
-// ---------------------------------------------------------------------------------------------------------
-template <int M>
-struct VTile {
-  float c[M / 16][8];
-};
-
-template <int M>
-__device__ __forceinline__ void vgemm(VTile<M>& C, const float* A, int a_r, int a_k, const float* B, int b_k, int b_c,
-                                      int K) {
-  const int t = threadIdx.x, ty = t >> 4, tx = t & 15;
-  for (int kk = 0; kk < K; ++kk) {
-    float av[M / 16], bv[8];
-#pragma unroll
-    for (int a = 0; a < M / 16; ++a) av[a] = A[(ty + 16 * a) * a_r + kk * a_k];
-#pragma unroll
-    for (int b = 0; b < 8; ++b) bv[b] = B[kk * b_k + (tx + 16 * b) * b_c];
-#pragma unroll
-    for (int a = 0; a < M / 16; ++a)
-#pragma unroll
-      for (int b = 0; b < 8; ++b) C.c[a][b] = fmaf(av[a], bv[b], C.c[a][b]);
-  }
-}
-
-template <int M>
-__device__ __forceinline__ void vzero(VTile<M>& C) {
-#pragma unroll
-  for (int a = 0; a < M / 16; ++a)
-#pragma unroll
-    for (int b = 0; b < 8; ++b) C.c[a][b] = 0.f;
-}
-
 __device__ __forceinline__ float dphi(float x) { return x > 0.f ? 1.f : __builtin_amdgcn_exp2f(x * kLog2e); }
 
 // ---------------------------------------------------------------------------------------------------------
@@ -838,42 +804,77 @@ __global__ __launch_bounds__(512) void kb_lin_k(const uint16_t* __restrict__ k, 
 }
 
 // ---------------------------------------------------------------------------------------------------------
-// kb_dw: grid (n_chunks, BH), 256 threads: partial [c][e] = sum over the chunk's rows i of O_l[i][c] dY[i][e]
-// (rows in ascending order); kb_dw_sum: dW_p = the partials added in (bh, chunk) order.
+// kb_dw: grid (n_chunks, BH), 256 threads (4 waves): partial [e][f] = sum over the chunk's rows i of
+// O_l[i][e] dY[i][f] on bf16 MFMA, O_l as hi + lo. Steps of 64 rows: O_l (hi, lo) and dY are staged as swizzled
+// tiles; A = O_l^T and B = dY^T come from transposing reads (contraction over the rows, in row order). Wave w
+// owns output rows e of tile w and all columns f. kb_dw_sum1 / kb_dw_sum2: dW_p = the partials added in
+// (bh, chunk) order, in kDwSeg segments and then over the segments.
 // ---------------------------------------------------------------------------------------------------------
 constexpr int kDwChunk = 1024;
+constexpr int kDwSeg = 64;
 
 __global__ __launch_bounds__(256) void kb_dw(const float* __restrict__ o_l, const uint16_t* __restrict__ dy,
                                              float* __restrict__ part, int N, int n_chunks) {
-  __shared__ float sO[32][kD], sY[32][kD];
-  const int ch = blockIdx.x, bh = blockIdx.y, t = threadIdx.x, ty = t >> 4, tx = t & 15;
+  __shared__ __align__(1024) unsigned char sOh[kTileBytes], sOl[kTileBytes], sY[kTileBytes];
+  const int ch = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6), l = t & 63;
   const int i0 = ch * kDwChunk, i1 = min(N, i0 + kDwChunk);
-  VTile<128> acc;
-  vzero(acc);
-  for (int s0 = i0; s0 < i1; s0 += 32) {
-    const int ns = min(32, i1 - s0);
-    __syncthreads();
-    for (int u = t; u < 32 * kD; u += 256) {
-      const int ii = u >> 7, c = u & 127;
-      const bool ok = ii < ns;
-      sO[ii][c] = ok ? o_l[((size_t)bh * N + s0 + ii) * kD + c] : 0.f;
-      sY[ii][c] = ok ? bf16_lo(dy[((size_t)bh * N + s0 + ii) * kD + c]) : 0.f;
+  v16f acc[4];
+#pragma unroll
+  for (int ft = 0; ft < 4; ++ft) acc[ft] = (v16f){};
+  for (int s0 = i0; s0 < i1; s0 += 64) {
+    const int ns = min(64, i1 - s0);
+    __syncthreads();  // the previous step's tiles are no longer read
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {  // O_l: 64 rows x 32 groups of 4 columns
+      const int u = t + 256 * it, row = u >> 5, c4 = 4 * (u & 31);
+      float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (row < ns) x = *(const float4*)(o_l + ((size_t)bh * N + s0 + row) * kD + c4);
+      const uint32_t h0 = pack_bf16x2(x.x, x.y), h1 = pack_bf16x2(x.z, x.w);
+      const uint32_t q0 = pack_bf16x2(x.x - __uint_as_float(h0 << 16), x.y - __uint_as_float(h0 & 0xffff0000u));
+      const uint32_t q1 = pack_bf16x2(x.z - __uint_as_float(h1 << 16), x.w - __uint_as_float(h1 & 0xffff0000u));
+      *(uint2*)(sOh + toff(row, c4)) = make_uint2(h0, h1);
+      *(uint2*)(sOl + toff(row, c4)) = make_uint2(q0, q1);
+    }
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {  // dY: 64 rows x 16 chunks of 8 columns
+      const int u = t + 256 * it, row = u >> 4, c8 = 8 * (u & 15);
+      uint4 x = make_uint4(0, 0, 0, 0);
+      if (row < ns) x = *(const uint4*)(dy + ((size_t)bh * N + s0 + row) * kD + c8);
+      *(uint4*)(sY + toff(row, c8)) = x;
     }
     __syncthreads();
-    vgemm(acc, &sO[0][0], 1, kD, &sY[0][0], kD, 1, 32);  // A[row = c][kk = i] = O_l[i][c]; B[kk = i][col = e]
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const v8bf ah = tr_op<false>(sOh, 16 * k, 32 * w, l), al = tr_op<false>(sOl, 16 * k, 32 * w, l);
+#pragma unroll
+      for (int ft = 0; ft < 4; ++ft) {
+        const v8bf by = tr_op<false>(sY, 16 * k, 32 * ft, l);
+        acc[ft] = mfma(ah, by, acc[ft]);
+        acc[ft] = mfma(al, by, acc[ft]);
+      }
+    }
   }
+  // acc[ft][r] = partial[e = 32 w + acc_row(r)][f = 32 ft + l % 32]
   float* out = part + ((size_t)bh * n_chunks + ch) * kD * kD;
 #pragma unroll
-  for (int a = 0; a < 8; ++a)
+  for (int ft = 0; ft < 4; ++ft)
 #pragma unroll
-    for (int b = 0; b < 8; ++b) out[(ty + 16 * a) * kD + tx + 16 * b] = acc.c[a][b];
+    for (int r = 0; r < 16; ++r) out[(32 * w + acc_row(r)) * kD + 32 * ft + (l & 31)] = acc[ft][r];
 }
 
-__global__ __launch_bounds__(256) void kb_dw_sum(const float* __restrict__ part, float* __restrict__ dw, int n_parts) {
-  const int x = blockIdx.x * 256 + threadIdx.x;
-  if (x >= kD * kD) return;
+__global__ __launch_bounds__(256) void kb_dw_sum1(const float* __restrict__ part, float* __restrict__ seg, int n_parts) {
+  const int x = blockIdx.x * 256 + threadIdx.x, sg = blockIdx.y;
+  const int per = (n_parts + kDwSeg - 1) / kDwSeg, p0 = sg * per, p1 = min(n_parts, p0 + per);
   float s = 0.f;
-  for (int p = 0; p < n_parts; ++p) s += part[(size_t)p * kD * kD + x];
+  for (int p = p0; p < p1; ++p) s += part[(size_t)p * kD * kD + x];
+  seg[(size_t)sg * kD * kD + x] = s;
+}
+
+__global__ __launch_bounds__(256) void kb_dw_sum2(const float* __restrict__ seg, float* __restrict__ dw) {
+  const int x = blockIdx.x * 256 + threadIdx.x;
+  float s = 0.f;
+  for (int sg = 0; sg < kDwSeg; ++sg) s += seg[(size_t)sg * kD * kD + x];
   dw[x] = s;
 }
 
@@ -934,10 +935,13 @@ hipError_t launch_backward_linear(const BwdPlan& b, hipStream_t s) {
   const int n_chunks = (p.N + kDwChunk - 1) / kDwChunk;
   hipLaunchKernelGGL(kb_dw, dim3(n_chunks, p.BH), dim3(256), 0, s, b.o_l, b.dy, b.dw_part, p.N, n_chunks);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(kb_dw_sum, dim3(kD * kD / 256), dim3(256), 0, s, b.dw_part, b.dw, p.BH * n_chunks);
+  hipLaunchKernelGGL(kb_dw_sum1, dim3(kD * kD / 256, kDwSeg), dim3(256), 0, s, b.dw_part, b.dw_seg, p.BH * n_chunks);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(kb_dw_sum2, dim3(kD * kD / 256), dim3(256), 0, s, b.dw_seg, b.dw);
   return hipGetLastError();
 }
 
 size_t backward_dw_chunks(int N) { return (size_t)(N + kDwChunk - 1) / kDwChunk; }
+size_t backward_dw_segments() { return kDwSeg; }
 
 }  // namespace sagesla

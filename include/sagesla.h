@@ -148,8 +148,9 @@ sagesla_status sagesla_forward(const void* q, const void* k, const void* v, void
    the selection in block_idx (required when topk > 0; each row's blocks are a set: order and repeats do not
    matter). dout: bf16 [B][H][N][D] = dL/d(out). Writes dq, dk, dv: fp32 [B][H][N][D], and with SAGESLA_LINEAR
    dw_proj: fp32 [D][D], dL/dW_p summed over every (b, h) (zeros when every block is selected). Accumulation is
-   fp32 in a fixed order (deterministic); the score products run on bf16 MFMA with P and dS split into bf16
-   hi + lo pairs, the linear branch on fp32 vector arithmetic from the forward's remaining state (bf16 hi + lo).
+   fp32 in a fixed order (deterministic); every product runs on bf16 MFMA with each operand that is not exactly
+   bf16 (P, dS, phi of q and k, the linear branch's states and intermediates) split into bf16 hi + lo pairs; the
+   linear branch starts from the forward's remaining state (bf16 hi + lo).
    SAGESLA_QK_RMSNORM is not differentiated (SAGESLA_E_UNSUPPORTED); SAGESLA_SMOOTH_K and SAGESLA_QUANT_GROUP32
    do not change the result. The workspace must hold sagesla_backward_workspace_bytes(p) bytes. */
 size_t sagesla_backward_workspace_bytes(const sagesla_params* p);

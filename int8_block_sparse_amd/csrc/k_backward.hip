@@ -7,11 +7,12 @@
 // shift, which leaves every softmax row unchanged, drops out.
 //
 // Sparse branch (bf16 MFMA, fp32 accumulation; P and dS enter the products as bf16 hi + lo pairs):
-//   kb_sel     bitmap [BH][n_kb][ceil(n_qb/32)]: bit I of key block J = J is selected by query block I
+//   kb_sel     bitmaps of the selection: [BH][n_kb][ceil(n_qb/32)] (bit I of key block J = I selected J) and
+//              [BH][n_qb][ceil(n_kb/32)] (bit J of query block I)
 //   kb_q       per query block: pass 1 the log-sum-exp of every row (base 2) and D_i = sum_j P_ij dP_ij, both
 //              online; pass 2 dS = P (dP - D) and dQ = dS K sm_scale; writes LSE, D and dQ
 //   kb_kv      per key block, over the query blocks that selected it: dV = P^T dY, dK = dS^T Q sm_scale
-// Linear branch (fp32 VALU tiles), after the forward's remaining-state product (H_m, Z_m per query block):
+// Linear branch (bf16 MFMA, hi + lo splits), after the forward's remaining-state product (H_m, Z_m per query block):
 //   kb_lin_q   per query block (bf16 MFMA, hi + lo): O_l, dO_l = dY W_p^T, dnum = dO_l / den,
 //              dden = -(dO_l . O_l) / den, dQ += (dnum H_m^T + dden Z_m) * phi'(q), and the block's
 //              dH_m = phi(Q)^T dnum, dZ_m = phi(Q)^T dden

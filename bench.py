@@ -14,6 +14,12 @@ The second workload, the W8A8 block-quantized linear layer ("Turbo Diffusion", l
 measured with --workload w8a8-<shape> (shapes: the synth module's LINEAR_WORKLOADS, e.g. w8a8-wan14b-720p-proj):
 a step is one whole layer (activation quantization, then the block-scaled INT8 product with the pre-quantized
 weights) and the line carries the product kernel's roofline.
+
+--workload sla-backward times sagesla_backward (SLA is trainable, §三(二)) on the same 720P pair for the
+forward's own selection; a step is one whole backward (every kernel of it).
+
+The headline line also reports a cold variant: the median forward time when a 512 MiB device fill (twice the
+Infinity Cache) precedes each forward.
 """
 from __future__ import annotations
 
@@ -116,6 +122,36 @@ def cpu_baseline_w8a8(x, w, bias, wl, rows, budget_s=30.0):
     del np
     return {"value": done * 2.0 * wl.N * wl.K / dt / 1e12, "unit": "TOPS (2*M*N*K per layer)", "cores": int(cores),
             "kind": "oracle", "sample": f"{done} of {wl.M} tokens (whole 128-token blocks), all {wl.N} outputs",
+            "seconds": round(dt, 2)}
+
+
+def cpu_baseline_backward(q, k, v, w, dy, sel, wl, budget_s=20.0):
+    """The fp64 backward oracle (unchanged, untuned) on whole query blocks of head (0, 0): the dQ rows of each
+    block through that block's forward (its selected blocks and its linear branch); TFLOP/s counted like the
+    GPU line (the five sparse-branch products of the block's selected pairs)."""
+    from oracle import sla_backward as ob
+    cores = len(os.sched_getaffinity(0))
+    try:
+        import torch
+        cores = torch.get_num_threads()
+    except Exception:  # noqa: BLE001
+        pass
+    f = lambda t: t.float().cpu().double().numpy()
+    Q, K, V, W, dY = f(q[0, 0]), f(k[0, 0]), f(v[0, 0]), f(w), f(dy[0, 0])
+    idx = sel[0, 0].cpu().numpy()
+    done, t0 = 0, time.perf_counter()
+    while done < wl.n_qb:
+        ob.dq_blocks(Q, K, V, W, idx, dY, wl.blk_q, wl.blk_k, [done], linear=wl.linear)
+        done += 1
+        log(f"cpu baseline: query block {done} at {time.perf_counter() - t0:.1f} s")
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    flops = done * wl.topk * 5 * 2.0 * wl.blk_q * wl.blk_k * wl.D
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s (5 products of 2*bq*bk*D per selected block pair)",
+            "cores": int(cores), "kind": "oracle",
+            "sample": f"dQ rows of {done} whole query blocks of head (0, 0) (each through its own forward, the linear "
+                      f"branch included, which dominates the oracle's time)",
             "seconds": round(dt, 2)}
 
 
@@ -255,6 +291,8 @@ def main_backward(args):
                      "traffic": None, "avg_launch_ms": round(ms_ev, 4), "flops_per_step": flops},
         "cpu_baseline": None,
     }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_backward(q, k, v, w, dy, mask, wl)
     print(json.dumps(result), flush=True)
 
 
@@ -312,6 +350,23 @@ def main():
     st_avg = {name: sum(s[name] for s in stages) / len(stages) for name in sg.STAGES}
     log(f"{ms:.3f} ms/layer; stages (ms): " + ", ".join(f"{n} {t:.3f}" for n, t in st_avg.items()))
 
+    # cold variant: before each forward a 512 MiB device fill (twice the Infinity Cache) evicts the inputs and
+    # intermediates from every cache; only the forward is timed (events on the current stream)
+    scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    cold = []
+    for i in range(args.steps):
+        scrub.fill_(i & 0xFF)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fwd()
+        e1.record()
+        cold.append((e0, e1))
+    torch.cuda.synchronize()
+    cold_ms = sorted(a.elapsed_time(b) for a, b in cold)
+    cold_med = cold_ms[len(cold_ms) // 2]
+    del scrub
+    log(f"cold (caches scrubbed before each forward): median {cold_med:.3f} ms/layer")
+
     if args.calib_copy_mib:
         n = args.calib_copy_mib << 20
         a = torch.empty(n, dtype=torch.uint8, device=dev)
@@ -348,6 +403,7 @@ def main():
                    "blk_q": wl.blk_q, "blk_k": wl.blk_k, "topk_frac": wl.topk_frac, "topk": wl.topk,
                    "linear": wl.linear, "parallelism": "single GPU"},
         "stages_ms": {n: round(t, 4) for n, t in st_avg.items()},
+        "cold_ms_per_step": round(cold_med, 4),
         "roofline": {
             "kernel": "k3_attn (block-sparse INT8 attention + linear-branch epilogue)",
             "bound": "mfma",

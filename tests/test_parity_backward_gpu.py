@@ -108,6 +108,54 @@ def test_backward_deterministic():
 
 
 # ---------------------------------------------------------------------------------------------------------
+# degenerate shapes and inputs
+# ---------------------------------------------------------------------------------------------------------
+def run(wl, topk, seed=0, linear=True, zero_dy=False):
+    q, k, v, w = synth.make(wl, seed)
+    dy = torch.randn(q.shape, generator=torch.Generator().manual_seed(seed + 11)).to(torch.bfloat16)
+    if zero_dy:
+        dy.zero_()
+    mask = make_mask(wl, topk, seed)
+    say(f"case {wl.name} B{wl.B} H{wl.H} N{wl.N} bq{wl.blk_q} topk{topk} linear{linear} zero_dy{zero_dy}")
+    got = sg.backward(q.cuda(), k.cuda(), v.cuda(), w.cuda(), dy.cuda(), torch.from_numpy(mask).cuda(), topk=topk,
+                      blk_q=wl.blk_q, blk_k=wl.blk_k, linear=linear)
+    torch.cuda.synchronize()
+    return (q, k, v, w, dy, mask), got
+
+
+def test_backward_single_token():
+    # one token: its only key gets P = 1, so dS = 0 (dQ = dK = 0 up to the rounding of LSE and D) and dV = dY;
+    # every block is selected, so the linear branch and dW_p vanish
+    wl = synth.custom(1, 2, 1, blk_q=64, topk_frac=1.0)
+    (q, k, v, w, dy, mask), (dq, dk, dv, dw) = run(wl, 1)
+    bound = 1e-5 * float(torch.abs(dy.float()).max()) * float(torch.abs(torch.cat([k, v]).float()).max())
+    assert float(torch.abs(dq).max()) <= bound and float(torch.abs(dk).max()) <= bound
+    np.testing.assert_array_equal(to_np(dv), to_np(dy))
+    assert not to_np(dw).any()
+
+
+@pytest.mark.parametrize("N,bq,topk", [(40, 128, 1), (40, 64, 0), (129, 64, 1), (129, 128, 2)])
+def test_backward_tiny_and_one_row_tails(N, bq, topk):
+    # fewer tokens than one key block, and tails of a single row in both block kinds
+    wl = synth.custom(1, 2, N, blk_q=bq, topk_frac=0.5)
+    case(wl, topk, seed=N)
+
+
+def test_backward_zero_dy_gives_zero_gradients():
+    _, (dq, dk, dv, dw) = run(SMALL["ragged128"], 3, zero_dy=True)
+    for g in (dq, dk, dv, dw):
+        assert not to_np(g).any()
+
+
+def test_backward_no_branch_gives_zero_gradients():
+    # no block selected and no linear branch: the output is identically zero
+    _, (dq, dk, dv, dw) = run(SMALL["ragged64"], 0, linear=False)
+    for g in (dq, dk, dv):
+        assert not to_np(g).any()
+    assert dw is None
+
+
+# ---------------------------------------------------------------------------------------------------------
 # the 720P layer at full size, with the forward's own selection: exact dQ rows on sampled query blocks of two
 # heads; with the linear branch off, the invariants of softmax attention (sum_j dK_j = 0 because every row of dS
 # sums to zero; sum_j dV_j = sum_i dY_i because every row of P sums to one)

@@ -136,6 +136,29 @@ def test_tensor_pointer_validation(lib):
     assert lib.sagesla_last_hip_error() == 0
 
 
+def bwd(lib, p, dq=FAKE, dk=FAKE, dv=FAKE, dw=FAKE, q=FAKE):
+    return lib.sagesla_backward(q, FAKE, FAKE, FAKE, dq, dk, dv, dw, ctypes.byref(p), None)
+
+
+@cpu_only
+def test_backward_validation(lib):
+    ok = dict(block_idx=FAKE)
+    need = lib.sagesla_backward_workspace_bytes(ctypes.byref(good(**ok)))
+    assert need > lib.sagesla_workspace_bytes(ctypes.byref(good(**ok)))  # the forward plan plus the backward's
+    assert bwd(lib, good()) == 1                       # topk > 0 without a selection
+    assert bwd(lib, good(**ok), dq=None) == 1
+    assert bwd(lib, good(**ok), q=None) == 1
+    assert bwd(lib, good(**ok), dw=None) == 1          # the linear branch needs dW_p
+    assert bwd(lib, good(**ok), dk=FAKE + 4) == 5
+    assert bwd(lib, good(workspace_bytes=need - 1, **ok)) == 4
+    assert bwd(lib, good(workspace=FAKE + 16, **ok)) == 5
+    norm = good(flags=sg.LINEAR | sg.QK_RMSNORM, q_norm_w=FAKE, k_norm_w=FAKE, norm_eps=1e-6, **ok)
+    assert bwd(lib, norm) == 3                         # the norm is not differentiated
+    assert lib.sagesla_backward_workspace_bytes(ctypes.byref(norm)) == 0
+    assert bwd(lib, good(D=64, **ok)) == 3
+    assert lib.sagesla_last_hip_error() == 0
+
+
 def test_workspace_bytes(lib):
     cfg = sg.Config(B=2, H=40, N=75600, blk_q=128, blk_k=64, topk=118, linear=True)
     n = lib.sagesla_workspace_bytes(ctypes.byref(cfg.params()))

@@ -356,8 +356,8 @@ __global__ __launch_bounds__(256, 2) void kb_kv(const uint16_t* __restrict__ q, 
                                                 const uint16_t* __restrict__ v, const uint16_t* __restrict__ dy,
                                                 const uint32_t* __restrict__ bits, const float* __restrict__ lse_in,
                                                 const float* __restrict__ d_in, float* __restrict__ dk,
-                                                float* __restrict__ dv, int N, int n_qb, int n_kb, int n_qbw,
-                                                int blk_q, float sm_scale) {
+                                                float* __restrict__ dv, int N, int n_kb, int n_qbw, int blk_q,
+                                                float sm_scale) {
   extern __shared__ __align__(1024) unsigned char smem[];
   unsigned char* sK = smem;
   unsigned char* sV = smem + kTileBytes;
@@ -911,7 +911,7 @@ hipError_t launch_backward_sparse(const BwdPlan& b, hipStream_t s) {
                      b.lse, b.dd, b.dq, p.N, p.n_qb, n_kbw, p.blk_q, p.sm_scale);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(kb_kv, dim3(p.n_kb, p.BH), dim3(256), kbkv_lds_bytes(), s, b.q, b.k, b.v, b.dy, b.sel_bits,
-                     b.lse, b.dd, b.dk, b.dv, p.N, p.n_qb, p.n_kb, n_qbw, p.blk_q, p.sm_scale);
+                     b.lse, b.dd, b.dk, b.dv, p.N, p.n_kb, n_qbw, p.blk_q, p.sm_scale);
   return hipGetLastError();
 }
 

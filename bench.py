@@ -71,6 +71,30 @@ def read_counters(path=COUNTERS, source=K3_SOURCE):
         return None
 
 
+MFMA_COUNTERS = os.path.join(ROOT, "profiles", "k3_attn_wan14b-720p-sla-pair_mfma_counters.txt")
+
+
+def read_mfma_util(path=MFMA_COUNTERS, source=K3_SOURCE):
+    """MFMA busy fraction of the attention kernel (busy cycles over active cycles, at the clock the box holds)
+    from its committed rocprofv3 counter summary, or None when absent or taken on a different kernel source."""
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ": " in line and not line.startswith("#"):
+            k, v = line.rsplit(": ", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get(f"{os.path.basename(source)} sha256[:16]") != source_sha(source):
+        return None
+    for k, v in kv.items():
+        if k.startswith("MfmaUtil"):
+            try:
+                return float(v)
+            except ValueError:
+                return None
+    return None
+
+
 def cpu_baseline(q, k, v, w, wl, heads, budget_s=30.0):
     """The fp64 oracle (unchanged, untuned) on whole heads of the same workload; dense-equivalent TOPS."""
     from oracle import sagesla as orc
@@ -412,6 +436,7 @@ def main():
             "unit": "TOPS (INT8-equivalent: INT8 ops + 2x BF16 flops)",
             "frac": round(int8_equiv / PEAK_INT8_TOPS, 4),
             "traffic": traffic,
+            "mfma_util_at_box_clock": read_mfma_util(),
             "avg_launch_ms": round(st_avg["attn"], 4),
             "ops_i8_per_launch": ops_i8,
             "flops_bf16_per_launch": ops_bf16,

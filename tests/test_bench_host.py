@@ -24,3 +24,15 @@ def test_committed_summaries_have_the_parsed_keys():
         text = open(path).read()
         assert f"{os.path.basename(source)} sha256[:16]: " in text
         assert "hbm bytes per launch (fetch+write, copy-calibrated): " in text
+
+
+def test_mfma_summary_parses_and_is_source_gated(tmp_path):
+    src = tmp_path / "k.hip"
+    src.write_text("// kernel\n")
+    f = tmp_path / "m.txt"
+    f.write_text(f"# a: b\nk.hip sha256[:16]: {bench.source_sha(str(src))}\n"
+                 "MfmaUtil (SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE per XCD x 1024 SIMDs)): 0.5552\n")
+    assert bench.read_mfma_util(str(f), str(src)) == 0.5552
+    src.write_text("// changed kernel\n")
+    assert bench.read_mfma_util(str(f), str(src)) is None
+    assert 0.0 < bench.read_mfma_util() <= 1.0  # the committed summary matches the committed kernel

@@ -1,0 +1,67 @@
+"""The entry points under HIP graph capture: sagesla_forward and sagesla_backward, captured once with caller-owned
+outputs and workspace, are replayed three times with eager work and synchronizations in between, and every replay
+must reproduce the eager result bit for bit (the library allocates nothing, clears with kernels rather than memset
+nodes, and is deterministic)."""
+import pytest
+import torch
+
+import int8_block_sparse_amd as sg
+import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def capture(fn):
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # one warm-up call off the capture, as torch recommends
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        res = fn()
+    return g, res
+
+
+def eager_noise():
+    x = torch.randn(1 << 20, device="cuda")
+    return float((x * x).sum())  # eager kernels and a synchronization between the replays
+
+
+def test_forward_replays():
+    wl = synth.custom(1, 2, 1000, blk_q=128, topk_frac=0.2)
+    q, k, v, w = (t.cuda() for t in synth.make(wl, 0))
+    cfg = sg.Config(wl.B, wl.H, wl.N, wl.D, wl.blk_q, wl.blk_k, wl.topk, wl.linear)
+    ws = torch.empty(sg.workspace_bytes(cfg), dtype=torch.uint8, device="cuda")
+    ref = sg.forward(q, k, v, w, topk=wl.topk, workspace=ws).clone()
+    out = torch.empty_like(q)
+    g, _ = capture(lambda: sg.forward(q, k, v, w, topk=wl.topk, out=out, workspace=ws))
+    for _ in range(3):
+        out.fill_(0)
+        eager_noise()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref)
+
+
+def test_backward_replays():
+    wl = synth.custom(1, 2, 1000, blk_q=128, topk_frac=0.2)
+    q, k, v, w = (t.cuda() for t in synth.make(wl, 1))
+    dy = torch.randn(q.shape, generator=torch.Generator().manual_seed(2)).to(torch.bfloat16).cuda()
+    _, ex = sg.forward(q, k, v, w, topk=wl.topk, export=True)
+    sel = ex["block_idx"][..., :wl.topk].contiguous()
+    cfg = sg.Config(wl.B, wl.H, wl.N, wl.D, wl.blk_q, wl.blk_k, wl.topk, wl.linear)
+    import ctypes
+    need = sg.load().sagesla_backward_workspace_bytes(ctypes.byref(cfg.params(w_proj=w.data_ptr())))
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    ref = [t.clone() for t in sg.backward(q, k, v, w, dy, sel, topk=wl.topk, workspace=ws)]
+    g, got = capture(lambda: sg.backward(q, k, v, w, dy, sel, topk=wl.topk, workspace=ws))
+    for _ in range(3):
+        for t in got:
+            t.fill_(0)
+        eager_noise()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(got, ref):
+            assert torch.equal(a, b)

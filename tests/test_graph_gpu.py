@@ -65,3 +65,20 @@ def test_backward_replays():
         torch.cuda.synchronize()
         for a, b in zip(got, ref):
             assert torch.equal(a, b)
+
+
+def test_w8a8_linear_replays():
+    import int8_block_sparse_amd.w8a8 as w8
+    wl = synth.LinearWorkload("graph", 300, 384, 640)
+    x, w, b = (t.cuda() for t in synth.make_linear(wl, 3))
+    wq, wsc = w8.quantize(w)
+    ws = torch.empty(w8.workspace_bytes(wl.M, wl.K), dtype=torch.uint8, device="cuda")
+    ref = w8.linear(x, wq, wsc, b, clip=0.9, workspace=ws).clone()
+    y = torch.empty_like(ref)
+    g, _ = capture(lambda: w8.linear(x, wq, wsc, b, clip=0.9, out=y, workspace=ws))
+    for _ in range(3):
+        y.fill_(0)
+        eager_noise()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, ref)

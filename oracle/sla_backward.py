@@ -17,6 +17,11 @@ with INT8 quantization passed straight through (the codes dequantize to the inpu
 dropped (it shifts every score of a row by the same amount, so no softmax row, and no gradient, changes).
 Given dY = dL/dF, the backward returns dQ, dK, dV of each head and dW_p summed over the heads (W_p is shared).
 
+With the RMSNorm of Q and K before the path ([TD-news] §三(四) item 2 point 1), the reading is the same
+straight-through one: the attention's gradient is taken at the normalized values the forward uses (Q-hat, K-hat
+after their bf16 roundings, which pass gradients unchanged), then through the float RMSNorm
+y_c = x_c r w_c (r = 1 / sqrt(mean over the token's H*D channels of x^2 + eps)) to the raw Q, K and the weights.
+
 The gradient is computed by torch's reverse-mode differentiation (fp64, CPU) of that forward written out
 plainly below, one query block at a time; the tests pin it against central finite differences of the same
 forward and, for the dense special case, against torch's scaled_dot_product_attention.
@@ -28,7 +33,7 @@ import math
 import numpy as np
 import torch
 
-__all__ = ["forward_float_head", "backward_head", "backward", "dq_blocks"]
+__all__ = ["forward_float_head", "backward_head", "backward", "dq_blocks", "rmsnorm_backward", "backward_with_norm"]
 
 
 def _blocks(n, blk):
@@ -125,3 +130,49 @@ def _linear_rows(Qb, K, V, W_p, sel, blk_k):
     Hm = phiK.T @ V[keys]
     Zm = phiK.sum(dim=0)
     return ((phiQ @ Hm) / (phiQ @ Zm)[:, None]) @ W_p
+
+
+def rmsnorm_backward(X, gamma, eps, dY):
+    """Backward of the RMSNorm before the path for one batch entry (straight-through roundings): X [H, N, D] raw
+    values, gamma [H*D] (index h*D + d), dY [H, N, D] = dL/d(normalized). Per token, with c over its n = H*D
+    channels and r = 1 / sqrt(sum_c x_c^2 / n + eps):
+        dL/dx_c = r w_c dy_c - x_c r^3 / n * sum_c' x_c' w_c' dy_c'
+        dL/dw_c = sum over the tokens of x_c r dy_c
+    (fp64). Returns (dX [H, N, D], dgamma [H*D])."""
+    X = np.asarray(X, np.float64)
+    H, N, D = X.shape
+    x = X.transpose(1, 0, 2).reshape(N, H * D)                 # token-major rows of n channels
+    dy = np.asarray(dY, np.float64).transpose(1, 0, 2).reshape(N, H * D)
+    w = np.asarray(gamma, np.float64).reshape(1, H * D)
+    n = float(H * D)
+    r = 1.0 / np.sqrt((x * x).sum(axis=1, keepdims=True) / n + float(np.float32(eps)))
+    s_ = (x * w * dy).sum(axis=1, keepdims=True)
+    dx = r * w * dy - x * (r ** 3) / n * s_
+    dw = (x * r * dy).sum(axis=0)
+    return dx.reshape(N, H, D).transpose(1, 0, 2), dw
+
+
+def backward_with_norm(q, k, v, w_p, idx, dy, blk_q, blk_k, gq, gk, eps, sm_scale=None, linear=True):
+    """The whole backward with the RMSNorm of Q and K before the path: q, k, v, dy [B, H, N, D] raw values,
+    gq, gk [H*D]. The attention part runs at the forward's normalized values (the oracle's qk_rmsnorm, the same
+    bf16 values the forward computes) and its dQ-hat, dK-hat pass through rmsnorm_backward. Returns (dq, dk, dv
+    as [B, H, N, D] arrays, dW_p, dgq, dgk), the weight gradients summed over the batch entries."""
+    from oracle.sagesla import qk_rmsnorm
+    q, k, v, dy = (np.asarray(a, np.float64) for a in (q, k, v, dy))
+    B, H, N, D = q.shape
+    qh = np.stack([qk_rmsnorm(q[b], gq, eps)[0] for b in range(B)])
+    kh = np.stack([qk_rmsnorm(k[b], gk, eps)[0] for b in range(B)])
+    dqh, dkh, dvd, dW = backward(qh, kh, v, w_p, idx, dy, blk_q, blk_k, sm_scale, linear)
+    dq, dk = np.zeros_like(q), np.zeros_like(k)
+    dv = np.zeros_like(v)
+    dgq, dgk = np.zeros(H * D), np.zeros(H * D)
+    for b in range(B):
+        gqh = np.stack([dqh[b, h] for h in range(H)])
+        gkh = np.stack([dkh[b, h] for h in range(H)])
+        dq[b], wq_ = rmsnorm_backward(q[b], gq, eps, gqh)
+        dk[b], wk_ = rmsnorm_backward(k[b], gk, eps, gkh)
+        dgq += wq_
+        dgk += wk_
+        for h in range(H):
+            dv[b, h] = dvd[b, h]
+    return dq, dk, dv, dW, dgq, dgk

@@ -99,3 +99,87 @@ def test_dq_blocks_equals_full_backward():
     part = ob.dq_blocks(Q, K, V, W, idx, dY, 64, 64, [0, 2, 5])
     for I, rows in part.items():
         np.testing.assert_allclose(rows, gQ[I * 64:min(330, I * 64 + 64)], rtol=1e-11, atol=1e-13)
+
+
+# ---------------------------------------------------------------------------------------------------------
+# the RMSNorm before the path: its backward pinned to torch's own rms_norm differentiated in fp64, and the
+# whole chain to central finite differences of the float forward through the float norm
+# ---------------------------------------------------------------------------------------------------------
+def test_rmsnorm_backward_matches_library_autograd():
+    import torch.nn.functional as F
+    rng = np.random.default_rng(5)
+    H, N, D = 3, 7, 128
+    X = rng.standard_normal((H, N, D)) * rng.uniform(0.2, 3.0, size=(1, N, 1))
+    g = 1.0 + 0.1 * rng.standard_normal(H * D)
+    dY = rng.standard_normal((H, N, D))
+    eps = 1e-6
+    dX, dg = ob.rmsnorm_backward(X, g, eps, dY)
+    x = torch.tensor(X.transpose(1, 0, 2).reshape(N, H * D), dtype=torch.float64, requires_grad=True)
+    w = torch.tensor(g, dtype=torch.float64, requires_grad=True)
+    y = F.rms_norm(x, (H * D,), weight=w, eps=float(np.float32(eps)))
+    (y * torch.tensor(dY.transpose(1, 0, 2).reshape(N, H * D))).sum().backward()
+    np.testing.assert_allclose(dX, x.grad.numpy().reshape(N, H, D).transpose(1, 0, 2), rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(dg, w.grad.numpy(), rtol=1e-11, atol=1e-13)
+
+
+def test_backward_with_norm_finite_differences():
+    # a float chain without roundings: the oracle's norm step is replaced by the float norm, so the straight-
+    # through gradient equals the exact derivative of the composed float function
+    import oracle.sagesla as osg
+    from types import SimpleNamespace
+    wl = SimpleNamespace(H=2, N=150, D=128, blk_q=64, blk_k=64)
+    wl.n_qb, wl.n_kb = (wl.N + 63) // 64, (wl.N + 63) // 64
+    rng = np.random.default_rng(6)
+    q, k, v = (rng.standard_normal((1, wl.H, wl.N, wl.D)) for _ in range(3))
+    w = rng.standard_normal((wl.D, wl.D)) / math.sqrt(wl.D)
+    gq = 1.0 + 0.1 * rng.standard_normal(wl.H * wl.D)
+    gk = 1.0 + 0.1 * rng.standard_normal(wl.H * wl.D)
+    dy = rng.standard_normal(q.shape)
+    idx = [[rng.choice(wl.n_kb, 1, replace=False) for _ in range(wl.n_qb)] for _ in range(wl.H)]
+    idx = np.array(idx).reshape(1, wl.H, wl.n_qb, 1).astype(np.int32)
+    eps = 1e-6
+
+    def float_norm(X, gamma, eps_):
+        X = np.asarray(X, np.float64)
+        H, N, D = X.shape
+        x = X.transpose(1, 0, 2).reshape(N, H * D)
+        r = 1.0 / np.sqrt((x * x).sum(axis=1, keepdims=True) / (H * D) + float(np.float32(eps_)))
+        return (x * r * np.asarray(gamma).reshape(1, -1)).reshape(N, H, D).transpose(1, 0, 2), None, None
+
+    orig = osg.qk_rmsnorm
+    osg.qk_rmsnorm = float_norm
+    try:
+        dq, dk, dv, dW, dgq, dgk = ob.backward_with_norm(q, k, v, w, idx, dy, wl.blk_q, wl.blk_k, gq, gk, eps)
+
+        def L(qq, kk, ggq, ggk):
+            qh = float_norm(qq[0], ggq, eps)[0]
+            kh = float_norm(kk[0], ggk, eps)[0]
+            tot = 0.0
+            for h in range(wl.H):
+                F_ = ob.forward_float_head(torch.tensor(qh[h]), torch.tensor(kh[h]), torch.tensor(v[0, h]),
+                                           torch.tensor(np.asarray(w, np.float64)), idx[0, h], wl.blk_q, wl.blk_k)
+                tot += float((F_.numpy() * dy[0, h]).sum())
+            return tot
+
+        rng2 = np.random.default_rng(7)
+        for name, arr, grad in (("q", q, dq), ("k", k, dk)):
+            for _ in range(3):
+                h, n, d = rng2.integers(wl.H), rng2.integers(wl.N), rng2.integers(wl.D)
+                e = 1e-5 * max(1.0, abs(arr[0, h, n, d]))
+                ap, am = arr.copy(), arr.copy()
+                ap[0, h, n, d] += e
+                am[0, h, n, d] -= e
+                fd = (L(ap, k, gq, gk) - L(am, k, gq, gk)) / (2 * e) if name == "q" else \
+                     (L(q, ap, gq, gk) - L(q, am, gq, gk)) / (2 * e)
+                assert abs(fd - grad[0, h, n, d]) <= 1e-6 * max(1.0, abs(fd)), (name, fd, grad[0, h, n, d])
+        for name, gam, grad in (("gq", gq, dgq), ("gk", gk, dgk)):
+            c = rng2.integers(wl.H * wl.D)
+            e = 1e-5
+            gp, gm = gam.copy(), gam.copy()
+            gp[c] += e
+            gm[c] -= e
+            fd = (L(q, k, gp, gk) - L(q, k, gm, gk)) / (2 * e) if name == "gq" else \
+                 (L(q, k, gq, gp) - L(q, k, gq, gm)) / (2 * e)
+            assert abs(fd - grad[c]) <= 1e-6 * max(1.0, abs(fd)), (name, fd, grad[c])
+    finally:
+        osg.qk_rmsnorm = orig

@@ -96,6 +96,10 @@ typedef struct sagesla_params {
   void* q_hat;
   void* k_hat;
   float norm_eps;
+  /* sagesla_backward with SAGESLA_QK_RMSNORM (required there, ignored elsewhere): fp32 [H*D] outputs, dL/d of the
+     norm weights of Q and of K (summed over every token of every batch entry). */
+  float* dq_norm_w;
+  float* dk_norm_w;
 } sagesla_params;
 
 /* Bytes of workspace the three entry points need for these parameters (all intermediates kept inside).
@@ -151,8 +155,11 @@ sagesla_status sagesla_forward(const void* q, const void* k, const void* v, void
    fp32 in a fixed order (deterministic); every product runs on bf16 MFMA with each operand that is not exactly
    bf16 (P, dS, phi of q and k, the linear branch's states and intermediates) split into bf16 hi + lo pairs; the
    linear branch starts from the forward's remaining state (bf16 hi + lo).
-   SAGESLA_QK_RMSNORM is not differentiated (SAGESLA_E_UNSUPPORTED); SAGESLA_SMOOTH_K and SAGESLA_QUANT_GROUP32
-   do not change the result. The workspace must hold sagesla_backward_workspace_bytes(p) bytes. */
+   With SAGESLA_QK_RMSNORM the attention's gradient is taken at the normalized Q and K the forward uses (their
+   bf16 roundings pass gradients unchanged, like the quantization) and carried through the norm: dq and dk are then
+   the gradients of the raw inputs, and dq_norm_w, dk_norm_w (required) receive those of the norm weights.
+   SAGESLA_SMOOTH_K and SAGESLA_QUANT_GROUP32 do not change the result. The workspace must hold
+   sagesla_backward_workspace_bytes(p) bytes. */
 size_t sagesla_backward_workspace_bytes(const sagesla_params* p);
 sagesla_status sagesla_backward(const void* q, const void* k, const void* v, const void* dout, float* dq, float* dk,
                                 float* dv, float* dw_proj, const sagesla_params* p, void* stream);

@@ -53,6 +53,7 @@ class Params(ctypes.Structure):
         ("events", ctypes.POINTER(ctypes.c_void_p)),
         ("q_norm_w", ctypes.c_void_p), ("k_norm_w", ctypes.c_void_p), ("q_hat", ctypes.c_void_p),
         ("k_hat", ctypes.c_void_p), ("norm_eps", ctypes.c_float),
+        ("dq_norm_w", ctypes.c_void_p), ("dk_norm_w", ctypes.c_void_p),
     ]
 
 
@@ -322,19 +323,22 @@ def select(q_pool, k_pool, *, N: int, topk: int, blk_q: int = 128, blk_k: int = 
 
 
 def backward(q, k, v, w_proj, dout, mask, *, topk: int, blk_q: int = 128, blk_k: int = 64, linear: bool = True,
-             sm_scale: float = 0.0, workspace=None):
+             sm_scale: float = 0.0, workspace=None, norm=None):
     """SLA backward for the fixed selection `mask` (int32 [B, H, n_qb, topk]): gradient of the float forward
     (INT8 quantization straight through) given dout = dL/d(out) (bf16 [B, H, N, 128]). Returns fp32 (dq, dk, dv)
-    and dW_p (fp32 [128, 128], summed over every head; None without the linear branch). Runs on the current
+    and dW_p (fp32 [128, 128], summed over every head; None without the linear branch). With norm =
+    (gamma_q, gamma_k, eps), the RMSNorm of Q and K before the path (as in forward): dq, dk are the gradients of the
+    raw q, k, and the norm weights' gradients (fp32 [H*128] each) follow dW_p in the result. Runs on the current
     stream."""
     import torch
     B, H, N, D = q.shape
-    cfg = Config(B, H, N, D, blk_q, blk_k, topk, linear, True, sm_scale)
+    cfg = Config(B, H, N, D, blk_q, blk_k, topk, linear, True, sm_scale, False, norm is not None)
     _shape_check(q, k, v, dout, cfg)
     if topk > 0 and (mask is None or mask.dtype != torch.int32 or not mask.is_contiguous()
                      or tuple(mask.shape) != (B, H, cfg.n_qb, topk)):
         raise ValueError("mask must be a contiguous int32 CUDA tensor [B, H, n_qb, topk]")
-    p0 = cfg.params(w_proj=_ptr(w_proj))
+    nargs = _norm_args(norm, H, D)
+    p0 = cfg.params(w_proj=_ptr(w_proj), **nargs)
     need = load().sagesla_backward_workspace_bytes(ctypes.byref(p0))
     if need == 0:
         _check(validate(cfg) or 3, "sagesla_backward_workspace_bytes")
@@ -343,9 +347,11 @@ def backward(q, k, v, w_proj, dout, mask, *, topk: int, blk_q: int = 128, blk_k:
     f32 = dict(dtype=torch.float32, device=q.device)
     dq, dk, dv = (torch.empty(B, H, N, D, **f32) for _ in range(3))
     dw = torch.empty(D, D, **f32) if linear else None
+    dwn = (torch.empty(H * D, **f32), torch.empty(H * D, **f32)) if norm is not None else (None, None)
     p = cfg.params(w_proj=_ptr(w_proj), workspace=workspace.data_ptr(), workspace_bytes=workspace.numel(),
-                   block_idx=_ptr(mask) if topk > 0 else None)
+                   block_idx=_ptr(mask) if topk > 0 else None, dq_norm_w=_ptr(dwn[0]), dk_norm_w=_ptr(dwn[1]),
+                   **nargs)
     _check(load().sagesla_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(), dq.data_ptr(),
                                    dk.data_ptr(), dv.data_ptr(), _ptr(dw), ctypes.byref(p), _stream(q.device)),
            "sagesla_backward")
-    return dq, dk, dv, dw
+    return (dq, dk, dv, dw) if norm is None else (dq, dk, dv, dw, dwn[0], dwn[1])

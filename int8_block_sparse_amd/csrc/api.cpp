@@ -349,13 +349,20 @@ size_t plan_backward(const Plan& pl, unsigned char* ws, BwdPlan* b) {
     b->dw_part = (float*)take(BH * backward_dw_chunks(pl.N) * kD * kD * sizeof(float));
     b->dw_seg = (float*)take(backward_dw_segments() * kD * kD * sizeof(float));
   }
+  if (pl.qk_norm) {
+    b->norm_rs = (float*)take((size_t)2 * pl.B * N * 2 * sizeof(float));
+    b->norm_part = (float*)take((size_t)2 * pl.B * backward_norm_chunks(pl.N) * pl.H * kD * sizeof(float));
+  }
   return off;
 }
 
 sagesla_status check_backward(const sagesla_params* p) {
   sagesla_status st = check_params(p);
   if (st != SAGESLA_OK) return st;
-  if (p->flags & SAGESLA_QK_RMSNORM) return SAGESLA_E_UNSUPPORTED;
+  if (p->flags & SAGESLA_QK_RMSNORM) {
+    if (!p->dq_norm_w || !p->dk_norm_w) return SAGESLA_E_NULL;
+    if (misaligned(p->dq_norm_w, 16) || misaligned(p->dk_norm_w, 16)) return SAGESLA_E_ALIGN;
+  }
   if (p->topk > 0 && !p->block_idx) return SAGESLA_E_NULL;
   return SAGESLA_OK;
 }
@@ -365,7 +372,7 @@ sagesla_status check_backward(const sagesla_params* p) {
 extern "C" {
 
 size_t sagesla_backward_workspace_bytes(const sagesla_params* p) {
-  if (check_shape(p) != SAGESLA_OK || (p->flags & SAGESLA_QK_RMSNORM)) return 0;
+  if (check_shape(p) != SAGESLA_OK) return 0;
   Plan pl;
   make_plan(p, nullptr, &pl);
   BwdPlan b{};
@@ -399,14 +406,21 @@ sagesla_status sagesla_backward(const void* q, const void* k, const void* v, con
   b.dv = dv;
   b.dw = dw_proj;
   const hipStream_t s = (hipStream_t)stream;
+  if (pl.qk_norm) {  // the attention part runs at the normalized values the forward uses
+    SAGESLA_TRY(launch_qk_norm(pl, (const uint16_t*)q, (const uint16_t*)k, s));
+    b.q = (const uint16_t*)pl.q_hat;
+    b.k = (const uint16_t*)pl.k_hat;
+  }
   const bool lin_active = pl.linear && pl.topk < pl.n_kb;
-  if (lin_active) SAGESLA_TRY(launch_linear(pl, (const uint16_t*)k, (const uint16_t*)v, s));
+  if (lin_active) SAGESLA_TRY(launch_linear(pl, b.k, (const uint16_t*)v, s));
   SAGESLA_TRY(launch_backward_sparse(b, s));
   if (lin_active) {
     SAGESLA_TRY(launch_backward_linear(b, s));
   } else if (dw_proj) {
     SAGESLA_TRY(launch_fill_f32(dw_proj, (size_t)kD * kD, 0.f, s));
   }
+  if (pl.qk_norm)  // dq, dk hold the gradients at the normalized values: carry them through the norm
+    SAGESLA_TRY(launch_norm_backward(b, (const uint16_t*)q, (const uint16_t*)k, p->dq_norm_w, p->dk_norm_w, s));
   return SAGESLA_OK;
 }
 

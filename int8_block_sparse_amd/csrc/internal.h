@@ -80,11 +80,16 @@ struct BwdPlan {
   float* dhj;                      // [BH][n_kb] records: dH_J as bf16 hi and lo planes (row c), then dZ_J fp32
   float* dw_part;                  // [BH][n_chunks][D][D]
   float* dw_seg;                   // [backward_dw_segments()][D][D]
+  float* norm_rs;                  // with the norm: [2][B][N][2] r and s of every token of Q and K
+  float* norm_part;                // with the norm: [2][B][backward_norm_chunks(N)][H*D] weight-gradient partials
 };
 hipError_t launch_backward_sparse(const BwdPlan& b, hipStream_t s);
 hipError_t launch_backward_linear(const BwdPlan& b, hipStream_t s);
 size_t backward_dw_chunks(int N);
 size_t backward_dw_segments();
+size_t backward_norm_chunks(int N);
+hipError_t launch_norm_backward(const BwdPlan& b, const uint16_t* q_raw, const uint16_t* k_raw, float* dwq,
+                                float* dwk, hipStream_t s);
 // fills (graph-capture friendly replacements for memset)
 hipError_t launch_fill_f32(float* dst, size_t n, float val, hipStream_t s);
 // dynamic LDS of the kernels that size it at run time

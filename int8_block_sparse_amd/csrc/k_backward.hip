@@ -880,6 +880,102 @@ __global__ __launch_bounds__(256) void kb_dw_sum2(const float* __restrict__ seg,
 }
 
 // ---------------------------------------------------------------------------------------------------------
+// Backward of the RMSNorm before the path (straight-through roundings). For Q (z = 0) and K (z = 1), with g the
+// attention's gradient at the normalized values (fp32, in the dq / dk buffers), per token with its n = H*D
+// channels and r = fp32(1 / sqrt(sum x^2 / n + eps)) as in the forward:
+//   dx_c = r w_c g_c - x_c r^3 / n * s,  s = sum_c x_c w_c g_c;   dw_c = sum over tokens of x_c r g_c
+// kb_norm_stats: grid (ceil(N / 8), B, 2), 512 threads, a wave per token: r and s (fp64 sums) -> rs[z][b][n][2].
+// kb_norm_dw: grid (ceil(n / 256), n_chunks, 2 B): thread = channel, partial over a chunk of kNormChunk tokens in
+// ascending order; kb_norm_dw_sum adds the partials in (b, chunk) order. kb_norm_dx then overwrites g with dx.
+// ---------------------------------------------------------------------------------------------------------
+constexpr int kNormChunk = 1024;
+
+__global__ __launch_bounds__(512) void kb_norm_stats(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                                                     const uint16_t* __restrict__ wq, const uint16_t* __restrict__ wk,
+                                                     const float* __restrict__ dq, const float* __restrict__ dk,
+                                                     float* __restrict__ rs, int B, int H, int N, float eps) {
+  const int z = blockIdx.z, b = blockIdx.y, l = threadIdx.x & 63;
+  const int n = blockIdx.x * 8 + (threadIdx.x >> 6);
+  if (n >= N) return;  // no barrier below
+  const size_t row0 = ((size_t)b * H * N + n) * kD;
+  const uint16_t* x = (z ? k : q) + row0;
+  const float* g = (z ? dk : dq) + row0;
+  const uint16_t* w = z ? wk : wq;
+  double ss = 0.0, sg = 0.0;
+  for (int h = 0; h < H; ++h) {
+    const uint32_t xv = *(const uint32_t*)(x + (size_t)h * N * kD + 2 * l);
+    const uint32_t wv = *(const uint32_t*)(w + h * kD + 2 * l);
+    const float2 gv = *(const float2*)(g + (size_t)h * N * kD + 2 * l);
+    const double x0 = bf16_lo(xv), x1 = bf16_hi(xv);
+    ss += x0 * x0 + x1 * x1;
+    sg += x0 * (double)bf16_lo(wv) * (double)gv.x + x1 * (double)bf16_hi(wv) * (double)gv.y;
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    ss += __shfl_xor(ss, o);
+    sg += __shfl_xor(sg, o);
+  }
+  if (l == 0) {
+    const double m = ss / (double)(H * kD);
+    float* o = rs + (((size_t)z * B + b) * N + n) * 2;
+    o[0] = (float)(1.0 / sqrt(m + (double)eps));
+    o[1] = (float)sg;
+  }
+}
+
+__global__ __launch_bounds__(256) void kb_norm_dw(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                                                  const float* __restrict__ dq, const float* __restrict__ dk,
+                                                  const float* __restrict__ rs, float* __restrict__ part, int B, int H,
+                                                  int N, int n_chunks) {
+  const int c = blockIdx.x * 256 + threadIdx.x, ch = blockIdx.y, z = blockIdx.z / B, b = blockIdx.z % B;
+  if (c >= H * kD) return;
+  const int h = c >> 7, d = c & 127;
+  const int n0 = ch * kNormChunk, n1 = min(N, n0 + kNormChunk);
+  const size_t hb = (((size_t)b * H + h) * N) * kD + d;
+  const uint16_t* x = (z ? k : q) + hb;
+  const float* g = (z ? dk : dq) + hb;
+  const float* r = rs + (((size_t)z * B + b) * N) * 2;
+  float acc = 0.f;
+  for (int n = n0; n < n1; ++n) acc = fmaf(bf16_lo(x[(size_t)n * kD]) * r[2 * n], g[(size_t)n * kD], acc);
+  part[(((size_t)z * B + b) * n_chunks + ch) * H * kD + c] = acc;
+}
+
+__global__ __launch_bounds__(256) void kb_norm_dw_sum(const float* __restrict__ part, float* __restrict__ dwq,
+                                                      float* __restrict__ dwk, int B, int H, int n_chunks) {
+  const int c = blockIdx.x * 256 + threadIdx.x, z = blockIdx.y;
+  if (c >= H * kD) return;
+  float acc = 0.f;
+  for (int i = 0; i < B * n_chunks; ++i) acc += part[((size_t)z * B * n_chunks + i) * H * kD + c];
+  (z ? dwk : dwq)[c] = acc;
+}
+
+__global__ __launch_bounds__(256) void kb_norm_dx(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                                                  const uint16_t* __restrict__ wq, const uint16_t* __restrict__ wk,
+                                                  float* __restrict__ dq, float* __restrict__ dk,
+                                                  const float* __restrict__ rs, int B, int H, int N) {
+  const int z = blockIdx.y;
+  const size_t e4 = (size_t)blockIdx.x * 256 + threadIdx.x;  // a group of 4 channels of one head row
+  const size_t total4 = (size_t)B * H * N * (kD / 4);
+  if (e4 >= total4) return;
+  const int d4 = (int)(e4 % (kD / 4));
+  const size_t rowi = e4 / (kD / 4);  // (b, h, n)
+  const int n = (int)(rowi % N), h = (int)((rowi / N) % H), b = (int)(rowi / ((size_t)N * H));
+  const uint2 xv = *(const uint2*)((z ? k : q) + rowi * kD + 4 * d4);
+  const uint2 wv = *(const uint2*)((z ? wk : wq) + h * kD + 4 * d4);
+  float* gp = (z ? dk : dq) + rowi * kD + 4 * d4;
+  const float4 gv = *(const float4*)gp;
+  const float* rr = rs + (((size_t)z * B + b) * N + n) * 2;
+  const float r = rr[0], sc = r * r * r * rr[1] / (float)(H * kD);
+  const float xs[4] = {bf16_lo(xv.x), bf16_hi(xv.x), bf16_lo(xv.y), bf16_hi(xv.y)};
+  const float ws[4] = {bf16_lo(wv.x), bf16_hi(wv.x), bf16_lo(wv.y), bf16_hi(wv.y)};
+  const float gs[4] = {gv.x, gv.y, gv.z, gv.w};
+  float o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = fmaf(r * ws[i], gs[i], -xs[i] * sc);
+  *(float4*)gp = make_float4(o[0], o[1], o[2], o[3]);
+}
+
+// ---------------------------------------------------------------------------------------------------------
 // launches
 // ---------------------------------------------------------------------------------------------------------
 size_t kbq_lds_bytes() { return (size_t)4 * kTileBytes; }
@@ -943,6 +1039,29 @@ hipError_t launch_backward_linear(const BwdPlan& b, hipStream_t s) {
 }
 
 size_t backward_dw_chunks(int N) { return (size_t)(N + kDwChunk - 1) / kDwChunk; }
+size_t backward_norm_chunks(int N) { return (size_t)(N + kNormChunk - 1) / kNormChunk; }
+
+hipError_t launch_norm_backward(const BwdPlan& b, const uint16_t* q_raw, const uint16_t* k_raw, float* dwq,
+                                float* dwk, hipStream_t s) {
+  const Plan& p = *b.fwd;
+  const uint16_t* wq = (const uint16_t*)p.q_norm_w;
+  const uint16_t* wk = (const uint16_t*)p.k_norm_w;
+  hipLaunchKernelGGL(kb_norm_stats, dim3((p.N + 7) / 8, p.B, 2), dim3(512), 0, s, q_raw, k_raw, wq, wk, b.dq, b.dk,
+                     b.norm_rs, p.B, p.H, p.N, p.norm_eps);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int n_chunks = (int)backward_norm_chunks(p.N), nch = p.H * kD;
+  hipLaunchKernelGGL(kb_norm_dw, dim3((nch + 255) / 256, n_chunks, 2 * p.B), dim3(256), 0, s, q_raw, k_raw, b.dq,
+                     b.dk, b.norm_rs, b.norm_part, p.B, p.H, p.N, n_chunks);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(kb_norm_dw_sum, dim3((nch + 255) / 256, 2), dim3(256), 0, s, b.norm_part, dwq, dwk, p.B, p.H,
+                     n_chunks);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const size_t total4 = (size_t)p.B * p.H * p.N * (kD / 4);
+  hipLaunchKernelGGL(kb_norm_dx, dim3((unsigned)((total4 + 255) / 256), 2), dim3(256), 0, s, q_raw, k_raw, wq, wk,
+                     b.dq, b.dk, b.norm_rs, p.B, p.H, p.N);
+  return hipGetLastError();
+}
 size_t backward_dw_segments() { return kDwSeg; }
 
 }  // namespace sagesla

@@ -153,8 +153,11 @@ def test_backward_validation(lib):
     assert bwd(lib, good(workspace_bytes=need - 1, **ok)) == 4
     assert bwd(lib, good(workspace=FAKE + 16, **ok)) == 5
     norm = good(flags=sg.LINEAR | sg.QK_RMSNORM, q_norm_w=FAKE, k_norm_w=FAKE, norm_eps=1e-6, **ok)
-    assert bwd(lib, norm) == 3                         # the norm is not differentiated
-    assert lib.sagesla_backward_workspace_bytes(ctypes.byref(norm)) == 0
+    assert bwd(lib, norm) == 1                         # the norm needs its weight-gradient outputs
+    norm.dq_norm_w, norm.dk_norm_w = FAKE, FAKE + 4
+    assert bwd(lib, norm) == 5
+    norm.dk_norm_w = FAKE
+    assert lib.sagesla_backward_workspace_bytes(ctypes.byref(norm)) > need  # normalized copies, norm partials
     assert bwd(lib, good(D=64, **ok)) == 3
     assert lib.sagesla_last_hip_error() == 0
 

@@ -222,3 +222,41 @@ def test_backward_with_qk_norm(topk):
     close("dW_p", to_np(dw), rw)
     close("d gamma_q", to_np(dgq), rgq)
     close("d gamma_k", to_np(dgk), rgk)
+
+
+def test_backward_full_size_720p_qk_norm_step():
+    # the norm step at full size: the backward without the norm on the forward's own normalized Q, K gives the
+    # gradient g at the normalized values; the backward with the norm must equal the norm's backward of that g
+    # (closed form in fp64 on sampled tokens over all heads; the weight gradients summed over every token)
+    wl = synth.workload(3)
+    q, k, v, w = synth.make(wl, 0, device="cuda")
+    gq, gk = synth.make_norm_weights(wl.H, wl.D, 0, device="cuda")
+    eps = synth.NORM_EPS
+    say(f"full-size {wl.name} with the norm: forward")
+    _, ex = sg.forward(q, k, v, w, topk=wl.topk, export=True, norm=(gq, gk, eps))
+    sel = ex["block_idx"][..., :wl.topk].contiguous()
+    qh, kh = ex["q_hat"], ex["k_hat"]
+    del ex
+    dy = torch.randn(q.shape, device="cuda", generator=torch.Generator(device="cuda").manual_seed(1)).to(torch.bfloat16)
+    say("backward with the norm")
+    dq, dk, dv, dw, dgq, dgk = sg.backward(q, k, v, w, dy, sel, topk=wl.topk, norm=(gq, gk, eps))
+    say("backward at the normalized values")
+    gq_, gk_, dv2, dw2, = sg.backward(qh, kh, v, w, dy, sel, topk=wl.topk)
+    torch.cuda.synchronize()
+    assert torch.equal(dv, dv2) and torch.equal(dw, dw2)
+    n = wl.H * wl.D
+    rng = np.random.default_rng(2)
+    for x, g, wt, dx, dwt, name in ((q, gq_, gq, dq, dgq, "q"), (k, gk_, gk, dk, dgk, "k")):
+        X = x.double().permute(0, 2, 1, 3).reshape(wl.B, wl.N, n)      # token-major [B, N, H*D]
+        G = g.double().permute(0, 2, 1, 3).reshape(wl.B, wl.N, n)
+        W = wt.double().reshape(1, 1, n)
+        r = 1.0 / torch.sqrt((X * X).sum(-1, keepdim=True) / n + float(np.float32(eps)))
+        want_dw = (X * r * G).sum(dim=(0, 1))
+        close(f"d gamma_{name}", to_np(dwt), want_dw.cpu().numpy())
+        for _ in range(6):
+            b, t = int(rng.integers(wl.B)), int(rng.integers(wl.N))
+            xs, gs, rs = X[b, t], G[b, t], r[b, t]
+            s = (xs * W[0, 0] * gs).sum()
+            want = rs * W[0, 0] * gs - xs * rs ** 3 * s / n
+            got = dx[b, :, t, :].double().reshape(n)
+            close(f"d{name} token ({b}, {t})", got.cpu().numpy(), want.cpu().numpy())

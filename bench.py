@@ -276,15 +276,20 @@ def main_backward(args):
     wl = synth.workload(WORKLOAD)
     log(f"generating {wl.name} inputs on the GPU")
     q, k, v, w = synth.make(wl, 0, device=dev)
-    _, ex = sg.forward(q, k, v, w, topk=wl.topk, export=True)
+    norm = None
+    if args.qk_norm:
+        gq, gk = synth.make_norm_weights(wl.H, wl.D, 0, device=dev)
+        norm = (gq, gk, synth.NORM_EPS)
+    _, ex = sg.forward(q, k, v, w, topk=wl.topk, export=True, norm=norm)
     mask = ex["block_idx"][..., :wl.topk].contiguous()
     del ex
     dy = torch.randn(q.shape, device=dev, generator=torch.Generator(device=dev).manual_seed(1)).to(torch.bfloat16)
-    cfg = sg.Config(wl.B, wl.H, wl.N, wl.D, wl.blk_q, wl.blk_k, wl.topk, wl.linear)
+    cfg = sg.Config(wl.B, wl.H, wl.N, wl.D, wl.blk_q, wl.blk_k, wl.topk, wl.linear, True, 0.0, False,
+                    norm is not None)
     import ctypes
-    ws = torch.empty(sg.load().sagesla_backward_workspace_bytes(ctypes.byref(cfg.params(w_proj=w.data_ptr()))),
-                     dtype=torch.uint8, device=dev)
-    step = lambda: sg.backward(q, k, v, w, dy, mask, topk=wl.topk, workspace=ws)
+    pw = cfg.params(w_proj=w.data_ptr(), **sg._norm_args(norm, wl.H, wl.D))
+    ws = torch.empty(sg.load().sagesla_backward_workspace_bytes(ctypes.byref(pw)), dtype=torch.uint8, device=dev)
+    step = lambda: sg.backward(q, k, v, w, dy, mask, topk=wl.topk, workspace=ws, norm=norm)
     for _ in range(args.warmup):
         step()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
@@ -309,7 +314,8 @@ def main_backward(args):
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16+f32", "data": "synthetic",
         "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "N": wl.N, "D": wl.D, "blk_q": wl.blk_q,
-                   "blk_k": wl.blk_k, "topk": wl.topk, "linear": wl.linear, "parallelism": "single GPU"},
+                   "blk_k": wl.blk_k, "topk": wl.topk, "linear": wl.linear, "qk_norm": bool(args.qk_norm),
+                   "parallelism": "single GPU"},
         "roofline": {"kernel": "sagesla_backward (all kernels)", "bound": "mfma", "achieved": round(tflops, 1),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s (bf16)", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": None, "avg_launch_ms": round(ms_ev, 4), "flops_per_step": flops},
@@ -328,6 +334,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (HBM-counter calibration under rocprofv3)")
+    ap.add_argument("--qk-norm", action="store_true",
+                    help="with the RMSNorm of Q and K before the path (sagesla and sla-backward workloads)")
     ap.add_argument("--workload", default="sagesla",
                     help="sagesla (the headline attention layer), sla-backward (its backward for the forward's "
                          "selection) or w8a8-<shape> (the W8A8 linear layer)")
@@ -358,8 +366,14 @@ def main():
     out = torch.empty_like(q)
     cfg = sg.Config(wl.B, wl.H, wl.N, wl.D, wl.blk_q, wl.blk_k, wl.topk, wl.linear)
     ws = torch.empty(sg.workspace_bytes(cfg), dtype=torch.uint8, device=dev)
+    norm = None
+    if args.qk_norm:
+        gq, gk = synth.make_norm_weights(wl.H, wl.D, 0, device=dev)
+        norm = (gq, gk, synth.NORM_EPS)
+        cfg.qk_norm = True
+        ws = torch.empty(sg.workspace_bytes(cfg), dtype=torch.uint8, device=dev)
     fwd = lambda ev=None: sg.forward(q, k, v, w, topk=wl.topk, blk_q=wl.blk_q, blk_k=wl.blk_k, linear=wl.linear,
-                                     out=out, workspace=ws, events=ev)
+                                     out=out, workspace=ws, events=ev, norm=norm)
     for _ in range(args.warmup):
         fwd()
     evs = [sg.stage_events() for _ in range(args.steps)]
@@ -425,7 +439,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "N": wl.N, "D": wl.D, "grid": list(wl.grid),
                    "blk_q": wl.blk_q, "blk_k": wl.blk_k, "topk_frac": wl.topk_frac, "topk": wl.topk,
-                   "linear": wl.linear, "parallelism": "single GPU"},
+                   "linear": wl.linear, "qk_norm": bool(args.qk_norm), "parallelism": "single GPU"},
         "stages_ms": {n: round(t, 4) for n, t in st_avg.items()},
         "cold_ms_per_step": round(cold_med, 4),
         "roofline": {

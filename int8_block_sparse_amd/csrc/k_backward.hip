@@ -21,6 +21,9 @@
 //   kb_lin_k   per key block: dK += (V dH_J^T + dZ_J) * phi'(k), dV += phi(K) dH_J (bf16 MFMA, hi + lo)
 //   kb_dw      dW_p = sum over all rows of O_l^T dY (bf16 MFMA, O_l as hi + lo; per-chunk partials, then a
 //              fixed-order sum in segments)
+// With the RMSNorm of Q and K before the path (the attention part then runs at the normalized values):
+//   kb_norm_stats, kb_norm_dw, kb_norm_dw_sum, kb_norm_dx carry dq, dk through the norm to the raw inputs and
+//   give the gradients of the norm weights
 // Every sum has a fixed order; no atomics touch floating-point data.
 #include "device_common.h"
 #include "internal.h"

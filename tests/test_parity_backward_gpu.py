@@ -201,24 +201,25 @@ def test_backward_full_size_720p_softmax_invariants():
 # ---------------------------------------------------------------------------------------------------------
 # with the RMSNorm of Q and K before the path: gradients of the raw inputs and of the norm weights
 # ---------------------------------------------------------------------------------------------------------
-@pytest.mark.parametrize("topk", [3, 0])
-def test_backward_with_qk_norm(topk):
-    wl = SMALL["ragged128"]
+@pytest.mark.parametrize("name,topk", [("ragged128", 3), ("ragged128", 0), ("ragged64", 2)])
+def test_backward_with_qk_norm(name, topk):
+    wl = SMALL[name]
     q, k, v, w = synth.make(wl, 8)
     gq, gk = synth.make_norm_weights(wl.H, wl.D, 8)
     dy = torch.randn(q.shape, generator=torch.Generator().manual_seed(19)).to(torch.bfloat16)
     mask = make_mask(wl, topk, 8)
-    say(f"case norm {wl.name} topk{topk}")
+    say(f"case norm {wl.name} B{wl.B} H{wl.H} N{wl.N} topk{topk}")
     dq, dk, dv, dw, dgq, dgk = sg.backward(q.cuda(), k.cuda(), v.cuda(), w.cuda(), dy.cuda(),
                                            torch.from_numpy(mask).cuda(), topk=topk, blk_q=wl.blk_q, blk_k=wl.blk_k,
                                            norm=(gq.cuda(), gk.cuda(), synth.NORM_EPS))
     torch.cuda.synchronize()
     rq, rk, rv, rw, rgq, rgk = ob.backward_with_norm(to_np(q), to_np(k), to_np(v), to_np(w), mask, to_np(dy),
                                                      wl.blk_q, wl.blk_k, to_np(gq), to_np(gk), synth.NORM_EPS)
-    for h in range(wl.H):
-        close(f"h{h} dq", to_np(dq[0, h]), rq[0, h])
-        close(f"h{h} dk", to_np(dk[0, h]), rk[0, h])
-        close(f"h{h} dv", to_np(dv[0, h]), rv[0, h])
+    for b in range(wl.B):
+        for h in range(wl.H):
+            close(f"b{b} h{h} dq", to_np(dq[b, h]), rq[b, h])
+            close(f"b{b} h{h} dk", to_np(dk[b, h]), rk[b, h])
+            close(f"b{b} h{h} dv", to_np(dv[b, h]), rv[b, h])
     close("dW_p", to_np(dw), rw)
     close("d gamma_q", to_np(dgq), rgq)
     close("d gamma_k", to_np(dgk), rgk)

@@ -44,9 +44,9 @@ import math
 import numpy as np
 
 __all__ = [
-    "bf16_round", "qk_rmsnorm", "topk_count", "n_blocks", "block_rows", "exact_sum_ok", "k_mean", "smooth", "quantize", "dequantize",
+    "bf16_round", "qk_rmsnorm", "topk_count", "n_blocks", "block_rows", "exact_sum_ok", "k_mean", "smooth", "quantize",
     "pool", "block_scores", "select_topk", "sparse_attention", "phi", "linear_states", "linear_branch",
-    "project", "forward_head", "forward", "dense_attention",
+    "project", "forward_head", "forward",
 ]
 
 QMAX = 127.0
@@ -78,7 +78,11 @@ def topk_count(frac: float, n_kb: int) -> int:
 #    rewritten for the GPU; §四 step 4: the sampler calls them)
 # --------------------------------------------------------------------------------------------------------
 def bf16_round(x):
-    """Round values that are exact fp32 numbers (held in fp64) to bf16, round-to-nearest-even (finite inputs)."""
+    """Round values that are exact fp32 numbers (held in fp64) to bf16, round-to-nearest-even (finite inputs).
+
+    bf16 keeps the top 16 bits of the fp32 pattern. Adding 0x7FFF plus the lowest kept bit to the pattern and
+    clearing the low half rounds to nearest: a dropped half below 0x8000 never carries, one above always does,
+    and an exact tie (0x8000) carries only when the kept part is odd, which makes it even."""
     u = np.asarray(x, dtype=np.float64).astype(np.float32).view(np.uint32).astype(np.uint64)
     u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
     return u.astype(np.uint32).view(np.float32).astype(np.float64)
@@ -195,15 +199,6 @@ def quantize(X: np.ndarray, blk: int):
     return codes, scales
 
 
-def dequantize(codes: np.ndarray, scales: np.ndarray, blk: int) -> np.ndarray:
-    n = codes.shape[0]
-    out = np.zeros(codes.shape, dtype=np.float64)
-    for i in range(len(scales)):
-        rows = block_rows(n, blk, i)
-        out[rows] = codes[rows].astype(np.float64) * scales[i]
-    return out
-
-
 # --------------------------------------------------------------------------------------------------------
 # 4-5. block scores and top-k selection  ([TD-news] §三(二) item 1; [TD-guide] --sla_topk)
 # --------------------------------------------------------------------------------------------------------
@@ -273,14 +268,6 @@ def sparse_attention(q_codes, q_scales, k_codes, k_scales, V, idx, blk_q, blk_k,
         p = np.exp(z)
         out[rows] = (p @ V[key_rows]) / p.sum(axis=1, keepdims=True)
     return out
-
-
-def dense_attention(Q, K, V, sm_scale):
-    """Textbook softmax(Q K^T sm_scale) V in fp64, every key attended."""
-    z = np.asarray(Q, np.float64) @ np.asarray(K, np.float64).T * sm_scale
-    z = z - z.max(axis=1, keepdims=True)
-    p = np.exp(z)
-    return (p @ np.asarray(V, np.float64)) / p.sum(axis=1, keepdims=True)
 
 
 # --------------------------------------------------------------------------------------------------------

@@ -113,7 +113,29 @@ def _rmsnorm_sum_not_mean(X, gamma, eps):
     return orc.bf16_round(n * np.asarray(gamma, np.float64).reshape(H, 1, D)), r, np.zeros(N, dtype=bool)
 
 
+def _bf16_ties_away(x):
+    # round half away from zero instead of to even
+    u = np.asarray(x, dtype=np.float64).astype(np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x8000) & 0xFFFF0000
+    return u.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def _bf16_truncate(x):
+    u = np.asarray(x, dtype=np.float64).astype(np.float32).view(np.uint32).astype(np.uint64)
+    return (u & 0xFFFF0000).astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def _bf16_bias_off_by_one(x):
+    # 0x8000 instead of 0x7FFF in the rounding constant: ties of even kept parts round up
+    u = np.asarray(x, dtype=np.float64).astype(np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x8000 + ((u >> 16) & 1)) & 0xFFFF0000
+    return u.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
 MUTATIONS = {
+    "bf16_ties_away": ("bf16_round", _bf16_ties_away),
+    "bf16_truncate": ("bf16_round", _bf16_truncate),
+    "bf16_bias_off_by_one": ("bf16_round", _bf16_bias_off_by_one),
     "rmsnorm_per_head": ("qk_rmsnorm", _rmsnorm_per_head),
     "rmsnorm_no_weight": ("qk_rmsnorm", _rmsnorm_no_weight),
     "rmsnorm_sum_not_mean": ("qk_rmsnorm", _rmsnorm_sum_not_mean),
@@ -154,6 +176,7 @@ def _run_pins():
         lambda: pins.test_combine_special_cases(),
         lambda: pins.test_rmsnorm_matches_library(),
         lambda: pins.test_rmsnorm_unit_rms_with_unit_weight(),
+        lambda: pins.test_bf16_round_matches_library_and_ties(),
     ]
     failed = 0
     for c in checks:

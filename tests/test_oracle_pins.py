@@ -365,6 +365,36 @@ def test_combine_special_cases():
 # ---------------------------------------------------------------------------------------------------------
 # RMSNorm of Q and K over all heads of a token (the optional step before the path)
 # ---------------------------------------------------------------------------------------------------------
+def test_bf16_round_matches_library_and_ties():
+    # bf16 round-to-nearest-even of exact fp32 values, against torch's fp32 -> bf16 conversion (RNE) on random
+    # values over a wide exponent range, and against hand-worked exact ties: a value halfway between two bf16
+    # neighbours goes to the one whose last kept mantissa bit is 0, for either sign
+    rng = np.random.default_rng(21)
+    x = (rng.standard_normal(200000) * 2.0 ** rng.integers(-40, 40, size=200000)).astype(np.float32)
+    # append patterns whose dropped half is exactly 0x8000 (ties), 0x7FFF and 0x8001 (just below / above a tie)
+    expo = rng.integers(1, 254, size=4000, dtype=np.uint32)  # finite, normal
+    base = (expo << 23) | (rng.integers(0, 1 << 7, size=4000, dtype=np.uint32) << 16)
+    u = np.concatenate([base | 0x8000, base | 0x7FFF, base | 0x8001, (base | 0x8000) | 0x80000000])
+    x = np.concatenate([x, u.view(np.float32)]).astype(np.float64)
+    got = orc.bf16_round(x)
+    ref = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(got, ref)
+    # hand-worked: ulp of bf16 on [1, 2) is 2^-7
+    cases = [
+        (1 + 2.0 ** -8, 1.0),                      # tie, kept bit even (1.0000000) -> stays
+        (1 + 3 * 2.0 ** -8, 1 + 2.0 ** -6),        # tie between 1+2^-7 (odd) and 1+2^-6 (even) -> up
+        (-(1 + 2.0 ** -8), -1.0),                  # negative tie, even -> magnitude stays
+        (-(1 + 3 * 2.0 ** -8), -(1 + 2.0 ** -6)),  # negative tie, odd -> magnitude up
+        (1 + 2.0 ** -8 + 2.0 ** -23, 1 + 2.0 ** -7),  # just above a tie -> up
+        (1 + 3 * 2.0 ** -8 - 2.0 ** -23, 1 + 2.0 ** -7),  # just below a tie -> down
+        (255.5, 256.0),                            # tie at ulp 1: 255 odd -> 256
+        (254.5, 254.0),                            # ulp 1 below 256: 254 even -> stays
+        (2.0 ** -130 * 1.5, 2.0 ** -130 * 1.5),    # fp32 subnormal with few bits: exact in bf16
+    ]
+    for v, want in cases:
+        assert orc.bf16_round(np.array([v]))[0] == want, (v, want)
+
+
 def _norm_inputs(H=3, N=50, D=128, seed=0):
     rng = np.random.default_rng(seed)
     X = rng.standard_normal((H, N, D)) * np.exp(rng.standard_normal((1, N, 1)))

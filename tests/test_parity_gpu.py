@@ -293,8 +293,8 @@ def test_stage_entry_points_agree_with_forward():
 # and sampled query blocks (quantization and selection of a sampled head are checked in full)
 # ---------------------------------------------------------------------------------------------------------
 def sampled_case(cfg_id, heads, n_blocks_sample=6, seed=0, group32=False, norm=False):
-    wl = synth.workload(cfg_id)
-    say(f"full-size {wl.name}: generating")
+    wl = synth.workload(cfg_id) if isinstance(cfg_id, int) else cfg_id
+    say(f"full-size {wl.name} B{wl.B} H{wl.H} N{wl.N} topk {wl.topk}/{wl.n_kb}: generating")
     q, k, v, w = synth.make(wl, seed, device="cuda")
     nw = synth.make_norm_weights(wl.H, wl.D, seed, device="cuda") if norm else None
     torch.cuda.synchronize()
@@ -302,7 +302,7 @@ def sampled_case(cfg_id, heads, n_blocks_sample=6, seed=0, group32=False, norm=F
     out, ex = run_gpu(q, k, v, w, wl, wl.topk, linear=wl.linear, group32=group32,
                       norm=(nw[0], nw[1], synth.NORM_EPS) if norm else None)
     W = to_np(w)
-    rng = np.random.default_rng(cfg_id)
+    rng = np.random.default_rng(cfg_id if isinstance(cfg_id, int) else wl.N)
     flagged = 0
     for (b, h) in heads:
         Q, K, V = to_np(q[b, h]), to_np(k[b, h]), to_np(v[b, h])
@@ -362,3 +362,84 @@ def test_full_size_sla_480p_qk_norm():
 def test_full_size_sla_720p_pair_qk_norm():
     # the benchmarked layer with the RMSNorm of Q and K before the path
     sampled_case(3, [(0, 0), (1, 39)], norm=True)
+
+
+# ---------------------------------------------------------------------------------------------------------
+# selection lists longer than the attention kernel keeps in LDS (1020 entries, 510 with 32-token groups): the
+# kernel then reads block indices and key scales through scalar loads
+# ---------------------------------------------------------------------------------------------------------
+def test_long_list_dense_scalar_path():
+    # dense top-k over 1021 key blocks, linear branch off
+    wl = synth.custom(1, 1, 1021 * 64, blk_q=128, topk_frac=1.0, linear=False, name="dense-1021kb")
+    assert wl.topk == 1021
+    sampled_case(wl, [(0, 0)], n_blocks_sample=4)
+
+
+def test_long_list_sparse_linear_scalar_path():
+    # 1021 of 1100 key blocks selected (the ragged last key block holds 14 keys), linear branch on
+    wl = synth.custom(1, 1, 70350, blk_q=128, topk_frac=1021 / 1100, name="sla-1021of1100")
+    assert wl.topk == 1021 and wl.n_kb == 1100
+    sampled_case(wl, [(0, 0)], n_blocks_sample=4)
+
+
+def test_long_list_group32_scalar_path():
+    # 32-token groups with 600 selected blocks (more than the 510 the LDS list holds in this mode)
+    wl = synth.custom(1, 1, 40000, blk_q=128, topk_frac=600 / 625, name="sla-g32-600of625")
+    assert wl.topk == 600 and wl.n_kb == 625
+    sampled_case(wl, [(0, 0)], n_blocks_sample=4, group32=True)
+
+
+# ---------------------------------------------------------------------------------------------------------
+# top-k on more than 256 candidates: the histogram passes, exact ties (lower block index first) and the
+# radix passes that take over when value-range passes stall, against the oracle's brute-force ranking on
+# pooled means given directly (small integers and powers of two, so every score is exact on both sides)
+# ---------------------------------------------------------------------------------------------------------
+def select_case(qp, kp, topk, blk_q=128):
+    n_kb = kp.shape[0]
+    N = n_kb * 64
+    assert qp.shape[0] == -(-N // blk_q)
+    got = sg.select(torch.from_numpy(qp)[None, None].cuda(), torch.from_numpy(kp)[None, None].cuda(), N=N,
+                    topk=topk, blk_q=blk_q)
+    torch.cuda.synchronize()
+    got = got.cpu().numpy()[0, 0]
+    want, _ = orc.select_topk(orc.block_scores(qp, kp), topk)
+    bad = [I for I in range(want.shape[0]) if not np.array_equal(got[I], want[I])]
+    assert not bad, f"{len(bad)} rows differ, first {bad[:5]}: got {got[bad[0]][:12]} want {want[bad[0]][:12]}"
+    return want
+
+
+def test_select_all_scores_equal():
+    # every key block has the same pooled mean: each row keeps blocks 0..k-1
+    rng = np.random.default_rng(40)
+    n_kb, D = 600, 128
+    qp = rng.integers(-3, 4, size=(n_kb // 2, D)).astype(np.float64)
+    kp = np.repeat(rng.integers(-3, 4, size=(1, D)).astype(np.float64), n_kb, axis=0)
+    want = select_case(qp, kp, 60)
+    assert (want == np.arange(60)).all()
+
+
+@pytest.mark.parametrize("topk", [200, 400])
+def test_select_two_score_values(topk):
+    # key-block means take two values (300 blocks high, 700 low along channel 0); query rows of either sign, so
+    # the k-th place falls inside a tier of 300 or 700 tied candidates
+    rng = np.random.default_rng(41)
+    n_kb, D = 1000, 128
+    a = np.ones(n_kb)
+    a[rng.permutation(n_kb)[:300]] = 2.0
+    kp = np.zeros((n_kb, D))
+    kp[:, 0] = a
+    qp = np.zeros((n_kb // 2, D))
+    qp[:, 0] = rng.choice([-3.0, -1.0, 1.0, 2.0], size=n_kb // 2)
+    select_case(qp, kp, topk)
+
+
+def test_select_scores_over_many_binades():
+    # scores +-2^-e over 600 binades: equal-width value bins cut off only ~8 binades per pass, so the radix
+    # passes must finish the selection
+    rng = np.random.default_rng(42)
+    n_kb, D = 600, 128
+    kp = np.zeros((n_kb, D))
+    kp[:, 0] = np.ldexp(1.0, -rng.permutation(n_kb))
+    qp = np.zeros((n_kb // 2, D))
+    qp[:, 0] = rng.choice([-1.0, 1.0], size=n_kb // 2)
+    select_case(qp, kp, 300)

@@ -51,9 +51,11 @@ REMAINING_BYTES_PER_QBLOCK = 2 * 128 * 128 * 2 + 128 * 4
 # bf16 products of bq x D x D per query block in the attention kernel's linear epilogue: phi(Q) H_m as hi*hi +
 # hi*lo + lo*hi, then (.) W_p on the hi and lo halves of the first result
 EPILOGUE_PRODUCTS_EXECUTED = 5
-# whole heads the CPU baseline runs per workload (about 10-30 s of oracle time each)
+# whole heads the CPU baseline runs per workload (about 10-30 s of oracle time each); on the longest layer one
+# head's attention outputs are formed for a sample of its query blocks only
 CPU_HEADS = {"tiny": 2, "wan1.3b-480p-dense": 4, "wan1.3b-480p-sla": 6, "wan14b-720p-sla-pair": 2,
              "1080p-long-sla": 1}
+CPU_BLOCKS = {"1080p-long-sla": 128}
 COUNTERS = os.path.join(ROOT, "profiles", "k3_attn_wan14b-720p-sla-pair_counters.txt")
 K3_SOURCE = os.path.join(ROOT, "int8_block_sparse_amd", "csrc", "k_attn.hip")
 W8A8_COUNTERS = os.path.join(ROOT, "profiles", "k5_gemm_wan14b-720p-proj_counters.txt")
@@ -136,27 +138,36 @@ def host_info():
             "affinity_cores": len(os.sched_getaffinity(0))}
 
 
-def cpu_baseline(q, k, v, w, wl, heads, budget_s=30.0):
-    """The fp64 oracle (unchanged, untuned) on whole heads of the same workload; dense-equivalent TOPS."""
+def cpu_baseline(q, k, v, w, wl, heads, budget_s=30.0, blocks=None):
+    """The fp64 oracle (unchanged, untuned) on whole heads of the same workload; dense-equivalent TOPS.
+
+    blocks: if given, each head's attention outputs are formed for that many evenly spaced query blocks only (its
+    quantization, selection and linear-branch states still in full), and the dense-equivalent work is counted for
+    those blocks' rows."""
     from oracle import sagesla as orc
     hi = host_info()
     cores = hi["blas_threads"]
     W = w.float().cpu().double().numpy()
     done, t0 = 0, time.perf_counter()
+    sel = None if blocks is None else sorted(set(int(x) for x in
+                                                 [round(i * (wl.n_qb - 1) / max(1, blocks - 1)) for i in range(blocks)]))
     for (b, h) in heads:
         Q = q[b, h].float().cpu().double().numpy()
         K = k[b, h].float().cpu().double().numpy()
         V = v[b, h].float().cpu().double().numpy()
-        orc.forward_head(Q, K, V, W, wl.blk_q, wl.blk_k, wl.topk, linear=wl.linear)
+        orc.forward_head(Q, K, V, W, wl.blk_q, wl.blk_k, wl.topk, linear=wl.linear, blocks=sel)
         done += 1
         log(f"cpu baseline: head {done}/{len(heads)} at {time.perf_counter() - t0:.1f} s")
         if time.perf_counter() - t0 > budget_s:
             break
     dt = time.perf_counter() - t0
-    ops = done * 4.0 * wl.N * wl.N * wl.D
+    rows = wl.N if sel is None else sum(min(wl.N, (I + 1) * wl.blk_q) - I * wl.blk_q for I in sel)
+    ops = done * 4.0 * rows * wl.N * wl.D
+    what = (f"each a full forward over all {wl.n_qb} query blocks" if sel is None else
+            f"each with its quantization, selection and linear-branch states in full and the outputs of {len(sel)} of "
+            f"its {wl.n_qb} query blocks (evenly spaced), counted as {rows} of {wl.N} rows")
     return {"value": ops / dt / 1e12, "unit": "TOPS (dense-equivalent)", "cores": int(cores), "kind": "oracle",
-            "sample": f"{done} of {wl.B * wl.H} (b,h) heads, each a full forward over all {wl.n_qb} query blocks",
-            "seconds": round(dt, 2), **hi}
+            "sample": f"{done} of {wl.B * wl.H} (b,h) heads, {what}", "seconds": round(dt, 2), **hi}
 
 
 def cpu_baseline_w8a8(x, w, bias, wl, rows, budget_s=30.0):
@@ -363,6 +374,55 @@ def main_backward(args):
     print(json.dumps(result), flush=True)
 
 
+def main_mfma_peak(args):
+    """Practical matrix-core peak: a loop of independent MFMAs (no memory traffic) on every CU, timed with events;
+    the clock the box holds under that load is what separates it from the published peaks."""
+    import ctypes
+    import torch
+
+    if not torch.cuda.is_available():
+        sys.exit("bench.py needs a GPU")
+    path = os.path.join(ROOT, "int8_block_sparse_amd", "libsagesla_probe.so")
+    if not os.path.exists(path):
+        sys.exit(f"{path} is missing: build it with `python -m int8_block_sparse_amd.build`")
+    lib = ctypes.CDLL(path)
+    lib.sagesla_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                       ctypes.c_void_p]
+    lib.sagesla_probe_mfma.restype = ctypes.c_int
+    dev = torch.device("cuda:0")
+    blocks, iters = 256 * 8, 4096  # 8 workgroups of 4 waves per CU: 8 waves per SIMD
+    out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    kinds = {0: ("int8 v_mfma_i32_32x32x32_i8", 65536.0, PEAK_INT8_TOPS),
+             1: ("bf16 v_mfma_f32_32x32x16_bf16", 32768.0, PEAK_BF16_TFLOPS),
+             2: ("fp16 v_mfma_f32_32x32x16_f16", 32768.0, PEAK_BF16_TFLOPS)}
+    res = {}
+    for kind, (name, ops_each, peak) in kinds.items():
+        for _ in range(max(1, args.warmup)):
+            assert lib.sagesla_probe_mfma(kind, blocks, iters, 1, out.data_ptr(), stream) == 0
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(args.steps):
+            assert lib.sagesla_probe_mfma(kind, blocks, iters, i + 2, out.data_ptr(), stream) == 0
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        ops = blocks * 4 * 4.0 * iters * ops_each  # 4 waves x 4 MFMAs per iteration
+        t = ops / (ms * 1e-3) / 1e12
+        # the MFMA pipe needs 32 cycles per 32x32 op of these shapes on each SIMD (1024 SIMDs): the clock it held
+        ghz = ops / ops_each * 32.0 / 1024 / (ms * 1e-3) / 1e9
+        res[name] = {"ms": round(ms, 4), "achieved": round(t, 1), "peak": peak, "frac": round(t / peak, 4),
+                     "implied_clock_ghz": round(ghz, 3)}
+        log(f"{name}: {t:.1f} T/s ({t / peak:.3f} of {peak:.0f}), implied clock {ghz:.3f} GHz")
+    name0 = kinds[0][0]
+    print(json.dumps({"metric": "practical MFMA peak (independent MFMA loop, no memory)", "value": res[name0]["achieved"],
+                      "unit": "TOPS (INT8)", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+                      "ms_per_step": res[name0]["ms"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+                      "dtype": "i8", "data": "synthetic",
+                      "config": {"workload": "mfma-peak", "workgroups": blocks, "iters": iters}, "kinds": res,
+                      "cpu_baseline": None}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -388,6 +448,8 @@ def main():
         return main_w8a8(args, args.workload[len("w8a8-"):])
     if args.workload == "sla-backward":
         return main_backward(args)
+    if args.workload == "mfma-peak":
+        return main_mfma_peak(args)
     import synth
     by_name = {w.name: w for w in synth.WORKLOADS.values()}
     name = HEADLINE if args.workload == "sagesla" else args.workload
@@ -553,7 +615,7 @@ def main_forward(args, wl):
         del ws
         heads = [(0, 0), (wl.B - 1, wl.H - 1)] + [(b, h) for b in range(wl.B) for h in range(wl.H)]
         heads = list(dict.fromkeys(heads))[:CPU_HEADS.get(wl.name, 2)]
-        result["cpu_baseline"] = cpu_baseline(q, k, v, w, wl, heads, budget_s=20.0)
+        result["cpu_baseline"] = cpu_baseline(q, k, v, w, wl, heads, budget_s=20.0, blocks=CPU_BLOCKS.get(wl.name))
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)

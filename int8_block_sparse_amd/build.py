@@ -14,6 +14,9 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libsagesla.so")
+# measurement tooling beside the library: the matrix-core peak probe the benchmark runs (--workload mfma-peak)
+PROBE_OUT = os.path.join(PKG, "libsagesla_probe.so")
+PROBE_SOURCES = ["probe_mfma.hip"]
 BUILD = os.path.join(ROOT, "_build")
 SOURCES = ["api.cpp", "k_quant.hip", "k_select.hip", "k_linear.hip", "k_attn.hip", "k_w8a8.hip", "k_backward.hip"]
 ARCH = "gfx950"
@@ -53,14 +56,16 @@ def build(verbose: bool = False) -> str:
             print(msgs, file=sys.stderr)
         return obj
 
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(compile_one, SOURCES))
-    tmp = OUT + ".tmp"
-    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
-    os.replace(tmp, OUT)
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES) + len(PROBE_SOURCES))) as ex:
+        objs = list(ex.map(compile_one, SOURCES + PROBE_SOURCES))
+    for out, srcs in ((OUT, SOURCES), (PROBE_OUT, PROBE_SOURCES)):
+        tmp = out + ".tmp"
+        cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp,
+               *[o for o, src in zip(objs, SOURCES + PROBE_SOURCES) if src in srcs]]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
+        os.replace(tmp, out)
     return OUT
 
 

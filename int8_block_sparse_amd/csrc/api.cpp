@@ -15,7 +15,6 @@ thread_local int g_last_hip_error = 0;
 
 constexpr size_t kAlign = 256;
 constexpr int kColsumChunk = 512;
-constexpr int kMaxKeyBlocks = 20480;
 constexpr int kMaxN = 1 << 24;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -55,8 +54,10 @@ sagesla_status check_params(const sagesla_params* p) {
   return SAGESLA_OK;
 }
 
-// Sizes and placement of every intermediate. With ws == nullptr only the sizes are computed.
-void make_plan(const sagesla_params* p, unsigned char* ws, Plan* pl) {
+// Sizes and placement of every intermediate. With ws == nullptr only the sizes are computed. The backward's plan
+// (backward = true) holds only what it reads: the normalized Q and K (with the norm) and its linear branch's fp32
+// state table, keep mask and bf16 hi + lo remaining states; the selection comes from the caller.
+void make_plan(const sagesla_params* p, unsigned char* ws, Plan* pl, bool backward = false) {
   memset(pl, 0, sizeof(*pl));
   pl->B = p->B;
   pl->H = p->H;
@@ -79,6 +80,7 @@ void make_plan(const sagesla_params* p, unsigned char* ws, Plan* pl) {
   pl->colsum_chunk = kColsumChunk;
   pl->n_colsum_chunks = (p->N + kColsumChunk - 1) / kColsumChunk;
   pl->w_proj = p->w_proj;
+  pl->lin_precise = backward;
   const bool lin_active = pl->linear && pl->topk < pl->n_kb;
   const size_t BH = pl->BH, N = pl->N, D = kD, nqb = pl->n_qb, nkb = pl->n_kb;
   size_t off = 0;
@@ -91,22 +93,30 @@ void make_plan(const sagesla_params* p, unsigned char* ws, Plan* pl) {
     pl->q_hat = (uint16_t*)take(BH * N * D * sizeof(uint16_t));
     pl->k_hat = (uint16_t*)take(BH * N * D * sizeof(uint16_t));
   }
-  pl->colsum_part = (double*)take(BH * pl->n_colsum_chunks * D * sizeof(double));
-  pl->k_mean = (float*)take(BH * D * sizeof(float));
-  pl->q_i8 = (int8_t*)take(BH * N * D);
-  pl->k_i8 = (int8_t*)take(BH * N * D);
-  pl->q_scale = (float*)take(BH * (pl->group32 ? (size_t)pl->n_g : nqb) * sizeof(float));
-  pl->k_scale = (float*)take(BH * (pl->group32 ? (size_t)pl->n_g : nkb) * sizeof(float));
-  pl->q_pool = (double*)take(BH * nqb * D * sizeof(double));
-  pl->k_pool = (double*)take(BH * nkb * D * sizeof(double));
-  pl->scores = (double*)take(BH * nqb * nkb * sizeof(double));
-  pl->v_img = (unsigned char*)take(BH * nkb * 16384);
-  pl->block_idx = (int32_t*)take(BH * nqb * (size_t)pl->topk * sizeof(int32_t));
+  if (!backward) {
+    pl->colsum_part = (double*)take(BH * pl->n_colsum_chunks * D * sizeof(double));
+    pl->k_mean = (float*)take(BH * D * sizeof(float));
+    pl->q_i8 = (int8_t*)take(BH * N * D);
+    pl->k_i8 = (int8_t*)take(BH * N * D);
+    pl->q_scale = (float*)take(BH * (pl->group32 ? (size_t)pl->n_g : nqb) * sizeof(float));
+    pl->k_scale = (float*)take(BH * (pl->group32 ? (size_t)pl->n_g : nkb) * sizeof(float));
+    pl->q_pool = (double*)take(BH * nqb * D * sizeof(double));
+    pl->k_pool = (double*)take(BH * nkb * D * sizeof(double));
+    pl->scores = (double*)take(BH * nqb * nkb * sizeof(double));
+    pl->v_img = (unsigned char*)take(BH * nkb * 16384);
+    pl->block_idx = (int32_t*)take(BH * nqb * (size_t)pl->topk * sizeof(int32_t));
+  }
   if (lin_active) {
     pl->wpt = (uint16_t*)take(D * D * sizeof(uint16_t));
-    pl->state = (float*)take(BH * nkb * kStateX * sizeof(float));
     pl->keep_mask = (uint32_t*)take(BH * (size_t)mask_row_pad(pl->n_qb) * ((nkb + 31) / 32) * sizeof(uint32_t));
-    pl->state_m = (float*)take(BH * nqb * kStateX * sizeof(float));
+    if (backward) {
+      pl->state = (float*)take(BH * nkb * kStateX * sizeof(float));
+      pl->state_m = (float*)take(BH * nqb * kStateX * sizeof(float));
+    } else {
+      pl->state16 = (uint16_t*)take(BH * nkb * kStateX * sizeof(uint16_t));
+      pl->state_exp = (int32_t*)take(BH * nkb * sizeof(int32_t));
+      pl->rec16 = (unsigned char*)take(BH * nqb * (size_t)kRec16Bytes);
+    }
   }
   pl->ws_bytes = off;
   // caller-owned exports replace their workspace slice
@@ -327,7 +337,7 @@ sagesla_status w8a8_linear(const void* x, const int8_t* w_i8, const float* w_sca
 
 namespace {
 
-// the backward's buffers after the forward plan's (ws == nullptr: sizes only); returns the total bytes
+// the backward's own buffers after its plan's (ws == nullptr: sizes only); returns the total bytes
 size_t plan_backward(const Plan& pl, unsigned char* ws, BwdPlan* b) {
   size_t off = pl.ws_bytes;
   auto take = [&](size_t bytes) -> unsigned char* {
@@ -374,7 +384,7 @@ extern "C" {
 size_t sagesla_backward_workspace_bytes(const sagesla_params* p) {
   if (check_shape(p) != SAGESLA_OK) return 0;
   Plan pl;
-  make_plan(p, nullptr, &pl);
+  make_plan(p, nullptr, &pl, true);
   BwdPlan b{};
   return plan_backward(pl, nullptr, &b);
 }
@@ -389,12 +399,12 @@ sagesla_status sagesla_backward(const void* q, const void* k, const void* v, con
       misaligned(dk, 16) || misaligned(dv, 16) || misaligned(dw_proj, 16))
     return SAGESLA_E_ALIGN;
   Plan pl;
-  make_plan(p, nullptr, &pl);
+  make_plan(p, nullptr, &pl, true);
   BwdPlan b{};
   const size_t need = plan_backward(pl, nullptr, &b);
   if (p->workspace_bytes < need || !p->workspace) return SAGESLA_E_WORKSPACE;
   if (misaligned(p->workspace, kAlign)) return SAGESLA_E_ALIGN;
-  make_plan(p, (unsigned char*)p->workspace, &pl);
+  make_plan(p, (unsigned char*)p->workspace, &pl, true);
   plan_backward(pl, (unsigned char*)p->workspace, &b);
   b.fwd = &pl;
   b.q = (const uint16_t*)q;

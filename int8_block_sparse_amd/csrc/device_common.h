@@ -13,10 +13,22 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef float v2f __attribute__((ext_vector_type(2)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef short v8s __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) v4s lds_v4s;
 
 // bf16 bit pattern -> fp32 (exact)
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// two fp32 -> packed fp16 pair, round to nearest even (v_cvt_pk_f16_f32)
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  v2f x = {a, b};
+  v2h y = __builtin_convertvector(x, v2h);
+  return __builtin_bit_cast(uint32_t, y);
+}
 
 // two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32)
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
@@ -86,6 +98,27 @@ __device__ __forceinline__ int quant_code(float x, float s, float r) {
 
 __device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {
   return (uint32_t)(a & 0xff) | ((uint32_t)(b & 0xff) << 8) | ((uint32_t)(c & 0xff) << 16) | ((uint32_t)d << 24);
+}
+
+// Swizzled tiles of rows of 256 B (128 16-bit elements): the 16-byte chunk c of row r sits at chunk position
+// c ^ tswz(r). Sixteen consecutive rows at one chunk fall on sixteen distinct positions (the row reads of an MFMA
+// operand), and four rows from a multiple of 4 over four aligned chunks fall on sixteen distinct positions
+// (transposing reads).
+__device__ __forceinline__ int tswz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+// byte offset of the 8-byte unit that holds columns col .. col + 3 (col a multiple of 4) of row r
+__device__ __forceinline__ int toff(int r, int col) { return r * 256 + (((col >> 3) ^ tswz(r)) << 4) + ((col & 4) << 1); }
+
+// Operand of a 32x32x16 16-bit MFMA read down the columns of a swizzled tile: lane l holds tile column
+// m0 + l % 32 at rows i0 + 8 (l / 32) .. + 7 (slot s = row i0 + 8 (l / 32) + s), the order of an operand read
+// along a row. Two transposing reads (ds_read_b64_tr_b16): within each group of 16 lanes, lane i receives
+// element i % 4 of the 8-byte units addressed by lanes 4 c + i / 4, c = 0..3.
+__device__ __forceinline__ v8s tr_col_op(const unsigned char* t, int i0, int m0, int l) {
+  const int j = l & 15;
+  const int r = i0 + 8 * (l >> 5) + (j >> 2);
+  const int col = m0 + 16 * ((l >> 4) & 1) + 4 * (j & 3);
+  const v4s a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(t + toff(r, col)));
+  const v4s b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(t + toff(r + 4, col)));
+  return (v8s){a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
 // Map a flat workgroup id to a work item so that each XCD (ids are dealt round-robin over 8 XCDs) gets one

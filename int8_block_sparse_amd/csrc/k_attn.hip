@@ -291,47 +291,59 @@ __device__ __forceinline__ void attn_iter(const unsigned char* __restrict__ sk_n
 }
 
 // Linear branch of one query block, run at the end of the attention kernel (the ring's LDS is free then):
-//   U^T[e][i] = sum_c H_m^T[e][c] phi(Q)^T[c][i]   (A = H_m^T hi/lo from LDS, B = phi(Q) hi/lo in registers)
-//   O^T[f][i] = sum_e W_p^T[f][e] U^T[e][i]         (A = W_p^T from LDS, B = U^T hi/lo from the accumulators)
-// and den[i] = phi(q_i) . Z_m. The block's remaining state arrives as bf16 hi and lo planes already in this LDS
-// layout (the keep-mask product stored them so) plus Z in fp32. Buffer loads bring the planes into the ring
-// slots (hi rows 0-63 in v0, 64-127 in v1; lo rows 0-63 in v2, 64-95 in k0, 96-127 in k1; Z in k2) while
-// phi(Q) is formed; after the first product the hi slots take W_p^T the same way. Wave w handles its own 32 rows.
-// acc2 returns O^T unnormalized in the attention accumulators' layout (row lr, channel 32 ft + 8 (r / 4) + 4 g +
-// r % 4) and inv_l = 1 / den. Products hi*hi + hi*lo + lo*hi keep ~16 significant bits.
+//   U^T[e][i] = f_e sum_c P^T[e][c] phi'(Q)^T[c][i]   (A = the record's fp16 plane from LDS, B = phi' in registers)
+//   O^T[f][i] = sum_e W_p^T[f][e] U^T[e][i]          (A = W_p^T from LDS, B = U^T hi/lo from the accumulators)
+// and den[i] = phi'(q_i) . Z_m. The record holds H_m^T as an fp16 plane P (rows e) with one factor f_e per row, and
+// Z_m in fp32, H_m and Z_m sharing one power-of-two scale; phi' = phi scaled per row by the power of two that puts
+// the row's largest value in [1, 2) (phi is increasing, so that is phi of the row's largest q). Both common
+// factors cancel in U / den. Buffer loads bring the plane into the ring's V slots (rows 0-63 in v0, 64-127 in v1)
+// and the row factors into k2 + 1024, while Z arrives in k2 by ordinary loads and phi' is formed; then W_p^T takes
+// the V slots the same way. Wave w handles its own 32 rows. acc2 returns O^T unnormalized in the attention
+// accumulators' layout (row lr, channel 32 ft + 8 (r / 4) + 4 g + r % 4) and inv_l = 1 / den.
 template <int NW>
-__device__ __forceinline__ void lin_epilogue(const uint16_t* __restrict__ q, const float* __restrict__ state_m,
+__device__ __forceinline__ void lin_epilogue(const uint16_t* __restrict__ q, const unsigned char* __restrict__ rec16,
                                              const uint16_t* __restrict__ wpt, int bh, int I, int N, int n_qb,
-                                             unsigned char* __restrict__ k0, unsigned char* __restrict__ k1,
                                              unsigned char* __restrict__ k2, unsigned char* __restrict__ v0,
-                                             unsigned char* __restrict__ v1, unsigned char* __restrict__ v2,
-                                             v16f (&acc2)[4], float& inv_l) {
+                                             unsigned char* __restrict__ v1, v16f (&acc2)[4], float& inv_l) {
   const int t = threadIdx.x, w = __builtin_amdgcn_readfirstlane(t >> 6), l = t & 63, g = l >> 5, lr = l & 31;
   constexpr int BLKQ = 32 * NW;
-  const unsigned char* srec = (const unsigned char*)state_m + ((size_t)bh * n_qb + I) * (size_t)kStateX * 4;
+  const unsigned char* srec = rec16 + ((size_t)bh * n_qb + I) * (size_t)kRec16Bytes;
   float* s_z = (float*)k2;
+  const float* s_f = (const float*)(k2 + 1024);
   __syncthreads();  // every wave is done with the ring slots
   float4 zv = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (t < kD / 4) zv = *(const float4*)(srec + 65536 + 16 * t);  // issued before the plane loads: waited alone
-  {  // the planes: 64 buffer loads of 1 KB (record chunks 0-31 hi plane, 32-63 lo plane)
+  if (t < kD / 4) zv = *(const float4*)(srec + kRec16Z + 16 * t);  // issued before the plane loads: waited alone
+  {  // the plane: 32 loads of 1 KB; the row factors: one load of 1 KB (its second half past the record reads 0)
     const __amdgpu_buffer_rsrc_t rb =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(srec), (short)0, kStateX * 4, 0x00020000);
-#pragma unroll
-    for (int i = 0; i < 64 / NW; ++i) {
-      const int k = w + NW * i, c = k & 31;
-      unsigned char* dst = k < 32 ? (c < 16 ? v0 + c * 1024 : v1 + (c - 16) * 1024)
-                                  : (c < 16 ? v2 + c * 1024 : c < 24 ? k0 + (c - 16) * 1024 : k1 + (c - 24) * 1024);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (__attribute__((address_space(3))) void*)dst, 16, l * 16,
-                                               k * 1024, 0, 0);
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(srec), (short)0, kRec16Bytes, 0x00020000);
+    for (int k = w; k < 33; k += NW) {  // (offsets per lane, so the range check sees all of them)
+      unsigned char* dst = k < 16 ? v0 + k * 1024 : k < 32 ? v1 + (k - 16) * 1024 : k2 + 1024;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (__attribute__((address_space(3))) void*)dst, 16,
+                                               l * 16 + (k < 32 ? k * 1024 : kRec16F), 0, 0, 0);
     }
   }
   if (t < kD / 4) *(float4*)(s_z + 4 * t) = zv;
-  __syncthreads();  // s_z
 
   const int row = I * BLKQ + 32 * w + lr;
   const bool rok = row < N;
   const uint16_t* qrow = q + ((size_t)bh * N + (rok ? row : 0)) * kD;
-  v8bf bqh[8], bql[8];
+  // first pass over the row: its largest q (the row is read again below, from the cache, to keep registers free)
+  float qm = -INFINITY;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    uint4 wq = make_uint4(0, 0, 0, 0);
+    if (rok) wq = *(const uint4*)(qrow + 16 * s + 8 * g);
+    const uint32_t ww[4] = {wq.x, wq.y, wq.z, wq.w};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) qm = fmaxf(qm, fmaxf(bf16_lo(ww[u]), bf16_hi(ww[u])));
+  }
+  qm = fmaxf(qm, swap_halves_f32(qm));
+  int kx = 0;
+  (void)frexpf(phi_f(qm), &kx);  // the row's largest phi < 2^kx
+  const int sh = 1 - kx;
+  const float sc = ldexpf(1.f, sh), shf = (float)sh;
+  __syncthreads();  // s_z
+  v8h bq16[8];
   float den = 0.f;
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
@@ -339,23 +351,24 @@ __device__ __forceinline__ void lin_epilogue(const uint16_t* __restrict__ q, con
     uint4 wq = make_uint4(0, 0, 0, 0);
     if (rok) wq = *(const uint4*)(qrow + c0);
     const uint32_t ww[4] = {wq.x, wq.y, wq.z, wq.w};
-    uint32_t hw[4], lw[4];
+    uint32_t hw[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const float p0 = phi_f(bf16_lo(ww[u])), p1 = phi_f(bf16_hi(ww[u]));
+      const float x0 = bf16_lo(ww[u]), x1 = bf16_hi(ww[u]);
+      const float p0 = x0 > 0.f ? fmaf(x0, sc, sc) : __builtin_amdgcn_exp2f(fmaf(x0, 1.4426950408889634f, shf));
+      const float p1 = x1 > 0.f ? fmaf(x1, sc, sc) : __builtin_amdgcn_exp2f(fmaf(x1, 1.4426950408889634f, shf));
       den = fmaf(p0, s_z[c0 + 2 * u], den);
       den = fmaf(p1, s_z[c0 + 2 * u + 1], den);
-      split2(p0, p1, hw[u], lw[u]);
+      hw[u] = pack_f16x2(p0, p1);
     }
-    bqh[s] = __builtin_bit_cast(v8bf, make_uint4(hw[0], hw[1], hw[2], hw[3]));
-    bql[s] = __builtin_bit_cast(v8bf, make_uint4(lw[0], lw[1], lw[2], lw[3]));
+    bq16[s] = __builtin_bit_cast(v8h, make_uint4(hw[0], hw[1], hw[2], hw[3]));
   }
   den += swap_halves_f32(den);
   __builtin_amdgcn_s_waitcnt(7 << 4);  // vmcnt(0) lgkmcnt(0): this wave's plane loads have landed
   __syncthreads();                      // ... and every other wave's
   inv_l = 1.f / den;
 
-  // ---- U^T = H_m^T phi(Q)^T (rows e >= 64 sit in the second slot of each plane: out_off(e - 64, c) has the
+  // ---- U^T = P^T phi'(Q)^T, then each row e times its factor (rows e >= 64 sit in v1: out_off(e - 64, c) has the
   // same swizzle bits as out_off(e, c))
   v16f acc[4];
 #pragma unroll
@@ -363,19 +376,23 @@ __device__ __forceinline__ void lin_epilogue(const uint16_t* __restrict__ q, con
     acc[et] = (v16f){};
     const int e = 32 * et + lr;
     const unsigned char* hp = et < 2 ? v0 : v1;
-    const unsigned char* lp = et < 2 ? v2 : et == 2 ? k0 : k1;
-    const int eh = et < 2 ? e : e - 64, el = et < 2 ? e : et == 2 ? e - 64 : e - 96;
+    const int eh = et < 2 ? e : e - 64;
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      const v8bf ah = *(const v8bf*)(hp + out_off(eh, 16 * s + 8 * g));
-      const v8bf al = *(const v8bf*)(lp + out_off(el, 16 * s + 8 * g));
-      acc[et] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bqh[s], acc[et], 0, 0, 0);
-      acc[et] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bql[s], acc[et], 0, 0, 0);
-      acc[et] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bqh[s], acc[et], 0, 0, 0);
+      const v8h a = *(const v8h*)(hp + out_off(eh, 16 * s + 8 * g));
+      acc[et] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, bq16[s], acc[et], 0, 0, 0);
+    }
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const float4 f = *(const float4*)(s_f + 32 * et + 8 * r4 + 4 * g);
+      acc[et][4 * r4] *= f.x;
+      acc[et][4 * r4 + 1] *= f.y;
+      acc[et][4 * r4 + 2] *= f.z;
+      acc[et][4 * r4 + 3] *= f.w;
     }
   }
-  __syncthreads();  // every wave is done with the state planes
-  {  // W_p^T (already in the plane layout) into the hi slots: 32 loads of 1 KB
+  __syncthreads();  // every wave is done with the plane
+  {  // W_p^T (already in the plane layout) into the V slots: 32 loads of 1 KB
     const __amdgpu_buffer_rsrc_t rw =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(wpt), (short)0, kD * kD * 2, 0x00020000);
 #pragma unroll
@@ -417,7 +434,7 @@ template <int NW, bool G>
 __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k3_attn(
     const int8_t* __restrict__ q8, const int8_t* __restrict__ k8, const unsigned char* __restrict__ vt,
     const float* __restrict__ qs, const float* __restrict__ ks, const int32_t* __restrict__ idx,
-    const uint16_t* __restrict__ qraw, const float* __restrict__ state_m, const uint16_t* __restrict__ wpt,
+    const uint16_t* __restrict__ qraw, const unsigned char* __restrict__ rec16, const uint16_t* __restrict__ wpt,
     float* __restrict__ o_lin, uint16_t* __restrict__ out, int N, int n_qb, int n_kb, int topk, float c0,
     int total) {
   constexpr int BLKQ = 32 * NW;
@@ -685,10 +702,10 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k3_attn(
 
   const float lt = l_run + swap_halves_f32(l_run);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
-  // the linear branch (state_m given): O_l in the same register layout as O
+  // the linear branch (rec16 given): O_l in the same register layout as O
   v16f ol[4];
   float inv_l = 0.f;
-  if (state_m) lin_epilogue<NW>(qraw, state_m, wpt, bh, I, N, n_qb, s_k0, s_k1, s_k2, s_v0, s_v1, s_v2, ol, inv_l);
+  if (rec16) lin_epilogue<NW>(qraw, rec16, wpt, bh, I, N, n_qb, s_k2, s_v0, s_v1, ol, inv_l);
   if (rok) {
     const size_t ro = ((size_t)bh * N + row) * kD;
 #pragma unroll
@@ -698,7 +715,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k3_attn(
         const int e0 = 32 * ct + 8 * r4 + 4 * g;
         float x0 = o[ct][4 * r4] * inv, x1 = o[ct][4 * r4 + 1] * inv;
         float x2 = o[ct][4 * r4 + 2] * inv, x3 = o[ct][4 * r4 + 3] * inv;
-        if (state_m) {
+        if (rec16) {
           const float4 a = make_float4(ol[ct][4 * r4] * inv_l, ol[ct][4 * r4 + 1] * inv_l, ol[ct][4 * r4 + 2] * inv_l,
                                        ol[ct][4 * r4 + 3] * inv_l);
           if (o_lin) *(float4*)(o_lin + ro + e0) = a;
@@ -713,7 +730,7 @@ hipError_t launch_attn(const Plan& p, const uint16_t* q, uint16_t* out, hipStrea
   const int total = p.BH * p.n_qb;
   const float c0 = p.sm_scale * 1.4426950408889634f;  // log2(e): scores enter exp2
   const bool lin = p.linear && p.topk < p.n_kb;
-  const float* sm = lin ? p.state_m : nullptr;
+  const unsigned char* sm = lin ? p.rec16 : nullptr;
   float* olin = lin ? p.o_lin : nullptr;  // optional export of the linear branch's output
 #define SAGESLA_ATTN(NWV, G)                                                                                     \
   hipLaunchKernelGGL((k3_attn<NWV, G>), dim3(total), dim3(64 * NWV), 0, s, p.q_i8, p.k_i8, p.v_img, p.q_scale,     \

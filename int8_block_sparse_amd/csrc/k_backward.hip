@@ -39,18 +39,10 @@ constexpr float kLog2e = 1.4426950408889634f;
 __device__ __forceinline__ int acc_row(int r) { return 8 * (r >> 2) + 4 * ((threadIdx.x & 63) >> 5) + (r & 3); }
 
 typedef __attribute__((address_space(3))) void bw_lds_void;
-typedef short v4s __attribute__((ext_vector_type(4)));
-typedef short v8s __attribute__((ext_vector_type(8)));
-typedef __attribute__((address_space(3))) v4s lds_v4s;
 
 constexpr int kTileBytes = 64 * 256;  // a swizzled tile: 64 rows of 128 bf16
 
-// Swizzled tiles hold 64 rows of 256 B; the 16-byte chunk c of row r sits at chunk position c ^ tswz(r). Sixteen
-// consecutive rows at one chunk fall on sixteen distinct positions (the row reads of an MFMA operand), and four
-// rows from a multiple of 4 over four aligned chunks fall on sixteen distinct positions (transposing reads).
-__device__ __forceinline__ int tswz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
-// byte offset of the 8-byte unit that holds columns col .. col + 3 (col a multiple of 4) of row r
-__device__ __forceinline__ int toff(int r, int col) { return r * 256 + (((col >> 3) ^ tswz(r)) << 4) + ((col & 4) << 1); }
+// (the swizzled tile layout, tswz / toff, and the transposing read are in device_common.h)
 
 // operand of a 32x32x16 MFMA from a swizzled tile: row r0 + l % 32, columns k0 + 8 (l / 32) .. + 7 (l = lane)
 __device__ __forceinline__ v8bf row_op(const unsigned char* t, int r0, int k0, int l) {

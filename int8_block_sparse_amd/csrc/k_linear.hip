@@ -130,6 +130,121 @@ __global__ __launch_bounds__(256) void k4_states(const uint16_t* __restrict__ k,
 }
 
 // ---------------------------------------------------------------------------------------------------------
+// k4_states16 (the forward): the same per-block product, stored in fp16 after scaling the whole block by a power
+// of two. With M the largest magnitude over H_J^T and Z_J and k the exponent with M < 2^k (frexp), every value x
+// is stored as fp16(x * 2^(15 - k)), all below 2^15 in magnitude, and e_J = k - 15, so x = entry * 2^e_J up to the
+// fp16 rounding (relative 2^-11); an all-zero block stores zeros with e_J = kExpZero. Table [BH][kStateX / 128]
+// [n_kb][128] fp16: the 128 columns of column group x of block J are 256 contiguous bytes.
+// ---------------------------------------------------------------------------------------------------------
+constexpr int kExpZero = -100000;
+
+__global__ __launch_bounds__(256) void k4_states16(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+                                                  uint16_t* __restrict__ table, int32_t* __restrict__ bexp, int N,
+                                                  int n_kb) {
+  __shared__ __attribute__((aligned(16))) unsigned char s_pkh[kD * 128];
+  __shared__ __attribute__((aligned(16))) unsigned char s_pkl[kD * 128];
+  __shared__ __attribute__((aligned(16))) unsigned char s_vt[kD * 128];
+  __shared__ float s_z[16][kD + 1];
+  __shared__ float s_m[4];
+  const int J = blockIdx.x, bh = blockIdx.y;
+  const int t = threadIdx.x, w = t >> 6, l = t & 63, g = l >> 5, lr = l & 31;
+  const int cg = t & 15, kg = t >> 4;  // loader: channels 8cg..+7, keys 4kg..+3
+  const size_t base = ((size_t)bh * N + (size_t)J * kBlkK) * kD;
+  const int nv = min(kBlkK, N - J * kBlkK);
+
+  // ---- load, phi, split, transpose into LDS (as k4_states)
+  uint32_t kw[4][4], vw[4][4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const int r = 4 * kg + b;
+    uint4 a = make_uint4(0, 0, 0, 0), c = make_uint4(0, 0, 0, 0);
+    if (r < nv) {
+      a = *(const uint4*)(k + base + (size_t)r * kD + cg * 8);
+      c = *(const uint4*)(v + base + (size_t)r * kD + cg * 8);
+    }
+    kw[b][0] = a.x; kw[b][1] = a.y; kw[b][2] = a.z; kw[b][3] = a.w;
+    vw[b][0] = c.x; vw[b][1] = c.y; vw[b][2] = c.z; vw[b][3] = c.w;
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int row = cg * 8 + e;
+    float pk[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const float x = (e & 1) ? bf16_hi(kw[b][e >> 1]) : bf16_lo(kw[b][e >> 1]);
+      pk[b] = (4 * kg + b < nv) ? phi_f(x) : 0.f;
+    }
+    uint32_t h01, l01, h23, l23;
+    split2(pk[0], pk[1], h01, l01);
+    split2(pk[2], pk[3], h23, l23);
+    const int off = lds_off(row, 4 * kg);
+    *(uint2*)(s_pkh + off) = make_uint2(h01, h23);
+    *(uint2*)(s_pkl + off) = make_uint2(l01, l23);
+    const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+    *(uint2*)(s_vt + off) = make_uint2(__builtin_amdgcn_perm(vw[1][e >> 1], vw[0][e >> 1], sel),
+                                       __builtin_amdgcn_perm(vw[3][e >> 1], vw[2][e >> 1], sel));
+    s_z[kg][row] = (pk[0] + pk[1]) + (pk[2] + pk[3]);
+  }
+  __syncthreads();
+
+  // ---- H^T = V^T phi(K): m = e (4 tiles), n = c (tile w), k = key (4 steps of 16)
+  v16f acc[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) acc[mt] = (v16f){};
+  const int crow = 32 * w + lr;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int key = 16 * s + 8 * g;
+    const v8bf bh_ = *(const v8bf*)(s_pkh + lds_off(crow, key));
+    const v8bf bl_ = *(const v8bf*)(s_pkl + lds_off(crow, key));
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const v8bf a = *(const v8bf*)(s_vt + lds_off(32 * mt + lr, key));
+      acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bh_, acc[mt], 0, 0, 0);
+      acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bl_, acc[mt], 0, 0, 0);
+    }
+  }
+  float z = 0.f;
+  if (t < kD) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) z += s_z[j][t];
+  }
+
+  // ---- the block's largest magnitude and its exponent
+  float m = z;  // z >= 0 (0 on threads past the 128 columns)
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) m = fmaxf(m, fabsf(acc[mt][r]));
+  m = wave_max_f32(m);
+  if (l == 0) s_m[w] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
+  int kx = 0;
+  (void)frexpf(m, &kx);  // m < 2^kx
+  const int sh = 15 - kx;
+  if (t == 0) bexp[(size_t)bh * n_kb + J] = m > 0.f ? kx - 15 : kExpZero;
+
+  // ---- store: neighbouring columns c, c + 1 of one row go out as one 4-byte word. Lanes c and c ^ 1 trade one
+  // value of each register pair (r, r + 1) (rows e, e + 1): the even lane writes row e, the odd lane row e + 1.
+  const size_t gstride = (size_t)n_kb * 128;  // halves between column groups
+  uint16_t* tb = table + (size_t)bh * (kStateX / 128) * gstride + (size_t)J * 128;
+  const bool odd = crow & 1;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      const float a0 = acc[mt][r], a1 = acc[mt][r + 1];
+      const float send = odd ? a0 : a1;
+      const float got = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(send), 0xB1, 0xF, 0xF, false));
+      const float x0 = odd ? got : a0, x1 = odd ? a1 : got;
+      const int e = 32 * mt + 8 * (r >> 2) + 4 * g + (r & 3) + (odd ? 1 : 0);
+      *(uint32_t*)(tb + (size_t)e * gstride + (crow & ~1)) = pack_f16x2(ldexpf(x0, sh), ldexpf(x1, sh));
+    }
+  if (t < kD) tb[(size_t)kD * gstride + t] = (uint16_t)(pack_f16x2(ldexpf(z, sh), 0.f) & 0xffffu);
+}
+
+// ---------------------------------------------------------------------------------------------------------
 // k4_mask: one wave per (bh, I) row. Bit J of word J/32 is 1 iff query block I did not select key block J
 // (bits past n_kb are 0). Built in LDS with atomic ANDs, so an index that occurs twice clears its bit once, as
 // a set would. Stored word-major per head, mask[bh][word][I] with rows padded to qpad, so that one word of a
@@ -189,6 +304,8 @@ constexpr int kGemmRows = kGemmIT * 32;  // query blocks per workgroup; mask row
 
 // wait until at most N of this wave's vector-memory operations are in flight (and every LDS operation is done),
 // then a workgroup barrier
+__device__ __forceinline__ void wait_vmem_all_lin() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 template <int N> __device__ __forceinline__ void gemm_sync() {
   static_assert(N >= 0 && N < 16, "vmcnt immediate");
   asm volatile("" ::: "memory");
@@ -402,19 +519,218 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k4_gemm(const float* __restri
     }
 }
 
+// ---------------------------------------------------------------------------------------------------------
+// k4_gemm16 (the forward): the same keep-mask x table product over the fp16 table of k4_states16. Each block J
+// carries its own power of two 2^e_J, so the A operand is keep[I][J] * 2^(e_J - E), E = max_J e_J over the head
+// (exact in fp16 down to 2^-24; a block more than 24 binades below the head's largest is dropped), and the sums are
+// the remaining state times 2^-E, H_m and Z_m alike (the linear branch's quotient does not see the common factor).
+// grid (kStateX / 128 column groups, ceil(n_qb / 640) query-block chunks, BH), 512 threads (8 waves).
+// Step = 32 key blocks (two k-steps of 16) = one mask word per query block. Table slices (32 rows of 256 B)
+// arrive by buffer loads to LDS with their 16-byte chunks swizzled (tswz), three steps ahead, with the chunk's
+// mask words; four-slot rings, one wait and one barrier per step. B operands come straight from the slice
+// by transposing reads; A operands are the byte table's 0 / 1.0 pattern ANDed with the step's eight scales.
+// Wave w owns query tiles 5 (w / 2) .. +4 and column tiles 2 (w % 2), +1.
+// The store writes each query block's row e = x of H_m^T as an fp16 plane row with its own factor (the row's
+// largest magnitude set below 2^15), and the Z group as fp32.
+// ---------------------------------------------------------------------------------------------------------
+constexpr int kAExpMin = -24;  // the smallest A scale 2^d, an fp16 subnormal
+
+__global__ __launch_bounds__(kGemmThreads, 1) void k4_gemm16(const uint16_t* __restrict__ table,
+                                                            const int32_t* __restrict__ bexp,
+                                                            const uint32_t* __restrict__ mask,
+                                                            unsigned char* __restrict__ rec, int n_qb, int n_kb,
+                                                            int n_kbw, int qpad) {
+  // four-slot rings: table slices (8 KB used; slots 0 and 1 are also the store's fp32 staging) and mask words
+  __shared__ __attribute__((aligned(1024))) unsigned char s_st0[16384], s_st1[16384], s_st2[8192], s_st3[8192];
+  __shared__ __attribute__((aligned(1024))) uint32_t s_w0[kGemmRows + 128], s_w1[kGemmRows + 128],
+      s_w2[kGemmRows + 128], s_w3[kGemmRows + 128];
+  __shared__ __attribute__((aligned(1024))) uint4 s_lut[256];            // byte -> 8 fp16 of 0 / 1.0
+  __shared__ __attribute__((aligned(16))) uint16_t s_asc[kMaxKeyBlocks + 64];  // fp16 2^(e_J - E)
+  __shared__ int s_red[kGemmThreads / 64];
+  constexpr int n_xt = kStateX / 128;
+  const int xg = blockIdx.x, ic = blockIdx.y, bh = blockIdx.z;
+  const int t = threadIdx.x, w = __builtin_amdgcn_readfirstlane(t >> 6), l = t & 63, g = l >> 5, lr = l & 31;
+  const int I0 = ic * kGemmRows;
+  const int n_it = min(kGemmIT, (n_qb - I0 + 31) >> 5);
+  const int nss = n_kbw;
+  const __amdgpu_buffer_rsrc_t rt = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(table + (size_t)bh * n_xt * n_kb * 128), (short)0, n_xt * n_kb * 256, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rm = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint32_t*>(mask + (size_t)bh * n_kbw * qpad), (short)0, n_kbw * qpad * 4, 0x00020000);
+  if (t < 256) {
+    uint32_t d[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) d[k] = ((t >> (2 * k)) & 1 ? 0x3C00u : 0u) | ((t >> (2 * k + 1)) & 1 ? 0x3C000000u : 0u);
+    s_lut[t] = make_uint4(d[0], d[1], d[2], d[3]);
+  }
+  // the head's largest block exponent, then the A scales of every key block (0 past n_kb)
+  const int32_t* be = bexp + (size_t)bh * n_kb;
+  int emax = INT_MIN;
+  for (int J = t; J < n_kb; J += kGemmThreads) emax = max(emax, be[J]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) emax = max(emax, __shfl_xor(emax, o));
+  if (l == 0) s_red[w] = emax;
+  __syncthreads();
+  int E = s_red[0];
+#pragma unroll
+  for (int k = 1; k < kGemmThreads / 64; ++k) E = max(E, s_red[k]);
+  for (int J = t; J < 32 * n_kbw; J += kGemmThreads) {
+    uint32_t h = 0;
+    if (J < n_kb) {
+      const int d = be[J] - E;  // <= 0
+      h = d >= -14 ? (uint32_t)(d + 15) << 10 : d >= kAExpMin ? 1u << (d + 24) : 0u;
+    }
+    s_asc[J] = (uint16_t)h;
+  }
+
+  // (every load offset is a per-lane offset, checked against the descriptor's range: past it a load reads zeros)
+  const uint32_t wlane = (uint32_t)(l * 16 + (I0 + 256 * w) * 4);
+  auto dma_w = [&](int ss, uint32_t* dst) {
+    if (w < 3)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rm, (__attribute__((address_space(3))) void*)(dst + 256 * w), 16,
+                                               wlane + (uint32_t)(ss * qpad * 4), 0, 0, 0);
+  };
+  // slice of step ss: rows 32 ss .. +31 of column group xg; wave w loads rows 4w .. 4w + 3, lane l row 4w + l / 16 at
+  // chunk position l % 16 with the chunk (l % 16) ^ tswz(row). Rows past n_kb (their A is 0) read the next column
+  // group's rows (finite) or, past the head's table, zeros.
+  const int srow = 4 * w + (l >> 4);
+  const uint32_t slane = (uint32_t)(srow * 256 + 16 * ((l & 15) ^ tswz(srow)) + xg * n_kb * 256);
+  auto dma_st = [&](int ss, unsigned char* dst) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rt, (__attribute__((address_space(3))) void*)(dst + w * 1024), 16,
+                                             slane + (uint32_t)(ss * 32 * 256), 0, 0, 0);
+  };
+
+  const int wit = 5 * (w >> 1), wxt = 2 * (w & 1);
+  v16f acc[10];
+#pragma unroll
+  for (int k = 0; k < 10; ++k) acc[k] = (v16f){};
+
+  auto step = [&](int ss, const uint32_t* __restrict__ W, const unsigned char* __restrict__ st,
+                  uint32_t* __restrict__ w_fill, unsigned char* __restrict__ st_fill) {
+    // slice ss and words ss (issued three steps back) have landed; the two later steps' loads may stay in flight
+    if (w < 3)
+      gemm_sync<4>();
+    else
+      gemm_sync<2>();
+    dma_st(ss + 3, st_fill);
+    dma_w(ss + 3, w_fill);
+    uint32_t wq[5];
+#pragma unroll
+    for (int q = 0; q < 5; ++q) wq[q] = W[32 * (wit + q) + lr];
+    uint4 sv[2];
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) sv[sub] = *(const uint4*)&s_asc[32 * ss + 16 * sub + 8 * g];
+    v8h bop[2][2];
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) bop[sub][c] = __builtin_bit_cast(v8h, tr_col_op(st, 16 * sub, 32 * (wxt + c), l));
+#pragma unroll
+    for (int i = 0; i < 10; ++i) {  // tiles past n_it have zero words, never stored
+      const int sub = i / 5, q = i % 5;
+      const uint4 m8 = s_lut[(wq[q] >> (16 * sub + 8 * g)) & 0xFFu];
+      const v8h a = __builtin_bit_cast(
+          v8h, make_uint4(m8.x & sv[sub].x, m8.y & sv[sub].y, m8.z & sv[sub].z, m8.w & sv[sub].w));
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+        acc[2 * q + c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, bop[sub][c], acc[2 * q + c], 0, 0, 0);
+    }
+  };
+
+  // prologue: slices and words of steps 0-2, interleaved so that every wave's count per step is fixed
+  dma_st(0, s_st0);
+  dma_w(0, s_w0);
+  dma_st(1, s_st1);
+  dma_w(1, s_w1);
+  dma_st(2, s_st2);
+  dma_w(2, s_w2);
+  for (int ss = 0; ss < nss; ss += 4) {
+    step(ss, s_w0, s_st0, s_w3, s_st3);
+    if (ss + 1 < nss) step(ss + 1, s_w1, s_st1, s_w0, s_st0);
+    if (ss + 2 < nss) step(ss + 2, s_w2, s_st2, s_w1, s_st1);
+    if (ss + 3 < nss) step(ss + 3, s_w3, s_st3, s_w2, s_st2);
+  }
+  wait_vmem_all_lin();  // no load may land in the staging below
+
+  // Store. acc[2q + c][r] is C[I][x] with I = I0 + 32 (wit + q) + 8(r/4) + 4g + r%4, x = 128 xg + 32 (wxt + c) + lr.
+  if (xg == kD) {  // Z_m, fp32
+#pragma unroll
+    for (int q = 0; q < 5; ++q)
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int I = I0 + 32 * (wit + q) + 8 * (r >> 2) + 4 * g + (r & 3);
+          if (wit + q < n_it && I < n_qb)
+            *(float*)(rec + ((size_t)bh * n_qb + I) * kRec16Bytes + kRec16Z + 4 * (32 * (wxt + c) + lr)) =
+                acc[2 * q + c][r];
+        }
+    return;
+  }
+  // row e = xg of H_m^T: half-rounds of 64 query blocks staged in LDS as fp32 (columns 0-63 in s_st0, 64-127 in
+  // s_st1); then 16 threads per query block take 8 columns each, agree on the row's largest magnitude and write
+  // the fp16 plane row (16 B each) and the row's factor.
+  float* const sg0 = (float*)s_st0;
+  float* const sg1 = (float*)s_st1;
+#pragma unroll
+  for (int q = 0; q < 5; ++q)
+#pragma unroll
+    for (int hr = 0; hr < 2; ++hr) {
+      __syncthreads();
+      if ((w >> 2) == hr) {
+        float* hw_ = (w & 1) ? sg1 : sg0;
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            hw_[(32 * ((w >> 1) & 1) + 8 * (r >> 2) + 4 * g + (r & 3)) * 64 + 32 * c + lr] = acc[2 * q + c][r];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {  // 64 rows x 16 chunks of 8 columns
+        const int u = t + kGemmThreads * j, row = u >> 4, k8 = u & 15;
+        const int it = 5 * (2 * hr + (row >> 5)) + q, I = I0 + 32 * it + (row & 31);
+        const float* src = (k8 < 8 ? sg0 : sg1) + row * 64 + 8 * (k8 & 7);
+        const float4 x0 = *(const float4*)src, x1 = *(const float4*)(src + 4);
+        float mx = fmaxf(fmaxf(fmaxf(fabsf(x0.x), fabsf(x0.y)), fmaxf(fabsf(x0.z), fabsf(x0.w))),
+                         fmaxf(fmaxf(fabsf(x1.x), fabsf(x1.y)), fmaxf(fabsf(x1.z), fabsf(x1.w))));
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+        int kx = 0;
+        (void)frexpf(mx, &kx);  // mx < 2^kx
+        const int sh = 15 - kx;
+        const uint4 hv = make_uint4(pack_f16x2(ldexpf(x0.x, sh), ldexpf(x0.y, sh)),
+                                    pack_f16x2(ldexpf(x0.z, sh), ldexpf(x0.w, sh)),
+                                    pack_f16x2(ldexpf(x1.x, sh), ldexpf(x1.y, sh)),
+                                    pack_f16x2(ldexpf(x1.z, sh), ldexpf(x1.w, sh)));
+        if (it < n_it && I < n_qb) {
+          unsigned char* r0 = rec + ((size_t)bh * n_qb + I) * kRec16Bytes;
+          *(uint4*)(r0 + out_off(xg, 8 * k8)) = hv;
+          if (k8 == 0) *(float*)(r0 + kRec16F + 4 * xg) = mx > 0.f ? ldexpf(1.f, kx - 15) : 0.f;
+        }
+      }
+    }
+}
+
 int mask_row_pad(int n_qb) { return (n_qb + kGemmRows - 1) / kGemmRows * kGemmRows; }
 
 hipError_t launch_linear(const Plan& p, const uint16_t* k, const uint16_t* v, hipStream_t s) {
   hipLaunchKernelGGL(k4_prep_wp, dim3(kD * kD / 256), dim3(256), 0, s, (const uint16_t*)p.w_proj, p.wpt);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k4_states, dim3(p.n_kb, p.BH), dim3(256), 0, s, k, v, p.state, p.N, p.n_kb, 7, kStateX / 128);
+  if (p.lin_precise)
+    hipLaunchKernelGGL(k4_states, dim3(p.n_kb, p.BH), dim3(256), 0, s, k, v, p.state, p.N, p.n_kb, 7, kStateX / 128);
+  else
+    hipLaunchKernelGGL(k4_states16, dim3(p.n_kb, p.BH), dim3(256), 0, s, k, v, p.state16, p.state_exp, p.N, p.n_kb);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int rows = p.BH * p.n_qb, n_kbw = (p.n_kb + 31) / 32, qpad = mask_row_pad(p.n_qb);
   hipLaunchKernelGGL(k4_mask, dim3(rows), dim3(64), 0, s, p.block_idx, p.keep_mask, p.n_qb, p.n_kb, p.topk, n_kbw,
                      qpad);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  return launch_state_sum(p.state, p.keep_mask, p.state_m, p.n_qb, p.n_kb, qpad, p.BH, s);
+  if (p.lin_precise) return launch_state_sum(p.state, p.keep_mask, p.state_m, p.n_qb, p.n_kb, qpad, p.BH, s);
+  hipLaunchKernelGGL(k4_gemm16, dim3(kStateX / 128, qpad / kGemmRows, p.BH), dim3(kGemmThreads), 0, s, p.state16,
+                     p.state_exp, p.keep_mask, p.rec16, p.n_qb, p.n_kb, n_kbw, qpad);
+  return hipGetLastError();
 }
 
 hipError_t launch_state_sum(const float* table, const uint32_t* mask, float* out, int n_out, int n_in, int pad, int BH,

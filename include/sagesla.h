@@ -166,6 +166,17 @@ size_t sagesla_backward_workspace_bytes(const sagesla_params* p);
 sagesla_status sagesla_backward(const void* q, const void* k, const void* v, const void* dout, float* dq, float* dk,
                                 float* dv, float* dw_proj, const sagesla_params* p, void* stream);
 
+/* The forward for callers that cannot allocate device memory (code under HIP graph capture, tight serving loops,
+   harnesses that forbid hipMalloc): the same computation and results as sagesla_forward, with the workspace
+   taken from a device array of SAGESLA_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on
+   (p->workspace and p->workspace_bytes are ignored). The caller still passes q, k, v, out and any exports.
+   Returns SAGESLA_E_WORKSPACE when sagesla_workspace_bytes(p) exceeds that size. Calls no allocating routine;
+   the first call on a device looks up the array's address there (with that device current). Every call on one
+   GPU shares its array, so calls that overlap on one GPU (other streams, other host threads) race. */
+#define SAGESLA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+sagesla_status sagesla_forward_noalloc(const void* q, const void* k, const void* v, void* out,
+                                       const sagesla_params* p, void* stream);
+
 /* Text of a status code (static storage). */
 const char* sagesla_status_str(sagesla_status s);
 

@@ -16,7 +16,7 @@ __all__ = [
     "LIB_PATH", "load", "Params", "SageSLAError", "topk_blocks", "n_blocks", "workspace_bytes", "validate",
     "quantize", "select", "forward", "LINEAR", "SMOOTH_K", "USE_GIVEN_MASK", "QUANT_GROUP32", "QK_RMSNORM", "STATUS", "STAGES",
     "stage_events",
-    "stage_ms", "Config", "backward",
+    "stage_ms", "Config", "backward", "forward_noalloc", "NOALLOC_SCRATCH_BYTES",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsagesla.so")
@@ -27,6 +27,7 @@ USE_GIVEN_MASK = 0x4
 QUANT_GROUP32 = 0x8  # one INT8 scale per 32 tokens of Q and of K (thread-level granularity)
 QK_RMSNORM = 0x10  # RMSNorm of Q and K over all heads of each token first
 
+NOALLOC_SCRATCH_BYTES = 64 << 20  # SAGESLA_NOALLOC_SCRATCH_BYTES
 STATUS = {0: "OK", 1: "E_NULL", 2: "E_SHAPE", 3: "E_UNSUPPORTED", 4: "E_WORKSPACE", 5: "E_ALIGN", 6: "E_HIP"}
 STAGES = ("quantize", "select", "linear", "attn")
 
@@ -83,6 +84,8 @@ def load():
     lib.sagesla_select.restype = ctypes.c_int
     lib.sagesla_forward.argtypes = [vp, vp, vp, vp, P, vp]
     lib.sagesla_forward.restype = ctypes.c_int
+    lib.sagesla_forward_noalloc.argtypes = [vp, vp, vp, vp, P, vp]
+    lib.sagesla_forward_noalloc.restype = ctypes.c_int
     lib.sagesla_backward_workspace_bytes.argtypes = [P]
     lib.sagesla_backward_workspace_bytes.restype = ctypes.c_size_t
     lib.sagesla_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, P, vp]
@@ -268,26 +271,43 @@ def forward(q, k, v, w_proj=None, *, topk: int, blk_q: int = 128, blk_k: int = 6
     norm: (gamma_q, gamma_k, eps) normalizes Q and K first (RMSNorm over the H*D channels of each token).
     export=True also returns a dict of every intermediate (codes, scales, K mean, pooled means, block lists,
     and the linear-branch output). Runs asynchronously on the current stream."""
+    return _forward(q, k, v, w_proj, topk, blk_q, blk_k, linear, smooth_k, sm_scale, mask, out, workspace, export,
+                    events, group32, norm, noalloc=False)
+
+
+def forward_noalloc(q, k, v, w_proj=None, *, topk: int, blk_q: int = 128, blk_k: int = 64, linear: bool = True,
+                    smooth_k: bool = True, sm_scale: float = 0.0, mask=None, out=None, export: bool = False,
+                    events=None, group32: bool = False, norm=None):
+    """forward() through sagesla_forward_noalloc: no workspace argument; the library's own device scratch of
+    NOALLOC_SCRATCH_BYTES serves (calls that overlap on one GPU race). Same results as forward()."""
+    return _forward(q, k, v, w_proj, topk, blk_q, blk_k, linear, smooth_k, sm_scale, mask, out, None, export,
+                    events, group32, norm, noalloc=True)
+
+
+def _forward(q, k, v, w_proj, topk, blk_q, blk_k, linear, smooth_k, sm_scale, mask, out, workspace, export, events,
+             group32, norm, noalloc):
     B, H, N, D = q.shape
     cfg = Config(B, H, N, D, blk_q, blk_k, topk, linear, smooth_k, sm_scale, group32, norm is not None)
     if out is None:
         import torch
         out = torch.empty_like(q)
     _shape_check(q, k, v, out, cfg)
-    ws = _workspace(cfg, q.device, workspace)
+    ws = None if noalloc else _workspace(cfg, q.device, workspace)
     ex = _exports(cfg, q.device) if export else {}
     if mask is not None:
         if not export:
             ex = {}
         ex["block_idx"] = mask
     ptrs = {name: _ptr(t) for name, t in ex.items()}
-    p = cfg.params(w_proj=_ptr(w_proj), workspace=ws.data_ptr(), workspace_bytes=ws.numel(),
-                   given_mask=mask is not None, **ptrs, **_norm_args(norm, H, D))
+    p = cfg.params(w_proj=_ptr(w_proj), workspace=None if noalloc else ws.data_ptr(),
+                   workspace_bytes=0 if noalloc else ws.numel(), given_mask=mask is not None, **ptrs,
+                   **_norm_args(norm, H, D))
     if events is not None:
         arr = (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
         p.events = ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p))
-    _check(load().sagesla_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), ctypes.byref(p),
-                                  _stream(q.device)), "sagesla_forward")
+    fn = load().sagesla_forward_noalloc if noalloc else load().sagesla_forward
+    _check(fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), ctypes.byref(p), _stream(q.device)),
+           "sagesla_forward_noalloc" if noalloc else "sagesla_forward")
     return (out, ex) if export else out
 
 

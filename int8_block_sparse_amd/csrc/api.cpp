@@ -3,6 +3,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "internal.h"
 #include "sagesla.h"
 #include "w8a8.h"
@@ -432,6 +434,60 @@ sagesla_status sagesla_backward(const void* q, const void* k, const void* v, con
   if (pl.qk_norm)  // dq, dk hold the gradients at the normalized values: carry them through the norm
     SAGESLA_TRY(launch_norm_backward(b, (const uint16_t*)q, (const uint16_t*)k, p->dq_norm_w, p->dk_norm_w, s));
   return SAGESLA_OK;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------------------------------------
+// The forward without a caller workspace (include/sagesla.h: sagesla_forward_noalloc)
+// ---------------------------------------------------------------------------------------------------------
+namespace {
+
+constexpr int kMaxDevices = 64;
+// The scratch of sagesla_forward_noalloc. In host code this name only stands for the array: its device address on
+// a device is looked up there (scratch_address) and only that address is ever passed on.
+static __device__ __align__(256) unsigned char scratch[SAGESLA_NOALLOC_SCRATCH_BYTES];
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices];  // per device, after the first lookup
+
+// device address of the scratch array on the current device, looked up once per device
+sagesla_status scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= kMaxDevices) return SAGESLA_E_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e);
+    if (!ptr || misaligned(ptr, kAlign)) return SAGESLA_E_ALIGN;
+    g_scratch_addr[dev] = ptr;
+  }
+  *out = g_scratch_addr[dev];
+  return SAGESLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+sagesla_status sagesla_forward_noalloc(const void* q, const void* k, const void* v, void* out,
+                                       const sagesla_params* p, void* stream) {
+  sagesla_status st = check_params(p);
+  if (st != SAGESLA_OK) return st;
+  if (!q || !k || !v || !out) return SAGESLA_E_NULL;
+  if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(out, 16)) return SAGESLA_E_ALIGN;
+  if ((p->flags & SAGESLA_USE_GIVEN_MASK) && p->topk > 0 && !p->block_idx) return SAGESLA_E_NULL;
+  Plan pl;
+  make_plan(p, nullptr, &pl);
+  if (pl.ws_bytes > SAGESLA_NOALLOC_SCRATCH_BYTES) return SAGESLA_E_WORKSPACE;
+  void* ws = nullptr;  // (the first device access of this call)
+  if ((st = scratch_address(&ws)) != SAGESLA_OK) return st;
+  sagesla_params p2 = *p;
+  p2.workspace = ws;
+  p2.workspace_bytes = SAGESLA_NOALLOC_SCRATCH_BYTES;
+  return sagesla_forward(q, k, v, out, &p2, stream);
 }
 
 const char* sagesla_status_str(sagesla_status s) {

@@ -136,6 +136,19 @@ def test_tensor_pointer_validation(lib):
     assert lib.sagesla_last_hip_error() == 0
 
 
+@cpu_only
+def test_forward_noalloc_validation(lib):
+    # the same checks as sagesla_forward, then the plan against the library's scratch, all before any device call
+    nf = lambda p, q=FAKE, out=FAKE: lib.sagesla_forward_noalloc(q, FAKE, FAKE, out, ctypes.byref(p), None)
+    assert nf(good(D=64)) == 3 and nf(good(topk=-1)) == 2 and nf(good(w_proj=None)) == 1
+    assert nf(good(), q=None) == 1 and nf(good(), out=FAKE + 2) == 5
+    assert nf(good(flags=sg.LINEAR | sg.USE_GIVEN_MASK)) == 1
+    big = sg.Config(B=1, H=12, N=32760, topk=51, linear=True).params(w_proj=FAKE)
+    assert lib.sagesla_workspace_bytes(ctypes.byref(big)) > sg.NOALLOC_SCRATCH_BYTES
+    assert nf(big) == 4  # more than the scratch holds
+    assert lib.sagesla_last_hip_error() == 0
+
+
 def bwd(lib, p, dq=FAKE, dk=FAKE, dv=FAKE, dw=FAKE, q=FAKE):
     return lib.sagesla_backward(q, FAKE, FAKE, FAKE, dq, dk, dv, dw, ctypes.byref(p), None)
 
@@ -144,7 +157,7 @@ def bwd(lib, p, dq=FAKE, dk=FAKE, dv=FAKE, dw=FAKE, q=FAKE):
 def test_backward_validation(lib):
     ok = dict(block_idx=FAKE)
     need = lib.sagesla_backward_workspace_bytes(ctypes.byref(good(**ok)))
-    assert need > lib.sagesla_workspace_bytes(ctypes.byref(good(**ok)))  # the forward plan plus the backward's
+    assert need > lib.sagesla_workspace_bytes(ctypes.byref(good(**ok)))  # fp32 states, O_l and the gradients' buffers
     assert bwd(lib, good()) == 1                       # topk > 0 without a selection
     assert bwd(lib, good(**ok), dq=None) == 1
     assert bwd(lib, good(**ok), q=None) == 1

@@ -44,13 +44,14 @@ HEADLINE = "wan14b-720p-sla-pair"
 PEAK_INT8_TOPS = 5000.0  # MI355X dense INT8 MFMA
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense BF16 MFMA
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E
-# Layouts of the linear branch as the kernels store them: the fp32 state table (H_J^T and Z_J per key block) and
-# the remaining state of each query block (bf16 hi and lo planes of H_m^T, then Z_m in fp32)
-STATE_BYTES_PER_BLOCK = (128 * 128 + 128) * 4
-REMAINING_BYTES_PER_QBLOCK = 2 * 128 * 128 * 2 + 128 * 4
-# bf16 products of bq x D x D per query block in the attention kernel's linear epilogue: phi(Q) H_m as hi*hi +
-# hi*lo + lo*hi, then (.) W_p on the hi and lo halves of the first result
-EPILOGUE_PRODUCTS_EXECUTED = 5
+# Layouts of the forward's linear branch as the kernels store them: the fp16 state table (H_J^T and Z_J per key
+# block, with the block's exponent) and the remaining state of each query block (the fp16 plane of H_m^T, then Z_m
+# and the plane rows' factors in fp32)
+STATE_BYTES_PER_BLOCK = (128 * 128 + 128) * 2 + 4
+REMAINING_BYTES_PER_QBLOCK = 128 * 128 * 2 + 2 * 128 * 4
+# products of bq x D x D per query block in the attention kernel's linear epilogue: phi(Q) H_m (one fp16 product),
+# then (.) W_p on the bf16 hi and lo halves of the first result
+EPILOGUE_PRODUCTS_EXECUTED = 3
 # whole heads the CPU baseline runs per workload (about 10-30 s of oracle time each); on the longest layer one
 # head's attention outputs are formed for a sample of its query blocks only
 CPU_HEADS = {"tiny": 2, "wan1.3b-480p-dense": 4, "wan1.3b-480p-sla": 6, "wan14b-720p-sla-pair": 2,

@@ -117,7 +117,8 @@ void make_plan(const sagesla_params* p, unsigned char* ws, Plan* pl, bool backwa
     } else {
       pl->state16 = (uint16_t*)take(BH * nkb * kStateX * sizeof(uint16_t));
       pl->state_exp = (int32_t*)take(BH * nkb * sizeof(int32_t));
-      pl->rec16 = (unsigned char*)take(BH * nqb * (size_t)kRec16Bytes);
+      pl->plane16 = (unsigned char*)take(BH * D * nqb * 256);
+      pl->aux16 = (unsigned char*)take(BH * nqb * (size_t)kAuxBytes);
     }
   }
   pl->ws_bytes = off;

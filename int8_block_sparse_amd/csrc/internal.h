@@ -11,12 +11,14 @@ constexpr int kD = 128;       // head dim (the only one supported)
 constexpr int kBlkK = 64;     // key block
 constexpr int kMaxKeyBlocks = 20480;  // n_kb limit of the parameter checks (sizes fixed-size LDS tables)
 constexpr int kStateX = kD * kD + kD;  // floats per linear-branch state: H^T (D×D, e-major) then Z (D)
-// The forward's remaining-state record of one query block: H_m^T as an fp16 plane (128 rows e of 128 columns c, in
-// the attention epilogue's swizzled LDS layout), then Z_m (fp32 [D]), then one fp32 factor per row e (a plane row's
-// values times its factor give that row of H_m^T). H_m and Z_m share one per-head power-of-two scale.
-constexpr int kRec16Z = 32768;
-constexpr int kRec16F = kRec16Z + kD * 4;
-constexpr int kRec16Bytes = kRec16F + kD * 4;
+// The forward's remaining state of one query block: H_m^T as an fp16 plane of 128 rows e of 128 columns c, each row
+// 256 B in the attention epilogue's swizzled LDS layout, stored row-major over the query blocks of a head
+// ([BH][e][n_qb][256 B]: the product kernel writes one e for every query block); and an aux record per query block
+// ([BH][n_qb][kAuxBytes]): Z_m (fp32 [D]) then one fp32 factor per row e (a plane row's values times its factor
+// give that row of H_m^T). H_m and Z_m share one per-head power-of-two scale.
+constexpr int kAuxZ = 0;
+constexpr int kAuxF = kD * 4;
+constexpr int kAuxBytes = 2 * kD * 4;
 
 // Everything a launch needs, resolved from the parameter block: sizes and where each intermediate lives
 // (a caller's export buffer or a slice of the workspace).
@@ -51,7 +53,8 @@ struct Plan {
   // the forward's linear branch (fp16 state table)
   uint16_t* state16;      // [BH][kStateX / 128][n_kb][128] fp16: block J's state times 2^-e_J
   int32_t* state_exp;     // [BH][n_kb] e_J
-  unsigned char* rec16;   // [BH][n_qb] remaining-state records of kRec16Bytes
+  unsigned char* plane16; // [BH][D][n_qb][256 B] rows of the fp16 planes of H_m^T
+  unsigned char* aux16;   // [BH][n_qb][kAuxBytes] Z_m and the plane rows' factors
   // the backward's linear branch (lin_precise: fp32 state table, remaining state as bf16 hi + lo planes)
   bool lin_precise;
   float* state;         // [BH][kStateX / 128][n_kb][128]   per-block states, tiles of 128 columns
@@ -70,7 +73,7 @@ hipError_t launch_quant(const Plan& p, const uint16_t* q, const uint16_t* k, con
 hipError_t launch_scores(const Plan& p, hipStream_t s);
 hipError_t launch_topk(const Plan& p, hipStream_t s);
 // K4: linear branch (block states, sum over the unselected blocks, contraction with phi(Q) and W_p): the forward's
-// fp16 table and records (state16, state_exp, rec16), or with lin_precise the backward's fp32 table and hi + lo
+// fp16 table and remaining state (state16, state_exp, plane16, aux16), or with lin_precise the backward's fp32 table and hi + lo
 // records (state, state_m)
 hipError_t launch_linear(const Plan& p, const uint16_t* k, const uint16_t* v, hipStream_t s);
 // K3: block-sparse INT8 attention, epilogue adds the linear branch and writes bf16

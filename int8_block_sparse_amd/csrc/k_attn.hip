@@ -293,33 +293,44 @@ __device__ __forceinline__ void attn_iter(const unsigned char* __restrict__ sk_n
 // Linear branch of one query block, run at the end of the attention kernel (the ring's LDS is free then):
 //   U^T[e][i] = f_e sum_c P^T[e][c] phi'(Q)^T[c][i]   (A = the record's fp16 plane from LDS, B = phi' in registers)
 //   O^T[f][i] = sum_e W_p^T[f][e] U^T[e][i]          (A = W_p^T from LDS, B = U^T hi/lo from the accumulators)
-// and den[i] = phi'(q_i) . Z_m. The record holds H_m^T as an fp16 plane P (rows e) with one factor f_e per row, and
-// Z_m in fp32, H_m and Z_m sharing one power-of-two scale; phi' = phi scaled per row by the power of two that puts
-// the row's largest value in [1, 2) (phi is increasing, so that is phi of the row's largest q). Both common
-// factors cancel in U / den. Buffer loads bring the plane into the ring's V slots (rows 0-63 in v0, 64-127 in v1)
-// and the row factors into k2 + 1024, while Z arrives in k2 by ordinary loads and phi' is formed; then W_p^T takes
-// the V slots the same way. Wave w handles its own 32 rows. acc2 returns O^T unnormalized in the attention
+// and den[i] = phi'(q_i) . Z_m. The remaining state is H_m^T as an fp16 plane P (rows e, each row 256 B at its own
+// place in the head's row-major planes) with one factor f_e per row, and Z_m in fp32 (the aux record), H_m and Z_m
+// sharing one power-of-two scale; phi' = phi scaled per row by the power of two that puts the row's largest value
+// in [1, 2) (phi is increasing, so that is phi of the row's largest q). Both common factors cancel in U / den.
+// Buffer loads gather the plane rows into the ring's V slots (rows 0-63 in v0, 64-127 in v1) and the row factors
+// into k2 + 1024, while Z arrives in k2 by ordinary loads and phi' is formed; then W_p^T takes the V slots the same
+// way. Wave w handles its own 32 rows. acc2 returns O^T unnormalized in the attention
 // accumulators' layout (row lr, channel 32 ft + 8 (r / 4) + 4 g + r % 4) and inv_l = 1 / den.
 template <int NW>
-__device__ __forceinline__ void lin_epilogue(const uint16_t* __restrict__ q, const unsigned char* __restrict__ rec16,
+__device__ __forceinline__ void lin_epilogue(const uint16_t* __restrict__ q, const unsigned char* __restrict__ plane16,
+                                             const unsigned char* __restrict__ aux16,
                                              const uint16_t* __restrict__ wpt, int bh, int I, int N, int n_qb,
                                              unsigned char* __restrict__ k2, unsigned char* __restrict__ v0,
                                              unsigned char* __restrict__ v1, v16f (&acc2)[4], float& inv_l) {
   const int t = threadIdx.x, w = __builtin_amdgcn_readfirstlane(t >> 6), l = t & 63, g = l >> 5, lr = l & 31;
   constexpr int BLKQ = 32 * NW;
-  const unsigned char* srec = rec16 + ((size_t)bh * n_qb + I) * (size_t)kRec16Bytes;
+  const unsigned char* sax = aux16 + ((size_t)bh * n_qb + I) * (size_t)kAuxBytes;
   float* s_z = (float*)k2;
   const float* s_f = (const float*)(k2 + 1024);
   __syncthreads();  // every wave is done with the ring slots
   float4 zv = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (t < kD / 4) zv = *(const float4*)(srec + kRec16Z + 16 * t);  // issued before the plane loads: waited alone
-  {  // the plane: 32 loads of 1 KB; the row factors: one load of 1 KB (its second half past the record reads 0)
-    const __amdgpu_buffer_rsrc_t rb =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(srec), (short)0, kRec16Bytes, 0x00020000);
-    for (int k = w; k < 33; k += NW) {  // (offsets per lane, so the range check sees all of them)
+  if (t < kD / 4) zv = *(const float4*)(sax + kAuxZ + 16 * t);  // issued before the plane loads: waited alone
+  {  // the plane: 32 loads of 1 KB, each four rows of 256 B (lane l: row 4k + l / 16, chunk l % 16); the row
+     // factors: one load of 1 KB (its second half past the aux record reads 0). Offsets are per lane, so the
+     // range check sees all of them.
+    const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<unsigned char*>(plane16 + (size_t)bh * kD * n_qb * 256), (short)0, kD * n_qb * 256, 0x00020000);
+    const __amdgpu_buffer_rsrc_t ra =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(sax), (short)0, kAuxBytes, 0x00020000);
+    const uint32_t lrow = (uint32_t)(((l >> 4) * n_qb + I) * 256 + (l & 15) * 16);
+    for (int k = w; k < 33; k += NW) {
       unsigned char* dst = k < 16 ? v0 + k * 1024 : k < 32 ? v1 + (k - 16) * 1024 : k2 + 1024;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (__attribute__((address_space(3))) void*)dst, 16,
-                                               l * 16 + (k < 32 ? k * 1024 : kRec16F), 0, 0, 0);
+      if (k < 32)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rp, (__attribute__((address_space(3))) void*)dst, 16,
+                                                 lrow + (uint32_t)(4 * k * n_qb * 256), 0, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (__attribute__((address_space(3))) void*)dst, 16,
+                                                 l * 16 + kAuxF, 0, 0, 0);
     }
   }
   if (t < kD / 4) *(float4*)(s_z + 4 * t) = zv;
@@ -434,7 +445,8 @@ template <int NW, bool G>
 __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k3_attn(
     const int8_t* __restrict__ q8, const int8_t* __restrict__ k8, const unsigned char* __restrict__ vt,
     const float* __restrict__ qs, const float* __restrict__ ks, const int32_t* __restrict__ idx,
-    const uint16_t* __restrict__ qraw, const unsigned char* __restrict__ rec16, const uint16_t* __restrict__ wpt,
+    const uint16_t* __restrict__ qraw, const unsigned char* __restrict__ plane16,
+    const unsigned char* __restrict__ aux16, const uint16_t* __restrict__ wpt,
     float* __restrict__ o_lin, uint16_t* __restrict__ out, int N, int n_qb, int n_kb, int topk, float c0,
     int total) {
   constexpr int BLKQ = 32 * NW;
@@ -705,7 +717,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k3_attn(
   // the linear branch (rec16 given): O_l in the same register layout as O
   v16f ol[4];
   float inv_l = 0.f;
-  if (rec16) lin_epilogue<NW>(qraw, rec16, wpt, bh, I, N, n_qb, s_k2, s_v0, s_v1, ol, inv_l);
+  if (plane16) lin_epilogue<NW>(qraw, plane16, aux16, wpt, bh, I, N, n_qb, s_k2, s_v0, s_v1, ol, inv_l);
   if (rok) {
     const size_t ro = ((size_t)bh * N + row) * kD;
 #pragma unroll
@@ -715,7 +727,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k3_attn(
         const int e0 = 32 * ct + 8 * r4 + 4 * g;
         float x0 = o[ct][4 * r4] * inv, x1 = o[ct][4 * r4 + 1] * inv;
         float x2 = o[ct][4 * r4 + 2] * inv, x3 = o[ct][4 * r4 + 3] * inv;
-        if (rec16) {
+        if (plane16) {
           const float4 a = make_float4(ol[ct][4 * r4] * inv_l, ol[ct][4 * r4 + 1] * inv_l, ol[ct][4 * r4 + 2] * inv_l,
                                        ol[ct][4 * r4 + 3] * inv_l);
           if (o_lin) *(float4*)(o_lin + ro + e0) = a;
@@ -730,11 +742,12 @@ hipError_t launch_attn(const Plan& p, const uint16_t* q, uint16_t* out, hipStrea
   const int total = p.BH * p.n_qb;
   const float c0 = p.sm_scale * 1.4426950408889634f;  // log2(e): scores enter exp2
   const bool lin = p.linear && p.topk < p.n_kb;
-  const unsigned char* sm = lin ? p.rec16 : nullptr;
+  const unsigned char* pl16 = lin ? p.plane16 : nullptr;
   float* olin = lin ? p.o_lin : nullptr;  // optional export of the linear branch's output
 #define SAGESLA_ATTN(NWV, G)                                                                                     \
   hipLaunchKernelGGL((k3_attn<NWV, G>), dim3(total), dim3(64 * NWV), 0, s, p.q_i8, p.k_i8, p.v_img, p.q_scale,     \
-                     p.k_scale, p.block_idx, q, sm, p.wpt, olin, out, p.N, p.n_qb, p.n_kb, p.topk, c0, total)
+                     p.k_scale, p.block_idx, q, pl16, p.aux16, p.wpt, olin, out, p.N, p.n_qb, p.n_kb, p.topk, c0,   \
+                     total)
   if (p.blk_q == 128) {
     if (p.group32) SAGESLA_ATTN(4, true); else SAGESLA_ATTN(4, false);
   } else {

@@ -521,30 +521,37 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k4_gemm(const float* __restri
 
 // ---------------------------------------------------------------------------------------------------------
 // k4_gemm16 (the forward): the same keep-mask x table product over the fp16 table of k4_states16. Each block J
-// carries its own power of two 2^e_J, so the A operand is keep[I][J] * 2^(e_J - E), E = max_J e_J over the head
+// carries its own power of two 2^e_J, so the mask operand is keep[I][J] * 2^(e_J - E), E = max_J e_J over the head
 // (exact in fp16 down to 2^-24; a block more than 24 binades below the head's largest is dropped), and the sums are
 // the remaining state times 2^-E, H_m and Z_m alike (the linear branch's quotient does not see the common factor).
 // grid (kStateX / 128 column groups, ceil(n_qb / 640) query-block chunks, BH), 512 threads (8 waves).
 // Step = 32 key blocks (two k-steps of 16) = one mask word per query block. Table slices (32 rows of 256 B)
 // arrive by buffer loads to LDS with their 16-byte chunks swizzled (tswz), three steps ahead, with the chunk's
-// mask words; four-slot rings, one wait and one barrier per step. B operands come straight from the slice
-// by transposing reads; A operands are the byte table's 0 / 1.0 pattern ANDed with the step's eight scales.
-// Wave w owns query tiles 5 (w / 2) .. +4 and column tiles 2 (w % 2), +1.
+// mask words; four-slot rings, one wait and one barrier per step. The table operand comes straight from the slice
+// by transposing reads; the mask operand is the nibble table's 0 / 1.0 patterns ANDed with the step's eight scales.
+// The table is the first operand, so the accumulators hold C^T: every lane holds runs of four consecutive columns
+// of one query block. Wave w owns query tiles 5 (w / 2) .. +4 and column tiles 2 (w % 2), +1.
 // The store writes each query block's row e = x of H_m^T as an fp16 plane row with its own factor (the row's
-// largest magnitude set below 2^15), and the Z group as fp32.
+// largest magnitude set below 2^15; the two waves of a row trade their halves' maxima through LDS) straight from
+// the registers, and the Z group as fp32. Plane rows are stored row-major over the query blocks (one workgroup's
+// rows are contiguous); the factors and Z go to each query block's aux record.
 // ---------------------------------------------------------------------------------------------------------
 constexpr int kAExpMin = -24;  // the smallest A scale 2^d, an fp16 subnormal
 
 __global__ __launch_bounds__(kGemmThreads, 1) void k4_gemm16(const uint16_t* __restrict__ table,
                                                             const int32_t* __restrict__ bexp,
                                                             const uint32_t* __restrict__ mask,
-                                                            unsigned char* __restrict__ rec, int n_qb, int n_kb,
+                                                            unsigned char* __restrict__ plane,
+                                                            unsigned char* __restrict__ aux, int n_qb, int n_kb,
                                                             int n_kbw, int qpad) {
-  // four-slot rings: table slices (8 KB used; slots 0 and 1 are also the store's fp32 staging) and mask words
-  __shared__ __attribute__((aligned(1024))) unsigned char s_st0[16384], s_st1[16384], s_st2[8192], s_st3[8192];
-  __shared__ __attribute__((aligned(1024))) uint32_t s_w0[kGemmRows + 128], s_w1[kGemmRows + 128],
-      s_w2[kGemmRows + 128], s_w3[kGemmRows + 128];
-  __shared__ __attribute__((aligned(1024))) uint4 s_lut[256];            // byte -> 8 fp16 of 0 / 1.0
+  // three-slot LDS rings (table slices of 32 rows of 256 B, mask words of the chunk's rows); slot 0 of the slices
+  // is also the store's exchange buffer
+  __shared__ __attribute__((aligned(1024))) unsigned char s_st0[8192], s_st1[8192], s_st2[8192];
+  __shared__ __attribute__((aligned(1024))) uint32_t s_w0[2 * kGemmThreads], s_w1[2 * kGemmThreads],
+      s_w2[2 * kGemmThreads];
+  // nibble -> 4 fp16 of 0 / 1.0 (element i = bit i): 128 B, so every entry sits on banks of its own and the lanes'
+  // reads of different entries never conflict
+  __shared__ __attribute__((aligned(128))) uint2 s_lut4[16];
   __shared__ __attribute__((aligned(16))) uint16_t s_asc[kMaxKeyBlocks + 64];  // fp16 2^(e_J - E)
   __shared__ int s_red[kGemmThreads / 64];
   constexpr int n_xt = kStateX / 128;
@@ -552,17 +559,14 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k4_gemm16(const uint16_t* __r
   const int t = threadIdx.x, w = __builtin_amdgcn_readfirstlane(t >> 6), l = t & 63, g = l >> 5, lr = l & 31;
   const int I0 = ic * kGemmRows;
   const int n_it = min(kGemmIT, (n_qb - I0 + 31) >> 5);
-  const int nss = n_kbw;
+  const int nss = n_kbw;  // steps of 32 key blocks
   const __amdgpu_buffer_rsrc_t rt = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(table + (size_t)bh * n_xt * n_kb * 128), (short)0, n_xt * n_kb * 256, 0x00020000);
   const __amdgpu_buffer_rsrc_t rm = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint32_t*>(mask + (size_t)bh * n_kbw * qpad), (short)0, n_kbw * qpad * 4, 0x00020000);
-  if (t < 256) {
-    uint32_t d[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) d[k] = ((t >> (2 * k)) & 1 ? 0x3C00u : 0u) | ((t >> (2 * k + 1)) & 1 ? 0x3C000000u : 0u);
-    s_lut[t] = make_uint4(d[0], d[1], d[2], d[3]);
-  }
+  if (t < 16)
+    s_lut4[t] = make_uint2(((t & 1) ? 0x3C00u : 0u) | ((t & 2) ? 0x3C000000u : 0u),
+                           ((t & 4) ? 0x3C00u : 0u) | ((t & 8) ? 0x3C000000u : 0u));
   // the head's largest block exponent, then the A scales of every key block (0 past n_kb)
   const int32_t* be = bexp + (size_t)bh * n_kb;
   int emax = INT_MIN;
@@ -574,7 +578,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k4_gemm16(const uint16_t* __r
   int E = s_red[0];
 #pragma unroll
   for (int k = 1; k < kGemmThreads / 64; ++k) E = max(E, s_red[k]);
-  for (int J = t; J < 32 * n_kbw; J += kGemmThreads) {
+  for (int J = t; J < 32 * nss; J += kGemmThreads) {
     uint32_t h = 0;
     if (J < n_kb) {
       const int d = be[J] - E;  // <= 0
@@ -583,21 +587,28 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k4_gemm16(const uint16_t* __r
     s_asc[J] = (uint16_t)h;
   }
 
-  // (every load offset is a per-lane offset, checked against the descriptor's range: past it a load reads zeros)
-  const uint32_t wlane = (uint32_t)(l * 16 + (I0 + 256 * w) * 4);
-  auto dma_w = [&](int ss, uint32_t* dst) {
-    if (w < 3)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rm, (__attribute__((address_space(3))) void*)(dst + 256 * w), 16,
-                                               wlane + (uint32_t)(ss * qpad * 4), 0, 0, 0);
-  };
-  // slice of step ss: rows 32 ss .. +31 of column group xg; wave w loads rows 4w .. 4w + 3, lane l row 4w + l / 16 at
-  // chunk position l % 16 with the chunk (l % 16) ^ tswz(row). Rows past n_kb (their A is 0) read the next column
+  // Staging through registers: the data of step s is loaded at step s - 4 (ordinary buffer loads, checked against
+  // the descriptors' ranges: past them a load reads zeros) and written to its LDS slot at step s - 1, so every wait
+  // is on a register and covers exactly the load it needs, with the loads of two later steps still in flight.
+  // Thread t loads the slice's 16-byte chunk t (row t / 16, chunk t % 16) and stores it at chunk position
+  // (t % 16) ^ tswz(row), and two mask words (rows 2t, 2t + 1 of the chunk; the 640 rows of the chunk and 384 that
+  // are not used, so that every thread issues the same loads). Rows past n_kb (their A is 0) read the next column
   // group's rows (finite) or, past the head's table, zeros.
-  const int srow = 4 * w + (l >> 4);
-  const uint32_t slane = (uint32_t)(srow * 256 + 16 * ((l & 15) ^ tswz(srow)) + xg * n_kb * 256);
-  auto dma_st = [&](int ss, unsigned char* dst) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rt, (__attribute__((address_space(3))) void*)(dst + w * 1024), 16,
-                                             slane + (uint32_t)(ss * 32 * 256), 0, 0, 0);
+  const int srow = t >> 4;
+  const uint32_t sgoff = (uint32_t)(xg * n_kb * 256 + srow * 256 + (t & 15) * 16);
+  const uint32_t slds = (uint32_t)(srow * 256 + (((t & 15) ^ tswz(srow)) << 4));
+  const uint32_t wgoff = (uint32_t)((I0 + 2 * t) * 4);
+  struct Stage {
+    v4i st;
+    uint2 wd;
+  };
+  auto load = [&](int ss, Stage& r) {
+    r.st = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rt, sgoff + (uint32_t)(ss * 32 * 256), 0, 0));
+    r.wd = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rm, wgoff + (uint32_t)(ss * qpad * 4), 0, 0));
+  };
+  auto put = [&](const Stage& r, unsigned char* __restrict__ st, uint32_t* __restrict__ wd) {
+    *(v4i*)(st + slds) = r.st;
+    *(uint2*)(wd + 2 * t) = r.wd;
   };
 
   const int wit = 5 * (w >> 1), wxt = 2 * (w & 1);
@@ -605,15 +616,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k4_gemm16(const uint16_t* __r
 #pragma unroll
   for (int k = 0; k < 10; ++k) acc[k] = (v16f){};
 
-  auto step = [&](int ss, const uint32_t* __restrict__ W, const unsigned char* __restrict__ st,
-                  uint32_t* __restrict__ w_fill, unsigned char* __restrict__ st_fill) {
-    // slice ss and words ss (issued three steps back) have landed; the two later steps' loads may stay in flight
-    if (w < 3)
-      gemm_sync<4>();
-    else
-      gemm_sync<2>();
-    dma_st(ss + 3, st_fill);
-    dma_w(ss + 3, w_fill);
+  auto mma = [&](int ss, const uint32_t* __restrict__ W, const unsigned char* __restrict__ st) {
     uint32_t wq[5];
 #pragma unroll
     for (int q = 0; q < 5; ++q) wq[q] = W[32 * (wit + q) + lr];
@@ -626,90 +629,104 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k4_gemm16(const uint16_t* __r
 #pragma unroll
       for (int c = 0; c < 2; ++c) bop[sub][c] = __builtin_bit_cast(v8h, tr_col_op(st, 16 * sub, 32 * (wxt + c), l));
 #pragma unroll
-    for (int i = 0; i < 10; ++i) {  // tiles past n_it have zero words, never stored
+    for (int i = 0; i < 10; ++i) {  // tiles past n_it have garbage words, never stored
       const int sub = i / 5, q = i % 5;
-      const uint4 m8 = s_lut[(wq[q] >> (16 * sub + 8 * g)) & 0xFFu];
+      const uint32_t b8 = wq[q] >> (16 * sub + 8 * g);
+      const uint2 m0 = s_lut4[b8 & 15u], m1 = s_lut4[(b8 >> 4) & 15u];
+      const uint4 m8 = make_uint4(m0.x, m0.y, m1.x, m1.y);
       const v8h a = __builtin_bit_cast(
           v8h, make_uint4(m8.x & sv[sub].x, m8.y & sv[sub].y, m8.z & sv[sub].z, m8.w & sv[sub].w));
 #pragma unroll
       for (int c = 0; c < 2; ++c)
-        acc[2 * q + c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, bop[sub][c], acc[2 * q + c], 0, 0, 0);
+        acc[2 * q + c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bop[sub][c], a, acc[2 * q + c], 0, 0, 0);
     }
   };
 
-  // prologue: slices and words of steps 0-2, interleaved so that every wave's count per step is fixed
-  dma_st(0, s_st0);
-  dma_w(0, s_w0);
-  dma_st(1, s_st1);
-  dma_w(1, s_w1);
-  dma_st(2, s_st2);
-  dma_w(2, s_w2);
-  for (int ss = 0; ss < nss; ss += 4) {
-    step(ss, s_w0, s_st0, s_w3, s_st3);
-    if (ss + 1 < nss) step(ss + 1, s_w1, s_st1, s_w0, s_st0);
-    if (ss + 2 < nss) step(ss + 2, s_w2, s_st2, s_w1, s_st1);
-    if (ss + 3 < nss) step(ss + 3, s_w3, s_st3, s_w2, s_st2);
+  // Step ss: barrier; stage step ss + 1 from its registers into slot (ss + 1) % 3; refill those registers with step
+  // ss + 4; products of step ss from slot ss % 3. Register sets and slots both rotate over three steps, so the main
+  // loop runs whole groups of three with no conditions (loads past the last step read zeros or finite rows that no
+  // mask bit selects) and the last one or two steps follow.
+  Stage r0, r1, r2;
+  load(0, r0);
+  load(1, r1);
+  load(2, r2);
+  put(r0, s_st0, s_w0);
+  load(3, r0);
+  auto step = [&](int ss, Stage& nx, const uint32_t* __restrict__ W, const unsigned char* __restrict__ st,
+                  unsigned char* __restrict__ st_next, uint32_t* __restrict__ w_next) {
+    __syncthreads();
+    put(nx, st_next, w_next);
+    load(ss + 4, nx);
+    mma(ss, W, st);
+  };
+  int ss = 0;
+  for (; ss + 3 <= nss; ss += 3) {
+    step(ss, r1, s_w0, s_st0, s_st1, s_w1);
+    step(ss + 1, r2, s_w1, s_st1, s_st2, s_w2);
+    step(ss + 2, r0, s_w2, s_st2, s_st0, s_w0);
   }
-  wait_vmem_all_lin();  // no load may land in the staging below
+  if (ss < nss) step(ss, r1, s_w0, s_st0, s_st1, s_w1);
+  if (ss + 1 < nss) step(ss + 1, r2, s_w1, s_st1, s_st2, s_w2);
+  wait_vmem_all_lin();  // the loads past the last step have landed in their registers: nothing is in flight
+  __syncthreads();  // every wave is done reading the slots reused below
 
-  // Store. acc[2q + c][r] is C[I][x] with I = I0 + 32 (wit + q) + 8(r/4) + 4g + r%4, x = 128 xg + 32 (wxt + c) + lr.
-  if (xg == kD) {  // Z_m, fp32
+  // Store. The products ran with the table as the first operand, so acc[2q + c][r] is C[I][x] for query block
+  // I = I0 + 32 (wit + q) + lr and column x = 128 xg + 32 (wxt + c) + 8 (r / 4) + 4 g + r % 4: every lane holds runs
+  // of four consecutive columns of one query block, which it stores as they stand.
+  if (xg == kD) {  // Z_m, fp32: 16 B per run
 #pragma unroll
-    for (int q = 0; q < 5; ++q)
+    for (int q = 0; q < 5; ++q) {
+      const int I = I0 + 32 * (wit + q) + lr;
+      if (wit + q >= n_it || I >= n_qb) continue;
+      unsigned char* r0 = aux + ((size_t)bh * n_qb + I) * kAuxBytes + kAuxZ;
 #pragma unroll
       for (int c = 0; c < 2; ++c)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int I = I0 + 32 * (wit + q) + 8 * (r >> 2) + 4 * g + (r & 3);
-          if (wit + q < n_it && I < n_qb)
-            *(float*)(rec + ((size_t)bh * n_qb + I) * kRec16Bytes + kRec16Z + 4 * (32 * (wxt + c) + lr)) =
-                acc[2 * q + c][r];
-        }
+        for (int r4 = 0; r4 < 4; ++r4)
+          *(float4*)(r0 + 4 * (32 * (wxt + c) + 8 * r4 + 4 * g)) =
+              make_float4(acc[2 * q + c][4 * r4], acc[2 * q + c][4 * r4 + 1], acc[2 * q + c][4 * r4 + 2],
+                          acc[2 * q + c][4 * r4 + 3]);
+    }
     return;
   }
-  // row e = xg of H_m^T: half-rounds of 64 query blocks staged in LDS as fp32 (columns 0-63 in s_st0, 64-127 in
-  // s_st1); then 16 threads per query block take 8 columns each, agree on the row's largest magnitude and write
-  // the fp16 plane row (16 B each) and the row's factor.
-  float* const sg0 = (float*)s_st0;
-  float* const sg1 = (float*)s_st1;
+  // row e = xg of H_m^T of each query block: its largest magnitude over the 128 columns (64 in this wave: two
+  // column tiles, the lane pair g = 0, 1; the other 64 in wave w ^ 1, traded through LDS), then the fp16 plane row
+  // in 8-byte runs and the row's factor
+  float* const s_mx = (float*)s_st0;  // [8 waves][5 q][32 lanes]
+  float mx[5];
 #pragma unroll
-  for (int q = 0; q < 5; ++q)
+  for (int q = 0; q < 5; ++q) {
+    float m = 0.f;
 #pragma unroll
-    for (int hr = 0; hr < 2; ++hr) {
-      __syncthreads();
-      if ((w >> 2) == hr) {
-        float* hw_ = (w & 1) ? sg1 : sg0;
+    for (int c = 0; c < 2; ++c)
 #pragma unroll
-        for (int c = 0; c < 2; ++c)
+      for (int r = 0; r < 16; ++r) m = fmaxf(m, fabsf(acc[2 * q + c][r]));
+    mx[q] = fmaxf(m, swap_halves_f32(m));
+    if (g == 0) s_mx[(w * 5 + q) * 32 + lr] = mx[q];
+  }
+  __syncthreads();
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            hw_[(32 * ((w >> 1) & 1) + 8 * (r >> 2) + 4 * g + (r & 3)) * 64 + 32 * c + lr] = acc[2 * q + c][r];
+  for (int q = 0; q < 5; ++q) {
+    const float m = fmaxf(mx[q], s_mx[((w ^ 1) * 5 + q) * 32 + lr]);
+    const int I = I0 + 32 * (wit + q) + lr;
+    if (wit + q >= n_it || I >= n_qb) continue;
+    int kx = 0;
+    (void)frexpf(m, &kx);  // m < 2^kx
+    const int sh = 15 - kx;
+    // the row's 256 B as the epilogue's LDS holds row xg of the plane (out_off with the row offset taken out)
+    unsigned char* r0 = plane + (((size_t)bh * kD + xg) * n_qb + I) * 256 - (size_t)xg * 256;
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const v4f x = {acc[2 * q + c][4 * r4], acc[2 * q + c][4 * r4 + 1], acc[2 * q + c][4 * r4 + 2],
+                       acc[2 * q + c][4 * r4 + 3]};
+        *(uint2*)(r0 + out_off(xg, 32 * (wxt + c) + 8 * r4 + 4 * g)) =
+            make_uint2(pack_f16x2(ldexpf(x[0], sh), ldexpf(x[1], sh)), pack_f16x2(ldexpf(x[2], sh), ldexpf(x[3], sh)));
       }
-      __syncthreads();
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {  // 64 rows x 16 chunks of 8 columns
-        const int u = t + kGemmThreads * j, row = u >> 4, k8 = u & 15;
-        const int it = 5 * (2 * hr + (row >> 5)) + q, I = I0 + 32 * it + (row & 31);
-        const float* src = (k8 < 8 ? sg0 : sg1) + row * 64 + 8 * (k8 & 7);
-        const float4 x0 = *(const float4*)src, x1 = *(const float4*)(src + 4);
-        float mx = fmaxf(fmaxf(fmaxf(fabsf(x0.x), fabsf(x0.y)), fmaxf(fabsf(x0.z), fabsf(x0.w))),
-                         fmaxf(fmaxf(fabsf(x1.x), fabsf(x1.y)), fmaxf(fabsf(x1.z), fabsf(x1.w))));
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-        int kx = 0;
-        (void)frexpf(mx, &kx);  // mx < 2^kx
-        const int sh = 15 - kx;
-        const uint4 hv = make_uint4(pack_f16x2(ldexpf(x0.x, sh), ldexpf(x0.y, sh)),
-                                    pack_f16x2(ldexpf(x0.z, sh), ldexpf(x0.w, sh)),
-                                    pack_f16x2(ldexpf(x1.x, sh), ldexpf(x1.y, sh)),
-                                    pack_f16x2(ldexpf(x1.z, sh), ldexpf(x1.w, sh)));
-        if (it < n_it && I < n_qb) {
-          unsigned char* r0 = rec + ((size_t)bh * n_qb + I) * kRec16Bytes;
-          *(uint4*)(r0 + out_off(xg, 8 * k8)) = hv;
-          if (k8 == 0) *(float*)(r0 + kRec16F + 4 * xg) = mx > 0.f ? ldexpf(1.f, kx - 15) : 0.f;
-        }
-      }
-    }
+    if (g == 0 && (w & 1) == 0)
+      *(float*)(aux + ((size_t)bh * n_qb + I) * kAuxBytes + kAuxF + 4 * xg) = m > 0.f ? ldexpf(1.f, kx - 15) : 0.f;
+  }
 }
 
 int mask_row_pad(int n_qb) { return (n_qb + kGemmRows - 1) / kGemmRows * kGemmRows; }
@@ -729,7 +746,7 @@ hipError_t launch_linear(const Plan& p, const uint16_t* k, const uint16_t* v, hi
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (p.lin_precise) return launch_state_sum(p.state, p.keep_mask, p.state_m, p.n_qb, p.n_kb, qpad, p.BH, s);
   hipLaunchKernelGGL(k4_gemm16, dim3(kStateX / 128, qpad / kGemmRows, p.BH), dim3(kGemmThreads), 0, s, p.state16,
-                     p.state_exp, p.keep_mask, p.rec16, p.n_qb, p.n_kb, n_kbw, qpad);
+                     p.state_exp, p.keep_mask, p.plane16, p.aux16, p.n_qb, p.n_kb, n_kbw, qpad);
   return hipGetLastError();
 }
 

@@ -180,7 +180,13 @@ sagesla_status sagesla_forward_noalloc(const void* q, const void* k, const void*
 /* Text of a status code (static storage). */
 const char* sagesla_status_str(sagesla_status s);
 
-/* hipError_t of the most recent SAGESLA_E_HIP in the calling thread (0 if none). */
+/* hipError_t of the most recent SAGESLA_E_HIP in the calling thread (0 if none; a later success does not clear it).
+ *
+ * Launches are asynchronous: SAGESLA_E_HIP from an entry point reports a failed launch, and a fault while a kernel
+ * runs surfaces at a later synchronizing HIP call. With the environment variable SAGESLA_DEBUG set to a value other
+ * than "" or "0" (read once, at the first launch of the process), every entry point synchronizes its stream after
+ * each stage's launches and returns SAGESLA_E_HIP for a fault of that stage, naming the stage's launcher on
+ * stderr. Debug mode blocks the host after every stage and must not be used while the stream is being captured. */
 int sagesla_last_hip_error(void);
 
 #ifdef __cplusplus

@@ -1,6 +1,8 @@
 // C ABI of the SageSLA forward: host-side validation, workspace plan and launch order.
 // The entry points and their contracts are declared in include/sagesla.h.
 #include <math.h>
+#include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <mutex>
@@ -149,10 +151,33 @@ sagesla_status hip_status(hipError_t e) {
   return SAGESLA_E_HIP;
 }
 
-#define SAGESLA_TRY(expr)                         \
-  do {                                            \
-    sagesla_status st_ = hip_status(expr);        \
-    if (st_ != SAGESLA_OK) return st_;            \
+// SAGESLA_DEBUG set to anything but "" or "0" (read at the first launch): every kernel launch is followed by a
+// synchronization of its stream, so that a fault while the kernel runs is reported as SAGESLA_E_HIP by the entry
+// point that launched it, with the launch named on stderr, instead of surfacing at a later call. It blocks the
+// host after every launch and cannot be used while the stream is being captured into a graph.
+bool debug_sync() {
+  static const bool on = [] {
+    const char* e = getenv("SAGESLA_DEBUG");
+    return e && e[0] && strcmp(e, "0") != 0;
+  }();
+  return on;
+}
+
+// status of a launch (its hipError_t) and, in debug mode, of the kernel's run
+sagesla_status launched(hipError_t e, const char* what, hipStream_t s) {
+  if (debug_sync()) {
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e == hipSuccess) e = hipGetLastError();
+    if (e != hipSuccess) fprintf(stderr, "sagesla: %s: %s\n", what, hipGetErrorString(e));
+  }
+  return hip_status(e);
+}
+
+// a kernel launch on stream s (the name of the launcher goes to the debug message)
+#define SAGESLA_LAUNCH(s, launcher, ...)                                           \
+  do {                                                                             \
+    sagesla_status st_ = launched(launcher(__VA_ARGS__), #launcher, (s));          \
+    if (st_ != SAGESLA_OK) return st_;                                             \
   } while (0)
 
 // records the caller's timing event of stage `stage` (begin: 0, end: 1) if events were given
@@ -168,17 +193,17 @@ const void* eff_q(const Plan& pl, const void* q) { return pl.qk_norm ? (const vo
 const void* eff_k(const Plan& pl, const void* k) { return pl.qk_norm ? (const void*)pl.k_hat : k; }
 
 sagesla_status run_quantize(const Plan& pl, const void* q_in, const void* k_in, const void* v, hipStream_t s) {
-  if (pl.qk_norm) SAGESLA_TRY(launch_qk_norm(pl, (const uint16_t*)q_in, (const uint16_t*)k_in, s));
+  if (pl.qk_norm) SAGESLA_LAUNCH(s, launch_qk_norm, pl, (const uint16_t*)q_in, (const uint16_t*)k_in, s);
   const void* q = eff_q(pl, q_in);
   const void* k = eff_k(pl, k_in);
-  SAGESLA_TRY(launch_kmean(pl, (const uint16_t*)k, s));
-  SAGESLA_TRY(launch_quant(pl, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, s));
+  SAGESLA_LAUNCH(s, launch_kmean, pl, (const uint16_t*)k, s);
+  SAGESLA_LAUNCH(s, launch_quant, pl, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, s);
   return SAGESLA_OK;
 }
 
 sagesla_status run_select(const Plan& pl, hipStream_t s) {
-  if (pl.topk > 0 && pl.topk < pl.n_kb) SAGESLA_TRY(launch_scores(pl, s));
-  if (pl.topk > 0) SAGESLA_TRY(launch_topk(pl, s));
+  if (pl.topk > 0 && pl.topk < pl.n_kb) SAGESLA_LAUNCH(s, launch_scores, pl, s);
+  if (pl.topk > 0) SAGESLA_LAUNCH(s, launch_topk, pl, s);
   return SAGESLA_OK;
 }
 
@@ -242,13 +267,13 @@ sagesla_status sagesla_forward(const void* q, const void* k, const void* v, void
   SAGESLA_STEP(mark(p, SAGESLA_STAGE_LINEAR, 0, s));
   const bool lin_active = pl.linear && pl.topk < pl.n_kb;
   if (lin_active) {
-    SAGESLA_TRY(launch_linear(pl, (const uint16_t*)eff_k(pl, k), (const uint16_t*)v, s));
+    SAGESLA_LAUNCH(s, launch_linear, pl, (const uint16_t*)eff_k(pl, k), (const uint16_t*)v, s);
   } else if (p->o_lin) {
-    SAGESLA_TRY(launch_fill_f32(p->o_lin, (size_t)pl.BH * pl.N * kD, 0.f, s));
+    SAGESLA_LAUNCH(s, launch_fill_f32, p->o_lin, (size_t)pl.BH * pl.N * kD, 0.f, s);
   }
   SAGESLA_STEP(mark(p, SAGESLA_STAGE_LINEAR, 1, s));
   SAGESLA_STEP(mark(p, SAGESLA_STAGE_ATTN, 0, s));
-  SAGESLA_TRY(launch_attn(pl, (const uint16_t*)eff_q(pl, q), (uint16_t*)out, s));
+  SAGESLA_LAUNCH(s, launch_attn, pl, (const uint16_t*)eff_q(pl, q), (uint16_t*)out, s);
   SAGESLA_STEP(mark(p, SAGESLA_STAGE_ATTN, 1, s));
 #undef SAGESLA_STEP
   return SAGESLA_OK;
@@ -293,7 +318,9 @@ sagesla_status w8a8_quantize(const void* x, int32_t rows, int32_t cols, float cl
   if (!(clip > 0.f && clip <= 1.f)) return SAGESLA_E_SHAPE;
   if (!x || !codes || !scales) return SAGESLA_E_NULL;
   if (misaligned(x, 16) || misaligned(codes, 16) || misaligned(scales, 16)) return SAGESLA_E_ALIGN;
-  return hip_status(launch_w8a8_quant((const uint16_t*)x, rows, cols, clip, codes, scales, (hipStream_t)stream));
+  const hipStream_t s = (hipStream_t)stream;
+  SAGESLA_LAUNCH(s, launch_w8a8_quant, (const uint16_t*)x, rows, cols, clip, codes, scales, s);
+  return SAGESLA_OK;
 }
 
 sagesla_status w8a8_gemm(const int8_t* x_i8, const float* x_scale, const int8_t* w_i8, const float* w_scale,
@@ -304,8 +331,9 @@ sagesla_status w8a8_gemm(const int8_t* x_i8, const float* x_scale, const int8_t*
   if (misaligned(x_i8, 16) || misaligned(x_scale, 16) || misaligned(w_i8, 16) || misaligned(w_scale, 16) ||
       misaligned(bias, 16) || misaligned(y, 16))
     return SAGESLA_E_ALIGN;
-  return hip_status(launch_w8a8_gemm(x_i8, x_scale, w_i8, w_scale, (const uint16_t*)bias, (uint16_t*)y, M, N, K,
-                                     (hipStream_t)stream));
+  const hipStream_t s = (hipStream_t)stream;
+  SAGESLA_LAUNCH(s, launch_w8a8_gemm, x_i8, x_scale, w_i8, w_scale, (const uint16_t*)bias, (uint16_t*)y, M, N, K, s);
+  return SAGESLA_OK;
 }
 
 size_t w8a8_workspace_bytes(int32_t M, int32_t K) {
@@ -328,8 +356,8 @@ sagesla_status w8a8_linear(const void* x, const int8_t* w_i8, const float* w_sca
   int8_t* x8 = (int8_t*)workspace;
   float* xs = (float*)((unsigned char*)workspace + align_up((size_t)M * K));
   const hipStream_t s = (hipStream_t)stream;
-  SAGESLA_TRY(launch_w8a8_quant((const uint16_t*)x, M, K, clip, x8, xs, s));
-  SAGESLA_TRY(launch_w8a8_gemm(x8, xs, w_i8, w_scale, (const uint16_t*)bias, (uint16_t*)y, M, N, K, s));
+  SAGESLA_LAUNCH(s, launch_w8a8_quant, (const uint16_t*)x, M, K, clip, x8, xs, s);
+  SAGESLA_LAUNCH(s, launch_w8a8_gemm, x8, xs, w_i8, w_scale, (const uint16_t*)bias, (uint16_t*)y, M, N, K, s);
   return SAGESLA_OK;
 }
 
@@ -420,20 +448,20 @@ sagesla_status sagesla_backward(const void* q, const void* k, const void* v, con
   b.dw = dw_proj;
   const hipStream_t s = (hipStream_t)stream;
   if (pl.qk_norm) {  // the attention part runs at the normalized values the forward uses
-    SAGESLA_TRY(launch_qk_norm(pl, (const uint16_t*)q, (const uint16_t*)k, s));
+    SAGESLA_LAUNCH(s, launch_qk_norm, pl, (const uint16_t*)q, (const uint16_t*)k, s);
     b.q = (const uint16_t*)pl.q_hat;
     b.k = (const uint16_t*)pl.k_hat;
   }
   const bool lin_active = pl.linear && pl.topk < pl.n_kb;
-  if (lin_active) SAGESLA_TRY(launch_linear(pl, b.k, (const uint16_t*)v, s));
-  SAGESLA_TRY(launch_backward_sparse(b, s));
+  if (lin_active) SAGESLA_LAUNCH(s, launch_linear, pl, b.k, (const uint16_t*)v, s);
+  SAGESLA_LAUNCH(s, launch_backward_sparse, b, s);
   if (lin_active) {
-    SAGESLA_TRY(launch_backward_linear(b, s));
+    SAGESLA_LAUNCH(s, launch_backward_linear, b, s);
   } else if (dw_proj) {
-    SAGESLA_TRY(launch_fill_f32(dw_proj, (size_t)kD * kD, 0.f, s));
+    SAGESLA_LAUNCH(s, launch_fill_f32, dw_proj, (size_t)kD * kD, 0.f, s);
   }
   if (pl.qk_norm)  // dq, dk hold the gradients at the normalized values: carry them through the norm
-    SAGESLA_TRY(launch_norm_backward(b, (const uint16_t*)q, (const uint16_t*)k, p->dq_norm_w, p->dk_norm_w, s));
+    SAGESLA_LAUNCH(s, launch_norm_backward, b, (const uint16_t*)q, (const uint16_t*)k, p->dq_norm_w, p->dk_norm_w, s);
   return SAGESLA_OK;
 }
 

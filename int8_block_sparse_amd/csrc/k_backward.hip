@@ -6,7 +6,8 @@
 // elu+1 linear attention over the unselected blocks; INT8 quantization passes straight through and the K-mean
 // shift, which leaves every softmax row unchanged, drops out.
 //
-// Sparse branch (bf16 MFMA, fp32 accumulation; P and dS enter the products as bf16 hi + lo pairs):
+// Sparse branch (bf16 MFMA, fp32 accumulation; P and dS enter their products rounded to bf16 once, as the
+// forward's P does):
 //   kb_sel     bitmaps of the selection: [BH][n_kb][ceil(n_qb/32)] (bit I of key block J = I selected J) and
 //              [BH][n_qb][ceil(n_kb/32)] (bit J of query block I)
 //   kb_q       per query block: pass 1 the log-sum-exp of every row (base 2) and D_i = sum_j P_ij dP_ij, both
@@ -87,6 +88,14 @@ __device__ __forceinline__ v8bf ld_tr(const unsigned char* p0, const unsigned ch
   const v4s b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)p1);
   const v8s ab = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
   return __builtin_bit_cast(v8bf, ab);
+}
+
+// accumulator rows 8 s .. 8 s + 7 of a lane as one bf16 operand (round to nearest even)
+__device__ __forceinline__ v8bf cvt8(const v16f& x, int s) {
+  uint32_t h[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) h[e] = pack_bf16x2(x[8 * s + 2 * e], x[8 * s + 2 * e + 1]);
+  return __builtin_bit_cast(v8bf, make_uint4(h[0], h[1], h[2], h[3]));
 }
 
 // accumulator rows 8 s .. 8 s + 7 of a lane as bf16 hi and lo operands (hi = bf16(x), lo = bf16(x - hi))
@@ -314,15 +323,10 @@ __global__ __launch_bounds__(256, 2) void kb_q(const uint16_t* __restrict__ q, c
       }
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        v8bf hi, lo;
-        split8(st, s, hi, lo);
+        const v8bf ds = cvt8(st, s);
         const unsigned char* rb = tk + 8192 * tt + 4096 * s;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const v8bf a = ld_tr(rb + to[u][0], rb + to[u][1]);
-          acc[u] = mfma(a, hi, acc[u]);
-          acc[u] = mfma(a, lo, acc[u]);
-        }
+        for (int u = 0; u < 4; ++u) acc[u] = mfma(ld_tr(rb + to[u][0], rb + to[u][1]), ds, acc[u]);
       }
     }
   });
@@ -426,18 +430,12 @@ __global__ __launch_bounds__(256, 2) void kb_kv(const uint16_t* __restrict__ q, 
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
           __builtin_amdgcn_sched_barrier(0);
-          v8bf ph, pl, dh, dl;
-          split8(s, st, ph, pl);
-          split8(dp, st, dh, dl);
+          const v8bf pb = cvt8(s, st), db = cvt8(dp, st);
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
             const uint32_t t0 = tq[0] ^ (64u * u), t1 = tq[1] ^ (64u * u);
-            const v8bf ay = ld_tr(sdY + 4096 * st + t0, sdY + 4096 * st + t1);
-            accv[u] = mfma(ay, ph, accv[u]);
-            accv[u] = mfma(ay, pl, accv[u]);
-            const v8bf aq = ld_tr(sQ + 4096 * st + t0, sQ + 4096 * st + t1);
-            acck[u] = mfma(aq, dh, acck[u]);
-            acck[u] = mfma(aq, dl, acck[u]);
+            accv[u] = mfma(ld_tr(sdY + 4096 * st + t0, sdY + 4096 * st + t1), pb, accv[u]);
+            acck[u] = mfma(ld_tr(sQ + 4096 * st + t0, sQ + 4096 * st + t1), db, acck[u]);
           }
         }
       }

@@ -20,7 +20,7 @@ sys.path.insert(0, sys.argv[1])
 import int8_block_sparse_amd as sg, synth
 wl = synth.custom(1, 2, 1000, blk_q=128, topk_frac=0.25, name="debug-mode")
 q, k, v, w = synth.make(wl, 3, device="cuda")
-out, _ = sg.forward(q, k, v, w, topk=wl.topk, blk_q=wl.blk_q)
+out = sg.forward(q, k, v, w, topk=wl.topk, blk_q=wl.blk_q)
 dy = torch.randn(q.shape, generator=torch.Generator().manual_seed(4)).to(torch.bfloat16).cuda()
 _, ex = sg.forward(q, k, v, w, topk=wl.topk, blk_q=wl.blk_q, export=True)
 g = sg.backward(q, k, v, w, dy, ex["block_idx"][..., :wl.topk].contiguous(), topk=wl.topk)
@@ -44,7 +44,7 @@ def test_debug_mode_matches_async(tmp_path):
     sg.load()
     wl = synth.custom(1, 2, 1000, blk_q=128, topk_frac=0.25, name="debug-mode")
     q, k, v, w = synth.make(wl, 3, device="cuda")
-    out, _ = sg.forward(q, k, v, w, topk=wl.topk, blk_q=wl.blk_q)
+    out = sg.forward(q, k, v, w, topk=wl.topk, blk_q=wl.blk_q)
     dy = torch.randn(q.shape, generator=torch.Generator().manual_seed(4)).to(torch.bfloat16).cuda()
     _, ex = sg.forward(q, k, v, w, topk=wl.topk, blk_q=wl.blk_q, export=True)
     g = sg.backward(q, k, v, w, dy, ex["block_idx"][..., :wl.topk].contiguous(), topk=wl.topk)

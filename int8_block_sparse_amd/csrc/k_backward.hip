@@ -122,6 +122,15 @@ __device__ __forceinline__ void dma_sync() {
   asm volatile("" ::: "memory");
 }
 
+// Wait for this wave's LDS accesses only, then meet the other waves: every wave is done with the tiles it read
+// (vector-memory loads in flight are left running; a __syncthreads would wait for them too).
+__device__ __forceinline__ void lds_sync() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // vmcnt 63 (no wait), expcnt 7, lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Direct-to-LDS staging of one 64-row tile of a [rows][128] bf16 matrix: wave w issues four loads of 1 KB (tile
 // rows 16 e + 4 w .. + 3); lane l fills row 16 e + 4 w + l / 16 at chunk position l % 16 with the chunk
 // (l % 16) ^ tswz(row). Tile rows at or past nvalid re-read the last valid row (finite values that the kernels
@@ -233,9 +242,12 @@ __global__ __launch_bounds__(256, 2) void kb_q(const uint16_t* __restrict__ q, c
     load(rk, J * 64, nv, t);
     load(rv, J * 64, nv, t + kTileBytes);
   };
-  // Runs body(J, K tile, V tile) over the selected blocks through the two-slot ring; the loop is unrolled by
-  // two so that each slot's tile addresses are constants.
+  // Runs body(J, K tile, V tile) over the selected blocks through the two-slot ring; the loop is unrolled by two
+  // so that each slot's tile addresses are constants.
   auto ring = [&](auto&& body) {
+    auto run = [&](int J, const unsigned char* tk, const unsigned char* tv) {
+      if (wave_live) body(J, tk, tv);
+    };
     int wi = 0;
     uint32_t cw = sb[0];
     int cur = next_block(wi, cw);
@@ -244,15 +256,25 @@ __global__ __launch_bounds__(256, 2) void kb_q(const uint16_t* __restrict__ q, c
       int nxt = next_block(wi, cw);
       dma_sync();
       if (nxt >= 0) stage(nxt, 1);
-      if (wave_live) body(cur, smem, smem + kTileBytes);
+      run(cur, smem, smem + kTileBytes);
       cur = nxt;
       if (cur < 0) break;
       nxt = next_block(wi, cw);
       dma_sync();
       if (nxt >= 0) stage(nxt, 0);
-      if (wave_live) body(cur, smem + 2 * kTileBytes, smem + 3 * kTileBytes);
+      run(cur, smem + 2 * kTileBytes, smem + 3 * kTileBytes);
       cur = nxt;
     }
+  };
+  // Only the head's last key block can hold fewer than 64 keys: there (a uniform branch) the scores of keys past
+  // N (rows re-read from the last valid key) are set to -inf, so that their exp2 is 0
+  const int ragged_J = (N % 64) ? (N - 1) / 64 : -1;
+  auto mask_tail = [&](v16f& st, int tt, int J) {
+    if (J != ragged_J) return;
+    const int nv = N - J * 64;
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (32 * tt + acc_row(r) >= nv) st[r] = -INFINITY;
   };
   // S^T and dP^T of one 32-key tile tt of the block in tiles tk (K), tv (V)
   auto tile_sdp = [&](const unsigned char* tk, const unsigned char* tv, int tt, v16f& st, v16f& dp) {
@@ -269,22 +291,21 @@ __global__ __launch_bounds__(256, 2) void kb_q(const uint16_t* __restrict__ q, c
   // rescaled when m grows; then LSE = m + log2(l) and D = u / l = sum_j P_ij dP_ij
   float m = -INFINITY, lsum = 0.f, usum = 0.f;
   ring([&](int J, const unsigned char* tk, const unsigned char* tv) {
-    const int nv = min(64, N - J * 64);
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       v16f st, dp;
       tile_sdp(tk, tv, tt, st, dp);
-      // keys past nv (rows re-read from the last valid key) are excluded by selects, not branches
-      float bm = -INFINITY;
+      mask_tail(st, tt, J);
+      // the tile's largest score times c2 > 0 (tile 0 always holds a valid key, so m is finite after it)
+      float bm = st[0];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) bm = fmaxf(bm, 32 * tt + acc_row(r) < nv ? st[r] * c2 : -INFINITY);
-      bm = fmaxf(bm, swap_halves_f32(bm));
+      for (int r = 1; r < 16; ++r) bm = fmaxf(bm, st[r]);
+      bm = fmaxf(bm, swap_halves_f32(bm)) * c2;
       const float mn = fmaxf(m, bm);
       float ps = 0.f, pu = 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float e = __builtin_amdgcn_exp2f(fmaf(st[r], c2, -mn));
-        const float ev = 32 * tt + acc_row(r) < nv ? e : 0.f;
+        const float ev = __builtin_amdgcn_exp2f(fmaf(st[r], c2, -mn));
         ps += ev;
         pu = fmaf(ev, dp[r], pu);
       }
@@ -309,16 +330,15 @@ __global__ __launch_bounds__(256, 2) void kb_q(const uint16_t* __restrict__ q, c
   for (int u = 0; u < 4; ++u) acc[u] = (v16f){};
   __syncthreads();  // pass 1's reads of both slots are done
   ring([&](int J, const unsigned char* tk, const unsigned char* tv) {
-    const int nv = min(64, N - J * 64);
     const float nl2 = -lse;
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       v16f st, dp;
       tile_sdp(tk, tv, tt, st, dp);
+      mask_tail(st, tt, J);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float e = __builtin_amdgcn_exp2f(fmaf(st[r], c2, nl2));
-        const float p = 32 * tt + acc_row(r) < nv ? e : 0.f;
+        const float p = __builtin_amdgcn_exp2f(fmaf(st[r], c2, nl2));
         st[r] = p * (dp[r] - dsum);
       }
 #pragma unroll
@@ -391,52 +411,74 @@ __global__ __launch_bounds__(256, 2) void kb_kv(const uint16_t* __restrict__ q, 
   v16f accv[4], acck[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) accv[u] = acck[u] = (v16f){};
-  const uint32_t* jb = bits + ((size_t)bh * n_kb + J) * n_qbw;
-  for (int wd = 0; wd < n_qbw; ++wd) {
-    uint32_t word = jb[wd];
-    while (word) {
-      const int I = 32 * wd + __builtin_ctz(word);
-      word &= word - 1;
+  // the steps: (query block I that selected J, 64-row half h0), in order; a cursor over the bitmap words (read
+  // through the constant address space: scalar loads, which leave the vector-memory counter to the tile loads)
+  typedef __attribute__((address_space(4))) const uint32_t c_u32;
+  c_u32* jb = (c_u32*)(bits + ((size_t)bh * n_kb + J) * n_qbw);
+  int wd = 0;
+  uint32_t word = jb[0];
+  auto next_I = [&]() -> int {
+    while (word == 0) {
+      if (++wd >= n_qbw) return -1;
+      word = jb[wd];
+    }
+    const int I = 32 * wd + __builtin_ctz(word);
+    word &= word - 1;
+    return I;
+  };
+  int I = next_I(), h0 = 0;
+  while (I >= 0) {
+    {
       const int q0 = I * blk_q, nq = min(blk_q, N - q0);
-      for (int h0 = 0; h0 < nq; h0 += 64) {
-        const int nh = min(64, nq - h0);
-        __syncthreads();  // the previous half's tiles are no longer read
-        load(rq, q0 + h0, nh, sQ);
-        load(ry, q0 + h0, nh, sdY);
-        if (threadIdx.x < 64) {
-          const int ii = threadIdx.x;
-          sL[ii] = ii < nh ? lse_in[(size_t)bh * N + q0 + h0 + ii] : 0.f;
-          sDd[ii] = ii < nh ? d_in[(size_t)bh * N + q0 + h0 + ii] : 0.f;
-        }
-        dma_sync();
-        v16f s = (v16f){}, dp = (v16f){};
+      const int nh = min(64, nq - h0);
+      int In = I, hn = h0 + 64;
+      if (hn >= nq) {
+        In = next_I();
+        hn = 0;
+      }
+      lds_sync();  // the previous half's tiles are no longer read
+      // the half's row statistics are loaded before its tiles, so that storing them waits for them alone
+      float lse_r = 0.f, d_r = 0.f;
+      if (threadIdx.x < nh) {
+        lse_r = lse_in[(size_t)bh * N + q0 + h0 + threadIdx.x];
+        d_r = d_in[(size_t)bh * N + q0 + h0 + threadIdx.x];
+      }
+      load(rq, q0 + h0, nh, sQ);
+      load(ry, q0 + h0, nh, sdY);
+      if (threadIdx.x < 64) {
+        sL[threadIdx.x] = lse_r;
+        sDd[threadIdx.x] = d_r;
+      }
+      dma_sync();
+      I = In;
+      h0 = hn;
+      v16f s = (v16f){}, dp = (v16f){};
 #pragma unroll
-        for (int sd = 0; sd < 8; ++sd) {
-          const uint32_t o = oq ^ (32u * sd), okv = o + dkv;
-          s = mfma(ld_row(sQ + o), ld_row(sK + okv), s);
-          dp = mfma(ld_row(sdY + o), ld_row(sV + okv), dp);
-        }
-        // s[r] -> P, dp[r] -> dS for row 32 ch + acc_row(r) and key j_loc (the fences keep the row statistics'
-        // reads and the transposed operand reads from being hoisted while every accumulator is live)
+      for (int sd = 0; sd < 8; ++sd) {
+        const uint32_t o = oq ^ (32u * sd), okv = o + dkv;
+        s = mfma(ld_row(sQ + o), ld_row(sK + okv), s);
+        dp = mfma(ld_row(sdY + o), ld_row(sV + okv), dp);
+      }
+      // s[r] -> P, dp[r] -> dS for row 32 ch + acc_row(r) and key j_loc (the fences keep the row statistics'
+      // reads and the transposed operand reads from being hoisted while every accumulator is live)
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int ii = 32 * ch + acc_row(r);  // < 64: the row statistics are read unconditionally
+        const float e = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -sL[ii]));
+        const float p = ii < nh ? e : 0.f;
+        dp[r] = p * (dp[r] - sDd[ii]);
+        s[r] = p;
+      }
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
         __builtin_amdgcn_sched_barrier(0);
+        const v8bf pb = cvt8(s, st), db = cvt8(dp, st);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int ii = 32 * ch + acc_row(r);  // < 64: the row statistics are read unconditionally
-          const float e = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -sL[ii]));
-          const float p = ii < nh ? e : 0.f;
-          dp[r] = p * (dp[r] - sDd[ii]);
-          s[r] = p;
-        }
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          __builtin_amdgcn_sched_barrier(0);
-          const v8bf pb = cvt8(s, st), db = cvt8(dp, st);
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const uint32_t t0 = tq[0] ^ (64u * u), t1 = tq[1] ^ (64u * u);
-            accv[u] = mfma(ld_tr(sdY + 4096 * st + t0, sdY + 4096 * st + t1), pb, accv[u]);
-            acck[u] = mfma(ld_tr(sQ + 4096 * st + t0, sQ + 4096 * st + t1), db, acck[u]);
-          }
+        for (int u = 0; u < 4; ++u) {
+          const uint32_t t0 = tq[0] ^ (64u * u), t1 = tq[1] ^ (64u * u);
+          accv[u] = mfma(ld_tr(sdY + 4096 * st + t0, sdY + 4096 * st + t1), pb, accv[u]);
+          acck[u] = mfma(ld_tr(sQ + 4096 * st + t0, sQ + 4096 * st + t1), db, acck[u]);
         }
       }
     }

@@ -57,8 +57,12 @@ EPILOGUE_PRODUCTS_EXECUTED = 3
 CPU_HEADS = {"tiny": 2, "wan1.3b-480p-dense": 4, "wan1.3b-480p-sla": 6, "wan14b-720p-sla-pair": 2,
              "1080p-long-sla": 1}
 CPU_BLOCKS = {"1080p-long-sla": 128}
-COUNTERS = os.path.join(ROOT, "profiles", "k3_attn_wan14b-720p-sla-pair_counters.txt")
-K3_SOURCE = os.path.join(ROOT, "int8_block_sparse_amd", "csrc", "k_attn.hip")
+CSRC = os.path.join(ROOT, "int8_block_sparse_amd", "csrc")
+COUNTERS = os.path.join(ROOT, "profiles", "forward_hbm_wan14b-720p-sla-pair.txt")
+K3_SOURCE = os.path.join(CSRC, "k_attn.hip")
+# the kernels whose HBM traffic the headline line reports from the committed counter summary, with their sources
+HBM_KERNELS = {"k3_attn<4, false>": "k_attn.hip", "k1_quant<128, false>": "k_quant.hip", "k4_states16": "k_linear.hip",
+               "k4_gemm16": "k_linear.hip"}
 W8A8_COUNTERS = os.path.join(ROOT, "profiles", "k5_gemm_wan14b-720p-proj_counters.txt")
 W8A8_SOURCE = os.path.join(ROOT, "int8_block_sparse_amd", "csrc", "k_w8a8.hip")
 
@@ -72,22 +76,49 @@ def source_sha(path):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def read_counters(path=COUNTERS, source=K3_SOURCE):
-    """HBM bytes per launch of a workload's dominant kernel from its committed rocprofv3 counter summary, or
-    None when absent or taken on a different kernel source."""
-    if not os.path.exists(path):
-        return None
+def _summary_kv(path):
     kv = {}
     for line in open(path):
         if ": " in line and not line.startswith("#"):
             k, v = line.rsplit(": ", 1)  # keys may hold ':' themselves ("sha256[:16]")
             kv[k.strip()] = v.strip()
+    return kv
+
+
+def read_counters(path=COUNTERS, source=K3_SOURCE, kernel=None):
+    """HBM bytes per launch of a kernel (default: the summary's dominant kernel) from a committed rocprofv3
+    counter summary, or None when absent or taken on a different kernel source."""
+    if not os.path.exists(path):
+        return None
+    kv = _summary_kv(path)
     if kv.get(f"{os.path.basename(source)} sha256[:16]") != source_sha(source):
         return None
+    key = (f"{kernel} hbm bytes per launch (fetch+write, copy-calibrated)" if kernel
+           else "hbm bytes per launch (fetch+write, copy-calibrated)")
     try:
-        return float(kv["hbm bytes per launch (fetch+write, copy-calibrated)"])
+        return float(kv[key])
     except (KeyError, ValueError):
         return None
+
+
+def read_kernel_hbm(path=COUNTERS):
+    """Per-kernel HBM bytes and kernel-trace time per launch of the forward's bandwidth-bound kernels from the
+    committed counter summary; a kernel whose source changed since is left out."""
+    if not os.path.exists(path):
+        return {}
+    kv = _summary_kv(path)
+    out = {}
+    for kern, src in HBM_KERNELS.items():
+        if kv.get(f"{src} sha256[:16]") != source_sha(os.path.join(CSRC, src)):
+            continue
+        try:
+            byt = float(kv[f"{kern} hbm bytes per launch (fetch+write, copy-calibrated)"])
+            ms = float(kv[f"{kern} average launch (kernel trace) ms"])
+        except (KeyError, ValueError):
+            continue
+        out[kern] = {"hbm_bytes": byt, "ms": ms, "achieved_GBps": round(byt / ms / 1e6, 1),
+                     "frac": round(byt / ms / 1e6 / PEAK_HBM_GBPS, 4)}
+    return out
 
 
 MFMA_COUNTERS = os.path.join(ROOT, "profiles", "k3_attn_wan14b-720p-sla-pair_mfma_counters.txt")
@@ -106,7 +137,7 @@ def read_mfma_util(path=MFMA_COUNTERS, source=K3_SOURCE):
     if kv.get(f"{os.path.basename(source)} sha256[:16]") != source_sha(source):
         return None
     for k, v in kv.items():
-        if k.startswith("MfmaUtil"):
+        if k.startswith("k3_attn<4, false> MfmaUtil"):
             try:
                 return float(v)
             except ValueError:
@@ -439,7 +470,17 @@ def main():
                          "the synth module by name (tiny, wan1.3b-480p-dense, wan1.3b-480p-sla, 1080p-long-sla), "
                          "sla-backward (the headline layer's backward for the forward's selection) or w8a8-<shape> "
                          "(the W8A8 linear layer)")
+    ap.add_argument("--summarize", choices=["trace", "hbm", "pmc"],
+                    help="print a summary of rocprofv3 csv output instead of benchmarking: trace DIR (kernel-trace "
+                         "stats), hbm FETCH_DIR WRITE_DIR (copy-calibrated FETCH_SIZE / WRITE_SIZE per kernel; with "
+                         "--trace DIR the kernel-trace times beside them), pmc DIR... (counters averaged per kernel)")
+    ap.add_argument("dirs", nargs="*", help="rocprofv3 output directories for --summarize")
+    ap.add_argument("--trace", help="kernel-trace output directory (--summarize hbm / pmc)")
+    ap.add_argument("--header", action="append", default=[], help="header line of the summary (repeatable)")
+    ap.add_argument("--kernels", default="", help="--summarize pmc: comma-separated kernel name prefixes to keep")
     args = ap.parse_args()
+    if args.summarize:
+        return summarize(args)
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the forward shards by "
               f"(batch, head) with no exchange, so N GPUs would each run this same kernel set on B*H/N heads.",
@@ -460,6 +501,146 @@ def main():
     return main_forward(args, by_name[name])
 
 
+# ---------------------------------------------------------------------------------------------------------------
+# summaries of rocprofv3 csv output (the tables committed under profiles/)
+# ---------------------------------------------------------------------------------------------------------------
+def _short_kernel(name):
+    """'void sagesla::k3_attn<4, false>(signed char const*, ...)' -> 'k3_attn<4, false>'; other kernels keep a
+    shortened name"""
+    n = name.replace("void ", "", 1)
+    if "sagesla::" in n:
+        n = n.split("sagesla::", 1)[1]
+        depth, cut = 0, len(n)
+        for i, ch in enumerate(n):
+            if ch == "<":
+                depth += 1
+            elif ch == ">":
+                depth -= 1
+            elif ch == "(" and depth == 0:
+                cut = i
+                break
+        return n[:cut]
+    return "torch " + n.split("(")[0][:40]
+
+
+def _csv_rows(d, suffix):
+    import csv
+    import glob
+    files = sorted(glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True))
+    if not files:
+        sys.exit(f"no *{suffix} under {d}")
+    rows = []
+    for f in files:
+        rows += list(csv.DictReader(open(f)))
+    return rows
+
+
+def _trace_ms(d):
+    """average launch time (ms) and calls per kernel from a kernel-trace stats csv"""
+    return {_short_kernel(r["Name"]): (float(r["AverageNs"]) * 1e-6, int(r["Calls"]))
+            for r in _csv_rows(d, "kernel_stats.csv")}
+
+
+def _counters(dirs):
+    """per kernel and counter, the values of every dispatch"""
+    acc = {}
+    for d in dirs:
+        for r in _csv_rows(d, "counter_collection.csv"):
+            acc.setdefault(_short_kernel(r["Kernel_Name"]), {}).setdefault(r["Counter_Name"], []).append(
+                float(r["Counter_Value"]))
+    return acc
+
+
+def summarize(args):
+    out = [f"# {h}" for h in args.header]
+    if args.summarize == "trace":
+        t = _trace_ms(args.dirs[0])
+        total = sum(ms * c for ms, c in t.values())
+        ours = {k: v for k, v in t.items() if not k.startswith("torch ")}
+        out.append(f"{'kernel':40s} {'calls':>6s} {'avg_ms':>10s} {'share':>7s}")
+        for k, (ms, c) in sorted(ours.items(), key=lambda kv: -kv[1][0] * kv[1][1]):
+            out.append(f"{k:40s} {c:6d} {ms:10.4f} {100 * ms * c / total:6.1f}%")
+        other = [(ms, c) for k, (ms, c) in t.items() if k.startswith("torch ")]
+        if other:
+            out.append(f"{'torch kernels (seeded inputs, copies)':40s} {sum(c for _, c in other):6d} {'':>10s} "
+                       f"{100 * sum(ms * c for ms, c in other) / total:6.1f}%")
+    elif args.summarize == "hbm":
+        f_dir, w_dir = args.dirs[:2]
+        fetch = {k: v["FETCH_SIZE"] for k, v in _counters([f_dir]).items() if "FETCH_SIZE" in v}
+        write = {k: v["WRITE_SIZE"] for k, v in _counters([w_dir]).items() if "WRITE_SIZE" in v}
+        copy = [k for k in fetch if "copyBuffer" in k]
+        if not copy or not args.calib_copy_mib:
+            sys.exit("--summarize hbm needs the calibration copy (--calib-copy-mib M, as in the profiled run)")
+        kib = args.calib_copy_mib * 1024.0
+        f_scale, w_scale = kib / fetch[copy[0]][-1], kib / write[copy[0]][-1]
+        out.append(f"# calibration: one {args.calib_copy_mib} MiB device copy reads FETCH_SIZE "
+                   f"{fetch[copy[0]][-1]:.1f} KiB and WRITE_SIZE {write[copy[0]][-1]:.1f} KiB -> scale factors "
+                   f"fetch {f_scale:.3f}, write {w_scale:.3f}")
+        out.append("# bytes past L2 (served by the Infinity Cache or HBM) per kernel, averaged over its dispatches")
+        tm = _trace_ms(args.trace) if args.trace else {}
+        out.append(f"{'kernel':40s} {'fetch_GB':>10s} {'write_GB':>10s} {'avg_ms':>9s} {'GB/s':>9s}")
+        per = {}
+        for k in sorted(fetch, key=lambda k: -sum(fetch[k]) / len(fetch[k])):
+            if k in copy or k not in write or k.startswith("torch "):
+                continue
+            fb = sum(fetch[k]) / len(fetch[k]) * f_scale * 1024
+            wb = sum(write[k]) / len(write[k]) * w_scale * 1024
+            per[k] = fb + wb
+            ms = tm.get(k, (float("nan"), 0))[0]
+            out.append(f"{k:40s} {fb / 1e9:10.3f} {wb / 1e9:10.3f} {ms:9.4f} {per[k] / ms / 1e6:9.1f}")
+        out.append("")
+        srcs = sorted({src for kern, src in HBM_KERNELS.items() if kern in per})
+        for src in srcs:
+            out.append(f"{src} sha256[:16]: {source_sha(os.path.join(CSRC, src))}")
+        for kern in HBM_KERNELS:
+            if kern in per:
+                out.append(f"{kern} hbm bytes per launch (fetch+write, copy-calibrated): {per[kern]:.6g}")
+                if kern in tm:
+                    out.append(f"{kern} average launch (kernel trace) ms: {tm[kern][0]:.4f}")
+        dom = max((k for k in per if k in HBM_KERNELS), key=lambda k: tm.get(k, (0, 0))[0], default=None)
+        if dom:
+            out.append(f"hbm bytes per launch (fetch+write, copy-calibrated): {per[dom]:.6g}")
+    else:
+        acc = _counters(args.dirs)
+        tm = _trace_ms(args.trace) if args.trace else {}
+        keep = [x for x in args.kernels.split(",") if x]
+        for k, cs in sorted(acc.items()):
+            if k.startswith("torch ") or (keep and not k.startswith(tuple(keep))):
+                continue
+            out.append(k + (f"   (kernel trace {tm[k][0]:.4f} ms)" if k in tm else ""))
+            avg = {c: sum(v) / len(v) for c, v in cs.items()}
+            for c in sorted(avg):
+                out.append(f"   {c:32s} {avg[c]:16.6g}")
+            if "GRBM_GUI_ACTIVE" in avg:
+                cyc = avg["GRBM_GUI_ACTIVE"] / 8  # per XCD
+                simd = 1024 * cyc
+                if "SQ_VALU_MFMA_BUSY_CYCLES" in avg:
+                    out.append(f"{k} MfmaUtil (SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE per XCD x 1024 SIMDs)): "
+                               f"{avg['SQ_VALU_MFMA_BUSY_CYCLES'] / simd:.4f}")
+                if "SQ_VALU_MFMA_COEXEC_CYCLES" in avg:
+                    out.append(f"{k} VALU-MFMA co-execution fraction of SIMD cycles: "
+                               f"{avg['SQ_VALU_MFMA_COEXEC_CYCLES'] / simd:.4f}")
+                if "SQ_ACTIVE_INST_VALU" in avg:
+                    out.append(f"{k} VALU active fraction of SIMD cycles (SQ_ACTIVE_INST_VALU x 4): "
+                               f"{4 * avg['SQ_ACTIVE_INST_VALU'] / simd:.4f}")
+                if "SQ_LDS_IDX_ACTIVE" in avg:
+                    out.append(f"{k} LDS active fraction of CU cycles (SQ_LDS_IDX_ACTIVE / (256 x cycles)): "
+                               f"{avg['SQ_LDS_IDX_ACTIVE'] / (256 * cyc):.4f}")
+                if k in tm:
+                    out.append(f"{k} shader clock implied over the launch: {cyc / tm[k][0] / 1e6:.3f} GHz")
+            if "SQ_WAIT_ANY" in avg and "SQ_WAVE_CYCLES" in avg:
+                out.append(f"{k} waiting (SQ_WAIT_ANY / SQ_WAVE_CYCLES): {avg['SQ_WAIT_ANY'] / avg['SQ_WAVE_CYCLES']:.4f}")
+            for key, mul, what in (("SQ_INSTS_VALU_MFMA_MOPS_I8", 512, "INT8 MFMA ops per launch"),
+                                   ("SQ_INSTS_VALU_MFMA_MOPS_BF16", 512, "BF16 MFMA flops per launch"),
+                                   ("SQ_INSTS_VALU_MFMA_MOPS_F16", 512, "FP16 MFMA flops per launch")):
+                if key in avg:
+                    out.append(f"{k} {what} ({key} x {mul}): {avg[key] * mul:.6g}")
+        srcs = sorted({src for kern, src in HBM_KERNELS.items() if kern in acc})
+        for src in srcs:
+            out.append(f"{src} sha256[:16]: {source_sha(os.path.join(CSRC, src))}")
+    print("\n".join(out))
+
+
 def stage_bytes(wl):
     """Algorithmic HBM bytes of the quantize and linear stages of one forward: every input a kernel of the stage
     reads, once per kernel that reads it, and every output it writes (an intermediate that a later kernel of
@@ -476,9 +657,9 @@ def stage_bytes(wl):
     lin = {}
     if wl.linear and wl.topk < nkb:
         lin = {
-            "k4_states": 2 * bf16 + BH * nkb * STATE_BYTES_PER_BLOCK,  # reads K, V; writes the state table
+            "k4_states16": 2 * bf16 + BH * nkb * STATE_BYTES_PER_BLOCK,  # reads K, V; writes the state table
             "k4_mask": 4 * BH * nqb * wl.topk + BH * nqb * ((nkb + 31) // 32) * 4,
-            "k4_gemm": BH * nkb * STATE_BYTES_PER_BLOCK + BH * nqb * REMAINING_BYTES_PER_QBLOCK,
+            "k4_gemm16": BH * nkb * STATE_BYTES_PER_BLOCK + BH * nqb * REMAINING_BYTES_PER_QBLOCK,
         }
     return {"quantize": quant, "linear": lin}
 
@@ -611,6 +792,17 @@ def main_forward(args, wl):
         },
         "hbm_stages": hbm,
     }
+    if headline:
+        # per kernel, from the committed counter summary of the same sources: HBM bytes past L2 (FETCH_SIZE +
+        # WRITE_SIZE, copy-calibrated) over the kernel-trace launch time, beside the algorithmic bytes
+        kern = read_kernel_hbm()
+        alg = {**sb["quantize"], **sb["linear"]}
+        for name, d in kern.items():
+            base = name.split("<")[0]
+            if base in alg:
+                d["algorithmic_bytes"] = float(alg[base])
+                d["algorithmic_frac"] = round(alg[base] / d["ms"] / 1e6 / PEAK_HBM_GBPS, 4)
+        result["hbm_kernels_profiled"] = kern
     if not args.no_cpu_baseline:
         # a bounded sample of whole (b, h) heads, about 10-30 s of CPU work
         del ws

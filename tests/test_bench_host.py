@@ -31,7 +31,9 @@ def test_mfma_summary_parses_and_is_source_gated(tmp_path):
     src.write_text("// kernel\n")
     f = tmp_path / "m.txt"
     f.write_text(f"# a: b\nk.hip sha256[:16]: {bench.source_sha(str(src))}\n"
-                 "MfmaUtil (SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE per XCD x 1024 SIMDs)): 0.5552\n")
+                 "k4_gemm16 MfmaUtil (SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE per XCD x 1024 SIMDs)): 0.11\n"
+                 "k3_attn<4, false> MfmaUtil (SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE per XCD x 1024 SIMDs)): "
+                 "0.5552\n")
     assert bench.read_mfma_util(str(f), str(src)) == 0.5552
     src.write_text("// changed kernel\n")
     assert bench.read_mfma_util(str(f), str(src)) is None
@@ -46,6 +48,32 @@ def test_stage_bytes_of_the_headline_layer():
     sb = bench.stage_bytes(wl)
     elems = wl.B * wl.H * wl.N * wl.D
     assert abs(sum(sb["quantize"].values()) - 12 * elems) < 0.02 * 12 * elems
-    assert set(sb["linear"]) == {"k4_states", "k4_mask", "k4_gemm"}
+    assert set(sb["linear"]) == {"k4_states16", "k4_mask", "k4_gemm16"}
     assert not bench.stage_bytes(synth.WORKLOADS[1])["linear"]  # the dense layer runs no linear branch
 
+
+
+def test_kernel_hbm_summary_parses_and_is_source_gated(tmp_path, monkeypatch):
+    csrc = tmp_path / "csrc"
+    csrc.mkdir()
+    for name in ("k_attn.hip", "k_quant.hip", "k_linear.hip"):
+        (csrc / name).write_text(f"// {name}\n")
+    monkeypatch.setattr(bench, "CSRC", str(csrc))
+    sha = {n: bench.source_sha(str(csrc / n)) for n in ("k_attn.hip", "k_quant.hip", "k_linear.hip")}
+    f = tmp_path / "h.txt"
+    f.write_text("# header: x\n" + "".join(f"{n} sha256[:16]: {s}\n" for n, s in sha.items())
+                 + "k1_quant<128, false> hbm bytes per launch (fetch+write, copy-calibrated): 8e+09\n"
+                 + "k1_quant<128, false> average launch (kernel trace) ms: 2.0\n"
+                 + "k4_gemm16 hbm bytes per launch (fetch+write, copy-calibrated): 4e+09\n"
+                 + "k4_gemm16 average launch (kernel trace) ms: 1.0\n")
+    got = bench.read_kernel_hbm(str(f))
+    assert got["k1_quant<128, false>"]["achieved_GBps"] == 4000.0 and got["k1_quant<128, false>"]["frac"] == 0.5
+    assert got["k4_gemm16"]["frac"] == 0.5 and "k3_attn<4, false>" not in got
+    (csrc / "k_linear.hip").write_text("// changed\n")
+    assert set(bench.read_kernel_hbm(str(f))) == {"k1_quant<128, false>"}
+
+
+def test_short_kernel_names():
+    assert bench._short_kernel("void sagesla::k3_attn<4, false>(signed char const*, int)") == "k3_attn<4, false>"
+    assert bench._short_kernel("sagesla::k4_gemm16(unsigned short const*, int)") == "k4_gemm16"
+    assert bench._short_kernel("void at::native::foo<1>(int)").startswith("torch ")

@@ -525,9 +525,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k4_gemm(const float* __restri
 // (exact in fp16 down to 2^-24; a block more than 24 binades below the head's largest is dropped), and the sums are
 // the remaining state times 2^-E, H_m and Z_m alike (the linear branch's quotient does not see the common factor).
 // grid (kStateX / 128 column groups, ceil(n_qb / 640) query-block chunks, BH), 512 threads (8 waves).
-// Step = 32 key blocks (two k-steps of 16) = one mask word per query block. Table slices (32 rows of 256 B)
-// arrive by buffer loads to LDS with their 16-byte chunks swizzled (tswz), three steps ahead, with the chunk's
-// mask words; four-slot rings, one wait and one barrier per step. The table operand comes straight from the slice
+// Step = 32 key blocks (two k-steps of 16) = one mask word per query block. Table slices (32 rows of 256 B) and
+// the chunk's mask words are loaded into registers four steps ahead and written to a three-slot LDS ring (16-byte
+// chunks swizzled by tswz) one step ahead; one barrier per step. The table operand comes straight from the slice
 // by transposing reads; the mask operand is the nibble table's 0 / 1.0 patterns ANDed with the step's eight scales.
 // The table is the first operand, so the accumulators hold C^T: every lane holds runs of four consecutive columns
 // of one query block. Wave w owns query tiles 5 (w / 2) .. +4 and column tiles 2 (w % 2), +1.

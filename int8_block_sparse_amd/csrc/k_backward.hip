@@ -543,8 +543,8 @@ __global__ __launch_bounds__(256) void kb_lin_q(const uint16_t* __restrict__ q, 
   unsigned char* sHh = smem + 4 * kTileBytes;   // H_m^T [e][c] hi, lo
   unsigned char* sHl = smem + 6 * kTileBytes;
   float* sZ = (float*)(smem + 8 * kTileBytes);  // [128]
-  float* sDen = sZ + kD;                        // [128]
-  float* sDd = sDen + kD;                       // [128] dden
+  float* sInv = sZ + kD;                        // [128] 1 / den (0 past nq)
+  float* sDd = sInv + kD;                       // [128] dden
   const int I = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6), l = t & 63, g = l >> 5;
   const int r0 = I * blk_q, nq = min(blk_q, N - r0);
@@ -558,7 +558,7 @@ __global__ __launch_bounds__(256) void kb_lin_q(const uint16_t* __restrict__ q, 
   {
     const int i = t >> 1, hc = t & 1;
     float dpart = 0.f;
-#pragma unroll 2
+#pragma unroll
     for (int qq = 0; qq < 8; ++qq) {
       const int c0 = 64 * hc + 8 * qq;
       uint4 raw = make_uint4(0, 0, 0, 0);
@@ -579,9 +579,9 @@ __global__ __launch_bounds__(256) void kb_lin_q(const uint16_t* __restrict__ q, 
       *(uint4*)(sPl + toff(i, c0)) = make_uint4(o[0], o[1], o[2], o[3]);
     }
     const float other = __shfl_xor(dpart, 1);
-    if (hc == 0) sDen[i] = dpart + other;
+    if (hc == 0) sInv[i] = i < nq ? 1.f / (dpart + other) : 0.f;  // the divisions below become products
   }
-#pragma unroll 4
+#pragma unroll
   for (int it = 0; it < 16; ++it) {  // the planes of H_m^T, re-swizzled: 2 planes x 128 rows x 16 chunks
     const int u = t + 256 * it, pl = u >> 11, e = (u >> 4) & 127, qq = u & 15;
     const uint4 x = *(const uint4*)(rec + 32768 * pl + out_off(e, 8 * qq));
@@ -612,7 +612,7 @@ __global__ __launch_bounds__(256) void kb_lin_q(const uint16_t* __restrict__ q, 
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int i = 32 * a + acc_row(r);
-      if (i < nq) o_l[((size_t)bh * N + r0 + i) * kD + ecol] = acc[a][r] / sDen[i];
+      if (i < nq) o_l[((size_t)bh * N + r0 + i) * kD + ecol] = acc[a][r] * sInv[i];
     }
 
   // dO_l (same tiles): D[i][e] = sum_f dY[i][f] W_p[e][f]; A read from global rows of dY, B from rows of W_p
@@ -627,14 +627,11 @@ __global__ __launch_bounds__(256) void kb_lin_q(const uint16_t* __restrict__ q, 
 #pragma unroll
     for (int s = 0; s < 8; ++s) acc[a] = mfma(*(const v8bf*)(yrow + 16 * s), wb[s], acc[a]);
   }
-  // dnum = dO_l / den (0 on rows past nq)
+  // dnum = dO_l / den (0 on rows past nq, whose 1 / den is stored as 0)
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int i = 32 * a + acc_row(r);
-      acc[a][r] = i < nq ? acc[a][r] / sDen[i] : 0.f;
-    }
+    for (int r = 0; r < 16; ++r) acc[a][r] *= sInv[32 * a + acc_row(r)];
 
   // dH_m (wave w: columns e of tile w): D[c][e] = sum_i phi(Q)^T[c][i] dnum[i][e], phi(Q)^T read transposed in
   // accumulator row order so that dnum serves as B from its registers
@@ -711,18 +708,28 @@ __global__ __launch_bounds__(256) void kb_lin_q(const uint16_t* __restrict__ q, 
       }
     }
   dot += swap_halves_f32(dot);
-  const float dden = iv ? -dot / sDen[irow] : 0.f;
+  const float dden = iv ? -dot * sInv[irow] : 0.f;
   if (l < 32) sDd[irow] = dden;
   if (iv) {
+    // read-modify-write of dQ: every load (dQ and the q values) issued before the first store
     float* dst = dq + ((size_t)bh * N + r0 + irow) * kD;
+    float4 dold[16];
+    uint2 qraw[16];
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
       for (int r = 0; r < 16; r += 4) {
         const int c0 = 32 * ct + acc_row(r);
-        const uint2 raw = *(const uint2*)(qrow + c0);
-        const uint32_t wv[2] = {raw.x, raw.y};
-        float4 d = *(float4*)(dst + c0);
+        dold[4 * ct + r / 4] = *(const float4*)(dst + c0);
+        qraw[4 * ct + r / 4] = *(const uint2*)(qrow + c0);
+      }
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+      for (int r = 0; r < 16; r += 4) {
+        const int c0 = 32 * ct + acc_row(r);
+        const uint32_t wv[2] = {qraw[4 * ct + r / 4].x, qraw[4 * ct + r / 4].y};
+        float4 d = dold[4 * ct + r / 4];
         float* dd = (float*)&d;
 #pragma unroll
         for (int e2 = 0; e2 < 4; ++e2) {
@@ -732,12 +739,34 @@ __global__ __launch_bounds__(256) void kb_lin_q(const uint16_t* __restrict__ q, 
         *(float4*)(dst + c0) = d;
       }
   }
+  __syncthreads();  // G's reads of the H_m^T tiles are done and dden is in LDS
+  // dZ_m[c] = sum_i phi(Q)[i][c] dden[i]: the block's Q rows into the free H_m^T tile (all loads issued before
+  // any is waited for), then per column two half sums (rows 0-63 and 64-127, ascending) added in that order
+  {
+    uint4 x[8];
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int u = t + 256 * it, i = u >> 4;
+      x[it] = i < nq ? *(const uint4*)(qr + (size_t)i * kD + 8 * (u & 15)) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int u = t + 256 * it;
+      *(uint4*)(sHh + 16 * u) = x[it];  // row u / 16 at 256 (u / 16), unswizzled
+    }
+  }
   __syncthreads();
-  // dZ_m[c] = sum_i phi(Q)[i][c] dden[i] (rows in ascending order)
-  if (t < kD) {
+  {
+    const int c = t & 127, half = t >> 7;
+    const uint16_t* qs = (const uint16_t*)sHh;
     float sz = 0.f;
-    for (int i = 0; i < nq; ++i) sz = fmaf(phi_f(bf16_lo(qr[(size_t)i * kD + t])), sDd[i], sz);
-    dhm[(((size_t)bh * (kStateX / 128) + kD) * n_qb + I) * 128 + t] = sz;
+#pragma unroll 8
+    for (int i = 64 * half; i < 64 * half + 64; ++i)
+      if (i < nq) sz = fmaf(phi_f(bf16_lo(qs[i * kD + c])), sDd[i], sz);
+    float* part = (float*)sHl;
+    if (half == 1) part[c] = sz;
+    __syncthreads();
+    if (half == 0) dhm[(((size_t)bh * (kStateX / 128) + kD) * n_qb + I) * 128 + c] = sz + part[c];
   }
 }
 
@@ -827,14 +856,24 @@ __global__ __launch_bounds__(512) void kb_lin_k(const uint16_t* __restrict__ k, 
   // acc[r]: key j = 32 jt + acc_row(r), column 32 ct + l % 32 (c for dK, e for dV)
   const int col = 32 * ct + (l & 31);
   const float zc = sZ[col];
+  // read-modify-write of dK and dV: every load issued before the first store (a store between them would make
+  // each load wait for the previous one)
+  float okv[16], ovv[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int j = 32 * jt + acc_row(r);
+    const size_t o = ((size_t)bh * N + j0 + min(j, nk - 1)) * kD + col;
+    okv[r] = dk[o];
+    ovv[r] = dv[o];
+  }
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int j = 32 * jt + acc_row(r);
     if (j < nk) {
       const size_t o = ((size_t)bh * N + j0 + j) * kD + col;
       const float kv = bf16_lo(*(const uint16_t*)(sK + toff(j, col & ~3) + 2 * (col & 3)));
-      dk[o] += (acck[r] + zc) * dphi(kv);
-      dv[o] += accv[r];
+      dk[o] = okv[r] + (acck[r] + zc) * dphi(kv);
+      dv[o] = ovv[r] + accv[r];
     }
   }
 }

@@ -528,7 +528,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k4_gemm(const float* __restri
 // Step = 32 key blocks (two k-steps of 16) = one mask word per query block. Table slices (32 rows of 256 B) and
 // the chunk's mask words are loaded into registers four steps ahead and written to a three-slot LDS ring (16-byte
 // chunks swizzled by tswz) one step ahead; one barrier per step. The table operand comes straight from the slice
-// by transposing reads; the mask operand is the nibble table's 0 / 1.0 patterns ANDed with the step's eight scales.
+// by transposing reads; the mask operand is two reads from the step's pattern tables (per group of four key blocks,
+// the nibble's 0 / scale patterns, built once per step).
 // The table is the first operand, so the accumulators hold C^T: every lane holds runs of four consecutive columns
 // of one query block. Wave w owns query tiles 5 (w / 2) .. +4 and column tiles 2 (w % 2), +1.
 // The store writes each query block's row e = x of H_m^T as an fp16 plane row with its own factor (the row's
@@ -549,9 +550,13 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k4_gemm16(const uint16_t* __r
   __shared__ __attribute__((aligned(1024))) unsigned char s_st0[8192], s_st1[8192], s_st2[8192];
   __shared__ __attribute__((aligned(1024))) uint32_t s_w0[2 * kGemmThreads], s_w1[2 * kGemmThreads],
       s_w2[2 * kGemmThreads];
-  // nibble -> 4 fp16 of 0 / 1.0 (element i = bit i): 128 B, so every entry sits on banks of its own and the lanes'
-  // reads of different entries never conflict
-  __shared__ __attribute__((aligned(128))) uint2 s_lut4[16];
+  // Per step, the mask operand's patterns with the scales applied: for each group of four key blocks (eight per step)
+  // a table nibble -> 4 fp16 (element i = bit i ? scale of block 4 q + i : 0), 16 entries of 8 B (128 B: the lanes'
+  // reads of different entries never share a bank). Group q = 4 sub + 2 g + h (k-step sub, lane half g, nibble h)
+  // sits at 640 sub + 384 g + 128 h, so the two lane halves of an operand read different banks too. Three slots, as
+  // the table slices.
+  constexpr int kLgSlot = 1280;
+  __shared__ __attribute__((aligned(1024))) unsigned char s_lg0[kLgSlot], s_lg1[kLgSlot], s_lg2[kLgSlot];
   __shared__ __attribute__((aligned(16))) uint16_t s_asc[kMaxKeyBlocks + 64];  // fp16 2^(e_J - E)
   __shared__ int s_red[kGemmThreads / 64];
   constexpr int n_xt = kStateX / 128;
@@ -564,9 +569,6 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k4_gemm16(const uint16_t* __r
       const_cast<uint16_t*>(table + (size_t)bh * n_xt * n_kb * 128), (short)0, n_xt * n_kb * 256, 0x00020000);
   const __amdgpu_buffer_rsrc_t rm = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint32_t*>(mask + (size_t)bh * n_kbw * qpad), (short)0, n_kbw * qpad * 4, 0x00020000);
-  if (t < 16)
-    s_lut4[t] = make_uint2(((t & 1) ? 0x3C00u : 0u) | ((t & 2) ? 0x3C000000u : 0u),
-                           ((t & 4) ? 0x3C00u : 0u) | ((t & 8) ? 0x3C000000u : 0u));
   // the head's largest block exponent, then the A scales of every key block (0 past n_kb)
   const int32_t* be = bexp + (size_t)bh * n_kb;
   int emax = INT_MIN;
@@ -616,13 +618,23 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k4_gemm16(const uint16_t* __r
 #pragma unroll
   for (int k = 0; k < 10; ++k) acc[k] = (v16f){};
 
-  auto mma = [&](int ss, const uint32_t* __restrict__ W, const unsigned char* __restrict__ st) {
+  // the pattern tables of step ss (threads 0-127, one entry each)
+  auto build = [&](int ss, unsigned char* __restrict__ lg) {
+    if (t < 128) {
+      const int q = t >> 4, n = t & 15;
+      const uint16_t* sc = &s_asc[32 * ss + 4 * q];
+      const uint32_t lo = ((n & 1) ? (uint32_t)sc[0] : 0u) | ((n & 2) ? (uint32_t)sc[1] << 16 : 0u);
+      const uint32_t hi = ((n & 4) ? (uint32_t)sc[2] : 0u) | ((n & 8) ? (uint32_t)sc[3] << 16 : 0u);
+      *(uint2*)(lg + 640 * (q >> 2) + 384 * ((q >> 1) & 1) + 128 * (q & 1) + 8 * n) = make_uint2(lo, hi);
+    }
+  };
+  // lane half g reads the groups 4 sub + 2 g + h at 640 sub + 384 g + 128 h
+  const uint32_t lg_lane = 384u * g;
+  auto mma = [&](int ss, const uint32_t* __restrict__ W, const unsigned char* __restrict__ st,
+                 const unsigned char* __restrict__ lg) {
     uint32_t wq[5];
 #pragma unroll
     for (int q = 0; q < 5; ++q) wq[q] = W[32 * (wit + q) + lr];
-    uint4 sv[2];
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub) sv[sub] = *(const uint4*)&s_asc[32 * ss + 16 * sub + 8 * g];
     v8h bop[2][2];
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub)
@@ -632,10 +644,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k4_gemm16(const uint16_t* __r
     for (int i = 0; i < 10; ++i) {  // tiles past n_it have garbage words, never stored
       const int sub = i / 5, q = i % 5;
       const uint32_t b8 = wq[q] >> (16 * sub + 8 * g);
-      const uint2 m0 = s_lut4[b8 & 15u], m1 = s_lut4[(b8 >> 4) & 15u];
-      const uint4 m8 = make_uint4(m0.x, m0.y, m1.x, m1.y);
-      const v8h a = __builtin_bit_cast(
-          v8h, make_uint4(m8.x & sv[sub].x, m8.y & sv[sub].y, m8.z & sv[sub].z, m8.w & sv[sub].w));
+      const unsigned char* lgs = lg + lg_lane + 640 * sub;
+      const uint2 m0 = *(const uint2*)(lgs + 8 * (b8 & 15u)), m1 = *(const uint2*)(lgs + 128 + 8 * ((b8 >> 4) & 15u));
+      const v8h a = __builtin_bit_cast(v8h, make_uint4(m0.x, m0.y, m1.x, m1.y));
 #pragma unroll
       for (int c = 0; c < 2; ++c)
         acc[2 * q + c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bop[sub][c], a, acc[2 * q + c], 0, 0, 0);
@@ -651,22 +662,26 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k4_gemm16(const uint16_t* __r
   load(1, r1);
   load(2, r2);
   put(r0, s_st0, s_w0);
+  __syncthreads();  // every block's scale is in s_asc
+  build(0, s_lg0);
   load(3, r0);
   auto step = [&](int ss, Stage& nx, const uint32_t* __restrict__ W, const unsigned char* __restrict__ st,
-                  unsigned char* __restrict__ st_next, uint32_t* __restrict__ w_next) {
+                  const unsigned char* __restrict__ lg, unsigned char* __restrict__ st_next,
+                  uint32_t* __restrict__ w_next, unsigned char* __restrict__ lg_next) {
     __syncthreads();
     put(nx, st_next, w_next);
+    build(ss + 1, lg_next);
     load(ss + 4, nx);
-    mma(ss, W, st);
+    mma(ss, W, st, lg);
   };
   int ss = 0;
   for (; ss + 3 <= nss; ss += 3) {
-    step(ss, r1, s_w0, s_st0, s_st1, s_w1);
-    step(ss + 1, r2, s_w1, s_st1, s_st2, s_w2);
-    step(ss + 2, r0, s_w2, s_st2, s_st0, s_w0);
+    step(ss, r1, s_w0, s_st0, s_lg0, s_st1, s_w1, s_lg1);
+    step(ss + 1, r2, s_w1, s_st1, s_lg1, s_st2, s_w2, s_lg2);
+    step(ss + 2, r0, s_w2, s_st2, s_lg2, s_st0, s_w0, s_lg0);
   }
-  if (ss < nss) step(ss, r1, s_w0, s_st0, s_st1, s_w1);
-  if (ss + 1 < nss) step(ss + 1, r2, s_w1, s_st1, s_st2, s_w2);
+  if (ss < nss) step(ss, r1, s_w0, s_st0, s_lg0, s_st1, s_w1, s_lg1);
+  if (ss + 1 < nss) step(ss + 1, r2, s_w1, s_st1, s_lg1, s_st2, s_w2, s_lg2);
   wait_vmem_all_lin();  // the loads past the last step have landed in their registers: nothing is in flight
   __syncthreads();  // every wave is done reading the slots reused below
 

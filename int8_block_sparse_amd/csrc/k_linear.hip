@@ -630,6 +630,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k4_gemm16(const uint16_t* __r
   };
   // lane half g reads the groups 4 sub + 2 g + h at 640 sub + 384 g + 128 h
   const uint32_t lg_lane = 384u * g;
+  const uint32_t bsh = 8u * g;  // the lane half's first mask bit in a k-step's 16
   auto mma = [&](int ss, const uint32_t* __restrict__ W, const unsigned char* __restrict__ st,
                  const unsigned char* __restrict__ lg) {
     uint32_t wq[5];
@@ -643,9 +644,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k4_gemm16(const uint16_t* __r
 #pragma unroll
     for (int i = 0; i < 10; ++i) {  // tiles past n_it have garbage words, never stored
       const int sub = i / 5, q = i % 5;
-      const uint32_t b8 = wq[q] >> (16 * sub + 8 * g);
+      const uint32_t n0 = __builtin_amdgcn_ubfe(wq[q], bsh + 16 * sub, 4);
+      const uint32_t n1 = __builtin_amdgcn_ubfe(wq[q], bsh + 16 * sub + 4, 4);
       const unsigned char* lgs = lg + lg_lane + 640 * sub;
-      const uint2 m0 = *(const uint2*)(lgs + 8 * (b8 & 15u)), m1 = *(const uint2*)(lgs + 128 + 8 * ((b8 >> 4) & 15u));
+      const uint2 m0 = *(const uint2*)(lgs + 8 * n0), m1 = *(const uint2*)(lgs + 128 + 8 * n1);
       const v8h a = __builtin_bit_cast(v8h, make_uint4(m0.x, m0.y, m1.x, m1.y));
 #pragma unroll
       for (int c = 0; c < 2; ++c)

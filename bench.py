@@ -61,8 +61,7 @@ CSRC = os.path.join(ROOT, "int8_block_sparse_amd", "csrc")
 COUNTERS = os.path.join(ROOT, "profiles", "forward_hbm_wan14b-720p-sla-pair.txt")
 K3_SOURCE = os.path.join(CSRC, "k_attn.hip")
 # the kernels whose HBM traffic the headline line reports from the committed counter summary, with their sources
-HBM_KERNELS = {"k3_attn<4, false>": "k_attn.hip", "k1_quant<128, false>": "k_quant.hip", "k4_states16": "k_linear.hip",
-               "k4_gemm16": "k_linear.hip"}
+HBM_KERNELS = {"k3_attn<4, false>": "k_attn.hip", "k1_quant<128, false>": "k_quant.hip", "k4_gemm16": "k_linear.hip"}
 W8A8_COUNTERS = os.path.join(ROOT, "profiles", "k5_gemm_wan14b-720p-proj_counters.txt")
 W8A8_SOURCE = os.path.join(ROOT, "int8_block_sparse_amd", "csrc", "k_w8a8.hip")
 
@@ -647,17 +646,18 @@ def stage_bytes(wl):
     the stage consumes counts once written and once read). Layouts as the kernels store them."""
     BH, N, D, nqb, nkb = wl.B * wl.H, wl.N, wl.D, wl.n_qb, wl.n_kb
     bf16 = 2 * BH * N * D  # one bf16 [B][H][N][D] tensor
+    lin_on = wl.linear and wl.topk < nkb
     quant = {
         "k1_colsum_partial": bf16,  # reads K
         "k1_quant": 3 * bf16  # reads Q, K, V
         + 2 * BH * N * D  # writes the INT8 codes of Q and K
         + BH * nkb * 16384  # V^T images of every key block (the tail block padded)
-        + 4 * BH * (nqb + nkb) + 8 * BH * D * (nqb + nkb),  # scales, pooled means (fp64)
+        + 4 * BH * (nqb + nkb) + 8 * BH * D * (nqb + nkb)  # scales, pooled means (fp64)
+        + (BH * nkb * STATE_BYTES_PER_BLOCK if lin_on else 0),  # the linear branch's state table
     }
     lin = {}
-    if wl.linear and wl.topk < nkb:
+    if lin_on:
         lin = {
-            "k4_states16": 2 * bf16 + BH * nkb * STATE_BYTES_PER_BLOCK,  # reads K, V; writes the state table
             "k4_mask": 4 * BH * nqb * wl.topk + BH * nqb * ((nkb + 31) // 32) * 4,
             "k4_gemm16": BH * nkb * STATE_BYTES_PER_BLOCK + BH * nqb * REMAINING_BYTES_PER_QBLOCK,
         }

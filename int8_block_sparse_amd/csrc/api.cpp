@@ -86,6 +86,7 @@ void make_plan(const sagesla_params* p, unsigned char* ws, Plan* pl, bool backwa
   pl->w_proj = p->w_proj;
   pl->lin_precise = backward;
   const bool lin_active = pl->linear && pl->topk < pl->n_kb;
+  pl->states_in_quant = lin_active && !backward;
   const size_t BH = pl->BH, N = pl->N, D = kD, nqb = pl->n_qb, nkb = pl->n_kb;
   size_t off = 0;
   auto take = [&](size_t bytes) -> unsigned char* {

@@ -50,7 +50,8 @@ struct Plan {
   int32_t* block_idx;   // [BH][n_qb][topk]
   uint16_t* wpt;        // [D][D] bf16: W_p^T in MFMA slot order
   uint32_t* keep_mask;  // [BH][ceil(n_kb/32)][mask_row_pad(n_qb)]   bit J set iff key block J is not selected
-  // the forward's linear branch (fp16 state table)
+  // the forward's linear branch (fp16 state table, written by the quantization kernel when states_in_quant)
+  bool states_in_quant;
   uint16_t* state16;      // [BH][kStateX / 128][n_kb][128] fp16: block J's state times 2^-e_J
   int32_t* state_exp;     // [BH][n_kb] e_J
   unsigned char* plane16; // [BH][D][n_qb][256 B] rows of the fp16 planes of H_m^T
@@ -67,14 +68,15 @@ struct Plan {
 hipError_t launch_qk_norm(const Plan& p, const uint16_t* q, const uint16_t* k, hipStream_t s);
 // K1: K-mean smoothing, per-block INT8 quantization and block mean pooling
 hipError_t launch_kmean(const Plan& p, const uint16_t* k, hipStream_t s);
-// (v may be null: then no V^T images are written)
+// (v may be null: then no V^T images are written; with v and states_in_quant the key-block workgroups also write
+// the forward's linear-branch state table, state16 and state_exp)
 hipError_t launch_quant(const Plan& p, const uint16_t* q, const uint16_t* k, const uint16_t* v, hipStream_t s);
 // K2: pooled block scores and top-k selection
 hipError_t launch_scores(const Plan& p, hipStream_t s);
 hipError_t launch_topk(const Plan& p, hipStream_t s);
 // K4: linear branch (block states, sum over the unselected blocks, contraction with phi(Q) and W_p): the forward's
-// fp16 table and remaining state (state16, state_exp, plane16, aux16), or with lin_precise the backward's fp32 table and hi + lo
-// records (state, state_m)
+// remaining state (plane16, aux16) from the fp16 table launch_quant wrote, or with lin_precise the backward's fp32
+// table and remaining state (state, state_m)
 hipError_t launch_linear(const Plan& p, const uint16_t* k, const uint16_t* v, hipStream_t s);
 // K3: block-sparse INT8 attention, epilogue adds the linear branch and writes bf16
 hipError_t launch_attn(const Plan& p, const uint16_t* q, uint16_t* out, hipStream_t s);

@@ -11,10 +11,12 @@
 //
 // Kernels:
 //   k4_prep_wp   W_p^T with the MFMA key-slot order, bf16 (32 KB, once per call)
-//   k4_states    per key block: H_J^T and Z_J into a column-tiled table (MFMA, HBM-bound)
+//   k4_states    per key block: H_J^T and Z_J into a column-tiled fp32 table (MFMA, HBM-bound; the backward).
+//                The forward's fp16 table is written by the quantization kernel (k1_quant, k_quant.hip), whose
+//                key-block workgroups already hold each block's V rows.
 //   k4_mask      per query block: bitmask of the key blocks it did not select
 //   k4_gemm      H_m = sum of the states of the unselected blocks, as the dense product keep-mask x table
-//                (bf16 MFMA; about 90% of the mask is ones at 10% top-k)
+//                (bf16 MFMA; about 90% of the mask is ones at 10% top-k); k4_gemm16 the same over the fp16 table
 // (the attention kernel's epilogue then forms O_lin = (phi(Q) H_m) W_p / (phi(Q) . Z_m) per query block, MFMA)
 // fp32 values enter the bf16 MFMAs as hi + lo bf16 pairs, so every product keeps ~16 significant bits.
 #include "device_common.h"
@@ -127,121 +129,6 @@ __global__ __launch_bounds__(256) void k4_states(const uint16_t* __restrict__ k,
     const int x = kD * kD + t;
     table[(size_t)bh * n_xt * n_kb * xw + ((size_t)(x >> lxw) * n_kb + J) * xw + (x & (xw - 1))] = z;
   }
-}
-
-// ---------------------------------------------------------------------------------------------------------
-// k4_states16 (the forward): the same per-block product, stored in fp16 after scaling the whole block by a power
-// of two. With M the largest magnitude over H_J^T and Z_J and k the exponent with M < 2^k (frexp), every value x
-// is stored as fp16(x * 2^(15 - k)), all below 2^15 in magnitude, and e_J = k - 15, so x = entry * 2^e_J up to the
-// fp16 rounding (relative 2^-11); an all-zero block stores zeros with e_J = kExpZero. Table [BH][kStateX / 128]
-// [n_kb][128] fp16: the 128 columns of column group x of block J are 256 contiguous bytes.
-// ---------------------------------------------------------------------------------------------------------
-constexpr int kExpZero = -100000;
-
-__global__ __launch_bounds__(256) void k4_states16(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-                                                  uint16_t* __restrict__ table, int32_t* __restrict__ bexp, int N,
-                                                  int n_kb) {
-  __shared__ __attribute__((aligned(16))) unsigned char s_pkh[kD * 128];
-  __shared__ __attribute__((aligned(16))) unsigned char s_pkl[kD * 128];
-  __shared__ __attribute__((aligned(16))) unsigned char s_vt[kD * 128];
-  __shared__ float s_z[16][kD + 1];
-  __shared__ float s_m[4];
-  const int J = blockIdx.x, bh = blockIdx.y;
-  const int t = threadIdx.x, w = t >> 6, l = t & 63, g = l >> 5, lr = l & 31;
-  const int cg = t & 15, kg = t >> 4;  // loader: channels 8cg..+7, keys 4kg..+3
-  const size_t base = ((size_t)bh * N + (size_t)J * kBlkK) * kD;
-  const int nv = min(kBlkK, N - J * kBlkK);
-
-  // ---- load, phi, split, transpose into LDS (as k4_states)
-  uint32_t kw[4][4], vw[4][4];
-#pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    const int r = 4 * kg + b;
-    uint4 a = make_uint4(0, 0, 0, 0), c = make_uint4(0, 0, 0, 0);
-    if (r < nv) {
-      a = *(const uint4*)(k + base + (size_t)r * kD + cg * 8);
-      c = *(const uint4*)(v + base + (size_t)r * kD + cg * 8);
-    }
-    kw[b][0] = a.x; kw[b][1] = a.y; kw[b][2] = a.z; kw[b][3] = a.w;
-    vw[b][0] = c.x; vw[b][1] = c.y; vw[b][2] = c.z; vw[b][3] = c.w;
-  }
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int row = cg * 8 + e;
-    float pk[4];
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const float x = (e & 1) ? bf16_hi(kw[b][e >> 1]) : bf16_lo(kw[b][e >> 1]);
-      pk[b] = (4 * kg + b < nv) ? phi_f(x) : 0.f;
-    }
-    uint32_t h01, l01, h23, l23;
-    split2(pk[0], pk[1], h01, l01);
-    split2(pk[2], pk[3], h23, l23);
-    const int off = lds_off(row, 4 * kg);
-    *(uint2*)(s_pkh + off) = make_uint2(h01, h23);
-    *(uint2*)(s_pkl + off) = make_uint2(l01, l23);
-    const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-    *(uint2*)(s_vt + off) = make_uint2(__builtin_amdgcn_perm(vw[1][e >> 1], vw[0][e >> 1], sel),
-                                       __builtin_amdgcn_perm(vw[3][e >> 1], vw[2][e >> 1], sel));
-    s_z[kg][row] = (pk[0] + pk[1]) + (pk[2] + pk[3]);
-  }
-  __syncthreads();
-
-  // ---- H^T = V^T phi(K): m = e (4 tiles), n = c (tile w), k = key (4 steps of 16)
-  v16f acc[4];
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt) acc[mt] = (v16f){};
-  const int crow = 32 * w + lr;
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    const int key = 16 * s + 8 * g;
-    const v8bf bh_ = *(const v8bf*)(s_pkh + lds_off(crow, key));
-    const v8bf bl_ = *(const v8bf*)(s_pkl + lds_off(crow, key));
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      const v8bf a = *(const v8bf*)(s_vt + lds_off(32 * mt + lr, key));
-      acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bh_, acc[mt], 0, 0, 0);
-      acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bl_, acc[mt], 0, 0, 0);
-    }
-  }
-  float z = 0.f;
-  if (t < kD) {
-#pragma unroll
-    for (int j = 0; j < 16; ++j) z += s_z[j][t];
-  }
-
-  // ---- the block's largest magnitude and its exponent
-  float m = z;  // z >= 0 (0 on threads past the 128 columns)
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) m = fmaxf(m, fabsf(acc[mt][r]));
-  m = wave_max_f32(m);
-  if (l == 0) s_m[w] = m;
-  __syncthreads();
-  m = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
-  int kx = 0;
-  (void)frexpf(m, &kx);  // m < 2^kx
-  const int sh = 15 - kx;
-  if (t == 0) bexp[(size_t)bh * n_kb + J] = m > 0.f ? kx - 15 : kExpZero;
-
-  // ---- store: neighbouring columns c, c + 1 of one row go out as one 4-byte word. Lanes c and c ^ 1 trade one
-  // value of each register pair (r, r + 1) (rows e, e + 1): the even lane writes row e, the odd lane row e + 1.
-  const size_t gstride = (size_t)n_kb * 128;  // halves between column groups
-  uint16_t* tb = table + (size_t)bh * (kStateX / 128) * gstride + (size_t)J * 128;
-  const bool odd = crow & 1;
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-      const float a0 = acc[mt][r], a1 = acc[mt][r + 1];
-      const float send = odd ? a0 : a1;
-      const float got = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(send), 0xB1, 0xF, 0xF, false));
-      const float x0 = odd ? got : a0, x1 = odd ? a1 : got;
-      const int e = 32 * mt + 8 * (r >> 2) + 4 * g + (r & 3) + (odd ? 1 : 0);
-      *(uint32_t*)(tb + (size_t)e * gstride + (crow & ~1)) = pack_f16x2(ldexpf(x0, sh), ldexpf(x1, sh));
-    }
-  if (t < kD) tb[(size_t)kD * gstride + t] = (uint16_t)(pack_f16x2(ldexpf(z, sh), 0.f) & 0xffffu);
 }
 
 // ---------------------------------------------------------------------------------------------------------
@@ -520,10 +407,11 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k4_gemm(const float* __restri
 }
 
 // ---------------------------------------------------------------------------------------------------------
-// k4_gemm16 (the forward): the same keep-mask x table product over the fp16 table of k4_states16. Each block J
-// carries its own power of two 2^e_J, so the mask operand is keep[I][J] * 2^(e_J - E), E = max_J e_J over the head
-// (exact in fp16 down to 2^-24; a block more than 24 binades below the head's largest is dropped), and the sums are
-// the remaining state times 2^-E, H_m and Z_m alike (the linear branch's quotient does not see the common factor).
+// k4_gemm16 (the forward): the same keep-mask x table product over the fp16 table (block_state16, k_quant.hip).
+// Each block J carries its own power of two 2^e_J, so the mask operand is keep[I][J] * 2^(e_J - E), E = max_J e_J
+// over the head (exact in fp16 down to 2^-24; a block more than 24 binades below the head's largest is dropped), and
+// the sums are the remaining state times 2^-E, H_m and Z_m alike (the linear branch's quotient does not see the
+// common factor).
 // grid (kStateX / 128 column groups, ceil(n_qb / 640) query-block chunks, BH), 512 threads (8 waves).
 // Step = 32 key blocks (two k-steps of 16) = one mask word per query block. Table slices (32 rows of 256 B) and
 // the chunk's mask words are loaded into registers four steps ahead and written to a three-slot LDS ring (16-byte
@@ -752,11 +640,10 @@ hipError_t launch_linear(const Plan& p, const uint16_t* k, const uint16_t* v, hi
   hipLaunchKernelGGL(k4_prep_wp, dim3(kD * kD / 256), dim3(256), 0, s, (const uint16_t*)p.w_proj, p.wpt);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (p.lin_precise)
+  if (p.lin_precise) {  // the forward's fp16 table was written by the quantization kernel
     hipLaunchKernelGGL(k4_states, dim3(p.n_kb, p.BH), dim3(256), 0, s, k, v, p.state, p.N, p.n_kb, 7, kStateX / 128);
-  else
-    hipLaunchKernelGGL(k4_states16, dim3(p.n_kb, p.BH), dim3(256), 0, s, k, v, p.state16, p.state_exp, p.N, p.n_kb);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   const int rows = p.BH * p.n_qb, n_kbw = (p.n_kb + 31) / 32, qpad = mask_row_pad(p.n_qb);
   hipLaunchKernelGGL(k4_mask, dim3(rows), dim3(64), 0, s, p.block_idx, p.keep_mask, p.n_qb, p.n_kb, p.topk, n_kbw,
                      qpad);

@@ -13,6 +13,7 @@
 // HBM bound: K is read twice (sum, then quantize), Q once; int8 codes are written once.
 #include "device_common.h"
 #include "internal.h"
+#include "lin_common.h"
 
 namespace sagesla {
 
@@ -272,17 +273,110 @@ __device__ __forceinline__ void write_v_image(const uint32_t (&wv)[4][4], unsign
   }
 }
 
+// The forward's linear-branch state of key block J ("Turbo Diffusion", lanhy.cn, §三(二) SLA item 2):
+// H_J^T = (phi(K_J)^T V_J)^T (D×D) and Z_J = sum over the block's keys of phi(K_J) (D), phi = elu + 1 on the raw
+// bf16 k, formed by the workgroup that has just quantized block J and still holds its V rows in registers (wv).
+// K is read again from global memory (the quantizer read it moments before, so it comes from L2); V^T and K^T go
+// to LDS in the V^T-image layout, which reuses the quantizer's reduction buffer (s_vt) and a buffer of its own
+// (s_kt). One MFMA operand is a V^T image row (channel e, 8 key slots), the other phi of a K^T image row (channel c,
+// the same key slots) split into bf16 hi + lo, so every product keeps ~16 significant bits; keys past a ragged
+// block's end are zero in both images and phi of them is taken as 0 for Z_J. Wave w owns channels c = 32 w ..
+// +31, so acc[mt] holds rows e = 32 mt .. +31.
+// Stored in fp16 with one power of two per block: with M the largest magnitude over H_J^T and Z_J and k its
+// frexp exponent (M < 2^k), x is stored as fp16(x * 2^(15 - k)) and e_J = k - 15 (kExpZero for an all-zero
+// block). Table [BH][kStateX / 128][n_kb][128] fp16: column group x < 128 of block J is row x of H_J^T, group 128
+// is Z_J, each 256 contiguous bytes.
+__device__ __forceinline__ void block_state16(const uint32_t (&wv)[4][4], const uint16_t* __restrict__ kblk, int nv,
+                                              unsigned char* __restrict__ s_vt, unsigned char* __restrict__ s_kt,
+                                              float* __restrict__ s_m, uint16_t* __restrict__ table,
+                                              int32_t* __restrict__ bexp, int bh, int J, int n_kb) {
+  const int t = threadIdx.x, w = t >> 6, l = t & 63, g = l >> 5, lr = l & 31;
+  uint32_t wk[4][4];
+  load_v_rows(kblk, nv, wk);
+  __syncthreads();  // the quantizer's last reads of the reused LDS are done
+  write_v_image(wv, s_vt);
+  write_v_image(wk, s_kt);
+  __syncthreads();
+
+  const int crow = 32 * w + lr;
+  v16f acc[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) acc[mt] = (v16f){};
+  float z = 0.f;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int ch = 2 * s + g;  // image chunk: key slots 16 s + 8 g .. +7
+    const uint4 kr = *(const uint4*)(s_kt + crow * 128 + ((ch ^ swz32(crow)) << 4));
+    const uint32_t kw[4] = {kr.x, kr.y, kr.z, kr.w};
+    float pk[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float x = (j & 1) ? bf16_hi(kw[j >> 1]) : bf16_lo(kw[j >> 1]);
+      pk[j] = 16 * s + key_pos16(8 * g + j) < nv ? phi_f(x) : 0.f;  // the slot's key index
+      z += pk[j];
+    }
+    uint32_t hi[4], lo[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) split2(pk[2 * i], pk[2 * i + 1], hi[i], lo[i]);
+    const v8bf bh_ = __builtin_bit_cast(v8bf, make_uint4(hi[0], hi[1], hi[2], hi[3]));
+    const v8bf bl_ = __builtin_bit_cast(v8bf, make_uint4(lo[0], lo[1], lo[2], lo[3]));
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const int er = 32 * mt + lr;
+      const v8bf a = *(const v8bf*)(s_vt + er * 128 + ((ch ^ swz32(er)) << 4));
+      acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bh_, acc[mt], 0, 0, 0);
+      acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bl_, acc[mt], 0, 0, 0);
+    }
+  }
+  z += swap_halves_f32(z);  // both halves of the wave now hold Z_J[crow]
+
+  // the block's largest magnitude and its exponent
+  float m = z;  // z >= 0
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) m = fmaxf(m, fabsf(acc[mt][r]));
+  m = wave_max_f32(m);
+  if (l == 0) s_m[w] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
+  int kx = 0;
+  (void)frexpf(m, &kx);  // m < 2^kx
+  const int sh = 15 - kx;
+  if (t == 0) bexp[(size_t)bh * n_kb + J] = m > 0.f ? kx - 15 : kExpZero;
+
+  // store: neighbouring columns c, c + 1 of one row go out as one 4-byte word. Lanes c and c ^ 1 trade one value
+  // of each register pair (r, r + 1) (rows e, e + 1): the even lane writes row e, the odd lane row e + 1.
+  const size_t gstride = (size_t)n_kb * 128;  // halves between column groups
+  uint16_t* tb = table + (size_t)bh * (kStateX / 128) * gstride + (size_t)J * 128;
+  const bool odd = crow & 1;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      const float a0 = acc[mt][r], a1 = acc[mt][r + 1];
+      const float send = odd ? a0 : a1;
+      const float got = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(send), 0xB1, 0xF, 0xF, false));
+      const float x0 = odd ? got : a0, x1 = odd ? a1 : got;
+      const int e = 32 * mt + 8 * (r >> 2) + 4 * g + (r & 3) + (odd ? 1 : 0);
+      *(uint32_t*)(tb + (size_t)e * gstride + (crow & ~1)) = pack_f16x2(ldexpf(x0, sh), ldexpf(x1, sh));
+    }
+  if (g == 0) tb[(size_t)kD * gstride + crow] = (uint16_t)(pack_f16x2(ldexpf(z, sh), 0.f) & 0xffffu);
+}
+
 // grid (n_qb + n_kb, BH): x < n_qb quantizes query block x, otherwise key block x - n_qb (and, when v is given,
-// writes that key block's V^T image).
+// writes that key block's V^T image and, when st16 is given too, its linear-branch state: block_state16).
 template <int BLKQ, bool G32>
-__global__ __launch_bounds__(256) void k1_quant(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-                                               const float* __restrict__ mu, int8_t* __restrict__ q8,
-                                               int8_t* __restrict__ k8, float* __restrict__ qs,
-                                               float* __restrict__ ks, double* __restrict__ qp,
-                                               double* __restrict__ kp, const uint16_t* __restrict__ v,
-                                               unsigned char* __restrict__ v_img, int N, int n_qb, int n_kb) {
+// four workgroups per CU (at most 128 registers): the state's MFMA accumulators then share the quantizer's VGPRs
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k1_quant(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const float* __restrict__ mu,
+    int8_t* __restrict__ q8, int8_t* __restrict__ k8, float* __restrict__ qs, float* __restrict__ ks,
+    double* __restrict__ qp, double* __restrict__ kp, const uint16_t* __restrict__ v,
+    unsigned char* __restrict__ v_img, uint16_t* __restrict__ st16, int32_t* __restrict__ st_exp, int N, int n_qb,
+    int n_kb) {
   __shared__ float s_amax[4][4];
-  __shared__ double s_red[16][kD + 1];
+  __shared__ __attribute__((aligned(16))) double s_red[16][kD + 1];  // 16512 B: also the state's V^T image
+  __shared__ __attribute__((aligned(16))) unsigned char s_kt[kD * 128];
   const int bh = blockIdx.y;
   const int x = blockIdx.x;
   const size_t base = (size_t)bh * N * kD;
@@ -306,6 +400,9 @@ __global__ __launch_bounds__(256) void k1_quant(const uint16_t* __restrict__ q, 
       quant_block<kBlkK, false, G32>(k + base + (size_t)r0 * kD, nv, nullptr, k8 + base + (size_t)r0 * kD, so,
                                      kp + ((size_t)bh * n_kb + j) * kD, s_amax, s_red);
     if (v) write_v_image(wv, v_img + ((size_t)bh * n_kb + j) * 16384);
+    if (v && st16)
+      block_state16(wv, k + base + (size_t)r0 * kD, nv, (unsigned char*)&s_red[0][0], s_kt, &s_amax[0][0], st16,
+                    st_exp, bh, j, n_kb);
   }
 }
 
@@ -340,9 +437,10 @@ hipError_t launch_kmean(const Plan& p, const uint16_t* k, hipStream_t s) {
 hipError_t launch_quant(const Plan& p, const uint16_t* q, const uint16_t* k, const uint16_t* v, hipStream_t s) {
   const dim3 grid(p.n_qb + p.n_kb, p.BH);
   const float* mu = p.smooth ? p.k_mean : nullptr;
+  uint16_t* st16 = p.states_in_quant ? p.state16 : nullptr;  // the forward's linear-branch state table
 #define SAGESLA_QUANT(BQ, G)                                                                                   \
   hipLaunchKernelGGL((k1_quant<BQ, G>), grid, dim3(256), 0, s, q, k, mu, p.q_i8, p.k_i8, p.q_scale, p.k_scale,     \
-                     p.q_pool, p.k_pool, v, p.v_img, p.N, p.n_qb, p.n_kb)
+                     p.q_pool, p.k_pool, v, p.v_img, st16, p.state_exp, p.N, p.n_qb, p.n_kb)
   if (p.blk_q == 128) {
     if (p.group32) SAGESLA_QUANT(128, true); else SAGESLA_QUANT(128, false);
   } else {

@@ -21,6 +21,10 @@ __device__ __forceinline__ float phi_f(float x) {
   return x > 0.f ? x + 1.f : __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
 }
 
+// The forward's per-block state table is fp16 with one power of two per key block: entries x * 2^(15 - k) for the
+// block's largest magnitude M < 2^k, and the block exponent e_J = k - 15; an all-zero block has e_J = kExpZero.
+constexpr int kExpZero = -100000;
+
 // two fp32 values -> bf16 pairs hi = bf16(x) and lo = bf16(x - hi), packed as (x0, x1)
 __device__ __forceinline__ void split2(float x0, float x1, uint32_t& hi, uint32_t& lo) {
   hi = pack_bf16x2(x0, x1);

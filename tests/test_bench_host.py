@@ -42,14 +42,20 @@ def test_mfma_summary_parses_and_is_source_gated(tmp_path):
 
 
 def test_stage_bytes_of_the_headline_layer():
-    # quantize stage: K read by the column sums, Q K V read and codes + V^T images written by the quantizer
+    # quantize stage: K read by the column sums, Q K V read and codes + V^T images written by the quantizer, which
+    # with the linear branch on also writes the fp16 state table (129 rows of 128 fp16 per 64-key block)
     import synth
     wl = synth.WORKLOADS[3]
     sb = bench.stage_bytes(wl)
     elems = wl.B * wl.H * wl.N * wl.D
-    assert abs(sum(sb["quantize"].values()) - 12 * elems) < 0.02 * 12 * elems
-    assert set(sb["linear"]) == {"k4_states16", "k4_mask", "k4_gemm16"}
-    assert not bench.stage_bytes(synth.WORKLOADS[1])["linear"]  # the dense layer runs no linear branch
+    table = wl.B * wl.H * wl.n_kb * 129 * 128 * 2
+    assert abs(sum(sb["quantize"].values()) - (12 * elems + table)) < 0.02 * 12 * elems
+    assert set(sb["linear"]) == {"k4_mask", "k4_gemm16"}
+    dense = synth.WORKLOADS[1]
+    sd = bench.stage_bytes(dense)
+    assert not sd["linear"]  # the dense layer runs no linear branch, and its quantizer writes no table
+    de = dense.B * dense.H * dense.N * dense.D
+    assert abs(sum(sd["quantize"].values()) - 12 * de) < 0.02 * 12 * de
 
 
 

@@ -170,11 +170,13 @@ __global__ __launch_bounds__(128) void k1_colsum_final(const double* __restrict_
 // where it is needed (the same single IEEE subtraction each time).
 // With G32 the block's rows get one scale per 32 rows (group g = rows 32 g .. +31 = the rows of steps i = 2g, 2g+1
 // of every thread); scale_out then receives one value per group that holds a valid row.
+// With kt_img (key blocks of 64 rows only) the block's raw rows also go to LDS as a K^T image in the V^T-image
+// layout (write_v_image below: channel rows of 64 key slots, zeros past `rows`), for the linear-branch state.
 template <int MAXROWS, bool SMOOTH, bool G32>
 __device__ __forceinline__ void quant_block(const uint16_t* __restrict__ src, int rows, const float* __restrict__ mu,
                                             int8_t* __restrict__ dst, float* __restrict__ scale_out,
                                             double* __restrict__ pool_out, float (*s_amax)[4],
-                                            double (*s_red)[kD + 1]) {
+                                            double (*s_red)[kD + 1], unsigned char* __restrict__ kt_img = nullptr) {
   constexpr int IT = MAXROWS / 16;
   constexpr int NG = G32 ? MAXROWS / 32 : 1;  // scales in this block
   const int t = threadIdx.x, cg = t & 15, rl = t >> 4;
@@ -186,6 +188,21 @@ __device__ __forceinline__ void quant_block(const uint16_t* __restrict__ src, in
   for (int i = 0; i < IT; ++i) {
     const int r = rl + 16 * i;
     raw[i] = (r < rows) ? *(const uint4*)(src + (size_t)r * kD + cg * 8) : make_uint4(0, 0, 0, 0);
+  }
+  if constexpr (MAXROWS == kBlkK) {
+    if (kt_img) {  // row rl + 16 i is key slot 16 i + key_pos16(rl) of channel rows 8 cg .. +7
+#pragma unroll
+      for (int i = 0; i < IT; ++i) {
+        const int pos = 16 * i + key_pos16(rl);
+        const uint32_t wd[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int row = cg * 8 + e;
+          *(uint16_t*)(kt_img + row * 128 + (((pos >> 3) ^ swz32(row)) << 4) + ((pos & 7) << 1)) =
+              (uint16_t)((e & 1) ? wd[e >> 1] >> 16 : wd[e >> 1] & 0xffffu);
+        }
+      }
+    }
   }
   auto value = [&](int i, int e) -> float {  // element e of row rl + 16 i, smoothed when SMOOTH (0 past rows)
     const uint32_t wd = e < 2 ? raw[i].x : e < 4 ? raw[i].y : e < 6 ? raw[i].z : raw[i].w;
@@ -276,9 +293,9 @@ __device__ __forceinline__ void write_v_image(const uint32_t (&wv)[4][4], unsign
 // The forward's linear-branch state of key block J ("Turbo Diffusion", lanhy.cn, §三(二) SLA item 2):
 // H_J^T = (phi(K_J)^T V_J)^T (D×D) and Z_J = sum over the block's keys of phi(K_J) (D), phi = elu + 1 on the raw
 // bf16 k, formed by the workgroup that has just quantized block J and still holds its V rows in registers (wv).
-// K is read again from global memory (the quantizer read it moments before, so it comes from L2); V^T and K^T go
-// to LDS in the V^T-image layout, which reuses the quantizer's reduction buffer (s_vt) and a buffer of its own
-// (s_kt). One MFMA operand is a V^T image row (channel e, 8 key slots), the other phi of a K^T image row (channel c,
+// K^T and V^T are in LDS in the V^T-image layout: the quantizer wrote K^T from its registers (s_kt), V^T goes to
+// the quantizer's reduction buffer once that is free (s_vt). One MFMA operand is a V^T image row (channel e, 8
+// key slots), the other phi of a K^T image row (channel c,
 // the same key slots) split into bf16 hi + lo, so every product keeps ~16 significant bits; keys past a ragged
 // block's end are zero in both images and phi of them is taken as 0 for Z_J. Wave w owns channels c = 32 w ..
 // +31, so acc[mt] holds rows e = 32 mt .. +31.
@@ -286,16 +303,13 @@ __device__ __forceinline__ void write_v_image(const uint32_t (&wv)[4][4], unsign
 // frexp exponent (M < 2^k), x is stored as fp16(x * 2^(15 - k)) and e_J = k - 15 (kExpZero for an all-zero
 // block). Table [BH][kStateX / 128][n_kb][128] fp16: column group x < 128 of block J is row x of H_J^T, group 128
 // is Z_J, each 256 contiguous bytes.
-__device__ __forceinline__ void block_state16(const uint32_t (&wv)[4][4], const uint16_t* __restrict__ kblk, int nv,
-                                              unsigned char* __restrict__ s_vt, unsigned char* __restrict__ s_kt,
+__device__ __forceinline__ void block_state16(const uint32_t (&wv)[4][4], int nv, unsigned char* __restrict__ s_vt,
+                                              const unsigned char* __restrict__ s_kt,
                                               float* __restrict__ s_m, uint16_t* __restrict__ table,
                                               int32_t* __restrict__ bexp, int bh, int J, int n_kb) {
   const int t = threadIdx.x, w = t >> 6, l = t & 63, g = l >> 5, lr = l & 31;
-  uint32_t wk[4][4];
-  load_v_rows(kblk, nv, wk);
-  __syncthreads();  // the quantizer's last reads of the reused LDS are done
+  __syncthreads();  // the quantizer's last reads of the reused LDS are done (and its K^T image is written)
   write_v_image(wv, s_vt);
-  write_v_image(wk, s_kt);
   __syncthreads();
 
   const int crow = 32 * w + lr;
@@ -393,16 +407,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
     float* so = G32 ? ks + (size_t)bh * n_g + j * (kBlkK / 32) : ks + (size_t)bh * n_kb + j;
     uint32_t wv[4][4];
     if (v) load_v_rows(v + base + (size_t)r0 * kD, nv, wv);  // in flight while K is quantized
+    unsigned char* kt = (v && st16) ? s_kt : nullptr;  // the state's K^T image, written by the quantizer
     if (mu)
       quant_block<kBlkK, true, G32>(k + base + (size_t)r0 * kD, nv, mu + bh * kD, k8 + base + (size_t)r0 * kD, so,
-                                    kp + ((size_t)bh * n_kb + j) * kD, s_amax, s_red);
+                                    kp + ((size_t)bh * n_kb + j) * kD, s_amax, s_red, kt);
     else
       quant_block<kBlkK, false, G32>(k + base + (size_t)r0 * kD, nv, nullptr, k8 + base + (size_t)r0 * kD, so,
-                                     kp + ((size_t)bh * n_kb + j) * kD, s_amax, s_red);
+                                     kp + ((size_t)bh * n_kb + j) * kD, s_amax, s_red, kt);
     if (v) write_v_image(wv, v_img + ((size_t)bh * n_kb + j) * 16384);
-    if (v && st16)
-      block_state16(wv, k + base + (size_t)r0 * kD, nv, (unsigned char*)&s_red[0][0], s_kt, &s_amax[0][0], st16,
-                    st_exp, bh, j, n_kb);
+    if (kt) block_state16(wv, nv, (unsigned char*)&s_red[0][0], s_kt, &s_amax[0][0], st16, st_exp, bh, j, n_kb);
   }
 }
 

@@ -17,7 +17,8 @@ namespace sagesla {
 // scores[bh][I][J] = sum_c q_pool[bh][I][c] * k_pool[bh][J][c]   (fp64, fixed order over c)
 // grid (ceil(n_kb/128), ceil(n_qb/128), BH), 256 threads; thread (tx, ty) = (t%16, t/16) owns rows
 // ty + 16 i and columns tx + 16 j (i, j < 8) of the 128×128 tile. Channels are staged 16 at a time in LDS,
-// stored transposed so a wave reads 16 consecutive doubles of the key tile and broadcasts the query tile.
+// stored transposed so a wave reads 16 consecutive doubles of the key tile and broadcasts the query tile; the
+// next 16 are loaded into registers during the products of the current ones.
 // ---------------------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k2_scores(const double* __restrict__ qp, const double* __restrict__ kp,
                                                 double* __restrict__ sc, int n_qb, int n_kb) {
@@ -35,9 +36,10 @@ __global__ __launch_bounds__(256) void k2_scores(const double* __restrict__ qp, 
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[i][j] = 0.0;
   const int lr = t >> 1, lc = (t & 1) * 8;  // loader: tile row, first channel of its 8
-  for (int c0 = 0; c0 < kD; c0 += KC) {
-    double av[8], bv[8];
-    const int I = I0 + lr, J = J0 + lr;
+  const int I = I0 + lr, J = J0 + lr;
+  // the next channel chunk is loaded into registers while this one is multiplied
+  double av[8], bv[8];
+  auto load = [&](int c0) {
 #pragma unroll
     for (int u = 0; u < 8; u += 2) {
       double2 a = make_double2(0.0, 0.0), b = make_double2(0.0, 0.0);
@@ -46,6 +48,9 @@ __global__ __launch_bounds__(256) void k2_scores(const double* __restrict__ qp, 
       av[u] = a.x; av[u + 1] = a.y;
       bv[u] = b.x; bv[u + 1] = b.y;
     }
+  };
+  load(0);
+  for (int c0 = 0; c0 < kD; c0 += KC) {
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
@@ -53,6 +58,7 @@ __global__ __launch_bounds__(256) void k2_scores(const double* __restrict__ qp, 
       Bs[lc + u][lr] = bv[u];
     }
     __syncthreads();
+    if (c0 + KC < kD) load(c0 + KC);
 #pragma unroll 4
     for (int c = 0; c < KC; ++c) {
       double a[8], b[8];

@@ -105,6 +105,7 @@ void make_plan(const sagesla_params* p, unsigned char* ws, Plan* pl, bool backwa
     pl->k_i8 = (int8_t*)take(BH * N * D);
     pl->q_scale = (float*)take(BH * (pl->group32 ? (size_t)pl->n_g : nqb) * sizeof(float));
     pl->k_scale = (float*)take(BH * (pl->group32 ? (size_t)pl->n_g : nkb) * sizeof(float));
+    pl->k_norm2 = (int32_t*)take(BH * (pl->group32 ? (size_t)pl->n_g : nkb) * sizeof(int32_t));
     pl->q_pool = (double*)take(BH * nqb * D * sizeof(double));
     pl->k_pool = (double*)take(BH * nkb * D * sizeof(double));
     pl->scores = (double*)take(BH * nqb * nkb * sizeof(double));

@@ -43,6 +43,7 @@ struct Plan {
   int8_t* k_i8;
   float* q_scale;       // [BH][n_qb] (or [BH][n_g] with group32)
   float* k_scale;       // [BH][n_kb] (or [BH][n_g] with group32)
+  int32_t* k_norm2;     // like k_scale: the largest squared norm of a K code row under that scale
   double* q_pool;       // [BH][n_qb][D]
   double* k_pool;       // [BH][n_kb][D]
   double* scores;       // [BH][n_qb][n_kb]

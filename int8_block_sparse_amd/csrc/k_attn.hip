@@ -19,6 +19,13 @@
 // core and the vector ALU of a wave overlap.
 // Softmax rescaling is lazy: the running max moves only when a block's max exceeds it by more than kLazy (log2
 // units), which keeps every exp2 argument <= kLazy and skips the O rescale for almost every block.
+// Bounded shift: the exponent of a softmax may subtract any per-row constant instead of the row max. Each wave
+// bounds its rows' scores from above by Cauchy-Schwarz, t_ij <= B_i = |codeQ_i| * scale_q * sm_scale * log2(e) *
+// max over the listed J of scale_k(J) * (largest |codeK_j| under that scale, from the quantizer), and when
+// B_i - M_i <= kBoundGap for every row, with M_i the row's score against the first key of its first listed block
+// (a lower bound of its max), it subtracts m_i = B_i - kBoundTop throughout: every p <= 2^kBoundTop, the row's
+// largest p >= 2^(kBoundTop - kBoundGap), so no per-block max, no rescale and no overflow or underflow of the sums.
+// Otherwise the wave keeps the lazy running max.
 #include <type_traits>
 
 #include "device_common.h"
@@ -134,6 +141,11 @@ constexpr int kListCap = 1020;  // selection-list entries the attention kernel k
 // below 2^45, far inside fp32; on smooth video-like inputs a running max of 32 rows moves for under 1% of
 // blocks (about 6% with a slack of 8).
 constexpr float kLazy = 24.f;
+// Bounded shift (see the header): p <= 2^kBoundTop keeps the row sums below 2^(kBoundTop + 17) for any list of
+// up to 2^17 keys and O far inside fp32; the largest p of a row is >= 2^(kBoundTop - kBoundGap) = 2^-96, a normal
+// fp32 and bf16 value, so the terms that do underflow are below 2^-30 of it.
+constexpr float kBoundTop = 64.f;
+constexpr float kBoundGap = 160.f;
 
 __device__ __forceinline__ void attn_scores(const unsigned char* __restrict__ sk, const v4i* bq, const int (&koff)[2][4],
                                             v16i (&sacc)[2]) {
@@ -181,7 +193,7 @@ __device__ __forceinline__ void attn_exp_pair(const v16i& s, int r, float c26, f
 // compiler from collapsing the read-ahead distance.
 // G (one scale per 32 keys): score tile 0 (keys 0-31) takes the scale product c and tile 1 (keys 32-63) c1;
 // otherwise both take c.
-template <bool RAGGED, bool HAS_NEXT, bool FAST, bool G = false>
+template <bool RAGGED, bool HAS_NEXT, bool FAST, bool G = false, bool BOUNDED = false>
 __device__ __forceinline__ void attn_iter(const unsigned char* __restrict__ sk_next,
                                           const unsigned char* __restrict__ sv, const v4i* bq,
                                           const int (&koff)[2][4], const int (&voff)[4][4], float c, float c1, int nv,
@@ -236,6 +248,7 @@ __device__ __forceinline__ void attn_iter(const unsigned char* __restrict__ sk_n
   // region 1: first operand reads; with a next block, its first four score MFMAs overlap the block max
 #pragma unroll
   for (int i = 0; i < AHEAD; ++i) read(i);
+  // (BOUNDED: m_run is the row's fixed shift; only a ragged block's keys past N are masked)
   int mx = INT_MIN, mx1 = INT_MIN;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
@@ -244,11 +257,14 @@ __device__ __forceinline__ void attn_iter(const unsigned char* __restrict__ sk_n
       read(q + AHEAD);
       mfma(q);
     }
-    if (G && q >= 2)
-      mx1 = max(mx1, part_max(q));
-    else
-      mx = max(mx, part_max(q));
+    if (!BOUNDED || RAGGED) {
+      if (G && q >= 2)
+        mx1 = max(mx1, part_max(q));
+      else
+        mx = max(mx, part_max(q));
+    }
   }
+  if constexpr (!BOUNDED) {
   mx = max_halves_i32(mx);
   float mblk = (float)(mx - kMagic) * c;
   if constexpr (G) {
@@ -268,6 +284,7 @@ __device__ __forceinline__ void attn_iter(const unsigned char* __restrict__ sk_n
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[ct][r] *= alpha;
     m_run = m_new;
+  }
   }
 
   // region 2: slot k runs MFMA k, the read for MFMA k + AHEAD and exp pair k - NK + 4
@@ -444,7 +461,8 @@ __device__ __forceinline__ void lin_epilogue(const uint16_t* __restrict__ q, con
 template <int NW, bool G>
 __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k3_attn(
     const int8_t* __restrict__ q8, const int8_t* __restrict__ k8, const unsigned char* __restrict__ vt,
-    const float* __restrict__ qs, const float* __restrict__ ks, const int32_t* __restrict__ idx,
+    const float* __restrict__ qs, const float* __restrict__ ks, const int32_t* __restrict__ kn2,
+    const int32_t* __restrict__ idx,
     const uint16_t* __restrict__ qraw, const unsigned char* __restrict__ plane16,
     const unsigned char* __restrict__ aux16, const uint16_t* __restrict__ wpt,
     float* __restrict__ o_lin, uint16_t* __restrict__ out, int N, int n_qb, int n_kb, int topk, float c0,
@@ -511,6 +529,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k3_attn(
   const __amdgpu_buffer_rsrc_t rk = slab_rsrc(k8 + (size_t)bh * N * kD, (uint32_t)N * kD);
   const __amdgpu_buffer_rsrc_t rv = slab_rsrc(vt + (size_t)bh * n_kb * 16384, (uint32_t)n_kb * 16384u);
   c_f32* ksrow = (c_f32*)(ks + (size_t)bh * (G ? n_g : n_kb));
+  c_i32* knrow = (c_i32*)(kn2 + (size_t)bh * (G ? n_g : n_kb));
   const int last_kb = n_kb - 1;
   const int nv_last = N - last_kb * kBlkK;  // valid keys of the last key block (64 unless ragged)
   const StageOffsets<NW> so_full = stage_offsets<NW>(kBlkK);
@@ -522,12 +541,27 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k3_attn(
   float m_run = -INFINITY, l_run = 0.f;
 
   auto blk = [&](int j) { return min(max(irow[j], 0), last_kb); };
+  // the codes of the first key of the first selected block (the bounded shift's lower bound), in the lane's half
+  // of the channels as bq holds them; loaded here so that their latency overlaps the list pass below
+  const int J0 = topk > 0 ? blk(0) : 0;
+  v4i kk0[4];
+  {
+    const int8_t* k0row = k8 + ((size_t)bh * N + (size_t)J0 * kBlkK) * kD;
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) kk0[s4] = *(const v4i*)(k0row + 32 * s4 + 16 * g);
+  }
   // key scales of block J for score tiles 0 and 1 (G: its two 32-key groups; the second group of a last block
   // that ends inside its first half does not exist and is clamped, its keys are masked anyway)
   auto kscale = [&](int J) -> float2 {
     if (G) return make_float2(ksrow[2 * J], ksrow[min(2 * J + 1, n_g - 1)]);
     const float k1 = ksrow[J];
     return make_float2(k1, k1);
+  };
+  // the largest code-row norm under each of those scales
+  auto knorm = [&](int J) -> float2 {
+    if (G) return make_float2(sqrtf((float)knrow[2 * J]), sqrtf((float)knrow[min(2 * J + 1, n_g - 1)]));
+    const float n1 = sqrtf((float)knrow[J]);
+    return make_float2(n1, n1);
   };
   auto stage = [&](int j, int buf) {
     const int J = blk(j);
@@ -547,12 +581,14 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k3_attn(
     const bool has_ragged = nv_last != kBlkK;
     // (G: the list keeps the two raw key scales per entry, in half the entries; each wave multiplies by its cq)
     const bool listed = topk <= (G ? kListCap / 2 : kListCap);
-    float kmax = 0.f;
+    float kmax = 0.f, kbn = 0.f;  // (kbn: the largest scale x code-row norm of the listed blocks)
     bool early_ragged = false;
     for (int j = l; j < topk; j += 64) {
       const int J = blk(j);
       const float2 kv = kscale(J);
       kmax = fmaxf(kmax, fmaxf(kv.x, kv.y));
+      const float2 kn = knorm(J);
+      kbn = fmaxf(kbn, fmaxf(kv.x * kn.x, kv.y * kn.y));
       early_ragged |= has_ragged && j < topk - 1 && J == last_kb;
       if (listed && w == 0) {
         s_lj[j] = J;
@@ -564,6 +600,27 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k3_attn(
     }
     if (listed && w == 0 && l < 4) s_lj[topk + l] = blk(topk - 1);
     kmax = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(wave_max_f32(kmax))));
+    kbn = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(wave_max_f32(kbn))));
+    // the bound of the row's scores in exponent units (bounded shift): |codeQ_i| * cq * kbn (Cauchy-Schwarz),
+    // rounded up (the two lane halves hold 64 codes each of the row; the squared norm is exact)
+    int qn2 = 0;
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) qn2 = __builtin_amdgcn_sdot4(bq[s4][e], bq[s4][e], qn2, false);
+    qn2 += swap_halves_i32(qn2);
+    const float brow = sqrtf((float)qn2) * cq * kbn * (1.f + 0x1p-16f);
+    // a lower bound of the row's max: its score against the first key of its first selected block
+    int s0 = 0;
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s0 = __builtin_amdgcn_sdot4(bq[s4][e], kk0[s4][e], s0, false);
+    s0 += swap_halves_i32(s0);
+    const float mlow = (float)s0 * (cq * kscale(J0).x);
+    // per wave (the two paths meet the same barriers); lists of one block keep the running max
+    const bool bounded = topk > 1 && __ballot(!(brow - mlow <= kBoundGap)) == 0;  // a NaN fails the test too
+    if (bounded) m_run = brow - kBoundTop;
     const bool elsewhere = __ballot(early_ragged) != 0;
     const bool tail_ragged = has_ragged && blk(topk - 1) == last_kb;
     // one-instruction exponent argument when every block's scale product is below 2^-10 (see attn_exp_pair)
@@ -580,11 +637,12 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k3_attn(
     // With the list in LDS (L), iteration j takes J[j+3] and the scale product of block j from LDS reads issued
     // one iteration earlier, which the ring's barrier wait has already completed: the steady loop then has no
     // scalar-memory waits (those would also drain the LDS operand reads in flight).
-    auto ring = [&](auto fastc, auto listc, unsigned char* __restrict__ k0, unsigned char* __restrict__ k1,
-                    unsigned char* __restrict__ k2, unsigned char* __restrict__ v0, unsigned char* __restrict__ v1,
-                    unsigned char* __restrict__ v2) {
+    auto ring = [&](auto fastc, auto listc, auto boundc, unsigned char* __restrict__ k0,
+                    unsigned char* __restrict__ k1, unsigned char* __restrict__ k2, unsigned char* __restrict__ v0,
+                    unsigned char* __restrict__ v1, unsigned char* __restrict__ v2) {
       constexpr bool F = decltype(fastc)::value;
       constexpr bool L = decltype(listc)::value;
+      constexpr bool BD = decltype(boundc)::value;
       unsigned char* const ks[3] = {k0, k1, k2};
       unsigned char* const vs[3] = {v0, v1, v2};
       // K tiles use the full-block offsets even for a ragged last block: its rows past N lie beyond the
@@ -647,7 +705,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k3_attn(
           put_v(j + 2, vs[(P + 2) % 3]);
           cpair(blk(j), c, c1);
         }
-        attn_iter<false, true, F, G>(ks[(P + 1) % 3], vs[P], bq, koff, voff, c, c1, kBlkK, g, o, m_run, l_run,
+        attn_iter<false, true, F, G, BD>(ks[(P + 1) % 3], vs[P], bq, koff, voff, c, c1, kBlkK, g, o, m_run, l_run,
                                      scur, snext);
         scur[0] = snext[0];
         scur[1] = snext[1];
@@ -663,7 +721,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k3_attn(
         if (j + 2 < topk) put_v(j + 2, pick(P == 0 ? 2 : P - 1, v0, v1, v2));
         float c, c1;
         cpair(blk(j), c, c1);
-        attn_iter<false, true, F, G>(pick(P == 2 ? 0 : P + 1, k0, k1, k2), pick(P, v0, v1, v2), bq, koff, voff, c,
+        attn_iter<false, true, F, G, BD>(pick(P == 2 ? 0 : P + 1, k0, k1, k2), pick(P, v0, v1, v2), bq, koff, voff, c,
                                      c1, kBlkK, g, o, m_run, l_run, scur, snext);
         scur[0] = snext[0];
         scur[1] = snext[1];
@@ -682,9 +740,11 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k3_attn(
       float c, c1;
       cpair(tail_ragged ? last_kb : blk(j), c, c1);
       if (tail_ragged)
-        attn_iter<true, false, F, G>(nullptr, vl, bq, koff, voff, c, c1, nv_last, g, o, m_run, l_run, scur, snext);
+        attn_iter<true, false, F, G, BD>(nullptr, vl, bq, koff, voff, c, c1, nv_last, g, o, m_run, l_run, scur,
+                                         snext);
       else
-        attn_iter<false, false, F, G>(nullptr, vl, bq, koff, voff, c, c1, kBlkK, g, o, m_run, l_run, scur, snext);
+        attn_iter<false, false, F, G, BD>(nullptr, vl, bq, koff, voff, c, c1, kBlkK, g, o, m_run, l_run, scur,
+                                          snext);
     };
     if (elsewhere) {
       stage(0, 0);
@@ -699,16 +759,24 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k3_attn(
                                          min(kBlkK, N - J * kBlkK), g, o, m_run, l_run, scur, snext);
         sync();
       }
-    } else if (fast) {
-      if (listed)
-        ring(std::true_type{}, std::true_type{}, s_k0, s_k1, s_k2, s_v0, s_v1, s_v2);
-      else
-        ring(std::true_type{}, std::false_type{}, s_k0, s_k1, s_k2, s_v0, s_v1, s_v2);
     } else {
-      if (listed)
-        ring(std::false_type{}, std::true_type{}, s_k0, s_k1, s_k2, s_v0, s_v1, s_v2);
-      else
-        ring(std::false_type{}, std::false_type{}, s_k0, s_k1, s_k2, s_v0, s_v1, s_v2);
+      auto with_bound = [&](auto fastc, auto listc) {
+        if (bounded)
+          ring(fastc, listc, std::true_type{}, s_k0, s_k1, s_k2, s_v0, s_v1, s_v2);
+        else
+          ring(fastc, listc, std::false_type{}, s_k0, s_k1, s_k2, s_v0, s_v1, s_v2);
+      };
+      if (fast) {
+        if (listed)
+          with_bound(std::true_type{}, std::true_type{});
+        else
+          with_bound(std::true_type{}, std::false_type{});
+      } else {
+        if (listed)
+          with_bound(std::false_type{}, std::true_type{});
+        else
+          with_bound(std::false_type{}, std::false_type{});
+      }
     }
   }
 
@@ -746,8 +814,8 @@ hipError_t launch_attn(const Plan& p, const uint16_t* q, uint16_t* out, hipStrea
   float* olin = lin ? p.o_lin : nullptr;  // optional export of the linear branch's output
 #define SAGESLA_ATTN(NWV, G)                                                                                     \
   hipLaunchKernelGGL((k3_attn<NWV, G>), dim3(total), dim3(64 * NWV), 0, s, p.q_i8, p.k_i8, p.v_img, p.q_scale,     \
-                     p.k_scale, p.block_idx, q, pl16, p.aux16, p.wpt, olin, out, p.N, p.n_qb, p.n_kb, p.topk, c0,   \
-                     total)
+                     p.k_scale, p.k_norm2, p.block_idx, q, pl16, p.aux16, p.wpt, olin, out, p.N, p.n_qb, p.n_kb,    \
+                     p.topk, c0, total)
   if (p.blk_q == 128) {
     if (p.group32) SAGESLA_ATTN(4, true); else SAGESLA_ATTN(4, false);
   } else {

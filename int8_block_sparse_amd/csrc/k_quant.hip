@@ -172,11 +172,14 @@ __global__ __launch_bounds__(128) void k1_colsum_final(const double* __restrict_
 // of every thread); scale_out then receives one value per group that holds a valid row.
 // With kt_img (key blocks of 64 rows only) the block's raw rows also go to LDS as a K^T image in the V^T-image
 // layout (write_v_image below: channel rows of 64 key slots, zeros past `rows`), for the linear-branch state.
+// With norm_out (key blocks only) each scale's rows also give the largest squared Euclidean norm of their codes
+// (exact in int32), in norm_out's slot for that scale: the attention kernel bounds its scores with it.
 template <int MAXROWS, bool SMOOTH, bool G32>
 __device__ __forceinline__ void quant_block(const uint16_t* __restrict__ src, int rows, const float* __restrict__ mu,
                                             int8_t* __restrict__ dst, float* __restrict__ scale_out,
                                             double* __restrict__ pool_out, float (*s_amax)[4],
-                                            double (*s_red)[kD + 1], unsigned char* __restrict__ kt_img = nullptr) {
+                                            double (*s_red)[kD + 1], unsigned char* __restrict__ kt_img = nullptr,
+                                            int32_t* __restrict__ norm_out = nullptr, int (*s_kn)[4] = nullptr) {
   constexpr int IT = MAXROWS / 16;
   constexpr int NG = G32 ? MAXROWS / 32 : 1;  // scales in this block
   const int t = threadIdx.x, cg = t & 15, rl = t >> 4;
@@ -238,9 +241,11 @@ __device__ __forceinline__ void quant_block(const uint16_t* __restrict__ src, in
     s[gi] = amax[gi] / 127.f;  // IEEE fp32 division (correctly rounded)
     rcp[gi] = 1.f / s[gi];
   }
+  int n2[IT];  // squared norm of this thread's 8 codes of row rl + 16 i (0 past the valid rows)
 #pragma unroll
   for (int i = 0; i < IT; ++i) {
     const int r = rl + 16 * i, gi = G32 ? i / 2 : 0;
+    n2[i] = 0;
     if (r < rows) {
       int c[8];
 #pragma unroll
@@ -249,6 +254,30 @@ __device__ __forceinline__ void quant_block(const uint16_t* __restrict__ src, in
       o.x = pack4_i8(c[0], c[1], c[2], c[3]);
       o.y = pack4_i8(c[4], c[5], c[6], c[7]);
       *(uint2*)(dst + (size_t)r * kD + cg * 8) = o;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) n2[i] += c[e] * c[e];
+    }
+  }
+  if constexpr (MAXROWS == kBlkK) {
+    if (norm_out) {  // a row's 16 threads are lanes 16 k .. 16 k + 15 of one wave
+      int nm[NG];
+#pragma unroll
+      for (int gi = 0; gi < NG; ++gi) nm[gi] = 0;
+#pragma unroll
+      for (int i = 0; i < IT; ++i) {
+        int v = n2[i];
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o);
+        nm[G32 ? i / 2 : 0] = max(nm[G32 ? i / 2 : 0], v);
+      }
+#pragma unroll
+      for (int gi = 0; gi < NG; ++gi) {
+        nm[gi] = max(nm[gi], __shfl_xor(nm[gi], 16));
+        nm[gi] = max(nm[gi], __shfl_xor(nm[gi], 32));
+        if ((t & 63) == 0) s_kn[t >> 6][gi] = nm[gi];
+      }
+      __syncthreads();
+      if (t < NG && 32 * t < rows) norm_out[t] = max(max(s_kn[0][t], s_kn[1][t]), max(s_kn[2][t], s_kn[3][t]));
     }
   }
   if (t < kD) {
@@ -385,10 +414,11 @@ template <int BLKQ, bool G32>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k1_quant(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const float* __restrict__ mu,
     int8_t* __restrict__ q8, int8_t* __restrict__ k8, float* __restrict__ qs, float* __restrict__ ks,
-    double* __restrict__ qp, double* __restrict__ kp, const uint16_t* __restrict__ v,
+    double* __restrict__ qp, double* __restrict__ kp, int32_t* __restrict__ kn2, const uint16_t* __restrict__ v,
     unsigned char* __restrict__ v_img, uint16_t* __restrict__ st16, int32_t* __restrict__ st_exp, int N, int n_qb,
     int n_kb) {
   __shared__ float s_amax[4][4];
+  __shared__ int s_kn[4][4];
   __shared__ __attribute__((aligned(16))) double s_red[16][kD + 1];  // 16512 B: also the state's V^T image
   __shared__ __attribute__((aligned(16))) unsigned char s_kt[kD * 128];
   const int bh = blockIdx.y;
@@ -404,16 +434,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
   } else {
     const int j = x - n_qb;
     const int r0 = j * kBlkK, nv = min(kBlkK, N - r0);
-    float* so = G32 ? ks + (size_t)bh * n_g + j * (kBlkK / 32) : ks + (size_t)bh * n_kb + j;
+    const size_t sidx = G32 ? (size_t)bh * n_g + j * (kBlkK / 32) : (size_t)bh * n_kb + j;
+    float* so = ks + sidx;
     uint32_t wv[4][4];
     if (v) load_v_rows(v + base + (size_t)r0 * kD, nv, wv);  // in flight while K is quantized
     unsigned char* kt = (v && st16) ? s_kt : nullptr;  // the state's K^T image, written by the quantizer
     if (mu)
       quant_block<kBlkK, true, G32>(k + base + (size_t)r0 * kD, nv, mu + bh * kD, k8 + base + (size_t)r0 * kD, so,
-                                    kp + ((size_t)bh * n_kb + j) * kD, s_amax, s_red, kt);
+                                    kp + ((size_t)bh * n_kb + j) * kD, s_amax, s_red, kt, kn2 + sidx, s_kn);
     else
       quant_block<kBlkK, false, G32>(k + base + (size_t)r0 * kD, nv, nullptr, k8 + base + (size_t)r0 * kD, so,
-                                     kp + ((size_t)bh * n_kb + j) * kD, s_amax, s_red, kt);
+                                     kp + ((size_t)bh * n_kb + j) * kD, s_amax, s_red, kt, kn2 + sidx, s_kn);
     if (v) write_v_image(wv, v_img + ((size_t)bh * n_kb + j) * 16384);
     if (kt) block_state16(wv, nv, (unsigned char*)&s_red[0][0], s_kt, &s_amax[0][0], st16, st_exp, bh, j, n_kb);
   }
@@ -453,7 +484,7 @@ hipError_t launch_quant(const Plan& p, const uint16_t* q, const uint16_t* k, con
   uint16_t* st16 = p.states_in_quant ? p.state16 : nullptr;  // the forward's linear-branch state table
 #define SAGESLA_QUANT(BQ, G)                                                                                   \
   hipLaunchKernelGGL((k1_quant<BQ, G>), grid, dim3(256), 0, s, q, k, mu, p.q_i8, p.k_i8, p.q_scale, p.k_scale,     \
-                     p.q_pool, p.k_pool, v, p.v_img, st16, p.state_exp, p.N, p.n_qb, p.n_kb)
+                     p.q_pool, p.k_pool, p.k_norm2, v, p.v_img, st16, p.state_exp, p.N, p.n_qb, p.n_kb)
   if (p.blk_q == 128) {
     if (p.group32) SAGESLA_QUANT(128, true); else SAGESLA_QUANT(128, false);
   } else {

@@ -266,6 +266,45 @@ def test_given_mask_ragged_block_first(group32):
         check_out(to_np(out[0, h]), r, lin=to_np(ex["o_lin"][0, h]))
 
 
+@pytest.mark.parametrize("group32", [False, True], ids=["block", "group32"])
+def test_bounded_shift_and_running_max_paths(group32):
+    # The attention kernel subtracts a per-row bound of the scores (Cauchy-Schwarz over the codes) instead of a
+    # running max when that bound lies within kBoundGap of a known score of the row; query block 1, scaled by 64,
+    # has its scores and their bound scaled alike, so its gap is far beyond and its waves keep the lazy running
+    # max, while the other blocks take the bounded shift. Lists of one block keep the running max too.
+    wl = SMALL["ragged128"]
+    q, k, v, w = synth.make(wl, 7)
+    q = q.clone()
+    q[:, :, 128:256] = (q[:, :, 128:256].float() * 64).to(torch.bfloat16)
+    c0 = math.log2(math.e) / math.sqrt(wl.D)
+    for topk in (wl.topk, 1):
+        out, ex = run_gpu(q.cuda(), k.cuda(), v.cuda(), w.cuda(), wl, topk, group32=group32)
+        for h in range(wl.H):
+            gidx = ex["block_idx"][0, h].cpu().numpy()[:, :topk]
+            if topk > 1:  # the gaps that decide each wave's path, from the exported codes and scales
+                qc = ex["q_i8"][0, h].cpu().numpy().astype(np.int64)
+                kc = ex["k_i8"][0, h].cpu().numpy().astype(np.int64)
+                qsc = ex["q_scale"][0, h].cpu().numpy().astype(np.float64)
+                ksc = ex["k_scale"][0, h].cpu().numpy().astype(np.float64)
+                per = 32 if group32 else wl.blk_k
+                kn = np.sqrt((kc ** 2).sum(1))
+                for I in range(wl.n_qb):
+                    rows = np.arange(I * wl.blk_q, min((I + 1) * wl.blk_q, wl.N))
+                    cq = (qsc[rows // 32] if group32 else qsc[I]) * c0
+                    keys = np.concatenate([np.arange(J * wl.blk_k, min((J + 1) * wl.blk_k, wl.N)) for J in gidx[I]])
+                    bound = np.sqrt((qc[rows] ** 2).sum(1)) * cq * (ksc[keys // per] * kn[keys]).max()
+                    j0 = gidx[I][0] * wl.blk_k
+                    gap = bound - (qc[rows] @ kc[j0]) * cq * ksc[j0 // per]
+                    if I == 1:
+                        assert gap.max() > 2 * 160, f"block 1 gap {gap.max():.1f}: its waves must keep the running max"
+                    else:
+                        assert gap.max() < 0.9 * 160, f"block {I} gap {gap.max():.1f}: expected the bounded shift"
+            r = orc.forward_head(to_np(q[0, h]), to_np(k[0, h]), to_np(v[0, h]), to_np(w), wl.blk_q, wl.blk_k, topk,
+                                 mask=gidx, quant_group=32 if group32 else None)
+            say(f"  topk {topk} head {h}: " + " ".join(f"{x:.3g}" for x in check_out(to_np(out[0, h]), r,
+                                                                                       lin=to_np(ex["o_lin"][0, h]))))
+
+
 def test_deterministic():
     wl = SMALL["grid"]
     q, k, v, w = (t.cuda() for t in synth.make(wl, 1))

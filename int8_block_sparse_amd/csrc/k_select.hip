@@ -14,41 +14,46 @@
 namespace sagesla {
 
 // ---------------------------------------------------------------------------------------------------------
-// scores[bh][I][J] = sum_c q_pool[bh][I][c] * k_pool[bh][J][c]   (fp64, fixed order over c)
-// grid (ceil(n_kb/128), ceil(n_qb/128), BH), 256 threads; thread (tx, ty) = (t%16, t/16) owns rows
-// ty + 16 i and columns tx + 16 j (i, j < 8) of the 128×128 tile. Channels are staged 16 at a time in LDS,
-// stored transposed so a wave reads 16 consecutive doubles of the key tile and broadcasts the query tile; the
-// next 16 are loaded into registers during the products of the current ones.
+// scores[bh][I][J] = sum_c q_pool[bh][I][c] * k_pool[bh][J][c]   (fp64)
+// grid (ceil(n_kb/128), ceil(n_qb/128), BH), 256 threads, fp64 MFMA (v_mfma_f64_16x16x4f64): wave w owns the
+// 64x64 quarter (rows 64 (w / 2), columns 64 (w % 2)) of the 128x128 tile as 4x4 accumulator tiles of 16x16.
+// Channels are staged 16 at a time in LDS, transposed ([channel][row], rows padded to 136 doubles), and the next
+// 16 are loaded into registers during the products of the current ones. Lane layout of the instruction (checked
+// on the device): A operand lane l = A[l % 16][l / 16], B operand lane l = B[l / 16][l % 16], accumulator lane l
+// element i = D[4 i + l / 16][l % 16]. The products of a step enter the sums in the unit's order, so a score can
+// differ from a sequential sum in its last bits; the selection treats scores that close as near-ties.
 // ---------------------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k2_scores(const double* __restrict__ qp, const double* __restrict__ kp,
-                                                double* __restrict__ sc, int n_qb, int n_kb) {
-  constexpr int TM = 128, TN = 128, KC = 16;
-  __shared__ double As[KC][TM];
-  __shared__ double Bs[KC][TN];
+typedef double v4d __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(256, 2) void k2_scores(const double* __restrict__ qp, const double* __restrict__ kp,
+                                                   double* __restrict__ sc, int n_qb, int n_kb) {
+  constexpr int TM = 128, TN = 128, KC = 16, LD = TM + 8;
+  __shared__ double As[KC][LD];
+  __shared__ double Bs[KC][LD];
   const int bh = blockIdx.z;
   const int I0 = blockIdx.y * TM, J0 = blockIdx.x * TN;
-  const int t = threadIdx.x, tx = t & 15, ty = t >> 4;
+  const int t = threadIdx.x, w = t >> 6, l = t & 63;
+  const int wm = (w >> 1) * 64, wn = (w & 1) * 64;
   const double* qb = qp + (size_t)bh * n_qb * kD;
   const double* kb = kp + (size_t)bh * n_kb * kD;
-  double acc[8][8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = 0.0;
   const int lr = t >> 1, lc = (t & 1) * 8;  // loader: tile row, first channel of its 8
   const int I = I0 + lr, J = J0 + lr;
-  // the next channel chunk is loaded into registers while this one is multiplied
   double av[8], bv[8];
   auto load = [&](int c0) {
 #pragma unroll
     for (int u = 0; u < 8; u += 2) {
-      double2 a = make_double2(0.0, 0.0), b = make_double2(0.0, 0.0);
-      if (I < n_qb) a = *(const double2*)(qb + (size_t)I * kD + c0 + lc + u);
-      if (J < n_kb) b = *(const double2*)(kb + (size_t)J * kD + c0 + lc + u);
-      av[u] = a.x; av[u + 1] = a.y;
-      bv[u] = b.x; bv[u + 1] = b.y;
+      double2 x = make_double2(0.0, 0.0), y = make_double2(0.0, 0.0);
+      if (I < n_qb) x = *(const double2*)(qb + (size_t)I * kD + c0 + lc + u);
+      if (J < n_kb) y = *(const double2*)(kb + (size_t)J * kD + c0 + lc + u);
+      av[u] = x.x; av[u + 1] = x.y;
+      bv[u] = y.x; bv[u + 1] = y.y;
     }
   };
+  v4d acc[4][4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = (v4d){0.0, 0.0, 0.0, 0.0};
   load(0);
   for (int c0 = 0; c0 < kD; c0 += KC) {
     __syncthreads();
@@ -59,30 +64,34 @@ __global__ __launch_bounds__(256) void k2_scores(const double* __restrict__ qp, 
     }
     __syncthreads();
     if (c0 + KC < kD) load(c0 + KC);
-#pragma unroll 4
-    for (int c = 0; c < KC; ++c) {
-      double a[8], b[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) a[i] = As[c][ty + 16 * i];
+    for (int ks = 0; ks < KC / 4; ++ks) {
+      const int kk = 4 * ks + (l >> 4);
+      double a[4], b[4];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) b[j] = Bs[c][tx + 16 * j];
+      for (int mt = 0; mt < 4; ++mt) a[mt] = As[kk][wm + 16 * mt + (l & 15)];
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
+      for (int nt = 0; nt < 4; ++nt) b[nt] = Bs[kk][wn + 16 * nt + (l & 15)];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = fma(a[i], b[j], acc[i][j]);
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+          acc[mt][nt] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[mt], b[nt], acc[mt][nt], 0, 0, 0);
     }
   }
   double* out = sc + (size_t)bh * n_qb * n_kb;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int I = I0 + ty + 16 * i;
-    if (I >= n_qb) continue;
+  for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int J = J0 + tx + 16 * j;
-      if (J < n_kb) out[(size_t)I * n_kb + J] = acc[i][j] + 0.0;  // +0.0 turns -0 into +0
+    for (int i = 0; i < 4; ++i) {
+      const int Ir = I0 + wm + 16 * mt + 4 * i + (l >> 4);
+      if (Ir >= n_qb) continue;
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const int Jc = J0 + wn + 16 * nt + (l & 15);
+        if (Jc < n_kb) out[(size_t)Ir * n_kb + Jc] = acc[mt][nt][i] + 0.0;  // +0.0 turns -0 into +0
+      }
     }
-  }
 }
 
 // ---------------------------------------------------------------------------------------------------------

@@ -107,6 +107,7 @@ __global__ __launch_bounds__(256, 2) void k2_scores(const double* __restrict__ q
 // asc), or candidates that are all equal are taken in ascending J.
 // ---------------------------------------------------------------------------------------------------------
 constexpr int kCandMax = 256;
+constexpr int kTopkBatch = 8;  // scores per lane loaded together in a pass over the row
 constexpr int kMaxPasses = 16;
 
 __device__ __forceinline__ unsigned long long lanemask_lt() {
@@ -153,13 +154,25 @@ __global__ __launch_bounds__(64) void k2_topk(const double* __restrict__ sc, int
     return;
   }
 
-  // initial candidates: everything
+  // initial candidates: everything. The row's loops take the scores kTopkBatch per lane at a time, all loads
+  // issued before the first is used, so that each pass waits for memory once per batch rather than per score.
   double lo = INFINITY, hi = -INFINITY;
-  for (int J = l; J < n_kb; J += 64) {
-    flags[J] = 2;
-    const double v = s[J];
-    lo = fmin(lo, v);
-    hi = fmax(hi, v);
+  for (int J0 = l; J0 < n_kb; J0 += 64 * kTopkBatch) {
+    double v[kTopkBatch];
+#pragma unroll
+    for (int u = 0; u < kTopkBatch; ++u) {
+      const int J = J0 + 64 * u;
+      v[u] = J < n_kb ? s[J] : 0.0;
+    }
+#pragma unroll
+    for (int u = 0; u < kTopkBatch; ++u) {
+      const int J = J0 + 64 * u;
+      if (J < n_kb) {
+        flags[J] = 2;
+        lo = fmin(lo, v[u]);
+        hi = fmax(hi, v[u]);
+      }
+    }
   }
   lo = wave_min_f64(lo);
   hi = wave_max_f64(hi);
@@ -168,16 +181,27 @@ __global__ __launch_bounds__(64) void k2_topk(const double* __restrict__ sc, int
   bool tie_mode = false;  // candidates all equal: take the lowest J
   __syncthreads();
 
-  // One histogram pass with the monotone bin function bin_of(J) in [0, 255] over the candidates; afterwards the
-  // candidates are those of the bin holding the need-th best, with their score range in [lo, hi].
+  // One histogram pass with the monotone bin function bin_of(score) in [0, 255] over the candidates; afterwards
+  // the candidates are those of the bin holding the need-th best, with their score range in [lo, hi].
   auto hist_pass = [&](auto bin_of) {
     for (int b = l; b < 256; b += 64) hist[b] = 0;
     __syncthreads();
-    for (int J = l; J < n_kb; J += 64) {
-      if (flags[J] != 2) continue;
-      const int b = bin_of(J);
-      bins[J] = (unsigned char)b;
-      atomicAdd(&hist[b], 1u);
+    for (int J0 = l; J0 < n_kb; J0 += 64 * kTopkBatch) {
+      double v[kTopkBatch];
+      bool c[kTopkBatch];
+#pragma unroll
+      for (int u = 0; u < kTopkBatch; ++u) {
+        const int J = J0 + 64 * u;
+        c[u] = J < n_kb && flags[J] == 2;
+        v[u] = c[u] ? s[J] : 0.0;
+      }
+#pragma unroll
+      for (int u = 0; u < kTopkBatch; ++u) {
+        if (!c[u]) continue;
+        const int b = bin_of(v[u]);
+        bins[J0 + 64 * u] = (unsigned char)b;
+        atomicAdd(&hist[b], 1u);
+      }
     }
     __syncthreads();
     // lane l owns bins 4l..4l+3; find the bin holding the need-th largest candidate
@@ -212,18 +236,29 @@ __global__ __launch_bounds__(64) void k2_topk(const double* __restrict__ sc, int
     // reclassify and measure the new candidates' range
     lo = INFINITY;
     hi = -INFINITY;
-    for (int J = l; J < n_kb; J += 64) {
-      if (flags[J] != 2) continue;
-      const int b = bins[J];
-      if (b > tbin) {
-        flags[J] = 1;
-      } else if (b < tbin) {
-        flags[J] = 0;
-      } else {
-        const double v = s[J];
-        lo = fmin(lo, v);
-        hi = fmax(hi, v);
+    for (int J0 = l; J0 < n_kb; J0 += 64 * kTopkBatch) {
+      double v[kTopkBatch];
+      bool c[kTopkBatch];
+#pragma unroll
+      for (int u = 0; u < kTopkBatch; ++u) {
+        const int J = J0 + 64 * u;
+        int b = -1;
+        if (J < n_kb && flags[J] == 2) {
+          b = bins[J];
+          if (b > tbin)
+            flags[J] = 1;
+          else if (b < tbin)
+            flags[J] = 0;
+        }
+        c[u] = b == tbin;
+        v[u] = c[u] ? s[J] : 0.0;
       }
+#pragma unroll
+      for (int u = 0; u < kTopkBatch; ++u)
+        if (c[u]) {
+          lo = fmin(lo, v[u]);
+          hi = fmax(hi, v[u]);
+        }
     }
     lo = wave_min_f64(lo);
     hi = wave_max_f64(hi);
@@ -254,7 +289,7 @@ __global__ __launch_bounds__(64) void k2_topk(const double* __restrict__ sc, int
       const double range = hi - lo;
       if (!(range < INFINITY)) break;  // beyond fp64: the radix passes take over
       // (s - lo) <= range, both rounded monotonically, so the ratio is in [0, 1]
-      hist_pass([&](int J) { return min(max((int)((s[J] - lo) / range * 256.0), 0), 255); });
+      hist_pass([&](double x) { return min(max((int)((x - lo) / range * 256.0), 0), 255); });
     }
   }
   if (!done) {
@@ -266,7 +301,7 @@ __global__ __launch_bounds__(64) void k2_topk(const double* __restrict__ sc, int
         break;
       }
       if (ncand <= kCandMax) break;
-      hist_pass([&](int J) { return (int)((order_key(s[J]) >> (8 * d)) & 255ull); });
+      hist_pass([&](double x) { return (int)((order_key(x) >> (8 * d)) & 255ull); });
     }
     if (need > 0 && need == ncand)
       keep_all();

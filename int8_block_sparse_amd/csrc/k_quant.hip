@@ -159,7 +159,15 @@ __global__ __launch_bounds__(128) void k1_colsum_final(const double* __restrict_
   const int bh = blockIdx.x, c = threadIdx.x;
   const double* p = part + (size_t)bh * n_chunks * kD + c;
   double s = 0.0;
-  for (int i = 0; i < n_chunks; ++i) s += p[(size_t)i * kD];
+  int i = 0;
+  for (; i + 8 <= n_chunks; i += 8) {  // eight loads in flight, added in chunk order
+    double x[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) x[u] = p[(size_t)(i + u) * kD];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s += x[u];
+  }
+  for (; i < n_chunks; ++i) s += p[(size_t)i * kD];
   mu[bh * kD + c] = (float)(s / (double)N);
 }
 

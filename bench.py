@@ -169,14 +169,33 @@ def host_info():
             "affinity_cores": len(os.sched_getaffinity(0))}
 
 
-def cpu_baseline(q, k, v, w, wl, heads, budget_s=30.0, blocks=None):
+def selection_check(r, scores, idx, D):
+    """The GPU's selection of one head against the oracle's: rows whose block list differs (each must be a near-tie
+    row, gap below NEAR_TIE), near-tie rows, and the largest score difference, also as a fraction of the fp64
+    rounding bound of the two sums (2^-44 |q_pool| . |k_pool|, both in the oracle's 1/sqrt(D) units)."""
+    import numpy as np
+    from oracle import sagesla as orc
+    got = idx[:, :r["idx"].shape[1]]
+    differ = np.any(got != r["idx"], axis=1)
+    near = r["gap"] < orc.NEAR_TIE
+    sg_ = scores / math.sqrt(D)
+    bound = 2.0 ** -44 * (np.abs(r["q_pool"]) @ np.abs(r["k_pool"]).T) / math.sqrt(D) + 1e-300
+    diff = np.abs(sg_ - r["scores"])
+    return {"rows": int(len(differ)), "rows_differ": int(differ.sum()), "rows_differ_not_near_tie":
+            int((differ & ~near).sum()), "near_tie_rows": int(near.sum()), "max_abs_score_diff": float(diff.max()),
+            "max_diff_over_bound": float((diff / bound).max())}
+
+
+def cpu_baseline(q, k, v, w, wl, heads, budget_s=30.0, blocks=None, gpu_sel=None):
     """The fp64 oracle (unchanged, untuned) on whole heads of the same workload; dense-equivalent TOPS.
 
     blocks: if given, each head's attention outputs are formed for that many evenly spaced query blocks only (its
     quantization, selection and linear-branch states still in full), and the dense-equivalent work is counted for
-    those blocks' rows."""
+    those blocks' rows. gpu_sel: {(b, h): (scores, block lists)} exported by the GPU for those heads; the oracle's
+    selection of each head is then compared with it (selection_check), outside the timed oracle work."""
     from oracle import sagesla as orc
     hi = host_info()
+    checks = []
     cores = hi["blas_threads"]
     W = w.float().cpu().double().numpy()
     done, t0 = 0, time.perf_counter()
@@ -186,7 +205,12 @@ def cpu_baseline(q, k, v, w, wl, heads, budget_s=30.0, blocks=None):
         Q = q[b, h].float().cpu().double().numpy()
         K = k[b, h].float().cpu().double().numpy()
         V = v[b, h].float().cpu().double().numpy()
-        orc.forward_head(Q, K, V, W, wl.blk_q, wl.blk_k, wl.topk, linear=wl.linear, blocks=sel)
+        t1 = time.perf_counter()
+        r = orc.forward_head(Q, K, V, W, wl.blk_q, wl.blk_k, wl.topk, linear=wl.linear, blocks=sel)
+        t_or = time.perf_counter() - t1
+        if gpu_sel is not None and (b, h) in gpu_sel:
+            checks.append(selection_check(r, *gpu_sel[(b, h)], wl.D))
+        t0 += time.perf_counter() - t1 - t_or  # the check is not oracle time
         done += 1
         log(f"cpu baseline: head {done}/{len(heads)} at {time.perf_counter() - t0:.1f} s")
         if time.perf_counter() - t0 > budget_s:
@@ -197,8 +221,12 @@ def cpu_baseline(q, k, v, w, wl, heads, budget_s=30.0, blocks=None):
     what = (f"each a full forward over all {wl.n_qb} query blocks" if sel is None else
             f"each with its quantization, selection and linear-branch states in full and the outputs of {len(sel)} of "
             f"its {wl.n_qb} query blocks (evenly spaced), counted as {rows} of {wl.N} rows")
-    return {"value": ops / dt / 1e12, "unit": "TOPS (dense-equivalent)", "cores": int(cores), "kind": "oracle",
-            "sample": f"{done} of {wl.B * wl.H} (b,h) heads, {what}", "seconds": round(dt, 2), **hi}
+    out = {"value": ops / dt / 1e12, "unit": "TOPS (dense-equivalent)", "cores": int(cores), "kind": "oracle",
+           "sample": f"{done} of {wl.B * wl.H} (b,h) heads, {what}", "seconds": round(dt, 2), **hi}
+    if checks:
+        out["selection_check"] = {"heads": len(checks), **{key: (max if key.startswith("max") else sum)(
+            c[key] for c in checks) for key in checks[0]}}
+    return out
 
 
 def cpu_baseline_w8a8(x, w, bias, wl, rows, budget_s=30.0):
@@ -808,7 +836,18 @@ def main_forward(args, wl):
         del ws
         heads = [(0, 0), (wl.B - 1, wl.H - 1)] + [(b, h) for b in range(wl.B) for h in range(wl.H)]
         heads = list(dict.fromkeys(heads))[:CPU_HEADS.get(wl.name, 2)]
-        result["cpu_baseline"] = cpu_baseline(q, k, v, w, wl, heads, budget_s=20.0, blocks=CPU_BLOCKS.get(wl.name))
+        gpu_sel = None
+        if 0 < wl.topk < wl.n_kb:
+            # one more forward (untimed) exporting the selection, checked against the oracle's on the same heads
+            _, ex = sg.forward(q, k, v, w, topk=wl.topk, blk_q=wl.blk_q, linear=wl.linear, export=True)
+            torch.cuda.synchronize()
+            gpu_sel = {(b, h): (ex["scores"][b, h].cpu().numpy(), ex["block_idx"][b, h].cpu().numpy())
+                       for (b, h) in heads}
+            del ex
+        cb = cpu_baseline(q, k, v, w, wl, heads, budget_s=20.0, blocks=CPU_BLOCKS.get(wl.name), gpu_sel=gpu_sel)
+        if "selection_check" in cb:
+            result["selection_check"] = cb.pop("selection_check")
+        result["cpu_baseline"] = cb
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)

@@ -100,6 +100,11 @@ typedef struct sagesla_params {
      norm weights of Q and of K (summed over every token of every batch entry). */
   float* dq_norm_w;
   float* dk_norm_w;
+  /* Optional export (device, caller-owned, 16-byte aligned): [B][H][n_qb][n_kb] fp64, the block scores
+     q_pool[I] . k_pool[J] that the top-k ranks ([TD-news] §三(二) item 1; the 1/sqrt(D) factor and a softmax
+     over J leave the ranking unchanged and are not applied). Written only when the selection runs
+     (0 < topk < n_kb and no SAGESLA_USE_GIVEN_MASK). */
+  double* scores;
 } sagesla_params;
 
 /* Bytes of workspace the three entry points need for these parameters (all intermediates kept inside).

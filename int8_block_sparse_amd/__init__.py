@@ -54,7 +54,7 @@ class Params(ctypes.Structure):
         ("events", ctypes.POINTER(ctypes.c_void_p)),
         ("q_norm_w", ctypes.c_void_p), ("k_norm_w", ctypes.c_void_p), ("q_hat", ctypes.c_void_p),
         ("k_hat", ctypes.c_void_p), ("norm_eps", ctypes.c_float),
-        ("dq_norm_w", ctypes.c_void_p), ("dk_norm_w", ctypes.c_void_p),
+        ("dq_norm_w", ctypes.c_void_p), ("dk_norm_w", ctypes.c_void_p), ("scores", ctypes.c_void_p),
     ]
 
 
@@ -226,6 +226,8 @@ def _exports(cfg: Config, device):
         "k_pool": torch.empty(cfg.B, cfg.H, cfg.n_kb, D, dtype=torch.float64, **f),
         "block_idx": torch.empty(cfg.B, cfg.H, cfg.n_qb, max(cfg.topk, 1), dtype=torch.int32, **f),
     }
+    if 0 < cfg.topk < cfg.n_kb:  # the block scores the top-k ranks (written when the selection runs)
+        ex["scores"] = torch.empty(cfg.B, cfg.H, cfg.n_qb, cfg.n_kb, dtype=torch.float64, **f)
     if cfg.linear:
         ex["o_lin"] = torch.empty(cfg.B, cfg.H, N, D, dtype=torch.float32, **f)
     if cfg.qk_norm:
@@ -269,8 +271,8 @@ def forward(q, k, v, w_proj=None, *, topk: int, blk_q: int = 128, blk_k: int = 6
     mask: optional int32 [B, H, n_qb, topk] ascending block lists used instead of the selection.
     group32: one INT8 scale per 32 tokens of Q and of K instead of one per block.
     norm: (gamma_q, gamma_k, eps) normalizes Q and K first (RMSNorm over the H*D channels of each token).
-    export=True also returns a dict of every intermediate (codes, scales, K mean, pooled means, block lists,
-    and the linear-branch output). Runs asynchronously on the current stream."""
+    export=True also returns a dict of every intermediate (codes, scales, K mean, pooled means, block scores when
+    the selection runs, block lists, and the linear-branch output). Runs asynchronously on the current stream."""
     return _forward(q, k, v, w_proj, topk, blk_q, blk_k, linear, smooth_k, sm_scale, mask, out, workspace, export,
                     events, group32, norm, noalloc=False)
 
@@ -298,6 +300,7 @@ def _forward(q, k, v, w_proj, topk, blk_q, blk_k, linear, smooth_k, sm_scale, ma
         if not export:
             ex = {}
         ex["block_idx"] = mask
+        ex.pop("scores", None)  # a given mask skips the selection
     ptrs = {name: _ptr(t) for name, t in ex.items()}
     p = cfg.params(w_proj=_ptr(w_proj), workspace=None if noalloc else ws.data_ptr(),
                    workspace_bytes=0 if noalloc else ws.numel(), given_mask=mask is not None, **ptrs,

@@ -53,7 +53,7 @@ sagesla_status check_params(const sagesla_params* p) {
       misaligned(p->q_scale, 16) || misaligned(p->k_scale, 16) || misaligned(p->k_mean, 16) ||
       misaligned(p->q_pool, 16) || misaligned(p->k_pool, 16) || misaligned(p->block_idx, 16) ||
       misaligned(p->o_lin, 16) || misaligned(p->q_norm_w, 16) || misaligned(p->k_norm_w, 16) ||
-      misaligned(p->q_hat, 16) || misaligned(p->k_hat, 16))
+      misaligned(p->q_hat, 16) || misaligned(p->k_hat, 16) || misaligned(p->scores, 16))
     return SAGESLA_E_ALIGN;
   return SAGESLA_OK;
 }
@@ -135,6 +135,7 @@ void make_plan(const sagesla_params* p, unsigned char* ws, Plan* pl, bool backwa
   if (p->q_pool) pl->q_pool = p->q_pool;
   if (p->k_pool) pl->k_pool = p->k_pool;
   if (p->block_idx) pl->block_idx = p->block_idx;
+  if (p->scores && !backward) pl->scores = p->scores;
   if (pl->qk_norm && p->q_hat) pl->q_hat = (uint16_t*)p->q_hat;
   if (pl->qk_norm && p->k_hat) pl->k_hat = (uint16_t*)p->k_hat;
   pl->o_lin = lin_active ? p->o_lin : nullptr;  // optional export

@@ -131,6 +131,7 @@ static void validation() {
       {[](sagesla_params& q) { q.k_pool = (double*)addr(0x70000008); }, SAGESLA_E_ALIGN},
       {[](sagesla_params& q) { q.block_idx = (int32_t*)addr(0x70000004); }, SAGESLA_E_ALIGN},
       {[](sagesla_params& q) { q.o_lin = (float*)addr(0x70000004); }, SAGESLA_E_ALIGN},
+      {[](sagesla_params& q) { q.scores = (double*)addr(0x70000008); }, SAGESLA_E_ALIGN},
       {[](sagesla_params& q) { q.flags |= SAGESLA_QK_RMSNORM; q.q_norm_w = addr(0x50000002); q.k_norm_w = kW; },
        SAGESLA_E_ALIGN},
       {[](sagesla_params& q) { q.flags |= SAGESLA_QK_RMSNORM; q.q_norm_w = kW; q.k_norm_w = kW;

@@ -74,6 +74,20 @@ def check_mask(gidx, r, topk):
     return flagged
 
 
+def check_scores(ex, r, b, h):
+    """The exported fp64 block scores against the oracle's, within the rounding bound of the two fp64 sums
+    (2^-44 |q_pool| . |k_pool|; the kernel's sums skip the oracle's 1/sqrt(D)). Returns the largest difference
+    as a fraction of that bound (0 when the selection did not run)."""
+    if "scores" not in ex:
+        return 0.0
+    D = r["q_pool"].shape[1]
+    got = ex["scores"][b, h].cpu().numpy() / math.sqrt(D)
+    bound = 2.0 ** -44 * (np.abs(r["q_pool"]) @ np.abs(r["k_pool"]).T) / math.sqrt(D) + 1e-300
+    ratio = float((np.abs(got - r["scores"]) / bound).max())
+    assert ratio <= 1.0, f"block scores off by {ratio:.2f} of their rounding bound"
+    return ratio
+
+
 def bf16_half_ulp(x):
     """Half the bf16 spacing at |x| (8 significant bits)."""
     e = np.frexp(np.maximum(np.abs(x), 2.0 ** -126))[1]
@@ -161,6 +175,7 @@ def full_case(wl, seed=0, topk=None, linear=None, smooth_k=True, w_mul=1.0, prep
                                  quant_group=qg)
             assert r["exact_sum_ok"]
             check_quant(ex, r, b, h)
+            check_scores(ex, r, b, h)
             flagged += check_mask(gidx, r, topk)
             rg = orc.forward_head(Q, K, V, W, wl.blk_q, wl.blk_k, topk, linear=linear, smooth_k=smooth_k,
                                   mask=gidx[:, :topk] if topk else np.zeros((wl.n_qb, 0), np.int32),
@@ -359,13 +374,14 @@ def sampled_case(cfg_id, heads, n_blocks_sample=6, seed=0, group32=False, norm=F
                              quant_group=32 if group32 else None)
         assert r["exact_sum_ok"]
         check_quant(ex, r, b, h)
+        sratio = check_scores(ex, r, b, h)
         flagged_h = check_mask(gidx, r, wl.topk)
         flagged += flagged_h
         rows = np.concatenate([np.arange(wl.N)[orc.block_rows(wl.N, wl.blk_q, I)] for I in blocks])
         lin = to_np(ex["o_lin"][b, h]) if wl.linear else None
         err, c = check_out(to_np(out[b, h]), r, rows=rows, lin=lin)
         say(f"  b{b} h{h}: {len(blocks)} query blocks, out max-abs {err:.2e} cos {c:.6f}, near-tie rows {flagged_h}"
-            f", min gap {np.min(r['gap']):.2e}")
+            f", min gap {np.min(r['gap']):.2e}, score difference {sratio:.3f} of its bound")
     del q, k, v, out, ex
     torch.cuda.empty_cache()
     return flagged

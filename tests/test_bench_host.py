@@ -83,3 +83,28 @@ def test_short_kernel_names():
     assert bench._short_kernel("void sagesla::k3_attn<4, false>(signed char const*, int)") == "k3_attn<4, false>"
     assert bench._short_kernel("sagesla::k4_gemm16(unsigned short const*, int)") == "k4_gemm16"
     assert bench._short_kernel("void at::native::foo<1>(int)").startswith("torch ")
+
+
+def test_selection_check_counts_rows_and_score_bound():
+    # the bench line's selection diagnostics on a tiny oracle head: the oracle's own scores and lists agree with
+    # themselves, a changed list row is counted (and, with a wide gap, as not a near tie), and a score moved by
+    # more than the rounding bound shows a ratio above 1
+    import math
+    import numpy as np
+    import synth
+    from oracle import sagesla as orc
+    wl = synth.workload(0)
+    q, k, v, w = synth.make(wl, 0)
+    f = lambda t: t.float().double().numpy()
+    r = orc.forward_head(f(q[0, 0]), f(k[0, 0]), f(v[0, 0]), f(w), wl.blk_q, wl.blk_k, wl.topk, linear=False)
+    s = r["scores"] * math.sqrt(wl.D)
+    c = bench.selection_check(r, s, r["idx"].copy(), wl.D)
+    assert c["rows"] == wl.n_qb and c["rows_differ"] == 0 and c["max_diff_over_bound"] <= 1.0
+    idx = r["idx"].copy()
+    row = int(np.argmax(r["gap"] * (r["gap"] < np.inf)))  # a row with a clear gap
+    idx[row, -1] = next(J for J in range(wl.n_kb) if J not in idx[row])
+    s2 = s.copy()
+    s2[0, 0] += 1e-6 * max(1.0, abs(s2[0, 0]))
+    c = bench.selection_check(r, s2, idx, wl.D)
+    assert c["rows_differ"] == 1 and c["rows_differ_not_near_tie"] == (1 if r["gap"][row] >= orc.NEAR_TIE else 0)
+    assert c["max_diff_over_bound"] > 1.0

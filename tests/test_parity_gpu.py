@@ -211,6 +211,17 @@ def test_forward_small_qk_norm(name):
     assert full_case(SMALL[name], norm=True) == 0
 
 
+@pytest.mark.parametrize("N,bq,topk", [(1, 64, 1), (1, 128, 0), (40, 128, 1), (64, 64, 0), (65, 64, 1),
+                                        (65, 128, 2), (129, 64, 2), (129, 128, 1)])
+@pytest.mark.parametrize("group32", [False, True], ids=["block", "group32"])
+def test_forward_tiny_and_one_row_tails(N, bq, topk, group32):
+    # a single token, fewer tokens than one key block, exactly one block, and tails of a single row in both block
+    # kinds; the list from empty (linear branch only) to every block (no linear branch)
+    wl = synth.custom(1, 2, N, blk_q=bq, topk_frac=0.5)
+    assert topk <= wl.n_kb
+    assert full_case(wl, topk=topk, group32=group32) == 0
+
+
 def test_topk_zero_linear_only():
     full_case(SMALL["ragged128"], topk=0)
 

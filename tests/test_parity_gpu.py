@@ -381,6 +381,7 @@ def sampled_case(cfg_id, heads, n_blocks_sample=6, seed=0, group32=False, norm=F
             check_hat(ex, b, h, K, "k_hat")
         gidx = ex["block_idx"][b, h].cpu().numpy()[:, :wl.topk]
         blocks = sorted(set([0, wl.n_qb - 1] + list(rng.choice(wl.n_qb, n_blocks_sample, replace=False))))
+        say(f"  b{b} h{h}: oracle")
         r = orc.forward_head(Q, K, V, W, wl.blk_q, wl.blk_k, wl.topk, linear=wl.linear, mask=gidx, blocks=blocks,
                              quant_group=32 if group32 else None)
         assert r["exact_sum_ok"]
@@ -428,6 +429,15 @@ def test_full_size_sla_480p_qk_norm():
 def test_full_size_sla_720p_pair_qk_norm():
     # the benchmarked layer with the RMSNorm of Q and K before the path
     sampled_case(3, [(0, 0), (1, 39)], norm=True)
+
+
+@pytest.mark.timeout(600)
+def test_full_size_max_key_blocks():
+    # the largest key-block count the parameter checks accept (20480, N = 1310697 with a ragged last block),
+    # 10% selected (2048-entry lists), linear branch on; the oracle ranks every query block's 20480 scores
+    wl = synth.custom(1, 1, 20480 * 64 - 23, blk_q=128, topk_frac=0.1, name="max-key-blocks")
+    assert wl.n_kb == 20480 and wl.topk == 2048
+    sampled_case(wl, [(0, 0)], n_blocks_sample=3)
 
 
 # ---------------------------------------------------------------------------------------------------------

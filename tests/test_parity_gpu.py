@@ -432,6 +432,15 @@ def test_full_size_sla_720p_pair_qk_norm():
 
 
 @pytest.mark.timeout(600)
+def test_full_size_large_batch():
+    # the 720P layer at batch 8 (B H N D = 8 40 75600 128): every activation tensor holds 3.1e9 elements (more than
+    # 2^31), so any 32-bit element or byte offset would wrap; the first and the last head are checked
+    wl = synth.custom(8, 40, 75600, grid=(21, 45, 80), structured=True, blk_q=128, topk_frac=0.1, name="720p-b8")
+    assert wl.B * wl.H * wl.N * wl.D > 2 ** 31
+    sampled_case(wl, [(0, 0), (7, 39)], n_blocks_sample=4)
+
+
+@pytest.mark.timeout(600)
 def test_full_size_max_key_blocks():
     # the largest key-block count the parameter checks accept (20480, N = 1310697 with a ragged last block),
     # 10% selected (2048-entry lists), linear branch on; the oracle ranks every query block's 20480 scores

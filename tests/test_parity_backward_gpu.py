@@ -205,8 +205,8 @@ def test_backward_no_branch_gives_zero_gradients():
 # heads; with the linear branch off, the invariants of softmax attention (sum_j dK_j = 0 because every row of dS
 # sums to zero; sum_j dV_j = sum_i dY_i because every row of P sums to one)
 # ---------------------------------------------------------------------------------------------------------
-def full_720p(linear):
-    wl = synth.workload(3)
+def full_720p(linear, wl=None):
+    wl = synth.workload(3) if wl is None else wl
     q, k, v, w = synth.make(wl, 0, device="cuda")
     say(f"full-size {wl.name}: forward for the selection")
     _, ex = sg.forward(q, k, v, w, topk=wl.topk, export=True)
@@ -219,10 +219,10 @@ def full_720p(linear):
     return wl, q, k, v, w, dy, mask, grads
 
 
-def test_backward_full_size_720p_dq_blocks():
-    wl, q, k, v, w, dy, mask, (dq, dk, dv, dw) = full_720p(True)
+def test_backward_full_size_720p_dq_blocks(wl=None, heads=((0, 0), (1, 39))):
+    wl, q, k, v, w, dy, mask, (dq, dk, dv, dw) = full_720p(True, wl)
     rng = np.random.default_rng(3)
-    for (b, h) in [(0, 0), (1, 39)]:
+    for (b, h) in heads:
         blocks = sorted({0, wl.n_qb - 1, *rng.choice(wl.n_qb, 3, replace=False).tolist()})
         sel = mask[b, h].cpu().numpy()
         ref = ob.dq_blocks(to_np(q[b, h]), to_np(k[b, h]), to_np(v[b, h]), to_np(w), sel, to_np(dy[b, h]), wl.blk_q,
@@ -235,13 +235,13 @@ def test_backward_full_size_720p_dq_blocks():
     assert torch.isfinite(dk).all() and torch.isfinite(dv).all() and torch.isfinite(dw).all()
 
 
-def test_backward_full_size_720p_softmax_invariants():
+def test_backward_full_size_720p_softmax_invariants(wl=None, heads=((0, 0), (0, 17), (1, 39))):
     # exact: sum_j dK_j = sm sum_i q_i sum_j dS_ij = 0 and sum_j dV_j = sum_i dY_i sum_j P_ij = sum_i dY_i. With dS and
     # P rounded to bf16 (<= 2^-9 each) the sums are off by at most 2^-9 sm sum_i |q_i| R_i (R_i = sum_j |dS_ij|) and
     # 2^-9 sum_i |dY_i| (the rows of P sum to one), checked at 2^-8 plus the fp32 floor
-    wl, q, k, v, w, dy, mask, (dq, dk, dv, dw) = full_720p(False)
+    wl, q, k, v, w, dy, mask, (dq, dk, dv, dw) = full_720p(False, wl)
     sm = 1.0 / np.sqrt(wl.D)
-    for (b, h) in [(0, 0), (0, 17), (1, 39)]:
+    for (b, h) in heads:
         Q, Y = to_np(q[b, h]).astype(np.float64), to_np(dy[b, h]).astype(np.float64)
         R = sparse_terms(Q, to_np(k[b, h]), to_np(v[b, h]), Y, mask[b, h].cpu().numpy(), wl.blk_q, wl.blk_k)[3]
         sk = to_np(dk[b, h]).astype(np.float64).sum(axis=0)
@@ -252,6 +252,20 @@ def test_backward_full_size_720p_softmax_invariants():
         lim_v = U * np.abs(Y).sum(axis=0) + FLOOR * np.abs(sy).max()
         say(f"  b{b} h{h}: |sum dV - sum dY| / bound = {np.max(np.abs(sv - sy) / lim_v):.3f}")
         assert np.all(np.abs(sv - sy) <= lim_v)
+
+
+WL_720P_B8 = synth.custom(8, 40, 75600, grid=(21, 45, 80), structured=True, blk_q=128, topk_frac=0.1, name="720p-b8")
+
+
+@pytest.mark.timeout(600)
+def test_backward_large_batch():
+    # the 720P layer at batch 8, 3.1e9 elements per tensor (past 32-bit offsets): the exact dQ rows of sampled query
+    # blocks with the linear branch on, then the softmax identities of dK and dV with it off, on the first and the
+    # last head
+    assert WL_720P_B8.B * WL_720P_B8.H * WL_720P_B8.N * WL_720P_B8.D > 2 ** 31
+    test_backward_full_size_720p_dq_blocks(WL_720P_B8, ((0, 0), (7, 39)))
+    torch.cuda.empty_cache()
+    test_backward_full_size_720p_softmax_invariants(WL_720P_B8, ((0, 0), (7, 39)))
 
 
 # ---------------------------------------------------------------------------------------------------------

@@ -207,6 +207,8 @@ LINEAR_WORKLOADS = {
     "wan14b-720p-proj": LinearWorkload("wan14b-720p-proj", 151200, 5120, 5120),
     "wan14b-720p-ffn-up": LinearWorkload("wan14b-720p-ffn-up", 151200, 13824, 5120),
     "wan14b-720p-ffn-down": LinearWorkload("wan14b-720p-ffn-down", 151200, 5120, 13824),
+    # the FFN-down layer at the most tokens the library takes for 13824 inputs (rows * cols < 2^31)
+    "wan14b-ffn-down-max-rows": LinearWorkload("wan14b-ffn-down-max-rows", 155344, 5120, 13824),
 }
 
 

@@ -288,6 +288,8 @@ static void w8a8(bool debug) {
   int8_t* const c8 = (int8_t*)addr(0xb0000000);
   float* const sc = (float*)addr(0xc0000000);
   CHECK(w8a8_quantize(x, 256, 200, 1.f, c8, sc, nullptr) == SAGESLA_E_UNSUPPORTED);
+  CHECK(w8a8_quantize(x, 155345, 13824, 1.f, c8, sc, nullptr) == SAGESLA_E_UNSUPPORTED);  // rows * cols >= 2^31
+  CHECK(w8a8_quantize(x, (1 << 24) + 1, 128, 1.f, c8, sc, nullptr) == SAGESLA_E_UNSUPPORTED);  // rows > 2^24
   CHECK(w8a8_quantize(x, 0, 256, 1.f, c8, sc, nullptr) == SAGESLA_E_SHAPE);
   CHECK(w8a8_quantize(x, 256, 256, 0.f, c8, sc, nullptr) == SAGESLA_E_SHAPE);
   CHECK(w8a8_quantize(x, 256, 256, 1.5f, c8, sc, nullptr) == SAGESLA_E_SHAPE);
@@ -298,6 +300,8 @@ static void w8a8(bool debug) {
   uint16_t* const y = (uint16_t*)addr(0xd0000000);
   CHECK(w8a8_gemm(c8, sc, c8, sc, nullptr, y, 256, 200, 256, nullptr) == SAGESLA_E_UNSUPPORTED);
   CHECK(w8a8_gemm(c8, sc, c8, sc, nullptr, y, 256, 256, 32768 + 128, nullptr) == SAGESLA_E_UNSUPPORTED);
+  CHECK(w8a8_gemm(c8, sc, c8, sc, nullptr, y, 155345, 256, 13824, nullptr) == SAGESLA_E_UNSUPPORTED);  // M K >= 2^31
+  CHECK(w8a8_gemm(c8, sc, c8, sc, nullptr, y, 256, 155345, 13824, nullptr) == SAGESLA_E_UNSUPPORTED);  // N K >= 2^31
   CHECK(w8a8_gemm(c8, sc, c8, nullptr, nullptr, y, 256, 256, 256, nullptr) == SAGESLA_E_NULL);
   CHECK(w8a8_gemm(c8, sc, c8, sc, addr(0xe0000002), y, 256, 256, 256, nullptr) == SAGESLA_E_ALIGN);
   check_sequence([=] { return w8a8_gemm(c8, sc, c8, sc, nullptr, y, 256, 256, 256, nullptr); }, {"w8a8_gemm"}, debug);

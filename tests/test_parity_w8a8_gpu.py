@@ -158,3 +158,12 @@ def test_full_size_720p_proj():
 
 def test_full_size_720p_ffn_down_clipped():
     sampled_full("wan14b-720p-ffn-down", [3, -1], 128, seed=1, clip=0.8)
+
+
+@pytest.mark.timeout(600)
+def test_full_size_ffn_down_max_rows():
+    # the largest activation matrix the limits allow for 13824 inputs (155344 tokens: 2^31 - 8192 elements, the
+    # last token block ragged; one more token is refused, which the host-side checks of the C ABI test)
+    wl = synth.LINEAR_WORKLOADS["wan14b-ffn-down-max-rows"]
+    assert wl.M * wl.K < 2 ** 31 <= (wl.M + 1) * wl.K
+    sampled_full("wan14b-ffn-down-max-rows", [0, 600, -2, -1], 96, seed=2)

@@ -153,6 +153,14 @@ static void validation() {
   CHECK(sagesla_validate(&p) == SAGESLA_OK);
   p = base(1000, 16);  // topk == n_kb
   CHECK(sagesla_validate(&p) == SAGESLA_OK);
+  p = base(20480 * 64, 2048);  // the largest key-block count
+  CHECK(sagesla_validate(&p) == SAGESLA_OK && sagesla_workspace_bytes(&p) > 0);
+  p = base();
+  p.B = 255;
+  p.H = 257;  // B * H = 65535
+  CHECK(sagesla_validate(&p) == SAGESLA_OK && sagesla_workspace_bytes(&p) > 0);
+  p = base(1, 1);  // one token
+  CHECK(sagesla_validate(&p) == SAGESLA_OK);
   p = base();
   p.sm_scale = 0.f;
   CHECK(sagesla_validate(&p) == SAGESLA_OK);

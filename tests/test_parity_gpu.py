@@ -440,6 +440,27 @@ def test_full_size_large_batch():
     sampled_case(wl, [(0, 0), (7, 39)], n_blocks_sample=4)
 
 
+def test_max_heads():
+    # B * H = 65535, the largest head count (grid dimensions), 200 tokens per head with 2 of 4 key blocks selected
+    # and the linear branch on; the first, a middle and the last head against the oracle
+    wl = synth.custom(255, 257, 200, blk_q=128, topk_frac=0.5, name="max-heads")
+    assert wl.B * wl.H == 65535 and wl.topk == 2
+    q, k, v, w = synth.make(wl, 5, device="cuda")
+    say(f"case {wl.name} B{wl.B} H{wl.H} N{wl.N}: forward")
+    out, ex = run_gpu(q, k, v, w, wl, wl.topk)
+    W = to_np(w)
+    for (b, h) in [(0, 0), (127, 128), (254, 256)]:
+        Q, K, V = to_np(q[b, h]), to_np(k[b, h]), to_np(v[b, h])
+        gidx = ex["block_idx"][b, h].cpu().numpy()[:, :wl.topk]
+        r = orc.forward_head(Q, K, V, W, wl.blk_q, wl.blk_k, wl.topk, linear=True)
+        check_quant(ex, r, b, h)
+        check_scores(ex, r, b, h)
+        assert check_mask(gidx, r, wl.topk) == 0
+        rg = orc.forward_head(Q, K, V, W, wl.blk_q, wl.blk_k, wl.topk, linear=True, mask=gidx)
+        err, c = check_out(to_np(out[b, h]), rg, lin=to_np(ex["o_lin"][b, h]))
+        say(f"  b{b} h{h}: out max-abs {err:.2e} cos {c:.6f}")
+
+
 @pytest.mark.timeout(600)
 def test_full_size_max_key_blocks():
     # the largest key-block count the parameter checks accept (20480, N = 1310697 with a ragged last block),

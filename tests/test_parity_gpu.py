@@ -142,7 +142,8 @@ def check_hat(ex, b, h, want, name):
     assert np.array_equal(got, want), f"{name}: {np.sum(got != want)} normalized values differ"
 
 
-def full_case(wl, seed=0, topk=None, linear=None, smooth_k=True, w_mul=1.0, prep=None, group32=False, norm=False):
+def full_case(wl, seed=0, topk=None, linear=None, smooth_k=True, w_mul=1.0, prep=None, group32=False, norm=False,
+              sm_scale=0.0):
     topk = wl.topk if topk is None else topk
     linear = wl.linear if linear is None else linear
     q, k, v, w = synth.make(wl, seed)
@@ -151,10 +152,11 @@ def full_case(wl, seed=0, topk=None, linear=None, smooth_k=True, w_mul=1.0, prep
     w = (w.float() * w_mul).to(torch.bfloat16)
     dq, dk, dv, dw = (t.cuda() for t in (q, k, v, w))
     say(f"case {wl.name} B{wl.B} H{wl.H} N{wl.N} bq{wl.blk_q} topk{topk} linear{linear} smooth{smooth_k}"
-        f" group32{group32} norm{norm}")
+        f" group32{group32} norm{norm} sm_scale{sm_scale}")
     nw = synth.make_norm_weights(wl.H, wl.D, seed) if norm else None
     out, ex = run_gpu(dq, dk, dv, dw, wl, topk, linear=linear, smooth_k=smooth_k, group32=group32,
-                      norm=(nw[0].cuda(), nw[1].cuda(), synth.NORM_EPS) if norm else None)
+                      norm=(nw[0].cuda(), nw[1].cuda(), synth.NORM_EPS) if norm else None, sm_scale=sm_scale)
+    sm = sm_scale if sm_scale > 0 else None
     qg = 32 if group32 else None
     outn = to_np(out)
     W = to_np(w)
@@ -172,14 +174,14 @@ def full_case(wl, seed=0, topk=None, linear=None, smooth_k=True, w_mul=1.0, prep
                 check_hat(ex, b, h, K, "k_hat")
             gidx = ex["block_idx"][b, h].cpu().numpy()
             r = orc.forward_head(Q, K, V, W, wl.blk_q, wl.blk_k, topk, linear=linear, smooth_k=smooth_k,
-                                 quant_group=qg)
+                                 quant_group=qg, sm_scale=sm)
             assert r["exact_sum_ok"]
             check_quant(ex, r, b, h)
             check_scores(ex, r, b, h)
             flagged += check_mask(gidx, r, topk)
             rg = orc.forward_head(Q, K, V, W, wl.blk_q, wl.blk_k, topk, linear=linear, smooth_k=smooth_k,
                                   mask=gidx[:, :topk] if topk else np.zeros((wl.n_qb, 0), np.int32),
-                                  quant_group=qg)
+                                  quant_group=qg, sm_scale=sm)
             lin = to_np(ex["o_lin"][b, h]) if linear else None
             err, c = check_out(outn[b, h], rg, lin=lin, bf16_bound=w_mul != 1.0)
             say(f"  b{b} h{h}: out max-abs {err:.2e} cos {c:.6f}")
@@ -220,6 +222,14 @@ def test_forward_tiny_and_one_row_tails(N, bq, topk, group32):
     wl = synth.custom(1, 2, N, blk_q=bq, topk_frac=0.5)
     assert topk <= wl.n_kb
     assert full_case(wl, topk=topk, group32=group32) == 0
+
+
+@pytest.mark.parametrize("sm_scale", [0.02, 0.5, 2.0])
+@pytest.mark.parametrize("group32", [False, True], ids=["block", "group32"])
+def test_softmax_scales(sm_scale, group32):
+    # softmax scales other than 1/sqrt(D) (0.088): flatter and far sharper rows, which move waves between the
+    # bounded shift and the running maximum and blocks between the two exponent forms
+    assert full_case(SMALL["ragged128"], sm_scale=sm_scale, group32=group32) == 0
 
 
 def test_topk_zero_linear_only():

@@ -90,21 +90,22 @@ def make_mask(wl, topk, seed):
     return np.stack(rows).reshape(wl.B, wl.H, wl.n_qb, topk).astype(np.int32)
 
 
-def case(wl, topk, linear=True, seed=0):
+def case(wl, topk, linear=True, seed=0, sm_scale=0.0):
     q, k, v, w = synth.make(wl, seed)
     dy = (torch.randn(q.shape, generator=torch.Generator().manual_seed(seed + 11))).to(torch.bfloat16)
     mask = make_mask(wl, topk, seed)
-    say(f"case {wl.name} B{wl.B} H{wl.H} N{wl.N} bq{wl.blk_q} topk{topk} linear{linear}")
+    say(f"case {wl.name} B{wl.B} H{wl.H} N{wl.N} bq{wl.blk_q} topk{topk} linear{linear} sm_scale{sm_scale}")
     dq, dk, dv, dw = sg.backward(q.cuda(), k.cuda(), v.cuda(), w.cuda(), dy.cuda(), torch.from_numpy(mask).cuda(),
-                                 topk=topk, blk_q=wl.blk_q, blk_k=wl.blk_k, linear=linear)
+                                 topk=topk, blk_q=wl.blk_q, blk_k=wl.blk_k, linear=linear, sm_scale=sm_scale)
     torch.cuda.synchronize()
+    sm = sm_scale if sm_scale > 0 else None
     rq, rk, rv, rw = ob.backward(to_np(q), to_np(k), to_np(v), to_np(w), mask, to_np(dy), wl.blk_q, wl.blk_k,
-                                 linear=linear)
+                                 linear=linear, sm_scale=sm)
     for b in range(wl.B):
         for h in range(wl.H):
             say(f"  b{b} h{h}")
             tq, tk, tv, _ = sparse_terms(to_np(q[b, h]), to_np(k[b, h]), to_np(v[b, h]), to_np(dy[b, h]), mask[b, h],
-                                         wl.blk_q, wl.blk_k)
+                                         wl.blk_q, wl.blk_k, sm_scale=sm)
             within("dq", to_np(dq[b, h]), rq[b, h], tq)
             within("dk", to_np(dk[b, h]), rk[b, h], tk)
             within("dv", to_np(dv[b, h]), rv[b, h], tv)
@@ -125,6 +126,12 @@ SMALL = {
 def test_backward_mixed(name):
     wl = SMALL[name]
     case(wl, max(1, wl.n_kb // 4))
+
+
+@pytest.mark.parametrize("sm_scale", [0.02, 0.5])
+def test_backward_softmax_scales(sm_scale):
+    # softmax scales other than 1/sqrt(D): a flatter and a sharper P
+    case(SMALL["ragged128"], 3, sm_scale=sm_scale)
 
 
 def test_backward_sparse_only():

@@ -246,6 +246,13 @@ def test_dense_no_linear():
     full_case(wl)
 
 
+@pytest.mark.parametrize("name", ["ragged128", "ragged64"])
+@pytest.mark.parametrize("group32", [False, True], ids=["block", "group32"])
+def test_sparse_no_linear(name, group32):
+    # the selection without the linear branch: the unselected blocks simply drop out of the output
+    assert full_case(SMALL[name], linear=False, group32=group32) == 0
+
+
 def test_no_smoothing():
     full_case(SMALL["ragged64"], smooth_k=False)
 

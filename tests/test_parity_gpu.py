@@ -246,6 +246,12 @@ def test_dense_no_linear():
     full_case(wl)
 
 
+@pytest.mark.parametrize("name,linear", [("ragged128", True), ("ragged64", True), ("ragged64", False)])
+def test_options_together(name, linear):
+    # every option of the forward at once: the RMSNorm of Q and K, 32-token scales and a softmax scale of 0.5
+    assert full_case(SMALL[name], norm=True, group32=True, linear=linear, sm_scale=0.5) == 0
+
+
 @pytest.mark.parametrize("name", ["ragged128", "ragged64"])
 @pytest.mark.parametrize("group32", [False, True], ids=["block", "group32"])
 def test_sparse_no_linear(name, group32):

@@ -364,6 +364,26 @@ def test_deterministic():
         assert torch.equal(e1[name], e2[name]), name
 
 
+def test_concurrent_streams():
+    # the library keeps no state between calls: two forwards of different inputs, each with its own workspace, run
+    # at once on two streams (default priority) and give the bits each gives alone
+    wl = SMALL["ragged128"]
+    cfg = sg.Config(wl.B, wl.H, wl.N, wl.D, wl.blk_q, wl.blk_k, wl.topk, wl.linear)
+    ins = [[t.cuda() for t in synth.make(wl, seed)] for seed in (3, 4)]
+    alone = [run_gpu(*x, wl, wl.topk)[0] for x in ins]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    wss = [torch.empty(sg.workspace_bytes(cfg), dtype=torch.uint8, device="cuda") for _ in range(2)]
+    outs = [torch.empty_like(ins[i][0]) for i in range(2)]
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for i in range(2):
+            with torch.cuda.stream(streams[i]):
+                sg.forward(*ins[i], topk=wl.topk, blk_q=wl.blk_q, out=outs[i], workspace=wss[i])
+        torch.cuda.synchronize()
+        for i in range(2):
+            assert torch.equal(outs[i], alone[i]), f"stream {i}, repetition {rep}"
+
+
 def test_stage_entry_points_agree_with_forward():
     wl = SMALL["ragged128"]
     q, k, v, w = (t.cuda() for t in synth.make(wl, 2))

@@ -275,6 +275,15 @@ def test_backward_large_batch():
     test_backward_full_size_720p_softmax_invariants(WL_720P_B8, ((0, 0), (7, 39)))
 
 
+@pytest.mark.timeout(600)
+def test_backward_max_key_blocks():
+    # the largest key-block count (20480 blocks, N = 1310697, 2048-entry selections, bitmaps of 320 and 640 words):
+    # the exact dQ rows of sampled query blocks with the linear branch on
+    wl = synth.custom(1, 1, 20480 * 64 - 23, blk_q=128, topk_frac=0.1, name="max-key-blocks")
+    assert wl.n_kb == 20480 and wl.topk == 2048
+    test_backward_full_size_720p_dq_blocks(wl, ((0, 0),))
+
+
 # ---------------------------------------------------------------------------------------------------------
 # with the RMSNorm of Q and K before the path: gradients of the raw inputs and of the norm weights
 # ---------------------------------------------------------------------------------------------------------

@@ -279,6 +279,17 @@ def test_zero_and_constant_blocks():
     full_case(SMALL["ragged128"], prep=prep)
 
 
+@pytest.mark.parametrize("mul", [32.0, 1.0 / 64])
+@pytest.mark.parametrize("group32", [False, True], ids=["block", "group32"])
+def test_large_and_small_qk(mul, group32):
+    # Q and K scaled by 32 (scores 1024 times larger: near one-hot rows, the running maximum and the two-instruction
+    # exponent form everywhere, phi(K) up to ~130 in the state table) and by 1/64 (almost flat rows)
+    def prep(q, k, v):
+        return (q.float() * mul).to(torch.bfloat16), (k.float() * mul).to(torch.bfloat16), v
+    # (scaled by 1/64 the pooled scores come within 1e-6 of each other: mask rows may differ there, flagged)
+    full_case(SMALL["ragged128"], prep=prep, group32=group32)
+
+
 def test_given_mask_matches_oracle_with_same_mask():
     wl = SMALL["ragged128"]
     q, k, v, w = synth.make(wl, 3)

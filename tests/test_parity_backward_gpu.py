@@ -90,8 +90,10 @@ def make_mask(wl, topk, seed):
     return np.stack(rows).reshape(wl.B, wl.H, wl.n_qb, topk).astype(np.int32)
 
 
-def case(wl, topk, linear=True, seed=0, sm_scale=0.0):
+def case(wl, topk, linear=True, seed=0, sm_scale=0.0, qk_mul=1.0):
     q, k, v, w = synth.make(wl, seed)
+    if qk_mul != 1.0:
+        q, k = ((t.float() * qk_mul).to(torch.bfloat16) for t in (q, k))
     dy = (torch.randn(q.shape, generator=torch.Generator().manual_seed(seed + 11))).to(torch.bfloat16)
     mask = make_mask(wl, topk, seed)
     say(f"case {wl.name} B{wl.B} H{wl.H} N{wl.N} bq{wl.blk_q} topk{topk} linear{linear} sm_scale{sm_scale}")
@@ -126,6 +128,12 @@ SMALL = {
 def test_backward_mixed(name):
     wl = SMALL[name]
     case(wl, max(1, wl.n_kb // 4))
+
+
+@pytest.mark.parametrize("qk_mul", [8.0, 1.0 / 16])
+def test_backward_large_and_small_qk(qk_mul):
+    # Q and K scaled by 8 (sharp rows, phi(K) large in the linear branch) and by 1/16 (flat rows)
+    case(SMALL["ragged128"], 3, qk_mul=qk_mul)
 
 
 @pytest.mark.parametrize("sm_scale", [0.02, 0.5])

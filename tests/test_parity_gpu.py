@@ -290,6 +290,21 @@ def test_large_and_small_qk(mul, group32):
     full_case(SMALL["ragged128"], prep=prep, group32=group32)
 
 
+@pytest.mark.parametrize("name", ["ragged128", "ragged64"])
+@pytest.mark.parametrize("group32", [False, True], ids=["block", "group32"])
+def test_v_power_of_two_scaling(name, group32):
+    # exact for any arithmetic of the path: V times 2^2 leaves the codes, scales, selection and probabilities as
+    # they are, and every later product, sum, per-block exponent and rounding scales by exactly 2^2, so the outputs
+    # (and the linear branch's) must be 4 times the unscaled ones bit for bit
+    wl = SMALL[name]
+    q, k, v, w = (t.cuda() for t in synth.make(wl, 6))
+    o1, e1 = run_gpu(q, k, v, w, wl, wl.topk, group32=group32)
+    o2, e2 = run_gpu(q, k, (v.float() * 4).to(torch.bfloat16), w, wl, wl.topk, group32=group32)
+    assert torch.equal(o2.float(), o1.float() * 4)
+    assert torch.equal(e2["o_lin"], e1["o_lin"] * 4)
+    assert torch.equal(e2["block_idx"], e1["block_idx"])
+
+
 def test_given_mask_matches_oracle_with_same_mask():
     wl = SMALL["ragged128"]
     q, k, v, w = synth.make(wl, 3)

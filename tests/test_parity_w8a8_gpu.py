@@ -101,6 +101,23 @@ def test_zero_blocks_and_rows():
     np.testing.assert_array_equal(to_np(y[290:]), np.broadcast_to(to_np(b), (10, wl.N)))
 
 
+@pytest.mark.parametrize("clip", [1.0, 0.5])
+def test_power_of_two_scaling(clip):
+    # exact for the arithmetic of the layer: X times 2^5 and W times 2^-2 leave every code as it is and scale each
+    # block scale, each fp32 scale product, each fused multiply-add and the bf16 rounding by powers of two, so
+    # (without a bias) the output must be 2^3 times the unscaled one bit for bit
+    w8 = lib_w8a8()
+    x, w, _ = synth.make_linear(SMALL[0], 9)
+    xg, wg = x.cuda(), w.cuda()
+    wq, ws = w8.quantize(wg)
+    wq2, ws2 = w8.quantize((wg.float() * 0.25).to(torch.bfloat16))
+    y1 = w8.linear(xg, wq, ws, None, clip=clip)
+    y2 = w8.linear((xg.float() * 32).to(torch.bfloat16), wq2, ws2, None, clip=clip)
+    torch.cuda.synchronize()
+    assert torch.equal(wq2, wq) and torch.equal(ws2, ws * 0.25)
+    assert torch.equal(y2.float(), y1.float() * 8)
+
+
 def test_deterministic():
     w8 = lib_w8a8()
     x, w, b = synth.make_linear(SMALL[4], 4)

@@ -130,6 +130,21 @@ def test_backward_mixed(name):
     case(wl, max(1, wl.n_kb // 4))
 
 
+@pytest.mark.parametrize("name", list(SMALL))
+def test_backward_power_of_two_scaling(name):
+    # exact for the arithmetic of the backward: dY times 4 scales dP, D, dS, their bf16 roundings, every product and
+    # sum by a power of two, so dQ, dK, dV and dW_p must be 4 times the unscaled ones bit for bit
+    wl = SMALL[name]
+    q, k, v, w = (t.cuda() for t in synth.make(wl, 12))
+    dy = torch.randn(q.shape, generator=torch.Generator().manual_seed(13)).to(torch.bfloat16).cuda()
+    mask = torch.from_numpy(make_mask(wl, 2, 12)).cuda()
+    g1 = sg.backward(q, k, v, w, dy, mask, topk=2, blk_q=wl.blk_q, blk_k=wl.blk_k)
+    g2 = sg.backward(q, k, v, w, (dy.float() * 4).to(torch.bfloat16), mask, topk=2, blk_q=wl.blk_q, blk_k=wl.blk_k)
+    torch.cuda.synchronize()
+    for name_, a, b in zip(("dq", "dk", "dv", "dw"), g1, g2):
+        assert torch.equal(b, a * 4), name_
+
+
 @pytest.mark.parametrize("qk_mul", [8.0, 1.0 / 16])
 def test_backward_large_and_small_qk(qk_mul):
     # Q and K scaled by 8 (sharp rows, phi(K) large in the linear branch) and by 1/16 (flat rows)

@@ -145,6 +145,23 @@ def test_backward_power_of_two_scaling(name):
         assert torch.equal(b, a * 4), name_
 
 
+def test_backward_heads_are_independent():
+    # exact: dQ, dK, dV of a (b, h) slice depend on that slice alone, so permuting the heads permutes them bit for bit
+    # (dW_p is a sum over heads in a fixed order, so only its value is checked)
+    wl = synth.custom(1, 3, 700, blk_q=128, topk_frac=0.3)
+    q, k, v, w = (t.cuda() for t in synth.make(wl, 15))
+    dy = torch.randn(q.shape, generator=torch.Generator().manual_seed(16)).to(torch.bfloat16).cuda()
+    mask = torch.from_numpy(make_mask(wl, 3, 15)).cuda()
+    g = sg.backward(q, k, v, w, dy, mask, topk=3, blk_q=wl.blk_q, blk_k=wl.blk_k)
+    perm = torch.tensor([1, 2, 0], device="cuda")
+    pc = lambda t: t[:, perm].contiguous()
+    gp = sg.backward(pc(q), pc(k), pc(v), w, pc(dy), pc(mask), topk=3, blk_q=wl.blk_q, blk_k=wl.blk_k)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("dq", "dk", "dv"), g[:3], gp[:3]):
+        assert torch.equal(b, a[:, perm]), name
+    assert torch.allclose(gp[3], g[3], rtol=1e-5, atol=1e-6 * float(g[3].abs().max()))
+
+
 @pytest.mark.parametrize("qk_mul", [8.0, 1.0 / 16])
 def test_backward_large_and_small_qk(qk_mul):
     # Q and K scaled by 8 (sharp rows, phi(K) large in the linear branch) and by 1/16 (flat rows)

@@ -305,6 +305,20 @@ def test_v_power_of_two_scaling(name, group32):
     assert torch.equal(e2["block_idx"], e1["block_idx"])
 
 
+def test_heads_and_batch_entries_are_independent():
+    # exact: every (b, h) slice is computed on its own (W_p is shared, nothing else), so permuting the heads or
+    # running one batch entry alone must reproduce the corresponding slices bit for bit
+    wl = synth.custom(2, 3, 700, blk_q=128, topk_frac=0.3)
+    q, k, v, w = (t.cuda() for t in synth.make(wl, 14))
+    o, e = run_gpu(q, k, v, w, wl, wl.topk)
+    perm = torch.tensor([2, 0, 1], device="cuda")
+    op, ep = run_gpu(q[:, perm].contiguous(), k[:, perm].contiguous(), v[:, perm].contiguous(), w, wl, wl.topk)
+    assert torch.equal(op, o[:, perm]) and torch.equal(ep["block_idx"], e["block_idx"][:, perm])
+    wl1 = synth.custom(1, 3, 700, blk_q=128, topk_frac=0.3)
+    o1, e1 = run_gpu(q[1:].contiguous(), k[1:].contiguous(), v[1:].contiguous(), w, wl1, wl.topk)
+    assert torch.equal(o1, o[1:]) and torch.equal(e1["o_lin"], e["o_lin"][1:])
+
+
 def test_given_mask_matches_oracle_with_same_mask():
     wl = SMALL["ragged128"]
     q, k, v, w = synth.make(wl, 3)
